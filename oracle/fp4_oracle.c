@@ -1,0 +1,518 @@
+/*
+ * fp4_oracle.c -- plain, slow CPU oracle for block-scaled FP4 quantization.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark, never by the product path. It shares no
+ * code with the HIP kernels.
+ *
+ * Build: gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC
+ * (no FMA contraction, no fast-math, SSE float arithmetic: every float
+ * expression below is one IEEE binary32 operation rounded to nearest-even).
+ *
+ * Sources (web pages explaining the papers; cited by title and section):
+ *  [RaZeR]  "RaZeR: Pushing the Limits of NVFP4 Quantization with Redundant Zero
+ *           Remapping", technical summary sec. 1 (E2M1 value set, the +0/-0
+ *           redundancy, the always-positive E4M3 block scale whose sign bit is
+ *           unused) and sec. 2.2 (a freed bit selects a special value that
+ *           replaces the redundant zero code; the block picks the candidate of
+ *           lowest mean squared quantization error; the activation pair is +-5,
+ *           a multiple of 0.5 filling the gap between 4 and 6).
+ *  [TORQ]   "TORQ: Two-Level Orthogonal Rotation for MXFP4 Quantization",
+ *           technical summary sec. 1 (32-element blocks sharing one exponent),
+ *           sec. 2(a) (orthogonal transform that equalises the block variances),
+ *           sec. 2(b) (intra-block rotation; the S-step maps each block's
+ *           largest magnitude onto the largest MXFP4 code).
+ * Where the pages are silent the reading used is stated at the function.
+ *
+ * Parity status of each function is recorded in oracle/__init__.py.
+ */
+#include "fp4_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int g_threads = 1;
+
+int orc_version(void) { return 1; }
+
+void orc_set_threads(int n) { g_threads = n > 0 ? n : 1; }
+
+int orc_get_threads(void) { return g_threads; }
+
+/* ------------------------------------------------------------------------ */
+/* Element format: FP4 E2M1, sign-magnitude.                                  */
+/* [RaZeR] sec. 1 prints the value set {+-0, +-0.5, +-1, +-1.5, +-2, +-3,    */
+/* +-4, +-6}. Code = sign << 3 | magnitude index, magnitudes in ascending    */
+/* order (the usual E2M1 bit layout: 2 exponent bits, 1 mantissa bit).       */
+/* ------------------------------------------------------------------------ */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_value(int code) {
+  double m = E2M1_MAG[code & 7];
+  return (code & 8) ? -m : m;
+}
+
+/* Index of the magnitude nearest to a >= 0. Reading (pages silent): ties go
+ * to the even index, i.e. round-half-to-even on the E2M1 mantissa bit; values
+ * above 6 saturate to 6 because 6 is then the nearest magnitude. For a <= 6
+ * that arises from an fp32 value times a power of two, every distance that
+ * decides a near-tie is exact in double. */
+static int nearest_mag(double a) {
+  /* Every a > 6 is nearest to 6; stated directly because for very large a
+   * the double distances below round to equal values. */
+  if (a > 6.0) return 7;
+  int best = 0;
+  double bestd = fabs(a - E2M1_MAG[0]);
+  for (int k = 1; k < 8; ++k) {
+    double d = fabs(a - E2M1_MAG[k]);
+    if (d < bestd || (d == bestd && (k % 2 == 0) && (best % 2 != 0))) {
+      best = k;
+      bestd = d;
+    }
+  }
+  return best;
+}
+
+/* Plain E2M1 code of a scaled value y. Reading: the sign is kept even when
+ * the magnitude rounds to zero (both zeros exist, [RaZeR] sec. 1), so a
+ * negative value that rounds to zero gets code 0x8. */
+int orc_e2m1_nearest(double y) {
+  int s = signbit(y) ? 1 : 0;
+  return (s << 3) | nearest_mag(fabs(y));
+}
+
+/* RaZeR code book: the fifteen standard values (zero only as +0, code 0x0)
+ * plus the special value at the freed code 0x8 ([RaZeR] sec. 2.2). The
+ * nearest entry wins; the special value wins only when strictly closer than
+ * every standard value (reading: ties keep the standard code). */
+int orc_e2m1_nearest_razer(double y, double special) {
+  int idx = nearest_mag(fabs(y));
+  double v_std = idx == 0 ? 0.0 : (signbit(y) ? -E2M1_MAG[idx] : E2M1_MAG[idx]);
+  int code_std = idx == 0 ? 0 : (((signbit(y) ? 1 : 0) << 3) | idx);
+  if (fabs(y - special) < fabs(y - v_std)) return 8;
+  return code_std;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block scale formats.                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* FP8 E4M3 as used for the NVFP4 block scale ([RaZeR] sec. 1 names the
+ * format). Reading: the OCP "E4M3FN" encoding -- bias 7, subnormals m*2^-9,
+ * largest finite 448, S.1111.111 is NaN, no infinities. */
+double orc_e4m3_value(int code) {
+  int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Nearest non-negative finite E4M3 value to v >= 0 by exhaustive search over
+ * the 127 codes 0x00..0x7E; ties go to the even code (round-half-to-even),
+ * values above 448 saturate to 448 (code 0x7E) because it is then nearest. */
+int orc_e4m3_encode(double v) {
+  /* stated directly: for very large v the double distances round to equal */
+  if (v > 448.0) return 0x7E;
+  int best = 0;
+  double bestd = fabs(v - orc_e4m3_value(0));
+  for (int c = 1; c <= 0x7E; ++c) {
+    double d = fabs(v - orc_e4m3_value(c));
+    if (d < bestd || (d == bestd && (c % 2 == 0) && (best % 2 != 0))) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return best;
+}
+
+/* E8M0: a bare power of two 2^(byte-127); byte 0xFF is NaN. */
+double orc_e8m0_value(int byte) {
+  if ((byte & 0xFF) == 0xFF) return NAN;
+  return ldexp(1.0, (byte & 0xFF) - 127);
+}
+
+/* MXFP4 shared exponent of a block with largest magnitude amax.
+ * Default rule ([TORQ] sec. 2(b), S-step: the block maximum maps onto the top
+ * code, 6): the smallest e in [-127, 127] with amax <= 6 * 2^e, found by
+ * trying every e in ascending order, so no element is clipped. amax == 0 gives
+ * e = -127. A block holding Inf or NaN gets the NaN byte 0xFF.
+ * floor_rule != 0 selects the alternative e = floor(log2 amax) - 2, clamped to
+ * [-127, 127], under which magnitudes above 6 * 2^e saturate to 6. */
+int orc_e8m0_scale(double amax, int floor_rule) {
+  if (!isfinite(amax)) return 0xFF;
+  if (floor_rule) {
+    if (amax == 0.0) return 0;
+    int k;
+    frexp(amax, &k); /* amax = f * 2^k, f in [0.5, 1): floor(log2) = k - 1 */
+    int e = (k - 1) - 2;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e + 127;
+  }
+  for (int e = -127; e <= 127; ++e)
+    if (amax <= ldexp(6.0, e)) return e + 127;
+  return 254;
+}
+
+float orc_bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* Round-to-nearest-even binary32 -> bfloat16, NaN kept as a quiet NaN,
+ * overflow to +-Inf. */
+uint16_t orc_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+static void put_nibble(uint8_t* row_codes, int64_t j, int code) {
+  uint8_t* b = row_codes + (j >> 1);
+  if (j & 1)
+    *b = (uint8_t)((*b & 0x0F) | ((code & 15) << 4));
+  else
+    *b = (uint8_t)((*b & 0xF0) | (code & 15));
+}
+
+static int get_nibble(const uint8_t* row_codes, int64_t j) {
+  uint8_t b = row_codes[j >> 1];
+  return (j & 1) ? (b >> 4) : (b & 15);
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP4 quantization: blocks of 32 consecutive elements of a row ([TORQ]    */
+/* sec. 1), one E8M0 byte per block, element 2i in the low nibble and 2i+1   */
+/* in the high nibble of byte i (reading: pages silent on packing order).    */
+/* ------------------------------------------------------------------------ */
+static void mx_block(const float* v, int floor_rule, uint8_t* row_codes, int64_t j0,
+                     uint8_t* scale_out) {
+  double amax = 0.0;
+  int nonfinite = 0;
+  for (int i = 0; i < 32; ++i) {
+    if (!isfinite(v[i])) nonfinite = 1;
+    double a = fabs((double)v[i]);
+    if (a > amax) amax = a;
+  }
+  if (nonfinite) {
+    *scale_out = 0xFF;
+    for (int i = 0; i < 32; ++i) put_nibble(row_codes, j0 + i, 0);
+    return;
+  }
+  int byte = orc_e8m0_scale(amax, floor_rule);
+  *scale_out = (uint8_t)byte;
+  int e = byte - 127;
+  for (int i = 0; i < 32; ++i) {
+    double y = ldexp((double)v[i], -e); /* exact: a power-of-two rescale */
+    put_nibble(row_codes, j0 + i, orc_e2m1_nearest(y));
+  }
+}
+
+void orc_mx_quantize_f32(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                         int floor_rule, uint8_t* codes, int64_t ld_codes,
+                         uint8_t* scales, int64_t ld_scales) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < cols / 32; ++b)
+      mx_block(x + r * ld_x + 32 * b, floor_rule, codes + r * ld_codes, 32 * b,
+               scales + r * ld_scales + b);
+}
+
+void orc_mx_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                          int floor_rule, uint8_t* codes, int64_t ld_codes,
+                          uint8_t* scales, int64_t ld_scales) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r) {
+    float v[32];
+    for (int64_t b = 0; b < cols / 32; ++b) {
+      for (int i = 0; i < 32; ++i) v[i] = orc_bf16_to_f32(x[r * ld_x + 32 * b + i]);
+      mx_block(v, floor_rule, codes + r * ld_codes, 32 * b, scales + r * ld_scales + b);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4: blocks of 16, E4M3 block scale, fp32 per-tensor scale s_t.          */
+/* The scale is derived from the block absmax and is therefore positive, so  */
+/* its sign bit is free ([RaZeR] sec. 1). Readings where the pages are       */
+/* silent: s_t = amax_t / (6 * 448) so the largest block product reaches     */
+/* 6 * 448; s_raw = amax_b / (6 * s_t); the E4M3 byte is the nearest value;  */
+/* the element scale is s_eff = e4m3(s_b) * s_t and elements are multiplied  */
+/* by the rounded reciprocal of s_eff. Each step is one fp32 operation.      */
+/* ------------------------------------------------------------------------ */
+float orc_nv_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x) {
+  float amax = 0.0f;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t j = 0; j < cols; ++j) {
+      float a = fabsf(orc_bf16_to_f32(x[r * ld_x + j]));
+      if (a > amax) amax = a;
+    }
+  return amax;
+}
+
+float orc_nv_tensor_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  return amax / 2688.0f; /* 2688 = 6 * 448 */
+}
+
+/* [RaZeR] sec. 2.2: per block, pick from the pair {+5, -5} the special value
+ * of least squared quantization error; the selector is stored in the block
+ * scale's free sign bit (reading: bit 0 -> +5, bit 1 -> -5; equal error ->
+ * bit 0). codes[] receives n unpacked codes for the chosen candidate.
+ *
+ * The two candidate code vectors differ only where the nearest entry changes;
+ * elsewhere both squared errors are the same double, so their difference is
+ * exactly zero. Where they differ, y lies in (4.5, 5.5), a binade in which
+ * fp32 values are multiples of 2^-21, so each squared error and each
+ * difference is exact in double and so is the sum. SSE(+5) - SSE(-5) is
+ * therefore computed without rounding error and the comparison is exact.
+ * Returns the selector bit. */
+int orc_razer_block(const float* y, int n, uint8_t* codes, double* sse_chosen,
+                    double* sse_plain) {
+  uint8_t cp[64], cm[64];
+  double diff = 0.0, ssp = 0.0, ssm = 0.0, ss0 = 0.0;
+  for (int i = 0; i < n; ++i) {
+    double v = (double)y[i];
+    cp[i] = (uint8_t)orc_e2m1_nearest_razer(v, 5.0);
+    cm[i] = (uint8_t)orc_e2m1_nearest_razer(v, -5.0);
+    double vp = cp[i] == 8 ? 5.0 : orc_e2m1_value(cp[i]);
+    double vm = cm[i] == 8 ? -5.0 : orc_e2m1_value(cm[i]);
+    double ep = (v - vp) * (v - vp), em = (v - vm) * (v - vm);
+    diff += ep - em;
+    ssp += ep;
+    ssm += em;
+    double v0 = orc_e2m1_value(orc_e2m1_nearest(v));
+    ss0 += (v - v0) * (v - v0);
+  }
+  int sel = diff > 0.0 ? 1 : 0;
+  for (int i = 0; i < n; ++i) codes[i] = sel ? cm[i] : cp[i];
+  if (sse_chosen) *sse_chosen = sel ? ssm : ssp;
+  if (sse_plain) *sse_plain = ss0;
+  return sel;
+}
+
+void orc_nv_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                          int razer, float tensor_scale, uint8_t* codes, int64_t ld_codes,
+                          uint8_t* scales, int64_t ld_scales) {
+  const float s_t = tensor_scale;
+  const float d = 6.0f * s_t;
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < cols / 16; ++b) {
+      float xv[16], y[16];
+      float amax = 0.0f;
+      for (int i = 0; i < 16; ++i) {
+        xv[i] = orc_bf16_to_f32(x[r * ld_x + 16 * b + i]);
+        if (fabsf(xv[i]) > amax) amax = fabsf(xv[i]);
+      }
+      float s_raw = amax / d;
+      int sb = orc_e4m3_encode((double)s_raw);
+      uint8_t* rc = codes + r * ld_codes;
+      if (sb == 0) { /* scale rounds to zero: the block is stored as zeros */
+        for (int i = 0; i < 16; ++i) put_nibble(rc, 16 * b + i, 0);
+        scales[r * ld_scales + b] = 0;
+        continue;
+      }
+      float s_eff = (float)orc_e4m3_value(sb) * s_t;
+      float rcp = 1.0f / s_eff;
+      for (int i = 0; i < 16; ++i) y[i] = xv[i] * rcp;
+      if (razer) {
+        uint8_t c[16];
+        int sel = orc_razer_block(y, 16, c, NULL, NULL);
+        for (int i = 0; i < 16; ++i) put_nibble(rc, 16 * b + i, c[i]);
+        scales[r * ld_scales + b] = (uint8_t)(sb | (sel << 7));
+      } else {
+        for (int i = 0; i < 16; ++i) put_nibble(rc, 16 * b + i, orc_e2m1_nearest((double)y[i]));
+        scales[r * ld_scales + b] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dequantization. MXFP4: value * 2^e, exact before the final rounding.      */
+/* NVFP4: fp32 product value * s_eff. RaZeR: code 0x8 decodes to the block's */
+/* special value, +5 or -5 by the scale's top bit ([RaZeR] sec. 2.2 and 2.3: */
+/* the decoder rebuilds the special value from the metadata bits).           */
+/* A NaN E8M0 byte decodes every element of its block to NaN.                */
+/* ------------------------------------------------------------------------ */
+static double dq_value(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
+                       int64_t ld_scales, float s_t, int64_t r, int64_t j, int format,
+                       int razer) {
+  int c = get_nibble(codes + r * ld_codes, j);
+  if (format == 0) {
+    int byte = scales[r * ld_scales + j / 32];
+    if (byte == 0xFF) return NAN;
+    return ldexp(orc_e2m1_value(c), byte - 127);
+  }
+  int byte = scales[r * ld_scales + j / 16];
+  double v;
+  float s_eff;
+  if (razer) {
+    s_eff = (float)orc_e4m3_value(byte & 0x7F) * s_t;
+    v = (c == 8) ? ((byte & 0x80) ? -5.0 : 5.0) : orc_e2m1_value(c);
+  } else {
+    s_eff = (float)orc_e4m3_value(byte) * s_t;
+    v = orc_e2m1_value(c);
+  }
+  float p = (float)v * s_eff;
+  return (double)p;
+}
+
+void orc_dequantize_f64(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
+                        int64_t ld_scales, float tensor_scale, int64_t rows, int64_t cols,
+                        int format, int razer, double* out, int64_t ld_out) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r)
+    for (int64_t j = 0; j < cols; ++j)
+      out[r * ld_out + j] =
+          dq_value(codes, ld_codes, scales, ld_scales, tensor_scale, r, j, format, razer);
+}
+
+void orc_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
+                    int64_t ld_scales, float tensor_scale, int64_t rows, int64_t cols,
+                    int format, int razer, uint16_t* out, int64_t ld_out) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r)
+    for (int64_t j = 0; j < cols; ++j) {
+      double v = dq_value(codes, ld_codes, scales, ld_scales, tensor_scale, r, j, format, razer);
+      out[r * ld_out + j] = orc_f32_to_bf16((float)v); /* exact or already fp32 */
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Two-level rotation ([TORQ] sec. 2(a) and 2(b)).                            */
+/* Level 1: a channel permutation pi, x'[j] = x[pi(j)], chosen offline so    */
+/* that every 32-block receives the same mix of high- and low-energy         */
+/* channels (an orthogonal transform that evens out the block variances).    */
+/* Level 2: the orthonormal Sylvester-Hadamard matrix inside each block,     */
+/* H[i][j] = (-1)^popcount(i & j) / sqrt(n), applied as a dense product in   */
+/* double and rounded once to fp32.                                          */
+/* ------------------------------------------------------------------------ */
+double orc_hadamard_entry(int n, int i, int j) {
+  int p = __builtin_popcount((unsigned)(i & j)) & 1;
+  return (p ? -1.0 : 1.0) / sqrt((double)n);
+}
+
+void orc_rotate(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                const int32_t* perm, int hadamard, float* out, int64_t ld_out) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r) {
+    double xp[64];
+    for (int64_t b0 = 0; b0 < cols; b0 += (hadamard ? hadamard : cols)) {
+      int64_t n = hadamard ? hadamard : cols;
+      for (int64_t j = 0; j < n; ++j) {
+        int64_t src = perm ? perm[b0 + j] : b0 + j;
+        double v = (double)orc_bf16_to_f32(x[r * ld_x + src]);
+        if (hadamard)
+          xp[j] = v;
+        else
+          out[r * ld_out + b0 + j] = (float)v;
+      }
+      if (!hadamard) break;
+      for (int i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < n; ++j) acc += orc_hadamard_entry((int)n, i, j) * xp[j];
+        out[r * ld_out + b0 + i] = (float)acc;
+      }
+    }
+  }
+}
+
+/* Inverse of orc_rotate in double: H is symmetric and orthonormal, so its
+ * inverse is H itself; the permutation is undone by scattering to pi(j). */
+void orc_unrotate_f64(const double* y, int64_t rows, int64_t cols, int64_t ld_y,
+                      const int32_t* perm, int hadamard, double* out, int64_t ld_out) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r) {
+    int64_t n = hadamard ? hadamard : 1;
+    for (int64_t b0 = 0; b0 < cols; b0 += n) {
+      for (int64_t j = 0; j < n; ++j) {
+        double acc;
+        if (hadamard) {
+          acc = 0.0;
+          for (int64_t i = 0; i < n; ++i)
+            acc += orc_hadamard_entry((int)n, (int)i, (int)j) * y[r * ld_y + b0 + i];
+        } else {
+          acc = y[r * ld_y + b0 + j];
+        }
+        int64_t dst = perm ? perm[b0 + j] : b0 + j;
+        out[r * ld_out + dst] = acc;
+      }
+    }
+  }
+}
+
+/* Per-channel energy E_c = sum over rows of x_rc^2, in double, row order.
+ * It is the diagonal of the (uncentred) activation second-moment matrix whose
+ * 32x32 diagonal blocks carry the block variances in [TORQ] sec. 2(a). */
+void orc_channel_energy(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                        double* energy) {
+  for (int64_t j = 0; j < cols; ++j) energy[j] = 0.0;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t j = 0; j < cols; ++j) {
+      double v = (double)orc_bf16_to_f32(x[r * ld_x + j]);
+      energy[j] += v * v;
+    }
+}
+
+static const float* g_sort_energy;
+
+static int by_energy_desc(const void* a, const void* b) {
+  int32_t ia = *(const int32_t*)a, ib = *(const int32_t*)b;
+  float ea = g_sort_energy[ia], eb = g_sort_energy[ib];
+  if (ea > eb) return -1;
+  if (ea < eb) return 1;
+  return ia < ib ? -1 : (ia > ib ? 1 : 0);
+}
+
+/* Magnitude-balancing permutation (reading of [TORQ] sec. 2(a) -- an
+ * orthogonal transform that makes the block variances equal -- restricted to
+ * permutations; the pages build their macro rotation from Givens rotations).
+ * Channels are taken largest energy first (equal energies by lower index)
+ * and each goes to the block whose accumulated energy is smallest among the
+ * blocks that still have a free slot (equal loads: lower block index), in the
+ * block's next free slot. Loads are summed in double. perm[j] is the source
+ * channel of position j. Not thread-safe (qsort comparator state). */
+void orc_build_perm(const float* energy, int64_t cols, int block, int32_t* perm) {
+  int64_t B = cols / block;
+  int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)cols);
+  double* load = (double*)calloc((size_t)B, sizeof(double));
+  int64_t* fill = (int64_t*)calloc((size_t)B, sizeof(int64_t));
+  for (int64_t j = 0; j < cols; ++j) order[j] = (int32_t)j;
+  g_sort_energy = energy;
+  qsort(order, (size_t)cols, sizeof(int32_t), by_energy_desc);
+  for (int64_t t = 0; t < cols; ++t) {
+    int64_t best = -1;
+    for (int64_t b = 0; b < B; ++b) {
+      if (fill[b] == block) continue;
+      if (best < 0 || load[b] < load[best]) best = b;
+    }
+    int32_t c = order[t];
+    perm[best * block + fill[best]] = c;
+    fill[best] += 1;
+    load[best] += (double)energy[c];
+  }
+  free(order);
+  free(load);
+  free(fill);
+}

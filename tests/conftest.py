@@ -1,0 +1,29 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size workload")
+
+
+@pytest.fixture(scope="session")
+def orc():
+    import oracle
+    oracle.build(force=False)
+    oracle.set_threads(min(8, os.cpu_count() or 1))
+    return oracle
+
+
+def read_golden(name):
+    """Non-comment, non-empty lines of a golden fixture."""
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
