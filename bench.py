@@ -1,0 +1,352 @@
+"""Throughput of the block-scaled FP4 hot path on one MI355X.
+
+Default workload: the two-level-rotation activation tensor, 16384 x 8192 bf16
+with per-32-channel-block variances exp(1.5 z) (synthetic, seeded). One step
+is one fused call of the online path -- channel permutation, 32-point block
+Hadamard, MXFP4 absmax / E8M0 scale / E2M1 rounding / nibble packing -- over
+the whole tensor (one kernel launch). The permutation is calibrated once,
+before timing, from the tensor's channel energies (offline step, reported).
+
+value = input bytes (rows * cols * 2) / time per step, GB/s, with the input
+resident in HBM: two input copies (2 x 268 MB, more than the 256 MB Infinity
+Cache) are used alternately so no step reads the previous step's data from
+cache. Timing uses HIP events on the stream the kernels run on.
+
+The same run also reports the other rows of the path on their own workloads
+(plain MXFP4, NVFP4 + RaZeR with and without the tensor-amax pass, the
+dequantizers) and the CPU oracle timed on a bounded sample of the workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload c4|c2|c5] [--no-extras]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "quantize+pack GB/s (bf16 in) and % of HBM peak on 1 MI355X; SQNR dB"
+HBM_PEAK_GBS = 8000.0
+B_MX = 2 + 0.5 + 1 / 32   # algorithmic bytes per element, MXFP4 quantize
+B_NV = 2 + 0.5 + 1 / 16   # NVFP4 quantize (without the tensor-amax read)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="c4", choices=["c4", "c2", "c5"])
+    p.add_argument("--no-extras", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def timed(torch, fn, steps, warmup):
+    """ms per call of fn(i), measured with events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for i in range(steps):
+        fn(warmup + i)
+    b.record(st)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def dev_copies(torch, x_u16, n):
+    import numpy as np
+    t = torch.from_numpy(x_u16.view(np.int16)).cuda().view(torch.bfloat16)
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+def copies_for(nbytes, floor=2):
+    """Enough copies that their total exceeds twice the 256 MB Infinity Cache."""
+    return max(floor, -(-512 * 2 ** 20 // nbytes))
+
+
+def sqnr_db(torch, x, xh):
+    x = x.double()
+    d = x - xh.double()
+    return float(10 * torch.log10((x * x).sum() / (d * d).sum()))
+
+
+def cpu_threads():
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baseline(workload, x, perm, target_s):
+    """The oracle as it stands on a bounded row sample of the same tensor."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    th = cpu_threads()
+    oracle.set_threads(th)
+    cols = x.shape[1]
+
+    def run(rows):
+        xs = np.ascontiguousarray(x[:rows])
+        t0 = time.perf_counter()
+        if workload == "c4":
+            oracle.rotate_quantize(xs, perm, 32)
+        else:
+            oracle.nv_quantize(xs, True)
+        return time.perf_counter() - t0
+
+    probe = min(x.shape[0], 64)
+    dt = run(probe)
+    rows = int(min(x.shape[0], max(probe, probe * target_s / max(dt, 1e-6))))
+    dt = run(rows)
+    return {"value": rows * cols * 2 / dt / 1e9, "unit": "GB/s", "cores": th, "kind": "oracle",
+            "sample": f"first {rows} rows x {cols} cols of the same tensor "
+                      f"({rows * cols} elements), {dt:.1f} s on {th} threads"}
+
+
+def bench_c4(torch, fp4, inputs, args):
+    import numpy as np
+    rows, cols = inputs.FULL_SHAPES["c4"]
+    log(f"[bench] generating c4 {rows}x{cols}")
+    x = inputs.gen_c4()
+    xs = dev_copies(torch, x, copies_for(x.nbytes))
+    n = len(xs)
+    codes = [torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda") for _ in range(n)]
+    scales = [torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda") for _ in range(n)]
+
+    log("[bench] calibrating the permutation (channel energy + host builder)")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    energy = fp4.channel_energy(xs[0])
+    perm_cpu = fp4.build_permutation(energy)
+    perm = perm_cpu.cuda()
+    torch.cuda.synchronize()
+    calib_ms = (time.perf_counter() - t0) * 1e3
+    e_ms = timed(torch, lambda i: fp4.channel_energy(xs[i % n]), 5, 1)
+
+    def step(i):
+        k = i % n
+        fp4.rotate_quantize(xs[k], perm, 32, codes=codes[k], scales=scales[k])
+
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
+    ms = timed(torch, step, args.steps, args.warmup)
+    elems = rows * cols
+    value = elems * 2 / (ms * 1e-3) / 1e9
+    achieved = elems * B_MX / (ms * 1e-3) / 1e9
+
+    xh = fp4.dequantize(codes[0], scales[0], fp4.MXFP4, perm=perm, hadamard=32)
+    q = sqnr_db(torch, xs[0].float(), xh.float())
+    c_pl, s_pl, _ = fp4.quantize(xs[0], fp4.MXFP4)
+    q_plain = sqnr_db(torch, xs[0].float(), fp4.dequantize(c_pl, s_pl, fp4.MXFP4).float())
+
+    extras = {"calibration_ms": round(calib_ms, 3), "channel_energy_ms": round(e_ms, 4),
+              "sqnr_db_plain_mxfp4": round(q_plain, 3)}
+    if not args.no_extras:
+        extras.update(extra_rows(torch, fp4, inputs, xs, perm, codes, scales))
+    res = {
+        "ms": ms, "value": value, "elems": elems, "sqnr": q,
+        "config": {"workload": "c4: 16384x8192 bf16 activations, per-32-channel-block "
+                               "variance exp(1.5 z); channel permutation + block Hadamard-32 "
+                               "+ MXFP4 (E8M0, block 32) quantize + pack",
+                   "rows": rows, "cols": cols, "format": "mxfp4", "block": 32,
+                   "rotation": "perm+hadamard32", "input_copies": n},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "mx_rotq_perm_kernel<true,false,false>",
+                     "bytes_per_launch": int(elems * B_MX)},
+        "extras": extras,
+    }
+    return res, x, perm_cpu.numpy()
+
+
+def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
+    """The other rows of the path, each on its own workload, same protocol."""
+    out = {}
+    n = len(xs)
+    rows, cols = xs[0].shape
+    el = rows * cols
+
+    def gbs(ms, elems, per_el):
+        return {"ms": round(ms, 5), "input_GBps": round(elems * 2 / ms / 1e6, 1),
+                "algorithmic_GBps": round(elems * per_el / ms / 1e6, 1)}
+
+    ms = timed(torch, lambda i: fp4.quantize(xs[i % n], fp4.MXFP4, codes=codes[i % n],
+                                             scales=scales[i % n]), 20, 3)
+    out["c4_mxfp4_plain_quantize"] = gbs(ms, el, B_MX)
+    ms = timed(torch, lambda i: fp4.rotate_quantize(xs[i % n], None, 32, codes=codes[i % n],
+                                                    scales=scales[i % n]), 20, 3)
+    out["c4_mxfp4_hadamard_only"] = gbs(ms, el, B_MX)
+    outb = torch.empty_like(xs[0])
+    ms = timed(torch, lambda i: fp4.dequantize(codes[i % n], scales[i % n], fp4.MXFP4, out=outb),
+               20, 3)
+    out["c4_mxfp4_dequantize"] = gbs(ms, el, B_MX)
+    ms = timed(torch, lambda i: fp4.dequantize(codes[i % n], scales[i % n], fp4.MXFP4, perm=perm,
+                                               hadamard=32, out=outb), 20, 3)
+    out["c4_mxfp4_dequantize_unrotate"] = gbs(ms, el, B_MX)
+
+    # NVFP4 + RaZeR on the 4096x4096 weight recipe, enough copies to defeat the cache
+    log("[bench] generating c2 for the NVFP4 rows")
+    x2 = inputs.gen_c2()
+    r2, c2 = x2.shape
+    ys = dev_copies(torch, x2, copies_for(x2.nbytes))
+    m = len(ys)
+    cs = [torch.empty((r2, c2 // 2), dtype=torch.uint8, device="cuda") for _ in range(m)]
+    ss = [torch.empty((r2, c2 // 16), dtype=torch.uint8, device="cuda") for _ in range(m)]
+    tss = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(m)]
+    el2 = r2 * c2
+    ms = timed(torch, lambda i: fp4.quantize(ys[i % m], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[i % m],
+                                             scale_given=False, codes=cs[i % m],
+                                             scales=ss[i % m]), 40, 5)
+    out["c2_nvfp4_razer_quantize_with_amax"] = gbs(ms, el2, B_NV + 2)
+    xh = fp4.dequantize(cs[0], ss[0], fp4.NVFP4, fp4.RAZER, tss[0])
+    out["c2_sqnr_db_razer"] = round(sqnr_db(torch, ys[0].float(), xh.float()), 3)
+    ms = timed(torch, lambda i: fp4.quantize(ys[i % m], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[i % m],
+                                             codes=cs[i % m], scales=ss[i % m]), 40, 5)
+    out["c2_nvfp4_razer_quantize_scale_given"] = gbs(ms, el2, B_NV)
+    ms = timed(torch, lambda i: fp4.quantize(ys[i % m], fp4.NVFP4, fp4.PLAIN, tensor_scale=tss[i % m],
+                                             codes=cs[i % m], scales=ss[i % m]), 40, 5)
+    out["c2_nvfp4_plain_quantize_scale_given"] = gbs(ms, el2, B_NV)
+    for k in range(m):
+        fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[k], codes=cs[k], scales=ss[k])
+    ob = torch.empty_like(ys[0])
+    ms = timed(torch, lambda i: fp4.dequantize(cs[i % m], ss[i % m], fp4.NVFP4, fp4.RAZER,
+                                               tss[i % m], out=ob), 40, 5)
+    out["c2_nvfp4_razer_dequantize"] = gbs(ms, el2, B_NV)
+    cp, sp, tp = fp4.quantize(ys[0], fp4.NVFP4, fp4.PLAIN)
+    xp = fp4.dequantize(cp, sp, fp4.NVFP4, fp4.PLAIN, tp)
+    out["c2_sqnr_db_plain_nvfp4"] = round(sqnr_db(torch, ys[0].float(), xp.float()), 3)
+    del ys, cs, ss
+    return out
+
+
+def bench_c2(torch, fp4, inputs, args):
+    r, c = inputs.FULL_SHAPES["c2"]
+    x = inputs.gen_c2()
+    ys = dev_copies(torch, x, copies_for(x.nbytes))
+    m = len(ys)
+    cs = [torch.empty((r, c // 2), dtype=torch.uint8, device="cuda") for _ in range(m)]
+    ss = [torch.empty((r, c // 16), dtype=torch.uint8, device="cuda") for _ in range(m)]
+    tss = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(m)]
+
+    def step(i):
+        k = i % m
+        fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[k], scale_given=False,
+                     codes=cs[k], scales=ss[k])
+
+    ms = timed(torch, step, args.steps, args.warmup)
+    el = r * c
+    xh = fp4.dequantize(cs[0], ss[0], fp4.NVFP4, fp4.RAZER, tss[0])
+    res = {"ms": ms, "value": el * 2 / ms / 1e6, "elems": el,
+           "sqnr": sqnr_db(torch, ys[0].float(), xh.float()),
+           "config": {"workload": "c2: 4096x4096 bf16 weights N(0,0.02) + 0.5% Laplace(0,0.3); "
+                                  "NVFP4 (E4M3 block 16 + fp32 tensor scale) + RaZeR, tensor "
+                                  "amax computed each step", "rows": r, "cols": c,
+                      "format": "nvfp4", "block": 16, "mode": "razer", "input_copies": m},
+           "roofline": {"bound": "hbm", "achieved": el * (B_NV + 2) / ms / 1e6,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": el * (B_NV + 2) / ms / 1e6 / HBM_PEAK_GBS, "traffic": None,
+                        "kernel": "nv_amax_kernel + nv_quant_kernel<true,true>",
+                        "bytes_per_launch": int(el * (B_NV + 2))},
+           "extras": {}}
+    return res, x, None
+
+
+def bench_c5(torch, fp4, inputs, args):
+    """Llama-70B-shaped layer: NVFP4+RaZeR quantize then dequantize of all 7 weights."""
+    xs, cs, ss, ts, outs = [], [], [], [], []
+    el = 0
+    for t, (name, r, c) in enumerate(inputs.C5_SHAPES):
+        log(f"[bench] generating c5 {name} {r}x{c}")
+        x = inputs.gen_c5(t)
+        xs.append(dev_copies(torch, x, 1)[0])
+        cs.append(torch.empty((r, c // 2), dtype=torch.uint8, device="cuda"))
+        ss.append(torch.empty((r, c // 16), dtype=torch.uint8, device="cuda"))
+        ts.append(torch.empty(1, dtype=torch.float32, device="cuda"))
+        outs.append(torch.empty_like(xs[-1]))
+        el += r * c
+        del x
+
+    def step(i):
+        for k in range(len(xs)):
+            fp4.quantize(xs[k], fp4.NVFP4, fp4.RAZER, tensor_scale=ts[k], scale_given=False,
+                         codes=cs[k], scales=ss[k])
+            fp4.dequantize(cs[k], ss[k], fp4.NVFP4, fp4.RAZER, ts[k], out=outs[k])
+
+    ms = timed(torch, step, max(1, args.steps // 5), max(1, args.warmup // 5))
+    num = sum(float((xs[k].double() ** 2).sum()) for k in range(len(xs)))
+    den = sum(float(((xs[k].double() - outs[k].double()) ** 2).sum()) for k in range(len(xs)))
+    import math
+    per_el = (B_NV + 2) + B_NV
+    res = {"ms": ms, "value": el * 2 / ms / 1e6, "elems": el, "sqnr": 10 * math.log10(num / den),
+           "config": {"workload": "c5: Llama-70B-shaped decoder-layer weights q,k,v,o,gate,up,"
+                                  "down (855,638,016 bf16), NVFP4+RaZeR quantize with tensor "
+                                  "amax, then dequantize to bf16", "tensors": 7,
+                      "format": "nvfp4", "block": 16, "mode": "razer"},
+           "roofline": {"bound": "hbm", "achieved": el * per_el / ms / 1e6, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": el * per_el / ms / 1e6 / HBM_PEAK_GBS,
+                        "traffic": None, "kernel": "nv_amax + nv_quant + nv_dequant (7 tensors)",
+                        "bytes_per_launch": int(el * per_el)},
+           "extras": {}}
+    return res, None, None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path runs on one MI355X and has no "
+              "multi-GPU mode (rows shard with no communication); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_scaled_fp4_absmax_amd as fp4
+    from block_scaled_fp4_absmax_amd import inputs
+
+    fp4.lib()  # fails loudly if the HIP library is not built
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    fn = {"c4": bench_c4, "c2": bench_c2, "c5": bench_c5}[args.workload]
+    res, x_host, perm = fn(torch, fp4, inputs, args)
+
+    cpu = None
+    if not args.no_cpu and x_host is not None:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(args.workload, x_host, perm, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(res["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": res["config"],
+        "hbm_frac_input": round(res["value"] / HBM_PEAK_GBS, 4),
+        "sqnr_db": round(res["sqnr"], 3),
+        "roofline": res["roofline"],
+        "cpu_baseline": cpu,
+        "extras": res["extras"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+"""Block-scaled FP4 (MXFP4 / NVFP4, RaZeR, two-level rotation) for MI355X.
+
+Thin Python binding over the C ABI in ``include/fp4.h`` (``libfp4.so``, built
+in-tree by ``block_scaled_fp4_absmax_amd.build``). Every step of the path runs
+in the library's HIP kernels; this module only allocates outputs with torch,
+passes pointers, sizes and torch's current stream, and turns a non-zero status
+into an exception. There is no fallback: if the library is missing, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "MXFP4", "NVFP4", "PLAIN", "RAZER", "FLAG_TENSOR_SCALE_GIVEN", "FLAG_SCALE_OCP_FLOOR",
+    "Fp4Error", "lib", "library_path", "quantize", "dequantize", "rotate_quantize",
+    "channel_energy", "build_permutation", "block_of",
+]
+
+MXFP4, NVFP4 = 0, 1
+PLAIN, RAZER = 0, 1
+FLAG_TENSOR_SCALE_GIVEN = 1
+FLAG_SCALE_OCP_FLOOR = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfp4.so")
+_lib = None
+
+
+class Fp4Error(RuntimeError):
+    """A libfp4 call returned a non-zero fp4_status."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfp4.so with argument types set (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -m block_scaled_fp4_absmax_amd.build` "
+            "or __graft_entry__.build() first")
+    L = ctypes.CDLL(_LIB_PATH)
+    i64, i32, u32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p
+    sig = {
+        "fp4_version": (i32, []),
+        "fp4_status_string": (ctypes.c_char_p, [i32]),
+        "fp4_quantize": (i32, [vp, i64, i64, i64, i32, i32, i32, u32, vp, i64, vp, i64, vp, vp]),
+        "fp4_dequantize": (i32, [vp, i64, vp, i64, vp, i64, i64, i32, i32, i32, vp, i32, vp, i64,
+                                 vp]),
+        "fp4_rotate_quantize": (i32, [vp, i64, i64, i64, vp, i32, i32, i32, i32, u32, vp, i64, vp,
+                                      i64, vp, vp, i64, vp]),
+        "fp4_channel_energy": (i32, [vp, i64, i64, i64, vp, vp]),
+        "fp4_build_permutation": (i32, [vp, i64, i32, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise Fp4Error(fn, status, lib().fp4_status_string(status).decode())
+
+
+def block_of(fmt: int) -> int:
+    return 32 if fmt == MXFP4 else 16
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _rows_ld(t) -> Tuple[int, int, int]:
+    assert t.dim() == 2 and t.stride(1) == 1, "expects a 2-D tensor with contiguous rows"
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _outputs(rows, cols, fmt, device, codes=None, scales=None):
+    import torch
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+    if scales is None:
+        scales = torch.empty((rows, cols // block_of(fmt)), dtype=torch.uint8, device=device)
+    return codes, scales
+
+
+def quantize(x, fmt: int = MXFP4, mode: int = PLAIN, floor_rule: bool = False,
+             tensor_scale=None, scale_given: Optional[bool] = None, codes=None, scales=None,
+             stream=None):
+    """Quantize a bf16 [rows, cols] CUDA tensor.
+
+    Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/block],
+    tensor_scale fp32 [1] for NVFP4 else None). For NVFP4, ``tensor_scale`` is
+    a 1-element fp32 device tensor: read as s_t when ``scale_given`` (the
+    default when it is passed), otherwise it receives the computed s_t
+    (allocated when None).
+    """
+    import torch
+    rows, cols, ld = _rows_ld(x)
+    codes, scales = _outputs(rows, cols, fmt, x.device, codes, scales)
+    flags = FLAG_SCALE_OCP_FLOOR if floor_rule else 0
+    ts = None
+    if fmt == NVFP4:
+        if scale_given is None:
+            scale_given = tensor_scale is not None
+        if scale_given:
+            flags |= FLAG_TENSOR_SCALE_GIVEN
+        ts = tensor_scale if tensor_scale is not None else torch.empty(
+            1, dtype=torch.float32, device=x.device)
+    st = lib().fp4_quantize(_ptr(x), rows, cols, ld, fmt, block_of(fmt), mode, flags,
+                            _ptr(codes), codes.stride(0), _ptr(scales), scales.stride(0),
+                            _ptr(ts), _stream(stream))
+    _check("fp4_quantize", st)
+    return codes, scales, ts
+
+
+def dequantize(codes, scales, fmt: int = MXFP4, mode: int = PLAIN, tensor_scale=None,
+               perm=None, hadamard: int = 0, out=None, stream=None):
+    """Decode to a bf16 [rows, cols] tensor (optionally undoing a rotation)."""
+    import torch
+    rows, half, ldc = _rows_ld(codes)
+    cols = half * 2
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
+    st = lib().fp4_dequantize(_ptr(codes), ldc, _ptr(scales), scales.stride(0),
+                              _ptr(tensor_scale), rows, cols, fmt, block_of(fmt), mode,
+                              _ptr(perm), hadamard, _ptr(out), out.stride(0), _stream(stream))
+    _check("fp4_dequantize", st)
+    return out
+
+
+def rotate_quantize(x, perm=None, hadamard: int = 32, floor_rule: bool = False,
+                    want_rotated: bool = False, codes=None, scales=None, rotated=None,
+                    stream=None):
+    """Permutation + block Hadamard fused with MXFP4 quantize + pack.
+
+    Returns (codes, scales, rotated fp32 [rows, cols] or None).
+    """
+    import torch
+    rows, cols, ld = _rows_ld(x)
+    codes, scales = _outputs(rows, cols, MXFP4, x.device, codes, scales)
+    if want_rotated and rotated is None:
+        rotated = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+    flags = FLAG_SCALE_OCP_FLOOR if floor_rule else 0
+    st = lib().fp4_rotate_quantize(_ptr(x), rows, cols, ld, _ptr(perm), hadamard, MXFP4, 32,
+                                   PLAIN, flags, _ptr(codes), codes.stride(0), _ptr(scales),
+                                   scales.stride(0), None, _ptr(rotated),
+                                   rotated.stride(0) if rotated is not None else 0,
+                                   _stream(stream))
+    _check("fp4_rotate_quantize", st)
+    return codes, scales, rotated
+
+
+def channel_energy(x, out=None, stream=None):
+    """fp32 [cols]: sum over rows of x^2 per channel (fp64 accumulation)."""
+    import torch
+    rows, cols, ld = _rows_ld(x)
+    if out is None:
+        out = torch.empty(cols, dtype=torch.float32, device=x.device)
+    st = lib().fp4_channel_energy(_ptr(x), rows, cols, ld, _ptr(out), _stream(stream))
+    _check("fp4_channel_energy", st)
+    return out
+
+
+def build_permutation(energy, block: int = 32):
+    """int32 [cols] host tensor: magnitude-balancing permutation (host code)."""
+    import torch
+    e = energy.detach().to("cpu", torch.float32).contiguous()
+    perm = torch.empty(e.numel(), dtype=torch.int32)
+    st = lib().fp4_build_permutation(_ptr(e), e.numel(), block, _ptr(perm))
+    _check("fp4_build_permutation", st)
+    return perm

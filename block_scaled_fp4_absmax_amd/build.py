@@ -1,0 +1,52 @@
+"""Build libfp4.so (the HIP kernels and the C ABI) in-tree for gfx950."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libfp4.so")
+SOURCES = ["quant.hip", "rotate.hip", "api.cpp", "perm.cpp"]
+HEADERS = ["fp4_device.hpp", "launch.hpp"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # exact IEEE fp32 arithmetic as written: no contraction, no fast-math
+    "-ffp-contract=off", "-fno-fast-math",
+    # no packed-fp32 VALU instructions in generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result",
+]
+
+
+def build(extra_flags=(), out=LIB, verbose=False) -> str:
+    """Compile every HIP/C++ source into ``out`` (always recompiles)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-o", tmp]
+    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(ln for ln in res.stderr.splitlines()
+                    if "packed-fp32-ops" not in ln and ln.strip())
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + err)
+    if verbose and err:
+        print(err, file=sys.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+def is_stale(out=LIB) -> bool:
+    if not os.path.exists(out):
+        return True
+    t = os.path.getmtime(out)
+    srcs = [os.path.join(CSRC, s) for s in SOURCES + HEADERS]
+    srcs.append(os.path.join(ROOT, "include", "fp4.h"))
+    return any(os.path.getmtime(s) > t for s in srcs)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

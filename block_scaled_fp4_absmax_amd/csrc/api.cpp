@@ -1,0 +1,149 @@
+// api.cpp -- C ABI of libfp4.so: argument checks, then kernel launches on the
+// caller's stream. Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include "../../include/fp4.h"
+#include "launch.hpp"
+
+using fp4::Shape;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int block_of(int format) { return format == FP4_MXFP4 ? 32 : 16; }
+
+// Checks shared by the quantizing entry points.
+int check_quant_args(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int format,
+                     int block, int mode, uint32_t flags, const void* codes, int64_t ld_codes,
+                     const void* scales, int64_t ld_scales, const float* tensor_scale) {
+  if (format != FP4_MXFP4 && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
+  if (block != block_of(format)) return FP4_ERR_UNSUPPORTED;
+  if (mode != FP4_PLAIN && mode != FP4_RAZER) return FP4_ERR_UNSUPPORTED;
+  if (mode == FP4_RAZER && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;  // E8M0 has no sign bit
+  if (flags & ~(FP4_FLAG_TENSOR_SCALE_GIVEN | FP4_FLAG_SCALE_OCP_FLOOR)) return FP4_ERR_UNSUPPORTED;
+  if ((flags & FP4_FLAG_TENSOR_SCALE_GIVEN) && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
+  if ((flags & FP4_FLAG_SCALE_OCP_FLOOR) && format != FP4_MXFP4) return FP4_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0 || cols % block != 0) return FP4_ERR_SHAPE;
+  if (ld_x < cols || ld_codes < cols / 2 || ld_scales < cols / block) return FP4_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && rows * cols / 8 >= (int64_t)1 << 31) return FP4_ERR_UNSUPPORTED;
+  if (format == FP4_NVFP4 && !tensor_scale) return FP4_ERR_NULL;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (!x || !codes || !scales) return FP4_ERR_NULL;
+  if (!aligned(x, 16) || ld_x % 8 != 0) return FP4_ERR_ALIGN;
+  if (!aligned(codes, 4) || ld_codes % 4 != 0) return FP4_ERR_ALIGN;
+  if (format == FP4_NVFP4 && !aligned(tensor_scale, 4)) return FP4_ERR_ALIGN;
+  return FP4_OK;
+}
+
+int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4_version(void) { return FP4_VERSION; }
+
+const char* fp4_status_string(int status) {
+  switch (status) {
+    case FP4_OK: return "ok";
+    case FP4_ERR_NULL: return "a required pointer is NULL";
+    case FP4_ERR_SHAPE: return "invalid shape or row stride";
+    case FP4_ERR_ALIGN: return "pointer or row stride not aligned";
+    case FP4_ERR_UNSUPPORTED: return "unsupported format, mode, flag, block or size";
+    case FP4_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, int format,
+                 int block, int mode, uint32_t flags, void* codes, int64_t ld_codes,
+                 void* scales, int64_t ld_scales, float* tensor_scale, void* stream) {
+  int rc = check_quant_args(x_bf16, rows, cols, ld_x, format, block, mode, flags, codes, ld_codes,
+                            scales, ld_scales, tensor_scale);
+  if (rc != FP4_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Shape s{rows, cols, ld_x, ld_codes, ld_scales};
+  const bool empty = rows == 0 || cols == 0;
+  const bool need_scale = format == FP4_NVFP4 && !(flags & FP4_FLAG_TENSOR_SCALE_GIVEN);
+  if (empty && !need_scale) return FP4_OK;  // nothing to enqueue
+  (void)hipGetLastError();  // clear a stale error so the status below is this call's
+  if (format == FP4_MXFP4) {
+    if (!empty) fp4::launch_mx_quant(s, (flags & FP4_FLAG_SCALE_OCP_FLOOR) != 0, x_bf16, codes, scales, st);
+  } else {
+    if (need_scale) fp4::launch_nv_tensor_scale(s, x_bf16, tensor_scale, st);
+    if (!empty) fp4::launch_nv_quant(s, mode == FP4_RAZER, x_bf16, codes, scales, tensor_scale, st);
+  }
+  return launch_status();
+}
+
+int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int64_t ld_scales,
+                   const float* tensor_scale, int64_t rows, int64_t cols, int format, int block,
+                   int mode, const int32_t* perm, int hadamard, void* out_bf16, int64_t ld_out,
+                   void* stream) {
+  if (format != FP4_MXFP4 && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
+  if (block != block_of(format)) return FP4_ERR_UNSUPPORTED;
+  if (mode != FP4_PLAIN && mode != FP4_RAZER) return FP4_ERR_UNSUPPORTED;
+  if (mode == FP4_RAZER && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
+  if (hadamard != 0 && hadamard != 32) return FP4_ERR_UNSUPPORTED;
+  if ((hadamard || perm) && format != FP4_MXFP4) return FP4_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0 || cols % block != 0) return FP4_ERR_SHAPE;
+  if (ld_out < cols || ld_codes < cols / 2 || ld_scales < cols / block) return FP4_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && rows * cols / 8 >= (int64_t)1 << 31) return FP4_ERR_UNSUPPORTED;
+  if (perm && cols > fp4::kMaxPermCols) return FP4_ERR_UNSUPPORTED;
+  if (format == FP4_NVFP4 && !tensor_scale) return FP4_ERR_NULL;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (!codes || !scales || !out_bf16) return FP4_ERR_NULL;
+  if (!aligned(out_bf16, 16) || ld_out % 8 != 0) return FP4_ERR_ALIGN;
+  if (!aligned(codes, 4) || ld_codes % 4 != 0) return FP4_ERR_ALIGN;
+  if (format == FP4_NVFP4 && !aligned(tensor_scale, 4)) return FP4_ERR_ALIGN;
+  if (perm && !aligned(perm, 4)) return FP4_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Shape s{rows, cols, ld_out, ld_codes, ld_scales};
+  (void)hipGetLastError();
+  if (hadamard || perm)
+    fp4::launch_mx_dequant_unrotate(s, perm, hadamard, codes, scales, out_bf16, st);
+  else
+    fp4::launch_dequant(s, format, mode == FP4_RAZER, codes, scales, tensor_scale, out_bf16, st);
+  return launch_status();
+}
+
+int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                        const int32_t* perm, int hadamard, int format, int block, int mode,
+                        uint32_t flags, void* codes, int64_t ld_codes, void* scales,
+                        int64_t ld_scales, float* tensor_scale, float* rotated_out,
+                        int64_t ld_rot, void* stream) {
+  int rc = check_quant_args(x_bf16, rows, cols, ld_x, format, block, mode, flags, codes, ld_codes,
+                            scales, ld_scales, tensor_scale);
+  if (rc != FP4_OK) return rc;
+  if (format != FP4_MXFP4) return FP4_ERR_UNSUPPORTED;
+  if (hadamard != 0 && hadamard != 32) return FP4_ERR_UNSUPPORTED;
+  if (perm && cols > fp4::kMaxPermCols) return FP4_ERR_UNSUPPORTED;
+  if (rotated_out && ld_rot < cols) return FP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (perm && !aligned(perm, 4)) return FP4_ERR_ALIGN;
+  if (rotated_out && (!aligned(rotated_out, 16) || ld_rot % 4 != 0)) return FP4_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Shape s{rows, cols, ld_x, ld_codes, ld_scales};
+  (void)hipGetLastError();
+  fp4::launch_mx_rotate_quant(s, perm, hadamard, (flags & FP4_FLAG_SCALE_OCP_FLOOR) != 0, x_bf16,
+                              codes, scales, rotated_out, ld_rot, st);
+  return launch_status();
+}
+
+int fp4_channel_energy(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                       float* energy, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0 || ld_x < cols) return FP4_ERR_SHAPE;
+  if (cols == 0) return FP4_OK;
+  if (!x_bf16 || !energy) return FP4_ERR_NULL;
+  if (!aligned(x_bf16, 16) || ld_x % 8 != 0 || !aligned(energy, 4)) return FP4_ERR_ALIGN;
+  if (cols / 32 >= (int64_t)1 << 31) return FP4_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  fp4::launch_channel_energy(rows, cols, ld_x, x_bf16, energy, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+}  // extern "C"

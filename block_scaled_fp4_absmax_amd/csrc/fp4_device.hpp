@@ -1,0 +1,142 @@
+// fp4_device.hpp -- gfx950 device helpers for block-scaled FP4 kernels.
+//
+// Element code: FP4 E2M1, sign << 3 | magnitude index, magnitudes
+// {0, .5, 1, 1.5, 2, 3, 4, 6} ("RaZeR: Pushing the Limits of NVFP4 Quantization
+// with Redundant Zero Remapping", technical summary sec. 1). Rounding to E2M1
+// uses gfx950's v_cvt_scalef32_pk_fp4_{bf16,f32}: it divides by the E8M0 scale
+// held in the exponent field of its fp32 scale operand, rounds to nearest with
+// ties to the even code, saturates at 6 and keeps the sign of zero.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4 {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;  // work-group size of the streaming kernels
+
+// Bit casts take a scalar by value: clang's __builtin_bit_cast applied
+// directly to an ext-vector element (v.y) reads element 0 instead.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+__device__ __forceinline__ u16x2_t as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2_t, v); }
+
+// ---- cross-lane ---------------------------------------------------------
+// quad_perm DPP controls: [1,0,3,2] swaps lane pairs, [2,3,0,1] swaps halves
+// of each group of four lanes.
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float dpp_xor1f(float v) {
+  return __uint_as_float(dpp_xor1(__float_as_uint(v)));
+}
+__device__ __forceinline__ float dpp_xor2f(float v) {
+  return __uint_as_float(dpp_xor2(__float_as_uint(v)));
+}
+
+// ---- bf16 ---------------------------------------------------------------
+// Largest |x| of eight bf16 held in four dwords, as a 16-bit pattern (bits
+// order like magnitudes for non-negative values; NaN > Inf > finite).
+__device__ __forceinline__ uint32_t absmax8_bf16(u32x4_t d) {
+  const u16x2_t m = {0x7FFF, 0x7FFF};
+  u16x2_t a = as_u16x2(d.x) & m;
+  u16x2_t b = as_u16x2(d.y) & m;
+  u16x2_t c = as_u16x2(d.z) & m;
+  u16x2_t e = as_u16x2(d.w) & m;
+  u16x2_t r = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                        __builtin_elementwise_max(c, e));
+  return r.x > r.y ? r.x : r.y;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  float2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));  // RNE
+}
+
+// ---- E8M0 shared exponent (MXFP4) -----------------------------------------
+// From the fp32 bit pattern m of a block's largest magnitude. Default: the
+// smallest e in [-127, 127] with amax <= 6 * 2^e. For normal amax =
+// (1 + f) * 2^(E-127), 6 * 2^e = 1.5 * 2^(e+2), so e = E - 129 when f <= 0.5
+// and E - 128 otherwise; byte = e + 127, clamped to 0 for tiny amax.
+// kFloor: e = floor(log2 amax) - 2 = E - 129. Inf/NaN -> 0xFF.
+template <bool kFloor>
+__device__ __forceinline__ uint32_t e8m0_byte(uint32_t m) {
+  if (m >= 0x7F800000u) return 0xFFu;
+  int E = (int)(m >> 23);
+  int b = kFloor ? E - 2 : E - 2 + ((m & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+  return (uint32_t)(b < 0 ? 0 : b);
+}
+
+__device__ __forceinline__ float e8m0_operand(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// Eight values (four bf16 pairs) -> eight E2M1 codes in one dword, element k
+// in nibble k.
+__device__ __forceinline__ uint32_t cvt8_bf16(u32x4_t d, float scale) {
+  uint32_t o = 0;
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, as_bf16x2(d.x), scale, 0);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, as_bf16x2(d.y), scale, 1);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, as_bf16x2(d.z), scale, 2);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, as_bf16x2(d.w), scale, 3);
+  return o;
+}
+
+__device__ __forceinline__ uint32_t cvt8_f32(const float* y, float scale) {
+  uint32_t o = 0;
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, y[0], y[1], scale, 0);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, y[2], y[3], scale, 1);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, y[4], y[5], scale, 2);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, y[6], y[7], scale, 3);
+  return o;
+}
+
+// ---- E4M3 block scale (NVFP4) ---------------------------------------------
+// OCP E4M3 "fn": bias 7, subnormals m * 2^-9, largest finite 448, 0x7F NaN.
+// Nearest code to s >= 0 with ties to the even code, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  if (!(s <= 448.0f)) return 0x7Eu;
+  if (s < 0x1p-6f) return (uint32_t)__builtin_rintf(s * 512.0f);  // exact scale, RNE
+  uint32_t u = __float_as_uint(s);
+  u += 0x7FFFFu + ((u >> 20) & 1u);  // round the 20 dropped mantissa bits, ties even
+  return (u >> 20) - (120u << 3);    // rebias exponent 127 -> 7
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  uint32_t mag = c & 0x7Fu;
+  float v = mag >= 8u ? __uint_as_float((((mag >> 3) + 120u) << 23) | ((mag & 7u) << 20))
+                      : (float)mag * 0x1p-9f;
+  if (mag == 0x7Fu) v = __builtin_nanf("");
+  return (c & 0x80u) ? -v : v;
+}
+
+// ---- RaZeR gain ---------------------------------------------------------
+// Squared-error gain of replacing an element's standard code by the special
+// value 5 (same sign): with d = |y| - 5, the standard neighbour is 4 or 6 and
+// (|y| - std)^2 - d^2 = 1 - 2|d| on |d| < 0.5, zero outside. In [4, 8) fp32
+// values are multiples of 2^-21, so the gain in units of 2^-21 is the integer
+// 2^21 - 2 |bits(|y|) - bits(5)|, clamped at 0; bits below 4 or from 8 up lie
+// more than 2^20 away from bits(5).
+__device__ __forceinline__ int32_t razer_gain(float y) {
+  uint32_t a = __float_as_uint(y) & 0x7FFFFFFFu;
+  uint32_t d = a > 0x40A00000u ? a - 0x40A00000u : 0x40A00000u - a;
+  d = d < 0x100000u ? d : 0x100000u;
+  return (int32_t)(0x200000u - 2u * d);
+}
+
+// Code dword with every nibble whose magnitude is zero cleared to 0x0.
+__device__ __forceinline__ uint32_t canonical_zero(uint32_t w) {
+  uint32_t nz = ((w & 0x77777777u) + 0x77777777u) & 0x88888888u;  // bit 3 set iff |code| != 0
+  return w & (nz | 0x77777777u);
+}
+
+}  // namespace fp4

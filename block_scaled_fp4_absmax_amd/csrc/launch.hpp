@@ -1,0 +1,37 @@
+// launch.hpp -- internal interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4 {
+
+// Upper bound on work-groups of the grid-stride streaming kernels.
+constexpr int kMaxGrid = 8192;
+// Largest row length that the permuting kernels stage in LDS (row + indices,
+// 4 bytes per column).
+constexpr int64_t kMaxPermCols = 16384;
+
+struct Shape {
+  int64_t rows, cols;
+  int64_t ld_x;  // bf16 input (or output, for dequantize) row stride, elements
+  int64_t ld_c;  // code row stride, bytes
+  int64_t ld_s;  // scale row stride, bytes
+};
+
+void launch_mx_quant(const Shape& s, bool floor_rule, const void* x, void* codes, void* scales,
+                     hipStream_t st);
+void launch_nv_tensor_scale(const Shape& s, const void* x, float* ts, hipStream_t st);
+void launch_nv_quant(const Shape& s, bool razer, const void* x, void* codes, void* scales,
+                     const float* ts, hipStream_t st);
+void launch_dequant(const Shape& s, int format, bool razer, const void* codes, const void* scales,
+                    const float* ts, void* out, hipStream_t st);
+void launch_mx_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, bool floor_rule,
+                            const void* x, void* codes, void* scales, float* rot, int64_t ld_rot,
+                            hipStream_t st);
+void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard,
+                                const void* codes, const void* scales, void* out, hipStream_t st);
+void launch_channel_energy(int64_t rows, int64_t cols, int64_t ld_x, const void* x, float* energy,
+                           hipStream_t st);
+
+}  // namespace fp4

@@ -1,0 +1,355 @@
+// quant.hip -- MXFP4 / NVFP4 (+RaZeR) quantize + pack, tensor amax, dequantize.
+//
+// Work decomposition: one lane owns one 16-byte chunk of eight consecutive
+// bf16 (a coalesced dwordx4 load), so four neighbouring lanes hold one
+// 32-element MXFP4 block and two hold one 16-element NVFP4 block. Block-wide
+// reductions are one or two DPP quad_perm steps; no LDS is used. The chunk
+// index v walks the matrix row-major; grid-stride loops process kUnroll
+// chunks per lane per trip with all loads issued before any arithmetic.
+// Since cols is a multiple of the block, chunks of one block are always
+// processed by adjacent lanes in the same trip.
+#include "fp4_device.hpp"
+#include "launch.hpp"
+
+namespace fp4 {
+
+constexpr int kUnroll = 4;
+
+// Address arithmetic for chunk v. kFlat: rows are contiguous in every array,
+// so the matrix is a single row of rows * cols elements.
+struct Geom {
+  uint32_t n;    // number of chunks = rows * cols / 8
+  uint32_t cpr;  // chunks per row
+  int64_t ld_x, ld_c, ld_s;
+};
+
+template <bool kFlat, int kBlock>
+__device__ __forceinline__ void locate(const Geom& g, uint32_t v, int64_t& xo, int64_t& co,
+                                       int64_t& so) {
+  if (kFlat) {
+    xo = 8 * (int64_t)v;
+    co = 4 * (int64_t)v;
+    so = (int64_t)(v / (kBlock / 8));
+  } else {
+    uint32_t r = v / g.cpr, c = v - r * g.cpr;
+    xo = r * g.ld_x + 8 * (int64_t)c;
+    co = r * g.ld_c + 4 * (int64_t)c;
+    so = r * g.ld_s + (int64_t)(c / (kBlock / 8));
+  }
+}
+
+// ---------------------------------------------------------------- MXFP4 ----
+template <bool kFlat, bool kFloor>
+__global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint16_t* __restrict__ x,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales, Geom g) {
+  const uint32_t stride = gridDim.x * kThreads;
+  const bool leader = (threadIdx.x & 3) == 0;
+  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < g.n; base += kUnroll * stride) {
+    u32x4_t d[kUnroll];
+    int64_t xo[kUnroll], co[kUnroll], so[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint32_t v = base + u * stride;
+      if (v < g.n) {
+        locate<kFlat, 32>(g, v, xo[u], co[u], so[u]);
+        d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo[u]));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint32_t v = base + u * stride;
+      if (v < g.n) {
+        uint32_t m = absmax8_bf16(d[u]);
+        m = max(m, dpp_xor1(m));
+        m = max(m, dpp_xor2(m));
+        uint32_t byte = e8m0_byte<kFloor>(m << 16);
+        uint32_t w = byte == 0xFFu ? 0u : cvt8_bf16(d[u], e8m0_operand(byte));
+        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + co[u]));
+        if (leader) scales[so[u]] = (uint8_t)byte;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- NVFP4 ----
+// Tensor amax as the fp32 bit pattern of max |x| (order-preserving for
+// non-negative floats), combined with one atomic max per work-group.
+template <bool kFlat>
+__global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint16_t* __restrict__ x,
+                                                           uint32_t* __restrict__ amax_bits,
+                                                           Geom g) {
+  __shared__ uint32_t red[kThreads / 64];
+  const uint32_t stride = gridDim.x * kThreads;
+  uint32_t m = 0;
+  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < g.n; base += kUnroll * stride) {
+    u32x4_t d[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint32_t v = base + u * stride;
+      d[u] = u32x4_t{0u, 0u, 0u, 0u};
+      if (v < g.n) {
+        int64_t xo, co, so;
+        locate<kFlat, 16>(g, v, xo, co, so);
+        d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) m = max(m, absmax8_bf16(d[u]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) r = max(r, red[i]);
+    if (r) atomicMax(amax_bits, r << 16);
+  }
+}
+
+__global__ void nv_clear_kernel(uint32_t* p) { *p = 0u; }
+
+// s_t = amax / 2688 (one fp32 division), or 1 for an all-zero tensor.
+__global__ void nv_tensor_scale_kernel(float* ts) {
+  float amax = __uint_as_float(*reinterpret_cast<uint32_t*>(ts));
+  *ts = amax == 0.0f ? 1.0f : amax / 2688.0f;
+}
+
+template <bool kFlat, bool kRazer>
+__global__ __launch_bounds__(kThreads) void nv_quant_kernel(const uint16_t* __restrict__ x,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales,
+                                                            const float* __restrict__ ts, Geom g) {
+  const uint32_t stride = gridDim.x * kThreads;
+  const bool leader = (threadIdx.x & 1) == 0;
+  const float s_t = *ts;
+  const float d6 = 6.0f * s_t;
+  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < g.n; base += kUnroll * stride) {
+    u32x4_t d[kUnroll];
+    int64_t xo[kUnroll], co[kUnroll], so[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint32_t v = base + u * stride;
+      if (v < g.n) {
+        locate<kFlat, 16>(g, v, xo[u], co[u], so[u]);
+        d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo[u]));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint32_t v = base + u * stride;
+      if (v >= g.n) continue;
+      uint32_t m = absmax8_bf16(d[u]);
+      m = max(m, dpp_xor1(m));
+      const float amax = __uint_as_float(m << 16);
+      const float s_raw = amax / d6;
+      const uint32_t sb = e4m3_encode(s_raw);
+      uint32_t w = 0, byte = 0;
+      if (sb != 0u) {
+        const float s_eff = e4m3_decode(sb) * s_t;
+        const float r = 1.0f / s_eff;
+        float y[8];
+        y[0] = bf16_lo(d[u].x) * r; y[1] = bf16_hi(d[u].x) * r;
+        y[2] = bf16_lo(d[u].y) * r; y[3] = bf16_hi(d[u].y) * r;
+        y[4] = bf16_lo(d[u].z) * r; y[5] = bf16_hi(d[u].z) * r;
+        y[6] = bf16_lo(d[u].w) * r; y[7] = bf16_hi(d[u].w) * r;
+        w = cvt8_f32(y, 1.0f);
+        byte = sb;
+        if (kRazer) {
+          // selector = [sum of gains of negative elements > that of positive ones]
+          int32_t g8[8];
+          int32_t dsum = 0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            g8[k] = razer_gain(y[k]);
+            dsum += (__float_as_uint(y[k]) >> 31) ? g8[k] : -g8[k];
+          }
+          dsum += (int32_t)dpp_xor1((uint32_t)dsum);
+          const uint32_t sel = dsum > 0 ? 1u : 0u;
+          uint32_t spm = 0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            spm |= (g8[k] > 0 && (__float_as_uint(y[k]) >> 31) == sel) ? (8u << (4 * k)) : 0u;
+          w = canonical_zero(w);
+          w = (w & ~((spm >> 3) * 0xFu)) | spm;
+          byte |= sel << 7;
+        }
+      }
+      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + co[u]));
+      if (leader) scales[so[u]] = (uint8_t)byte;
+    }
+  }
+}
+
+// ------------------------------------------------------------ dequantize ----
+template <bool kFlat>
+__global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                              const uint8_t* __restrict__ scales,
+                                                              uint16_t* __restrict__ out, Geom g) {
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < g.n; base += kUnroll * stride) {
+    uint32_t w[kUnroll], sb[kUnroll];
+    int64_t xo[kUnroll], co[kUnroll], so[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint32_t v = base + u * stride;
+      if (v < g.n) {
+        locate<kFlat, 32>(g, v, xo[u], co[u], so[u]);
+        w[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + co[u]));
+        sb[u] = scales[so[u]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint32_t v = base + u * stride;
+      if (v >= g.n) continue;
+      const float s = e8m0_operand(sb[u]);  // byte 0xFF -> NaN scale -> NaN outputs
+      u32x4_t o;
+      o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], s, 0));
+      o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], s, 1));
+      o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], s, 2));
+      o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], s, 3));
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + xo[u]));
+    }
+  }
+}
+
+template <bool kFlat, bool kRazer>
+__global__ __launch_bounds__(kThreads) void nv_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                              const uint8_t* __restrict__ scales,
+                                                              const float* __restrict__ ts,
+                                                              uint16_t* __restrict__ out, Geom g) {
+  const uint32_t stride = gridDim.x * kThreads;
+  const float s_t = *ts;
+  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < g.n; base += kUnroll * stride) {
+    uint32_t w[kUnroll], sb[kUnroll];
+    int64_t xo[kUnroll], co[kUnroll], so[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint32_t v = base + u * stride;
+      if (v < g.n) {
+        locate<kFlat, 16>(g, v, xo[u], co[u], so[u]);
+        w[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + co[u]));
+        sb[u] = scales[so[u]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint32_t v = base + u * stride;
+      if (v >= g.n) continue;
+      const uint32_t byte = sb[u];
+      const float s_eff = e4m3_decode(kRazer ? (byte & 0x7Fu) : byte) * s_t;
+      const float special = (byte & 0x80u) ? -5.0f : 5.0f;
+      float val[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float2_t p;
+        if (k == 0) p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 0);
+        if (k == 1) p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 1);
+        if (k == 2) p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 2);
+        if (k == 3) p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 3);
+        val[2 * k] = p.x;
+        val[2 * k + 1] = p.y;
+      }
+      if (kRazer) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (((w[u] >> (4 * k)) & 0xFu) == 8u) val[k] = special;
+      }
+      u32x4_t o;
+      o.x = pack_bf16x2(val[0] * s_eff, val[1] * s_eff);
+      o.y = pack_bf16x2(val[2] * s_eff, val[3] * s_eff);
+      o.z = pack_bf16x2(val[4] * s_eff, val[5] * s_eff);
+      o.w = pack_bf16x2(val[6] * s_eff, val[7] * s_eff);
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + xo[u]));
+    }
+  }
+}
+
+// --------------------------------------------------------------- launchers ----
+static inline int grid_for(uint32_t n) {
+  uint64_t per = (uint64_t)kThreads * kUnroll;
+  uint64_t gsz = (n + per - 1) / per;
+  if (gsz > (uint64_t)kMaxGrid) gsz = kMaxGrid;
+  return (int)(gsz ? gsz : 1);
+}
+
+static inline Geom make_geom(const Shape& s, int block) {
+  Geom g;
+  g.n = (uint32_t)(s.rows * s.cols / 8);
+  g.cpr = (uint32_t)(s.cols / 8);
+  g.ld_x = s.ld_x;
+  g.ld_c = s.ld_c;
+  g.ld_s = s.ld_s;
+  (void)block;
+  return g;
+}
+
+#define FP4_LAUNCH(kern, grid, stream, ...) \
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, __VA_ARGS__)
+
+void launch_mx_quant(const Shape& s, bool floor_rule, const void* x, void* codes, void* scales,
+                     hipStream_t st) {
+  Geom g = make_geom(s, 32);
+  const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / 32;
+  const int grid = grid_for(g.n);
+  auto xp = static_cast<const uint16_t*>(x);
+  auto cp = static_cast<uint8_t*>(codes);
+  auto sp = static_cast<uint8_t*>(scales);
+  if (flat && !floor_rule) FP4_LAUNCH((mx_quant_kernel<true, false>), grid, st, xp, cp, sp, g);
+  if (flat && floor_rule) FP4_LAUNCH((mx_quant_kernel<true, true>), grid, st, xp, cp, sp, g);
+  if (!flat && !floor_rule) FP4_LAUNCH((mx_quant_kernel<false, false>), grid, st, xp, cp, sp, g);
+  if (!flat && floor_rule) FP4_LAUNCH((mx_quant_kernel<false, true>), grid, st, xp, cp, sp, g);
+}
+
+void launch_nv_tensor_scale(const Shape& s, const void* x, float* ts, hipStream_t st) {
+  Geom g = make_geom(s, 16);
+  const bool flat = s.ld_x == s.cols;
+  auto xp = static_cast<const uint16_t*>(x);
+  auto bits = reinterpret_cast<uint32_t*>(ts);
+  hipLaunchKernelGGL(nv_clear_kernel, dim3(1), dim3(1), 0, st, bits);
+  if (g.n > 0) {
+    const int grid = grid_for(g.n);
+    if (flat) FP4_LAUNCH((nv_amax_kernel<true>), grid, st, xp, bits, g);
+    else FP4_LAUNCH((nv_amax_kernel<false>), grid, st, xp, bits, g);
+  }
+  hipLaunchKernelGGL(nv_tensor_scale_kernel, dim3(1), dim3(1), 0, st, ts);
+}
+
+void launch_nv_quant(const Shape& s, bool razer, const void* x, void* codes, void* scales,
+                     const float* ts, hipStream_t st) {
+  Geom g = make_geom(s, 16);
+  const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / 16;
+  const int grid = grid_for(g.n);
+  auto xp = static_cast<const uint16_t*>(x);
+  auto cp = static_cast<uint8_t*>(codes);
+  auto sp = static_cast<uint8_t*>(scales);
+  if (flat && razer) FP4_LAUNCH((nv_quant_kernel<true, true>), grid, st, xp, cp, sp, ts, g);
+  if (flat && !razer) FP4_LAUNCH((nv_quant_kernel<true, false>), grid, st, xp, cp, sp, ts, g);
+  if (!flat && razer) FP4_LAUNCH((nv_quant_kernel<false, true>), grid, st, xp, cp, sp, ts, g);
+  if (!flat && !razer) FP4_LAUNCH((nv_quant_kernel<false, false>), grid, st, xp, cp, sp, ts, g);
+}
+
+void launch_dequant(const Shape& s, int format, bool razer, const void* codes, const void* scales,
+                    const float* ts, void* out, hipStream_t st) {
+  const int block = format == 0 ? 32 : 16;
+  Geom g = make_geom(s, block);
+  // here ld_x is the output row stride
+  const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / block;
+  const int grid = grid_for(g.n);
+  auto cp = static_cast<const uint8_t*>(codes);
+  auto sp = static_cast<const uint8_t*>(scales);
+  auto op = static_cast<uint16_t*>(out);
+  if (format == 0) {
+    if (flat) FP4_LAUNCH((mx_dequant_kernel<true>), grid, st, cp, sp, op, g);
+    else FP4_LAUNCH((mx_dequant_kernel<false>), grid, st, cp, sp, op, g);
+  } else {
+    if (flat && razer) FP4_LAUNCH((nv_dequant_kernel<true, true>), grid, st, cp, sp, ts, op, g);
+    if (flat && !razer) FP4_LAUNCH((nv_dequant_kernel<true, false>), grid, st, cp, sp, ts, op, g);
+    if (!flat && razer) FP4_LAUNCH((nv_dequant_kernel<false, true>), grid, st, cp, sp, ts, op, g);
+    if (!flat && !razer) FP4_LAUNCH((nv_dequant_kernel<false, false>), grid, st, cp, sp, ts, op, g);
+  }
+}
+
+}  // namespace fp4

@@ -1,0 +1,201 @@
+/*
+ * fp4.h -- block-scaled 4-bit (MXFP4 / NVFP4) quantization on AMD Instinct
+ * MI355X (gfx950): C ABI of libfp4.so.
+ *
+ * Sources (web pages explaining the papers; cited by title and section):
+ *  [RaZeR] "RaZeR: Pushing the Limits of NVFP4 Quantization with Redundant Zero
+ *          Remapping", technical summary sec. 1 (FP4 E2M1 value set with both
+ *          zeros; E4M3 block scale that is always positive, so its sign bit is
+ *          free) and sec. 2.2 (the freed bit selects a special value, +5 or -5,
+ *          that replaces the redundant zero code; chosen per block by least
+ *          squared error).
+ *  [TORQ]  "TORQ: Two-Level Orthogonal Rotation for MXFP4 Quantization",
+ *          technical summary sec. 1 (32-element blocks sharing one exponent)
+ *          and sec. 2 (an inter-block transform that evens out block variances,
+ *          then a rotation inside each block; the scale maps the block maximum
+ *          onto the largest code).
+ *
+ * Conventions shared by every entry point
+ *  - Matrices are row-major. A block is `block` consecutive elements of one
+ *    row (32 for MXFP4, 16 for NVFP4). `ld_*` is the row stride in elements
+ *    of that array (bytes for the uint8 code and scale arrays).
+ *  - codes: uint8 [rows, ld_codes], element 2i of a row in the low nibble of
+ *    byte i and element 2i+1 in the high nibble. FP4 E2M1 code =
+ *    sign << 3 | magnitude index, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}.
+ *  - scales: uint8 [rows, ld_scales], one byte per block. MXFP4: E8M0 byte,
+ *    scale 2^(byte-127), 0xFF = NaN. NVFP4: E4M3 (OCP "fn") byte; in RaZeR
+ *    mode bit 7 holds the selector (0: code 0x8 means +5, 1: -5) and bits 0-6
+ *    the positive scale.
+ *  - tensor_scale (NVFP4 only): one fp32 in device memory; element scale of a
+ *    block = e4m3(scale byte) * tensor_scale.
+ *  - Ownership: every pointer except those marked "host" is device memory
+ *    owned by the caller. The library allocates nothing and keeps no handle
+ *    between calls. Work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream) and the call returns without waiting: outputs are valid
+ *    once the stream has reached this point.
+ *  - Errors: arguments are checked before anything is enqueued; on failure
+ *    nothing is enqueued and a negative fp4_status is returned. FP4_ERR_HIP
+ *    means a launch failed after the arguments were accepted.
+ *  - Rounding (readings where the pages are silent): nearest E2M1 value with
+ *    ties to the even code, saturating at 6; the sign of an element that
+ *    rounds to zero is kept (code 0x8) except in RaZeR mode, where zero is
+ *    always 0x0.
+ */
+#ifndef FP4_H
+#define FP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4_VERSION 1
+
+enum fp4_format { FP4_MXFP4 = 0, FP4_NVFP4 = 1 };
+enum fp4_mode { FP4_PLAIN = 0, FP4_RAZER = 1 };
+
+/* NVFP4: read tensor_scale as an input instead of computing it. */
+#define FP4_FLAG_TENSOR_SCALE_GIVEN 1u
+/* MXFP4: shared exponent floor(log2 amax) - 2 (elements above 6 * 2^e
+ * saturate) instead of the default smallest e with amax <= 6 * 2^e. */
+#define FP4_FLAG_SCALE_OCP_FLOOR 2u
+
+enum fp4_status {
+  FP4_OK = 0,
+  FP4_ERR_NULL = -1,        /* a required pointer is NULL */
+  FP4_ERR_SHAPE = -2,       /* negative size, cols % block != 0, ld too small */
+  FP4_ERR_ALIGN = -3,       /* pointer or row stride not aligned as stated */
+  FP4_ERR_UNSUPPORTED = -4, /* unknown enum/flag, bad combination, size limit */
+  FP4_ERR_HIP = -5          /* a kernel launch failed */
+};
+
+/* Library version (FP4_VERSION of the build). */
+int fp4_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* fp4_status_string(int status);
+
+/*
+ * fp4_quantize -- block absmax -> scale -> round to E2M1 -> pack.
+ *
+ * MXFP4 ([TORQ] sec. 1 and the S-step of sec. 2(b)): block 32; the E8M0
+ * exponent is the smallest e in [-127, 127] with amax <= 6 * 2^e (so the block
+ * maximum maps onto the top code 6 without clipping; amax = 0 gives e = -127),
+ * or floor(log2 amax) - 2 with FP4_FLAG_SCALE_OCP_FLOOR. Elements are
+ * x * 2^-e exactly. A block holding Inf or NaN gets scale byte 0xFF and codes 0.
+ *
+ * NVFP4 ([RaZeR] sec. 1): block 16. Each step is one fp32 operation rounded to
+ * nearest-even: s_t = amax_tensor / 2688 (2688 = 6 * 448; 1.0 if the tensor is
+ * all zero) unless FP4_FLAG_TENSOR_SCALE_GIVEN; s_b = E4M3 nearest to
+ * amax_block / (6 * s_t), saturating at 448 (a block whose s_b is 0 is stored
+ * as scale 0, codes 0); s_eff = e4m3(s_b) * s_t; y = x * (1 / s_eff).
+ * Non-finite NVFP4 inputs give unspecified codes.
+ *
+ * RaZeR mode ([RaZeR] sec. 2.2; NVFP4 only): per block, the code book is the
+ * fifteen values other than -0 plus one special value at code 0x8, +5 or -5;
+ * the block takes the one with the smaller sum of squared errors in y (equal:
+ * +5), an element takes the special code only when strictly closer to it.
+ *
+ *  x_bf16       device, bf16 [rows, ld_x]; 16-byte aligned, ld_x % 8 == 0
+ *  rows, cols   rows >= 0, cols >= 0, cols % block == 0; rows * cols / 8 < 2^31
+ *  format       FP4_MXFP4 or FP4_NVFP4
+ *  block        32 for MXFP4, 16 for NVFP4
+ *  mode         FP4_PLAIN, or FP4_RAZER with NVFP4
+ *  flags        FP4_FLAG_* bits valid for the format
+ *  codes        device, uint8 [rows, ld_codes]; 4-byte aligned, ld_codes % 4 == 0,
+ *               ld_codes >= cols / 2
+ *  scales       device, uint8 [rows, ld_scales], ld_scales >= cols / block
+ *  tensor_scale NVFP4: device fp32[1], written (or read with the flag);
+ *               MXFP4: ignored, may be NULL
+ *  stream       hipStream_t
+ * Returns FP4_OK or an fp4_status. With NVFP4 and a computed s_t, four
+ * kernels are enqueued (clear, tensor amax, s_t, quantize); otherwise one.
+ */
+int fp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, int format,
+                 int block, int mode, uint32_t flags, void* codes, int64_t ld_codes,
+                 void* scales, int64_t ld_scales, float* tensor_scale, void* stream);
+
+/*
+ * fp4_dequantize -- decode codes and scales back to bf16.
+ *
+ * MXFP4: bf16(value * 2^e) (exact unless it overflows to Inf; scale 0xFF
+ * gives NaN). NVFP4: bf16_rne(fp32(value * s_eff)); RaZeR mode decodes code
+ * 0x8 to the block's special value, the decoder rebuilding it from the scale
+ * byte's top bit ([RaZeR] sec. 2.3).
+ * Optional inverse rotation (MXFP4 only) so the result lies in the original
+ * basis: with hadamard == 32 the block Hadamard is applied again (it is its own
+ * inverse), then with perm != NULL element j is written to column perm[j].
+ * The inverse-rotated values are computed in fp32 and rounded once to bf16.
+ *
+ *  codes, scales, tensor_scale  as produced by fp4_quantize / fp4_rotate_quantize
+ *  rows, cols, format, block, mode  as for fp4_quantize
+ *  perm         NULL or device int32[cols], a permutation of 0..cols-1;
+ *               requires cols <= 16384
+ *  hadamard     0 or 32 (MXFP4)
+ *  out_bf16     device, bf16 [rows, ld_out]; 16-byte aligned, ld_out % 8 == 0
+ */
+int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int64_t ld_scales,
+                   const float* tensor_scale, int64_t rows, int64_t cols, int format,
+                   int block, int mode, const int32_t* perm, int hadamard, void* out_bf16,
+                   int64_t ld_out, void* stream);
+
+/*
+ * fp4_rotate_quantize -- two-level rotation fused with MXFP4 quantize + pack
+ * ([TORQ] sec. 2(a) and 2(b)).
+ *
+ * Level 1: channel permutation x'[r, j] = x[r, perm[j]] (perm computed offline,
+ * e.g. by fp4_build_permutation from fp4_channel_energy, so that every block
+ * receives a balanced share of channel energy). Level 2: the orthonormal
+ * Sylvester-Hadamard matrix H[i][j] = (-1)^popcount(i & j) / sqrt(32) inside
+ * each 32-block, y = H x' in fp32. Then MXFP4 quantization of y exactly as in
+ * fp4_quantize (the shared exponent comes from the fp32 amax of y).
+ *
+ *  perm         NULL (identity) or device int32[cols], a permutation of
+ *               0..cols-1 (entries are clamped to cols-1); requires
+ *               cols <= 16384
+ *  hadamard     32 or 0 (none)
+ *  format       FP4_MXFP4 (NVFP4 returns FP4_ERR_UNSUPPORTED)
+ *  rotated_out  NULL, or device fp32 [rows, ld_rot] receiving y; 16-byte
+ *               aligned, ld_rot % 4 == 0 (for parity checks)
+ *  others       as for fp4_quantize
+ */
+int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                        const int32_t* perm, int hadamard, int format, int block, int mode,
+                        uint32_t flags, void* codes, int64_t ld_codes, void* scales,
+                        int64_t ld_scales, float* tensor_scale, float* rotated_out,
+                        int64_t ld_rot, void* stream);
+
+/*
+ * fp4_channel_energy -- calibration statistic for the permutation: energy[c] =
+ * sum over rows of x[r, c]^2, accumulated in fp64 in a fixed order (the result
+ * is deterministic) and rounded to fp32. It is the diagonal of the activation
+ * second-moment matrix whose diagonal blocks hold the block variances that
+ * [TORQ] sec. 2(a) equalises.
+ *
+ *  x_bf16   device, bf16 [rows, ld_x]; 16-byte aligned, ld_x % 8 == 0
+ *  cols     cols % 32 == 0
+ *  energy   device fp32[cols], 4-byte aligned (overwritten)
+ */
+int fp4_channel_energy(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                       float* energy, void* stream);
+
+/*
+ * fp4_build_permutation -- host-side, synchronous. Magnitude-balancing
+ * permutation from channel energies (reading of [TORQ] sec. 2(a) as a
+ * permutation): channels are taken in order of decreasing energy (equal
+ * energies: lower index first); each goes to the next free slot of the block
+ * whose accumulated energy (summed in fp64) is smallest among blocks that still
+ * have a free slot (equal loads: lower block index).
+ *
+ *  energy_host  host fp32[cols]
+ *  cols         cols > 0, cols % block == 0
+ *  block        32 (MXFP4) or 16 (NVFP4)
+ *  perm_host    host int32[cols]; perm[j] = source channel of column j
+ */
+int fp4_build_permutation(const float* energy_host, int64_t cols, int block, int32_t* perm_host);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4_H */

@@ -1,0 +1,122 @@
+"""C ABI checks that need no GPU: exports, argument validation, host code."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_scaled_fp4_absmax_amd as fp4
+from block_scaled_fp4_absmax_amd import build as hip_build
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "fp4.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if hip_build.is_stale():
+        hip_build.build()
+    return fp4.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("fp4_quantize", "fp4_dequantize", "fp4_rotate_quantize", "fp4_channel_energy",
+              "fp4_build_permutation", "fp4_status_string", "fp4_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert L.fp4_version() == 1
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4, -5, -99):
+        assert L.fp4_status_string(st)
+
+
+# fp4_quantize(x, rows, cols, ld_x, format, block, mode, flags, codes, ld_codes,
+#              scales, ld_scales, tensor_scale, stream)
+FAKE = 0x10000  # never dereferenced: every case below fails before any launch
+TS = FAKE + 0x100
+
+
+@pytest.mark.parametrize("args,want", [
+    ((FAKE, 4, 64, 64, 2, 32, 0, 0, FAKE, 32, FAKE, 2, None), -4),      # bad format
+    ((FAKE, 4, 64, 64, 0, 16, 0, 0, FAKE, 32, FAKE, 4, None), -4),      # MXFP4 needs block 32
+    ((FAKE, 4, 64, 64, 1, 32, 0, 0, FAKE, 32, FAKE, 2, TS), -4),        # NVFP4 needs block 16
+    ((FAKE, 4, 64, 64, 0, 32, 1, 0, FAKE, 32, FAKE, 2, None), -4),      # RaZeR needs NVFP4
+    ((FAKE, 4, 64, 64, 0, 32, 0, 8, FAKE, 32, FAKE, 2, None), -4),      # unknown flag
+    ((FAKE, 4, 64, 64, 0, 32, 0, 1, FAKE, 32, FAKE, 2, None), -4),      # scale-given on MXFP4
+    ((FAKE, 4, 64, 64, 1, 16, 0, 2, FAKE, 32, FAKE, 4, TS), -4),        # floor rule on NVFP4
+    ((FAKE, -1, 64, 64, 0, 32, 0, 0, FAKE, 32, FAKE, 2, None), -2),     # negative rows
+    ((FAKE, 4, 48, 48, 0, 32, 0, 0, FAKE, 24, FAKE, 2, None), -2),      # cols % block
+    ((FAKE, 4, 64, 32, 0, 32, 0, 0, FAKE, 32, FAKE, 2, None), -2),      # ld_x < cols
+    ((FAKE, 4, 64, 64, 0, 32, 0, 0, FAKE, 16, FAKE, 2, None), -2),      # ld_codes < cols/2
+    ((FAKE, 4, 64, 64, 0, 32, 0, 0, FAKE, 32, FAKE, 1, None), -2),      # ld_scales < cols/32
+    ((None, 4, 64, 64, 0, 32, 0, 0, FAKE, 32, FAKE, 2, None), -1),      # null input
+    ((FAKE, 4, 64, 64, 1, 16, 0, 0, FAKE, 32, FAKE, 4, None), -1),      # NVFP4 needs s_t slot
+    ((FAKE + 2, 4, 64, 64, 0, 32, 0, 0, FAKE, 32, FAKE, 2, None), -3),  # misaligned input
+    ((FAKE, 4, 64, 68, 0, 32, 0, 0, FAKE, 32, FAKE, 2, None), -3),      # ld_x % 8
+    ((FAKE, 4, 64, 64, 0, 32, 0, 0, FAKE + 1, 32, FAKE, 2, None), -3),  # misaligned codes
+    ((FAKE, 1 << 20, 1 << 14, 1 << 14, 0, 32, 0, 0, FAKE, 1 << 13, FAKE, 512, None), -4),  # too big
+])
+def test_quantize_validation(L, args, want):
+    assert L.fp4_quantize(*args, None) == want
+
+
+def test_empty_mxfp4_is_a_no_op(L):
+    # rows == 0: nothing to do and nothing enqueued, even with NULL buffers
+    assert L.fp4_quantize(None, 0, 64, 64, 0, 32, 0, 0, None, 32, None, 2, None, None) == 0
+
+
+def test_rotate_and_dequant_validation(L):
+    # rotate_quantize(x, rows, cols, ld, perm, had, fmt, block, mode, flags, codes, ldc,
+    #                 scales, lds, ts, rot, ld_rot, stream)
+    R = L.fp4_rotate_quantize
+    assert R(FAKE, 4, 64, 64, None, 16, 0, 32, 0, 0, FAKE, 32, FAKE, 2, None, None, 0, None) == -4
+    assert R(FAKE, 4, 64, 64, None, 32, 1, 16, 0, 0, FAKE, 32, FAKE, 4, TS, None, 0, None) == -4
+    assert R(FAKE, 4, 32768, 32768, FAKE, 32, 0, 32, 0, 0, FAKE, 16384, FAKE, 1024, None, None,
+             0, None) == -4  # permutation wider than the LDS row buffer
+    assert R(FAKE, 4, 64, 64, None, 32, 0, 32, 0, 0, FAKE, 32, FAKE, 2, None, FAKE, 32,
+             None) == -2
+    assert R(FAKE, 4, 64, 64, None, 32, 0, 32, 0, 0, FAKE, 32, FAKE, 2, None, FAKE + 4, 64,
+             None) == -3
+    # dequantize(codes, ldc, scales, lds, ts, rows, cols, fmt, block, mode, perm, had, out, ldo, s)
+    D = L.fp4_dequantize
+    assert D(FAKE, 32, FAKE, 4, TS, 4, 64, 1, 16, 0, None, 32, FAKE, 64, None) == -4
+    assert D(FAKE, 32, FAKE, 2, None, 4, 64, 0, 32, 1, None, 0, FAKE, 64, None) == -4
+    assert D(FAKE, 32, FAKE, 4, None, 4, 64, 1, 16, 0, None, 0, FAKE, 64, None) == -1
+    assert D(FAKE, 32, FAKE, 2, None, 4, 64, 0, 32, 0, None, 0, FAKE + 8, 64, None) == -3
+    assert D(FAKE, 32, FAKE, 2, None, 0, 64, 0, 32, 0, None, 0, None, 64, None) == 0
+    E = L.fp4_channel_energy
+    assert E(FAKE, 4, 48, 48, FAKE, None) == -2
+    assert E(None, 4, 64, 64, FAKE, None) == -1
+
+
+def test_binding_raises_without_gpu_work():
+    with pytest.raises(fp4.Fp4Error):
+        fp4._check("fp4_quantize", -2)
+
+
+def test_host_permutation_matches_oracle(L, orc):
+    rng = np.random.default_rng(3)
+    for cols, block in ((64, 32), (8192, 32), (1024, 16), (28672, 32)):
+        e = np.exp(3 * rng.standard_normal(cols)).astype(np.float32)
+        e[rng.integers(0, cols, cols // 8)] = e[0]  # plenty of exact ties
+        want = orc.build_perm(e, block)
+        got = np.zeros(cols, np.int32)
+        assert L.fp4_build_permutation(e.ctypes.data, cols, block, got.ctypes.data) == 0
+        assert np.array_equal(got, want)
+    bad = np.zeros(64, np.int32)
+    assert L.fp4_build_permutation(e.ctypes.data, 48, 32, bad.ctypes.data) == -2
+    assert L.fp4_build_permutation(None, 64, 32, bad.ctypes.data) == -1

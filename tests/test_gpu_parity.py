@@ -1,0 +1,338 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Without rotation codes, scales, tensor scales and dequantized bf16 must match
+bit for bit. With rotation the tolerances in parity_util apply.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import block_scaled_fp4_absmax_amd as fp4
+from block_scaled_fp4_absmax_amd import inputs
+from parity_util import bf16_bits, check_rotated, note, same_bf16, to_dev, unpack
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fp4.lib()
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def np_u8(t):
+    return t.cpu().numpy()
+
+
+# -------------------------------------------------------------------- MXFP4 --
+def test_mx_c1_bitexact(orc):
+    note("case: MXFP4 256x4096 quantize + dequantize (seed 0)")
+    x = inputs.gen_c1()
+    c, s, _ = fp4.quantize(to_dev(x), fp4.MXFP4)
+    d = fp4.dequantize(c, s, fp4.MXFP4)
+    sync()
+    oc, os_ = orc.mx_quantize(x)
+    assert np.array_equal(np_u8(s), os_)
+    assert np.array_equal(np_u8(c), oc)
+    assert np.array_equal(bf16_bits(d), orc.dequantize(oc, os_, 0))
+
+
+def exhaustive_mx_tensor():
+    """Blocks pairing every finite bf16 pattern with an anchor for every
+    reachable E8M0 exponent (anchor 6*2^e, or the largest bf16)."""
+    pats = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        f = (pats << 16).view(np.float32)
+    mag = np.abs(f.astype(np.float64))
+    finite = np.isfinite(f)
+    blocks = []
+    for e in range(-127, 127):
+        top = 6.0 * 2.0 ** e
+        anchor_f = np.float32(min(top, 3.3895313892515355e38))
+        anchor = np.uint16(anchor_f.view(np.uint32) >> 16)
+        a = float((np.uint32(anchor) << 16).view(np.float32))
+        members = pats[finite & (mag <= a)].astype(np.uint16)
+        nblk = -(-members.size // 31)
+        body = np.zeros(nblk * 31, np.uint16)
+        body[:members.size] = members
+        body = body.reshape(nblk, 31)
+        sign = np.where(np.arange(nblk) % 2 == 0, 0, 0x8000).astype(np.uint16)[:, None]
+        blocks.append(np.concatenate([anchor | sign, body], axis=1))
+    allb = np.concatenate(blocks)
+    pad = (-allb.shape[0]) % 32
+    allb = np.concatenate([allb, np.zeros((pad, 32), np.uint16)])
+    return allb.reshape(-1, 1024)
+
+
+@pytest.mark.parametrize("floor_rule", [False, True])
+def test_mx_exhaustive_bf16_patterns(orc, floor_rule):
+    x = exhaustive_mx_tensor()
+    # add blocks holding Inf / NaN
+    x[0, 3] = 0x7F80
+    x[1, 40] = 0xFFC1
+    note(f"case: MXFP4 exhaustive bf16 x exponent sweep {x.shape} floor={floor_rule}")
+    c, s, _ = fp4.quantize(to_dev(x), fp4.MXFP4, floor_rule=floor_rule)
+    sync()
+    oc, os_ = orc.mx_quantize(x, floor_rule)
+    assert np.array_equal(np_u8(s), os_)
+    assert np.array_equal(np_u8(c), oc)
+
+
+@pytest.mark.parametrize("fmt,razer", [(0, False), (1, False), (1, True)])
+def test_dequant_every_code_and_scale(orc, fmt, razer):
+    note(f"case: dequantize every code x scale byte fmt={fmt} razer={razer}")
+    blk = 32 if fmt == 0 else 16
+    rows, cols = 256, 512
+    codes = np.tile(np.arange(256, dtype=np.uint8), (rows, 1))
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], cols // blk, axis=1)
+    ts = np.float32(0.37109375) if fmt == 1 else np.float32(1.0)
+    tst = torch.tensor([ts], device="cuda")
+    d = fp4.dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), fmt,
+                       fp4.RAZER if razer else fp4.PLAIN, tst if fmt == 1 else None)
+    sync()
+    want = orc.dequantize(codes, scales, fmt, razer, float(ts))
+    assert same_bf16(bf16_bits(d), want)
+
+
+# -------------------------------------------------------------------- NVFP4 --
+@pytest.mark.parametrize("razer", [True, False])
+def test_nv_c2_bitexact(orc, razer):
+    note(f"case: NVFP4 4096x4096 razer={razer} (seed 1)")
+    x = inputs.gen_c2()
+    mode = fp4.RAZER if razer else fp4.PLAIN
+    c, s, ts = fp4.quantize(to_dev(x), fp4.NVFP4, mode)
+    d = fp4.dequantize(c, s, fp4.NVFP4, mode, ts)
+    sync()
+    oc, os_, ots = orc.nv_quantize(x, razer)
+    assert np.float32(ts.cpu().numpy()[0]).view(np.uint32) == np.float32(ots).view(np.uint32)
+    assert np.array_equal(np_u8(s), os_)
+    assert np.array_equal(np_u8(c), oc)
+    assert np.array_equal(bf16_bits(d), orc.dequantize(oc, os_, 1, razer, ots))
+    if razer:
+        u = unpack(oc)
+        assert (u == 8).sum() > 1000 and (os_ >> 7).sum() > 100
+
+
+@pytest.mark.parametrize("shrink", [1.0, 0.25, 1e-3])
+def test_nv_given_tensor_scale_saturates(orc, shrink):
+    """A caller-given s_t smaller than amax/2688 saturates block scales at 448
+    and elements at 6, including scaled values far above 16."""
+    note(f"case: NVFP4 RaZeR with given tensor scale x{shrink}")
+    x = inputs.gen_c2(rows=256, cols=2048)
+    st = np.float32(orc.nv_tensor_scale(orc.nv_tensor_amax(x)) * shrink)
+    tst = torch.tensor([st], device="cuda")
+    c, s, _ = fp4.quantize(to_dev(x), fp4.NVFP4, fp4.RAZER, tensor_scale=tst)
+    sync()
+    oc, os_, _ = orc.nv_quantize(x, True, float(st))
+    assert np.array_equal(np_u8(s), os_)
+    assert np.array_equal(np_u8(c), oc)
+    assert float(tst.cpu()[0]) == float(st)  # the given scale is left untouched
+
+
+def test_nv_edge_cases(orc):
+    rows, cols = 8, 64
+    x = np.zeros((rows, cols), np.uint16)  # all-zero tensor: s_t = 1, codes 0
+    note("case: NVFP4 all-zero tensor")
+    c, s, ts = fp4.quantize(to_dev(x), fp4.NVFP4, fp4.RAZER)
+    sync()
+    assert float(ts.cpu()[0]) == 1.0 and not np_u8(c).any() and not np_u8(s).any()
+    # blocks whose E4M3 scale rounds to zero, negative zeros, tiny values
+    f = np.zeros((rows, cols), np.float32)
+    f[0, 0] = 3.0e4
+    f[1, :16] = 1e-3
+    f[2, :16] = -1e-9
+    f[3, 16:32] = -0.0
+    f[4, :] = np.linspace(-5.4, 5.4, cols) * 1e2
+    x = inputs.f64_to_bf16_bits(f.astype(np.float64))
+    for razer in (False, True):
+        note(f"case: NVFP4 edge blocks razer={razer}")
+        c, s, ts = fp4.quantize(to_dev(x), fp4.NVFP4, fp4.RAZER if razer else fp4.PLAIN)
+        sync()
+        oc, os_, ots = orc.nv_quantize(x, razer)
+        assert float(ts.cpu()[0]) == ots
+        assert np.array_equal(np_u8(s), os_) and np.array_equal(np_u8(c), oc)
+    # empty tensor with a computed scale still writes s_t = 1
+    note("case: NVFP4 empty tensor")
+    ts = torch.full((1,), 7.0, device="cuda")
+    st = fp4.lib().fp4_quantize(None, 0, 64, 64, 1, 16, 1, 0, None, 32, None, 4,
+                                ts.data_ptr(), None)
+    sync()
+    assert st == 0 and float(ts.cpu()[0]) == 1.0
+
+
+# ------------------------------------------------------ layouts and shapes ---
+@pytest.mark.parametrize("fmt,razer", [(0, False), (1, False), (1, True)])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (7, 96), (33, 160), (129, 4128)])
+def test_strided_ragged(orc, fmt, razer, rows, cols):
+    """Row strides larger than the row, odd row counts, rows that are not a
+    multiple of the work-group footprint."""
+    blk = 32 if fmt == 0 else 16
+    if cols % blk:
+        pytest.skip("cols not a multiple of the block")
+    note(f"case: strided fmt={fmt} razer={razer} {rows}x{cols}")
+    x_full = inputs.gen_c2(rows=rows, cols=cols + 24, seed=rows)
+    xt = to_dev(x_full)[:, :cols]
+    x = np.ascontiguousarray(x_full[:, :cols])
+    cbuf = torch.full((rows, cols // 2 + 12), 0xAB, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((rows, cols // blk + 5), 0xCD, dtype=torch.uint8, device="cuda")
+    c, s = cbuf[:, :cols // 2], sbuf[:, :cols // blk]
+    mode = fp4.RAZER if razer else fp4.PLAIN
+    _, _, ts = fp4.quantize(xt, fmt, mode, codes=c, scales=s)
+    obuf = torch.zeros((rows, cols + 8), dtype=torch.bfloat16, device="cuda")
+    fp4.dequantize(c, s, fmt, mode, ts, out=obuf[:, :cols])
+    sync()
+    if fmt == 0:
+        oc, os_ = orc.mx_quantize(x)
+        od = orc.dequantize(oc, os_, 0)
+    else:
+        oc, os_, ots = orc.nv_quantize(x, razer)
+        assert float(ts.cpu()[0]) == ots
+        od = orc.dequantize(oc, os_, 1, razer, ots)
+    assert np.array_equal(np_u8(c), oc) and np.array_equal(np_u8(s), os_)
+    assert np.all(np_u8(cbuf)[:, cols // 2:] == 0xAB) and np.all(np_u8(sbuf)[:, cols // blk:] == 0xCD)
+    assert np.array_equal(bf16_bits(obuf[:, :cols]), od)
+    assert not bf16_bits(obuf[:, cols:]).any()
+
+
+def test_deterministic():
+    x = to_dev(inputs.gen_c2(rows=512, cols=4096))
+    note("case: determinism, two identical calls")
+    a = fp4.quantize(x, fp4.NVFP4, fp4.RAZER)
+    b = fp4.quantize(x, fp4.NVFP4, fp4.RAZER)
+    r1 = fp4.rotate_quantize(x, None, 32, want_rotated=True)
+    r2 = fp4.rotate_quantize(x, None, 32, want_rotated=True)
+    sync()
+    for p, q in zip(a, b):
+        assert torch.equal(p, q)
+    for p, q in zip(r1, r2):
+        assert torch.equal(p, q)
+
+
+# ---------------------------------------------------------------- rotation --
+def _rot_case(orc, x, perm, had):
+    pt = None if perm is None else torch.from_numpy(perm).cuda()
+    c, s, y = fp4.rotate_quantize(to_dev(x), pt, had, want_rotated=True)
+    sync()
+    oc, os_, oy = orc.rotate_quantize(x, perm, had)
+    return check_rotated(y.cpu().numpy(), oy, np_u8(c), np_u8(s), oc, os_)
+
+
+def test_rotate_hadamard_c3_small(orc):
+    note("case: MXFP4 + H32, 512x8192 Student-t(3) with outlier channels")
+    x = inputs.gen_c3(rows=512)
+    r = _rot_case(orc, x, None, 32)
+    note(f"  {r}")
+
+
+def test_rotate_identity_matches_plain(orc):
+    """With no permutation and no Hadamard the fused kernel is plain MXFP4."""
+    x = inputs.gen_c1(rows=64, cols=1024)
+    note("case: rotate_quantize(identity) vs oracle plain MXFP4")
+    c, s, y = fp4.rotate_quantize(to_dev(x), None, 0, want_rotated=True)
+    sync()
+    oc, os_ = orc.mx_quantize(x)
+    assert np.array_equal(np_u8(c), oc) and np.array_equal(np_u8(s), os_)
+    assert np.array_equal(y.cpu().numpy(), inputs.bf16_bits_to_f32(x))
+
+
+@pytest.mark.parametrize("had", [32, 0])
+def test_rotate_two_level_c4_small(orc, had):
+    note(f"case: permutation + H{had}, 1024x8192 log-normal block variances")
+    x = inputs.gen_c4(rows=1024)
+    e_gpu = fp4.channel_energy(to_dev(x))
+    sync()
+    e_orc = orc.channel_energy(x)
+    assert np.allclose(e_gpu.cpu().numpy(), e_orc, rtol=1e-6, atol=0)
+    perm = orc.build_perm(e_orc.astype(np.float32), 32)
+    assert np.array_equal(fp4.build_permutation(e_gpu).numpy(),
+                          orc.build_perm(e_gpu.cpu().numpy(), 32))
+    r = _rot_case(orc, x, perm, had)
+    note(f"  {r}")
+
+
+@pytest.mark.parametrize("rows,cols", [(3, 96), (37, 2080), (5, 16384)])
+def test_rotate_ragged(orc, rows, cols):
+    note(f"case: rotate ragged {rows}x{cols}")
+    x = inputs.gen_c3(rows=rows, cols=cols)
+    perm = np.random.default_rng(cols).permutation(cols).astype(np.int32)
+    _rot_case(orc, x, perm, 32)
+    _rot_case(orc, x, None, 32)
+
+
+@pytest.mark.parametrize("perm_on", [False, True])
+def test_dequant_unrotate(orc, perm_on):
+    note(f"case: dequantize with inverse rotation perm={perm_on}")
+    x = inputs.gen_c4(rows=256, cols=4096)
+    perm = np.random.default_rng(5).permutation(4096).astype(np.int32) if perm_on else None
+    pt = None if perm is None else torch.from_numpy(perm).cuda()
+    c, s, _ = fp4.rotate_quantize(to_dev(x), pt, 32)
+    d = fp4.dequantize(c, s, fp4.MXFP4, perm=pt, hadamard=32)
+    sync()
+    yh = orc.dequantize_f64(np_u8(c), np_u8(s), 0)
+    want = orc.unrotate_f64(yh, perm, 32)
+    got = inputs.bf16_bits_to_f32(bf16_bits(d)).astype(np.float64)
+    rowmax = np.abs(want).max(1, keepdims=True)
+    assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-6 * rowmax)
+    # and the round trip is close to the input (SQNR of the two-level path)
+    sq = orc.sqnr_db(inputs.bf16_bits_to_f32(x), got)
+    note(f"  round-trip SQNR {sq:.2f} dB")
+    assert sq > 15
+
+
+# ------------------------------------------------------- full-size configs --
+def _sample_rows(rows, k, seed):
+    return np.sort(np.random.default_rng(seed).choice(rows, size=min(k, rows), replace=False))
+
+
+def test_c3_full_size_sampled(orc):
+    note("case: C3 full 8192x8192 MXFP4 + H32, sampled rows vs oracle")
+    x = inputs.gen_c3()
+    c, s, y = fp4.rotate_quantize(to_dev(x), None, 32, want_rotated=True)
+    sync()
+    rows = _sample_rows(x.shape[0], 48, 7)
+    xs = np.ascontiguousarray(x[rows])
+    oc, os_, oy = orc.rotate_quantize(xs, None, 32)
+    ri = torch.from_numpy(rows).cuda()
+    check_rotated(y[ri].cpu().numpy(), oy, np_u8(c[ri]), np_u8(s[ri]), oc, os_)
+
+
+def test_c4_full_size_sampled(orc):
+    note("case: C4 full 16384x8192 energy + permutation + H32, sampled rows vs oracle")
+    x = inputs.gen_c4()
+    xt = to_dev(x)
+    e_gpu = fp4.channel_energy(xt)
+    sync()
+    e_orc = orc.channel_energy(x)
+    assert np.allclose(e_gpu.cpu().numpy(), e_orc, rtol=1e-6, atol=0)
+    perm = fp4.build_permutation(e_gpu).numpy()
+    c, s, y = fp4.rotate_quantize(xt, torch.from_numpy(perm).cuda(), 32, want_rotated=True)
+    sync()
+    rows = _sample_rows(x.shape[0], 48, 8)
+    xs = np.ascontiguousarray(x[rows])
+    oc, os_, oy = orc.rotate_quantize(xs, perm, 32)
+    ri = torch.from_numpy(rows).cuda()
+    check_rotated(y[ri].cpu().numpy(), oy, np_u8(c[ri]), np_u8(s[ri]), oc, os_)
+
+
+@pytest.mark.parametrize("t", range(7))
+def test_c5_layer_sweep_sampled(orc, t):
+    name, R, C = inputs.C5_SHAPES[t]
+    note(f"case: C5 {name} {R}x{C} NVFP4+RaZeR round trip, sampled rows vs oracle")
+    x = inputs.gen_c5(t)
+    c, s, ts = fp4.quantize(to_dev(x), fp4.NVFP4, fp4.RAZER)
+    d = fp4.dequantize(c, s, fp4.NVFP4, fp4.RAZER, ts)
+    sync()
+    ots = orc.nv_tensor_scale(orc.nv_tensor_amax(x))
+    assert float(ts.cpu()[0]) == ots
+    rows = _sample_rows(R, 32, t)
+    xs = np.ascontiguousarray(x[rows])
+    oc, os_, _ = orc.nv_quantize(xs, True, ots)
+    ri = torch.from_numpy(rows).cuda()
+    assert np.array_equal(np_u8(c[ri]), oc) and np.array_equal(np_u8(s[ri]), os_)
+    assert np.array_equal(bf16_bits(d[ri]), orc.dequantize(oc, os_, 1, True, ots))
