@@ -77,6 +77,14 @@ def copies_for(nbytes, floor=2):
     return max(floor, -(-512 * 2 ** 20 // nbytes))
 
 
+def device_copy(torch):
+    """Reference: torch's device-to-device copy of 1 GiB (read + write bytes / time)."""
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms = timed(torch, lambda i: dst.copy_(src), 10, 2)
+    return {"bytes_moved": 2 << 30, "ms": round(ms, 4), "GBps": round(2 * (1 << 30) / ms / 1e6, 1)}
+
+
 def sqnr_db(torch, x, xh):
     x = x.double()
     d = x - xh.double()
@@ -154,7 +162,7 @@ def bench_c4(torch, fp4, inputs, args):
     q_plain = sqnr_db(torch, xs[0].float(), fp4.dequantize(c_pl, s_pl, fp4.MXFP4).float())
 
     extras = {"calibration_ms": round(calib_ms, 3), "channel_energy_ms": round(e_ms, 4),
-              "sqnr_db_plain_mxfp4": round(q_plain, 3)}
+              "sqnr_db_plain_mxfp4": round(q_plain, 3), "device_copy": device_copy(torch)}
     if not args.no_extras:
         extras.update(extra_rows(torch, fp4, inputs, xs, perm, codes, scales))
     res = {

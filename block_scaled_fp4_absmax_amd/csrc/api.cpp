@@ -74,7 +74,7 @@ int fp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, i
   if (format == FP4_MXFP4) {
     if (!empty) fp4::launch_mx_quant(s, (flags & FP4_FLAG_SCALE_OCP_FLOOR) != 0, x_bf16, codes, scales, st);
   } else {
-    if (need_scale) fp4::launch_nv_tensor_scale(s, x_bf16, tensor_scale, st);
+    if (need_scale) fp4::launch_nv_tensor_scale(s, x_bf16, codes, tensor_scale, st);
     if (!empty) fp4::launch_nv_quant(s, mode == FP4_RAZER, x_bf16, codes, scales, tensor_scale, st);
   }
   return launch_status();

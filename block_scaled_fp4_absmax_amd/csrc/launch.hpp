@@ -11,6 +11,10 @@ constexpr int kMaxGrid = 8192;
 // Largest row length that the permuting kernels stage in LDS (row + indices,
 // 4 bytes per column).
 constexpr int64_t kMaxPermCols = 16384;
+// Work-groups of the row-at-a-time (LDS-staged) kernels.
+constexpr int kPermGrid = 1024;
+// Work-groups of the tensor-amax pass (each leaves one partial maximum).
+constexpr int kAmaxGrid = 1024;
 
 struct Shape {
   int64_t rows, cols;
@@ -21,7 +25,9 @@ struct Shape {
 
 void launch_mx_quant(const Shape& s, bool floor_rule, const void* x, void* codes, void* scales,
                      hipStream_t st);
-void launch_nv_tensor_scale(const Shape& s, const void* x, float* ts, hipStream_t st);
+// Writes s_t; uses the code buffer as scratch for per-work-group partial maxima.
+void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float* ts,
+                            hipStream_t st);
 void launch_nv_quant(const Shape& s, bool razer, const void* x, void* codes, void* scales,
                      const float* ts, hipStream_t st);
 void launch_dequant(const Shape& s, int format, bool razer, const void* codes, const void* scales,

@@ -73,12 +73,15 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------- NVFP4 ----
-// Tensor amax as the fp32 bit pattern of max |x| (order-preserving for
-// non-negative floats), combined with one atomic max per work-group.
+// Tensor amax without atomics or scratch memory: each work-group reduces its
+// chunks to max |x| (the fp32 bit pattern, which orders like the magnitude)
+// and stores it in the code slot of its own first chunk -- output space that
+// the quantize kernel overwrites later in the same call. A single work-group
+// then reduces those partials and writes s_t = amax / 2688 (6 * 448), or 1
+// for an all-zero tensor.
 template <bool kFlat>
 __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint16_t* __restrict__ x,
-                                                           uint32_t* __restrict__ amax_bits,
-                                                           Geom g) {
+                                                           uint8_t* __restrict__ codes, Geom g) {
   __shared__ uint32_t red[kThreads / 64];
   const uint32_t stride = gridDim.x * kThreads;
   uint32_t m = 0;
@@ -104,17 +107,37 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint16_t* __res
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
     for (int i = 1; i < kThreads / 64; ++i) r = max(r, red[i]);
-    if (r) atomicMax(amax_bits, r << 16);
+    int64_t xo, co, so;
+    locate<kFlat, 16>(g, blockIdx.x * kThreads, xo, co, so);
+    *reinterpret_cast<uint32_t*>(codes + co) = r << 16;
   }
 }
 
-__global__ void nv_clear_kernel(uint32_t* p) { *p = 0u; }
-
-// s_t = amax / 2688 (one fp32 division), or 1 for an all-zero tensor.
-__global__ void nv_tensor_scale_kernel(float* ts) {
-  float amax = __uint_as_float(*reinterpret_cast<uint32_t*>(ts));
-  *ts = amax == 0.0f ? 1.0f : amax / 2688.0f;
+template <bool kFlat>
+__global__ __launch_bounds__(kThreads) void nv_tensor_scale_kernel(const uint8_t* __restrict__ codes,
+                                                                   uint32_t nparts, Geom g,
+                                                                   float* __restrict__ ts) {
+  __shared__ uint32_t red[kThreads / 64];
+  uint32_t m = 0;
+  for (uint32_t i = threadIdx.x; i < nparts; i += kThreads) {
+    int64_t xo, co, so;
+    locate<kFlat, 16>(g, i * kThreads, xo, co, so);
+    m = max(m, *reinterpret_cast<const uint32_t*>(codes + co));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) r = max(r, red[i]);
+    const float amax = __uint_as_float(r);
+    *ts = amax == 0.0f ? 1.0f : amax / 2688.0f;
+  }
 }
+
+// Empty tensor: nothing to reduce, s_t = 1.
+__global__ void nv_unit_scale_kernel(float* ts) { *ts = 1.0f; }
 
 template <bool kFlat, bool kRazer>
 __global__ __launch_bounds__(kThreads) void nv_quant_kernel(const uint16_t* __restrict__ x,
@@ -303,18 +326,26 @@ void launch_mx_quant(const Shape& s, bool floor_rule, const void* x, void* codes
   if (!flat && floor_rule) FP4_LAUNCH((mx_quant_kernel<false, true>), grid, st, xp, cp, sp, g);
 }
 
-void launch_nv_tensor_scale(const Shape& s, const void* x, float* ts, hipStream_t st) {
+void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float* ts,
+                            hipStream_t st) {
   Geom g = make_geom(s, 16);
-  const bool flat = s.ld_x == s.cols;
-  auto xp = static_cast<const uint16_t*>(x);
-  auto bits = reinterpret_cast<uint32_t*>(ts);
-  hipLaunchKernelGGL(nv_clear_kernel, dim3(1), dim3(1), 0, st, bits);
-  if (g.n > 0) {
-    const int grid = grid_for(g.n);
-    if (flat) FP4_LAUNCH((nv_amax_kernel<true>), grid, st, xp, bits, g);
-    else FP4_LAUNCH((nv_amax_kernel<false>), grid, st, xp, bits, g);
+  if (g.n == 0) {
+    hipLaunchKernelGGL(nv_unit_scale_kernel, dim3(1), dim3(1), 0, st, ts);
+    return;
   }
-  hipLaunchKernelGGL(nv_tensor_scale_kernel, dim3(1), dim3(1), 0, st, ts);
+  const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2;
+  auto xp = static_cast<const uint16_t*>(x);
+  auto cp = static_cast<uint8_t*>(codes);
+  uint64_t per = (uint64_t)kThreads * kUnroll;
+  uint64_t grid = (g.n + per - 1) / per;
+  if (grid > (uint64_t)kAmaxGrid) grid = kAmaxGrid;
+  if (flat) {
+    FP4_LAUNCH((nv_amax_kernel<true>), (int)grid, st, xp, cp, g);
+    FP4_LAUNCH((nv_tensor_scale_kernel<true>), 1, st, cp, (uint32_t)grid, g, ts);
+  } else {
+    FP4_LAUNCH((nv_amax_kernel<false>), (int)grid, st, xp, cp, g);
+    FP4_LAUNCH((nv_tensor_scale_kernel<false>), 1, st, cp, (uint32_t)grid, g, ts);
+  }
 }
 
 void launch_nv_quant(const Shape& s, bool razer, const void* x, void* codes, void* scales,

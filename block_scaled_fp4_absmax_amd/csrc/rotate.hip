@@ -7,22 +7,41 @@
 // rotation inside each 32-block (here the orthonormal Sylvester-Hadamard
 // matrix, H[i][j] = (-1)^popcount(i & j) / sqrt(32)).
 //
-// Layout in registers: lane q of a group of four holds elements 8q..8q+7 of a
-// block. H32 = H2 (x) H2 (x) H2 (x) H2 (x) H2 over the five index bits; bits
-// 0-2 are butterflies inside a lane, bits 3-4 are butterflies with the lane
-// xor 1 / xor 2 partner through DPP. The result is scaled by fp32(1/sqrt(32)).
+// The block Hadamard is a dense contraction y = H x over 32-element blocks, so
+// it runs on the matrix cores: one wave takes 32 blocks as the columns of a
+// 32x32 bf16 operand X and computes D = H X with two
+// v_mfma_f32_32x32x16_bf16 (K = 16 each) against the constant +-1 matrix H,
+// accumulating in fp32; bf16 inputs and +-1 entries make every product exact.
+// The MFMA's K order and output-row order are free to choose, so they are
+// chosen such that lane (n, h) -- block n = lane % 32, half h = lane / 32 --
+// loads the 32 contiguous bytes holding elements 16h..16h+15 of block n and
+// receives outputs 16h..16h+15 of the same block: loads and packed stores
+// stay contiguous and no lane exchange is needed except one max for the
+// block's absmax. The result is scaled by fp32(1/sqrt(32)).
+//
+// A second implementation (compile-time, FP4_HADAMARD_MFMA=0) runs the
+// transform as a radix-2 butterfly in registers and DPP lane exchanges; it is
+// kept for measuring one against the other.
 //
 // The permutation x'[j] = x[perm[j]] is applied by staging whole rows in LDS:
 // a work-group loads a row with coalesced 16-byte loads, then each lane
-// gathers its eight permuted elements with 2-byte LDS reads. The next row's
-// global loads are issued before the current row is processed.
+// gathers its permuted elements with 2-byte LDS reads. The next row's global
+// loads are issued before the current row is processed.
 #include "fp4_device.hpp"
 #include "launch.hpp"
 
+#ifndef FP4_HADAMARD_MFMA
+#define FP4_HADAMARD_MFMA 1
+#endif
+
 namespace fp4 {
 
-constexpr int kRotUnroll = 2;
+constexpr bool kUseMfma = FP4_HADAMARD_MFMA != 0;
 constexpr float kInvSqrt32 = 0.17677669529663688f;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ void widen8(u32x4_t d, float* v) {
   v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
@@ -31,8 +50,85 @@ __device__ __forceinline__ void widen8(u32x4_t d, float* v) {
   v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
 }
 
-// In-place y = H32 v / sqrt(32) for the lane's eight elements (see header).
-__device__ __forceinline__ void hadamard32(float* v, uint32_t lane) {
+__device__ __forceinline__ void store_rot8(float* rot, const float* y) {
+  f32x4_t a = {y[0], y[1], y[2], y[3]};
+  f32x4_t b = {y[4], y[5], y[6], y[7]};
+  __builtin_nontemporal_store(a, reinterpret_cast<f32x4_t*>(rot));
+  __builtin_nontemporal_store(b, reinterpret_cast<f32x4_t*>(rot) + 1);
+}
+
+// Largest |y| of n fp32 values as a bit pattern (NaN above Inf above finite).
+template <int n>
+__device__ __forceinline__ uint32_t absmax_bits(const float* y) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < n; ++k) m = max(m, __float_as_uint(y[k]) & 0x7FFFFFFFu);
+  return m;
+}
+
+// ============================ MFMA implementation ===========================
+// Row tau(m) of H held in MFMA output row m: lane half h' = (m / 4) % 2 owns
+// outputs 16h'..16h'+15, register r = 4 (m / 8) + m % 4 holds output 16h' + r.
+__device__ __forceinline__ uint32_t out_index_of_row(uint32_t m) {
+  return 16u * ((m >> 2) & 1u) + 4u * (m >> 3) + (m & 3u);
+}
+
+// Constant A operands: lane l holds A[m = l % 32][kk = 8 (l / 32) + j]; for
+// the first MFMA kk stands for element 16 (kk / 8) + kk % 8, for the second
+// 16 (kk / 8) + 8 + kk % 8 (matching the B halves each lane loads).
+__device__ __forceinline__ void hadamard_operands(bf16x8_t& a0, bf16x8_t& a1) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t row = out_index_of_row(lane & 31u);
+  const uint32_t k0 = 16u * (lane >> 5);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a0[j] = (__popc(row & (k0 + j)) & 1) ? (__bf16)-1.0f : (__bf16)1.0f;
+    a1[j] = (__popc(row & (k0 + 8 + j)) & 1) ? (__bf16)-1.0f : (__bf16)1.0f;
+  }
+}
+
+// y[0..15] = (H x)[16h .. 16h+15] / sqrt(32) for this lane's block, from the
+// lane's 16 inputs x[16h .. 16h+15] (bf16 pairs in lo/hi).
+__device__ __forceinline__ void hadamard_mfma(const bf16x8_t& a0, const bf16x8_t& a1,
+                                              u32x4_t lo, u32x4_t hi, float* y) {
+  f32x16_t acc = {};
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, __builtin_bit_cast(bf16x8_t, lo), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, __builtin_bit_cast(bf16x8_t, hi), acc, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) y[r] = acc[r] * kInvSqrt32;
+}
+
+// MXFP4-quantize the lane's 16 outputs; the block spans lanes l and l ^ 32.
+template <bool kFloor>
+__device__ __forceinline__ void mx_quant16_pair(const float* y, uint32_t& w0, uint32_t& w1,
+                                                uint32_t& byte) {
+  uint32_t m = absmax_bits<16>(y);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+  byte = e8m0_byte<kFloor>(m);
+  if (byte == 0xFFu) {
+    w0 = w1 = 0u;
+  } else {
+    const float s = e8m0_operand(byte);
+    w0 = cvt8_f32(y, s);
+    w1 = cvt8_f32(y + 8, s);
+  }
+}
+
+// ========================= butterfly implementation =========================
+// Lane q of a group of four holds elements 8q..8q+7: bits 0-2 of the index
+// are butterflies inside the lane, bits 3-4 exchanges with lane q ^ 1 and
+// q ^ 2 (DPP), folded as partner + (+-own) and, for the last stage,
+// partner * c + (+-c * own) with c = 1/sqrt(32).
+__device__ __forceinline__ float dpp1(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0xB1,
+                                                               0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp2(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x4E,
+                                                               0xF, 0xF, true));
+}
+
+__device__ __forceinline__ void hadamard_butterfly(float* v, uint32_t q) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -43,152 +139,275 @@ __device__ __forceinline__ void hadamard32(float* v, uint32_t lane) {
       v[k + h] = a - b;
     }
   }
-  // partner value t: lower lane takes own + t, upper lane t - own
-  const float s1 = (lane & 1u) ? -1.0f : 1.0f;
-  const float s2 = (lane & 2u) ? -1.0f : 1.0f;
+  const float s1 = (q & 1u) ? -1.0f : 1.0f;
+  const float s2 = (q & 2u) ? -kInvSqrt32 : kInvSqrt32;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(s1, v[k], dpp_xor1f(v[k]));
+  for (int k = 0; k < 8; ++k) {
+    float u = s1 * v[k];
+    v[k] = dpp1(v[k]) + u;
+  }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(s2, v[k], dpp_xor2f(v[k]));
-#pragma unroll
-  for (int k = 0; k < 8; ++k) v[k] *= kInvSqrt32;
+  for (int k = 0; k < 8; ++k) {
+    float u = s2 * v[k];
+    v[k] = __builtin_fmaf(dpp2(v[k]), kInvSqrt32, u);
+  }
 }
 
-// MXFP4 quantization of eight fp32 values whose block spans the lane's quad.
 template <bool kFloor>
-__device__ __forceinline__ void mx_quant8_f32(const float* y, uint32_t& w, uint32_t& byte) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(y[k]) & 0x7FFFFFFFu);
+__device__ __forceinline__ void mx_quant8_quad(const float* y, uint32_t& w, uint32_t& byte) {
+  uint32_t m = absmax_bits<8>(y);
   m = max(m, dpp_xor1(m));
   m = max(m, dpp_xor2(m));
   byte = e8m0_byte<kFloor>(m);
   w = byte == 0xFFu ? 0u : cvt8_f32(y, e8m0_operand(byte));
 }
 
-__device__ __forceinline__ void store_rot(float* rot, const float* y) {
-  f32x4_t a = {y[0], y[1], y[2], y[3]};
-  f32x4_t b = {y[4], y[5], y[6], y[7]};
-  __builtin_nontemporal_store(a, reinterpret_cast<f32x4_t*>(rot));
-  __builtin_nontemporal_store(b, reinterpret_cast<f32x4_t*>(rot) + 1);
-}
-
 struct RotGeom {
-  int32_t rows, cols, cpr;  // cpr = chunks (of 8 elements) per row
+  int32_t rows, cols;
+  int32_t bpr;   // 32-element blocks per row
+  uint32_t nblk; // rows * bpr
   int64_t ld_x, ld_c, ld_s, ld_rot;
 };
 
-// ---- no permutation: streaming, one chunk per lane ------------------------
-template <bool kHad, bool kFloor, bool kRot>
-__global__ __launch_bounds__(kThreads) void mx_rotq_stream_kernel(
+// ===================== streaming kernels (no permutation) ===================
+// MFMA: a wave owns a tile of 32 consecutive blocks (row-major block order);
+// tiles are dealt to waves grid-stride, kTiles per trip.
+constexpr int kTiles = 2;
+
+template <bool kFlat, bool kHad, bool kFloor, bool kRot>
+__global__ __launch_bounds__(kThreads) void mx_rotq_stream_mfma_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    float* __restrict__ rot, RotGeom g, uint32_t n) {
-  const uint32_t stride = gridDim.x * kThreads;
-  const uint32_t lane = threadIdx.x & 3u;
-  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < n;
-       base += kRotUnroll * stride) {
-    u32x4_t d[kRotUnroll];
-    uint32_t rr[kRotUnroll], cc[kRotUnroll];
+    float* __restrict__ rot, RotGeom g) {
+  bf16x8_t a0, a1;
+  hadamard_operands(a0, a1);
+  const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
+  const uint32_t wave = (blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const uint32_t nwaves = (gridDim.x * kThreads) >> 6;
+  const uint32_t ntiles = (g.nblk + 31u) >> 5;
+  for (uint32_t t0 = wave; t0 < ntiles; t0 += kTiles * nwaves) {
+    u32x4_t lo[kTiles], hi[kTiles];
+    int64_t xo[kTiles], co[kTiles], so[kTiles], ro[kTiles];
+    bool ok[kTiles];
 #pragma unroll
-    for (int u = 0; u < kRotUnroll; ++u) {
-      uint32_t v = base + u * stride;
-      if (v < n) {
-        rr[u] = v / (uint32_t)g.cpr;
-        cc[u] = v - rr[u] * (uint32_t)g.cpr;
-        d[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(x + rr[u] * g.ld_x + 8 * (int64_t)cc[u]));
+    for (int u = 0; u < kTiles; ++u) {
+      const uint32_t b = (t0 + u * nwaves) * 32u + n;
+      ok[u] = (t0 + u * nwaves) < ntiles && b < g.nblk;
+      lo[u] = u32x4_t{0u, 0u, 0u, 0u};
+      hi[u] = lo[u];
+      if (ok[u]) {
+        uint32_t r = kFlat ? 0u : b / (uint32_t)g.bpr;
+        uint32_t cb = kFlat ? b : b - r * (uint32_t)g.bpr;
+        xo[u] = r * g.ld_x + 32 * (int64_t)cb + 16 * h;
+        co[u] = r * g.ld_c + 16 * (int64_t)cb + 8 * h;
+        so[u] = r * g.ld_s + cb;
+        ro[u] = r * g.ld_rot + 32 * (int64_t)cb + 16 * h;
+        const u32x4_t* p = reinterpret_cast<const u32x4_t*>(x + xo[u]);
+        lo[u] = __builtin_nontemporal_load(p);
+        hi[u] = __builtin_nontemporal_load(p + 1);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kRotUnroll; ++u) {
-      uint32_t v = base + u * stride;
-      if (v >= n) continue;
-      float y[8];
-      widen8(d[u], y);
-      if (kHad) hadamard32(y, lane);
-      uint32_t w, byte;
-      mx_quant8_f32<kFloor>(y, w, byte);
-      __builtin_nontemporal_store(
-          w, reinterpret_cast<uint32_t*>(codes + rr[u] * g.ld_c + 4 * (int64_t)cc[u]));
-      if (lane == 0) scales[rr[u] * g.ld_s + cc[u] / 4] = (uint8_t)byte;
-      if (kRot) store_rot(rot + rr[u] * g.ld_rot + 8 * (int64_t)cc[u], y);
+    for (int u = 0; u < kTiles; ++u) {
+      if ((t0 + u * nwaves) >= ntiles) break;  // uniform across the wave
+      float y[16];
+      if (kHad) {
+        hadamard_mfma(a0, a1, lo[u], hi[u], y);
+      } else {
+        widen8(lo[u], y);
+        widen8(hi[u], y + 8);
+      }
+      uint32_t w0, w1, byte;
+      mx_quant16_pair<kFloor>(y, w0, w1, byte);
+      if (ok[u]) {
+        uint32_t* cp = reinterpret_cast<uint32_t*>(codes + co[u]);
+        __builtin_nontemporal_store(w0, cp);
+        __builtin_nontemporal_store(w1, cp + 1);
+        if (h == 0) scales[so[u]] = (uint8_t)byte;
+        if (kRot) {
+          store_rot8(rot + ro[u], y);
+          store_rot8(rot + ro[u] + 8, y + 8);
+        }
+      }
     }
   }
 }
 
-// ---- with permutation: one row at a time through LDS ---------------------
-// Dynamic LDS: row[cols] bf16 followed by perm[cols] uint16.
+// Butterfly: one 16-byte chunk of eight elements per lane, four lanes per block.
+template <bool kFlat, bool kHad, bool kFloor, bool kRot>
+__global__ __launch_bounds__(kThreads) void mx_rotq_stream_bfly_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    float* __restrict__ rot, RotGeom g) {
+  const uint32_t stride = gridDim.x * kThreads;
+  const uint32_t q = threadIdx.x & 3u;
+  const uint32_t n = g.nblk * 4u;
+  constexpr int U = 4;
+  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < n; base += U * stride) {
+    u32x4_t d[U];
+    int64_t xo[U], co[U], so[U], ro[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t v = base + u * stride;
+      if (v < n) {
+        uint32_t cpr = 4u * (uint32_t)g.bpr;
+        uint32_t r = kFlat ? 0u : v / cpr;
+        uint32_t c = kFlat ? v : v - r * cpr;
+        xo[u] = r * g.ld_x + 8 * (int64_t)c;
+        co[u] = r * g.ld_c + 4 * (int64_t)c;
+        so[u] = r * g.ld_s + c / 4;
+        ro[u] = r * g.ld_rot + 8 * (int64_t)c;
+        d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo[u]));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t v = base + u * stride;
+      if (v >= n) continue;
+      float y[8];
+      widen8(d[u], y);
+      if (kHad) hadamard_butterfly(y, q);
+      uint32_t w, byte;
+      mx_quant8_quad<kFloor>(y, w, byte);
+      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + co[u]));
+      if (q == 0) scales[so[u]] = (uint8_t)byte;
+      if (kRot) store_rot8(rot + ro[u], y);
+    }
+  }
+}
+
+// ================== permuting kernels (one row at a time, LDS) ==============
+// Dynamic LDS: row[cols] bf16 followed by perm[cols] uint16 (entries clamped
+// to cols - 1, so no gather leaves the row).
 constexpr int kMaxChunksPerLane = (int)(kMaxPermCols / 8 / kThreads);  // 8
 
+__device__ __forceinline__ void stage_perm(const int32_t* __restrict__ perm, uint16_t* sperm,
+                                           int32_t cols) {
+  const int32_t cmax = cols - 1;
+  for (int32_t j = threadIdx.x; j < cols; j += kThreads) {
+    int32_t p = perm[j];
+    p = p < 0 ? 0 : (p > cmax ? cmax : p);
+    sperm[j] = (uint16_t)p;
+  }
+}
+
+__device__ __forceinline__ void load_row(const uint16_t* __restrict__ src, int32_t cpr,
+                                         u32x4_t* pre) {
+#pragma unroll
+  for (int i = 0; i < kMaxChunksPerLane; ++i) {
+    int32_t c = threadIdx.x + i * kThreads;
+    if (c < cpr) pre[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src) + c);
+  }
+}
+
+__device__ __forceinline__ void put_row(uint16_t* srow, int32_t cpr, const u32x4_t* pre) {
+#pragma unroll
+  for (int i = 0; i < kMaxChunksPerLane; ++i) {
+    int32_t c = threadIdx.x + i * kThreads;
+    if (c < cpr) reinterpret_cast<u32x4_t*>(srow)[c] = pre[i];
+  }
+}
+
+// Eight gathered bf16, packed in pairs, from eight LDS indices.
+__device__ __forceinline__ u32x4_t gather8(const uint16_t* srow, u32x4_t id) {
+  u32x4_t r;
+  r.x = (uint32_t)srow[id.x & 0xFFFFu] | ((uint32_t)srow[id.x >> 16] << 16);
+  r.y = (uint32_t)srow[id.y & 0xFFFFu] | ((uint32_t)srow[id.y >> 16] << 16);
+  r.z = (uint32_t)srow[id.z & 0xFFFFu] | ((uint32_t)srow[id.z >> 16] << 16);
+  r.w = (uint32_t)srow[id.w & 0xFFFFu] | ((uint32_t)srow[id.w >> 16] << 16);
+  return r;
+}
+
 template <bool kHad, bool kFloor, bool kRot>
-__global__ __launch_bounds__(kThreads) void mx_rotq_perm_kernel(
+__global__ __launch_bounds__(kThreads) void mx_rotq_perm_mfma_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ rot, RotGeom g) {
   extern __shared__ uint16_t smem[];
   uint16_t* srow = smem;
   uint16_t* sperm = smem + g.cols;
-  const uint32_t lane = threadIdx.x & 3u;
-  const int32_t cmax = g.cols - 1;
-  for (int32_t j = threadIdx.x; j < g.cols; j += kThreads) {
-    int32_t p = perm[j];
-    p = p < 0 ? 0 : (p > cmax ? cmax : p);  // an invalid entry cannot leave the row
-    sperm[j] = (uint16_t)p;
-  }
+  bf16x8_t a0, a1;
+  hadamard_operands(a0, a1);
+  stage_perm(perm, sperm, g.cols);
+  const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
+  const int32_t wave = threadIdx.x >> 6;
+  const int32_t cpr = g.cols / 8;
+  const int32_t ntiles = (g.bpr + 31) / 32;
   u32x4_t pre[kMaxChunksPerLane];
   int32_t r = blockIdx.x;
-  if (r < g.rows) {
-#pragma unroll
-    for (int i = 0; i < kMaxChunksPerLane; ++i) {
-      int32_t c = threadIdx.x + i * kThreads;
-      if (c < g.cpr)
-        pre[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(x + r * g.ld_x + 8 * (int64_t)c));
-    }
-  }
+  if (r < g.rows) load_row(x + r * g.ld_x, cpr, pre);
   for (; r < g.rows; r += gridDim.x) {
-    __syncthreads();  // the previous row's gathers are done
-#pragma unroll
-    for (int i = 0; i < kMaxChunksPerLane; ++i) {
-      int32_t c = threadIdx.x + i * kThreads;
-      if (c < g.cpr) reinterpret_cast<u32x4_t*>(srow)[c] = pre[i];
-    }
+    __syncthreads();  // the previous row's gathers are done (and sperm is visible)
+    put_row(srow, cpr, pre);
     __syncthreads();
-    const int32_t rn = r + gridDim.x;
-    if (rn < g.rows) {
-#pragma unroll
-      for (int i = 0; i < kMaxChunksPerLane; ++i) {
-        int32_t c = threadIdx.x + i * kThreads;
-        if (c < g.cpr)
-          pre[i] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4_t*>(x + rn * g.ld_x + 8 * (int64_t)c));
+    if (r + (int32_t)gridDim.x < g.rows) load_row(x + (r + gridDim.x) * g.ld_x, cpr, pre);
+    for (int32_t t = wave; t < ntiles; t += kThreads / 64) {
+      const int32_t b = 32 * t + (int32_t)n;
+      const bool ok = b < g.bpr;
+      u32x4_t lo = {0u, 0u, 0u, 0u}, hi = lo;
+      if (ok) {
+        const u32x4_t* ip = reinterpret_cast<const u32x4_t*>(sperm + 32 * b + 16 * h);
+        lo = gather8(srow, ip[0]);
+        hi = gather8(srow, ip[1]);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < kMaxChunksPerLane; ++i) {
-      int32_t c = threadIdx.x + i * kThreads;
-      if (c >= g.cpr) continue;
-      u32x4_t id = reinterpret_cast<const u32x4_t*>(sperm)[c];
-      float y[8];
-      y[0] = __uint_as_float((uint32_t)srow[id.x & 0xFFFFu] << 16);
-      y[1] = __uint_as_float((uint32_t)srow[id.x >> 16] << 16);
-      y[2] = __uint_as_float((uint32_t)srow[id.y & 0xFFFFu] << 16);
-      y[3] = __uint_as_float((uint32_t)srow[id.y >> 16] << 16);
-      y[4] = __uint_as_float((uint32_t)srow[id.z & 0xFFFFu] << 16);
-      y[5] = __uint_as_float((uint32_t)srow[id.z >> 16] << 16);
-      y[6] = __uint_as_float((uint32_t)srow[id.w & 0xFFFFu] << 16);
-      y[7] = __uint_as_float((uint32_t)srow[id.w >> 16] << 16);
-      if (kHad) hadamard32(y, lane);
-      uint32_t w, byte;
-      mx_quant8_f32<kFloor>(y, w, byte);
-      __builtin_nontemporal_store(
-          w, reinterpret_cast<uint32_t*>(codes + r * g.ld_c + 4 * (int64_t)c));
-      if (lane == 0) scales[r * g.ld_s + c / 4] = (uint8_t)byte;
-      if (kRot) store_rot(rot + r * g.ld_rot + 8 * (int64_t)c, y);
+      float y[16];
+      if (kHad) {
+        hadamard_mfma(a0, a1, lo, hi, y);
+      } else {
+        widen8(lo, y);
+        widen8(hi, y + 8);
+      }
+      uint32_t w0, w1, byte;
+      mx_quant16_pair<kFloor>(y, w0, w1, byte);
+      if (ok) {
+        uint32_t* cp = reinterpret_cast<uint32_t*>(codes + r * g.ld_c + 16 * (int64_t)b + 8 * h);
+        __builtin_nontemporal_store(w0, cp);
+        __builtin_nontemporal_store(w1, cp + 1);
+        if (h == 0) scales[r * g.ld_s + b] = (uint8_t)byte;
+        if (kRot) {
+          float* rp = rot + r * g.ld_rot + 32 * (int64_t)b + 16 * h;
+          store_rot8(rp, y);
+          store_rot8(rp + 8, y + 8);
+        }
+      }
     }
   }
 }
 
-// ---- inverse rotation after MXFP4 decoding --------------------------------
+template <bool kHad, bool kFloor, bool kRot>
+__global__ __launch_bounds__(kThreads) void mx_rotq_perm_bfly_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ rot, RotGeom g) {
+  extern __shared__ uint16_t smem[];
+  uint16_t* srow = smem;
+  uint16_t* sperm = smem + g.cols;
+  stage_perm(perm, sperm, g.cols);
+  const uint32_t q = threadIdx.x & 3u;
+  const int32_t cpr = g.cols / 8;
+  u32x4_t pre[kMaxChunksPerLane];
+  int32_t r = blockIdx.x;
+  if (r < g.rows) load_row(x + r * g.ld_x, cpr, pre);
+  for (; r < g.rows; r += gridDim.x) {
+    __syncthreads();
+    put_row(srow, cpr, pre);
+    __syncthreads();
+    if (r + (int32_t)gridDim.x < g.rows) load_row(x + (r + gridDim.x) * g.ld_x, cpr, pre);
+#pragma unroll
+    for (int i = 0; i < kMaxChunksPerLane; ++i) {
+      int32_t c = threadIdx.x + i * kThreads;
+      if (c >= cpr) continue;
+      float y[8];
+      widen8(gather8(srow, reinterpret_cast<const u32x4_t*>(sperm)[c]), y);
+      if (kHad) hadamard_butterfly(y, q);
+      uint32_t w, byte;
+      mx_quant8_quad<kFloor>(y, w, byte);
+      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + r * g.ld_c + 4 * (int64_t)c));
+      if (q == 0) scales[r * g.ld_s + c / 4] = (uint8_t)byte;
+      if (kRot) store_rot8(rot + r * g.ld_rot + 8 * (int64_t)c, y);
+    }
+  }
+}
+
+// ============================ inverse rotation ==============================
+// Decode MXFP4 exactly to fp32, apply H (its own inverse) with the butterfly,
+// then scatter element j to column perm[j] through LDS.
 template <bool kHad, bool kPerm>
 __global__ __launch_bounds__(kThreads) void mx_dequant_unrotate_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
@@ -196,18 +415,12 @@ __global__ __launch_bounds__(kThreads) void mx_dequant_unrotate_kernel(
   extern __shared__ uint16_t smem[];
   uint16_t* srow = smem;
   uint16_t* sperm = smem + g.cols;
-  const uint32_t lane = threadIdx.x & 3u;
-  const int32_t cmax = g.cols - 1;
-  if (kPerm) {
-    for (int32_t j = threadIdx.x; j < g.cols; j += kThreads) {
-      int32_t p = perm[j];
-      p = p < 0 ? 0 : (p > cmax ? cmax : p);
-      sperm[j] = (uint16_t)p;
-    }
-  }
+  const uint32_t q = threadIdx.x & 3u;
+  const int32_t cpr = g.cols / 8;
+  if (kPerm) stage_perm(perm, sperm, g.cols);
   for (int32_t r = blockIdx.x; r < g.rows; r += gridDim.x) {
     if (kPerm) __syncthreads();  // previous row copied out, indices visible
-    for (int32_t c = threadIdx.x; c < g.cpr; c += kThreads) {
+    for (int32_t c = threadIdx.x; c < cpr; c += kThreads) {
       uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * g.ld_c + 4 * (int64_t)c);
       float s = e8m0_operand(scales[r * g.ld_s + c / 4]);
       float y[8];
@@ -217,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void mx_dequant_unrotate_kernel(
       float2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 3);
       y[0] = p0.x; y[1] = p0.y; y[2] = p1.x; y[3] = p1.y;
       y[4] = p2.x; y[5] = p2.y; y[6] = p3.x; y[7] = p3.y;
-      if (kHad) hadamard32(y, lane);  // H is symmetric and orthonormal: its own inverse
+      if (kHad) hadamard_butterfly(y, q);
       u32x4_t o;
       o.x = pack_bf16x2(y[0], y[1]);
       o.y = pack_bf16x2(y[2], y[3]);
@@ -234,19 +447,19 @@ __global__ __launch_bounds__(kThreads) void mx_dequant_unrotate_kernel(
         srow[id.w & 0xFFFFu] = (uint16_t)(o.w & 0xFFFFu);
         srow[id.w >> 16] = (uint16_t)(o.w >> 16);
       } else {
-        *reinterpret_cast<u32x4_t*>(out + r * g.ld_x + 8 * (int64_t)c) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + r * g.ld_x) + c);
       }
     }
     if (kPerm) {
       __syncthreads();
-      for (int32_t c = threadIdx.x; c < g.cpr; c += kThreads)
-        *reinterpret_cast<u32x4_t*>(out + r * g.ld_x + 8 * (int64_t)c) =
-            reinterpret_cast<const u32x4_t*>(srow)[c];
+      for (int32_t c = threadIdx.x; c < cpr; c += kThreads)
+        __builtin_nontemporal_store(reinterpret_cast<const u32x4_t*>(srow)[c],
+                                    reinterpret_cast<u32x4_t*>(out + r * g.ld_x) + c);
     }
   }
 }
 
-// ---- channel energy ------------------------------------------------------
+// ============================== channel energy ==============================
 // One work-group per 32-column slice; lane (q, rg) = (t & 3, t >> 2) adds the
 // squares of chunk q of rows rg, rg + 64, ... in fp64; the 64 partial sums of
 // each column are then added in row-group order, so the result does not
@@ -275,12 +488,13 @@ __global__ __launch_bounds__(kThreads) void channel_energy_kernel(const uint16_t
   }
 }
 
-// --------------------------------------------------------------- launchers ----
+// ================================ launchers =================================
 static RotGeom rot_geom(const Shape& s, int64_t ld_rot) {
   RotGeom g;
   g.rows = (int32_t)s.rows;
   g.cols = (int32_t)s.cols;
-  g.cpr = (int32_t)(s.cols / 8);
+  g.bpr = (int32_t)(s.cols / 32);
+  g.nblk = (uint32_t)(s.rows * (s.cols / 32));
   g.ld_x = s.ld_x;
   g.ld_c = s.ld_c;
   g.ld_s = s.ld_s;
@@ -288,21 +502,41 @@ static RotGeom rot_geom(const Shape& s, int64_t ld_rot) {
   return g;
 }
 
+static int perm_grid(int64_t rows) { return (int)(rows < kPermGrid ? rows : kPermGrid); }
+
 template <bool kHad, bool kFloor, bool kRot>
 static void rotq_dispatch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
-                          uint8_t* sc, float* rot, const RotGeom& g, hipStream_t st) {
+                          uint8_t* sc, float* rot, const RotGeom& g, bool flat, hipStream_t st) {
   if (perm) {
-    int grid = (int)(s.rows < 2048 ? s.rows : 2048);
     size_t lds = (size_t)4 * s.cols;
-    hipLaunchKernelGGL((mx_rotq_perm_kernel<kHad, kFloor, kRot>), dim3(grid), dim3(kThreads), lds,
-                       st, x, perm, c, sc, rot, g);
-  } else {
-    uint32_t n = (uint32_t)(s.rows * s.cols / 8);
-    uint64_t per = (uint64_t)kThreads * kRotUnroll;
-    uint64_t grid = (n + per - 1) / per;
+    if (kUseMfma)
+      hipLaunchKernelGGL((mx_rotq_perm_mfma_kernel<kHad, kFloor, kRot>), dim3(perm_grid(s.rows)),
+                         dim3(kThreads), lds, st, x, perm, c, sc, rot, g);
+    else
+      hipLaunchKernelGGL((mx_rotq_perm_bfly_kernel<kHad, kFloor, kRot>), dim3(perm_grid(s.rows)),
+                         dim3(kThreads), lds, st, x, perm, c, sc, rot, g);
+    return;
+  }
+  if (kUseMfma) {
+    uint64_t waves = ((uint64_t)g.nblk + 31) / 32;
+    uint64_t grid = (waves + (kThreads / 64) * kTiles - 1) / ((kThreads / 64) * kTiles);
     if (grid > (uint64_t)kMaxGrid) grid = kMaxGrid;
-    hipLaunchKernelGGL((mx_rotq_stream_kernel<kHad, kFloor, kRot>), dim3((int)grid),
-                       dim3(kThreads), 0, st, x, c, sc, rot, g, n);
+    if (flat)
+      hipLaunchKernelGGL((mx_rotq_stream_mfma_kernel<true, kHad, kFloor, kRot>), dim3((int)grid),
+                         dim3(kThreads), 0, st, x, c, sc, rot, g);
+    else
+      hipLaunchKernelGGL((mx_rotq_stream_mfma_kernel<false, kHad, kFloor, kRot>), dim3((int)grid),
+                         dim3(kThreads), 0, st, x, c, sc, rot, g);
+  } else {
+    uint64_t chunks = (uint64_t)g.nblk * 4;
+    uint64_t grid = (chunks + kThreads * 4 - 1) / (kThreads * 4);
+    if (grid > (uint64_t)kMaxGrid) grid = kMaxGrid;
+    if (flat)
+      hipLaunchKernelGGL((mx_rotq_stream_bfly_kernel<true, kHad, kFloor, kRot>), dim3((int)grid),
+                         dim3(kThreads), 0, st, x, c, sc, rot, g);
+    else
+      hipLaunchKernelGGL((mx_rotq_stream_bfly_kernel<false, kHad, kFloor, kRot>), dim3((int)grid),
+                         dim3(kThreads), 0, st, x, c, sc, rot, g);
   }
 }
 
@@ -314,14 +548,16 @@ void launch_mx_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, b
   auto cp = static_cast<uint8_t*>(codes);
   auto sp = static_cast<uint8_t*>(scales);
   const bool had = hadamard != 0, r = rot != nullptr;
-  if (had && !floor_rule && !r) rotq_dispatch<true, false, false>(s, perm, xp, cp, sp, rot, g, st);
-  if (had && !floor_rule && r) rotq_dispatch<true, false, true>(s, perm, xp, cp, sp, rot, g, st);
-  if (had && floor_rule && !r) rotq_dispatch<true, true, false>(s, perm, xp, cp, sp, rot, g, st);
-  if (had && floor_rule && r) rotq_dispatch<true, true, true>(s, perm, xp, cp, sp, rot, g, st);
-  if (!had && !floor_rule && !r) rotq_dispatch<false, false, false>(s, perm, xp, cp, sp, rot, g, st);
-  if (!had && !floor_rule && r) rotq_dispatch<false, false, true>(s, perm, xp, cp, sp, rot, g, st);
-  if (!had && floor_rule && !r) rotq_dispatch<false, true, false>(s, perm, xp, cp, sp, rot, g, st);
-  if (!had && floor_rule && r) rotq_dispatch<false, true, true>(s, perm, xp, cp, sp, rot, g, st);
+  const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / 32 &&
+                    (!r || ld_rot == s.cols);
+  if (had && !floor_rule && !r) rotq_dispatch<true, false, false>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (had && !floor_rule && r) rotq_dispatch<true, false, true>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (had && floor_rule && !r) rotq_dispatch<true, true, false>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (had && floor_rule && r) rotq_dispatch<true, true, true>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (!had && !floor_rule && !r) rotq_dispatch<false, false, false>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (!had && !floor_rule && r) rotq_dispatch<false, false, true>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (!had && floor_rule && !r) rotq_dispatch<false, true, false>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (!had && floor_rule && r) rotq_dispatch<false, true, true>(s, perm, xp, cp, sp, rot, g, flat, st);
 }
 
 void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard,
@@ -330,7 +566,7 @@ void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamar
   auto cp = static_cast<const uint8_t*>(codes);
   auto sp = static_cast<const uint8_t*>(scales);
   auto op = static_cast<uint16_t*>(out);
-  int grid = (int)(s.rows < 2048 ? s.rows : 2048);
+  const int grid = perm_grid(s.rows);
   size_t lds = perm ? (size_t)4 * s.cols : 0;
   if (hadamard && perm)
     hipLaunchKernelGGL((mx_dequant_unrotate_kernel<true, true>), dim3(grid), dim3(kThreads), lds,

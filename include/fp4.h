@@ -109,8 +109,10 @@ const char* fp4_status_string(int status);
  *  tensor_scale NVFP4: device fp32[1], written (or read with the flag);
  *               MXFP4: ignored, may be NULL
  *  stream       hipStream_t
- * Returns FP4_OK or an fp4_status. With NVFP4 and a computed s_t, four
- * kernels are enqueued (clear, tensor amax, s_t, quantize); otherwise one.
+ * Returns FP4_OK or an fp4_status. With NVFP4 and a computed s_t, three
+ * kernels are enqueued (tensor amax, s_t, quantize) and the codes array also
+ * carries the amax pass's per-work-group partial maxima until the quantize
+ * kernel overwrites it; otherwise one kernel is enqueued.
  */
 int fp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, int format,
                  int block, int mode, uint32_t flags, void* codes, int64_t ld_codes,
