@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
         "fp4_rotate_quantize": (i32, [vp, i64, i64, i64, vp, i32, i32, i32, i32, u32, vp, i64, vp,
                                       i64, vp, vp, i64, vp]),
         "fp4_channel_energy": (i32, [vp, i64, i64, i64, vp, vp]),
-        "fp4_build_permutation": (i32, [vp, i64, i32, vp]),
+        "fp4_build_permutation": (i32, [vp, i64, i32, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -182,11 +182,12 @@ def channel_energy(x, out=None, stream=None):
     return out
 
 
-def build_permutation(energy, block: int = 32):
-    """int32 [cols] host tensor: magnitude-balancing permutation (host code)."""
+def build_permutation(energy, block: int = 32, group: int = 1):
+    """int32 [cols] host tensor: magnitude-balancing permutation (host code)
+    moving aligned runs of ``group`` channels (1, 2, 4 or 8)."""
     import torch
     e = energy.detach().to("cpu", torch.float32).contiguous()
     perm = torch.empty(e.numel(), dtype=torch.int32)
-    st = lib().fp4_build_permutation(_ptr(e), e.numel(), block, _ptr(perm))
+    st = lib().fp4_build_permutation(_ptr(e), e.numel(), block, group, _ptr(perm))
     _check("fp4_build_permutation", st)
     return perm

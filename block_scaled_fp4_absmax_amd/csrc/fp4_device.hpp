@@ -102,35 +102,42 @@ __device__ __forceinline__ uint32_t cvt8_f32(const float* y, float scale) {
 
 // ---- E4M3 block scale (NVFP4) ---------------------------------------------
 // OCP E4M3 "fn": bias 7, subnormals m * 2^-9, largest finite 448, 0x7F NaN.
-// Nearest code to s >= 0 with ties to the even code, saturating at 448.
+// Nearest code to s >= 0 with ties to the even code, saturating at 448;
+// branch-free (both the subnormal and the normal candidate are computed).
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  if (!(s <= 448.0f)) return 0x7Eu;
-  if (s < 0x1p-6f) return (uint32_t)__builtin_rintf(s * 512.0f);  // exact scale, RNE
+  // subnormals m * 2^-9: exact rescale, round half even
+  const uint32_t sub = (uint32_t)__builtin_rintf(s * 512.0f);
+  // normals: round the 20 dropped mantissa bits (ties even), rebias 127 -> 7
   uint32_t u = __float_as_uint(s);
-  u += 0x7FFFFu + ((u >> 20) & 1u);  // round the 20 dropped mantissa bits, ties even
-  return (u >> 20) - (120u << 3);    // rebias exponent 127 -> 7
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  const uint32_t nrm = (u >> 20) - (120u << 3);
+  const uint32_t c = s < 0x1p-6f ? sub : nrm;
+  return s <= 448.0f ? c : 0x7Eu;
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  uint32_t mag = c & 0x7Fu;
-  float v = mag >= 8u ? __uint_as_float((((mag >> 3) + 120u) << 23) | ((mag & 7u) << 20))
-                      : (float)mag * 0x1p-9f;
+  const uint32_t mag = c & 0x7Fu;
+  const float nrm = __uint_as_float((((mag >> 3) + 120u) << 23) | ((mag & 7u) << 20));
+  const float sub = (float)mag * 0x1p-9f;
+  float v = mag >= 8u ? nrm : sub;
   if (mag == 0x7Fu) v = __builtin_nanf("");
   return (c & 0x80u) ? -v : v;
 }
 
 // ---- RaZeR gain ---------------------------------------------------------
 // Squared-error gain of replacing an element's standard code by the special
-// value 5 (same sign): with d = |y| - 5, the standard neighbour is 4 or 6 and
-// (|y| - std)^2 - d^2 = 1 - 2|d| on |d| < 0.5, zero outside. In [4, 8) fp32
-// values are multiples of 2^-21, so the gain in units of 2^-21 is the integer
-// 2^21 - 2 |bits(|y|) - bits(5)|, clamped at 0; bits below 4 or from 8 up lie
-// more than 2^20 away from bits(5).
-__device__ __forceinline__ int32_t razer_gain(float y) {
-  uint32_t a = __float_as_uint(y) & 0x7FFFFFFFu;
-  uint32_t d = a > 0x40A00000u ? a - 0x40A00000u : 0x40A00000u - a;
-  d = d < 0x100000u ? d : 0x100000u;
-  return (int32_t)(0x200000u - 2u * d);
+// value 5 of the same sign: with d = |y| - 5, the standard neighbour is 4 or
+// 6 and (|y| - std)^2 - d^2 = 1 - 2|d| on |d| < 0.5, and no gain outside.
+// Returned with the sign of y. Exact in fp32: for |y| in [2.5, 10], |y| - 5 is
+// exact (Sterbenz), and where the gain is positive |y| lies in [4, 8), so d is
+// a multiple of 2^-21 and 1 - 2|d| a multiple of 2^-20 in (0, 1]; elsewhere
+// 1 - 2|d| < 0 whatever the rounding and is clamped to 0. A block sum of 16
+// such gains (at most 16, on the 2^-20 grid) is exact too.
+__device__ __forceinline__ float razer_signed_gain(float y) {
+  const float d = __builtin_fabsf(y) - 5.0f;
+  const float g = __builtin_amdgcn_fmed3f(__builtin_fmaf(-2.0f, __builtin_fabsf(d), 1.0f), 0.0f,
+                                          1.0f);
+  return __builtin_copysignf(g, y);
 }
 
 // Code dword with every nibble whose magnitude is zero cleared to 0x0.

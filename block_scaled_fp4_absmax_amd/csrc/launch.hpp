@@ -6,15 +6,14 @@
 
 namespace fp4 {
 
-// Upper bound on work-groups of the grid-stride streaming kernels.
-constexpr int kMaxGrid = 8192;
 // Largest row length that the permuting kernels stage in LDS (row + indices,
 // 4 bytes per column).
 constexpr int64_t kMaxPermCols = 16384;
 // Work-groups of the row-at-a-time (LDS-staged) kernels.
-constexpr int kPermGrid = 1024;
-// Work-groups of the tensor-amax pass (each leaves one partial maximum).
-constexpr int kAmaxGrid = 1024;
+#ifndef FP4_PERM_GRID
+#define FP4_PERM_GRID 1024
+#endif
+constexpr int kPermGrid = FP4_PERM_GRID;
 
 struct Shape {
   int64_t rows, cols;

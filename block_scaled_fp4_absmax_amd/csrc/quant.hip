@@ -4,16 +4,22 @@
 // bf16 (a coalesced dwordx4 load), so four neighbouring lanes hold one
 // 32-element MXFP4 block and two hold one 16-element NVFP4 block. Block-wide
 // reductions are one or two DPP quad_perm steps; no LDS is used. The chunk
-// index v walks the matrix row-major; grid-stride loops process kUnroll
-// chunks per lane per trip with all loads issued before any arithmetic.
-// Since cols is a multiple of the block, chunks of one block are always
-// processed by adjacent lanes in the same trip.
+// index v walks the matrix row-major. Each work-group makes a single pass over
+// one contiguous range of kThreads * kUnroll chunks (lane t takes chunks
+// base + u * kThreads + t), issuing all its loads before any arithmetic: on
+// MI355X this keeps whole cache lines of codes and scales inside one
+// work-group and measured faster than grid-stride loops. Since cols is a
+// multiple of the block, the chunks of one block are always held by adjacent
+// lanes at the same u.
 #include "fp4_device.hpp"
 #include "launch.hpp"
 
 namespace fp4 {
 
-constexpr int kUnroll = 4;
+#ifndef FP4_UNROLL
+#define FP4_UNROLL 4
+#endif
+constexpr int kUnroll = FP4_UNROLL;  // chunks per lane (one pass per work-group)
 
 // Address arithmetic for chunk v. kFlat: rows are contiguous in every array,
 // so the matrix is a single row of rows * cols elements.
@@ -43,9 +49,10 @@ template <bool kFlat, bool kFloor>
 __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint16_t* __restrict__ x,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales, Geom g) {
-  const uint32_t stride = gridDim.x * kThreads;
   const bool leader = (threadIdx.x & 3) == 0;
-  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < g.n; base += kUnroll * stride) {
+  const uint32_t base = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  constexpr uint32_t stride = kThreads;
+  {
     u32x4_t d[kUnroll];
     int64_t xo[kUnroll], co[kUnroll], so[kUnroll];
 #pragma unroll
@@ -79,27 +86,29 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint16_t* __re
 // the quantize kernel overwrites later in the same call. A single work-group
 // then reduces those partials and writes s_t = amax / 2688 (6 * 448), or 1
 // for an all-zero tensor.
+// Read-only, so each lane keeps kAmaxUnroll loads in flight and the pass
+// leaves one partial per kThreads * kAmaxUnroll chunks.
+constexpr int kAmaxUnroll = 16;
+
 template <bool kFlat>
 __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint16_t* __restrict__ x,
                                                            uint8_t* __restrict__ codes, Geom g) {
   __shared__ uint32_t red[kThreads / 64];
-  const uint32_t stride = gridDim.x * kThreads;
   uint32_t m = 0;
-  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < g.n; base += kUnroll * stride) {
-    u32x4_t d[kUnroll];
+  const uint32_t base = blockIdx.x * (kThreads * kAmaxUnroll) + threadIdx.x;
+  u32x4_t d[kAmaxUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      uint32_t v = base + u * stride;
-      d[u] = u32x4_t{0u, 0u, 0u, 0u};
-      if (v < g.n) {
-        int64_t xo, co, so;
-        locate<kFlat, 16>(g, v, xo, co, so);
-        d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo));
-      }
+  for (int u = 0; u < kAmaxUnroll; ++u) {
+    uint32_t v = base + u * kThreads;
+    d[u] = u32x4_t{0u, 0u, 0u, 0u};
+    if (v < g.n) {
+      int64_t xo, co, so;
+      locate<kFlat, 16>(g, v, xo, co, so);
+      d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo));
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) m = max(m, absmax8_bf16(d[u]));
   }
+#pragma unroll
+  for (int u = 0; u < kAmaxUnroll; ++u) m = max(m, absmax8_bf16(d[u]));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -108,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint16_t* __res
     uint32_t r = red[0];
     for (int i = 1; i < kThreads / 64; ++i) r = max(r, red[i]);
     int64_t xo, co, so;
-    locate<kFlat, 16>(g, blockIdx.x * kThreads, xo, co, so);
+    locate<kFlat, 16>(g, blockIdx.x * (kThreads * kAmaxUnroll), xo, co, so);
     *reinterpret_cast<uint32_t*>(codes + co) = r << 16;
   }
 }
@@ -121,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void nv_tensor_scale_kernel(const uint8_t
   uint32_t m = 0;
   for (uint32_t i = threadIdx.x; i < nparts; i += kThreads) {
     int64_t xo, co, so;
-    locate<kFlat, 16>(g, i * kThreads, xo, co, so);
+    locate<kFlat, 16>(g, i * (kThreads * kAmaxUnroll), xo, co, so);
     m = max(m, *reinterpret_cast<const uint32_t*>(codes + co));
   }
 #pragma unroll
@@ -144,11 +153,12 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(const uint16_t* __re
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
                                                             const float* __restrict__ ts, Geom g) {
-  const uint32_t stride = gridDim.x * kThreads;
   const bool leader = (threadIdx.x & 1) == 0;
   const float s_t = *ts;
   const float d6 = 6.0f * s_t;
-  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < g.n; base += kUnroll * stride) {
+  const uint32_t base = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  constexpr uint32_t stride = kThreads;
+  {
     u32x4_t d[kUnroll];
     int64_t xo[kUnroll], co[kUnroll], so[kUnroll];
 #pragma unroll
@@ -180,20 +190,20 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(const uint16_t* __re
         w = cvt8_f32(y, 1.0f);
         byte = sb;
         if (kRazer) {
-          // selector = [sum of gains of negative elements > that of positive ones]
-          int32_t g8[8];
-          int32_t dsum = 0;
+          // selector = [gains of negative elements exceed those of positive ones]
+          float sg[8];
+          float dsum = 0.0f;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            g8[k] = razer_gain(y[k]);
-            dsum += (__float_as_uint(y[k]) >> 31) ? g8[k] : -g8[k];
+            sg[k] = razer_signed_gain(y[k]);
+            dsum -= sg[k];
           }
-          dsum += (int32_t)dpp_xor1((uint32_t)dsum);
-          const uint32_t sel = dsum > 0 ? 1u : 0u;
+          dsum += dpp_xor1f(dsum);
+          const uint32_t sel = dsum > 0.0f ? 1u : 0u;
+          const float flip = sel ? -1.0f : 1.0f;  // special value's sign
           uint32_t spm = 0;
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            spm |= (g8[k] > 0 && (__float_as_uint(y[k]) >> 31) == sel) ? (8u << (4 * k)) : 0u;
+          for (int k = 0; k < 8; ++k) spm |= (sg[k] * flip > 0.0f) ? (8u << (4 * k)) : 0u;
           w = canonical_zero(w);
           w = (w & ~((spm >> 3) * 0xFu)) | spm;
           byte |= sel << 7;
@@ -210,8 +220,9 @@ template <bool kFlat>
 __global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __restrict__ codes,
                                                               const uint8_t* __restrict__ scales,
                                                               uint16_t* __restrict__ out, Geom g) {
-  const uint32_t stride = gridDim.x * kThreads;
-  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < g.n; base += kUnroll * stride) {
+  const uint32_t base = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  constexpr uint32_t stride = kThreads;
+  {
     uint32_t w[kUnroll], sb[kUnroll];
     int64_t xo[kUnroll], co[kUnroll], so[kUnroll];
 #pragma unroll
@@ -243,9 +254,10 @@ __global__ __launch_bounds__(kThreads) void nv_dequant_kernel(const uint8_t* __r
                                                               const uint8_t* __restrict__ scales,
                                                               const float* __restrict__ ts,
                                                               uint16_t* __restrict__ out, Geom g) {
-  const uint32_t stride = gridDim.x * kThreads;
   const float s_t = *ts;
-  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < g.n; base += kUnroll * stride) {
+  const uint32_t base = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  constexpr uint32_t stride = kThreads;
+  {
     uint32_t w[kUnroll], sb[kUnroll];
     int64_t xo[kUnroll], co[kUnroll], so[kUnroll];
 #pragma unroll
@@ -291,10 +303,10 @@ __global__ __launch_bounds__(kThreads) void nv_dequant_kernel(const uint8_t* __r
 }
 
 // --------------------------------------------------------------- launchers ----
+// One work-group per kThreads * kUnroll chunks (n < 2^31, so this fits).
 static inline int grid_for(uint32_t n) {
   uint64_t per = (uint64_t)kThreads * kUnroll;
   uint64_t gsz = (n + per - 1) / per;
-  if (gsz > (uint64_t)kMaxGrid) gsz = kMaxGrid;
   return (int)(gsz ? gsz : 1);
 }
 
@@ -336,14 +348,13 @@ void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float* t
   const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2;
   auto xp = static_cast<const uint16_t*>(x);
   auto cp = static_cast<uint8_t*>(codes);
-  uint64_t per = (uint64_t)kThreads * kUnroll;
-  uint64_t grid = (g.n + per - 1) / per;
-  if (grid > (uint64_t)kAmaxGrid) grid = kAmaxGrid;
+  const uint64_t per = (uint64_t)kThreads * kAmaxUnroll;
+  const int grid = (int)((g.n + per - 1) / per);
   if (flat) {
-    FP4_LAUNCH((nv_amax_kernel<true>), (int)grid, st, xp, cp, g);
+    FP4_LAUNCH((nv_amax_kernel<true>), grid, st, xp, cp, g);
     FP4_LAUNCH((nv_tensor_scale_kernel<true>), 1, st, cp, (uint32_t)grid, g, ts);
   } else {
-    FP4_LAUNCH((nv_amax_kernel<false>), (int)grid, st, xp, cp, g);
+    FP4_LAUNCH((nv_amax_kernel<false>), grid, st, xp, cp, g);
     FP4_LAUNCH((nv_tensor_scale_kernel<false>), 1, st, cp, (uint32_t)grid, g, ts);
   }
 }

@@ -42,6 +42,7 @@ constexpr float kInvSqrt32 = 0.17677669529663688f;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void widen8(u32x4_t d, float* v) {
   v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
@@ -75,16 +76,25 @@ __device__ __forceinline__ uint32_t out_index_of_row(uint32_t m) {
 
 // Constant A operands: lane l holds A[m = l % 32][kk = 8 (l / 32) + j]; for
 // the first MFMA kk stands for element 16 (kk / 8) + kk % 8, for the second
-// 16 (kk / 8) + 8 + kk % 8 (matching the B halves each lane loads).
+// 16 (kk / 8) + 8 + kk % 8 (matching the B halves each lane loads). So the 16
+// operand entries of lane l are H[tau(l % 32)][k0 + j], k0 = 16 (l / 32),
+// j = 0..15, with sign parity(row & (k0 + j)) = parity(row & k0) ^
+// parity(row & j); bit j of the Walsh mask W(row & 15) is parity(row & j).
 __device__ __forceinline__ void hadamard_operands(bf16x8_t& a0, bf16x8_t& a1) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t row = out_index_of_row(lane & 31u);
-  const uint32_t k0 = 16u * (lane >> 5);
+  uint32_t m = ((row & 1u) ? 0xAAAAu : 0u) ^ ((row & 2u) ? 0xCCCCu : 0u) ^
+               ((row & 4u) ? 0xF0F0u : 0u) ^ ((row & 8u) ? 0xFF00u : 0u);
+  if ((lane >> 5) & (row >> 4)) m ^= 0xFFFFu;
+  u32x4_t v0, v1;
+  uint32_t w[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    a0[j] = (__popc(row & (k0 + j)) & 1) ? (__bf16)-1.0f : (__bf16)1.0f;
-    a1[j] = (__popc(row & (k0 + 8 + j)) & 1) ? (__bf16)-1.0f : (__bf16)1.0f;
-  }
+  for (int i = 0; i < 8; ++i)  // bf16 pair: +-1 = 0x3F80 with the sign bit from the mask
+    w[i] = 0x3F803F80u | (((m >> (2 * i)) & 1u) << 15) | (((m >> (2 * i + 1)) & 1u) << 31);
+  v0 = u32x4_t{w[0], w[1], w[2], w[3]};
+  v1 = u32x4_t{w[4], w[5], w[6], w[7]};
+  a0 = __builtin_bit_cast(bf16x8_t, v0);
+  a1 = __builtin_bit_cast(bf16x8_t, v1);
 }
 
 // y[0..15] = (H x)[16h .. 16h+15] / sqrt(32) for this lane's block, from the
@@ -170,9 +180,16 @@ struct RotGeom {
 };
 
 // ===================== streaming kernels (no permutation) ===================
-// MFMA: a wave owns a tile of 32 consecutive blocks (row-major block order);
-// tiles are dealt to waves grid-stride, kTiles per trip.
-constexpr int kTiles = 2;
+// MFMA: a wave owns a tile of 32 consecutive blocks (row-major block order).
+// Each work-group makes one pass over kWaves * kTiles consecutive tiles; wave w
+// takes tiles base + u * kWaves + w, so at each u the work-group covers one
+// contiguous stretch of input, codes and scales.
+#ifndef FP4_TILES
+#define FP4_TILES 1
+#endif
+constexpr int kTiles = FP4_TILES;
+
+constexpr int kWaves = kThreads / 64;
 
 template <bool kFlat, bool kHad, bool kFloor, bool kRot>
 __global__ __launch_bounds__(kThreads) void mx_rotq_stream_mfma_kernel(
@@ -181,126 +198,146 @@ __global__ __launch_bounds__(kThreads) void mx_rotq_stream_mfma_kernel(
   bf16x8_t a0, a1;
   hadamard_operands(a0, a1);
   const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
-  const uint32_t wave = (blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const uint32_t nwaves = (gridDim.x * kThreads) >> 6;
+  const uint32_t tile0 = blockIdx.x * (kWaves * kTiles) + (threadIdx.x >> 6);
   const uint32_t ntiles = (g.nblk + 31u) >> 5;
-  for (uint32_t t0 = wave; t0 < ntiles; t0 += kTiles * nwaves) {
-    u32x4_t lo[kTiles], hi[kTiles];
-    int64_t xo[kTiles], co[kTiles], so[kTiles], ro[kTiles];
-    bool ok[kTiles];
+  u32x4_t lo[kTiles], hi[kTiles];
+  int64_t xo[kTiles], co[kTiles], so[kTiles], ro[kTiles];
+  bool ok[kTiles];
 #pragma unroll
-    for (int u = 0; u < kTiles; ++u) {
-      const uint32_t b = (t0 + u * nwaves) * 32u + n;
-      ok[u] = (t0 + u * nwaves) < ntiles && b < g.nblk;
-      lo[u] = u32x4_t{0u, 0u, 0u, 0u};
-      hi[u] = lo[u];
-      if (ok[u]) {
-        uint32_t r = kFlat ? 0u : b / (uint32_t)g.bpr;
-        uint32_t cb = kFlat ? b : b - r * (uint32_t)g.bpr;
-        xo[u] = r * g.ld_x + 32 * (int64_t)cb + 16 * h;
-        co[u] = r * g.ld_c + 16 * (int64_t)cb + 8 * h;
-        so[u] = r * g.ld_s + cb;
-        ro[u] = r * g.ld_rot + 32 * (int64_t)cb + 16 * h;
-        const u32x4_t* p = reinterpret_cast<const u32x4_t*>(x + xo[u]);
-        lo[u] = __builtin_nontemporal_load(p);
-        hi[u] = __builtin_nontemporal_load(p + 1);
-      }
+  for (int u = 0; u < kTiles; ++u) {
+    const uint32_t tile = tile0 + u * kWaves;
+    const uint32_t b = tile * 32u + n;
+    ok[u] = tile < ntiles && b < g.nblk;
+    lo[u] = u32x4_t{0u, 0u, 0u, 0u};
+    hi[u] = lo[u];
+    if (ok[u]) {
+      uint32_t r = kFlat ? 0u : b / (uint32_t)g.bpr;
+      uint32_t cb = kFlat ? b : b - r * (uint32_t)g.bpr;
+      xo[u] = r * g.ld_x + 32 * (int64_t)cb + 16 * h;
+      co[u] = r * g.ld_c + 16 * (int64_t)cb + 8 * h;
+      so[u] = r * g.ld_s + cb;
+      ro[u] = r * g.ld_rot + 32 * (int64_t)cb + 16 * h;
+      const u32x4_t* p = reinterpret_cast<const u32x4_t*>(x + xo[u]);
+      lo[u] = __builtin_nontemporal_load(p);
+      hi[u] = __builtin_nontemporal_load(p + 1);
     }
+  }
 #pragma unroll
-    for (int u = 0; u < kTiles; ++u) {
-      if ((t0 + u * nwaves) >= ntiles) break;  // uniform across the wave
-      float y[16];
-      if (kHad) {
-        hadamard_mfma(a0, a1, lo[u], hi[u], y);
-      } else {
-        widen8(lo[u], y);
-        widen8(hi[u], y + 8);
-      }
-      uint32_t w0, w1, byte;
-      mx_quant16_pair<kFloor>(y, w0, w1, byte);
-      if (ok[u]) {
-        uint32_t* cp = reinterpret_cast<uint32_t*>(codes + co[u]);
-        __builtin_nontemporal_store(w0, cp);
-        __builtin_nontemporal_store(w1, cp + 1);
-        if (h == 0) scales[so[u]] = (uint8_t)byte;
-        if (kRot) {
-          store_rot8(rot + ro[u], y);
-          store_rot8(rot + ro[u] + 8, y + 8);
-        }
+  for (int u = 0; u < kTiles; ++u) {
+    if (tile0 + u * kWaves >= ntiles) break;  // uniform across the wave
+    float y[16];
+    if (kHad) {
+      hadamard_mfma(a0, a1, lo[u], hi[u], y);
+    } else {
+      widen8(lo[u], y);
+      widen8(hi[u], y + 8);
+    }
+    uint32_t w0, w1, byte;
+    mx_quant16_pair<kFloor>(y, w0, w1, byte);
+    if (ok[u]) {
+      uint32_t* cp = reinterpret_cast<uint32_t*>(codes + co[u]);
+      __builtin_nontemporal_store(w0, cp);
+      __builtin_nontemporal_store(w1, cp + 1);
+      if (h == 0) scales[so[u]] = (uint8_t)byte;
+      if (kRot) {
+        store_rot8(rot + ro[u], y);
+        store_rot8(rot + ro[u] + 8, y + 8);
       }
     }
   }
 }
 
-// Butterfly: one 16-byte chunk of eight elements per lane, four lanes per block.
+// Butterfly: one 16-byte chunk of eight elements per lane, four lanes per
+// block; each work-group makes one pass over kThreads * 4 consecutive chunks.
 template <bool kFlat, bool kHad, bool kFloor, bool kRot>
 __global__ __launch_bounds__(kThreads) void mx_rotq_stream_bfly_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ rot, RotGeom g) {
-  const uint32_t stride = gridDim.x * kThreads;
   const uint32_t q = threadIdx.x & 3u;
   const uint32_t n = g.nblk * 4u;
   constexpr int U = 4;
-  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < n; base += U * stride) {
-    u32x4_t d[U];
-    int64_t xo[U], co[U], so[U], ro[U];
+  const uint32_t base = blockIdx.x * (kThreads * U) + threadIdx.x;
+  u32x4_t d[U];
+  int64_t xo[U], co[U], so[U], ro[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint32_t v = base + u * stride;
-      if (v < n) {
-        uint32_t cpr = 4u * (uint32_t)g.bpr;
-        uint32_t r = kFlat ? 0u : v / cpr;
-        uint32_t c = kFlat ? v : v - r * cpr;
-        xo[u] = r * g.ld_x + 8 * (int64_t)c;
-        co[u] = r * g.ld_c + 4 * (int64_t)c;
-        so[u] = r * g.ld_s + c / 4;
-        ro[u] = r * g.ld_rot + 8 * (int64_t)c;
-        d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo[u]));
-      }
+  for (int u = 0; u < U; ++u) {
+    uint32_t v = base + u * kThreads;
+    if (v < n) {
+      uint32_t cpr = 4u * (uint32_t)g.bpr;
+      uint32_t r = kFlat ? 0u : v / cpr;
+      uint32_t c = kFlat ? v : v - r * cpr;
+      xo[u] = r * g.ld_x + 8 * (int64_t)c;
+      co[u] = r * g.ld_c + 4 * (int64_t)c;
+      so[u] = r * g.ld_s + c / 4;
+      ro[u] = r * g.ld_rot + 8 * (int64_t)c;
+      d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo[u]));
     }
+  }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint32_t v = base + u * stride;
-      if (v >= n) continue;
-      float y[8];
-      widen8(d[u], y);
-      if (kHad) hadamard_butterfly(y, q);
-      uint32_t w, byte;
-      mx_quant8_quad<kFloor>(y, w, byte);
-      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + co[u]));
-      if (q == 0) scales[so[u]] = (uint8_t)byte;
-      if (kRot) store_rot8(rot + ro[u], y);
-    }
+  for (int u = 0; u < U; ++u) {
+    uint32_t v = base + u * kThreads;
+    if (v >= n) continue;
+    float y[8];
+    widen8(d[u], y);
+    if (kHad) hadamard_butterfly(y, q);
+    uint32_t w, byte;
+    mx_quant8_quad<kFloor>(y, w, byte);
+    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + co[u]));
+    if (q == 0) scales[so[u]] = (uint8_t)byte;
+    if (kRot) store_rot8(rot + ro[u], y);
   }
 }
 
 // ================== permuting kernels (one row at a time, LDS) ==============
 // Dynamic LDS: row[cols] bf16 followed by perm[cols] uint16 (entries clamped
-// to cols - 1, so no gather leaves the row).
+// to cols - 1, so no gather leaves the row). A work-group walks rows
+// r0, r0 + G, r0 + 2G, ... (G = grid size). The global loads of the row kDepth
+// steps ahead are issued into registers before the current row is processed,
+// so kDepth rows per work-group are in flight; kCpl = 16-byte chunks per lane
+// per row (cols <= 8 * kThreads * kCpl).
 constexpr int kMaxChunksPerLane = (int)(kMaxPermCols / 8 / kThreads);  // 8
 
-__device__ __forceinline__ void stage_perm(const int32_t* __restrict__ perm, uint16_t* sperm,
-                                           int32_t cols) {
+// Stage perm into LDS as uint16 (clamped to the row) and return the largest
+// run length G in {8, 4, 2, 1} such that perm maps every aligned run of G
+// positions onto an aligned run of G consecutive channels (same for the whole
+// work-group, so the caller's branch on it is uniform).
+__device__ __forceinline__ int stage_perm(const int32_t* __restrict__ perm, uint16_t* sperm,
+                                          int32_t cols) {
   const int32_t cmax = cols - 1;
   for (int32_t j = threadIdx.x; j < cols; j += kThreads) {
     int32_t p = perm[j];
     p = p < 0 ? 0 : (p > cmax ? cmax : p);
     sperm[j] = (uint16_t)p;
   }
+  __syncthreads();
+  int ok2 = 1, ok4 = 1, ok8 = 1;
+  for (int32_t j = threadIdx.x; j < cols; j += kThreads) {
+    const uint32_t p = sperm[j];
+    const uint32_t b2 = sperm[j & ~1], b4 = sperm[j & ~3], b8 = sperm[j & ~7];
+    ok2 &= (p == b2 + (uint32_t)(j & 1)) && (b2 % 2u == 0u);
+    ok4 &= (p == b4 + (uint32_t)(j & 3)) && (b4 % 4u == 0u);
+    ok8 &= (p == b8 + (uint32_t)(j & 7)) && (b8 % 8u == 0u);
+  }
+  if (__syncthreads_and(ok8)) return 8;
+  if (__syncthreads_and(ok4)) return 4;
+  if (__syncthreads_and(ok2)) return 2;
+  return 1;
 }
 
+template <int kCpl>
 __device__ __forceinline__ void load_row(const uint16_t* __restrict__ src, int32_t cpr,
                                          u32x4_t* pre) {
 #pragma unroll
-  for (int i = 0; i < kMaxChunksPerLane; ++i) {
+  for (int i = 0; i < kCpl; ++i) {
     int32_t c = threadIdx.x + i * kThreads;
     if (c < cpr) pre[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src) + c);
   }
 }
 
+template <int kCpl>
 __device__ __forceinline__ void put_row(uint16_t* srow, int32_t cpr, const u32x4_t* pre) {
 #pragma unroll
-  for (int i = 0; i < kMaxChunksPerLane; ++i) {
+  for (int i = 0; i < kCpl; ++i) {
     int32_t c = threadIdx.x + i * kThreads;
     if (c < cpr) reinterpret_cast<u32x4_t*>(srow)[c] = pre[i];
   }
@@ -316,92 +353,148 @@ __device__ __forceinline__ u32x4_t gather8(const uint16_t* srow, u32x4_t id) {
   return r;
 }
 
+// The 16 gathered bf16 x'[e0 .. e0+15] (e0 a multiple of 16), as the MFMA's two
+// B halves, when perm is made of aligned runs of G channels: one LDS read of
+// 2G bytes per run.
+template <int G>
+__device__ __forceinline__ void gather16(const uint16_t* srow, const uint16_t* sperm, int32_t e0,
+                                         u32x4_t& lo, u32x4_t& hi) {
+  if constexpr (G == 1) {
+    const u32x4_t* ip = reinterpret_cast<const u32x4_t*>(sperm + e0);
+    lo = gather8(srow, ip[0]);
+    hi = gather8(srow, ip[1]);
+  } else if constexpr (G == 2) {
+    const u32x4_t* ip = reinterpret_cast<const u32x4_t*>(sperm + e0);
+    const u32x4_t i0 = ip[0], i1 = ip[1];
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(srow);
+    lo.x = w[(i0.x & 0xFFFFu) >> 1]; lo.y = w[(i0.y & 0xFFFFu) >> 1];
+    lo.z = w[(i0.z & 0xFFFFu) >> 1]; lo.w = w[(i0.w & 0xFFFFu) >> 1];
+    hi.x = w[(i1.x & 0xFFFFu) >> 1]; hi.y = w[(i1.y & 0xFFFFu) >> 1];
+    hi.z = w[(i1.z & 0xFFFFu) >> 1]; hi.w = w[(i1.w & 0xFFFFu) >> 1];
+  } else if constexpr (G == 4) {
+    const u32x2_t* w = reinterpret_cast<const u32x2_t*>(srow);
+    const u32x2_t a = w[sperm[e0] >> 2], b = w[sperm[e0 + 4] >> 2];
+    const u32x2_t c = w[sperm[e0 + 8] >> 2], d = w[sperm[e0 + 12] >> 2];
+    lo = u32x4_t{a.x, a.y, b.x, b.y};
+    hi = u32x4_t{c.x, c.y, d.x, d.y};
+  } else {
+    const u32x4_t* w = reinterpret_cast<const u32x4_t*>(srow);
+    lo = w[sperm[e0] >> 3];
+    hi = w[sperm[e0 + 8] >> 3];
+  }
+}
+
+// Permute + Hadamard + quantize one staged row (MFMA: a wave takes tiles of 32
+// blocks, lane (n, h) gathers elements 16h..16h+15 of block n).
+template <int G, bool kHad, bool kFloor, bool kRot>
+__device__ __forceinline__ void rotq_row_mfma(const uint16_t* srow, const uint16_t* sperm,
+                                              const bf16x8_t& a0, const bf16x8_t& a1, int32_t r,
+                                              uint8_t* __restrict__ codes,
+                                              uint8_t* __restrict__ scales,
+                                              float* __restrict__ rot, const RotGeom& g) {
+  const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
+  const int32_t ntiles = (g.bpr + 31) / 32;
+  for (int32_t t = threadIdx.x >> 6; t < ntiles; t += kWaves) {
+    const int32_t b = 32 * t + (int32_t)n;
+    const bool ok = b < g.bpr;
+    u32x4_t lo = {0u, 0u, 0u, 0u}, hi = lo;
+    if (ok) gather16<G>(srow, sperm, 32 * b + 16 * (int32_t)h, lo, hi);
+    float y[16];
+    if (kHad) {
+      hadamard_mfma(a0, a1, lo, hi, y);
+    } else {
+      widen8(lo, y);
+      widen8(hi, y + 8);
+    }
+    uint32_t w0, w1, byte;
+    mx_quant16_pair<kFloor>(y, w0, w1, byte);
+    if (ok) {
+      uint32_t* cp = reinterpret_cast<uint32_t*>(codes + r * g.ld_c + 16 * (int64_t)b + 8 * h);
+      __builtin_nontemporal_store(w0, cp);
+      __builtin_nontemporal_store(w1, cp + 1);
+      if (h == 0) scales[r * g.ld_s + b] = (uint8_t)byte;
+      if (kRot) {
+        float* rp = rot + r * g.ld_rot + 32 * (int64_t)b + 16 * h;
+        store_rot8(rp, y);
+        store_rot8(rp + 8, y + 8);
+      }
+    }
+  }
+}
+
+// Same row, butterfly implementation: lane takes 16-byte chunks c = t + i * kThreads.
 template <bool kHad, bool kFloor, bool kRot>
-__global__ __launch_bounds__(kThreads) void mx_rotq_perm_mfma_kernel(
+__device__ __forceinline__ void rotq_row_bfly(const uint16_t* srow, const uint16_t* sperm,
+                                              int32_t r, uint8_t* __restrict__ codes,
+                                              uint8_t* __restrict__ scales,
+                                              float* __restrict__ rot, const RotGeom& g) {
+  const uint32_t q = threadIdx.x & 3u;
+  const int32_t cpr = g.cols / 8;
+  for (int32_t c = threadIdx.x; c < cpr; c += kThreads) {
+    float y[8];
+    widen8(gather8(srow, reinterpret_cast<const u32x4_t*>(sperm)[c]), y);
+    if (kHad) hadamard_butterfly(y, q);
+    uint32_t w, byte;
+    mx_quant8_quad<kFloor>(y, w, byte);
+    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + r * g.ld_c + 4 * (int64_t)c));
+    if (q == 0) scales[r * g.ld_s + c / 4] = (uint8_t)byte;
+    if (kRot) store_rot8(rot + r * g.ld_rot + 8 * (int64_t)c, y);
+  }
+}
+
+template <int G, int kCpl, int kDepth, bool kHad, bool kFloor, bool kRot>
+__device__ __forceinline__ void perm_rows(const uint16_t* __restrict__ x, uint16_t* srow,
+                                          const uint16_t* sperm, const bf16x8_t& a0,
+                                          const bf16x8_t& a1, uint8_t* __restrict__ codes,
+                                          uint8_t* __restrict__ scales, float* __restrict__ rot,
+                                          const RotGeom& g) {
+  const int32_t cpr = g.cols / 8;
+  const int32_t G_ = gridDim.x;
+  u32x4_t pre[kDepth][kCpl];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    const int32_t rr = (int32_t)blockIdx.x + d * G_;
+    if (rr < g.rows) load_row<kCpl>(x + rr * g.ld_x, cpr, pre[d]);
+  }
+  for (int32_t r = blockIdx.x; r < g.rows; r += kDepth * G_) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int32_t rr = r + d * G_;
+      if (rr >= g.rows) break;  // uniform across the work-group
+      __syncthreads();          // the previous row's gathers are done
+      put_row<kCpl>(srow, cpr, pre[d]);
+      __syncthreads();
+      const int32_t rn = rr + kDepth * G_;
+      if (rn < g.rows) load_row<kCpl>(x + rn * g.ld_x, cpr, pre[d]);
+      if constexpr (kUseMfma)
+        rotq_row_mfma<G, kHad, kFloor, kRot>(srow, sperm, a0, a1, rr, codes, scales, rot, g);
+      else
+        rotq_row_bfly<kHad, kFloor, kRot>(srow, sperm, rr, codes, scales, rot, g);
+    }
+  }
+}
+
+template <int kCpl, int kDepth, bool kHad, bool kFloor, bool kRot>
+__global__ __launch_bounds__(kThreads) void mx_rotq_perm_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ rot, RotGeom g) {
   extern __shared__ uint16_t smem[];
   uint16_t* srow = smem;
   uint16_t* sperm = smem + g.cols;
   bf16x8_t a0, a1;
-  hadamard_operands(a0, a1);
-  stage_perm(perm, sperm, g.cols);
-  const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
-  const int32_t wave = threadIdx.x >> 6;
-  const int32_t cpr = g.cols / 8;
-  const int32_t ntiles = (g.bpr + 31) / 32;
-  u32x4_t pre[kMaxChunksPerLane];
-  int32_t r = blockIdx.x;
-  if (r < g.rows) load_row(x + r * g.ld_x, cpr, pre);
-  for (; r < g.rows; r += gridDim.x) {
-    __syncthreads();  // the previous row's gathers are done (and sperm is visible)
-    put_row(srow, cpr, pre);
-    __syncthreads();
-    if (r + (int32_t)gridDim.x < g.rows) load_row(x + (r + gridDim.x) * g.ld_x, cpr, pre);
-    for (int32_t t = wave; t < ntiles; t += kThreads / 64) {
-      const int32_t b = 32 * t + (int32_t)n;
-      const bool ok = b < g.bpr;
-      u32x4_t lo = {0u, 0u, 0u, 0u}, hi = lo;
-      if (ok) {
-        const u32x4_t* ip = reinterpret_cast<const u32x4_t*>(sperm + 32 * b + 16 * h);
-        lo = gather8(srow, ip[0]);
-        hi = gather8(srow, ip[1]);
-      }
-      float y[16];
-      if (kHad) {
-        hadamard_mfma(a0, a1, lo, hi, y);
-      } else {
-        widen8(lo, y);
-        widen8(hi, y + 8);
-      }
-      uint32_t w0, w1, byte;
-      mx_quant16_pair<kFloor>(y, w0, w1, byte);
-      if (ok) {
-        uint32_t* cp = reinterpret_cast<uint32_t*>(codes + r * g.ld_c + 16 * (int64_t)b + 8 * h);
-        __builtin_nontemporal_store(w0, cp);
-        __builtin_nontemporal_store(w1, cp + 1);
-        if (h == 0) scales[r * g.ld_s + b] = (uint8_t)byte;
-        if (kRot) {
-          float* rp = rot + r * g.ld_rot + 32 * (int64_t)b + 16 * h;
-          store_rot8(rp, y);
-          store_rot8(rp + 8, y + 8);
-        }
-      }
-    }
-  }
-}
-
-template <bool kHad, bool kFloor, bool kRot>
-__global__ __launch_bounds__(kThreads) void mx_rotq_perm_bfly_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ rot, RotGeom g) {
-  extern __shared__ uint16_t smem[];
-  uint16_t* srow = smem;
-  uint16_t* sperm = smem + g.cols;
-  stage_perm(perm, sperm, g.cols);
-  const uint32_t q = threadIdx.x & 3u;
-  const int32_t cpr = g.cols / 8;
-  u32x4_t pre[kMaxChunksPerLane];
-  int32_t r = blockIdx.x;
-  if (r < g.rows) load_row(x + r * g.ld_x, cpr, pre);
-  for (; r < g.rows; r += gridDim.x) {
-    __syncthreads();
-    put_row(srow, cpr, pre);
-    __syncthreads();
-    if (r + (int32_t)gridDim.x < g.rows) load_row(x + (r + gridDim.x) * g.ld_x, cpr, pre);
-#pragma unroll
-    for (int i = 0; i < kMaxChunksPerLane; ++i) {
-      int32_t c = threadIdx.x + i * kThreads;
-      if (c >= cpr) continue;
-      float y[8];
-      widen8(gather8(srow, reinterpret_cast<const u32x4_t*>(sperm)[c]), y);
-      if (kHad) hadamard_butterfly(y, q);
-      uint32_t w, byte;
-      mx_quant8_quad<kFloor>(y, w, byte);
-      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + r * g.ld_c + 4 * (int64_t)c));
-      if (q == 0) scales[r * g.ld_s + c / 4] = (uint8_t)byte;
-      if (kRot) store_rot8(rot + r * g.ld_rot + 8 * (int64_t)c, y);
-    }
+  if constexpr (kUseMfma) hadamard_operands(a0, a1);
+  const int run = stage_perm(perm, sperm, g.cols);
+  if constexpr (kUseMfma) {
+    if (run == 8)
+      perm_rows<8, kCpl, kDepth, kHad, kFloor, kRot>(x, srow, sperm, a0, a1, codes, scales, rot, g);
+    else if (run == 4)
+      perm_rows<4, kCpl, kDepth, kHad, kFloor, kRot>(x, srow, sperm, a0, a1, codes, scales, rot, g);
+    else if (run == 2)
+      perm_rows<2, kCpl, kDepth, kHad, kFloor, kRot>(x, srow, sperm, a0, a1, codes, scales, rot, g);
+    else
+      perm_rows<1, kCpl, kDepth, kHad, kFloor, kRot>(x, srow, sperm, a0, a1, codes, scales, rot, g);
+  } else {
+    perm_rows<1, kCpl, kDepth, kHad, kFloor, kRot>(x, srow, sperm, a0, a1, codes, scales, rot, g);
   }
 }
 
@@ -417,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void mx_dequant_unrotate_kernel(
   uint16_t* sperm = smem + g.cols;
   const uint32_t q = threadIdx.x & 3u;
   const int32_t cpr = g.cols / 8;
-  if (kPerm) stage_perm(perm, sperm, g.cols);
+  if (kPerm) (void)stage_perm(perm, sperm, g.cols);
   for (int32_t r = blockIdx.x; r < g.rows; r += gridDim.x) {
     if (kPerm) __syncthreads();  // previous row copied out, indices visible
     for (int32_t c = threadIdx.x; c < cpr; c += kThreads) {
@@ -504,23 +597,30 @@ static RotGeom rot_geom(const Shape& s, int64_t ld_rot) {
 
 static int perm_grid(int64_t rows) { return (int)(rows < kPermGrid ? rows : kPermGrid); }
 
+template <int kCpl, int kDepth, bool kHad, bool kFloor, bool kRot>
+static void perm_launch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
+                        uint8_t* sc, float* rot, const RotGeom& g, hipStream_t st) {
+  const int grid = perm_grid(s.rows);
+  const size_t lds = (size_t)4 * s.cols;
+  hipLaunchKernelGGL((mx_rotq_perm_kernel<kCpl, kDepth, kHad, kFloor, kRot>), dim3(grid),
+                     dim3(kThreads), lds, st, x, perm, c, sc, rot, g);
+}
+
 template <bool kHad, bool kFloor, bool kRot>
 static void rotq_dispatch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
                           uint8_t* sc, float* rot, const RotGeom& g, bool flat, hipStream_t st) {
   if (perm) {
-    size_t lds = (size_t)4 * s.cols;
-    if (kUseMfma)
-      hipLaunchKernelGGL((mx_rotq_perm_mfma_kernel<kHad, kFloor, kRot>), dim3(perm_grid(s.rows)),
-                         dim3(kThreads), lds, st, x, perm, c, sc, rot, g);
-    else
-      hipLaunchKernelGGL((mx_rotq_perm_bfly_kernel<kHad, kFloor, kRot>), dim3(perm_grid(s.rows)),
-                         dim3(kThreads), lds, st, x, perm, c, sc, rot, g);
+    const int64_t cpl = (s.cols / 8 + kThreads - 1) / kThreads;
+    // chunks per lane and prefetch depth: about 32 VGPRs of rows in flight
+    if (cpl <= 1) perm_launch<1, 4, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
+    else if (cpl <= 2) perm_launch<2, 4, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
+    else if (cpl <= 4) perm_launch<4, 2, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
+    else perm_launch<kMaxChunksPerLane, 1, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
     return;
   }
-  if (kUseMfma) {
-    uint64_t waves = ((uint64_t)g.nblk + 31) / 32;
-    uint64_t grid = (waves + (kThreads / 64) * kTiles - 1) / ((kThreads / 64) * kTiles);
-    if (grid > (uint64_t)kMaxGrid) grid = kMaxGrid;
+  if constexpr (kUseMfma) {
+    const uint64_t tiles = ((uint64_t)g.nblk + 31) / 32;
+    const uint64_t grid = (tiles + kWaves * kTiles - 1) / (kWaves * kTiles);
     if (flat)
       hipLaunchKernelGGL((mx_rotq_stream_mfma_kernel<true, kHad, kFloor, kRot>), dim3((int)grid),
                          dim3(kThreads), 0, st, x, c, sc, rot, g);
@@ -528,9 +628,8 @@ static void rotq_dispatch(const Shape& s, const int32_t* perm, const uint16_t* x
       hipLaunchKernelGGL((mx_rotq_stream_mfma_kernel<false, kHad, kFloor, kRot>), dim3((int)grid),
                          dim3(kThreads), 0, st, x, c, sc, rot, g);
   } else {
-    uint64_t chunks = (uint64_t)g.nblk * 4;
-    uint64_t grid = (chunks + kThreads * 4 - 1) / (kThreads * 4);
-    if (grid > (uint64_t)kMaxGrid) grid = kMaxGrid;
+    const uint64_t chunks = (uint64_t)g.nblk * 4;
+    const uint64_t grid = (chunks + kThreads * 4 - 1) / (kThreads * 4);
     if (flat)
       hipLaunchKernelGGL((mx_rotq_stream_bfly_kernel<true, kHad, kFloor, kRot>), dim3((int)grid),
                          dim3(kThreads), 0, st, x, c, sc, rot, g);

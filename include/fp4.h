@@ -155,7 +155,9 @@ int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int6
  *
  *  perm         NULL (identity) or device int32[cols], a permutation of
  *               0..cols-1 (entries are clamped to cols-1); requires
- *               cols <= 16384
+ *               cols <= 16384. A permutation made of aligned runs of 2, 4 or
+ *               8 consecutive channels (fp4_build_permutation with group > 1)
+ *               is detected and gathered with 4-, 8- or 16-byte LDS reads
  *  hadamard     32 or 0 (none)
  *  format       FP4_MXFP4 (NVFP4 returns FP4_ERR_UNSUPPORTED)
  *  rotated_out  NULL, or device fp32 [rows, ld_rot] receiving y; 16-byte
@@ -185,17 +187,23 @@ int fp4_channel_energy(const void* x_bf16, int64_t rows, int64_t cols, int64_t l
 /*
  * fp4_build_permutation -- host-side, synchronous. Magnitude-balancing
  * permutation from channel energies (reading of [TORQ] sec. 2(a) as a
- * permutation): channels are taken in order of decreasing energy (equal
- * energies: lower index first); each goes to the next free slot of the block
- * whose accumulated energy (summed in fp64) is smallest among blocks that still
- * have a free slot (equal loads: lower block index).
+ * permutation). The unit moved is an aligned run of `group` channels with
+ * energy the fp64 sum of its channels'. Units are taken in order of decreasing
+ * energy (equal energies: lower index first); each goes to the next free slot
+ * of the block whose accumulated energy (summed in fp64) is smallest among
+ * blocks with a free slot (equal loads: lower block index), its channels kept
+ * in order. group 1 balances single channels best; 2, 4 or 8 keep runs of
+ * neighbouring channels together, which fp4_rotate_quantize gathers with one
+ * 4-, 8- or 16-byte LDS read per run.
  *
  *  energy_host  host fp32[cols]
  *  cols         cols > 0, cols % block == 0
  *  block        32 (MXFP4) or 16 (NVFP4)
+ *  group        1, 2, 4 or 8
  *  perm_host    host int32[cols]; perm[j] = source channel of column j
  */
-int fp4_build_permutation(const float* energy_host, int64_t cols, int block, int32_t* perm_host);
+int fp4_build_permutation(const float* energy_host, int64_t cols, int block, int group,
+                          int32_t* perm_host);
 
 #ifdef __cplusplus
 }

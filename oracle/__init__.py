@@ -95,7 +95,7 @@ def _load():
         "orc_rotate": (None, [vp, i64, i64, i64, vp, i32, vp, i64]),
         "orc_unrotate_f64": (None, [vp, i64, i64, i64, vp, i32, vp, i64]),
         "orc_channel_energy": (None, [vp, i64, i64, i64, vp]),
-        "orc_build_perm": (None, [vp, i64, i32, vp]),
+        "orc_build_perm": (None, [vp, i64, i32, i32, vp]),
         "orc_hadamard_entry": (f64, [i32, i32, i32]),
     }
     for name, (res, args) in sig.items():
@@ -283,12 +283,13 @@ def channel_energy(x_bf16: np.ndarray) -> np.ndarray:
     return e
 
 
-def build_perm(energy: np.ndarray, block: int = 32) -> np.ndarray:
+def build_perm(energy: np.ndarray, block: int = 32, group: int = 1) -> np.ndarray:
+    """Balancing permutation moving aligned runs of ``group`` channels."""
     energy = np.ascontiguousarray(energy, np.float32)
     cols = energy.size
-    assert cols % block == 0
+    assert cols % block == 0 and block % group == 0
     perm = np.zeros(cols, np.int32)
-    _load().orc_build_perm(_ptr(energy), cols, int(block), _ptr(perm))
+    _load().orc_build_perm(_ptr(energy), cols, int(block), int(group), _ptr(perm))
     return perm
 
 

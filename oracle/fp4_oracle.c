@@ -475,11 +475,11 @@ void orc_channel_energy(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
     }
 }
 
-static const float* g_sort_energy;
+static const double* g_sort_energy;
 
 static int by_energy_desc(const void* a, const void* b) {
   int32_t ia = *(const int32_t*)a, ib = *(const int32_t*)b;
-  float ea = g_sort_energy[ia], eb = g_sort_energy[ib];
+  double ea = g_sort_energy[ia], eb = g_sort_energy[ib];
   if (ea > eb) return -1;
   if (ea < eb) return 1;
   return ia < ib ? -1 : (ia > ib ? 1 : 0);
@@ -488,31 +488,41 @@ static int by_energy_desc(const void* a, const void* b) {
 /* Magnitude-balancing permutation (reading of [TORQ] sec. 2(a) -- an
  * orthogonal transform that makes the block variances equal -- restricted to
  * permutations; the pages build their macro rotation from Givens rotations).
- * Channels are taken largest energy first (equal energies by lower index)
- * and each goes to the block whose accumulated energy is smallest among the
- * blocks that still have a free slot (equal loads: lower block index), in the
- * block's next free slot. Loads are summed in double. perm[j] is the source
- * channel of position j. Not thread-safe (qsort comparator state). */
-void orc_build_perm(const float* energy, int64_t cols, int block, int32_t* perm) {
-  int64_t B = cols / block;
-  int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)cols);
+ * The unit moved is an aligned run of `group` channels (1 = single channels;
+ * 2, 4 or 8 keep neighbouring channels together), with energy the sum of its
+ * channels' energies in double, in channel order. Units are taken largest
+ * energy first (equal energies: lower index first); each goes to the block
+ * whose accumulated energy is smallest among the blocks that still have a
+ * free unit slot (equal loads: lower block index), in the block's next free
+ * slot, keeping its channels in order. Loads are summed in double. perm[j] is
+ * the source channel of position j. Not thread-safe (qsort comparator state). */
+void orc_build_perm(const float* energy, int64_t cols, int block, int group, int32_t* perm) {
+  int64_t B = cols / block, nu = cols / group, slots = block / group;
+  int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)nu);
+  double* ue = (double*)malloc(sizeof(double) * (size_t)nu);
   double* load = (double*)calloc((size_t)B, sizeof(double));
   int64_t* fill = (int64_t*)calloc((size_t)B, sizeof(int64_t));
-  for (int64_t j = 0; j < cols; ++j) order[j] = (int32_t)j;
-  g_sort_energy = energy;
-  qsort(order, (size_t)cols, sizeof(int32_t), by_energy_desc);
-  for (int64_t t = 0; t < cols; ++t) {
+  for (int64_t u = 0; u < nu; ++u) {
+    order[u] = (int32_t)u;
+    ue[u] = 0.0;
+    for (int i = 0; i < group; ++i) ue[u] += (double)energy[u * group + i];
+  }
+  g_sort_energy = ue;
+  qsort(order, (size_t)nu, sizeof(int32_t), by_energy_desc);
+  for (int64_t t = 0; t < nu; ++t) {
     int64_t best = -1;
     for (int64_t b = 0; b < B; ++b) {
-      if (fill[b] == block) continue;
+      if (fill[b] == slots) continue;
       if (best < 0 || load[b] < load[best]) best = b;
     }
-    int32_t c = order[t];
-    perm[best * block + fill[best]] = c;
+    int32_t u = order[t];
+    for (int i = 0; i < group; ++i)
+      perm[best * block + fill[best] * group + i] = u * group + i;
     fill[best] += 1;
-    load[best] += (double)energy[c];
+    load[best] += ue[u];
   }
   free(order);
+  free(ue);
   free(load);
   free(fill);
 }

@@ -65,7 +65,7 @@ void orc_unrotate_f64(const double* y, int64_t rows, int64_t cols, int64_t ld_y,
                       const int32_t* perm, int hadamard, double* out, int64_t ld_out);
 void orc_channel_energy(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                         double* energy);
-void orc_build_perm(const float* energy, int64_t cols, int block, int32_t* perm);
+void orc_build_perm(const float* energy, int64_t cols, int block, int group, int32_t* perm);
 double orc_hadamard_entry(int n, int i, int j);
 
 #ifdef __cplusplus

@@ -108,15 +108,19 @@ def test_binding_raises_without_gpu_work():
         fp4._check("fp4_quantize", -2)
 
 
-def test_host_permutation_matches_oracle(L, orc):
-    rng = np.random.default_rng(3)
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_host_permutation_matches_oracle(L, orc, group):
+    rng = np.random.default_rng(3 + group)
     for cols, block in ((64, 32), (8192, 32), (1024, 16), (28672, 32)):
+        if block % group:
+            continue
         e = np.exp(3 * rng.standard_normal(cols)).astype(np.float32)
         e[rng.integers(0, cols, cols // 8)] = e[0]  # plenty of exact ties
-        want = orc.build_perm(e, block)
+        want = orc.build_perm(e, block, group)
         got = np.zeros(cols, np.int32)
-        assert L.fp4_build_permutation(e.ctypes.data, cols, block, got.ctypes.data) == 0
+        assert L.fp4_build_permutation(e.ctypes.data, cols, block, group, got.ctypes.data) == 0
         assert np.array_equal(got, want)
     bad = np.zeros(64, np.int32)
-    assert L.fp4_build_permutation(e.ctypes.data, 48, 32, bad.ctypes.data) == -2
-    assert L.fp4_build_permutation(None, 64, 32, bad.ctypes.data) == -1
+    assert L.fp4_build_permutation(e.ctypes.data, 48, 32, group, bad.ctypes.data) == -2
+    assert L.fp4_build_permutation(None, 64, 32, group, bad.ctypes.data) == -1
+    assert L.fp4_build_permutation(e.ctypes.data, 64, 32, 3, bad.ctypes.data) == -4

@@ -256,6 +256,23 @@ def test_rotate_two_level_c4_small(orc, had):
     note(f"  {r}")
 
 
+@pytest.mark.parametrize("group", [2, 4, 8])
+def test_rotate_grouped_permutation(orc, group):
+    """Permutations of aligned channel runs take the wide-gather path."""
+    note(f"case: permutation of {group}-channel runs + H32, 512x8192")
+    x = inputs.gen_c4(rows=512)
+    e = orc.channel_energy(x).astype(np.float32)
+    perm = orc.build_perm(e, 32, group)
+    host = fp4.build_permutation(torch.from_numpy(e), 32, group).numpy()
+    assert np.array_equal(host, perm)
+    r = _rot_case(orc, x, perm, 32)
+    note(f"  {r}")
+    # one swap breaks the 8/4-alignment: the kernel must fall back, not misread
+    bad = perm.copy()
+    bad[[0, 2]] = bad[[2, 0]]
+    _rot_case(orc, x, bad, 32)
+
+
 @pytest.mark.parametrize("rows,cols", [(3, 96), (37, 2080), (5, 16384)])
 def test_rotate_ragged(orc, rows, cols):
     note(f"case: rotate ragged {rows}x{cols}")
@@ -263,6 +280,9 @@ def test_rotate_ragged(orc, rows, cols):
     perm = np.random.default_rng(cols).permutation(cols).astype(np.int32)
     _rot_case(orc, x, perm, 32)
     _rot_case(orc, x, None, 32)
+    runs = np.random.default_rng(cols + 1).permutation(cols // 8).astype(np.int32)
+    perm8 = (8 * runs[:, None] + np.arange(8)[None, :]).reshape(-1).astype(np.int32)
+    _rot_case(orc, x, perm8, 32)
 
 
 @pytest.mark.parametrize("perm_on", [False, True])

@@ -131,3 +131,33 @@ def test_two_level_rotation_on_imbalanced_blocks(orc):
     s_plain, _ = _mx_sqnr(orc, x, None, 0)
     s_two, _ = _mx_sqnr(orc, x, perm, 32)
     assert s_two > s_plain + 0.2, (s_plain, s_two)
+
+
+@pytest.mark.parametrize("group", [2, 4, 8])
+def test_grouped_permutation(orc, group):
+    """Units of `group` aligned channels move together; the greedy invariant
+    holds on the unit energies; group 1 is the single-channel permutation."""
+    x = inputs.gen_c4(rows=256)
+    e = orc.channel_energy(x).astype(np.float32)
+    perm = orc.build_perm(e, 32, group)
+    assert np.array_equal(np.sort(perm), np.arange(perm.size))
+    runs = perm.reshape(-1, group)
+    assert np.all(runs[:, 0] % group == 0)
+    assert np.all(runs - runs[:, :1] == np.arange(group)[None, :])
+    ue = e.astype(np.float64).reshape(-1, group).sum(1)
+    order = np.argsort(-ue, kind="stable")
+    unit_pos = np.empty(ue.size, int)
+    unit_pos[runs[:, 0] // group] = np.arange(runs.shape[0])
+    load = np.zeros(perm.size // 32)
+    fill = np.zeros(perm.size // 32, int)
+    for u in order:
+        b = unit_pos[u] // (32 // group)
+        open_ = fill < 32 // group
+        assert open_[b] and load[b] == load[open_].min()
+        assert unit_pos[u] % (32 // group) == fill[b]
+        fill[b] += 1
+        load[b] += ue[u]
+    blk = e.astype(np.float64)[perm].reshape(-1, 32).sum(1)
+    blk0 = e.astype(np.float64).reshape(-1, 32).sum(1)
+    assert blk.std() / blk.mean() < blk0.std() / blk0.mean()
+    assert np.array_equal(orc.build_perm(e, 32, 1), orc.build_perm(e, 32))
