@@ -18,8 +18,28 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;  // work-group size of the streaming kernels
+
+// ---- buffer resources -----------------------------------------------------
+// A raw buffer resource covers [base, base + bytes) and the hardware
+// range-checks every access through it: a load at an offset past the end
+// returns zero without touching memory, a store there is dropped. Kernels
+// that keep loads in flight across rows use this to issue every load and store
+// unconditionally (offset kOob for a lane or row with nothing to do). With no
+// branch around a memory operation, the compiler knows how many operations
+// were issued after each load and waits for that load alone, instead of
+// draining the whole vector-memory counter, which on gfx9 also counts stores.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOob = 0x80000000u;  // beyond every resource (byte counts < 2^31)
+constexpr int kNt = 2;                  // cache policy bit: nontemporal
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // word 3: raw (unswizzled, stride 0) buffer with 32-bit data format
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
 
 // Bit casts take a scalar by value: clang's __builtin_bit_cast applied
 // directly to an ext-vector element (v.y) reads element 0 instead.

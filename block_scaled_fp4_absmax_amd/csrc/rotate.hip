@@ -19,14 +19,16 @@
 // stay contiguous and no lane exchange is needed except one max for the
 // block's absmax. The result is scaled by fp32(1/sqrt(32)).
 //
-// A second implementation (compile-time, FP4_HADAMARD_MFMA=0) runs the
-// transform as a radix-2 butterfly in registers and DPP lane exchanges; it is
-// kept for measuring one against the other.
+// A second implementation of the streaming (no permutation) kernel,
+// compile-time FP4_HADAMARD_MFMA=0, runs the transform as a radix-2 butterfly
+// in registers and DPP lane exchanges; it is kept for measuring one against
+// the other. The inverse rotation uses the butterfly (decode gives fp32 there).
 //
-// The permutation x'[j] = x[perm[j]] is applied by staging whole rows in LDS:
-// a work-group loads a row with coalesced 16-byte loads, then each lane
-// gathers its permuted elements with 2-byte LDS reads. The next row's global
-// loads are issued before the current row is processed.
+// The permutation x'[j] = x[perm[j]] is applied by staging whole rows in LDS.
+// A work-group alternates between two LDS row buffers: while its lanes gather
+// the permuted elements of one row from one buffer (LDS reads of 2 bytes, or
+// 4, 8, 16 when perm moves aligned runs of channels), the next row, fetched
+// with coalesced 16-byte loads, is written to the other.
 #include "fp4_device.hpp"
 #include "launch.hpp"
 
@@ -41,8 +43,7 @@ constexpr float kInvSqrt32 = 0.17677669529663688f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void widen8(u32x4_t d, float* v) {
   v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
@@ -288,117 +289,168 @@ __global__ __launch_bounds__(kThreads) void mx_rotq_stream_bfly_kernel(
   }
 }
 
-// ================== permuting kernels (one row at a time, LDS) ==============
-// Dynamic LDS: row[cols] bf16 followed by perm[cols] uint16 (entries clamped
-// to cols - 1, so no gather leaves the row). A work-group walks rows
-// r0, r0 + G, r0 + 2G, ... (G = grid size). The global loads of the row kDepth
-// steps ahead are issued into registers before the current row is processed,
-// so kDepth rows per work-group are in flight; kCpl = 16-byte chunks per lane
-// per row (cols <= 8 * kThreads * kCpl).
-constexpr int kMaxChunksPerLane = (int)(kMaxPermCols / 8 / kThreads);  // 8
+// ================== permuting kernel (rows staged in LDS) ===================
+// A work-group walks rows r0 + k G (G = grid size) and stages each row in one
+// of two LDS buffers of 8192 kTpw bytes (cols <= 4096 kTpw), so a single
+// barrier per row suffices: row k + 1 is written to one buffer while row k is
+// gathered from the other. Global loads run one row ahead in registers.
+//
+// Lane (n, h) of wave w handles, for i < kTpw, tile t = w + kWaves i: block
+// b = 32 t + n, elements e0 .. e0 + 15 with e0 = 32 b + 16 h, gathered from
+// row positions perm[e0 .. e0 + 15]. Those positions are the same for every
+// row, so each lane loads them once and keeps them in registers as LDS byte
+// offsets (clamped to the row), packed in pairs.
+//
+// Every global load and store goes through a per-row buffer resource and is
+// issued by every lane (rows past the end and idle lanes use out-of-range
+// offsets): with a fixed count of memory operations per row, the wait before
+// a row is staged covers that row's loads and not the stores issued since.
 
-// Stage perm into LDS as uint16 (clamped to the row) and return the largest
-// run length G in {8, 4, 2, 1} such that perm maps every aligned run of G
-// positions onto an aligned run of G consecutive channels (same for the whole
-// work-group, so the caller's branch on it is uniform).
-__device__ __forceinline__ int stage_perm(const int32_t* __restrict__ perm, uint16_t* sperm,
-                                          int32_t cols) {
-  const int32_t cmax = cols - 1;
-  for (int32_t j = threadIdx.x; j < cols; j += kThreads) {
-    int32_t p = perm[j];
-    p = p < 0 ? 0 : (p > cmax ? cmax : p);
-    sperm[j] = (uint16_t)p;
-  }
-  __syncthreads();
-  int ok2 = 1, ok4 = 1, ok8 = 1;
-  for (int32_t j = threadIdx.x; j < cols; j += kThreads) {
-    const uint32_t p = sperm[j];
-    const uint32_t b2 = sperm[j & ~1], b4 = sperm[j & ~3], b8 = sperm[j & ~7];
-    ok2 &= (p == b2 + (uint32_t)(j & 1)) && (b2 % 2u == 0u);
-    ok4 &= (p == b4 + (uint32_t)(j & 3)) && (b4 % 4u == 0u);
-    ok8 &= (p == b8 + (uint32_t)(j & 7)) && (b8 % 8u == 0u);
-  }
-  if (__syncthreads_and(ok8)) return 8;
-  if (__syncthreads_and(ok4)) return 4;
-  if (__syncthreads_and(ok2)) return 2;
-  return 1;
+// Per-row buffer resources (empty for rows past the end).
+struct RowRsrc {
+  rsrc_t x, c, s, rot;
+};
+
+template <bool kRot>
+__device__ __forceinline__ RowRsrc row_rsrc(const uint16_t* x, uint8_t* codes, uint8_t* scales,
+                                            float* rot, int32_t r, const RotGeom& g) {
+  const bool in = r < g.rows;
+  const int64_t rr = in ? r : 0;
+  RowRsrc q;
+  q.x = make_rsrc(x + rr * g.ld_x, in ? 2u * (uint32_t)g.cols : 0u);
+  q.c = make_rsrc(codes + rr * g.ld_c, in ? (uint32_t)g.cols / 2u : 0u);
+  q.s = make_rsrc(scales + rr * g.ld_s, in ? (uint32_t)g.bpr : 0u);
+  if (kRot) q.rot = make_rsrc(rot + rr * g.ld_rot, in ? 4u * (uint32_t)g.cols : 0u);
+  return q;
 }
 
 template <int kCpl>
-__device__ __forceinline__ void load_row(const uint16_t* __restrict__ src, int32_t cpr,
-                                         u32x4_t* pre) {
+__device__ __forceinline__ void load_row(rsrc_t src, int32_t cpr, u32x4_t* pre) {
 #pragma unroll
   for (int i = 0; i < kCpl; ++i) {
-    int32_t c = threadIdx.x + i * kThreads;
-    if (c < cpr) pre[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src) + c);
+    const int32_t c = threadIdx.x + i * kThreads;
+    pre[i] = __builtin_amdgcn_raw_buffer_load_b128(src, c < cpr ? 16u * c : kOob, 0, kNt);
   }
 }
 
 template <int kCpl>
-__device__ __forceinline__ void put_row(uint16_t* srow, int32_t cpr, const u32x4_t* pre) {
+__device__ __forceinline__ void put_row(uint8_t* buf, int32_t cpr, const u32x4_t* pre) {
 #pragma unroll
   for (int i = 0; i < kCpl; ++i) {
     int32_t c = threadIdx.x + i * kThreads;
-    if (c < cpr) reinterpret_cast<u32x4_t*>(srow)[c] = pre[i];
+    if (c < cpr) reinterpret_cast<u32x4_t*>(buf)[c] = pre[i];
   }
 }
 
-// Eight gathered bf16, packed in pairs, from eight LDS indices.
-__device__ __forceinline__ u32x4_t gather8(const uint16_t* srow, u32x4_t id) {
-  u32x4_t r;
-  r.x = (uint32_t)srow[id.x & 0xFFFFu] | ((uint32_t)srow[id.x >> 16] << 16);
-  r.y = (uint32_t)srow[id.y & 0xFFFFu] | ((uint32_t)srow[id.y >> 16] << 16);
-  r.z = (uint32_t)srow[id.z & 0xFFFFu] | ((uint32_t)srow[id.z >> 16] << 16);
-  r.w = (uint32_t)srow[id.w & 0xFFFFu] | ((uint32_t)srow[id.w >> 16] << 16);
-  return r;
+// Issue the loads of this lane's perm entries (16 per tile, zeros for tiles
+// past the row).
+template <int kTpw>
+__device__ __forceinline__ void load_lane_perm(const int32_t* __restrict__ perm,
+                                               const RotGeom& g, i32x4_t (*v)[4]) {
+  const rsrc_t rp = make_rsrc(perm, 4u * (uint32_t)g.cols);
+  const int32_t lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < kTpw; ++i) {
+    const int32_t b = 32 * (w + kWaves * i) + n;
+    const uint32_t o = b < g.bpr ? 4u * (32u * b + 16u * h) : kOob;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[i][q] = __builtin_bit_cast(
+          i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, o == kOob ? kOob : o + 16u * q, 0, 0));
+  }
 }
 
-// The 16 gathered bf16 x'[e0 .. e0+15] (e0 a multiple of 16), as the MFMA's two
-// B halves, when perm is made of aligned runs of G channels: one LDS read of
-// 2G bytes per run.
-template <int G>
-__device__ __forceinline__ void gather16(const uint16_t* srow, const uint16_t* sperm, int32_t e0,
-                                         u32x4_t& lo, u32x4_t& hi) {
+// Clamp to the row, convert to byte offsets packed in pairs, and return the
+// largest run length G in {8, 4, 2, 1} such that the lane's indices form
+// aligned runs of G consecutive channels (lanes without a block: 8).
+template <int kTpw>
+__device__ __forceinline__ int pack_lane_perm(const i32x4_t (*v)[4], const RotGeom& g,
+                                              uint32_t (*off)[8]) {
+  const int32_t lane = threadIdx.x & 63, n = lane & 31, w = threadIdx.x >> 6;
+  const int32_t cmax = g.cols - 1;
+  bool r8 = true, r4 = true, r2 = true;
+#pragma unroll
+  for (int i = 0; i < kTpw; ++i) {
+    int32_t p[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      p[4 * q + 0] = min(max(v[i][q].x, 0), cmax);
+      p[4 * q + 1] = min(max(v[i][q].y, 0), cmax);
+      p[4 * q + 2] = min(max(v[i][q].z, 0), cmax);
+      p[4 * q + 3] = min(max(v[i][q].w, 0), cmax);
+    }
+    if (32 * (w + kWaves * i) + n < g.bpr) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        r8 = r8 && p[k] == p[k & 8] + (k & 7) && (p[k & 8] & 7) == 0;
+        r4 = r4 && p[k] == p[k & 12] + (k & 3) && (p[k & 12] & 3) == 0;
+        r2 = r2 && p[k] == p[k & 14] + (k & 1) && (p[k & 14] & 1) == 0;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) off[i][k] = 2u * (uint32_t)p[2 * k] | (2u * (uint32_t)p[2 * k + 1]) << 16;
+  }
+  return r8 ? 8 : r4 ? 4 : r2 ? 2 : 1;
+}
+
+// The 16 gathered bf16 of one tile (MFMA B halves lo, hi) from the row staged
+// at LDS byte kOff of buf; G: the packed offsets form aligned runs of G, read
+// 2G bytes at a time.
+template <int G, uint32_t kOff>
+__device__ __forceinline__ void gather_tile(const uint8_t* buf, const uint32_t* off, u32x4_t& lo,
+                                            u32x4_t& hi) {
+  const uint8_t* base = buf + kOff;
   if constexpr (G == 1) {
-    const u32x4_t* ip = reinterpret_cast<const u32x4_t*>(sperm + e0);
-    lo = gather8(srow, ip[0]);
-    hi = gather8(srow, ip[1]);
+    uint32_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      v[k] = (uint32_t)*reinterpret_cast<const uint16_t*>(base + (off[k] & 0xFFFFu)) |
+             ((uint32_t)*reinterpret_cast<const uint16_t*>(base + (off[k] >> 16)) << 16);
+    lo = u32x4_t{v[0], v[1], v[2], v[3]};
+    hi = u32x4_t{v[4], v[5], v[6], v[7]};
   } else if constexpr (G == 2) {
-    const u32x4_t* ip = reinterpret_cast<const u32x4_t*>(sperm + e0);
-    const u32x4_t i0 = ip[0], i1 = ip[1];
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(srow);
-    lo.x = w[(i0.x & 0xFFFFu) >> 1]; lo.y = w[(i0.y & 0xFFFFu) >> 1];
-    lo.z = w[(i0.z & 0xFFFFu) >> 1]; lo.w = w[(i0.w & 0xFFFFu) >> 1];
-    hi.x = w[(i1.x & 0xFFFFu) >> 1]; hi.y = w[(i1.y & 0xFFFFu) >> 1];
-    hi.z = w[(i1.z & 0xFFFFu) >> 1]; hi.w = w[(i1.w & 0xFFFFu) >> 1];
+    uint32_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const uint32_t*>(base + (off[k] & 0xFFFFu));
+    lo = u32x4_t{v[0], v[1], v[2], v[3]};
+    hi = u32x4_t{v[4], v[5], v[6], v[7]};
   } else if constexpr (G == 4) {
-    const u32x2_t* w = reinterpret_cast<const u32x2_t*>(srow);
-    const u32x2_t a = w[sperm[e0] >> 2], b = w[sperm[e0 + 4] >> 2];
-    const u32x2_t c = w[sperm[e0 + 8] >> 2], d = w[sperm[e0 + 12] >> 2];
+    const u32x2_t a = *reinterpret_cast<const u32x2_t*>(base + (off[0] & 0xFFFFu));
+    const u32x2_t b = *reinterpret_cast<const u32x2_t*>(base + (off[2] & 0xFFFFu));
+    const u32x2_t c = *reinterpret_cast<const u32x2_t*>(base + (off[4] & 0xFFFFu));
+    const u32x2_t d = *reinterpret_cast<const u32x2_t*>(base + (off[6] & 0xFFFFu));
     lo = u32x4_t{a.x, a.y, b.x, b.y};
     hi = u32x4_t{c.x, c.y, d.x, d.y};
   } else {
-    const u32x4_t* w = reinterpret_cast<const u32x4_t*>(srow);
-    lo = w[sperm[e0] >> 3];
-    hi = w[sperm[e0 + 8] >> 3];
+    lo = *reinterpret_cast<const u32x4_t*>(base + (off[0] & 0xFFFFu));
+    hi = *reinterpret_cast<const u32x4_t*>(base + (off[4] & 0xFFFFu));
   }
 }
 
-// Permute + Hadamard + quantize one staged row (MFMA: a wave takes tiles of 32
-// blocks, lane (n, h) gathers elements 16h..16h+15 of block n).
-template <int G, bool kHad, bool kFloor, bool kRot>
-__device__ __forceinline__ void rotq_row_mfma(const uint16_t* srow, const uint16_t* sperm,
-                                              const bf16x8_t& a0, const bf16x8_t& a1, int32_t r,
-                                              uint8_t* __restrict__ codes,
-                                              uint8_t* __restrict__ scales,
-                                              float* __restrict__ rot, const RotGeom& g) {
+// One row step: stage the next row (already loaded into pre) into the other
+// buffer, load the row after it into pre, then gather, rotate, quantize and
+// store row r from buffer kBuf; a barrier closes the step.
+template <int G, int kTpw, int kBuf, bool kHad, bool kFloor, bool kRot>
+__device__ __forceinline__ void perm_step(const uint16_t* __restrict__ x, uint8_t* sbuf,
+                                          const uint32_t (*off)[8], const bf16x8_t& a0,
+                                          const bf16x8_t& a1, uint8_t* __restrict__ codes,
+                                          uint8_t* __restrict__ scales, float* __restrict__ rot,
+                                          const RotGeom& g, int32_t r, bool has_next,
+                                          u32x4_t* pre) {
+  constexpr int kCpl = 2 * kTpw;
+  constexpr uint32_t kBufBytes = 8192u * kTpw;
+  const int32_t cpr = g.cols / 8;
+  const int32_t G_ = gridDim.x;
+  if (has_next) put_row<kCpl>(sbuf + (1 - kBuf) * kBufBytes, cpr, pre);
+  load_row<kCpl>(row_rsrc<kRot>(x, codes, scales, rot, r + 2 * G_, g).x, cpr, pre);
+  const RowRsrc q = row_rsrc<kRot>(x, codes, scales, rot, r, g);
   const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
-  const int32_t ntiles = (g.bpr + 31) / 32;
-  for (int32_t t = threadIdx.x >> 6; t < ntiles; t += kWaves) {
-    const int32_t b = 32 * t + (int32_t)n;
+#pragma unroll
+  for (int i = 0; i < kTpw; ++i) {
+    const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kWaves * i) + (int32_t)n;
     const bool ok = b < g.bpr;
-    u32x4_t lo = {0u, 0u, 0u, 0u}, hi = lo;
-    if (ok) gather16<G>(srow, sperm, 32 * b + 16 * (int32_t)h, lo, hi);
+    u32x4_t lo, hi;
+    gather_tile<G, kBuf * kBufBytes>(sbuf, off[i], lo, hi);
     float y[16];
     if (kHad) {
       hadamard_mfma(a0, a1, lo, hi, y);
@@ -408,97 +460,124 @@ __device__ __forceinline__ void rotq_row_mfma(const uint16_t* srow, const uint16
     }
     uint32_t w0, w1, byte;
     mx_quant16_pair<kFloor>(y, w0, w1, byte);
-    if (ok) {
-      uint32_t* cp = reinterpret_cast<uint32_t*>(codes + r * g.ld_c + 16 * (int64_t)b + 8 * h);
-      __builtin_nontemporal_store(w0, cp);
-      __builtin_nontemporal_store(w1, cp + 1);
-      if (h == 0) scales[r * g.ld_s + b] = (uint8_t)byte;
-      if (kRot) {
-        float* rp = rot + r * g.ld_rot + 32 * (int64_t)b + 16 * h;
-        store_rot8(rp, y);
-        store_rot8(rp + 8, y + 8);
-      }
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w0, w1}, q.c, ok ? 16u * b + 8u * h : kOob, 0,
+                                          kNt);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, q.s, ok && h == 0 ? (uint32_t)b : kOob,
+                                         0, 0);
+    if (kRot) {
+      const uint32_t o = ok ? 4u * (32u * b + 16u * h) : kOob;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4_t, f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]}),
+            q.rot, o == kOob ? kOob : o + 16u * k, 0, kNt);
     }
   }
+  __syncthreads();
 }
 
-// Same row, butterfly implementation: lane takes 16-byte chunks c = t + i * kThreads.
-template <bool kHad, bool kFloor, bool kRot>
-__device__ __forceinline__ void rotq_row_bfly(const uint16_t* srow, const uint16_t* sperm,
-                                              int32_t r, uint8_t* __restrict__ codes,
-                                              uint8_t* __restrict__ scales,
-                                              float* __restrict__ rot, const RotGeom& g) {
-  const uint32_t q = threadIdx.x & 3u;
-  const int32_t cpr = g.cols / 8;
-  for (int32_t c = threadIdx.x; c < cpr; c += kThreads) {
-    float y[8];
-    widen8(gather8(srow, reinterpret_cast<const u32x4_t*>(sperm)[c]), y);
-    if (kHad) hadamard_butterfly(y, q);
-    uint32_t w, byte;
-    mx_quant8_quad<kFloor>(y, w, byte);
-    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + r * g.ld_c + 4 * (int64_t)c));
-    if (q == 0) scales[r * g.ld_s + c / 4] = (uint8_t)byte;
-    if (kRot) store_rot8(rot + r * g.ld_rot + 8 * (int64_t)c, y);
-  }
-}
-
-template <int G, int kCpl, int kDepth, bool kHad, bool kFloor, bool kRot>
-__device__ __forceinline__ void perm_rows(const uint16_t* __restrict__ x, uint16_t* srow,
-                                          const uint16_t* sperm, const bf16x8_t& a0,
+// Rows r0 + k G, k < K. Step 0 is peeled and the loop takes steps in pairs
+// (buffer 1, then 0), so every path into a step's wait has the same memory
+// operations after the loads it waits for: the previous step's stores.
+template <int G, int kTpw, bool kHad, bool kFloor, bool kRot>
+__device__ __forceinline__ void perm_rows(const uint16_t* __restrict__ x, uint8_t* sbuf,
+                                          const uint32_t (*off)[8], const bf16x8_t& a0,
                                           const bf16x8_t& a1, uint8_t* __restrict__ codes,
                                           uint8_t* __restrict__ scales, float* __restrict__ rot,
-                                          const RotGeom& g) {
-  const int32_t cpr = g.cols / 8;
-  const int32_t G_ = gridDim.x;
-  u32x4_t pre[kDepth][kCpl];
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d) {
-    const int32_t rr = (int32_t)blockIdx.x + d * G_;
-    if (rr < g.rows) load_row<kCpl>(x + rr * g.ld_x, cpr, pre[d]);
+                                          const RotGeom& g, u32x4_t* pre) {
+  const int32_t G_ = gridDim.x, r0 = blockIdx.x;
+  const int32_t K = (g.rows - r0 + G_ - 1) / G_;
+  perm_step<G, kTpw, 0, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g, r0,
+                                            K > 1, pre);
+  int32_t k = 1;
+  for (; k + 1 < K; k += 2) {
+    perm_step<G, kTpw, 1, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g,
+                                              r0 + k * G_, true, pre);
+    perm_step<G, kTpw, 0, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g,
+                                              r0 + (k + 1) * G_, k + 2 < K, pre);
   }
-  for (int32_t r = blockIdx.x; r < g.rows; r += kDepth * G_) {
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int32_t rr = r + d * G_;
-      if (rr >= g.rows) break;  // uniform across the work-group
-      __syncthreads();          // the previous row's gathers are done
-      put_row<kCpl>(srow, cpr, pre[d]);
-      __syncthreads();
-      const int32_t rn = rr + kDepth * G_;
-      if (rn < g.rows) load_row<kCpl>(x + rn * g.ld_x, cpr, pre[d]);
-      if constexpr (kUseMfma)
-        rotq_row_mfma<G, kHad, kFloor, kRot>(srow, sperm, a0, a1, rr, codes, scales, rot, g);
-      else
-        rotq_row_bfly<kHad, kFloor, kRot>(srow, sperm, rr, codes, scales, rot, g);
-    }
-  }
+  if (k < K)
+    perm_step<G, kTpw, 1, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g,
+                                              r0 + k * G_, false, pre);
 }
 
-template <int kCpl, int kDepth, bool kHad, bool kFloor, bool kRot>
-__global__ __launch_bounds__(kThreads) void mx_rotq_perm_kernel(
+// Waves per SIMD the register allocation is held to, and work-groups per CU
+// in the grid. Two row buffers of 8 KB kTpw each bound the work-groups a CU
+// can hold; on MI355X at cols = 8192 two per CU (32 rows each) measured
+// faster than three or four, and one per CU slower.
+template <int kTpw>
+constexpr int perm_waves_cap() {
+  return kTpw <= 2 ? 4 : 2;
+}
+template <int kTpw>
+constexpr int perm_wgs_per_cu() {
+  return kTpw == 1 ? 4 : 2;
+}
+
+#ifndef FP4_PERM_WAVES
+#define FP4_PERM_WAVES perm_waves_cap<kTpw>()
+#endif
+template <int kTpw, bool kHad, bool kFloor, bool kRot>
+__global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void mx_rotq_perm_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ rot, RotGeom g) {
-  extern __shared__ uint16_t smem[];
-  uint16_t* srow = smem;
-  uint16_t* sperm = smem + g.cols;
+  constexpr int kCpl = 2 * kTpw;
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf[2 * 8192 * kTpw];
+  const int32_t cpr = g.cols / 8;
+  // perm entries first, then row r0, so the row load is in flight while the
+  // entries are unpacked
+  i32x4_t v[kTpw][4];
+  load_lane_perm<kTpw>(perm, g, v);
+  u32x4_t pre[kCpl];
+  load_row<kCpl>(row_rsrc<kRot>(x, codes, scales, rot, blockIdx.x, g).x, cpr, pre);
+  uint32_t off[kTpw][8];
+  const int lr = pack_lane_perm<kTpw>(v, g, off);
   bf16x8_t a0, a1;
-  if constexpr (kUseMfma) hadamard_operands(a0, a1);
-  const int run = stage_perm(perm, sperm, g.cols);
-  if constexpr (kUseMfma) {
-    if (run == 8)
-      perm_rows<8, kCpl, kDepth, kHad, kFloor, kRot>(x, srow, sperm, a0, a1, codes, scales, rot, g);
-    else if (run == 4)
-      perm_rows<4, kCpl, kDepth, kHad, kFloor, kRot>(x, srow, sperm, a0, a1, codes, scales, rot, g);
-    else if (run == 2)
-      perm_rows<2, kCpl, kDepth, kHad, kFloor, kRot>(x, srow, sperm, a0, a1, codes, scales, rot, g);
-    else
-      perm_rows<1, kCpl, kDepth, kHad, kFloor, kRot>(x, srow, sperm, a0, a1, codes, scales, rot, g);
-  } else {
-    perm_rows<1, kCpl, kDepth, kHad, kFloor, kRot>(x, srow, sperm, a0, a1, codes, scales, rot, g);
-  }
+  hadamard_operands(a0, a1);
+  put_row<kCpl>(sbuf, cpr, pre);
+  load_row<kCpl>(row_rsrc<kRot>(x, codes, scales, rot, blockIdx.x + gridDim.x, g).x, cpr, pre);
+  // run length agreed by the whole work-group (this also publishes row r0)
+  const int run = __syncthreads_and(lr >= 8) ? 8
+                  : __syncthreads_and(lr >= 4) ? 4
+                  : __syncthreads_and(lr >= 2) ? 2 : 1;
+  if (run == 8)
+    perm_rows<8, kTpw, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g, pre);
+  else if (run == 4)
+    perm_rows<4, kTpw, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g, pre);
+  else if (run == 2)
+    perm_rows<2, kTpw, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g, pre);
+  else
+    perm_rows<1, kTpw, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g, pre);
 }
 
 // ============================ inverse rotation ==============================
+// perm staged into LDS as uint16, clamped to [0, cols - 1] (cols <= 16384):
+// sixteen 16-byte loads per lane in flight at once, then one wait.
+__device__ __forceinline__ void stage_perm(const int32_t* __restrict__ perm, uint16_t* sperm,
+                                           int32_t cols) {
+  constexpr int kPv = (int)(kMaxPermCols / 4 / kThreads);
+  const rsrc_t rp = make_rsrc(perm, 4u * (uint32_t)cols);
+  const int32_t nv = cols / 4, cmax = cols - 1;
+  i32x4_t p[kPv];
+#pragma unroll
+  for (int u = 0; u < kPv; ++u) {
+    const int32_t v = threadIdx.x + u * kThreads;
+    p[u] = __builtin_bit_cast(
+        i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, v < nv ? 16u * v : kOob, 0, 0));
+  }
+#pragma unroll
+  for (int u = 0; u < kPv; ++u) {
+    const int32_t v = threadIdx.x + u * kThreads;
+    if (v < nv) {
+      const i32x4_t q = p[u];
+      const uint32_t c0 = (uint32_t)min(max(q.x, 0), cmax), c1 = (uint32_t)min(max(q.y, 0), cmax);
+      const uint32_t c2 = (uint32_t)min(max(q.z, 0), cmax), c3 = (uint32_t)min(max(q.w, 0), cmax);
+      reinterpret_cast<u32x2_t*>(sperm)[v] = u32x2_t{c0 | (c1 << 16), c2 | (c3 << 16)};
+    }
+  }
+  __syncthreads();
+}
+
 // Decode MXFP4 exactly to fp32, apply H (its own inverse) with the butterfly,
 // then scatter element j to column perm[j] through LDS.
 template <bool kHad, bool kPerm>
@@ -510,7 +589,7 @@ __global__ __launch_bounds__(kThreads) void mx_dequant_unrotate_kernel(
   uint16_t* sperm = smem + g.cols;
   const uint32_t q = threadIdx.x & 3u;
   const int32_t cpr = g.cols / 8;
-  if (kPerm) (void)stage_perm(perm, sperm, g.cols);
+  if (kPerm) stage_perm(perm, sperm, g.cols);
   for (int32_t r = blockIdx.x; r < g.rows; r += gridDim.x) {
     if (kPerm) __syncthreads();  // previous row copied out, indices visible
     for (int32_t c = threadIdx.x; c < cpr; c += kThreads) {
@@ -597,25 +676,38 @@ static RotGeom rot_geom(const Shape& s, int64_t ld_rot) {
 
 static int perm_grid(int64_t rows) { return (int)(rows < kPermGrid ? rows : kPermGrid); }
 
-template <int kCpl, int kDepth, bool kHad, bool kFloor, bool kRot>
+// Compute units of the current device.
+static int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  return n;
+}
+
+template <int kTpw, bool kHad, bool kFloor, bool kRot>
 static void perm_launch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
                         uint8_t* sc, float* rot, const RotGeom& g, hipStream_t st) {
-  const int grid = perm_grid(s.rows);
-  const size_t lds = (size_t)4 * s.cols;
-  hipLaunchKernelGGL((mx_rotq_perm_kernel<kCpl, kDepth, kHad, kFloor, kRot>), dim3(grid),
-                     dim3(kThreads), lds, st, x, perm, c, sc, rot, g);
+#ifdef FP4_PERM_WG_PER_CU
+  const int64_t wgs = (int64_t)cu_count() * FP4_PERM_WG_PER_CU;
+#else
+  const int64_t wgs = (int64_t)cu_count() * perm_wgs_per_cu<kTpw>();
+#endif
+  const int grid = (int)(s.rows < wgs ? s.rows : wgs);
+  hipLaunchKernelGGL((mx_rotq_perm_kernel<kTpw, kHad, kFloor, kRot>), dim3(grid), dim3(kThreads),
+                     0, st, x, perm, c, sc, rot, g);
 }
 
 template <bool kHad, bool kFloor, bool kRot>
 static void rotq_dispatch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
                           uint8_t* sc, float* rot, const RotGeom& g, bool flat, hipStream_t st) {
   if (perm) {
-    const int64_t cpl = (s.cols / 8 + kThreads - 1) / kThreads;
-    // chunks per lane and prefetch depth: about 32 VGPRs of rows in flight
-    if (cpl <= 1) perm_launch<1, 4, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
-    else if (cpl <= 2) perm_launch<2, 4, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
-    else if (cpl <= 4) perm_launch<4, 2, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
-    else perm_launch<kMaxChunksPerLane, 1, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
+    // MFMA tiles (32 blocks) per wave per row
+    const int64_t tpw = (s.cols + 32 * 32 * kWaves - 1) / (32 * 32 * kWaves);
+    if (tpw <= 1) perm_launch<1, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
+    else if (tpw <= 2) perm_launch<2, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
+    else if (tpw <= 3) perm_launch<3, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
+    else perm_launch<4, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
     return;
   }
   if constexpr (kUseMfma) {

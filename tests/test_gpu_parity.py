@@ -273,7 +273,11 @@ def test_rotate_grouped_permutation(orc, group):
     _rot_case(orc, x, bad, 32)
 
 
-@pytest.mark.parametrize("rows,cols", [(3, 96), (37, 2080), (5, 16384)])
+# cols 96 .. 16384 cover one to four MFMA tiles per wave per row (partial
+# tiles at 2080 and 8224); 1537 and 2500 rows give work-groups unequal row
+# counts, odd and even, in the row-at-a-time permuting kernel
+@pytest.mark.parametrize("rows,cols", [(3, 96), (37, 2080), (5, 16384), (6, 8224), (4, 12288),
+                                       (1537, 8192), (2500, 1024)])
 def test_rotate_ragged(orc, rows, cols):
     note(f"case: rotate ragged {rows}x{cols}")
     x = inputs.gen_c3(rows=rows, cols=cols)
