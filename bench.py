@@ -17,6 +17,15 @@ The same run also reports the other rows of the path on their own workloads
 dequantizers) and the CPU oracle timed on a bounded sample of the workload.
 
   python bench.py [--steps K] [--warmup W] [--workload c4|c2|c5] [--no-extras]
+  python bench.py --pmc-summary FETCH_DIR WRITE_DIR [MFMA_DIR]
+
+roofline.traffic is the HBM traffic per launch of the fused kernel taken from
+rocprofv3 counters (FETCH_SIZE and WRITE_SIZE runs of this same program, each
+scaled by the reading for torch's 1 GiB device copy in the same run). The
+numbers live in profiles/traffic_perm_rotate_quantize_c4.md together with a
+hash of the kernel's sources; when the sources have changed since, traffic is
+reported as null. --pmc-summary writes that file's text from the rocprofv3
+output directories.
 """
 import argparse
 import json
@@ -34,19 +43,60 @@ B_MX = 2 + 0.5 + 1 / 32   # algorithmic bytes per element, MXFP4 quantize
 B_NV = 2 + 0.5 + 1 / 16   # NVFP4 quantize (without the tensor-amax read)
 
 
+MFMA_PEAK_BF16_TFLOPS = 2500.0
+ROT_KERNEL = "mx_rotq_perm_kernel"  # fused permutation + Hadamard + MXFP4 quantize
+ROT_SOURCES = ["block_scaled_fp4_absmax_amd/csrc/rotate.hip",
+               "block_scaled_fp4_absmax_amd/csrc/rotation.hpp",
+               "block_scaled_fp4_absmax_amd/csrc/fp4_device.hpp",
+               "block_scaled_fp4_absmax_amd/csrc/launch.hpp"]
+TRAFFIC_FILE = "profiles/traffic_perm_rotate_quantize_c4.md"
+COPY_BYTES = 1 << 30  # torch device copy in device_copy(): 1 GiB read, 1 GiB written
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def rot_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ROT_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """(bytes per launch, source) from the counter summary, or (None, why)."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    kv = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ln.startswith("- ") and ": " in ln:
+                k, v = ln[2:].split(": ", 1)
+                kv[k.strip()] = v.strip().strip("`")
+    if kv.get("source_hash") != rot_source_hash():
+        return None, "kernel sources changed since the counters were taken"
+    return int(kv["traffic_bytes_per_launch"]), TRAFFIC_FILE
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="c4", choices=["c4", "c2", "c5"])
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
+                   help="write the kernel-time summary from a rocprofv3 --kernel-trace --stats "
+                        "directory and the JSON line that the profiled run printed, and exit")
+    p.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                   help="write the traffic summary from rocprofv3 --pmc output directories "
+                        "(FETCH_SIZE run, WRITE_SIZE run[, MFMA busy run]) and exit")
     return p.parse_args()
 
 
@@ -172,13 +222,26 @@ def bench_c4(torch, fp4, inputs, args):
                                "+ MXFP4 (E8M0, block 32) quantize + pack",
                    "rows": rows, "cols": cols, "format": "mxfp4", "block": 32,
                    "rotation": "perm+hadamard32", "input_copies": n},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "mx_rotq_perm_kernel<true,false,false>",
-                     "bytes_per_launch": int(elems * B_MX)},
+        "roofline": roofline_c4(elems, ms),
         "extras": extras,
     }
     return res, x, perm_cpu.numpy()
+
+
+def roofline_c4(elems, ms):
+    achieved = elems * B_MX / (ms * 1e-3) / 1e9
+    traffic, src = committed_traffic()
+    r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(achieved / HBM_PEAK_GBS, 4),
+         "traffic": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1),
+         "kernel": ROT_KERNEL + "<2,true,false,false> (2 MFMA tiles per wave per row)",
+         "bytes_per_launch": int(elems * B_MX),
+         "traffic_bytes_per_launch": traffic, "traffic_source": src,
+         # the block Hadamard as a dense contraction: 2 x (32x32x16) MFMAs per 32 blocks
+         "mfma_bf16_tflops_algorithmic": round(elems * 64 / (ms * 1e-3) / 1e12, 1),
+         "mfma_bf16_frac_of_peak": round(elems * 64 / (ms * 1e-3) / 1e12 / MFMA_PEAK_BF16_TFLOPS,
+                                         4)}
+    return r
 
 
 def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
@@ -294,7 +357,7 @@ def bench_c5(torch, fp4, inputs, args):
                          codes=cs[k], scales=ss[k])
             fp4.dequantize(cs[k], ss[k], fp4.NVFP4, fp4.RAZER, ts[k], out=outs[k])
 
-    ms = timed(torch, step, max(1, args.steps // 5), max(1, args.warmup // 5))
+    ms = timed(torch, step, args.steps, args.warmup)
     num = sum(float((xs[k].double() ** 2).sum()) for k in range(len(xs)))
     den = sum(float(((xs[k].double() - outs[k].double()) ** 2).sum()) for k in range(len(xs)))
     import math
@@ -312,8 +375,140 @@ def bench_c5(torch, fp4, inputs, args):
     return res, None, None
 
 
+def _pmc_rows(d, counter):
+    """{kernel name: [per-dispatch counter value]} from a rocprofv3 --pmc CSV directory."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        per = {}
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter:
+                    continue
+                key = (row["Kernel_Name"], row["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+        for (k, _), v in per.items():
+            out.setdefault(k, []).append(v)
+    return out
+
+
+def pmc_summary(dirs):
+    """Markdown traffic summary for profiles/ from FETCH_SIZE / WRITE_SIZE runs."""
+    def pick(rows, sub):
+        ks = [k for k in rows if sub in k]
+        if not ks:
+            raise SystemExit(f"no kernel matching {sub!r} in the counter output")
+        vals = [v for k in ks for v in rows[k]]
+        return ks[0], vals
+
+    fetch = _pmc_rows(dirs[0], "FETCH_SIZE")
+    write = _pmc_rows(dirs[1], "WRITE_SIZE")
+    copy_k, f_copy = pick(fetch, "copy")
+    _, w_copy = pick(write, "copy")
+    rot_k, f_rot = pick(fetch, ROT_KERNEL)
+    _, w_rot = pick(write, ROT_KERNEL)
+    med = lambda v: sorted(v)[len(v) // 2]
+    f_fac = COPY_BYTES / (med(f_copy) * 1024)
+    w_fac = COPY_BYTES / (med(w_copy) * 1024)
+    rd = med(f_rot) * 1024 * f_fac
+    wr = med(w_rot) * 1024 * w_fac
+    rows, cols = 16384, 8192
+    alg = rows * cols * B_MX
+    lines = [
+        "# HBM traffic of the fused permutation + Hadamard + MXFP4 kernel (16384x8192)",
+        "",
+        "Counters: rocprofv3 `FETCH_SIZE` and `WRITE_SIZE` (KiB per dispatch), one pass each,",
+        "median over the dispatches of one run. Each is scaled by the same counter's reading",
+        "for torch's 1 GiB device-to-device copy in the same run (1 GiB read, 1 GiB written).",
+        "",
+        "| | FETCH_SIZE KiB | WRITE_SIZE KiB |",
+        "|---|---|---|",
+        f"| copy 1 GiB (`{copy_k[:60]}`) | {med(f_copy):.0f} | {med(w_copy):.0f} |",
+        f"| `{rot_k[:60]}` | {med(f_rot):.0f} | {med(w_rot):.0f} |",
+        "",
+        f"Scale factors: fetch {f_fac:.4f}, write {w_fac:.4f}.",
+        "",
+        f"Per launch: read {rd / 1e6:.1f} MB, written {wr / 1e6:.1f} MB, total "
+        f"{(rd + wr) / 1e6:.1f} MB against {alg / 1e6:.1f} MB algorithmic "
+        f"({(rd + wr) / alg:.3f}x).",
+        "",
+    ]
+    if len(dirs) > 2:
+        busy = _pmc_rows(dirs[2], "SQ_VALU_MFMA_BUSY_CYCLES")
+        cu = _pmc_rows(dirs[2], "SQ_BUSY_CU_CYCLES")
+        _, b = pick(busy, ROT_KERNEL)
+        _, c = pick(cu, ROT_KERNEL)
+        lines += [f"MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES = "
+                  f"{med(b) / max(med(c), 1):.4f} (median dispatch).", ""]
+    lines += [
+        "Commands (from the repository root, TMPDIR=/tmp):",
+        "",
+        "```",
+        "rocprofv3 --pmc FETCH_SIZE --kernel-trace -d <fetch_dir> -o run --output-format csv "
+        "-- python3 bench.py --steps 3 --warmup 1 --no-extras --no-cpu",
+        "rocprofv3 --pmc WRITE_SIZE --kernel-trace -d <write_dir> -o run --output-format csv "
+        "-- python3 bench.py --steps 3 --warmup 1 --no-extras --no-cpu",
+        "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES --kernel-trace -d <mfma_dir> "
+        "-o run --output-format csv -- python3 bench.py --steps 3 --warmup 1 --no-extras --no-cpu",
+        "python3 bench.py --pmc-summary <fetch_dir> <write_dir> <mfma_dir>",
+        "```",
+        "",
+        "Values read by bench.py (source_hash: sha256 of the kernel sources, first 16 hex):",
+        "",
+        f"- source_hash: `{rot_source_hash()}`",
+        f"- traffic_bytes_per_launch: {int(round(rd + wr))}",
+        f"- read_bytes_per_launch: {int(round(rd))}",
+        f"- write_bytes_per_launch: {int(round(wr))}",
+        f"- algorithmic_bytes_per_launch: {int(alg)}",
+    ]
+    print("\n".join(lines))
+
+
+def trace_summary(trace_dir, bench_log):
+    """Markdown per-kernel time summary of a profiled bench.py run."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not f:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = list(csv.DictReader(open(f[0])))
+    line = None
+    with open(bench_log) as fh:
+        for ln in fh:
+            if ln.startswith("{") and '"metric"' in ln:
+                line = json.loads(ln)
+    out = ["# Kernel times of one profiled bench.py run (16384x8192 workload and extras)", "",
+           "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].split("(")[0].replace("void ", "")
+        if not name.startswith("fp4::") and "copyBuffer" not in name:
+            continue
+        out.append(f"| `{name[:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    rot = [r for r in rows if ROT_KERNEL in r["Name"]]
+    out.append("")
+    if rot and line:
+        avg = float(rot[0]["AverageNs"]) / 1e3
+        ev = line["ms_per_step"] * 1e3
+        out += [f"The fused kernel `{ROT_KERNEL}` averages {avg:.2f} us per launch here (warm-up "
+                f"launches included); the same run's HIP-event time per step is {ev:.2f} us "
+                f"({ev / avg:.3f}x), one launch per step.", ""]
+    out += ["Command (from the repository root, TMPDIR=/tmp):", "", "```",
+            "rocprofv3 --kernel-trace --stats -d <trace_dir> -o run --output-format csv "
+            "-- python3 bench.py --steps 100 --warmup 20 --no-cpu > <bench_log>",
+            "python3 bench.py --trace-summary <trace_dir> <bench_log>", "```"]
+    print("\n".join(out))
+
+
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on one MI355X and has no "
               "multi-GPU mode (rows shard with no communication); run with --gpus 1",

@@ -9,8 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp4.so")
-SOURCES = ["quant.hip", "rotate.hip", "api.cpp", "perm.cpp"]
-HEADERS = ["fp4_device.hpp", "launch.hpp"]
+SOURCES = ["quant.hip", "rotate.hip", "unrotate.hip", "api.cpp", "perm.cpp", "device.cpp"]
+HEADERS = ["fp4_device.hpp", "launch.hpp", "rotation.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -15,6 +15,12 @@ constexpr int64_t kMaxPermCols = 16384;
 #endif
 constexpr int kPermGrid = FP4_PERM_GRID;
 
+// Compute units and LDS bytes per CU of the current device.
+struct DeviceInfo {
+  int cus, lds;
+};
+DeviceInfo device_info();
+
 struct Shape {
   int64_t rows, cols;
   int64_t ld_x;  // bf16 input (or output, for dequantize) row stride, elements

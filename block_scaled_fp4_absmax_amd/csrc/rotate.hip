@@ -1,5 +1,4 @@
-// rotate.hip -- two-level rotation fused with MXFP4 quantize + pack, the
-// inverse rotation for dequantization, and the channel-energy statistic.
+// rotate.hip -- two-level rotation fused with MXFP4 quantize + pack.
 //
 // "TORQ: Two-Level Orthogonal Rotation for MXFP4 Quantization", technical
 // summary sec. 2(a): an inter-block orthogonal transform that evens out the
@@ -22,15 +21,14 @@
 // A second implementation of the streaming (no permutation) kernel,
 // compile-time FP4_HADAMARD_MFMA=0, runs the transform as a radix-2 butterfly
 // in registers and DPP lane exchanges; it is kept for measuring one against
-// the other. The inverse rotation uses the butterfly (decode gives fp32 there).
+// the other. (The inverse rotation, unrotate.hip, uses the butterfly.)
 //
 // The permutation x'[j] = x[perm[j]] is applied by staging whole rows in LDS.
 // A work-group alternates between two LDS row buffers: while its lanes gather
 // the permuted elements of one row from one buffer (LDS reads of 2 bytes, or
 // 4, 8, 16 when perm moves aligned runs of channels), the next row, fetched
 // with coalesced 16-byte loads, is written to the other.
-#include "fp4_device.hpp"
-#include "launch.hpp"
+#include "rotation.hpp"
 
 #ifndef FP4_HADAMARD_MFMA
 #define FP4_HADAMARD_MFMA 1
@@ -39,146 +37,6 @@
 namespace fp4 {
 
 constexpr bool kUseMfma = FP4_HADAMARD_MFMA != 0;
-constexpr float kInvSqrt32 = 0.17677669529663688f;
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void widen8(u32x4_t d, float* v) {
-  v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
-  v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
-  v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z);
-  v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
-}
-
-__device__ __forceinline__ void store_rot8(float* rot, const float* y) {
-  f32x4_t a = {y[0], y[1], y[2], y[3]};
-  f32x4_t b = {y[4], y[5], y[6], y[7]};
-  __builtin_nontemporal_store(a, reinterpret_cast<f32x4_t*>(rot));
-  __builtin_nontemporal_store(b, reinterpret_cast<f32x4_t*>(rot) + 1);
-}
-
-// Largest |y| of n fp32 values as a bit pattern (NaN above Inf above finite).
-template <int n>
-__device__ __forceinline__ uint32_t absmax_bits(const float* y) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < n; ++k) m = max(m, __float_as_uint(y[k]) & 0x7FFFFFFFu);
-  return m;
-}
-
-// ============================ MFMA implementation ===========================
-// Row tau(m) of H held in MFMA output row m: lane half h' = (m / 4) % 2 owns
-// outputs 16h'..16h'+15, register r = 4 (m / 8) + m % 4 holds output 16h' + r.
-__device__ __forceinline__ uint32_t out_index_of_row(uint32_t m) {
-  return 16u * ((m >> 2) & 1u) + 4u * (m >> 3) + (m & 3u);
-}
-
-// Constant A operands: lane l holds A[m = l % 32][kk = 8 (l / 32) + j]; for
-// the first MFMA kk stands for element 16 (kk / 8) + kk % 8, for the second
-// 16 (kk / 8) + 8 + kk % 8 (matching the B halves each lane loads). So the 16
-// operand entries of lane l are H[tau(l % 32)][k0 + j], k0 = 16 (l / 32),
-// j = 0..15, with sign parity(row & (k0 + j)) = parity(row & k0) ^
-// parity(row & j); bit j of the Walsh mask W(row & 15) is parity(row & j).
-__device__ __forceinline__ void hadamard_operands(bf16x8_t& a0, bf16x8_t& a1) {
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t row = out_index_of_row(lane & 31u);
-  uint32_t m = ((row & 1u) ? 0xAAAAu : 0u) ^ ((row & 2u) ? 0xCCCCu : 0u) ^
-               ((row & 4u) ? 0xF0F0u : 0u) ^ ((row & 8u) ? 0xFF00u : 0u);
-  if ((lane >> 5) & (row >> 4)) m ^= 0xFFFFu;
-  u32x4_t v0, v1;
-  uint32_t w[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)  // bf16 pair: +-1 = 0x3F80 with the sign bit from the mask
-    w[i] = 0x3F803F80u | (((m >> (2 * i)) & 1u) << 15) | (((m >> (2 * i + 1)) & 1u) << 31);
-  v0 = u32x4_t{w[0], w[1], w[2], w[3]};
-  v1 = u32x4_t{w[4], w[5], w[6], w[7]};
-  a0 = __builtin_bit_cast(bf16x8_t, v0);
-  a1 = __builtin_bit_cast(bf16x8_t, v1);
-}
-
-// y[0..15] = (H x)[16h .. 16h+15] / sqrt(32) for this lane's block, from the
-// lane's 16 inputs x[16h .. 16h+15] (bf16 pairs in lo/hi).
-__device__ __forceinline__ void hadamard_mfma(const bf16x8_t& a0, const bf16x8_t& a1,
-                                              u32x4_t lo, u32x4_t hi, float* y) {
-  f32x16_t acc = {};
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, __builtin_bit_cast(bf16x8_t, lo), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, __builtin_bit_cast(bf16x8_t, hi), acc, 0, 0, 0);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) y[r] = acc[r] * kInvSqrt32;
-}
-
-// MXFP4-quantize the lane's 16 outputs; the block spans lanes l and l ^ 32.
-template <bool kFloor>
-__device__ __forceinline__ void mx_quant16_pair(const float* y, uint32_t& w0, uint32_t& w1,
-                                                uint32_t& byte) {
-  uint32_t m = absmax_bits<16>(y);
-  m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
-  byte = e8m0_byte<kFloor>(m);
-  if (byte == 0xFFu) {
-    w0 = w1 = 0u;
-  } else {
-    const float s = e8m0_operand(byte);
-    w0 = cvt8_f32(y, s);
-    w1 = cvt8_f32(y + 8, s);
-  }
-}
-
-// ========================= butterfly implementation =========================
-// Lane q of a group of four holds elements 8q..8q+7: bits 0-2 of the index
-// are butterflies inside the lane, bits 3-4 exchanges with lane q ^ 1 and
-// q ^ 2 (DPP), folded as partner + (+-own) and, for the last stage,
-// partner * c + (+-c * own) with c = 1/sqrt(32).
-__device__ __forceinline__ float dpp1(float v) {
-  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0xB1,
-                                                               0xF, 0xF, true));
-}
-__device__ __forceinline__ float dpp2(float v) {
-  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x4E,
-                                                               0xF, 0xF, true));
-}
-
-__device__ __forceinline__ void hadamard_butterfly(float* v, uint32_t q) {
-#pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (k & h) continue;
-      float a = v[k], b = v[k + h];
-      v[k] = a + b;
-      v[k + h] = a - b;
-    }
-  }
-  const float s1 = (q & 1u) ? -1.0f : 1.0f;
-  const float s2 = (q & 2u) ? -kInvSqrt32 : kInvSqrt32;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    float u = s1 * v[k];
-    v[k] = dpp1(v[k]) + u;
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    float u = s2 * v[k];
-    v[k] = __builtin_fmaf(dpp2(v[k]), kInvSqrt32, u);
-  }
-}
-
-template <bool kFloor>
-__device__ __forceinline__ void mx_quant8_quad(const float* y, uint32_t& w, uint32_t& byte) {
-  uint32_t m = absmax_bits<8>(y);
-  m = max(m, dpp_xor1(m));
-  m = max(m, dpp_xor2(m));
-  byte = e8m0_byte<kFloor>(m);
-  w = byte == 0xFFu ? 0u : cvt8_f32(y, e8m0_operand(byte));
-}
-
-struct RotGeom {
-  int32_t rows, cols;
-  int32_t bpr;   // 32-element blocks per row
-  uint32_t nblk; // rows * bpr
-  int64_t ld_x, ld_c, ld_s, ld_rot;
-};
 
 // ===================== streaming kernels (no permutation) ===================
 // MFMA: a wave owns a tile of 32 consecutive blocks (row-major block order).
@@ -189,8 +47,6 @@ struct RotGeom {
 #define FP4_TILES 1
 #endif
 constexpr int kTiles = FP4_TILES;
-
-constexpr int kWaves = kThreads / 64;
 
 template <bool kFlat, bool kHad, bool kFloor, bool kRot>
 __global__ __launch_bounds__(kThreads) void mx_rotq_stream_mfma_kernel(
@@ -550,152 +406,27 @@ __global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void mx_rotq_perm_kernel(
     perm_rows<1, kTpw, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g, pre);
 }
 
-// ============================ inverse rotation ==============================
-// perm staged into LDS as uint16, clamped to [0, cols - 1] (cols <= 16384):
-// sixteen 16-byte loads per lane in flight at once, then one wait.
-__device__ __forceinline__ void stage_perm(const int32_t* __restrict__ perm, uint16_t* sperm,
-                                           int32_t cols) {
-  constexpr int kPv = (int)(kMaxPermCols / 4 / kThreads);
-  const rsrc_t rp = make_rsrc(perm, 4u * (uint32_t)cols);
-  const int32_t nv = cols / 4, cmax = cols - 1;
-  i32x4_t p[kPv];
-#pragma unroll
-  for (int u = 0; u < kPv; ++u) {
-    const int32_t v = threadIdx.x + u * kThreads;
-    p[u] = __builtin_bit_cast(
-        i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, v < nv ? 16u * v : kOob, 0, 0));
-  }
-#pragma unroll
-  for (int u = 0; u < kPv; ++u) {
-    const int32_t v = threadIdx.x + u * kThreads;
-    if (v < nv) {
-      const i32x4_t q = p[u];
-      const uint32_t c0 = (uint32_t)min(max(q.x, 0), cmax), c1 = (uint32_t)min(max(q.y, 0), cmax);
-      const uint32_t c2 = (uint32_t)min(max(q.z, 0), cmax), c3 = (uint32_t)min(max(q.w, 0), cmax);
-      reinterpret_cast<u32x2_t*>(sperm)[v] = u32x2_t{c0 | (c1 << 16), c2 | (c3 << 16)};
-    }
-  }
-  __syncthreads();
-}
-
-// Decode MXFP4 exactly to fp32, apply H (its own inverse) with the butterfly,
-// then scatter element j to column perm[j] through LDS.
-template <bool kHad, bool kPerm>
-__global__ __launch_bounds__(kThreads) void mx_dequant_unrotate_kernel(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const int32_t* __restrict__ perm, uint16_t* __restrict__ out, RotGeom g) {
-  extern __shared__ uint16_t smem[];
-  uint16_t* srow = smem;
-  uint16_t* sperm = smem + g.cols;
-  const uint32_t q = threadIdx.x & 3u;
-  const int32_t cpr = g.cols / 8;
-  if (kPerm) stage_perm(perm, sperm, g.cols);
-  for (int32_t r = blockIdx.x; r < g.rows; r += gridDim.x) {
-    if (kPerm) __syncthreads();  // previous row copied out, indices visible
-    for (int32_t c = threadIdx.x; c < cpr; c += kThreads) {
-      uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * g.ld_c + 4 * (int64_t)c);
-      float s = e8m0_operand(scales[r * g.ld_s + c / 4]);
-      float y[8];
-      float2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 0);
-      float2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 1);
-      float2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 2);
-      float2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 3);
-      y[0] = p0.x; y[1] = p0.y; y[2] = p1.x; y[3] = p1.y;
-      y[4] = p2.x; y[5] = p2.y; y[6] = p3.x; y[7] = p3.y;
-      if (kHad) hadamard_butterfly(y, q);
-      u32x4_t o;
-      o.x = pack_bf16x2(y[0], y[1]);
-      o.y = pack_bf16x2(y[2], y[3]);
-      o.z = pack_bf16x2(y[4], y[5]);
-      o.w = pack_bf16x2(y[6], y[7]);
-      if (kPerm) {
-        u32x4_t id = reinterpret_cast<const u32x4_t*>(sperm)[c];
-        srow[id.x & 0xFFFFu] = (uint16_t)(o.x & 0xFFFFu);
-        srow[id.x >> 16] = (uint16_t)(o.x >> 16);
-        srow[id.y & 0xFFFFu] = (uint16_t)(o.y & 0xFFFFu);
-        srow[id.y >> 16] = (uint16_t)(o.y >> 16);
-        srow[id.z & 0xFFFFu] = (uint16_t)(o.z & 0xFFFFu);
-        srow[id.z >> 16] = (uint16_t)(o.z >> 16);
-        srow[id.w & 0xFFFFu] = (uint16_t)(o.w & 0xFFFFu);
-        srow[id.w >> 16] = (uint16_t)(o.w >> 16);
-      } else {
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + r * g.ld_x) + c);
-      }
-    }
-    if (kPerm) {
-      __syncthreads();
-      for (int32_t c = threadIdx.x; c < cpr; c += kThreads)
-        __builtin_nontemporal_store(reinterpret_cast<const u32x4_t*>(srow)[c],
-                                    reinterpret_cast<u32x4_t*>(out + r * g.ld_x) + c);
-    }
-  }
-}
-
-// ============================== channel energy ==============================
-// One work-group per 32-column slice; lane (q, rg) = (t & 3, t >> 2) adds the
-// squares of chunk q of rows rg, rg + 64, ... in fp64; the 64 partial sums of
-// each column are then added in row-group order, so the result does not
-// depend on scheduling.
-__global__ __launch_bounds__(kThreads) void channel_energy_kernel(const uint16_t* __restrict__ x,
-                                                                  float* __restrict__ energy,
-                                                                  int64_t rows, int64_t ld_x) {
-  __shared__ double part[kThreads / 4][33];
-  const int q = threadIdx.x & 3, rg = threadIdx.x >> 2;
-  const int64_t col0 = 32 * (int64_t)blockIdx.x + 8 * q;
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t r = rg; r < rows; r += kThreads / 4) {
-    u32x4_t d = *reinterpret_cast<const u32x4_t*>(x + r * ld_x + col0);
-    float v[8];
-    widen8(d, v);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] += (double)v[k] * (double)v[k];
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) part[rg][8 * q + k] = acc[k];
-  __syncthreads();
-  if (threadIdx.x < 32) {
-    double s = 0.0;
-    for (int i = 0; i < kThreads / 4; ++i) s += part[i][threadIdx.x];
-    energy[32 * (int64_t)blockIdx.x + threadIdx.x] = (float)s;
-  }
-}
-
 // ================================ launchers =================================
-static RotGeom rot_geom(const Shape& s, int64_t ld_rot) {
-  RotGeom g;
-  g.rows = (int32_t)s.rows;
-  g.cols = (int32_t)s.cols;
-  g.bpr = (int32_t)(s.cols / 32);
-  g.nblk = (uint32_t)(s.rows * (s.cols / 32));
-  g.ld_x = s.ld_x;
-  g.ld_c = s.ld_c;
-  g.ld_s = s.ld_s;
-  g.ld_rot = ld_rot;
-  return g;
-}
-
-static int perm_grid(int64_t rows) { return (int)(rows < kPermGrid ? rows : kPermGrid); }
-
-// Compute units of the current device.
-static int cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    n = 256;
-  return n;
-}
-
+// Each work-group owns a fixed share of the rows, so the grid is balanced
+// only if every CU holds the same number of work-groups: the launch asks for
+// enough (unused) dynamic LDS that no more than perm_wgs_per_cu fit on a CU,
+// and launches exactly that many per CU.
 template <int kTpw, bool kHad, bool kFloor, bool kRot>
 static void perm_launch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
                         uint8_t* sc, float* rot, const RotGeom& g, hipStream_t st) {
 #ifdef FP4_PERM_WG_PER_CU
-  const int64_t wgs = (int64_t)cu_count() * FP4_PERM_WG_PER_CU;
+  constexpr int kWgs = FP4_PERM_WG_PER_CU;
 #else
-  const int64_t wgs = (int64_t)cu_count() * perm_wgs_per_cu<kTpw>();
+  constexpr int kWgs = perm_wgs_per_cu<kTpw>();
 #endif
+  const DeviceInfo ci = device_info();
+  const int64_t wgs = (int64_t)ci.cus * kWgs;
   const int grid = (int)(s.rows < wgs ? s.rows : wgs);
+  constexpr size_t kStatic = 2 * 8192 * kTpw;
+  const size_t share = (size_t)ci.lds / kWgs;  // > lds / (kWgs + 1), so kWgs fit, not more
+  const size_t pad = share > kStatic + 1024 ? share - kStatic - 1024 : 0;
   hipLaunchKernelGGL((mx_rotq_perm_kernel<kTpw, kHad, kFloor, kRot>), dim3(grid), dim3(kThreads),
-                     0, st, x, perm, c, sc, rot, g);
+                     pad, st, x, perm, c, sc, rot, g);
 }
 
 template <bool kHad, bool kFloor, bool kRot>
@@ -749,31 +480,6 @@ void launch_mx_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, b
   if (!had && !floor_rule && r) rotq_dispatch<false, false, true>(s, perm, xp, cp, sp, rot, g, flat, st);
   if (!had && floor_rule && !r) rotq_dispatch<false, true, false>(s, perm, xp, cp, sp, rot, g, flat, st);
   if (!had && floor_rule && r) rotq_dispatch<false, true, true>(s, perm, xp, cp, sp, rot, g, flat, st);
-}
-
-void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard,
-                                const void* codes, const void* scales, void* out, hipStream_t st) {
-  RotGeom g = rot_geom(s, 0);
-  auto cp = static_cast<const uint8_t*>(codes);
-  auto sp = static_cast<const uint8_t*>(scales);
-  auto op = static_cast<uint16_t*>(out);
-  const int grid = perm_grid(s.rows);
-  size_t lds = perm ? (size_t)4 * s.cols : 0;
-  if (hadamard && perm)
-    hipLaunchKernelGGL((mx_dequant_unrotate_kernel<true, true>), dim3(grid), dim3(kThreads), lds,
-                       st, cp, sp, perm, op, g);
-  if (hadamard && !perm)
-    hipLaunchKernelGGL((mx_dequant_unrotate_kernel<true, false>), dim3(grid), dim3(kThreads), lds,
-                       st, cp, sp, perm, op, g);
-  if (!hadamard && perm)
-    hipLaunchKernelGGL((mx_dequant_unrotate_kernel<false, true>), dim3(grid), dim3(kThreads), lds,
-                       st, cp, sp, perm, op, g);
-}
-
-void launch_channel_energy(int64_t rows, int64_t cols, int64_t ld_x, const void* x, float* energy,
-                           hipStream_t st) {
-  hipLaunchKernelGGL(channel_energy_kernel, dim3((int)(cols / 32)), dim3(kThreads), 0, st,
-                     static_cast<const uint16_t*>(x), energy, rows, ld_x);
 }
 
 }  // namespace fp4

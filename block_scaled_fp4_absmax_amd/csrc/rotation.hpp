@@ -1,0 +1,171 @@
+// rotation.hpp -- helpers shared by the rotation kernels: the 32-point block
+// Hadamard (MFMA and butterfly forms), MXFP4 quantization of rotated fp32
+// values, and the row geometry.
+//
+// "TORQ: Two-Level Orthogonal Rotation for MXFP4 Quantization", technical
+// summary sec. 2(b): a rotation inside each 32-block, here the orthonormal
+// Sylvester-Hadamard matrix H[i][j] = (-1)^popcount(i & j) / sqrt(32).
+#pragma once
+
+#include "fp4_device.hpp"
+#include "launch.hpp"
+
+namespace fp4 {
+
+constexpr float kInvSqrt32 = 0.17677669529663688f;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void widen8(u32x4_t d, float* v) {
+  v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
+  v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
+  v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z);
+  v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
+}
+
+__device__ __forceinline__ void store_rot8(float* rot, const float* y) {
+  f32x4_t a = {y[0], y[1], y[2], y[3]};
+  f32x4_t b = {y[4], y[5], y[6], y[7]};
+  __builtin_nontemporal_store(a, reinterpret_cast<f32x4_t*>(rot));
+  __builtin_nontemporal_store(b, reinterpret_cast<f32x4_t*>(rot) + 1);
+}
+
+// Largest |y| of n fp32 values as a bit pattern (NaN above Inf above finite).
+template <int n>
+__device__ __forceinline__ uint32_t absmax_bits(const float* y) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < n; ++k) m = max(m, __float_as_uint(y[k]) & 0x7FFFFFFFu);
+  return m;
+}
+
+// ============================ MFMA implementation ===========================
+// Row tau(m) of H held in MFMA output row m: lane half h' = (m / 4) % 2 owns
+// outputs 16h'..16h'+15, register r = 4 (m / 8) + m % 4 holds output 16h' + r.
+__device__ __forceinline__ uint32_t out_index_of_row(uint32_t m) {
+  return 16u * ((m >> 2) & 1u) + 4u * (m >> 3) + (m & 3u);
+}
+
+// Constant A operands: lane l holds A[m = l % 32][kk = 8 (l / 32) + j]; for
+// the first MFMA kk stands for element 16 (kk / 8) + kk % 8, for the second
+// 16 (kk / 8) + 8 + kk % 8 (matching the B halves each lane loads). So the 16
+// operand entries of lane l are H[tau(l % 32)][k0 + j], k0 = 16 (l / 32),
+// j = 0..15, with sign parity(row & (k0 + j)) = parity(row & k0) ^
+// parity(row & j); bit j of the Walsh mask W(row & 15) is parity(row & j).
+__device__ __forceinline__ void hadamard_operands(bf16x8_t& a0, bf16x8_t& a1) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t row = out_index_of_row(lane & 31u);
+  uint32_t m = ((row & 1u) ? 0xAAAAu : 0u) ^ ((row & 2u) ? 0xCCCCu : 0u) ^
+               ((row & 4u) ? 0xF0F0u : 0u) ^ ((row & 8u) ? 0xFF00u : 0u);
+  if ((lane >> 5) & (row >> 4)) m ^= 0xFFFFu;
+  u32x4_t v0, v1;
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)  // bf16 pair: +-1 = 0x3F80 with the sign bit from the mask
+    w[i] = 0x3F803F80u | (((m >> (2 * i)) & 1u) << 15) | (((m >> (2 * i + 1)) & 1u) << 31);
+  v0 = u32x4_t{w[0], w[1], w[2], w[3]};
+  v1 = u32x4_t{w[4], w[5], w[6], w[7]};
+  a0 = __builtin_bit_cast(bf16x8_t, v0);
+  a1 = __builtin_bit_cast(bf16x8_t, v1);
+}
+
+// y[0..15] = (H x)[16h .. 16h+15] / sqrt(32) for this lane's block, from the
+// lane's 16 inputs x[16h .. 16h+15] (bf16 pairs in lo/hi).
+__device__ __forceinline__ void hadamard_mfma(const bf16x8_t& a0, const bf16x8_t& a1,
+                                              u32x4_t lo, u32x4_t hi, float* y) {
+  f32x16_t acc = {};
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, __builtin_bit_cast(bf16x8_t, lo), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, __builtin_bit_cast(bf16x8_t, hi), acc, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) y[r] = acc[r] * kInvSqrt32;
+}
+
+// MXFP4-quantize the lane's 16 outputs; the block spans lanes l and l ^ 32.
+template <bool kFloor>
+__device__ __forceinline__ void mx_quant16_pair(const float* y, uint32_t& w0, uint32_t& w1,
+                                                uint32_t& byte) {
+  uint32_t m = absmax_bits<16>(y);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+  byte = e8m0_byte<kFloor>(m);
+  if (byte == 0xFFu) {
+    w0 = w1 = 0u;
+  } else {
+    const float s = e8m0_operand(byte);
+    w0 = cvt8_f32(y, s);
+    w1 = cvt8_f32(y + 8, s);
+  }
+}
+
+// ========================= butterfly implementation =========================
+// Lane q of a group of four holds elements 8q..8q+7: bits 0-2 of the index
+// are butterflies inside the lane, bits 3-4 exchanges with lane q ^ 1 and
+// q ^ 2 (DPP), folded as partner + (+-own) and, for the last stage,
+// partner * c + (+-c * own) with c = 1/sqrt(32).
+__device__ __forceinline__ float dpp1(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0xB1,
+                                                               0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp2(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x4E,
+                                                               0xF, 0xF, true));
+}
+
+__device__ __forceinline__ void hadamard_butterfly(float* v, uint32_t q) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k & h) continue;
+      float a = v[k], b = v[k + h];
+      v[k] = a + b;
+      v[k + h] = a - b;
+    }
+  }
+  const float s1 = (q & 1u) ? -1.0f : 1.0f;
+  const float s2 = (q & 2u) ? -kInvSqrt32 : kInvSqrt32;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float u = s1 * v[k];
+    v[k] = dpp1(v[k]) + u;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float u = s2 * v[k];
+    v[k] = __builtin_fmaf(dpp2(v[k]), kInvSqrt32, u);
+  }
+}
+
+template <bool kFloor>
+__device__ __forceinline__ void mx_quant8_quad(const float* y, uint32_t& w, uint32_t& byte) {
+  uint32_t m = absmax_bits<8>(y);
+  m = max(m, dpp_xor1(m));
+  m = max(m, dpp_xor2(m));
+  byte = e8m0_byte<kFloor>(m);
+  w = byte == 0xFFu ? 0u : cvt8_f32(y, e8m0_operand(byte));
+}
+
+constexpr int kWaves = kThreads / 64;  // waves per work-group
+
+struct RotGeom {
+  int32_t rows, cols;
+  int32_t bpr;   // 32-element blocks per row
+  uint32_t nblk; // rows * bpr
+  int64_t ld_x, ld_c, ld_s, ld_rot;
+};
+
+inline RotGeom rot_geom(const Shape& s, int64_t ld_rot) {
+  RotGeom g;
+  g.rows = (int32_t)s.rows;
+  g.cols = (int32_t)s.cols;
+  g.bpr = (int32_t)(s.cols / 32);
+  g.nblk = (uint32_t)(s.rows * (s.cols / 32));
+  g.ld_x = s.ld_x;
+  g.ld_c = s.ld_c;
+  g.ld_s = s.ld_s;
+  g.ld_rot = ld_rot;
+  return g;
+}
+
+}  // namespace fp4
