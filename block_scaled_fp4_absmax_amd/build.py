@@ -19,6 +19,8 @@ FLAGS = [
     "-ffp-contract=off", "-fno-fast-math",
     # no packed-fp32 VALU instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs (no copies out of accumulation registers)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -28,6 +28,8 @@
 // the permuted elements of one row from one buffer (LDS reads of 2 bytes, or
 // 4, 8, 16 when perm moves aligned runs of channels), the next row, fetched
 // with coalesced 16-byte loads, is written to the other.
+#include <utility>
+
 #include "rotation.hpp"
 
 #ifndef FP4_HADAMARD_MFMA
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void mx_rotq_stream_mfma_kernel(
       widen8(hi[u], y + 8);
     }
     uint32_t w0, w1, byte;
-    mx_quant16_pair<kFloor>(y, w0, w1, byte);
+    mx_quant16_pair<kFloor, kHad>(y, w0, w1, byte);
     if (ok[u]) {
       uint32_t* cp = reinterpret_cast<uint32_t*>(codes + co[u]);
       __builtin_nontemporal_store(w0, cp);
@@ -283,127 +285,171 @@ __device__ __forceinline__ void gather_tile(const uint8_t* buf, const uint32_t* 
   }
 }
 
-// One row step: stage the next row (already loaded into pre) into the other
-// buffer, load the row after it into pre, then gather, rotate, quantize and
-// store row r from buffer kBuf; a barrier closes the step.
-template <int G, int kTpw, int kBuf, bool kHad, bool kFloor, bool kRot>
-__device__ __forceinline__ void perm_step(const uint16_t* __restrict__ x, uint8_t* sbuf,
-                                          const uint32_t (*off)[8], const bf16x8_t& a0,
-                                          const bf16x8_t& a1, uint8_t* __restrict__ codes,
-                                          uint8_t* __restrict__ scales, float* __restrict__ rot,
-                                          const RotGeom& g, int32_t r, bool has_next,
-                                          u32x4_t* pre) {
-  constexpr int kCpl = 2 * kTpw;
-  constexpr uint32_t kBufBytes = 8192u * kTpw;
-  const int32_t cpr = g.cols / 8;
-  const int32_t G_ = gridDim.x;
-  if (has_next) put_row<kCpl>(sbuf + (1 - kBuf) * kBufBytes, cpr, pre);
-  load_row<kCpl>(row_rsrc<kRot>(x, codes, scales, rot, r + 2 * G_, g).x, cpr, pre);
-  const RowRsrc q = row_rsrc<kRot>(x, codes, scales, rot, r, g);
-  const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < kTpw; ++i) {
-    const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kWaves * i) + (int32_t)n;
-    const bool ok = b < g.bpr;
-    u32x4_t lo, hi;
-    gather_tile<G, kBuf * kBufBytes>(sbuf, off[i], lo, hi);
-    float y[16];
-    if (kHad) {
-      hadamard_mfma(a0, a1, lo, hi, y);
-    } else {
-      widen8(lo, y);
-      widen8(hi, y + 8);
-    }
-    uint32_t w0, w1, byte;
-    mx_quant16_pair<kFloor>(y, w0, w1, byte);
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w0, w1}, q.c, ok ? 16u * b + 8u * h : kOob, 0,
-                                          kNt);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, q.s, ok && h == 0 ? (uint32_t)b : kOob,
-                                         0, 0);
-    if (kRot) {
-      const uint32_t o = ok ? 4u * (32u * b + 16u * h) : kOob;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(u32x4_t, f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]}),
-            q.rot, o == kOob ? kOob : o + 16u * k, 0, kNt);
-    }
-  }
-  __syncthreads();
-}
+// State shared by the row steps of one work-group.
+template <int kTpw, int kAhead>
+struct PermCtx {
+  const uint16_t* __restrict__ x;
+  uint8_t* sbuf;                       // two LDS row buffers
+  uint32_t (*off)[8];                  // the lane's gather offsets, per tile
+  bf16x8_t a0, a1;                     // Hadamard MFMA operands
+  uint8_t* __restrict__ codes;
+  uint8_t* __restrict__ scales;
+  float* __restrict__ rot;
+  RotGeom g;
+  u32x4_t (*pre)[2 * kTpw];            // kAhead register buffers of rows in flight
+};
 
-// Rows r0 + k G, k < K. Step 0 is peeled and the loop takes steps in pairs
-// (buffer 1, then 0), so every path into a step's wait has the same memory
-// operations after the loads it waits for: the previous step's stores.
-template <int G, int kTpw, bool kHad, bool kFloor, bool kRot>
-__device__ __forceinline__ void perm_rows(const uint16_t* __restrict__ x, uint8_t* sbuf,
-                                          const uint32_t (*off)[8], const bf16x8_t& a0,
-                                          const bf16x8_t& a1, uint8_t* __restrict__ codes,
-                                          uint8_t* __restrict__ scales, float* __restrict__ rot,
-                                          const RotGeom& g, u32x4_t* pre) {
-  const int32_t G_ = gridDim.x, r0 = blockIdx.x;
-  const int32_t K = (g.rows - r0 + G_ - 1) / G_;
-  perm_step<G, kTpw, 0, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g, r0,
-                                            K > 1, pre);
-  int32_t k = 1;
-  for (; k + 1 < K; k += 2) {
-    perm_step<G, kTpw, 1, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g,
-                                              r0 + k * G_, true, pre);
-    perm_step<G, kTpw, 0, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g,
-                                              r0 + (k + 1) * G_, k + 2 < K, pre);
-  }
-  if (k < K)
-    perm_step<G, kTpw, 1, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g,
-                                              r0 + k * G_, false, pre);
-}
+// Rows r0 + k G (G = grid size), k < K. Row k is gathered from LDS buffer
+// k % 2; during its step, rows k + 1 .. k + kAhead are in flight in register
+// buffers (row j in buffer j % kAhead). A step stages row k + 1 into the other
+// LDS buffer, loads row k + 1 + kAhead into the register buffer just freed,
+// then gathers, rotates, quantizes and stores row k; a barrier closes it.
+// Step 0 is peeled and the loop runs whole groups of U = lcm(2, kAhead) steps,
+// so both buffer choices are compile-time constants and every path into a
+// step's wait has at least the steady state's memory operations after the
+// loads it waits for; a tail takes the last steps.
+template <int G, int kTpw, int kAhead, bool kHad, bool kFloor, bool kRot>
+struct PermRows {
+  using Ctx = PermCtx<kTpw, kAhead>;
+  static constexpr int kCpl = 2 * kTpw;
+  static constexpr uint32_t kBufBytes = 8192u * kTpw;
+  static constexpr int U = kAhead % 2 == 0 ? kAhead : 2 * kAhead;
 
-// Waves per SIMD the register allocation is held to, and work-groups per CU
-// in the grid. Two row buffers of 8 KB kTpw each bound the work-groups a CU
-// can hold; on MI355X at cols = 8192 two per CU (32 rows each) measured
-// faster than three or four, and one per CU slower.
-template <int kTpw>
-constexpr int perm_waves_cap() {
-  return kTpw <= 2 ? 4 : 2;
-}
+  // kS = k mod U for the step of row k
+  template <int kS>
+  static __device__ __forceinline__ void step(const Ctx& c, int32_t r, bool has_next) {
+    constexpr int kBuf = kS & 1;
+    u32x4_t* pre = c.pre[(kS + 1) % kAhead];
+    const RotGeom& g = c.g;
+    const int32_t cpr = g.cols / 8;
+    if (has_next) put_row<kCpl>(c.sbuf + (1 - kBuf) * kBufBytes, cpr, pre);
+    load_row<kCpl>(row_rsrc<kRot>(c.x, c.codes, c.scales, c.rot,
+                                  r + (1 + kAhead) * (int32_t)gridDim.x, g).x,
+                   cpr, pre);
+    const RowRsrc q = row_rsrc<kRot>(c.x, c.codes, c.scales, c.rot, r, g);
+    const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < kTpw; ++i) {
+      const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kWaves * i) + (int32_t)n;
+      const bool ok = b < g.bpr;
+      u32x4_t lo, hi;
+      gather_tile<G, kBuf * kBufBytes>(c.sbuf, c.off[i], lo, hi);
+      float y[16];
+      if (kHad) {
+        hadamard_mfma(c.a0, c.a1, lo, hi, y);
+      } else {
+        widen8(lo, y);
+        widen8(hi, y + 8);
+      }
+      uint32_t w0, w1, byte;
+      mx_quant16_pair<kFloor, kHad>(y, w0, w1, byte);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w0, w1}, q.c, ok ? 16u * b + 8u * h : kOob,
+                                            0, kNt);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, q.s,
+                                           ok && h == 0 ? (uint32_t)b : kOob, 0, 0);
+      if (kRot) {
+        const uint32_t o = ok ? 4u * (32u * b + 16u * h) : kOob;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u32x4_t,
+                                 f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]}),
+              q.rot, o == kOob ? kOob : o + 16u * k, 0, kNt);
+      }
+    }
+    __syncthreads();
+  }
+
+  // Steps k .. k + U - 1 (k = 1 mod U), all present.
+  template <int... us>
+  static __device__ __forceinline__ void group(const Ctx& c, int32_t k, int32_t K,
+                                               std::integer_sequence<int, us...>) {
+    const int32_t G_ = gridDim.x, r0 = blockIdx.x;
+    (step<(1 + us) % U>(c, r0 + (k + us) * G_, k + us + 1 < K), ...);
+  }
+
+  // Steps k .. K - 1, fewer than U.
+  template <int... us>
+  static __device__ __forceinline__ void tail(const Ctx& c, int32_t k, int32_t K,
+                                              std::integer_sequence<int, us...>) {
+    const int32_t G_ = gridDim.x, r0 = blockIdx.x;
+    (void)((k + us < K ? (step<(1 + us) % U>(c, r0 + (k + us) * G_, k + us + 1 < K), true)
+                       : false) &&
+           ...);
+  }
+
+  static __device__ __forceinline__ void run(const Ctx& c) {
+    const int32_t G_ = gridDim.x, r0 = blockIdx.x;
+    const int32_t K = (c.g.rows - r0 + G_ - 1) / G_;
+    step<0>(c, r0, K > 1);
+    int32_t k = 1;
+    for (; k + U - 1 < K; k += U) group(c, k, K, std::make_integer_sequence<int, U>{});
+    tail(c, k, K, std::make_integer_sequence<int, U - 1>{});
+  }
+};
+
+// Tuning per row length (kTpw tiles per wave per row; measured on MI355X at
+// cols = 8192): work-groups per CU in the grid, rows of look-ahead held in
+// registers, and the waves per SIMD the register allocation is held to. Two
+// row buffers of 8 KB kTpw each bound the work-groups a CU can hold; two per
+// CU (32 rows each at 16384 rows) ran faster than three or four, and one per
+// CU slower. A second row of look-ahead gained about 1%, more none.
 template <int kTpw>
 constexpr int perm_wgs_per_cu() {
+  return kTpw == 1 ? 4 : 2;
+}
+template <int kTpw>
+constexpr int perm_ahead() {
+  return kTpw <= 2 ? 2 : 1;
+}
+template <int kTpw>
+constexpr int perm_waves_cap() {
   return kTpw == 1 ? 4 : 2;
 }
 
 #ifndef FP4_PERM_WAVES
 #define FP4_PERM_WAVES perm_waves_cap<kTpw>()
 #endif
+#ifndef FP4_PERM_AHEAD
+#define FP4_PERM_AHEAD perm_ahead<kTpw>()
+#endif
+
 template <int kTpw, bool kHad, bool kFloor, bool kRot>
 __global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void mx_rotq_perm_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ rot, RotGeom g) {
   constexpr int kCpl = 2 * kTpw;
+  constexpr int kAhead = FP4_PERM_AHEAD;  // rows in flight in registers beyond the next
   __shared__ __attribute__((aligned(16))) uint8_t sbuf[2 * 8192 * kTpw];
   const int32_t cpr = g.cols / 8;
-  // perm entries first, then row r0, so the row load is in flight while the
-  // entries are unpacked
+  // perm entries first, then rows 0 .. kAhead, so the row loads are in flight
+  // while the entries are unpacked
   i32x4_t v[kTpw][4];
   load_lane_perm<kTpw>(perm, g, v);
-  u32x4_t pre[kCpl];
-  load_row<kCpl>(row_rsrc<kRot>(x, codes, scales, rot, blockIdx.x, g).x, cpr, pre);
+  u32x4_t first[kCpl], pre[kAhead][kCpl];
+  load_row<kCpl>(row_rsrc<kRot>(x, codes, scales, rot, blockIdx.x, g).x, cpr, first);
+#pragma unroll
+  for (int j = 1; j <= kAhead; ++j)
+    load_row<kCpl>(row_rsrc<kRot>(x, codes, scales, rot, blockIdx.x + j * gridDim.x, g).x, cpr,
+                   pre[j % kAhead]);
   uint32_t off[kTpw][8];
   const int lr = pack_lane_perm<kTpw>(v, g, off);
   bf16x8_t a0, a1;
   hadamard_operands(a0, a1);
-  put_row<kCpl>(sbuf, cpr, pre);
-  load_row<kCpl>(row_rsrc<kRot>(x, codes, scales, rot, blockIdx.x + gridDim.x, g).x, cpr, pre);
+  put_row<kCpl>(sbuf, cpr, first);
   // run length agreed by the whole work-group (this also publishes row r0)
   const int run = __syncthreads_and(lr >= 8) ? 8
                   : __syncthreads_and(lr >= 4) ? 4
                   : __syncthreads_and(lr >= 2) ? 2 : 1;
+  PermCtx<kTpw, kAhead> c{x, sbuf, off, a0, a1, codes, scales, rot, g, pre};
   if (run == 8)
-    perm_rows<8, kTpw, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g, pre);
+    PermRows<8, kTpw, kAhead, kHad, kFloor, kRot>::run(c);
   else if (run == 4)
-    perm_rows<4, kTpw, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g, pre);
+    PermRows<4, kTpw, kAhead, kHad, kFloor, kRot>::run(c);
   else if (run == 2)
-    perm_rows<2, kTpw, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g, pre);
+    PermRows<2, kTpw, kAhead, kHad, kFloor, kRot>::run(c);
   else
-    perm_rows<1, kTpw, kHad, kFloor, kRot>(x, sbuf, off, a0, a1, codes, scales, rot, g, pre);
+    PermRows<1, kTpw, kAhead, kHad, kFloor, kRot>::run(c);
 }
 
 // ================================ launchers =================================

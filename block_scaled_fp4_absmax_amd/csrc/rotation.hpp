@@ -82,12 +82,31 @@ __device__ __forceinline__ void hadamard_mfma(const bf16x8_t& a0, const bf16x8_t
   for (int r = 0; r < 16; ++r) y[r] = acc[r] * kInvSqrt32;
 }
 
+// Largest |y| of 16 fp32 values as a bit pattern, for values that are the
+// Hadamard transform of a block: a NaN or Inf input makes every output of the
+// block NaN or +-Inf, so a float maximum of magnitudes (which may drop a NaN
+// operand in favour of another) still yields a non-finite result for such a
+// block, and for finite values its bits order like the magnitudes.
+__device__ __forceinline__ uint32_t absmax16_mixed(const float* y) {
+  float m = __builtin_fmaxf(__builtin_fabsf(y[0]), __builtin_fabsf(y[1]));
+#pragma unroll
+  for (int k = 2; k < 16; k += 2)  // three-operand maxima
+    m = __builtin_fmaxf(__builtin_fmaxf(m, __builtin_fabsf(y[k])), __builtin_fabsf(y[k + 1]));
+  return __float_as_uint(m);
+}
+
+// Larger of v in lanes l and l ^ 32 (gfx950 lane-half swap).
+__device__ __forceinline__ uint32_t max_xor32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+
 // MXFP4-quantize the lane's 16 outputs; the block spans lanes l and l ^ 32.
-template <bool kFloor>
+// kMixed: y is a Hadamard transform of the block (see absmax16_mixed).
+template <bool kFloor, bool kMixed>
 __device__ __forceinline__ void mx_quant16_pair(const float* y, uint32_t& w0, uint32_t& w1,
                                                 uint32_t& byte) {
-  uint32_t m = absmax_bits<16>(y);
-  m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+  const uint32_t m = max_xor32(kMixed ? absmax16_mixed(y) : absmax_bits<16>(y));
   byte = e8m0_byte<kFloor>(m);
   if (byte == 0xFFu) {
     w0 = w1 = 0u;
