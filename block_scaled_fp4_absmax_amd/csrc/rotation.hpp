@@ -187,4 +187,62 @@ inline RotGeom rot_geom(const Shape& s, int64_t ld_rot) {
   return g;
 }
 
+// ---- per-lane permutation entries (MFMA tile layout) ----------------------
+// Lane (n, h) of wave w handles, for i < kTpw, tile t = w + kWaves i: block
+// b = 32 t + n, elements e0 .. e0 + 15 with e0 = 32 b + 16 h, whose row
+// positions are perm[e0 .. e0 + 15]. The positions are the same for every
+// row, so a lane loads them once and keeps them as LDS byte offsets (clamped
+// to the row), packed in pairs.
+
+// Issue the loads of this lane's perm entries (16 per tile, zeros for tiles
+// past the row).
+template <int kTpw>
+__device__ __forceinline__ void load_lane_perm(const int32_t* __restrict__ perm,
+                                               const RotGeom& g, i32x4_t (*v)[4]) {
+  const rsrc_t rp = make_rsrc(perm, 4u * (uint32_t)g.cols);
+  const int32_t lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < kTpw; ++i) {
+    const int32_t b = 32 * (w + kWaves * i) + n;
+    const uint32_t o = b < g.bpr ? 4u * (32u * b + 16u * h) : kOob;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[i][q] = __builtin_bit_cast(
+          i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, o == kOob ? kOob : o + 16u * q, 0, 0));
+  }
+}
+
+// Clamp to the row, convert to byte offsets packed in pairs, and return the
+// largest run length G in {8, 4, 2, 1} such that the lane's indices form
+// aligned runs of G consecutive channels (lanes without a block: 8).
+template <int kTpw>
+__device__ __forceinline__ int pack_lane_perm(const i32x4_t (*v)[4], const RotGeom& g,
+                                              uint32_t (*off)[8]) {
+  const int32_t lane = threadIdx.x & 63, n = lane & 31, w = threadIdx.x >> 6;
+  const int32_t cmax = g.cols - 1;
+  bool r8 = true, r4 = true, r2 = true;
+#pragma unroll
+  for (int i = 0; i < kTpw; ++i) {
+    int32_t p[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      p[4 * q + 0] = min(max(v[i][q].x, 0), cmax);
+      p[4 * q + 1] = min(max(v[i][q].y, 0), cmax);
+      p[4 * q + 2] = min(max(v[i][q].z, 0), cmax);
+      p[4 * q + 3] = min(max(v[i][q].w, 0), cmax);
+    }
+    if (32 * (w + kWaves * i) + n < g.bpr) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        r8 = r8 && p[k] == p[k & 8] + (k & 7) && (p[k & 8] & 7) == 0;
+        r4 = r4 && p[k] == p[k & 12] + (k & 3) && (p[k & 12] & 3) == 0;
+        r2 = r2 && p[k] == p[k & 14] + (k & 1) && (p[k & 14] & 1) == 0;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) off[i][k] = 2u * (uint32_t)p[2 * k] | (2u * (uint32_t)p[2 * k + 1]) << 16;
+  }
+  return r8 ? 8 : r4 ? 4 : r2 ? 2 : 1;
+}
+
 }  // namespace fp4

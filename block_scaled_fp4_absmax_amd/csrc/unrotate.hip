@@ -6,88 +6,243 @@
 // basis applies H (its own inverse) and then the inverse permutation; the
 // permutation balances the energy of the blocks (sec. 2(a)), measured here
 // per channel over the calibration rows.
+#include <utility>
+
 #include "rotation.hpp"
 
 namespace fp4 {
 
 // ============================ inverse rotation ==============================
-// perm staged into LDS as uint16, clamped to [0, cols - 1] (cols <= 16384):
-// sixteen 16-byte loads per lane in flight at once, then one wait.
-__device__ __forceinline__ void stage_perm(const int32_t* __restrict__ perm, uint16_t* sperm,
-                                           int32_t cols) {
-  constexpr int kPv = (int)(kMaxPermCols / 4 / kThreads);
-  const rsrc_t rp = make_rsrc(perm, 4u * (uint32_t)cols);
-  const int32_t nv = cols / 4, cmax = cols - 1;
-  i32x4_t p[kPv];
-#pragma unroll
-  for (int u = 0; u < kPv; ++u) {
-    const int32_t v = threadIdx.x + u * kThreads;
-    p[u] = __builtin_bit_cast(
-        i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, v < nv ? 16u * v : kOob, 0, 0));
-  }
-#pragma unroll
-  for (int u = 0; u < kPv; ++u) {
-    const int32_t v = threadIdx.x + u * kThreads;
-    if (v < nv) {
-      const i32x4_t q = p[u];
-      const uint32_t c0 = (uint32_t)min(max(q.x, 0), cmax), c1 = (uint32_t)min(max(q.y, 0), cmax);
-      const uint32_t c2 = (uint32_t)min(max(q.z, 0), cmax), c3 = (uint32_t)min(max(q.w, 0), cmax);
-      reinterpret_cast<u32x2_t*>(sperm)[v] = u32x2_t{c0 | (c1 << 16), c2 | (c3 << 16)};
-    }
-  }
-  __syncthreads();
+// Lane (n, h) of wave w decodes, per row and for i < kTpw, the 16 elements
+// 16h .. 16h + 15 of block b = 32 (w + kWaves i) + n -- the MFMA tile layout
+// of the forward kernel. Decoded MXFP4 values (code * 2^e) are exact in bf16,
+// and the 32 products of a block's Hadamard row sum exactly in fp32, so the
+// transform runs on the matrix cores (two v_mfma_f32_32x32x16_bf16 per tile)
+// and gives the same fp32 results as any exact-sum order; then y * 1/sqrt(32)
+// is rounded to bf16. Element j = e0 + k goes to column perm[j]: the lane
+// scatters its 16 values into an LDS copy of the output row (2-byte writes,
+// or wider ones when perm moves aligned runs of channels), and the
+// work-group writes the row out with coalesced 16-byte stores. Rows alternate
+// between two LDS buffers with one barrier per row; the codes and scales of
+// the next kAhead rows are in flight in registers. Without a permutation the
+// lane stores its 32 contiguous bytes directly.
+
+// Per-row buffer resources of the inverse (empty for rows past the end).
+struct UnrotRsrc {
+  rsrc_t c, s, o;
+};
+__device__ __forceinline__ UnrotRsrc unrot_rsrc(const uint8_t* codes, const uint8_t* scales,
+                                                uint16_t* out, int32_t r, const RotGeom& g) {
+  const bool in = r < g.rows;
+  const int64_t rr = in ? r : 0;
+  UnrotRsrc q;
+  q.c = make_rsrc(codes + rr * g.ld_c, in ? (uint32_t)g.cols / 2u : 0u);
+  q.s = make_rsrc(scales + rr * g.ld_s, in ? (uint32_t)g.bpr : 0u);
+  q.o = make_rsrc(out + rr * g.ld_x, in ? 2u * (uint32_t)g.cols : 0u);
+  return q;
 }
 
-// Decode MXFP4 exactly to fp32, apply H (its own inverse) with the butterfly,
-// then scatter element j to column perm[j] through LDS.
-template <bool kHad, bool kPerm>
-__global__ __launch_bounds__(kThreads) void mx_dequant_unrotate_kernel(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const int32_t* __restrict__ perm, uint16_t* __restrict__ out, RotGeom g) {
-  extern __shared__ uint16_t smem[];
-  uint16_t* srow = smem;
-  uint16_t* sperm = smem + g.cols;
-  const uint32_t q = threadIdx.x & 3u;
-  const int32_t cpr = g.cols / 8;
-  if (kPerm) stage_perm(perm, sperm, g.cols);
-  for (int32_t r = blockIdx.x; r < g.rows; r += gridDim.x) {
-    if (kPerm) __syncthreads();  // previous row copied out, indices visible
-    for (int32_t c = threadIdx.x; c < cpr; c += kThreads) {
-      uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * g.ld_c + 4 * (int64_t)c);
-      float s = e8m0_operand(scales[r * g.ld_s + c / 4]);
-      float y[8];
-      float2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 0);
-      float2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 1);
-      float2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 2);
-      float2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 3);
-      y[0] = p0.x; y[1] = p0.y; y[2] = p1.x; y[3] = p1.y;
-      y[4] = p2.x; y[5] = p2.y; y[6] = p3.x; y[7] = p3.y;
-      if (kHad) hadamard_butterfly(y, q);
-      u32x4_t o;
-      o.x = pack_bf16x2(y[0], y[1]);
-      o.y = pack_bf16x2(y[2], y[3]);
-      o.z = pack_bf16x2(y[4], y[5]);
-      o.w = pack_bf16x2(y[6], y[7]);
-      if (kPerm) {
-        u32x4_t id = reinterpret_cast<const u32x4_t*>(sperm)[c];
-        srow[id.x & 0xFFFFu] = (uint16_t)(o.x & 0xFFFFu);
-        srow[id.x >> 16] = (uint16_t)(o.x >> 16);
-        srow[id.y & 0xFFFFu] = (uint16_t)(o.y & 0xFFFFu);
-        srow[id.y >> 16] = (uint16_t)(o.y >> 16);
-        srow[id.z & 0xFFFFu] = (uint16_t)(o.z & 0xFFFFu);
-        srow[id.z >> 16] = (uint16_t)(o.z >> 16);
-        srow[id.w & 0xFFFFu] = (uint16_t)(o.w & 0xFFFFu);
-        srow[id.w >> 16] = (uint16_t)(o.w >> 16);
-      } else {
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + r * g.ld_x) + c);
+// Codes (8 bytes) and scale byte of the lane's half-blocks of one row.
+template <int kTpw>
+struct RowCodes {
+  u32x2_t c[kTpw];
+  uint32_t s[kTpw];
+};
+
+template <int kTpw>
+__device__ __forceinline__ void load_codes(const UnrotRsrc& q, const RotGeom& g,
+                                           RowCodes<kTpw>& rc) {
+  const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < kTpw; ++i) {
+    const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kWaves * i) + (int32_t)n;
+    const bool ok = b < g.bpr;
+    rc.c[i] = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(q.c, ok ? 16u * b + 8u * h : kOob, 0, kNt));
+    rc.s[i] = __builtin_amdgcn_raw_buffer_load_b8(q.s, ok ? (uint32_t)b : kOob, 0, 0);
+  }
+}
+
+// bf16 outputs of one tile: decode, Hadamard (kHad), scale, round.
+template <bool kHad>
+__device__ __forceinline__ void unrotate_tile(u32x2_t c, uint32_t sbyte, const bf16x8_t& a0,
+                                              const bf16x8_t& a1, u32x4_t& lo, u32x4_t& hi) {
+  const float s = e8m0_operand(sbyte & 0xFFu);
+#define FP4_CVT2(w, k) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, k))
+  const uint32_t d[8] = {FP4_CVT2(c.x, 0), FP4_CVT2(c.x, 1), FP4_CVT2(c.x, 2), FP4_CVT2(c.x, 3),
+                         FP4_CVT2(c.y, 0), FP4_CVT2(c.y, 1), FP4_CVT2(c.y, 2), FP4_CVT2(c.y, 3)};
+#undef FP4_CVT2
+  lo = u32x4_t{d[0], d[1], d[2], d[3]};
+  hi = u32x4_t{d[4], d[5], d[6], d[7]};
+  if (kHad) {
+    float y[16];
+    hadamard_mfma(a0, a1, lo, hi, y);
+    lo = u32x4_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                 pack_bf16x2(y[6], y[7])};
+    hi = u32x4_t{pack_bf16x2(y[8], y[9]), pack_bf16x2(y[10], y[11]), pack_bf16x2(y[12], y[13]),
+                 pack_bf16x2(y[14], y[15])};
+  }
+}
+
+// Scatter one tile's 16 bf16 (lo: elements 0..7, hi: 8..15 of the lane's
+// half-block) into the row staged at LDS byte kOff of buf; G as for the
+// gather of the forward kernel.
+template <int G, uint32_t kOff>
+__device__ __forceinline__ void scatter_tile(uint8_t* buf, const uint32_t* off, u32x4_t lo,
+                                             u32x4_t hi) {
+  uint8_t* base = buf + kOff;
+  const uint32_t v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  if constexpr (G == 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      *reinterpret_cast<uint16_t*>(base + (off[k] & 0xFFFFu)) = (uint16_t)(v[k] & 0xFFFFu);
+      *reinterpret_cast<uint16_t*>(base + (off[k] >> 16)) = (uint16_t)(v[k] >> 16);
+    }
+  } else if constexpr (G == 2) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) *reinterpret_cast<uint32_t*>(base + (off[k] & 0xFFFFu)) = v[k];
+  } else if constexpr (G == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<u32x2_t*>(base + (off[2 * k] & 0xFFFFu)) = u32x2_t{v[2 * k], v[2 * k + 1]};
+  } else {
+    *reinterpret_cast<u32x4_t*>(base + (off[0] & 0xFFFFu)) = lo;
+    *reinterpret_cast<u32x4_t*>(base + (off[4] & 0xFFFFu)) = hi;
+  }
+}
+
+template <int kTpw, int kAhead>
+struct UnrotCtx {
+  const uint8_t* __restrict__ codes;
+  const uint8_t* __restrict__ scales;
+  uint16_t* __restrict__ out;
+  uint8_t* sbuf;        // two LDS row buffers (with a permutation)
+  uint32_t (*off)[8];   // the lane's scatter offsets, per tile
+  bf16x8_t a0, a1;      // Hadamard MFMA operands
+  RotGeom g;
+  RowCodes<kTpw>* rc;   // kAhead + 1 register buffers: rows k .. k + kAhead
+};
+
+// Rows r0 + k G (G = grid size), k < K, row k's codes in register buffer
+// k % (kAhead + 1). Step k decodes row k, loads the codes of row
+// k + kAhead + 1 into the buffer just used, and (with a permutation)
+// scatters into LDS buffer k % 2, waits at a barrier and writes the row out.
+// The loop runs whole groups of U = lcm(2, kAhead + 1) steps so every buffer
+// choice is a compile-time constant; a tail takes the last steps.
+template <int G, int kTpw, int kAhead, bool kHad, bool kPerm>
+struct UnrotRows {
+  using Ctx = UnrotCtx<kTpw, kAhead>;
+  static constexpr int kCpl = 2 * kTpw;
+  static constexpr uint32_t kBufBytes = 8192u * kTpw;
+  static constexpr int kRing = kAhead + 1;
+  static constexpr int U = kRing % 2 == 0 ? kRing : 2 * kRing;
+
+  template <int kS>
+  static __device__ __forceinline__ void step(const Ctx& c, int32_t r) {
+    constexpr int kBuf = kS & 1;
+    RowCodes<kTpw>& rc = c.rc[kS % kRing];
+    const RotGeom& g = c.g;
+    const int32_t G_ = gridDim.x;
+    const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
+    u32x4_t lo[kTpw], hi[kTpw];
+#pragma unroll
+    for (int i = 0; i < kTpw; ++i) unrotate_tile<kHad>(rc.c[i], rc.s[i], c.a0, c.a1, lo[i], hi[i]);
+    load_codes<kTpw>(unrot_rsrc(c.codes, c.scales, c.out, r + kRing * G_, g), g, rc);
+    const UnrotRsrc q = unrot_rsrc(c.codes, c.scales, c.out, r, g);
+    if constexpr (kPerm) {
+#pragma unroll
+      for (int i = 0; i < kTpw; ++i) {  // lanes without a block (offsets 0) write nothing
+        const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kWaves * i) + (int32_t)n;
+        if (b < g.bpr) scatter_tile<G, kBuf * kBufBytes>(c.sbuf, c.off[i], lo[i], hi[i]);
+      }
+      __syncthreads();
+      const int32_t cpr = g.cols / 8;
+#pragma unroll
+      for (int i = 0; i < kCpl; ++i) {
+        const int32_t ch = threadIdx.x + i * kThreads;
+        const u32x4_t v = reinterpret_cast<const u32x4_t*>(c.sbuf + kBuf * kBufBytes)[ch < cpr ? ch : 0];
+        __builtin_amdgcn_raw_buffer_store_b128(v, q.o, ch < cpr ? 16u * ch : kOob, 0, kNt);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTpw; ++i) {
+        const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kWaves * i) + (int32_t)n;
+        const uint32_t o = b < g.bpr ? 64u * b + 32u * h : kOob;
+        __builtin_amdgcn_raw_buffer_store_b128(lo[i], q.o, o, 0, kNt);
+        __builtin_amdgcn_raw_buffer_store_b128(hi[i], q.o, o == kOob ? kOob : o + 16u, 0, kNt);
       }
     }
-    if (kPerm) {
-      __syncthreads();
-      for (int32_t c = threadIdx.x; c < cpr; c += kThreads)
-        __builtin_nontemporal_store(reinterpret_cast<const u32x4_t*>(srow)[c],
-                                    reinterpret_cast<u32x4_t*>(out + r * g.ld_x) + c);
-    }
+  }
+
+  template <int... us>
+  static __device__ __forceinline__ void group(const Ctx& c, int32_t k,
+                                               std::integer_sequence<int, us...>) {
+    const int32_t G_ = gridDim.x, r0 = blockIdx.x;
+    (step<us>(c, r0 + (k + us) * G_), ...);
+  }
+
+  template <int... us>
+  static __device__ __forceinline__ void tail(const Ctx& c, int32_t k, int32_t K,
+                                              std::integer_sequence<int, us...>) {
+    const int32_t G_ = gridDim.x, r0 = blockIdx.x;
+    (void)((k + us < K ? (step<us>(c, r0 + (k + us) * G_), true) : false) && ...);
+  }
+
+  static __device__ __forceinline__ void run(const Ctx& c) {
+    const int32_t G_ = gridDim.x, r0 = blockIdx.x;
+    const int32_t K = (c.g.rows - r0 + G_ - 1) / G_;
+    int32_t k = 0;
+    for (; k + U - 1 < K; k += U) group(c, k, std::make_integer_sequence<int, U>{});
+    tail(c, k, K, std::make_integer_sequence<int, U - 1>{});
+  }
+};
+
+// Tuning (measured on MI355X at 16384 x 8192): work-groups per CU and rows of
+// codes in flight (a row's codes take 3 registers per tile). One work-group
+// per CU ran about 2% faster than two and 7% faster than four; the
+// look-ahead made little difference.
+template <int kTpw>
+constexpr int unrot_wgs_per_cu() {
+  return kTpw == 1 ? 2 : 1;
+}
+#ifndef FP4_UNROT_AHEAD
+#define FP4_UNROT_AHEAD 3
+#endif
+
+template <int kTpw, bool kHad, bool kPerm>
+__global__ __launch_bounds__(kThreads, 2) void mx_dequant_unrotate_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const int32_t* __restrict__ perm, uint16_t* __restrict__ out, RotGeom g) {
+  constexpr int kAhead = FP4_UNROT_AHEAD;
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf[kPerm ? 2 * 8192 * kTpw : 16];
+  i32x4_t v[kTpw][4];
+  if (kPerm) load_lane_perm<kTpw>(perm, g, v);
+  RowCodes<kTpw> rc[kAhead + 1];
+#pragma unroll
+  for (int j = 0; j <= kAhead; ++j)
+    load_codes<kTpw>(unrot_rsrc(codes, scales, out, (int32_t)(blockIdx.x + j * gridDim.x), g), g,
+                     rc[j]);
+  uint32_t off[kTpw][8];
+  int lr = 8;
+  if (kPerm) lr = pack_lane_perm<kTpw>(v, g, off);
+  bf16x8_t a0, a1;
+  hadamard_operands(a0, a1);
+  UnrotCtx<kTpw, kAhead> c{codes, scales, out, sbuf, off, a0, a1, g, rc};
+  if constexpr (kPerm) {
+    // run length agreed by the whole work-group
+    const int run = __syncthreads_and(lr >= 8) ? 8
+                    : __syncthreads_and(lr >= 4) ? 4
+                    : __syncthreads_and(lr >= 2) ? 2 : 1;
+    if (run == 8)
+      UnrotRows<8, kTpw, kAhead, kHad, true>::run(c);
+    else if (run == 4)
+      UnrotRows<4, kTpw, kAhead, kHad, true>::run(c);
+    else if (run == 2)
+      UnrotRows<2, kTpw, kAhead, kHad, true>::run(c);
+    else
+      UnrotRows<1, kTpw, kAhead, kHad, true>::run(c);
+  } else {
+    UnrotRows<8, kTpw, kAhead, kHad, false>::run(c);
   }
 }
 
@@ -121,7 +276,34 @@ __global__ __launch_bounds__(kThreads) void channel_energy_kernel(const uint16_t
 }
 
 // ================================ launchers =================================
-static int perm_grid(int64_t rows) { return (int)(rows < kPermGrid ? rows : kPermGrid); }
+template <int kTpw, bool kHad, bool kPerm>
+static void unrot_launch(const Shape& s, const int32_t* perm, const uint8_t* c, const uint8_t* sc,
+                         uint16_t* o, const RotGeom& g, hipStream_t st) {
+  // as for the forward kernel: pad LDS so that exactly kWgs work-groups fit per CU
+#ifdef FP4_UNROT_WG_PER_CU
+  constexpr int kWgs = FP4_UNROT_WG_PER_CU;
+#else
+  constexpr int kWgs = unrot_wgs_per_cu<kTpw>();
+#endif
+  const DeviceInfo di = device_info();
+  const int64_t wgs = (int64_t)di.cus * kWgs;
+  const int grid = (int)(s.rows < wgs ? s.rows : wgs);
+  constexpr size_t kStatic = kPerm ? 2 * 8192 * kTpw : 16;
+  const size_t share = (size_t)di.lds / kWgs;
+  const size_t pad = share > kStatic + 1024 ? share - kStatic - 1024 : 0;
+  hipLaunchKernelGGL((mx_dequant_unrotate_kernel<kTpw, kHad, kPerm>), dim3(grid), dim3(kThreads),
+                     pad, st, c, sc, perm, o, g);
+}
+
+template <bool kHad, bool kPerm>
+static void unrot_dispatch(const Shape& s, const int32_t* perm, const uint8_t* c,
+                           const uint8_t* sc, uint16_t* o, const RotGeom& g, hipStream_t st) {
+  const int64_t tpw = (s.cols + 32 * 32 * kWaves - 1) / (32 * 32 * kWaves);
+  if (tpw <= 1) unrot_launch<1, kHad, kPerm>(s, perm, c, sc, o, g, st);
+  else if (tpw <= 2) unrot_launch<2, kHad, kPerm>(s, perm, c, sc, o, g, st);
+  else if (tpw <= 3) unrot_launch<3, kHad, kPerm>(s, perm, c, sc, o, g, st);
+  else unrot_launch<4, kHad, kPerm>(s, perm, c, sc, o, g, st);
+}
 
 void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard,
                                 const void* codes, const void* scales, void* out, hipStream_t st) {
@@ -129,17 +311,9 @@ void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamar
   auto cp = static_cast<const uint8_t*>(codes);
   auto sp = static_cast<const uint8_t*>(scales);
   auto op = static_cast<uint16_t*>(out);
-  const int grid = perm_grid(s.rows);
-  size_t lds = perm ? (size_t)4 * s.cols : 0;
-  if (hadamard && perm)
-    hipLaunchKernelGGL((mx_dequant_unrotate_kernel<true, true>), dim3(grid), dim3(kThreads), lds,
-                       st, cp, sp, perm, op, g);
-  if (hadamard && !perm)
-    hipLaunchKernelGGL((mx_dequant_unrotate_kernel<true, false>), dim3(grid), dim3(kThreads), lds,
-                       st, cp, sp, perm, op, g);
-  if (!hadamard && perm)
-    hipLaunchKernelGGL((mx_dequant_unrotate_kernel<false, true>), dim3(grid), dim3(kThreads), lds,
-                       st, cp, sp, perm, op, g);
+  if (hadamard && perm) unrot_dispatch<true, true>(s, perm, cp, sp, op, g, st);
+  if (hadamard && !perm) unrot_dispatch<true, false>(s, perm, cp, sp, op, g, st);
+  if (!hadamard && perm) unrot_dispatch<false, true>(s, perm, cp, sp, op, g, st);
 }
 
 void launch_channel_energy(int64_t rows, int64_t cols, int64_t ld_x, const void* x, float* energy,

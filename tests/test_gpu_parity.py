@@ -289,24 +289,53 @@ def test_rotate_ragged(orc, rows, cols):
     _rot_case(orc, x, perm8, 32)
 
 
+def _unrotate_case(orc, x, perm, had):
+    pt = None if perm is None else torch.from_numpy(perm).cuda()
+    c, s, _ = fp4.rotate_quantize(to_dev(x), pt, had)
+    d = fp4.dequantize(c, s, fp4.MXFP4, perm=pt, hadamard=had)
+    sync()
+    yh = orc.dequantize_f64(np_u8(c), np_u8(s), 0)
+    want = orc.unrotate_f64(yh, perm, had)
+    got = inputs.bf16_bits_to_f32(bf16_bits(d)).astype(np.float64)
+    rowmax = np.abs(want).max(1, keepdims=True)
+    # one bf16 rounding of the fp32 result (exact sums, one fp32 scaling)
+    assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-6 * rowmax)
+    return got
+
+
+def _perm_of(kind, cols, seed):
+    rng = np.random.default_rng(seed)
+    if kind is None:
+        return None
+    if kind == 1:
+        return rng.permutation(cols).astype(np.int32)
+    runs = rng.permutation(cols // kind).astype(np.int32)
+    return (kind * runs[:, None] + np.arange(kind)[None, :]).reshape(-1).astype(np.int32)
+
+
 @pytest.mark.parametrize("perm_on", [False, True])
 def test_dequant_unrotate(orc, perm_on):
     note(f"case: dequantize with inverse rotation perm={perm_on}")
     x = inputs.gen_c4(rows=256, cols=4096)
     perm = np.random.default_rng(5).permutation(4096).astype(np.int32) if perm_on else None
-    pt = None if perm is None else torch.from_numpy(perm).cuda()
-    c, s, _ = fp4.rotate_quantize(to_dev(x), pt, 32)
-    d = fp4.dequantize(c, s, fp4.MXFP4, perm=pt, hadamard=32)
-    sync()
-    yh = orc.dequantize_f64(np_u8(c), np_u8(s), 0)
-    want = orc.unrotate_f64(yh, perm, 32)
-    got = inputs.bf16_bits_to_f32(bf16_bits(d)).astype(np.float64)
-    rowmax = np.abs(want).max(1, keepdims=True)
-    assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-6 * rowmax)
+    got = _unrotate_case(orc, x, perm, 32)
     # and the round trip is close to the input (SQNR of the two-level path)
     sq = orc.sqnr_db(inputs.bf16_bits_to_f32(x), got)
     note(f"  round-trip SQNR {sq:.2f} dB")
     assert sq > 15
+
+
+# one to four MFMA tiles per wave per row (partial tiles at 96, 2080, 8224),
+# many rows per work-group (1537), aligned channel runs (wider LDS scatters),
+# the permutation alone, and the Hadamard alone
+@pytest.mark.parametrize("rows,cols,kind,had", [
+    (3, 96, 1, 32), (37, 2080, 1, 32), (6, 8224, 1, 32), (5, 16384, 1, 32), (4, 12288, 1, 32),
+    (1537, 8192, 1, 32), (2500, 1024, 1, 32), (300, 8192, 2, 32), (300, 8192, 4, 32),
+    (300, 8192, 8, 32), (300, 8192, 1, 0), (1537, 8192, None, 32), (37, 2080, None, 32)])
+def test_dequant_unrotate_shapes(orc, rows, cols, kind, had):
+    note(f"case: dequantize + inverse rotation {rows}x{cols} perm runs={kind} H{had}")
+    x = inputs.gen_c3(rows=rows, cols=cols)
+    _unrotate_case(orc, x, _perm_of(kind, cols, cols + rows), had)
 
 
 # ------------------------------------------------------- full-size configs --
