@@ -148,16 +148,14 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 // Squared-error gain of replacing an element's standard code by the special
 // value 5 of the same sign: with d = |y| - 5, the standard neighbour is 4 or
 // 6 and (|y| - std)^2 - d^2 = 1 - 2|d| on |d| < 0.5, and no gain outside.
-// Returned with the sign of y. Exact in fp32: for |y| in [2.5, 10], |y| - 5 is
-// exact (Sterbenz), and where the gain is positive |y| lies in [4, 8), so d is
-// a multiple of 2^-21 and 1 - 2|d| a multiple of 2^-20 in (0, 1]; elsewhere
-// 1 - 2|d| < 0 whatever the rounding and is clamped to 0. A block sum of 16
-// such gains (at most 16, on the 2^-20 grid) is exact too.
-__device__ __forceinline__ float razer_signed_gain(float y) {
+// Exact in fp32: for |y| in [2.5, 10], |y| - 5 is exact (Sterbenz), and
+// where the gain is positive |y| lies in [4, 8), so d is a multiple of 2^-21
+// and 1 - 2|d| a multiple of 2^-20 in (0, 1]; elsewhere 1 - 2|d| < 0 whatever
+// the rounding and is clamped to 0. A block sum of 16 such gains, signed (at
+// most 16 in magnitude, on the 2^-20 grid), is exact too.
+__device__ __forceinline__ float razer_gain(float y) {
   const float d = __builtin_fabsf(y) - 5.0f;
-  const float g = __builtin_amdgcn_fmed3f(__builtin_fmaf(-2.0f, __builtin_fabsf(d), 1.0f), 0.0f,
-                                          1.0f);
-  return __builtin_copysignf(g, y);
+  return __builtin_amdgcn_fmed3f(__builtin_fmaf(-2.0f, __builtin_fabsf(d), 1.0f), 0.0f, 1.0f);
 }
 
 // Code dword with every nibble whose magnitude is zero cleared to 0x0.

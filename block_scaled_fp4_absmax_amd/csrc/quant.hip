@@ -122,16 +122,30 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint16_t* __res
   }
 }
 
+// One work-group of kScaleThreads reduces the partials; each lane keeps 16
+// loads in flight, so a tensor of up to 16 * kScaleThreads partials takes a
+// single round trip.
+constexpr int kScaleThreads = 1024;
+
 template <bool kFlat>
-__global__ __launch_bounds__(kThreads) void nv_tensor_scale_kernel(const uint8_t* __restrict__ codes,
-                                                                   uint32_t nparts, Geom g,
-                                                                   float* __restrict__ ts) {
-  __shared__ uint32_t red[kThreads / 64];
+__global__ __launch_bounds__(kScaleThreads) void nv_tensor_scale_kernel(
+    const uint8_t* __restrict__ codes, uint32_t nparts, Geom g, float* __restrict__ ts) {
+  __shared__ uint32_t red[kScaleThreads / 64];
   uint32_t m = 0;
-  for (uint32_t i = threadIdx.x; i < nparts; i += kThreads) {
-    int64_t xo, co, so;
-    locate<kFlat, 16>(g, i * (kThreads * kAmaxUnroll), xo, co, so);
-    m = max(m, *reinterpret_cast<const uint32_t*>(codes + co));
+  for (uint32_t i0 = threadIdx.x; i0 < nparts; i0 += 16 * kScaleThreads) {
+    uint32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t i = i0 + u * kScaleThreads;
+      v[u] = 0;
+      if (i < nparts) {
+        int64_t xo, co, so;
+        locate<kFlat, 16>(g, i * (kThreads * kAmaxUnroll), xo, co, so);
+        v[u] = *reinterpret_cast<const uint32_t*>(codes + co);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) m = max(m, v[u]);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
@@ -139,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void nv_tensor_scale_kernel(const uint8_t
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
-    for (int i = 1; i < kThreads / 64; ++i) r = max(r, red[i]);
+    for (int i = 1; i < kScaleThreads / 64; ++i) r = max(r, red[i]);
     const float amax = __uint_as_float(r);
     *ts = amax == 0.0f ? 1.0f : amax / 2688.0f;
   }
@@ -148,71 +162,126 @@ __global__ __launch_bounds__(kThreads) void nv_tensor_scale_kernel(const uint8_t
 // Empty tensor: nothing to reduce, s_t = 1.
 __global__ void nv_unit_scale_kernel(float* ts) { *ts = 1.0f; }
 
+// Per block: s_raw = RN(amax / d6) with d6 = RN(6 s_t), s_b = E4M3(s_raw),
+// r = RN(1 / RN(e4m3(s_b) s_t)), y = RN(x r). Two reductions of the divisions:
+//  - r depends only on the 7-bit code s_b, so the work-group tabulates it once
+//    (128 correctly rounded divisions) and a block reads it from LDS;
+//  - with y6 = RN(1 / d6), q = RN(amax y6) and the exact residual
+//    fma(-q, d6, amax), q' = fma(residual, y6, q) is the correctly rounded
+//    quotient whenever the residual does not underflow (amax >= 2^-100).
+//    With d6 in [2^-80, 2^125] every quotient that can round to a code other
+//    than 0 or 0x7E comes from such an amax; smaller ones stay below 2^-11
+//    (code 0) and overflowing ones give Inf or NaN, both code 0x7E like the
+//    Inf of the true division. (Checked against IEEE division for all finite
+//    bf16 amax and 40000 divisors.) Outside that range of d6 the kernel
+//    divides.
+template <bool kRazer>
+__device__ __forceinline__ void nv_quant_chunk(u32x4_t d, float d6, float y6, bool rcp_quotient,
+                                               const float* rcp_tab, uint32_t& w, uint32_t& byte) {
+  uint32_t m = absmax8_bf16(d);
+  m = max(m, dpp_xor1(m));
+  const float amax = __uint_as_float(m << 16);
+  float s_raw;
+  if (__builtin_expect(rcp_quotient, 1)) {  // uniform
+    const float q = amax * y6;
+    s_raw = __builtin_fmaf(__builtin_fmaf(-q, d6, amax), y6, q);
+  } else {
+    s_raw = amax / d6;
+  }
+  const uint32_t sb = e4m3_encode(s_raw);
+  w = 0;
+  byte = 0;
+  if (sb != 0u) {
+    const float r = rcp_tab[sb];
+    float y[8];
+    y[0] = bf16_lo(d.x) * r; y[1] = bf16_hi(d.x) * r;
+    y[2] = bf16_lo(d.y) * r; y[3] = bf16_hi(d.y) * r;
+    y[4] = bf16_lo(d.z) * r; y[5] = bf16_hi(d.z) * r;
+    y[6] = bf16_lo(d.w) * r; y[7] = bf16_hi(d.w) * r;
+    w = cvt8_f32(y, 1.0f);
+    byte = sb;
+    if (kRazer) {
+      // selector = [gains of negative elements exceed those of positive ones];
+      // an element is a candidate for the special value when its gain is > 0
+      float dsum = 0.0f;
+      uint32_t cm = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float gk = razer_gain(y[k]);  // in [0, 1]
+        dsum -= __builtin_copysignf(gk, y[k]);
+        // bit 31 of bits(g) + 0x7FFFFFFF is set iff g > 0
+        cm |= ((__float_as_uint(gk) + 0x7FFFFFFFu) >> 31) << (4 * k + 3);
+      }
+      dsum += dpp_xor1f(dsum);
+      const uint32_t sel = dsum > 0.0f ? 1u : 0u;
+      // a candidate's standard code is non-zero, so its bit 3 is the sign of
+      // y: it takes the special code when that sign is the selected one
+      const uint32_t spm = cm & ~(w ^ (sel ? 0x88888888u : 0u));
+      w = canonical_zero(w);
+      w = (w & ~((spm >> 3) * 0xFu)) | spm;
+      byte |= sel << 7;
+    }
+  }
+}
+
+// kFull: the work-group's kThreads * kUnroll chunks all exist (every
+// work-group but the last), so loads and stores need no bounds check.
+template <bool kFlat, bool kRazer, bool kFull>
+__device__ __forceinline__ void nv_quant_pass(const uint16_t* __restrict__ x,
+                                              uint8_t* __restrict__ codes,
+                                              uint8_t* __restrict__ scales, const float* rcp_tab,
+                                              float d6, float y6, bool rcp_quotient,
+                                              const Geom& g, const u32x4_t* d, const int64_t* co,
+                                              const int64_t* so) {
+  const bool leader = (threadIdx.x & 1) == 0;
+  const uint32_t base = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    if (!kFull && base + u * kThreads >= g.n) continue;
+    uint32_t w, byte;
+    nv_quant_chunk<kRazer>(d[u], d6, y6, rcp_quotient, rcp_tab, w, byte);
+    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + co[u]));
+    if (leader) scales[so[u]] = (uint8_t)byte;
+  }
+}
+
 template <bool kFlat, bool kRazer>
 __global__ __launch_bounds__(kThreads) void nv_quant_kernel(const uint16_t* __restrict__ x,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
                                                             const float* __restrict__ ts, Geom g) {
-  const bool leader = (threadIdx.x & 1) == 0;
+  __shared__ float rcp_tab[128];
+  const uint32_t base = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  const bool full = (blockIdx.x + 1) * (kThreads * kUnroll) <= g.n;  // uniform
+  u32x4_t d[kUnroll];
+  int64_t xo[kUnroll], co[kUnroll], so[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t v = base + u * kThreads;
+    locate<kFlat, 16>(g, v < g.n ? v : 0, xo[u], co[u], so[u]);
+  }
+  if (full) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo[u]));
+  } else {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (base + u * kThreads < g.n)
+        d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo[u]));
+  }
   const float s_t = *ts;
   const float d6 = 6.0f * s_t;
-  const uint32_t base = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
-  constexpr uint32_t stride = kThreads;
-  {
-    u32x4_t d[kUnroll];
-    int64_t xo[kUnroll], co[kUnroll], so[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      uint32_t v = base + u * stride;
-      if (v < g.n) {
-        locate<kFlat, 16>(g, v, xo[u], co[u], so[u]);
-        d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo[u]));
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      uint32_t v = base + u * stride;
-      if (v >= g.n) continue;
-      uint32_t m = absmax8_bf16(d[u]);
-      m = max(m, dpp_xor1(m));
-      const float amax = __uint_as_float(m << 16);
-      const float s_raw = amax / d6;
-      const uint32_t sb = e4m3_encode(s_raw);
-      uint32_t w = 0, byte = 0;
-      if (sb != 0u) {
-        const float s_eff = e4m3_decode(sb) * s_t;
-        const float r = 1.0f / s_eff;
-        float y[8];
-        y[0] = bf16_lo(d[u].x) * r; y[1] = bf16_hi(d[u].x) * r;
-        y[2] = bf16_lo(d[u].y) * r; y[3] = bf16_hi(d[u].y) * r;
-        y[4] = bf16_lo(d[u].z) * r; y[5] = bf16_hi(d[u].z) * r;
-        y[6] = bf16_lo(d[u].w) * r; y[7] = bf16_hi(d[u].w) * r;
-        w = cvt8_f32(y, 1.0f);
-        byte = sb;
-        if (kRazer) {
-          // selector = [gains of negative elements exceed those of positive ones]
-          float sg[8];
-          float dsum = 0.0f;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            sg[k] = razer_signed_gain(y[k]);
-            dsum -= sg[k];
-          }
-          dsum += dpp_xor1f(dsum);
-          const uint32_t sel = dsum > 0.0f ? 1u : 0u;
-          const float flip = sel ? -1.0f : 1.0f;  // special value's sign
-          uint32_t spm = 0;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) spm |= (sg[k] * flip > 0.0f) ? (8u << (4 * k)) : 0u;
-          w = canonical_zero(w);
-          w = (w & ~((spm >> 3) * 0xFu)) | spm;
-          byte |= sel << 7;
-        }
-      }
-      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + co[u]));
-      if (leader) scales[so[u]] = (uint8_t)byte;
-    }
-  }
+  if (threadIdx.x < 128) rcp_tab[threadIdx.x] = 1.0f / (e4m3_decode(threadIdx.x) * s_t);
+  const float y6 = 1.0f / d6;
+  const bool rcp_quotient = d6 >= 0x1p-80f && d6 <= 0x1p125f;  // uniform
+  __syncthreads();
+  if (full)
+    nv_quant_pass<kFlat, kRazer, true>(x, codes, scales, rcp_tab, d6, y6, rcp_quotient, g, d, co,
+                                       so);
+  else
+    nv_quant_pass<kFlat, kRazer, false>(x, codes, scales, rcp_tab, d6, y6, rcp_quotient, g, d,
+                                        co, so);
 }
 
 // ------------------------------------------------------------ dequantize ----
@@ -352,10 +421,12 @@ void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float* t
   const int grid = (int)((g.n + per - 1) / per);
   if (flat) {
     FP4_LAUNCH((nv_amax_kernel<true>), grid, st, xp, cp, g);
-    FP4_LAUNCH((nv_tensor_scale_kernel<true>), 1, st, cp, (uint32_t)grid, g, ts);
+    hipLaunchKernelGGL((nv_tensor_scale_kernel<true>), dim3(1), dim3(kScaleThreads), 0, st, cp,
+                       (uint32_t)grid, g, ts);
   } else {
     FP4_LAUNCH((nv_amax_kernel<false>), grid, st, xp, cp, g);
-    FP4_LAUNCH((nv_tensor_scale_kernel<false>), 1, st, cp, (uint32_t)grid, g, ts);
+    hipLaunchKernelGGL((nv_tensor_scale_kernel<false>), dim3(1), dim3(kScaleThreads), 0, st, cp,
+                       (uint32_t)grid, g, ts);
   }
 }
 
