@@ -478,25 +478,38 @@ def trace_summary(trace_dir, bench_log):
         for ln in fh:
             if ln.startswith("{") and '"metric"' in ln:
                 line = json.loads(ln)
-    out = ["# Kernel times of one profiled bench.py run (16384x8192 workload and extras)", "",
-           "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    wl = line["config"]["workload"].split(":")[0] if line else "?"
+    args = f"--workload {wl}" if wl != "c4" else ""
+    out = [f"# Kernel times of one profiled bench.py run ({line['config']['workload'] if line else wl})",
+           "", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    fp4_total = 0.0
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         name = r["Name"].split("(")[0].replace("void ", "")
         if not name.startswith("fp4::") and "copyBuffer" not in name:
             continue
+        if name.startswith("fp4::"):
+            fp4_total += float(r["TotalDurationNs"])
         out.append(f"| `{name[:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    rot = [r for r in rows if ROT_KERNEL in r["Name"]]
     out.append("")
-    if rot and line:
+    rot = [r for r in rows if ROT_KERNEL in r["Name"]]
+    if line and wl == "c4" and rot:
         avg = float(rot[0]["AverageNs"]) / 1e3
         ev = line["ms_per_step"] * 1e3
         out += [f"The fused kernel `{ROT_KERNEL}` averages {avg:.2f} us per launch here (warm-up "
                 f"launches included); the same run's HIP-event time per step is {ev:.2f} us "
                 f"({ev / avg:.3f}x), one launch per step.", ""]
+    elif line:
+        n = line["steps"] + line["warmup"]
+        ev = line["ms_per_step"] * 1e3
+        out += [f"All fp4 kernels together take {fp4_total / 1e3 / n:.1f} us per step here "
+                f"(total over the {n} warm-up and timed steps); the same run's HIP-event time per "
+                f"step is {ev:.1f} us.", ""]
     out += ["Command (from the repository root, TMPDIR=/tmp):", "", "```",
             "rocprofv3 --kernel-trace --stats -d <trace_dir> -o run --output-format csv "
-            "-- python3 bench.py --steps 100 --warmup 20 --no-cpu > <bench_log>",
+            f"-- python3 bench.py {args + ' ' if args else ''}"
+            f"--steps {line['steps'] if line else 'K'} --warmup {line['warmup'] if line else 'W'} "
+            "--no-cpu > <bench_log>",
             "python3 bench.py --trace-summary <trace_dir> <bench_log>", "```"]
     print("\n".join(out))
 

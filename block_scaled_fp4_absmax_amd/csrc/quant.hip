@@ -82,10 +82,11 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint16_t* __re
 // ---------------------------------------------------------------- NVFP4 ----
 // Tensor amax without atomics or scratch memory: each work-group reduces its
 // chunks to max |x| (the fp32 bit pattern, which orders like the magnitude)
-// and stores it in the code slot of its own first chunk -- output space that
-// the quantize kernel overwrites later in the same call. A single work-group
-// then reduces those partials and writes s_t = amax / 2688 (6 * 448), or 1
-// for an all-zero tensor.
+// and work-group i stores it in the code slot of chunk i -- output space that
+// the quantize kernel overwrites later in the same call, and contiguous (row
+// by row for strided codes) so the reduction reads it with coalesced loads. A
+// single work-group then reduces those partials and writes s_t = amax / 2688
+// (6 * 448), or 1 for an all-zero tensor.
 // Read-only, so each lane keeps kAmaxUnroll loads in flight and the pass
 // leaves one partial per kThreads * kAmaxUnroll chunks.
 constexpr int kAmaxUnroll = 16;
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint16_t* __res
     uint32_t r = red[0];
     for (int i = 1; i < kThreads / 64; ++i) r = max(r, red[i]);
     int64_t xo, co, so;
-    locate<kFlat, 16>(g, blockIdx.x * (kThreads * kAmaxUnroll), xo, co, so);
+    locate<kFlat, 16>(g, blockIdx.x, xo, co, so);
     *reinterpret_cast<uint32_t*>(codes + co) = r << 16;
   }
 }
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(kScaleThreads) void nv_tensor_scale_kernel(
       v[u] = 0;
       if (i < nparts) {
         int64_t xo, co, so;
-        locate<kFlat, 16>(g, i * (kThreads * kAmaxUnroll), xo, co, so);
+        locate<kFlat, 16>(g, i, xo, co, so);
         v[u] = *reinterpret_cast<const uint32_t*>(codes + co);
       }
     }
@@ -356,10 +357,10 @@ __global__ __launch_bounds__(kThreads) void nv_dequant_kernel(const uint8_t* __r
         val[2 * k] = p.x;
         val[2 * k + 1] = p.y;
       }
-      if (kRazer) {
+      if (kRazer) {  // code 8 is the only code that decodes to -0.0
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          if (((w[u] >> (4 * k)) & 0xFu) == 8u) val[k] = special;
+          if (__float_as_uint(val[k]) == 0x80000000u) val[k] = special;
       }
       u32x4_t o;
       o.x = pack_bf16x2(val[0] * s_eff, val[1] * s_eff);
