@@ -19,11 +19,16 @@ than itself (the pins live in ``tests/test_oracle_*.py``):
   to ``torch.float8_e8m0fnu``.
 * ``mx_quantize*``, ``nv_quantize``, ``dequantize*``: pinned by the nearest-grid
   property, scale invariance, sign symmetry and idempotence.
+* ``nv_quantize_f32`` / ``nv_tensor_amax_f32``: pinned by an element-wise
+  restatement of the NVFP4 steps with an independent brute-force code search
+  on fp32 inputs, and by the nearest-grid and error-bound properties.
 * ``razer_block``: pinned by exact Fraction SSE arg-min and exhaustive tiny-block
   enumeration.
-* ``rotate`` / ``unrotate_f64``: pinned to ``scipy.linalg.hadamard`` and norm
-  preservation.
-* ``build_perm``: pinned by bijectivity and block-energy balancing.
+* ``rotate`` / ``unrotate_f64``: pinned to ``scipy.linalg.hadamard`` (orders 16
+  and 32) and norm preservation.
+* ``build_perm``: pinned by bijectivity, block-energy balancing, a replay of the
+  greedy invariant (every unit goes to an open block of least load) and, for
+  aligned channel runs, the run structure.
 * Whole-pipeline bit patterns on the five synthetic workloads: parity unpinned
   beyond the properties above, since the pages print no worked example.
 """
@@ -89,6 +94,8 @@ def _load():
         "orc_nv_tensor_amax": (f32, [vp, i64, i64, i64]),
         "orc_nv_tensor_scale": (f32, [f32]),
         "orc_nv_quantize_bf16": (None, [vp, i64, i64, i64, i32, f32, vp, i64, vp, i64]),
+        "orc_nv_quantize_f32": (None, [vp, i64, i64, i64, i32, f32, vp, i64, vp, i64]),
+        "orc_nv_tensor_amax_f32": (f32, [vp, i64, i64, i64]),
         "orc_razer_block": (i32, [vp, i32, vp, vp, vp]),
         "orc_dequantize": (None, [vp, i64, vp, i64, f32, i64, i64, i32, i32, vp, i64]),
         "orc_dequantize_f64": (None, [vp, i64, vp, i64, f32, i64, i64, i32, i32, vp, i64]),
@@ -245,6 +252,27 @@ def dequantize_f64(codes: np.ndarray, scales: np.ndarray, fmt: int, razer: bool 
     return out
 
 
+def nv_tensor_amax_f32(y: np.ndarray) -> float:
+    y = np.ascontiguousarray(y, np.float32)
+    rows, cols = y.shape
+    return float(_load().orc_nv_tensor_amax_f32(_ptr(y), rows, cols, cols))
+
+
+def nv_quantize_f32(y: np.ndarray, razer: bool, tensor_scale: Optional[float] = None
+                    ) -> Tuple[np.ndarray, np.ndarray, float]:
+    """NVFP4 of fp32 values: codes, E4M3 scale bytes (RaZeR selector in bit 7), s_t."""
+    y = np.ascontiguousarray(y, np.float32)
+    rows, cols = y.shape
+    assert cols % 16 == 0
+    if tensor_scale is None:
+        tensor_scale = nv_tensor_scale(nv_tensor_amax_f32(y))
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 16), np.uint8)
+    _load().orc_nv_quantize_f32(_ptr(y), rows, cols, cols, int(razer), float(tensor_scale),
+                                _ptr(codes), cols // 2, _ptr(scales), cols // 16)
+    return codes, scales, float(tensor_scale)
+
+
 def rotate(x_bf16: np.ndarray, perm: Optional[np.ndarray], hadamard: int) -> np.ndarray:
     """fp32 [rows, cols]: permute channels, then Hadamard inside each block."""
     rows, cols = x_bf16.shape
@@ -263,6 +291,15 @@ def rotate_quantize(x_bf16: np.ndarray, perm: Optional[np.ndarray], hadamard: in
     y = rotate(x_bf16, perm, hadamard)
     codes, scales = mx_quantize_f32(y, floor_rule)
     return codes, scales, y
+
+
+def rotate_quantize_nv(x_bf16: np.ndarray, perm: Optional[np.ndarray], hadamard: int,
+                       razer: bool, tensor_scale: Optional[float] = None):
+    """Rotation (block-16 Hadamard) then NVFP4 of the fp32 rotated values:
+    (codes, scales, s_t, rotated). s_t from the rotated tensor's amax unless given."""
+    y = rotate(x_bf16, perm, hadamard)
+    codes, scales, ts = nv_quantize_f32(y, razer, tensor_scale)
+    return codes, scales, ts, y
 
 
 def unrotate_f64(y: np.ndarray, perm: Optional[np.ndarray], hadamard: int) -> np.ndarray:

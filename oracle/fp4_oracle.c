@@ -305,43 +305,74 @@ int orc_razer_block(const float* y, int n, uint8_t* codes, double* sse_chosen,
   return sel;
 }
 
+/* One NVFP4 block of 16 values (already widened to fp32): [RaZeR] sec. 1 with
+ * the arithmetic of the NVFP4 section comment above:
+ * s_raw = RN(amax / RN(6 s_t)), s_b = E4M3(s_raw), s_eff = RN(e4m3(s_b) s_t),
+ * y = RN(x * RN(1 / s_eff)), then the nearest code (RaZeR: sec. 2.2). */
+static void nv_block(const float* xv, int razer, float s_t, uint8_t* rc, int64_t b,
+                     uint8_t* scale) {
+  const float d = 6.0f * s_t;
+  float y[16];
+  float amax = 0.0f;
+  for (int i = 0; i < 16; ++i)
+    if (fabsf(xv[i]) > amax) amax = fabsf(xv[i]);
+  float s_raw = amax / d;
+  int sb = orc_e4m3_encode((double)s_raw);
+  if (sb == 0) { /* scale rounds to zero: the block is stored as zeros */
+    for (int i = 0; i < 16; ++i) put_nibble(rc, 16 * b + i, 0);
+    *scale = 0;
+    return;
+  }
+  float s_eff = (float)orc_e4m3_value(sb) * s_t;
+  float rcp = 1.0f / s_eff;
+  for (int i = 0; i < 16; ++i) y[i] = xv[i] * rcp;
+  if (razer) {
+    uint8_t c[16];
+    int sel = orc_razer_block(y, 16, c, NULL, NULL);
+    for (int i = 0; i < 16; ++i) put_nibble(rc, 16 * b + i, c[i]);
+    *scale = (uint8_t)(sb | (sel << 7));
+  } else {
+    for (int i = 0; i < 16; ++i) put_nibble(rc, 16 * b + i, orc_e2m1_nearest((double)y[i]));
+    *scale = (uint8_t)sb;
+  }
+}
+
 void orc_nv_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                           int razer, float tensor_scale, uint8_t* codes, int64_t ld_codes,
                           uint8_t* scales, int64_t ld_scales) {
-  const float s_t = tensor_scale;
-  const float d = 6.0f * s_t;
   int64_t r;
 #pragma omp parallel for schedule(static) num_threads(g_threads)
   for (r = 0; r < rows; ++r) {
     for (int64_t b = 0; b < cols / 16; ++b) {
-      float xv[16], y[16];
-      float amax = 0.0f;
-      for (int i = 0; i < 16; ++i) {
-        xv[i] = orc_bf16_to_f32(x[r * ld_x + 16 * b + i]);
-        if (fabsf(xv[i]) > amax) amax = fabsf(xv[i]);
-      }
-      float s_raw = amax / d;
-      int sb = orc_e4m3_encode((double)s_raw);
-      uint8_t* rc = codes + r * ld_codes;
-      if (sb == 0) { /* scale rounds to zero: the block is stored as zeros */
-        for (int i = 0; i < 16; ++i) put_nibble(rc, 16 * b + i, 0);
-        scales[r * ld_scales + b] = 0;
-        continue;
-      }
-      float s_eff = (float)orc_e4m3_value(sb) * s_t;
-      float rcp = 1.0f / s_eff;
-      for (int i = 0; i < 16; ++i) y[i] = xv[i] * rcp;
-      if (razer) {
-        uint8_t c[16];
-        int sel = orc_razer_block(y, 16, c, NULL, NULL);
-        for (int i = 0; i < 16; ++i) put_nibble(rc, 16 * b + i, c[i]);
-        scales[r * ld_scales + b] = (uint8_t)(sb | (sel << 7));
-      } else {
-        for (int i = 0; i < 16; ++i) put_nibble(rc, 16 * b + i, orc_e2m1_nearest((double)y[i]));
-        scales[r * ld_scales + b] = (uint8_t)sb;
-      }
+      float xv[16];
+      for (int i = 0; i < 16; ++i) xv[i] = orc_bf16_to_f32(x[r * ld_x + 16 * b + i]);
+      nv_block(xv, razer, tensor_scale, codes + r * ld_codes, b, scales + r * ld_scales + b);
     }
   }
+}
+
+/* The same quantizer on fp32 values (for instance the rotated values of the
+ * two-level rotation, which are not bf16). */
+void orc_nv_quantize_f32(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int razer,
+                         float tensor_scale, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                         int64_t ld_scales) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < cols / 16; ++b)
+      nv_block(x + r * ld_x + 16 * b, razer, tensor_scale, codes + r * ld_codes, b,
+               scales + r * ld_scales + b);
+}
+
+/* Largest |x| over an fp32 tensor. */
+float orc_nv_tensor_amax_f32(const float* x, int64_t rows, int64_t cols, int64_t ld_x) {
+  float m = 0.0f;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      float v = fabsf(x[r * ld_x + c]);
+      if (v > m) m = v;
+    }
+  return m;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -47,6 +47,10 @@ float orc_nv_tensor_scale(float amax);
 void orc_nv_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                           int razer, float tensor_scale, uint8_t* codes, int64_t ld_codes,
                           uint8_t* scales, int64_t ld_scales);
+void orc_nv_quantize_f32(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int razer,
+                         float tensor_scale, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                         int64_t ld_scales);
+float orc_nv_tensor_amax_f32(const float* x, int64_t rows, int64_t cols, int64_t ld_x);
 int orc_razer_block(const float* y, int n, uint8_t* codes, double* sse_chosen,
                     double* sse_plain);
 
