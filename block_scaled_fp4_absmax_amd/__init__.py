@@ -149,25 +149,42 @@ def dequantize(codes, scales, fmt: int = MXFP4, mode: int = PLAIN, tensor_scale=
     return out
 
 
-def rotate_quantize(x, perm=None, hadamard: int = 32, floor_rule: bool = False,
+def rotate_quantize(x, perm=None, hadamard: Optional[int] = None, floor_rule: bool = False,
                     want_rotated: bool = False, codes=None, scales=None, rotated=None,
-                    stream=None):
-    """Permutation + block Hadamard fused with MXFP4 quantize + pack.
+                    fmt: int = MXFP4, mode: int = PLAIN, tensor_scale=None,
+                    scale_given: Optional[bool] = None, stream=None):
+    """Permutation + block Hadamard fused with FP4 quantize + pack.
 
-    Returns (codes, scales, rotated fp32 [rows, cols] or None).
+    ``hadamard`` defaults to the format's block size (32 MXFP4, 16 NVFP4); 0
+    turns the transform off. NVFP4 takes ``mode`` (PLAIN or RAZER) and a
+    tensor scale as in :func:`quantize`. Returns (codes, scales, rotated fp32
+    [rows, cols] or None) for MXFP4 and (codes, scales, rotated, tensor_scale)
+    for NVFP4.
     """
     import torch
     rows, cols, ld = _rows_ld(x)
-    codes, scales = _outputs(rows, cols, MXFP4, x.device, codes, scales)
+    if hadamard is None:
+        hadamard = block_of(fmt)
+    codes, scales = _outputs(rows, cols, fmt, x.device, codes, scales)
     if want_rotated and rotated is None:
         rotated = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
     flags = FLAG_SCALE_OCP_FLOOR if floor_rule else 0
-    st = lib().fp4_rotate_quantize(_ptr(x), rows, cols, ld, _ptr(perm), hadamard, MXFP4, 32,
-                                   PLAIN, flags, _ptr(codes), codes.stride(0), _ptr(scales),
-                                   scales.stride(0), None, _ptr(rotated),
+    ts = None
+    if fmt == NVFP4:
+        if scale_given is None:
+            scale_given = tensor_scale is not None
+        if scale_given:
+            flags |= FLAG_TENSOR_SCALE_GIVEN
+        ts = tensor_scale if tensor_scale is not None else torch.empty(
+            1, dtype=torch.float32, device=x.device)
+    st = lib().fp4_rotate_quantize(_ptr(x), rows, cols, ld, _ptr(perm), hadamard, fmt,
+                                   block_of(fmt), mode, flags, _ptr(codes), codes.stride(0),
+                                   _ptr(scales), scales.stride(0), _ptr(ts), _ptr(rotated),
                                    rotated.stride(0) if rotated is not None else 0,
                                    _stream(stream))
     _check("fp4_rotate_quantize", st)
+    if fmt == NVFP4:
+        return codes, scales, rotated, ts
     return codes, scales, rotated
 
 

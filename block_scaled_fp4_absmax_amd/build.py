@@ -1,9 +1,11 @@
 """Build libfp4.so (the HIP kernels and the C ABI) in-tree for gfx950."""
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -25,16 +27,28 @@ FLAGS = [
 ]
 
 
-def build(extra_flags=(), out=LIB, verbose=False) -> str:
-    """Compile every HIP/C++ source into ``out`` (always recompiles)."""
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-o", tmp]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(ln for ln in res.stderr.splitlines()
                     if "packed-fp32-ops" not in ln and ln.strip())
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + err)
+    return err
+
+
+def build(extra_flags=(), out=LIB, verbose=False) -> str:
+    """Compile every HIP/C++ source (in parallel, one object each) and link
+    them into ``out`` (always recompiles)."""
+    common = [HIPCC, *FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include")]
+    with tempfile.TemporaryDirectory(prefix="fp4build") as tmpdir:
+        objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
+        cmds = [[c for c in common if c != "-shared"] + ["-c", "-o", o, os.path.join(CSRC, s)]
+                for s, o in zip(SOURCES, objs)]
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            errs = list(ex.map(_run, cmds))
+        tmp = out + ".tmp%d" % os.getpid()
+        errs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs))
+    err = "\n".join(e for e in errs if e)
     if verbose and err:
         print(err, file=sys.stderr)
     os.replace(tmp, out)

@@ -88,9 +88,9 @@ int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int6
   if (block != block_of(format)) return FP4_ERR_UNSUPPORTED;
   if (mode != FP4_PLAIN && mode != FP4_RAZER) return FP4_ERR_UNSUPPORTED;
   if (mode == FP4_RAZER && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
-  if (hadamard != 0 && hadamard != 32) return FP4_ERR_UNSUPPORTED;
-  if ((hadamard || perm) && format != FP4_MXFP4) return FP4_ERR_UNSUPPORTED;
+  if (hadamard != 0 && hadamard != block) return FP4_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 0 || cols % block != 0) return FP4_ERR_SHAPE;
+  if ((hadamard || perm) && cols % 32 != 0) return FP4_ERR_SHAPE;  // 32-element segments
   if (ld_out < cols || ld_codes < cols / 2 || ld_scales < cols / block) return FP4_ERR_SHAPE;
   if (rows > 0 && cols > 0 && rows * cols / 8 >= (int64_t)1 << 31) return FP4_ERR_UNSUPPORTED;
   if (perm && cols > fp4::kMaxPermCols) return FP4_ERR_UNSUPPORTED;
@@ -104,8 +104,11 @@ int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int6
   hipStream_t st = static_cast<hipStream_t>(stream);
   Shape s{rows, cols, ld_out, ld_codes, ld_scales};
   (void)hipGetLastError();
-  if (hadamard || perm)
+  if ((hadamard || perm) && format == FP4_MXFP4)
     fp4::launch_mx_dequant_unrotate(s, perm, hadamard, codes, scales, out_bf16, st);
+  else if (hadamard || perm)
+    fp4::launch_nv_dequant_unrotate(s, perm, hadamard, mode == FP4_RAZER, codes, scales,
+                                    tensor_scale, out_bf16, st);
   else
     fp4::launch_dequant(s, format, mode == FP4_RAZER, codes, scales, tensor_scale, out_bf16, st);
   return launch_status();
@@ -119,18 +122,24 @@ int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t 
   int rc = check_quant_args(x_bf16, rows, cols, ld_x, format, block, mode, flags, codes, ld_codes,
                             scales, ld_scales, tensor_scale);
   if (rc != FP4_OK) return rc;
-  if (format != FP4_MXFP4) return FP4_ERR_UNSUPPORTED;
-  if (hadamard != 0 && hadamard != 32) return FP4_ERR_UNSUPPORTED;
+  if (hadamard != 0 && hadamard != block) return FP4_ERR_UNSUPPORTED;
+  if (cols % 32 != 0) return FP4_ERR_SHAPE;  // the kernels work on 32-element segments
   if (perm && cols > fp4::kMaxPermCols) return FP4_ERR_UNSUPPORTED;
   if (rotated_out && ld_rot < cols) return FP4_ERR_SHAPE;
-  if (rows == 0 || cols == 0) return FP4_OK;
-  if (perm && !aligned(perm, 4)) return FP4_ERR_ALIGN;
-  if (rotated_out && (!aligned(rotated_out, 16) || ld_rot % 4 != 0)) return FP4_ERR_ALIGN;
+  const bool need_scale = format == FP4_NVFP4 && !(flags & FP4_FLAG_TENSOR_SCALE_GIVEN);
+  const bool empty = rows == 0 || cols == 0;
+  if (empty && !need_scale) return FP4_OK;
+  if (!empty && perm && !aligned(perm, 4)) return FP4_ERR_ALIGN;
+  if (!empty && rotated_out && (!aligned(rotated_out, 16) || ld_rot % 4 != 0)) return FP4_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Shape s{rows, cols, ld_x, ld_codes, ld_scales};
   (void)hipGetLastError();
-  fp4::launch_mx_rotate_quant(s, perm, hadamard, (flags & FP4_FLAG_SCALE_OCP_FLOOR) != 0, x_bf16,
-                              codes, scales, rotated_out, ld_rot, st);
+  if (format == FP4_MXFP4)
+    fp4::launch_mx_rotate_quant(s, perm, hadamard, (flags & FP4_FLAG_SCALE_OCP_FLOOR) != 0,
+                                x_bf16, codes, scales, rotated_out, ld_rot, st);
+  else
+    fp4::launch_nv_rotate_quant(s, perm, hadamard, mode == FP4_RAZER, !need_scale, x_bf16, codes,
+                                scales, tensor_scale, rotated_out, ld_rot, st);
   return launch_status();
 }
 

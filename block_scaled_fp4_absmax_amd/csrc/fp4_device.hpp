@@ -164,4 +164,66 @@ __device__ __forceinline__ uint32_t canonical_zero(uint32_t w) {
   return w & (nz | 0x77777777u);
 }
 
+// ---- NVFP4 block scale ------------------------------------------------------
+// Per block: s_raw = RN(amax / d6) with d6 = RN(6 s_t), s_b = E4M3(s_raw),
+// r = RN(1 / RN(e4m3(s_b) s_t)), y = RN(x r). Two reductions of the divisions:
+//  - r depends only on the 7-bit code s_b, so a work-group tabulates it once
+//    (nv_rcp_table, 128 correctly rounded divisions) and a block reads it;
+//  - with y6 = RN(1 / d6), q = RN(amax y6) and the exact residual
+//    fma(-q, d6, amax), q' = fma(residual, y6, q) is the correctly rounded
+//    quotient whenever the residual does not underflow (amax >= 2^-100).
+//    With d6 in [2^-80, 2^125] every quotient that can round to a code other
+//    than 0 or 0x7E comes from such an amax; smaller ones stay below 2^-11
+//    (code 0) and overflowing ones give Inf or NaN, both code 0x7E like the
+//    Inf of the true division. (Checked against IEEE division for all finite
+//    bf16 amax and 40000 divisors.) Outside that range of d6 the caller
+//    passes rcp_quotient = false and the quotient is divided.
+struct NvScale {
+  float d6, y6;
+  bool rcp_quotient;  // uniform
+};
+
+__device__ __forceinline__ NvScale nv_scale_setup(float s_t) {
+  NvScale n;
+  n.d6 = 6.0f * s_t;
+  n.y6 = 1.0f / n.d6;
+  n.rcp_quotient = n.d6 >= 0x1p-80f && n.d6 <= 0x1p125f;
+  return n;
+}
+
+// E4M3 code of the block with largest magnitude amax.
+__device__ __forceinline__ uint32_t nv_block_code(float amax, const NvScale& n) {
+  float s_raw;
+  if (__builtin_expect(n.rcp_quotient, 1)) {
+    const float q = amax * n.y6;
+    s_raw = __builtin_fmaf(__builtin_fmaf(-q, n.d6, amax), n.y6, q);
+  } else {
+    s_raw = amax / n.d6;
+  }
+  return e4m3_encode(s_raw);
+}
+
+// tab[c] = RN(1 / RN(e4m3(c) s_t)) for the 128 codes; the first 128 lanes of
+// the work-group write it, the caller synchronises before reading.
+__device__ __forceinline__ void nv_rcp_table(float* tab, float s_t) {
+  if (threadIdx.x < 128) tab[threadIdx.x] = 1.0f / (e4m3_decode(threadIdx.x) * s_t);
+}
+
+// RaZeR: apply the selector to a code word w (standard codes) given the
+// candidate flags cm (bit 3 of each nibble: the element's gain is > 0). A
+// candidate's standard code is non-zero, so its bit 3 is the sign of y: it
+// takes the special code 0x8 when that sign is the selected one. Zeros are
+// stored as 0x0.
+__device__ __forceinline__ uint32_t razer_apply(uint32_t w, uint32_t cm, uint32_t sel) {
+  const uint32_t spm = cm & ~(w ^ (sel ? 0x88888888u : 0u));
+  w = canonical_zero(w);
+  return (w & ~((spm >> 3) * 0xFu)) | spm;
+}
+
+// Gain flag of one element in nibble k (see razer_gain): bit 31 of
+// bits(g) + 0x7FFFFFFF is set iff g > 0.
+__device__ __forceinline__ uint32_t razer_flag(float g, int k) {
+  return ((__float_as_uint(g) + 0x7FFFFFFFu) >> 31) << (4 * k + 3);
+}
+
 }  // namespace fp4

@@ -33,6 +33,10 @@ void launch_mx_quant(const Shape& s, bool floor_rule, const void* x, void* codes
 // Writes s_t; uses the code buffer as scratch for per-work-group partial maxima.
 void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float* ts,
                             hipStream_t st);
+// s_t from nparts amax partials, partial i in the code slot of chunk i (row-major
+// chunks of 8 elements, 4 code bytes each).
+void launch_nv_scale_from_partials(const Shape& s, void* codes, uint32_t nparts, float* ts,
+                                   hipStream_t st);
 void launch_nv_quant(const Shape& s, bool razer, const void* x, void* codes, void* scales,
                      const float* ts, hipStream_t st);
 void launch_dequant(const Shape& s, int format, bool razer, const void* codes, const void* scales,
@@ -40,8 +44,19 @@ void launch_dequant(const Shape& s, int format, bool razer, const void* codes, c
 void launch_mx_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, bool floor_rule,
                             const void* x, void* codes, void* scales, float* rot, int64_t ld_rot,
                             hipStream_t st);
+// NVFP4 (block 16) after the two-level rotation with the 16-point Hadamard;
+// with !scale_given, s_t is computed from the rotated tensor first (the code
+// buffer holds the amax partials meanwhile). Requires cols % 32 == 0.
+void launch_nv_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, bool razer,
+                            bool scale_given, const void* x, void* codes, void* scales,
+                            float* ts, float* rot, int64_t ld_rot, hipStream_t st);
 void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard,
                                 const void* codes, const void* scales, void* out, hipStream_t st);
+// NVFP4 decode followed by the inverse rotation (16-point Hadamard, then the
+// inverse permutation). Requires cols % 32 == 0.
+void launch_nv_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard, bool razer,
+                                const void* codes, const void* scales, const float* ts, void* out,
+                                hipStream_t st);
 void launch_channel_energy(int64_t rows, int64_t cols, int64_t ld_x, const void* x, float* energy,
                            hipStream_t st);
 

@@ -163,33 +163,14 @@ __global__ __launch_bounds__(kScaleThreads) void nv_tensor_scale_kernel(
 // Empty tensor: nothing to reduce, s_t = 1.
 __global__ void nv_unit_scale_kernel(float* ts) { *ts = 1.0f; }
 
-// Per block: s_raw = RN(amax / d6) with d6 = RN(6 s_t), s_b = E4M3(s_raw),
-// r = RN(1 / RN(e4m3(s_b) s_t)), y = RN(x r). Two reductions of the divisions:
-//  - r depends only on the 7-bit code s_b, so the work-group tabulates it once
-//    (128 correctly rounded divisions) and a block reads it from LDS;
-//  - with y6 = RN(1 / d6), q = RN(amax y6) and the exact residual
-//    fma(-q, d6, amax), q' = fma(residual, y6, q) is the correctly rounded
-//    quotient whenever the residual does not underflow (amax >= 2^-100).
-//    With d6 in [2^-80, 2^125] every quotient that can round to a code other
-//    than 0 or 0x7E comes from such an amax; smaller ones stay below 2^-11
-//    (code 0) and overflowing ones give Inf or NaN, both code 0x7E like the
-//    Inf of the true division. (Checked against IEEE division for all finite
-//    bf16 amax and 40000 divisors.) Outside that range of d6 the kernel
-//    divides.
+// One NVFP4 chunk (half a block; the block spans lanes l and l ^ 1): the scale
+// arithmetic is in fp4_device.hpp (nv_block_code, nv_rcp_table).
 template <bool kRazer>
-__device__ __forceinline__ void nv_quant_chunk(u32x4_t d, float d6, float y6, bool rcp_quotient,
-                                               const float* rcp_tab, uint32_t& w, uint32_t& byte) {
+__device__ __forceinline__ void nv_quant_chunk(u32x4_t d, const NvScale& ns, const float* rcp_tab,
+                                               uint32_t& w, uint32_t& byte) {
   uint32_t m = absmax8_bf16(d);
   m = max(m, dpp_xor1(m));
-  const float amax = __uint_as_float(m << 16);
-  float s_raw;
-  if (__builtin_expect(rcp_quotient, 1)) {  // uniform
-    const float q = amax * y6;
-    s_raw = __builtin_fmaf(__builtin_fmaf(-q, d6, amax), y6, q);
-  } else {
-    s_raw = amax / d6;
-  }
-  const uint32_t sb = e4m3_encode(s_raw);
+  const uint32_t sb = nv_block_code(__uint_as_float(m << 16), ns);
   w = 0;
   byte = 0;
   if (sb != 0u) {
@@ -202,24 +183,18 @@ __device__ __forceinline__ void nv_quant_chunk(u32x4_t d, float d6, float y6, bo
     w = cvt8_f32(y, 1.0f);
     byte = sb;
     if (kRazer) {
-      // selector = [gains of negative elements exceed those of positive ones];
-      // an element is a candidate for the special value when its gain is > 0
+      // selector = [gains of negative elements exceed those of positive ones]
       float dsum = 0.0f;
       uint32_t cm = 0;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const float gk = razer_gain(y[k]);  // in [0, 1]
         dsum -= __builtin_copysignf(gk, y[k]);
-        // bit 31 of bits(g) + 0x7FFFFFFF is set iff g > 0
-        cm |= ((__float_as_uint(gk) + 0x7FFFFFFFu) >> 31) << (4 * k + 3);
+        cm |= razer_flag(gk, k);
       }
       dsum += dpp_xor1f(dsum);
       const uint32_t sel = dsum > 0.0f ? 1u : 0u;
-      // a candidate's standard code is non-zero, so its bit 3 is the sign of
-      // y: it takes the special code when that sign is the selected one
-      const uint32_t spm = cm & ~(w ^ (sel ? 0x88888888u : 0u));
-      w = canonical_zero(w);
-      w = (w & ~((spm >> 3) * 0xFu)) | spm;
+      w = razer_apply(w, cm, sel);
       byte |= sel << 7;
     }
   }
@@ -231,16 +206,15 @@ template <bool kFlat, bool kRazer, bool kFull>
 __device__ __forceinline__ void nv_quant_pass(const uint16_t* __restrict__ x,
                                               uint8_t* __restrict__ codes,
                                               uint8_t* __restrict__ scales, const float* rcp_tab,
-                                              float d6, float y6, bool rcp_quotient,
-                                              const Geom& g, const u32x4_t* d, const int64_t* co,
-                                              const int64_t* so) {
+                                              const NvScale& ns, const Geom& g, const u32x4_t* d,
+                                              const int64_t* co, const int64_t* so) {
   const bool leader = (threadIdx.x & 1) == 0;
   const uint32_t base = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     if (!kFull && base + u * kThreads >= g.n) continue;
     uint32_t w, byte;
-    nv_quant_chunk<kRazer>(d[u], d6, y6, rcp_quotient, rcp_tab, w, byte);
+    nv_quant_chunk<kRazer>(d[u], ns, rcp_tab, w, byte);
     __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + co[u]));
     if (leader) scales[so[u]] = (uint8_t)byte;
   }
@@ -272,17 +246,13 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(const uint16_t* __re
         d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo[u]));
   }
   const float s_t = *ts;
-  const float d6 = 6.0f * s_t;
-  if (threadIdx.x < 128) rcp_tab[threadIdx.x] = 1.0f / (e4m3_decode(threadIdx.x) * s_t);
-  const float y6 = 1.0f / d6;
-  const bool rcp_quotient = d6 >= 0x1p-80f && d6 <= 0x1p125f;  // uniform
+  const NvScale ns = nv_scale_setup(s_t);
+  nv_rcp_table(rcp_tab, s_t);
   __syncthreads();
   if (full)
-    nv_quant_pass<kFlat, kRazer, true>(x, codes, scales, rcp_tab, d6, y6, rcp_quotient, g, d, co,
-                                       so);
+    nv_quant_pass<kFlat, kRazer, true>(x, codes, scales, rcp_tab, ns, g, d, co, so);
   else
-    nv_quant_pass<kFlat, kRazer, false>(x, codes, scales, rcp_tab, d6, y6, rcp_quotient, g, d,
-                                        co, so);
+    nv_quant_pass<kFlat, kRazer, false>(x, codes, scales, rcp_tab, ns, g, d, co, so);
 }
 
 // ------------------------------------------------------------ dequantize ----
@@ -429,6 +399,17 @@ void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float* t
     hipLaunchKernelGGL((nv_tensor_scale_kernel<false>), dim3(1), dim3(kScaleThreads), 0, st, cp,
                        (uint32_t)grid, g, ts);
   }
+}
+
+void launch_nv_scale_from_partials(const Shape& s, void* codes, uint32_t nparts, float* ts,
+                                   hipStream_t st) {
+  if (nparts == 0) {
+    hipLaunchKernelGGL(nv_unit_scale_kernel, dim3(1), dim3(1), 0, st, ts);
+    return;
+  }
+  Geom g = make_geom(s, 16);
+  hipLaunchKernelGGL((nv_tensor_scale_kernel<false>), dim3(1), dim3(kScaleThreads), 0, st,
+                     static_cast<const uint8_t*>(codes), nparts, g, ts);
 }
 
 void launch_nv_quant(const Shape& s, bool razer, const void* x, void* codes, void* scales,

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void mx_rotq_stream_mfma_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ rot, RotGeom g) {
   bf16x8_t a0, a1;
-  hadamard_operands(a0, a1);
+  hadamard_operands<32>(a0, a1);
   const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
   const uint32_t tile0 = blockIdx.x * (kWaves * kTiles) + (threadIdx.x >> 6);
   const uint32_t ntiles = (g.nblk + 31u) >> 5;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void mx_rotq_stream_mfma_kernel(
     if (tile0 + u * kWaves >= ntiles) break;  // uniform across the wave
     float y[16];
     if (kHad) {
-      hadamard_mfma(a0, a1, lo[u], hi[u], y);
+      hadamard_mfma<32>(a0, a1, lo[u], hi[u], y);
     } else {
       widen8(lo[u], y);
       widen8(hi[u], y + 8);
@@ -177,7 +177,7 @@ __device__ __forceinline__ RowRsrc row_rsrc(const uint16_t* x, uint8_t* codes, u
   RowRsrc q;
   q.x = make_rsrc(x + rr * g.ld_x, in ? 2u * (uint32_t)g.cols : 0u);
   q.c = make_rsrc(codes + rr * g.ld_c, in ? (uint32_t)g.cols / 2u : 0u);
-  q.s = make_rsrc(scales + rr * g.ld_s, in ? (uint32_t)g.bpr : 0u);
+  q.s = make_rsrc(scales + rr * g.ld_s, in ? (uint32_t)g.spr : 0u);
   if (kRot) q.rot = make_rsrc(rot + rr * g.ld_rot, in ? 4u * (uint32_t)g.cols : 0u);
   return q;
 }
@@ -246,6 +246,9 @@ struct PermCtx {
   float* __restrict__ rot;
   RotGeom g;
   u32x4_t (*pre)[2 * kTpw];            // kAhead register buffers of rows in flight
+  NvScale ns;                          // NVFP4: tensor-scale arithmetic
+  const float* rcp_tab;                // NVFP4: block reciprocals by E4M3 code
+  float* amax;                         // NVFP4 pre-pass: the lane's running maximum
 };
 
 // Rows r0 + k G (G = grid size), k < K. Row k is gathered from LDS buffer
@@ -257,7 +260,7 @@ struct PermCtx {
 // so both buffer choices are compile-time constants and every path into a
 // step's wait has at least the steady state's memory operations after the
 // loads it waits for; a tail takes the last steps.
-template <int G, int kTpw, int kAhead, bool kHad, bool kFloor, bool kRot>
+template <int G, int kTpw, int kAhead, int kFmt, bool kHad, bool kOpt, bool kRot>
 struct PermRows {
   using Ctx = PermCtx<kTpw, kAhead>;
   static constexpr int kCpl = 2 * kTpw;
@@ -285,25 +288,34 @@ struct PermRows {
       gather_tile<G, kBuf * kBufBytes>(c.sbuf, c.off[i], lo, hi);
       float y[16];
       if (kHad) {
-        hadamard_mfma(c.a0, c.a1, lo, hi, y);
+        hadamard_mfma<kFmt == kFmtMx ? 32 : 16>(c.a0, c.a1, lo, hi, y);
       } else {
         widen8(lo, y);
         widen8(hi, y + 8);
       }
-      uint32_t w0, w1, byte;
-      mx_quant16_pair<kFloor, kHad>(y, w0, w1, byte);
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w0, w1}, q.c, ok ? 16u * b + 8u * h : kOob,
-                                            0, kNt);
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, q.s,
-                                           ok && h == 0 ? (uint32_t)b : kOob, 0, 0);
-      if (kRot) {
-        const uint32_t o = ok ? 4u * (32u * b + 16u * h) : kOob;
+      if constexpr (kFmt == kFmtNvAmax) {
+        if (ok) *c.amax = __builtin_fmaxf(*c.amax, absmax16f(y));
+      } else {
+        uint32_t w0, w1, byte, so;
+        if constexpr (kFmt == kFmtMx) {  // kOpt: OCP floor rule
+          mx_quant16_pair<kOpt, kHad>(y, w0, w1, byte);
+          so = ok && h == 0 ? (uint32_t)b : kOob;
+        } else {  // kOpt: RaZeR; lane h holds block 2 b + h
+          nv_quant16<kOpt>(y, c.ns, c.rcp_tab, w0, w1, byte);
+          so = ok ? 2u * b + h : kOob;
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w0, w1}, q.c,
+                                              ok ? 16u * b + 8u * h : kOob, 0, kNt);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, q.s, so, 0, 0);
+        if (kRot) {
+          const uint32_t o = ok ? 4u * (32u * b + 16u * h) : kOob;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          __builtin_amdgcn_raw_buffer_store_b128(
-              __builtin_bit_cast(u32x4_t,
-                                 f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]}),
-              q.rot, o == kOob ? kOob : o + 16u * k, 0, kNt);
+          for (int k = 0; k < 4; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t,
+                                   f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]}),
+                q.rot, o == kOob ? kOob : o + 16u * k, 0, kNt);
+        }
       }
     }
     __syncthreads();
@@ -363,13 +375,18 @@ constexpr int perm_waves_cap() {
 #define FP4_PERM_AHEAD perm_ahead<kTpw>()
 #endif
 
-template <int kTpw, bool kHad, bool kFloor, bool kRot>
-__global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void mx_rotq_perm_kernel(
+// kFmt: kFmtMx (kOpt = OCP floor rule), kFmtNv (kOpt = RaZeR; ts holds s_t),
+// kFmtNvAmax (no stores; work-group i leaves its largest rotated magnitude in
+// the code slot of chunk i).
+template <int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot>
+__global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void rotq_perm_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ rot, RotGeom g) {
+    uint8_t* __restrict__ scales, const float* __restrict__ ts, float* __restrict__ rot,
+    RotGeom g) {
   constexpr int kCpl = 2 * kTpw;
   constexpr int kAhead = FP4_PERM_AHEAD;  // rows in flight in registers beyond the next
   __shared__ __attribute__((aligned(16))) uint8_t sbuf[2 * 8192 * kTpw];
+  __shared__ float rcp_tab[128];
   const int32_t cpr = g.cols / 8;
   // perm entries first, then rows 0 .. kAhead, so the row loads are in flight
   // while the entries are unpacked
@@ -381,24 +398,112 @@ __global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void mx_rotq_perm_kernel(
   for (int j = 1; j <= kAhead; ++j)
     load_row<kCpl>(row_rsrc<kRot>(x, codes, scales, rot, blockIdx.x + j * gridDim.x, g).x, cpr,
                    pre[j % kAhead]);
+  NvScale ns{1.0f, 1.0f, true};
+  if constexpr (kFmt == kFmtNv) {
+    const float s_t = *ts;
+    ns = nv_scale_setup(s_t);
+    nv_rcp_table(rcp_tab, s_t);
+  }
   uint32_t off[kTpw][8];
   const int lr = pack_lane_perm<kTpw>(v, g, off);
   bf16x8_t a0, a1;
-  hadamard_operands(a0, a1);
+  hadamard_operands<kFmt == kFmtMx ? 32 : 16>(a0, a1);
   put_row<kCpl>(sbuf, cpr, first);
-  // run length agreed by the whole work-group (this also publishes row r0)
+  // run length agreed by the whole work-group (this also publishes row r0 and
+  // the reciprocal table)
   const int run = __syncthreads_and(lr >= 8) ? 8
                   : __syncthreads_and(lr >= 4) ? 4
                   : __syncthreads_and(lr >= 2) ? 2 : 1;
-  PermCtx<kTpw, kAhead> c{x, sbuf, off, a0, a1, codes, scales, rot, g, pre};
+  float amax = 0.0f;
+  PermCtx<kTpw, kAhead> c{x, sbuf, off, a0, a1, codes, scales, rot, g, pre, ns, rcp_tab, &amax};
   if (run == 8)
-    PermRows<8, kTpw, kAhead, kHad, kFloor, kRot>::run(c);
+    PermRows<8, kTpw, kAhead, kFmt, kHad, kOpt, kRot>::run(c);
   else if (run == 4)
-    PermRows<4, kTpw, kAhead, kHad, kFloor, kRot>::run(c);
+    PermRows<4, kTpw, kAhead, kFmt, kHad, kOpt, kRot>::run(c);
   else if (run == 2)
-    PermRows<2, kTpw, kAhead, kHad, kFloor, kRot>::run(c);
+    PermRows<2, kTpw, kAhead, kFmt, kHad, kOpt, kRot>::run(c);
   else
-    PermRows<1, kTpw, kAhead, kHad, kFloor, kRot>::run(c);
+    PermRows<1, kTpw, kAhead, kFmt, kHad, kOpt, kRot>::run(c);
+  if constexpr (kFmt == kFmtNvAmax) {
+    const float m = block_max(amax, rcp_tab);
+    if (threadIdx.x == 0) *amax_partial_slot(codes, blockIdx.x, g) = __float_as_uint(m);
+  }
+}
+
+// NVFP4 without a permutation: the tile layout of the MXFP4 streaming kernel
+// (a wave takes 32 consecutive 32-element segments); lane (n, h) holds one
+// whole 16-element block, 2 (32 t + n) + h in row-major block order.
+template <bool kFlat, bool kHad, bool kRazer, bool kRot, bool kAmax>
+__global__ __launch_bounds__(kThreads) void nv_rotq_stream_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    const float* __restrict__ ts, float* __restrict__ rot, RotGeom g) {
+  __shared__ float rcp_tab[128];
+  bf16x8_t a0, a1;
+  hadamard_operands<16>(a0, a1);
+  const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
+  const uint32_t tile0 = blockIdx.x * (kWaves * kTiles) + (threadIdx.x >> 6);
+  const uint32_t ntiles = (g.nblk + 31u) >> 5;
+  u32x4_t lo[kTiles], hi[kTiles];
+  int64_t xo[kTiles], co[kTiles], so[kTiles], ro[kTiles];
+  bool ok[kTiles];
+#pragma unroll
+  for (int u = 0; u < kTiles; ++u) {
+    const uint32_t tile = tile0 + u * kWaves;
+    const uint32_t b = tile * 32u + n;
+    ok[u] = tile < ntiles && b < g.nblk;
+    lo[u] = u32x4_t{0u, 0u, 0u, 0u};
+    hi[u] = lo[u];
+    if (ok[u]) {
+      uint32_t r = kFlat ? 0u : b / (uint32_t)g.bpr;
+      uint32_t cb = kFlat ? b : b - r * (uint32_t)g.bpr;
+      xo[u] = r * g.ld_x + 32 * (int64_t)cb + 16 * h;
+      co[u] = r * g.ld_c + 16 * (int64_t)cb + 8 * h;
+      so[u] = r * g.ld_s + 2 * (int64_t)cb + h;
+      ro[u] = r * g.ld_rot + 32 * (int64_t)cb + 16 * h;
+      const u32x4_t* p = reinterpret_cast<const u32x4_t*>(x + xo[u]);
+      lo[u] = __builtin_nontemporal_load(p);
+      hi[u] = __builtin_nontemporal_load(p + 1);
+    }
+  }
+  NvScale ns{1.0f, 1.0f, true};
+  if constexpr (!kAmax) {
+    const float s_t = *ts;
+    ns = nv_scale_setup(s_t);
+    nv_rcp_table(rcp_tab, s_t);
+    __syncthreads();
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kTiles; ++u) {
+    if (tile0 + u * kWaves >= ntiles) break;  // uniform across the wave
+    float y[16];
+    if (kHad) {
+      hadamard_mfma<16>(a0, a1, lo[u], hi[u], y);
+    } else {
+      widen8(lo[u], y);
+      widen8(hi[u], y + 8);
+    }
+    if constexpr (kAmax) {
+      if (ok[u]) amax = __builtin_fmaxf(amax, absmax16f(y));
+    } else {
+      uint32_t w0, w1, byte;
+      nv_quant16<kRazer>(y, ns, rcp_tab, w0, w1, byte);
+      if (ok[u]) {
+        uint32_t* cp = reinterpret_cast<uint32_t*>(codes + co[u]);
+        __builtin_nontemporal_store(w0, cp);
+        __builtin_nontemporal_store(w1, cp + 1);
+        scales[so[u]] = (uint8_t)byte;
+        if (kRot) {
+          store_rot8(rot + ro[u], y);
+          store_rot8(rot + ro[u] + 8, y + 8);
+        }
+      }
+    }
+  }
+  if constexpr (kAmax) {
+    const float m = block_max(amax, rcp_tab);
+    if (threadIdx.x == 0) *amax_partial_slot(codes, blockIdx.x, g) = __float_as_uint(m);
+  }
 }
 
 // ================================ launchers =================================
@@ -406,9 +511,10 @@ __global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void mx_rotq_perm_kernel(
 // only if every CU holds the same number of work-groups: the launch asks for
 // enough (unused) dynamic LDS that no more than perm_wgs_per_cu fit on a CU,
 // and launches exactly that many per CU.
-template <int kTpw, bool kHad, bool kFloor, bool kRot>
-static void perm_launch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
-                        uint8_t* sc, float* rot, const RotGeom& g, hipStream_t st) {
+template <int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot>
+static int perm_launch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
+                       uint8_t* sc, const float* ts, float* rot, const RotGeom& g,
+                       hipStream_t st) {
 #ifdef FP4_PERM_WG_PER_CU
   constexpr int kWgs = FP4_PERM_WG_PER_CU;
 #else
@@ -420,20 +526,29 @@ static void perm_launch(const Shape& s, const int32_t* perm, const uint16_t* x, 
   constexpr size_t kStatic = 2 * 8192 * kTpw;
   const size_t share = (size_t)ci.lds / kWgs;  // > lds / (kWgs + 1), so kWgs fit, not more
   const size_t pad = share > kStatic + 1024 ? share - kStatic - 1024 : 0;
-  hipLaunchKernelGGL((mx_rotq_perm_kernel<kTpw, kHad, kFloor, kRot>), dim3(grid), dim3(kThreads),
-                     pad, st, x, perm, c, sc, rot, g);
+  hipLaunchKernelGGL((rotq_perm_kernel<kTpw, kFmt, kHad, kOpt, kRot>), dim3(grid), dim3(kThreads),
+                     pad, st, x, perm, c, sc, ts, rot, g);
+  return grid;
+}
+
+// Permuting path; returns the number of work-groups launched.
+template <int kFmt, bool kHad, bool kOpt, bool kRot>
+static int perm_dispatch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
+                         uint8_t* sc, const float* ts, float* rot, const RotGeom& g,
+                         hipStream_t st) {
+  // MFMA tiles (32 segments) per wave per row
+  const int64_t tpw = (s.cols + 32 * 32 * kWaves - 1) / (32 * 32 * kWaves);
+  if (tpw <= 1) return perm_launch<1, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
+  if (tpw <= 2) return perm_launch<2, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
+  if (tpw <= 3) return perm_launch<3, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
+  return perm_launch<4, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
 }
 
 template <bool kHad, bool kFloor, bool kRot>
 static void rotq_dispatch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
                           uint8_t* sc, float* rot, const RotGeom& g, bool flat, hipStream_t st) {
   if (perm) {
-    // MFMA tiles (32 blocks) per wave per row
-    const int64_t tpw = (s.cols + 32 * 32 * kWaves - 1) / (32 * 32 * kWaves);
-    if (tpw <= 1) perm_launch<1, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
-    else if (tpw <= 2) perm_launch<2, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
-    else if (tpw <= 3) perm_launch<3, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
-    else perm_launch<4, kHad, kFloor, kRot>(s, perm, x, c, sc, rot, g, st);
+    (void)perm_dispatch<kFmtMx, kHad, kFloor, kRot>(s, perm, x, c, sc, nullptr, rot, g, st);
     return;
   }
   if constexpr (kUseMfma) {
@@ -475,6 +590,61 @@ void launch_mx_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, b
   if (!had && !floor_rule && r) rotq_dispatch<false, false, true>(s, perm, xp, cp, sp, rot, g, flat, st);
   if (!had && floor_rule && !r) rotq_dispatch<false, true, false>(s, perm, xp, cp, sp, rot, g, flat, st);
   if (!had && floor_rule && r) rotq_dispatch<false, true, true>(s, perm, xp, cp, sp, rot, g, flat, st);
+}
+
+template <bool kHad, bool kRazer, bool kRot, bool kAmax>
+static int nv_stream_launch(const uint16_t* x, uint8_t* c, uint8_t* sc, const float* ts,
+                            float* rot, const RotGeom& g, bool flat, hipStream_t st) {
+  const uint64_t tiles = ((uint64_t)g.nblk + 31) / 32;
+  const int grid = (int)((tiles + kWaves * kTiles - 1) / (kWaves * kTiles));
+  if (flat)
+    hipLaunchKernelGGL((nv_rotq_stream_kernel<true, kHad, kRazer, kRot, kAmax>), dim3(grid),
+                       dim3(kThreads), 0, st, x, c, sc, ts, rot, g);
+  else
+    hipLaunchKernelGGL((nv_rotq_stream_kernel<false, kHad, kRazer, kRot, kAmax>), dim3(grid),
+                       dim3(kThreads), 0, st, x, c, sc, ts, rot, g);
+  return grid;
+}
+
+template <bool kHad, bool kRazer, bool kRot>
+static void nv_rotq(const Shape& s, const int32_t* perm, bool scale_given, const uint16_t* x,
+                    uint8_t* c, uint8_t* sc, float* ts, float* rot, const RotGeom& g, bool flat,
+                    hipStream_t st) {
+  if (!scale_given) {  // s_t from the largest rotated magnitude
+    const int nparts = perm ? perm_dispatch<kFmtNvAmax, kHad, false, false>(s, perm, x, c, sc,
+                                                                             nullptr, nullptr, g, st)
+                            : nv_stream_launch<kHad, false, false, true>(x, c, sc, nullptr,
+                                                                        nullptr, g, flat, st);
+    launch_nv_scale_from_partials(s, c, (uint32_t)nparts, ts, st);
+  }
+  if (perm)
+    (void)perm_dispatch<kFmtNv, kHad, kRazer, kRot>(s, perm, x, c, sc, ts, rot, g, st);
+  else
+    (void)nv_stream_launch<kHad, kRazer, kRot, false>(x, c, sc, ts, rot, g, flat, st);
+}
+
+void launch_nv_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, bool razer,
+                            bool scale_given, const void* x, void* codes, void* scales,
+                            float* ts, float* rot, int64_t ld_rot, hipStream_t st) {
+  if (s.rows == 0 || s.cols == 0) {  // nothing to quantize; a computed s_t is 1
+    if (!scale_given) launch_nv_scale_from_partials(s, codes, 0, ts, st);
+    return;
+  }
+  RotGeom g = rot_geom(s, ld_rot, 16);
+  auto xp = static_cast<const uint16_t*>(x);
+  auto cp = static_cast<uint8_t*>(codes);
+  auto sp = static_cast<uint8_t*>(scales);
+  const bool had = hadamard != 0, r = rot != nullptr;
+  const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / 16 &&
+                    (!r || ld_rot == s.cols);
+  if (had && razer && r) nv_rotq<true, true, true>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
+  if (had && razer && !r) nv_rotq<true, true, false>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
+  if (had && !razer && r) nv_rotq<true, false, true>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
+  if (had && !razer && !r) nv_rotq<true, false, false>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
+  if (!had && razer && r) nv_rotq<false, true, true>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
+  if (!had && razer && !r) nv_rotq<false, true, false>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
+  if (!had && !razer && r) nv_rotq<false, false, true>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
+  if (!had && !razer && !r) nv_rotq<false, false, false>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
 }
 
 }  // namespace fp4

@@ -51,35 +51,44 @@ __device__ __forceinline__ uint32_t out_index_of_row(uint32_t m) {
 // Constant A operands: lane l holds A[m = l % 32][kk = 8 (l / 32) + j]; for
 // the first MFMA kk stands for element 16 (kk / 8) + kk % 8, for the second
 // 16 (kk / 8) + 8 + kk % 8 (matching the B halves each lane loads). So the 16
-// operand entries of lane l are H[tau(l % 32)][k0 + j], k0 = 16 (l / 32),
-// j = 0..15, with sign parity(row & (k0 + j)) = parity(row & k0) ^
-// parity(row & j); bit j of the Walsh mask W(row & 15) is parity(row & j).
+// operand entries of lane l are A[tau(l % 32)][k0 + j], k0 = 16 (l / 32),
+// j = 0..15. For the 32-point transform A = H32, with sign
+// parity(row & (k0 + j)) = parity(row & k0) ^ parity(row & j); bit j of the
+// Walsh mask W(row & 15) is parity(row & j). For 16-point blocks A is
+// diag(H16, H16) on each 32-element segment: entries couple an output row
+// only to inputs of the same half (row / 16 == l / 32), with sign W(row & 15).
+template <int kN>
 __device__ __forceinline__ void hadamard_operands(bf16x8_t& a0, bf16x8_t& a1) {
+  static_assert(kN == 16 || kN == 32, "block Hadamard of 16 or 32 points");
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t row = out_index_of_row(lane & 31u);
   uint32_t m = ((row & 1u) ? 0xAAAAu : 0u) ^ ((row & 2u) ? 0xCCCCu : 0u) ^
                ((row & 4u) ? 0xF0F0u : 0u) ^ ((row & 8u) ? 0xFF00u : 0u);
-  if ((lane >> 5) & (row >> 4)) m ^= 0xFFFFu;
+  if (kN == 32 && ((lane >> 5) & (row >> 4))) m ^= 0xFFFFu;
+  const uint32_t one = (kN == 16 && (row >> 4) != (lane >> 5)) ? 0u : 0x3F803F80u;
   u32x4_t v0, v1;
   uint32_t w[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)  // bf16 pair: +-1 = 0x3F80 with the sign bit from the mask
-    w[i] = 0x3F803F80u | (((m >> (2 * i)) & 1u) << 15) | (((m >> (2 * i + 1)) & 1u) << 31);
+    w[i] = one ? (one | (((m >> (2 * i)) & 1u) << 15) | (((m >> (2 * i + 1)) & 1u) << 31)) : 0u;
   v0 = u32x4_t{w[0], w[1], w[2], w[3]};
   v1 = u32x4_t{w[4], w[5], w[6], w[7]};
   a0 = __builtin_bit_cast(bf16x8_t, v0);
   a1 = __builtin_bit_cast(bf16x8_t, v1);
 }
 
-// y[0..15] = (H x)[16h .. 16h+15] / sqrt(32) for this lane's block, from the
-// lane's 16 inputs x[16h .. 16h+15] (bf16 pairs in lo/hi).
+// y[0..15] = (A x)[16h .. 16h+15] / sqrt(kN) for this lane's segment, from
+// the lane's 16 inputs x[16h .. 16h+15] (bf16 pairs in lo/hi); for kN = 16
+// these are the 16 outputs of one 16-element block, and 1/4 is exact.
+template <int kN>
 __device__ __forceinline__ void hadamard_mfma(const bf16x8_t& a0, const bf16x8_t& a1,
                                               u32x4_t lo, u32x4_t hi, float* y) {
   f32x16_t acc = {};
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, __builtin_bit_cast(bf16x8_t, lo), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, __builtin_bit_cast(bf16x8_t, hi), acc, 0, 0, 0);
+  constexpr float kScale = kN == 32 ? kInvSqrt32 : 0.25f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) y[r] = acc[r] * kInvSqrt32;
+  for (int r = 0; r < 16; ++r) y[r] = acc[r] * kScale;
 }
 
 // Largest |y| of 16 fp32 values as a bit pattern, for values that are the
@@ -114,6 +123,51 @@ __device__ __forceinline__ void mx_quant16_pair(const float* y, uint32_t& w0, ui
     const float s = e8m0_operand(byte);
     w0 = cvt8_f32(y, s);
     w1 = cvt8_f32(y + 8, s);
+  }
+}
+
+// Largest magnitude of 16 fp32 values (a NaN operand may be dropped).
+__device__ __forceinline__ float absmax16f(const float* y) {
+  float m = __builtin_fmaxf(__builtin_fabsf(y[0]), __builtin_fabsf(y[1]));
+#pragma unroll
+  for (int k = 2; k < 16; k += 2)
+    m = __builtin_fmaxf(__builtin_fmaxf(m, __builtin_fabsf(y[k])), __builtin_fabsf(y[k + 1]));
+  return m;
+}
+
+// NVFP4 of the lane's 16 values, one whole 16-element block (the arithmetic of
+// nv_block_code and the RaZeR selection of the streaming NVFP4 quantizer,
+// here inside one lane). Non-finite values give unspecified codes.
+template <bool kRazer>
+__device__ __forceinline__ void nv_quant16(const float* y, const NvScale& ns, const float* rcp_tab,
+                                           uint32_t& w0, uint32_t& w1, uint32_t& byte) {
+  const uint32_t sb = nv_block_code(absmax16f(y), ns);
+  w0 = w1 = 0u;
+  byte = 0u;
+  if (sb != 0u) {
+    const float r = rcp_tab[sb];
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = y[k] * r;
+    w0 = cvt8_f32(v, 1.0f);
+    w1 = cvt8_f32(v + 8, 1.0f);
+    byte = sb;
+    if (kRazer) {
+      float dsum = 0.0f;
+      uint32_t cm0 = 0, cm1 = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float g0 = razer_gain(v[k]), g1 = razer_gain(v[k + 8]);
+        dsum -= __builtin_copysignf(g0, v[k]);
+        dsum -= __builtin_copysignf(g1, v[k + 8]);
+        cm0 |= razer_flag(g0, k);
+        cm1 |= razer_flag(g1, k);
+      }
+      const uint32_t sel = dsum > 0.0f ? 1u : 0u;
+      w0 = razer_apply(w0, cm0, sel);
+      w1 = razer_apply(w1, cm1, sel);
+      byte |= sel << 7;
+    }
   }
 }
 
@@ -169,23 +223,53 @@ constexpr int kWaves = kThreads / 64;  // waves per work-group
 
 struct RotGeom {
   int32_t rows, cols;
-  int32_t bpr;   // 32-element blocks per row
+  int32_t bpr;   // 32-element segments per row (MXFP4 blocks; two NVFP4 blocks each)
   uint32_t nblk; // rows * bpr
+  int32_t spr;   // scale bytes per row: cols / block
   int64_t ld_x, ld_c, ld_s, ld_rot;
 };
 
-inline RotGeom rot_geom(const Shape& s, int64_t ld_rot) {
+// Formats of the rotation kernels: MXFP4 (32-point transform), NVFP4
+// (16-point), and the NVFP4 pre-pass that only finds the largest rotated
+// magnitude (for a computed tensor scale).
+enum RotFmt : int { kFmtMx = 0, kFmtNv = 1, kFmtNvAmax = 2 };
+
+inline RotGeom rot_geom(const Shape& s, int64_t ld_rot, int block = 32) {
   RotGeom g;
   g.rows = (int32_t)s.rows;
   g.cols = (int32_t)s.cols;
   g.bpr = (int32_t)(s.cols / 32);
   g.nblk = (uint32_t)(s.rows * (s.cols / 32));
+  g.spr = (int32_t)(s.cols / block);
   g.ld_x = s.ld_x;
   g.ld_c = s.ld_c;
   g.ld_s = s.ld_s;
   g.ld_rot = ld_rot;
   return g;
 }
+
+// Where work-group i of an amax pre-pass leaves its partial: the code slot of
+// chunk i (row-major chunks of 8 elements, 4 code bytes each), which the
+// quantize pass overwrites afterwards.
+__device__ __forceinline__ uint32_t* amax_partial_slot(uint8_t* codes, uint32_t i,
+                                                       const RotGeom& g) {
+  const uint32_t cpr = (uint32_t)g.cols / 8u, r = i / cpr;
+  return reinterpret_cast<uint32_t*>(codes + r * g.ld_c + 4 * (int64_t)(i - r * cpr));
+}
+
+// Work-group maximum of a non-negative per-lane value; lane 0 of the
+// work-group receives it. red: kWaves floats of shared memory.
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) m = __builtin_fmaxf(m, red[i]);
+  return m;
+}
+
 
 // ---- per-lane permutation entries (MFMA tile layout) ----------------------
 // Lane (n, h) of wave w handles, for i < kTpw, tile t = w + kWaves i: block

@@ -37,7 +37,7 @@ __device__ __forceinline__ UnrotRsrc unrot_rsrc(const uint8_t* codes, const uint
   const int64_t rr = in ? r : 0;
   UnrotRsrc q;
   q.c = make_rsrc(codes + rr * g.ld_c, in ? (uint32_t)g.cols / 2u : 0u);
-  q.s = make_rsrc(scales + rr * g.ld_s, in ? (uint32_t)g.bpr : 0u);
+  q.s = make_rsrc(scales + rr * g.ld_s, in ? (uint32_t)g.spr : 0u);
   q.o = make_rsrc(out + rr * g.ld_x, in ? 2u * (uint32_t)g.cols : 0u);
   return q;
 }
@@ -49,7 +49,8 @@ struct RowCodes {
   uint32_t s[kTpw];
 };
 
-template <int kTpw>
+// kNv: the lane's 16 elements are NVFP4 block 2 b + h with its own scale byte.
+template <int kTpw, bool kNv>
 __device__ __forceinline__ void load_codes(const UnrotRsrc& q, const RotGeom& g,
                                            RowCodes<kTpw>& rc) {
   const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
@@ -59,7 +60,8 @@ __device__ __forceinline__ void load_codes(const UnrotRsrc& q, const RotGeom& g,
     const bool ok = b < g.bpr;
     rc.c[i] = __builtin_bit_cast(
         u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(q.c, ok ? 16u * b + 8u * h : kOob, 0, kNt));
-    rc.s[i] = __builtin_amdgcn_raw_buffer_load_b8(q.s, ok ? (uint32_t)b : kOob, 0, 0);
+    const uint32_t so = kNv ? 2u * b + h : (uint32_t)b;
+    rc.s[i] = __builtin_amdgcn_raw_buffer_load_b8(q.s, ok ? so : kOob, 0, 0);
   }
 }
 
@@ -76,12 +78,53 @@ __device__ __forceinline__ void unrotate_tile(u32x2_t c, uint32_t sbyte, const b
   hi = u32x4_t{d[4], d[5], d[6], d[7]};
   if (kHad) {
     float y[16];
-    hadamard_mfma(a0, a1, lo, hi, y);
+    hadamard_mfma<32>(a0, a1, lo, hi, y);
     lo = u32x4_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
                  pack_bf16x2(y[6], y[7])};
     hi = u32x4_t{pack_bf16x2(y[8], y[9]), pack_bf16x2(y[10], y[11]), pack_bf16x2(y[12], y[13]),
                  pack_bf16x2(y[14], y[15])};
   }
+}
+
+// NVFP4: one whole 16-element block per lane. The E2M1 values (RaZeR: code 8
+// is the block's +-5) are exact in bf16 and the 16-point transform of them is
+// exact (sums of at most 16 multiples of 0.5 below 100, then times 1/4); the
+// block scale commutes with a transform inside the block, so s_eff multiplies
+// once afterwards: one fp32 rounding, then bf16.
+template <bool kHad, bool kRazer>
+__device__ __forceinline__ void nv_unrotate_tile(u32x2_t c, uint32_t sbyte, float s_t,
+                                                 const bf16x8_t& a0, const bf16x8_t& a1,
+                                                 u32x4_t& lo, u32x4_t& hi) {
+  const float s_eff = e4m3_decode(kRazer ? (sbyte & 0x7Fu) : (sbyte & 0xFFu)) * s_t;
+  const float special = (sbyte & 0x80u) ? -5.0f : 5.0f;
+  float v[16];
+#define FP4_DEC2(w, k, o)                                                      \
+  {                                                                            \
+    const float2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, k); \
+    v[o] = p.x;                                                                \
+    v[o + 1] = p.y;                                                            \
+  }
+  FP4_DEC2(c.x, 0, 0) FP4_DEC2(c.x, 1, 2) FP4_DEC2(c.x, 2, 4) FP4_DEC2(c.x, 3, 6)
+  FP4_DEC2(c.y, 0, 8) FP4_DEC2(c.y, 1, 10) FP4_DEC2(c.y, 2, 12) FP4_DEC2(c.y, 3, 14)
+#undef FP4_DEC2
+  if (kRazer) {  // code 8 is the only code that decodes to -0.0
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (__float_as_uint(v[k]) == 0x80000000u) v[k] = special;
+  }
+  if (kHad) {
+    lo = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                 pack_bf16x2(v[6], v[7])};
+    hi = u32x4_t{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]),
+                 pack_bf16x2(v[14], v[15])};
+    hadamard_mfma<16>(a0, a1, lo, hi, v);
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] *= s_eff;
+  lo = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+               pack_bf16x2(v[6], v[7])};
+  hi = u32x4_t{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]),
+               pack_bf16x2(v[14], v[15])};
 }
 
 // Scatter one tile's 16 bf16 (lo: elements 0..7, hi: 8..15 of the lane's
@@ -121,6 +164,7 @@ struct UnrotCtx {
   bf16x8_t a0, a1;      // Hadamard MFMA operands
   RotGeom g;
   RowCodes<kTpw>* rc;   // kAhead + 1 register buffers: rows k .. k + kAhead
+  float s_t;            // NVFP4 tensor scale
 };
 
 // Rows r0 + k G (G = grid size), k < K, row k's codes in register buffer
@@ -129,7 +173,9 @@ struct UnrotCtx {
 // scatters into LDS buffer k % 2, waits at a barrier and writes the row out.
 // The loop runs whole groups of U = lcm(2, kAhead + 1) steps so every buffer
 // choice is a compile-time constant; a tail takes the last steps.
-template <int G, int kTpw, int kAhead, bool kHad, bool kPerm>
+// kNv: NVFP4 (kRazer: RaZeR codes) with the 16-point transform; else MXFP4
+// with the 32-point one.
+template <int G, int kTpw, int kAhead, bool kNv, bool kRazer, bool kHad, bool kPerm>
 struct UnrotRows {
   using Ctx = UnrotCtx<kTpw, kAhead>;
   static constexpr int kCpl = 2 * kTpw;
@@ -146,8 +192,13 @@ struct UnrotRows {
     const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
     u32x4_t lo[kTpw], hi[kTpw];
 #pragma unroll
-    for (int i = 0; i < kTpw; ++i) unrotate_tile<kHad>(rc.c[i], rc.s[i], c.a0, c.a1, lo[i], hi[i]);
-    load_codes<kTpw>(unrot_rsrc(c.codes, c.scales, c.out, r + kRing * G_, g), g, rc);
+    for (int i = 0; i < kTpw; ++i) {
+      if constexpr (kNv)
+        nv_unrotate_tile<kHad, kRazer>(rc.c[i], rc.s[i], c.s_t, c.a0, c.a1, lo[i], hi[i]);
+      else
+        unrotate_tile<kHad>(rc.c[i], rc.s[i], c.a0, c.a1, lo[i], hi[i]);
+    }
+    load_codes<kTpw, kNv>(unrot_rsrc(c.codes, c.scales, c.out, r + kRing * G_, g), g, rc);
     const UnrotRsrc q = unrot_rsrc(c.codes, c.scales, c.out, r, g);
     if constexpr (kPerm) {
 #pragma unroll
@@ -209,10 +260,13 @@ constexpr int unrot_wgs_per_cu() {
 #define FP4_UNROT_AHEAD 3
 #endif
 
-template <int kTpw, bool kHad, bool kPerm>
-__global__ __launch_bounds__(kThreads, 2) void mx_dequant_unrotate_kernel(
+// kNv: NVFP4 blocks of 16 (scales 2 b + h, tensor scale *ts), the 16-point
+// transform; else MXFP4 blocks of 32 with the 32-point one.
+template <int kTpw, bool kNv, bool kRazer, bool kHad, bool kPerm>
+__global__ __launch_bounds__(kThreads, 2) void dequant_unrotate_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const int32_t* __restrict__ perm, uint16_t* __restrict__ out, RotGeom g) {
+    const float* __restrict__ ts, const int32_t* __restrict__ perm, uint16_t* __restrict__ out,
+    RotGeom g) {
   constexpr int kAhead = FP4_UNROT_AHEAD;
   __shared__ __attribute__((aligned(16))) uint8_t sbuf[kPerm ? 2 * 8192 * kTpw : 16];
   i32x4_t v[kTpw][4];
@@ -220,29 +274,30 @@ __global__ __launch_bounds__(kThreads, 2) void mx_dequant_unrotate_kernel(
   RowCodes<kTpw> rc[kAhead + 1];
 #pragma unroll
   for (int j = 0; j <= kAhead; ++j)
-    load_codes<kTpw>(unrot_rsrc(codes, scales, out, (int32_t)(blockIdx.x + j * gridDim.x), g), g,
-                     rc[j]);
+    load_codes<kTpw, kNv>(unrot_rsrc(codes, scales, out, (int32_t)(blockIdx.x + j * gridDim.x), g),
+                          g, rc[j]);
   uint32_t off[kTpw][8];
   int lr = 8;
   if (kPerm) lr = pack_lane_perm<kTpw>(v, g, off);
   bf16x8_t a0, a1;
-  hadamard_operands(a0, a1);
-  UnrotCtx<kTpw, kAhead> c{codes, scales, out, sbuf, off, a0, a1, g, rc};
+  hadamard_operands<kNv ? 16 : 32>(a0, a1);
+  const float s_t = kNv ? *ts : 1.0f;
+  UnrotCtx<kTpw, kAhead> c{codes, scales, out, sbuf, off, a0, a1, g, rc, s_t};
   if constexpr (kPerm) {
     // run length agreed by the whole work-group
     const int run = __syncthreads_and(lr >= 8) ? 8
                     : __syncthreads_and(lr >= 4) ? 4
                     : __syncthreads_and(lr >= 2) ? 2 : 1;
     if (run == 8)
-      UnrotRows<8, kTpw, kAhead, kHad, true>::run(c);
+      UnrotRows<8, kTpw, kAhead, kNv, kRazer, kHad, true>::run(c);
     else if (run == 4)
-      UnrotRows<4, kTpw, kAhead, kHad, true>::run(c);
+      UnrotRows<4, kTpw, kAhead, kNv, kRazer, kHad, true>::run(c);
     else if (run == 2)
-      UnrotRows<2, kTpw, kAhead, kHad, true>::run(c);
+      UnrotRows<2, kTpw, kAhead, kNv, kRazer, kHad, true>::run(c);
     else
-      UnrotRows<1, kTpw, kAhead, kHad, true>::run(c);
+      UnrotRows<1, kTpw, kAhead, kNv, kRazer, kHad, true>::run(c);
   } else {
-    UnrotRows<8, kTpw, kAhead, kHad, false>::run(c);
+    UnrotRows<8, kTpw, kAhead, kNv, kRazer, kHad, false>::run(c);
   }
 }
 
@@ -276,9 +331,9 @@ __global__ __launch_bounds__(kThreads) void channel_energy_kernel(const uint16_t
 }
 
 // ================================ launchers =================================
-template <int kTpw, bool kHad, bool kPerm>
+template <int kTpw, bool kNv, bool kRazer, bool kHad, bool kPerm>
 static void unrot_launch(const Shape& s, const int32_t* perm, const uint8_t* c, const uint8_t* sc,
-                         uint16_t* o, const RotGeom& g, hipStream_t st) {
+                         const float* ts, uint16_t* o, const RotGeom& g, hipStream_t st) {
   // as for the forward kernel: pad LDS so that exactly kWgs work-groups fit per CU
 #ifdef FP4_UNROT_WG_PER_CU
   constexpr int kWgs = FP4_UNROT_WG_PER_CU;
@@ -291,29 +346,46 @@ static void unrot_launch(const Shape& s, const int32_t* perm, const uint8_t* c, 
   constexpr size_t kStatic = kPerm ? 2 * 8192 * kTpw : 16;
   const size_t share = (size_t)di.lds / kWgs;
   const size_t pad = share > kStatic + 1024 ? share - kStatic - 1024 : 0;
-  hipLaunchKernelGGL((mx_dequant_unrotate_kernel<kTpw, kHad, kPerm>), dim3(grid), dim3(kThreads),
-                     pad, st, c, sc, perm, o, g);
+  hipLaunchKernelGGL((dequant_unrotate_kernel<kTpw, kNv, kRazer, kHad, kPerm>), dim3(grid),
+                     dim3(kThreads), pad, st, c, sc, ts, perm, o, g);
 }
 
-template <bool kHad, bool kPerm>
+template <bool kNv, bool kRazer, bool kHad, bool kPerm>
 static void unrot_dispatch(const Shape& s, const int32_t* perm, const uint8_t* c,
-                           const uint8_t* sc, uint16_t* o, const RotGeom& g, hipStream_t st) {
+                           const uint8_t* sc, const float* ts, uint16_t* o, const RotGeom& g,
+                           hipStream_t st) {
   const int64_t tpw = (s.cols + 32 * 32 * kWaves - 1) / (32 * 32 * kWaves);
-  if (tpw <= 1) unrot_launch<1, kHad, kPerm>(s, perm, c, sc, o, g, st);
-  else if (tpw <= 2) unrot_launch<2, kHad, kPerm>(s, perm, c, sc, o, g, st);
-  else if (tpw <= 3) unrot_launch<3, kHad, kPerm>(s, perm, c, sc, o, g, st);
-  else unrot_launch<4, kHad, kPerm>(s, perm, c, sc, o, g, st);
+  if (tpw <= 1) unrot_launch<1, kNv, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
+  else if (tpw <= 2) unrot_launch<2, kNv, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
+  else if (tpw <= 3) unrot_launch<3, kNv, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
+  else unrot_launch<4, kNv, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
+}
+
+template <bool kNv, bool kRazer>
+static void unrot_variants(const Shape& s, const int32_t* perm, bool hadamard, const uint8_t* c,
+                           const uint8_t* sc, const float* ts, uint16_t* o, const RotGeom& g,
+                           hipStream_t st) {
+  if (hadamard && perm) unrot_dispatch<kNv, kRazer, true, true>(s, perm, c, sc, ts, o, g, st);
+  if (hadamard && !perm) unrot_dispatch<kNv, kRazer, true, false>(s, perm, c, sc, ts, o, g, st);
+  if (!hadamard && perm) unrot_dispatch<kNv, kRazer, false, true>(s, perm, c, sc, ts, o, g, st);
 }
 
 void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard,
                                 const void* codes, const void* scales, void* out, hipStream_t st) {
-  RotGeom g = rot_geom(s, 0);
-  auto cp = static_cast<const uint8_t*>(codes);
-  auto sp = static_cast<const uint8_t*>(scales);
-  auto op = static_cast<uint16_t*>(out);
-  if (hadamard && perm) unrot_dispatch<true, true>(s, perm, cp, sp, op, g, st);
-  if (hadamard && !perm) unrot_dispatch<true, false>(s, perm, cp, sp, op, g, st);
-  if (!hadamard && perm) unrot_dispatch<false, true>(s, perm, cp, sp, op, g, st);
+  unrot_variants<false, false>(s, perm, hadamard != 0, static_cast<const uint8_t*>(codes),
+                               static_cast<const uint8_t*>(scales), nullptr,
+                               static_cast<uint16_t*>(out), rot_geom(s, 0), st);
+}
+
+void launch_nv_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard, bool razer,
+                                const void* codes, const void* scales, const float* ts, void* out,
+                                hipStream_t st) {
+  const RotGeom g = rot_geom(s, 0, 16);
+  auto c = static_cast<const uint8_t*>(codes);
+  auto sc = static_cast<const uint8_t*>(scales);
+  auto o = static_cast<uint16_t*>(out);
+  if (razer) unrot_variants<true, true>(s, perm, hadamard != 0, c, sc, ts, o, g, st);
+  else unrot_variants<true, false>(s, perm, hadamard != 0, c, sc, ts, o, g, st);
 }
 
 void launch_channel_energy(int64_t rows, int64_t cols, int64_t ld_x, const void* x, float* energy,

@@ -125,16 +125,19 @@ int fp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, i
  * gives NaN). NVFP4: bf16_rne(fp32(value * s_eff)); RaZeR mode decodes code
  * 0x8 to the block's special value, the decoder rebuilding it from the scale
  * byte's top bit ([RaZeR] sec. 2.3).
- * Optional inverse rotation (MXFP4 only) so the result lies in the original
- * basis: with hadamard == 32 the block Hadamard is applied again (it is its own
+ * Optional inverse rotation so the result lies in the original basis: with
+ * hadamard == block the block Hadamard is applied again (it is its own
  * inverse), then with perm != NULL element j is written to column perm[j].
- * The inverse-rotated values are computed in fp32 and rounded once to bf16.
+ * The inverse-rotated values are computed in fp32 and rounded once to bf16:
+ * the transform of the decoded grid values is exact, and the block scale
+ * (MXFP4 2^e, NVFP4 s_eff) multiplies once, after it.
  *
  *  codes, scales, tensor_scale  as produced by fp4_quantize / fp4_rotate_quantize
  *  rows, cols, format, block, mode  as for fp4_quantize
  *  perm         NULL or device int32[cols], a permutation of 0..cols-1;
  *               requires cols <= 16384
- *  hadamard     0 or 32 (MXFP4)
+ *  hadamard     0, or the block size (32 for MXFP4, 16 for NVFP4); with a
+ *               rotation (perm or hadamard) cols % 32 == 0
  *  out_bf16     device, bf16 [rows, ld_out]; 16-byte aligned, ld_out % 8 == 0
  */
 int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int64_t ld_scales,
@@ -143,23 +146,28 @@ int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int6
                    int64_t ld_out, void* stream);
 
 /*
- * fp4_rotate_quantize -- two-level rotation fused with MXFP4 quantize + pack
- * ([TORQ] sec. 2(a) and 2(b)).
+ * fp4_rotate_quantize -- two-level rotation fused with FP4 quantize + pack
+ * ([TORQ] sec. 2(a) and 2(b); NVFP4: the generalisation remark of its results).
  *
  * Level 1: channel permutation x'[r, j] = x[r, perm[j]] (perm computed offline,
  * e.g. by fp4_build_permutation from fp4_channel_energy, so that every block
  * receives a balanced share of channel energy). Level 2: the orthonormal
- * Sylvester-Hadamard matrix H[i][j] = (-1)^popcount(i & j) / sqrt(32) inside
- * each 32-block, y = H x' in fp32. Then MXFP4 quantization of y exactly as in
- * fp4_quantize (the shared exponent comes from the fp32 amax of y).
+ * Sylvester-Hadamard matrix H[i][j] = (-1)^popcount(i & j) / sqrt(n) inside
+ * each n-block (n = block: 32 for MXFP4, 16 for NVFP4), y = H x' in fp32.
+ * Then quantization of y exactly as in fp4_quantize, with every amax taken
+ * over the fp32 y: MXFP4's shared exponent; NVFP4's block scales, RaZeR
+ * choice and (unless FP4_FLAG_TENSOR_SCALE_GIVEN) s_t = amax(y) / 2688. With
+ * a computed s_t three kernels are enqueued (rotation + amax partials held in
+ * the code array, s_t, rotation + quantize); otherwise one.
  *
  *  perm         NULL (identity) or device int32[cols], a permutation of
  *               0..cols-1 (entries are clamped to cols-1); requires
  *               cols <= 16384. A permutation made of aligned runs of 2, 4 or
  *               8 consecutive channels (fp4_build_permutation with group > 1)
  *               is detected and gathered with 4-, 8- or 16-byte LDS reads
- *  hadamard     32 or 0 (none)
- *  format       FP4_MXFP4 (NVFP4 returns FP4_ERR_UNSUPPORTED)
+ *  hadamard     the block size (32 MXFP4, 16 NVFP4) or 0 (none)
+ *  format       FP4_MXFP4, or FP4_NVFP4 with mode FP4_PLAIN or FP4_RAZER
+ *  cols         cols % 32 == 0
  *  rotated_out  NULL, or device fp32 [rows, ld_rot] receiving y; 16-byte
  *               aligned, ld_rot % 4 == 0 (for parity checks)
  *  others       as for fp4_quantize

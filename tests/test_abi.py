@@ -85,6 +85,8 @@ def test_rotate_and_dequant_validation(L):
     R = L.fp4_rotate_quantize
     assert R(FAKE, 4, 64, 64, None, 16, 0, 32, 0, 0, FAKE, 32, FAKE, 2, None, None, 0, None) == -4
     assert R(FAKE, 4, 64, 64, None, 32, 1, 16, 0, 0, FAKE, 32, FAKE, 4, TS, None, 0, None) == -4
+    # NVFP4 rotation works on 32-element segments: cols % 32
+    assert R(FAKE, 4, 48, 48, None, 16, 1, 16, 1, 0, FAKE, 24, FAKE, 3, TS, None, 0, None) == -2
     assert R(FAKE, 4, 32768, 32768, FAKE, 32, 0, 32, 0, 0, FAKE, 16384, FAKE, 1024, None, None,
              0, None) == -4  # permutation wider than the LDS row buffer
     assert R(FAKE, 4, 64, 64, None, 32, 0, 32, 0, 0, FAKE, 32, FAKE, 2, None, FAKE, 32,
@@ -94,6 +96,7 @@ def test_rotate_and_dequant_validation(L):
     # dequantize(codes, ldc, scales, lds, ts, rows, cols, fmt, block, mode, perm, had, out, ldo, s)
     D = L.fp4_dequantize
     assert D(FAKE, 32, FAKE, 4, TS, 4, 64, 1, 16, 0, None, 32, FAKE, 64, None) == -4
+    assert D(FAKE, 24, FAKE, 3, TS, 4, 48, 1, 16, 1, None, 16, FAKE, 48, None) == -2
     assert D(FAKE, 32, FAKE, 2, None, 4, 64, 0, 32, 1, None, 0, FAKE, 64, None) == -4
     assert D(FAKE, 32, FAKE, 4, None, 4, 64, 1, 16, 0, None, 0, FAKE, 64, None) == -1
     assert D(FAKE, 32, FAKE, 2, None, 4, 64, 0, 32, 0, None, 0, FAKE + 8, 64, None) == -3
