@@ -44,7 +44,8 @@ B_NV = 2 + 0.5 + 1 / 16   # NVFP4 quantize (without the tensor-amax read)
 
 
 MFMA_PEAK_BF16_TFLOPS = 2500.0
-ROT_KERNEL = "mx_rotq_perm_kernel"  # fused permutation + Hadamard + MXFP4 quantize
+ROT_KERNEL = "rotq_perm_kernel"  # fused permutation + Hadamard + FP4 quantize
+ROT_INSTANCE = ROT_KERNEL + "<2, 0, true, false, false>"  # the MXFP4 instance timed at 16384x8192
 ROT_SOURCES = ["block_scaled_fp4_absmax_amd/csrc/rotate.hip",
                "block_scaled_fp4_absmax_amd/csrc/rotation.hpp",
                "block_scaled_fp4_absmax_amd/csrc/fp4_device.hpp",
@@ -234,7 +235,7 @@ def roofline_c4(elems, ms):
     r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
          "frac": round(achieved / HBM_PEAK_GBS, 4),
          "traffic": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1),
-         "kernel": ROT_KERNEL + "<2,true,false,false> (2 MFMA tiles per wave per row)",
+         "kernel": ROT_KERNEL + "<2,0,true,false,false> (MXFP4; 2 MFMA tiles per wave per row)",
          "bytes_per_launch": int(elems * B_MX),
          "traffic_bytes_per_launch": traffic, "traffic_source": src,
          # the block Hadamard as a dense contraction: 2 x (32x32x16) MFMAs per 32 blocks
@@ -268,6 +269,33 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     ms = timed(torch, lambda i: fp4.dequantize(codes[i % n], scales[i % n], fp4.MXFP4, perm=perm,
                                                hadamard=32, out=outb), 20, 3)
     out["c4_mxfp4_dequantize_unrotate"] = gbs(ms, el, B_MX)
+
+    # NVFP4 + RaZeR after the two-level rotation on the same tensor (permutation
+    # balanced over 16-channel blocks, 16-point Hadamard)
+    perm16 = fp4.build_permutation(fp4.channel_energy(xs[0]), 16).cuda()
+    s16 = [torch.empty((rows, cols // 16), dtype=torch.uint8, device="cuda") for _ in range(n)]
+    t16 = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(n)]
+
+    def nv_rot(i, given):
+        k = i % n
+        fp4.rotate_quantize(xs[k], perm16, 16, codes=codes[k], scales=s16[k], fmt=fp4.NVFP4,
+                            mode=fp4.RAZER, tensor_scale=t16[k], scale_given=given)
+
+    ms = timed(torch, lambda i: nv_rot(i, False), 20, 3)
+    out["c4_nvfp4_razer_perm_h16_with_amax"] = gbs(ms, el, B_NV + 2)
+    ms = timed(torch, lambda i: nv_rot(i, True), 20, 3)
+    out["c4_nvfp4_razer_perm_h16_scale_given"] = gbs(ms, el, B_NV)
+    ms = timed(torch, lambda i: fp4.dequantize(codes[i % n], s16[i % n], fp4.NVFP4, fp4.RAZER,
+                                               t16[i % n], perm=perm16, hadamard=16, out=outb),
+               20, 3)
+    out["c4_nvfp4_razer_dequantize_unrotate"] = gbs(ms, el, B_NV)
+    xf = xs[0].float()
+    for name, (pm, had) in {"perm_h16": (perm16, 16), "h16": (None, 16),
+                            "plain": (None, 0)}.items():
+        c, sc, _, ts = fp4.rotate_quantize(xs[0], pm, had, fmt=fp4.NVFP4, mode=fp4.RAZER)
+        xh = fp4.dequantize(c, sc, fp4.NVFP4, fp4.RAZER, ts, perm=pm, hadamard=had)
+        out[f"c4_sqnr_db_nvfp4_razer_{name}"] = round(sqnr_db(torch, xf, xh.float()), 3)
+    del s16, xf
 
     # NVFP4 + RaZeR on the 4096x4096 weight recipe, enough copies to defeat the cache
     log("[bench] generating c2 for the NVFP4 rows")
@@ -406,8 +434,8 @@ def pmc_summary(dirs):
     write = _pmc_rows(dirs[1], "WRITE_SIZE")
     copy_k, f_copy = pick(fetch, "copy")
     _, w_copy = pick(write, "copy")
-    rot_k, f_rot = pick(fetch, ROT_KERNEL)
-    _, w_rot = pick(write, ROT_KERNEL)
+    rot_k, f_rot = pick(fetch, ROT_INSTANCE)
+    _, w_rot = pick(write, ROT_INSTANCE)
     med = lambda v: sorted(v)[len(v) // 2]
     f_fac = COPY_BYTES / (med(f_copy) * 1024)
     w_fac = COPY_BYTES / (med(w_copy) * 1024)
@@ -437,8 +465,8 @@ def pmc_summary(dirs):
     if len(dirs) > 2:
         busy = _pmc_rows(dirs[2], "SQ_VALU_MFMA_BUSY_CYCLES")
         cu = _pmc_rows(dirs[2], "SQ_BUSY_CU_CYCLES")
-        _, b = pick(busy, ROT_KERNEL)
-        _, c = pick(cu, ROT_KERNEL)
+        _, b = pick(busy, ROT_INSTANCE)
+        _, c = pick(cu, ROT_INSTANCE)
         lines += [f"MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES = "
                   f"{med(b) / max(med(c), 1):.4f} (median dispatch).", ""]
     lines += [
@@ -492,11 +520,11 @@ def trace_summary(trace_dir, bench_log):
         out.append(f"| `{name[:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     out.append("")
-    rot = [r for r in rows if ROT_KERNEL in r["Name"]]
+    rot = [r for r in rows if ROT_INSTANCE in r["Name"]]
     if line and wl == "c4" and rot:
         avg = float(rot[0]["AverageNs"]) / 1e3
         ev = line["ms_per_step"] * 1e3
-        out += [f"The fused kernel `{ROT_KERNEL}` averages {avg:.2f} us per launch here (warm-up "
+        out += [f"The fused kernel `{ROT_INSTANCE}` averages {avg:.2f} us per launch here (warm-up "
                 f"launches included); the same run's HIP-event time per step is {ev:.2f} us "
                 f"({ev / avg:.3f}x), one launch per step.", ""]
     elif line:
