@@ -22,6 +22,12 @@ than itself (the pins live in ``tests/test_oracle_*.py``):
 * ``nv_quantize_f32`` / ``nv_tensor_amax_f32``: pinned by an element-wise
   restatement of the NVFP4 steps with an independent brute-force code search
   on fp32 inputs, and by the nearest-grid and error-bound properties.
+* ``int4_value`` / ``int4_nearest`` / ``mxint4_scale`` / ``mxint4_quantize*``:
+  decoder pinned to numpy's two's complement sign extension; nearest search
+  to ``np.rint`` (round half to even) and exact Fraction brute force; the
+  scale pinned exhaustively by minimality over every bf16 magnitude; whole
+  tensors by the nearest-grid property, the half-step error bound, scale
+  invariance and sign symmetry.
 * ``razer_block``: pinned by exact Fraction SSE arg-min and exhaustive tiny-block
   enumeration.
 * ``rotate`` / ``unrotate_f64``: pinned to ``scipy.linalg.hadamard`` (orders 16
@@ -91,6 +97,11 @@ def _load():
         "orc_f32_to_bf16": (ctypes.c_uint16, [f32]),
         "orc_mx_quantize_f32": (None, [vp, i64, i64, i64, i32, vp, i64, vp, i64]),
         "orc_mx_quantize_bf16": (None, [vp, i64, i64, i64, i32, vp, i64, vp, i64]),
+        "orc_int4_value": (f64, [i32]),
+        "orc_int4_nearest": (i32, [f64]),
+        "orc_mxint4_scale": (i32, [f64, i32]),
+        "orc_mxint4_quantize_f32": (None, [vp, i64, i64, i64, i32, vp, i64, vp, i64]),
+        "orc_mxint4_quantize_bf16": (None, [vp, i64, i64, i64, i32, vp, i64, vp, i64]),
         "orc_nv_tensor_amax": (f32, [vp, i64, i64, i64]),
         "orc_nv_tensor_scale": (f32, [f32]),
         "orc_nv_quantize_bf16": (None, [vp, i64, i64, i64, i32, f32, vp, i64, vp, i64]),
@@ -192,6 +203,43 @@ def mx_quantize_f32(x: np.ndarray, floor_rule: bool = False) -> Tuple[np.ndarray
     return codes, scales
 
 
+def int4_value(code: int) -> float:
+    return _load().orc_int4_value(int(code))
+
+
+def int4_nearest(y: float) -> int:
+    return _load().orc_int4_nearest(float(y))
+
+
+def mxint4_scale(amax: float, floor_rule: bool = False) -> int:
+    return _load().orc_mxint4_scale(float(amax), int(floor_rule))
+
+
+def mxint4_quantize(x_bf16: np.ndarray, floor_rule: bool = False
+                    ) -> Tuple[np.ndarray, np.ndarray]:
+    """MXINT4 codes [rows, cols/2] and E8M0 scale bytes [rows, cols/32] of bf16 bits."""
+    assert x_bf16.dtype == np.uint16
+    rows, cols = x_bf16.shape
+    assert cols % 32 == 0
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 32), np.uint8)
+    _load().orc_mxint4_quantize_bf16(_ptr(x_bf16), rows, cols, _ld(x_bf16), int(floor_rule),
+                                     _ptr(codes), cols // 2, _ptr(scales), cols // 32)
+    return codes, scales
+
+
+def mxint4_quantize_f32(x: np.ndarray, floor_rule: bool = False
+                        ) -> Tuple[np.ndarray, np.ndarray]:
+    x = np.ascontiguousarray(x, np.float32)
+    rows, cols = x.shape
+    assert cols % 32 == 0
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 32), np.uint8)
+    _load().orc_mxint4_quantize_f32(_ptr(x), rows, cols, cols, int(floor_rule), _ptr(codes),
+                                    cols // 2, _ptr(scales), cols // 32)
+    return codes, scales
+
+
 def nv_tensor_amax(x_bf16: np.ndarray) -> float:
     rows, cols = x_bf16.shape
     return _load().orc_nv_tensor_amax(_ptr(x_bf16), rows, cols, _ld(x_bf16))
@@ -231,7 +279,7 @@ def razer_block(y: np.ndarray) -> Tuple[np.ndarray, int, float, float]:
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: int, razer: bool = False,
                tensor_scale: float = 1.0) -> np.ndarray:
-    """bf16 bits [rows, cols] of the decoded values (fmt 0 = MXFP4, 1 = NVFP4)."""
+    """bf16 bits [rows, cols] of the decoded values (fmt 0 = MXFP4, 1 = NVFP4, 2 = MXINT4)."""
     rows = codes.shape[0]
     cols = codes.shape[1] * 2
     out = np.zeros((rows, cols), np.uint16)
@@ -300,6 +348,14 @@ def rotate_quantize_nv(x_bf16: np.ndarray, perm: Optional[np.ndarray], hadamard:
     y = rotate(x_bf16, perm, hadamard)
     codes, scales, ts = nv_quantize_f32(y, razer, tensor_scale)
     return codes, scales, ts, y
+
+
+def rotate_quantize_mxint4(x_bf16: np.ndarray, perm: Optional[np.ndarray], hadamard: int,
+                           floor_rule: bool = False):
+    """Rotation then MXINT4 quantization of the fp32 rotated values."""
+    y = rotate(x_bf16, perm, hadamard)
+    codes, scales = mxint4_quantize_f32(y, floor_rule)
+    return codes, scales, y
 
 
 def unrotate_f64(y: np.ndarray, perm: Optional[np.ndarray], hadamard: int) -> np.ndarray:

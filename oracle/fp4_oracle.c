@@ -246,6 +246,101 @@ void orc_mx_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* MXINT4: [TORQ] (the generalisation remark of its results) reports the     */
+/* rotation with an MXINT4 grid as well; the pages name the format only.     */
+/* Reading: the microscaling integer element of the OCP MX family at 4 bits: */
+/* a two's complement integer k in [-8, 7] read as fixed point with two      */
+/* fraction bits (value k / 4, largest power of two 1, the 4-bit analogue of */
+/* MXINT8's k / 64), 32-element blocks, one E8M0 byte per block.             */
+/* Encoding: nearest grid value, ties to even k, clamped to k in [-7, 7] so  */
+/* the grid is symmetric (k = -8 only decodes). Scale rule, as for MXFP4:    */
+/* the smallest e with amax <= 1.75 * 2^e (the top symmetric code), so no    */
+/* element is clipped (e is capped at 127, so a magnitude above 1.75 * 2^127 */
+/* saturates); the floor rule takes e = floor(log2 amax), the element        */
+/* format's largest power of two being 1, and saturates at 1.75.             */
+/* ------------------------------------------------------------------------ */
+double orc_int4_value(int code) {
+  int k = code & 15;
+  if (k >= 8) k -= 16;
+  return k / 4.0;
+}
+
+/* Nearest k / 4 (|k| <= 7) to y by brute force; ties to the even k. */
+int orc_int4_nearest(double y) {
+  int best = 0;
+  double bd = INFINITY;
+  for (int k = -7; k <= 7; ++k) {
+    double d = fabs(y - k / 4.0);
+    if (d < bd || (d == bd && (k & 1) == 0)) {
+      bd = d;
+      best = k;
+    }
+  }
+  return best & 15;
+}
+
+int orc_mxint4_scale(double amax, int floor_rule) {
+  if (!isfinite(amax)) return 0xFF;
+  if (floor_rule) {
+    if (amax == 0.0) return 0;
+    int k;
+    frexp(amax, &k); /* floor(log2 amax) = k - 1 */
+    int e = k - 1;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e + 127;
+  }
+  for (int e = -127; e <= 127; ++e)
+    if (amax <= ldexp(1.75, e)) return e + 127;
+  return 254;
+}
+
+static void mxint_block(const float* v, int floor_rule, uint8_t* row_codes, int64_t j0,
+                        uint8_t* scale_out) {
+  double amax = 0.0;
+  int nonfinite = 0;
+  for (int i = 0; i < 32; ++i) {
+    if (!isfinite(v[i])) nonfinite = 1;
+    double a = fabs((double)v[i]);
+    if (a > amax) amax = a;
+  }
+  if (nonfinite) { /* as for MXFP4: the NaN scale byte, codes 0 */
+    *scale_out = 0xFF;
+    for (int i = 0; i < 32; ++i) put_nibble(row_codes, j0 + i, 0);
+    return;
+  }
+  int byte = orc_mxint4_scale(amax, floor_rule);
+  *scale_out = (uint8_t)byte;
+  for (int i = 0; i < 32; ++i)
+    put_nibble(row_codes, j0 + i, orc_int4_nearest(ldexp((double)v[i], 127 - byte)));
+}
+
+void orc_mxint4_quantize_f32(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                             int floor_rule, uint8_t* codes, int64_t ld_codes,
+                             uint8_t* scales, int64_t ld_scales) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < cols / 32; ++b)
+      mxint_block(x + r * ld_x + 32 * b, floor_rule, codes + r * ld_codes, 32 * b,
+                  scales + r * ld_scales + b);
+}
+
+void orc_mxint4_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                              int floor_rule, uint8_t* codes, int64_t ld_codes,
+                              uint8_t* scales, int64_t ld_scales) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r) {
+    float v[32];
+    for (int64_t b = 0; b < cols / 32; ++b) {
+      for (int i = 0; i < 32; ++i) v[i] = orc_bf16_to_f32(x[r * ld_x + 32 * b + i]);
+      mxint_block(v, floor_rule, codes + r * ld_codes, 32 * b, scales + r * ld_scales + b);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* NVFP4: blocks of 16, E4M3 block scale, fp32 per-tensor scale s_t.          */
 /* The scale is derived from the block absmax and is therefore positive, so  */
 /* its sign bit is free ([RaZeR] sec. 1). Readings where the pages are       */
@@ -376,7 +471,8 @@ float orc_nv_tensor_amax_f32(const float* x, int64_t rows, int64_t cols, int64_t
 }
 
 /* ------------------------------------------------------------------------ */
-/* Dequantization. MXFP4: value * 2^e, exact before the final rounding.      */
+/* Dequantization. MXFP4 and MXINT4: value * 2^e, exact before the final   */
+/* rounding.                                                                 */
 /* NVFP4: fp32 product value * s_eff. RaZeR: code 0x8 decodes to the block's */
 /* special value, +5 or -5 by the scale's top bit ([RaZeR] sec. 2.2 and 2.3: */
 /* the decoder rebuilds the special value from the metadata bits).           */
@@ -386,10 +482,10 @@ static double dq_value(const uint8_t* codes, int64_t ld_codes, const uint8_t* sc
                        int64_t ld_scales, float s_t, int64_t r, int64_t j, int format,
                        int razer) {
   int c = get_nibble(codes + r * ld_codes, j);
-  if (format == 0) {
+  if (format == 0 || format == 2) {
     int byte = scales[r * ld_scales + j / 32];
     if (byte == 0xFF) return NAN;
-    return ldexp(orc_e2m1_value(c), byte - 127);
+    return ldexp(format == 0 ? orc_e2m1_value(c) : orc_int4_value(c), byte - 127);
   }
   int byte = scales[r * ld_scales + j / 16];
   double v;

@@ -41,6 +41,17 @@ void orc_mx_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t
                           int floor_rule, uint8_t* codes, int64_t ld_codes,
                           uint8_t* scales, int64_t ld_scales);
 
+/* MXINT4: 32-element blocks, E8M0 scale, two's complement k / 4 elements */
+double orc_int4_value(int code);
+int orc_int4_nearest(double y);
+int orc_mxint4_scale(double amax, int floor_rule);
+void orc_mxint4_quantize_f32(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                             int floor_rule, uint8_t* codes, int64_t ld_codes,
+                             uint8_t* scales, int64_t ld_scales);
+void orc_mxint4_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                              int floor_rule, uint8_t* codes, int64_t ld_codes,
+                              uint8_t* scales, int64_t ld_scales);
+
 /* NVFP4: 16-element blocks, E4M3 block scale, fp32 tensor scale; RaZeR option */
 float orc_nv_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x);
 float orc_nv_tensor_scale(float amax);
@@ -54,7 +65,7 @@ float orc_nv_tensor_amax_f32(const float* x, int64_t rows, int64_t cols, int64_t
 int orc_razer_block(const float* y, int n, uint8_t* codes, double* sse_chosen,
                     double* sse_plain);
 
-/* dequantization; format 0 = MXFP4, 1 = NVFP4 */
+/* dequantization; format 0 = MXFP4, 1 = NVFP4, 2 = MXINT4 */
 void orc_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                     int64_t ld_scales, float tensor_scale, int64_t rows, int64_t cols,
                     int format, int razer, uint16_t* out, int64_t ld_out);
