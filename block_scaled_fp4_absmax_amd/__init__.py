@@ -1,4 +1,4 @@
-"""Block-scaled FP4 (MXFP4 / NVFP4, RaZeR, two-level rotation) for MI355X.
+"""Block-scaled 4-bit (MXFP4 / NVFP4 / MXINT4, RaZeR, two-level rotation) for MI355X.
 
 Thin Python binding over the C ABI in ``include/fp4.h`` (``libfp4.so``, built
 in-tree by ``block_scaled_fp4_absmax_amd.build``). Every step of the path runs
@@ -14,12 +14,12 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "MXFP4", "NVFP4", "PLAIN", "RAZER", "FLAG_TENSOR_SCALE_GIVEN", "FLAG_SCALE_OCP_FLOOR",
+    "MXFP4", "NVFP4", "MXINT4", "PLAIN", "RAZER", "FLAG_TENSOR_SCALE_GIVEN", "FLAG_SCALE_OCP_FLOOR",
     "Fp4Error", "lib", "library_path", "quantize", "dequantize", "rotate_quantize",
     "channel_energy", "build_permutation", "block_of",
 ]
 
-MXFP4, NVFP4 = 0, 1
+MXFP4, NVFP4, MXINT4 = 0, 1, 2
 PLAIN, RAZER = 0, 1
 FLAG_TENSOR_SCALE_GIVEN = 1
 FLAG_SCALE_OCP_FLOOR = 2
@@ -77,7 +77,7 @@ def _check(fn: str, status: int) -> None:
 
 
 def block_of(fmt: int) -> int:
-    return 32 if fmt == MXFP4 else 16
+    return 16 if fmt == NVFP4 else 32
 
 
 def _stream(stream):
@@ -158,8 +158,8 @@ def rotate_quantize(x, perm=None, hadamard: Optional[int] = None, floor_rule: bo
     ``hadamard`` defaults to the format's block size (32 MXFP4, 16 NVFP4); 0
     turns the transform off. NVFP4 takes ``mode`` (PLAIN or RAZER) and a
     tensor scale as in :func:`quantize`. Returns (codes, scales, rotated fp32
-    [rows, cols] or None) for MXFP4 and (codes, scales, rotated, tensor_scale)
-    for NVFP4.
+    [rows, cols] or None) for MXFP4 and MXINT4, and (codes, scales, rotated,
+    tensor_scale) for NVFP4.
     """
     import torch
     rows, cols, ld = _rows_ld(x)

@@ -11,19 +11,23 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int block_of(int format) { return format == FP4_MXFP4 ? 32 : 16; }
+int block_of(int format) { return format == FP4_NVFP4 ? 16 : 32; }
+
+bool known_format(int format) {
+  return format == FP4_MXFP4 || format == FP4_NVFP4 || format == FP4_MXINT4;
+}
 
 // Checks shared by the quantizing entry points.
 int check_quant_args(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int format,
                      int block, int mode, uint32_t flags, const void* codes, int64_t ld_codes,
                      const void* scales, int64_t ld_scales, const float* tensor_scale) {
-  if (format != FP4_MXFP4 && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
+  if (!known_format(format)) return FP4_ERR_UNSUPPORTED;
   if (block != block_of(format)) return FP4_ERR_UNSUPPORTED;
   if (mode != FP4_PLAIN && mode != FP4_RAZER) return FP4_ERR_UNSUPPORTED;
   if (mode == FP4_RAZER && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;  // E8M0 has no sign bit
   if (flags & ~(FP4_FLAG_TENSOR_SCALE_GIVEN | FP4_FLAG_SCALE_OCP_FLOOR)) return FP4_ERR_UNSUPPORTED;
   if ((flags & FP4_FLAG_TENSOR_SCALE_GIVEN) && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
-  if ((flags & FP4_FLAG_SCALE_OCP_FLOOR) && format != FP4_MXFP4) return FP4_ERR_UNSUPPORTED;
+  if ((flags & FP4_FLAG_SCALE_OCP_FLOOR) && format == FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 0 || cols % block != 0) return FP4_ERR_SHAPE;
   if (ld_x < cols || ld_codes < cols / 2 || ld_scales < cols / block) return FP4_ERR_SHAPE;
   if (rows > 0 && cols > 0 && rows * cols / 8 >= (int64_t)1 << 31) return FP4_ERR_UNSUPPORTED;
@@ -71,8 +75,10 @@ int fp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, i
   const bool need_scale = format == FP4_NVFP4 && !(flags & FP4_FLAG_TENSOR_SCALE_GIVEN);
   if (empty && !need_scale) return FP4_OK;  // nothing to enqueue
   (void)hipGetLastError();  // clear a stale error so the status below is this call's
-  if (format == FP4_MXFP4) {
-    if (!empty) fp4::launch_mx_quant(s, (flags & FP4_FLAG_SCALE_OCP_FLOOR) != 0, x_bf16, codes, scales, st);
+  if (format != FP4_NVFP4) {
+    if (!empty)
+      fp4::launch_mx_quant(s, (flags & FP4_FLAG_SCALE_OCP_FLOOR) != 0, format == FP4_MXINT4, x_bf16,
+                           codes, scales, st);
   } else {
     if (need_scale) fp4::launch_nv_tensor_scale(s, x_bf16, codes, tensor_scale, st);
     if (!empty) fp4::launch_nv_quant(s, mode == FP4_RAZER, x_bf16, codes, scales, tensor_scale, st);
@@ -84,7 +90,7 @@ int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int6
                    const float* tensor_scale, int64_t rows, int64_t cols, int format, int block,
                    int mode, const int32_t* perm, int hadamard, void* out_bf16, int64_t ld_out,
                    void* stream) {
-  if (format != FP4_MXFP4 && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
+  if (!known_format(format)) return FP4_ERR_UNSUPPORTED;
   if (block != block_of(format)) return FP4_ERR_UNSUPPORTED;
   if (mode != FP4_PLAIN && mode != FP4_RAZER) return FP4_ERR_UNSUPPORTED;
   if (mode == FP4_RAZER && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
@@ -104,8 +110,9 @@ int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int6
   hipStream_t st = static_cast<hipStream_t>(stream);
   Shape s{rows, cols, ld_out, ld_codes, ld_scales};
   (void)hipGetLastError();
-  if ((hadamard || perm) && format == FP4_MXFP4)
-    fp4::launch_mx_dequant_unrotate(s, perm, hadamard, codes, scales, out_bf16, st);
+  if ((hadamard || perm) && format != FP4_NVFP4)
+    fp4::launch_mx_dequant_unrotate(s, perm, hadamard, format == FP4_MXINT4, codes, scales,
+                                    out_bf16, st);
   else if (hadamard || perm)
     fp4::launch_nv_dequant_unrotate(s, perm, hadamard, mode == FP4_RAZER, codes, scales,
                                     tensor_scale, out_bf16, st);
@@ -134,9 +141,10 @@ int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t 
   hipStream_t st = static_cast<hipStream_t>(stream);
   Shape s{rows, cols, ld_x, ld_codes, ld_scales};
   (void)hipGetLastError();
-  if (format == FP4_MXFP4)
+  if (format != FP4_NVFP4)
     fp4::launch_mx_rotate_quant(s, perm, hadamard, (flags & FP4_FLAG_SCALE_OCP_FLOOR) != 0,
-                                x_bf16, codes, scales, rotated_out, ld_rot, st);
+                                format == FP4_MXINT4, x_bf16, codes, scales, rotated_out, ld_rot,
+                                st);
   else
     fp4::launch_nv_rotate_quant(s, perm, hadamard, mode == FP4_RAZER, !need_scale, x_bf16, codes,
                                 scales, tensor_scale, rotated_out, ld_rot, st);

@@ -120,6 +120,58 @@ __device__ __forceinline__ uint32_t cvt8_f32(const float* y, float scale) {
   return o;
 }
 
+// ---- MXINT4 -----------------------------------------------------------------
+// Element: a two's complement nibble k in [-8, 7] with value k / 4, one E8M0
+// byte per 32-element block. Default scale: the smallest e in [-127, 127]
+// with amax <= 1.75 * 2^e (the top symmetric code, so nothing is clipped):
+// for normal amax = (1 + f) 2^(E - 127) that is e = E - 127 + [f > 0.75],
+// capped at 127 (larger magnitudes saturate); a subnormal amax = f 2^-149
+// fits e = -127 while f <= 1.75 * 2^22. Floor rule: e = floor(log2 amax) =
+// E - 127 (byte 0 for zero and subnormal amax). m: fp32 bits of amax.
+template <bool kFloor>
+__device__ __forceinline__ uint32_t mxint_byte(uint32_t m) {
+  if (m >= 0x7F800000u) return 0xFFu;
+  const uint32_t E = m >> 23, f = m & 0x7FFFFFu;
+  if (kFloor) return E;
+  if (E == 0u) return f > 0x700000u ? 1u : 0u;
+  const uint32_t b = E + (f > 0x600000u ? 1u : 0u);
+  return b > 254u ? 254u : b;
+}
+
+// Eight values -> eight nibbles, element k in nibble k: y 2^sh (sh = 2 - e,
+// an exact rescale wherever the result can round to a non-zero k) clamped to
+// [-7, 7], then rounded to the nearest integer with ties to even by adding
+// 1.5 * 2^23, which leaves k in the low mantissa bits (two's complement mod 16).
+__device__ __forceinline__ uint32_t int4x8_f32(const float* y, int sh) {
+  uint32_t o = 0u;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float t = __builtin_amdgcn_fmed3f(__builtin_amdgcn_ldexpf(y[k], sh), -7.0f, 7.0f);
+    o |= (__float_as_uint(t + 12582912.0f) & 15u) << (4 * k);
+  }
+  return o;
+}
+
+// Eight nibbles -> bf16 pairs of k 2^(e - 2), exact (k has at most 3
+// significant bits); the NaN scale byte decodes to NaN.
+__device__ __forceinline__ u32x4_t int4x8_decode(uint32_t w, uint32_t byte) {
+  const int sh = (int)byte - 129;
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    v[k] = __builtin_amdgcn_ldexpf((float)((int32_t)(w << (28 - 4 * k)) >> 28), sh);
+  if (byte == 0xFFu) return u32x4_t{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+  return u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                 pack_bf16x2(v[6], v[7])};
+}
+
+__device__ __forceinline__ void widen8(u32x4_t d, float* v) {
+  v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
+  v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
+  v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z);
+  v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
+}
+
 // ---- E4M3 block scale (NVFP4) ---------------------------------------------
 // OCP E4M3 "fn": bias 7, subnormals m * 2^-9, largest finite 448, 0x7F NaN.
 // Nearest code to s >= 0 with ties to the even code, saturating at 448;

@@ -28,8 +28,9 @@ struct Shape {
   int64_t ld_s;  // scale row stride, bytes
 };
 
-void launch_mx_quant(const Shape& s, bool floor_rule, const void* x, void* codes, void* scales,
-                     hipStream_t st);
+// MXFP4, or MXINT4 with mxint.
+void launch_mx_quant(const Shape& s, bool floor_rule, bool mxint, const void* x, void* codes,
+                     void* scales, hipStream_t st);
 // Writes s_t; uses the code buffer as scratch for per-work-group partial maxima.
 void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float* ts,
                             hipStream_t st);
@@ -41,16 +42,17 @@ void launch_nv_quant(const Shape& s, bool razer, const void* x, void* codes, voi
                      const float* ts, hipStream_t st);
 void launch_dequant(const Shape& s, int format, bool razer, const void* codes, const void* scales,
                     const float* ts, void* out, hipStream_t st);
+// MXFP4, or MXINT4 with mxint.
 void launch_mx_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, bool floor_rule,
-                            const void* x, void* codes, void* scales, float* rot, int64_t ld_rot,
-                            hipStream_t st);
+                            bool mxint, const void* x, void* codes, void* scales, float* rot,
+                            int64_t ld_rot, hipStream_t st);
 // NVFP4 (block 16) after the two-level rotation with the 16-point Hadamard;
 // with !scale_given, s_t is computed from the rotated tensor first (the code
 // buffer holds the amax partials meanwhile). Requires cols % 32 == 0.
 void launch_nv_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, bool razer,
                             bool scale_given, const void* x, void* codes, void* scales,
                             float* ts, float* rot, int64_t ld_rot, hipStream_t st);
-void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard,
+void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard, bool mxint,
                                 const void* codes, const void* scales, void* out, hipStream_t st);
 // NVFP4 decode followed by the inverse rotation (16-point Hadamard, then the
 // inverse permutation). Requires cols % 32 == 0.

@@ -1,4 +1,5 @@
-// quant.hip -- MXFP4 / NVFP4 (+RaZeR) quantize + pack, tensor amax, dequantize.
+// quant.hip -- MXFP4 / MXINT4 / NVFP4 (+RaZeR) quantize + pack, tensor amax,
+// dequantize.
 //
 // Work decomposition: one lane owns one 16-byte chunk of eight consecutive
 // bf16 (a coalesced dwordx4 load), so four neighbouring lanes hold one
@@ -44,8 +45,9 @@ __device__ __forceinline__ void locate(const Geom& g, uint32_t v, int64_t& xo, i
   }
 }
 
-// ---------------------------------------------------------------- MXFP4 ----
-template <bool kFlat, bool kFloor>
+// ------------------------------------------------------- MXFP4 / MXINT4 ----
+// kInt: MXINT4 elements (two's complement k / 4) instead of E2M1.
+template <bool kFlat, bool kFloor, bool kInt>
 __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint16_t* __restrict__ x,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales, Geom g) {
@@ -70,8 +72,16 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint16_t* __re
         uint32_t m = absmax8_bf16(d[u]);
         m = max(m, dpp_xor1(m));
         m = max(m, dpp_xor2(m));
-        uint32_t byte = e8m0_byte<kFloor>(m << 16);
-        uint32_t w = byte == 0xFFu ? 0u : cvt8_bf16(d[u], e8m0_operand(byte));
+        uint32_t byte, w;
+        if constexpr (kInt) {
+          byte = mxint_byte<kFloor>(m << 16);
+          float v[8];
+          widen8(d[u], v);
+          w = byte == 0xFFu ? 0u : int4x8_f32(v, 129 - (int)byte);
+        } else {
+          byte = e8m0_byte<kFloor>(m << 16);
+          w = byte == 0xFFu ? 0u : cvt8_bf16(d[u], e8m0_operand(byte));
+        }
         __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + co[u]));
         if (leader) scales[so[u]] = (uint8_t)byte;
       }
@@ -256,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(const uint16_t* __re
 }
 
 // ------------------------------------------------------------ dequantize ----
-template <bool kFlat>
+template <bool kFlat, bool kInt>
 __global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __restrict__ codes,
                                                               const uint8_t* __restrict__ scales,
                                                               uint16_t* __restrict__ out, Geom g) {
@@ -278,12 +288,16 @@ __global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __r
     for (int u = 0; u < kUnroll; ++u) {
       uint32_t v = base + u * stride;
       if (v >= g.n) continue;
-      const float s = e8m0_operand(sb[u]);  // byte 0xFF -> NaN scale -> NaN outputs
       u32x4_t o;
-      o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], s, 0));
-      o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], s, 1));
-      o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], s, 2));
-      o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], s, 3));
+      if constexpr (kInt) {
+        o = int4x8_decode(w[u], sb[u]);
+      } else {
+        const float s = e8m0_operand(sb[u]);  // byte 0xFF -> NaN scale -> NaN outputs
+        o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], s, 0));
+        o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], s, 1));
+        o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], s, 2));
+        o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], s, 3));
+      }
       __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + xo[u]));
     }
   }
@@ -364,18 +378,25 @@ static inline Geom make_geom(const Shape& s, int block) {
 #define FP4_LAUNCH(kern, grid, stream, ...) \
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, __VA_ARGS__)
 
-void launch_mx_quant(const Shape& s, bool floor_rule, const void* x, void* codes, void* scales,
-                     hipStream_t st) {
+template <bool kInt>
+static void mx_quant_variants(const Shape& s, bool floor_rule, const void* x, void* codes,
+                              void* scales, hipStream_t st) {
   Geom g = make_geom(s, 32);
   const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / 32;
   const int grid = grid_for(g.n);
   auto xp = static_cast<const uint16_t*>(x);
   auto cp = static_cast<uint8_t*>(codes);
   auto sp = static_cast<uint8_t*>(scales);
-  if (flat && !floor_rule) FP4_LAUNCH((mx_quant_kernel<true, false>), grid, st, xp, cp, sp, g);
-  if (flat && floor_rule) FP4_LAUNCH((mx_quant_kernel<true, true>), grid, st, xp, cp, sp, g);
-  if (!flat && !floor_rule) FP4_LAUNCH((mx_quant_kernel<false, false>), grid, st, xp, cp, sp, g);
-  if (!flat && floor_rule) FP4_LAUNCH((mx_quant_kernel<false, true>), grid, st, xp, cp, sp, g);
+  if (flat && !floor_rule) FP4_LAUNCH((mx_quant_kernel<true, false, kInt>), grid, st, xp, cp, sp, g);
+  if (flat && floor_rule) FP4_LAUNCH((mx_quant_kernel<true, true, kInt>), grid, st, xp, cp, sp, g);
+  if (!flat && !floor_rule) FP4_LAUNCH((mx_quant_kernel<false, false, kInt>), grid, st, xp, cp, sp, g);
+  if (!flat && floor_rule) FP4_LAUNCH((mx_quant_kernel<false, true, kInt>), grid, st, xp, cp, sp, g);
+}
+
+void launch_mx_quant(const Shape& s, bool floor_rule, bool mxint, const void* x, void* codes,
+                     void* scales, hipStream_t st) {
+  if (mxint) mx_quant_variants<true>(s, floor_rule, x, codes, scales, st);
+  else mx_quant_variants<false>(s, floor_rule, x, codes, scales, st);
 }
 
 void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float* ts,
@@ -428,7 +449,7 @@ void launch_nv_quant(const Shape& s, bool razer, const void* x, void* codes, voi
 
 void launch_dequant(const Shape& s, int format, bool razer, const void* codes, const void* scales,
                     const float* ts, void* out, hipStream_t st) {
-  const int block = format == 0 ? 32 : 16;
+  const int block = format == 1 ? 16 : 32;
   Geom g = make_geom(s, block);
   // here ld_x is the output row stride
   const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / block;
@@ -437,8 +458,11 @@ void launch_dequant(const Shape& s, int format, bool razer, const void* codes, c
   auto sp = static_cast<const uint8_t*>(scales);
   auto op = static_cast<uint16_t*>(out);
   if (format == 0) {
-    if (flat) FP4_LAUNCH((mx_dequant_kernel<true>), grid, st, cp, sp, op, g);
-    else FP4_LAUNCH((mx_dequant_kernel<false>), grid, st, cp, sp, op, g);
+    if (flat) FP4_LAUNCH((mx_dequant_kernel<true, false>), grid, st, cp, sp, op, g);
+    else FP4_LAUNCH((mx_dequant_kernel<false, false>), grid, st, cp, sp, op, g);
+  } else if (format == 2) {
+    if (flat) FP4_LAUNCH((mx_dequant_kernel<true, true>), grid, st, cp, sp, op, g);
+    else FP4_LAUNCH((mx_dequant_kernel<false, true>), grid, st, cp, sp, op, g);
   } else {
     if (flat && razer) FP4_LAUNCH((nv_dequant_kernel<true, true>), grid, st, cp, sp, ts, op, g);
     if (flat && !razer) FP4_LAUNCH((nv_dequant_kernel<true, false>), grid, st, cp, sp, ts, op, g);

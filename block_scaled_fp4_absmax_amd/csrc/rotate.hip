@@ -1,4 +1,5 @@
-// rotate.hip -- two-level rotation fused with MXFP4 quantize + pack.
+// rotate.hip -- two-level rotation fused with FP4 quantize + pack (MXFP4,
+// MXINT4 and NVFP4).
 //
 // "TORQ: Two-Level Orthogonal Rotation for MXFP4 Quantization", technical
 // summary sec. 2(a): an inter-block orthogonal transform that evens out the
@@ -50,7 +51,8 @@ constexpr bool kUseMfma = FP4_HADAMARD_MFMA != 0;
 #endif
 constexpr int kTiles = FP4_TILES;
 
-template <bool kFlat, bool kHad, bool kFloor, bool kRot>
+// kInt: MXINT4 elements instead of E2M1.
+template <bool kFlat, bool kHad, bool kFloor, bool kRot, bool kInt>
 __global__ __launch_bounds__(kThreads) void mx_rotq_stream_mfma_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ rot, RotGeom g) {
@@ -92,7 +94,10 @@ __global__ __launch_bounds__(kThreads) void mx_rotq_stream_mfma_kernel(
       widen8(hi[u], y + 8);
     }
     uint32_t w0, w1, byte;
-    mx_quant16_pair<kFloor, kHad>(y, w0, w1, byte);
+    if constexpr (kInt)
+      mxint_quant16_pair<kFloor, kHad>(y, w0, w1, byte);
+    else
+      mx_quant16_pair<kFloor, kHad>(y, w0, w1, byte);
     if (ok[u]) {
       uint32_t* cp = reinterpret_cast<uint32_t*>(codes + co[u]);
       __builtin_nontemporal_store(w0, cp);
@@ -288,7 +293,7 @@ struct PermRows {
       gather_tile<G, kBuf * kBufBytes>(c.sbuf, c.off[i], lo, hi);
       float y[16];
       if (kHad) {
-        hadamard_mfma<kFmt == kFmtMx ? 32 : 16>(c.a0, c.a1, lo, hi, y);
+        hadamard_mfma<kFmt == kFmtMx || kFmt == kFmtMxInt ? 32 : 16>(c.a0, c.a1, lo, hi, y);
       } else {
         widen8(lo, y);
         widen8(hi, y + 8);
@@ -297,8 +302,11 @@ struct PermRows {
         if (ok) *c.amax = __builtin_fmaxf(*c.amax, absmax16f(y));
       } else {
         uint32_t w0, w1, byte, so;
-        if constexpr (kFmt == kFmtMx) {  // kOpt: OCP floor rule
-          mx_quant16_pair<kOpt, kHad>(y, w0, w1, byte);
+        if constexpr (kFmt == kFmtMx || kFmt == kFmtMxInt) {  // kOpt: OCP floor rule
+          if constexpr (kFmt == kFmtMx)
+            mx_quant16_pair<kOpt, kHad>(y, w0, w1, byte);
+          else
+            mxint_quant16_pair<kOpt, kHad>(y, w0, w1, byte);
           so = ok && h == 0 ? (uint32_t)b : kOob;
         } else {  // kOpt: RaZeR; lane h holds block 2 b + h
           nv_quant16<kOpt>(y, c.ns, c.rcp_tab, w0, w1, byte);
@@ -375,7 +383,8 @@ constexpr int perm_waves_cap() {
 #define FP4_PERM_AHEAD perm_ahead<kTpw>()
 #endif
 
-// kFmt: kFmtMx (kOpt = OCP floor rule), kFmtNv (kOpt = RaZeR; ts holds s_t),
+// kFmt: kFmtMx or kFmtMxInt (kOpt = OCP floor rule), kFmtNv (kOpt = RaZeR; ts
+// holds s_t),
 // kFmtNvAmax (no stores; work-group i leaves its largest rotated magnitude in
 // the code slot of chunk i).
 template <int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot>
@@ -407,7 +416,7 @@ __global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void rotq_perm_kernel(
   uint32_t off[kTpw][8];
   const int lr = pack_lane_perm<kTpw>(v, g, off);
   bf16x8_t a0, a1;
-  hadamard_operands<kFmt == kFmtMx ? 32 : 16>(a0, a1);
+  hadamard_operands<kFmt == kFmtMx || kFmt == kFmtMxInt ? 32 : 16>(a0, a1);
   put_row<kCpl>(sbuf, cpr, first);
   // run length agreed by the whole work-group (this also publishes row r0 and
   // the reciprocal table)
@@ -544,22 +553,24 @@ static int perm_dispatch(const Shape& s, const int32_t* perm, const uint16_t* x,
   return perm_launch<4, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
 }
 
-template <bool kHad, bool kFloor, bool kRot>
+template <bool kHad, bool kFloor, bool kRot, bool kInt>
 static void rotq_dispatch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
                           uint8_t* sc, float* rot, const RotGeom& g, bool flat, hipStream_t st) {
   if (perm) {
-    (void)perm_dispatch<kFmtMx, kHad, kFloor, kRot>(s, perm, x, c, sc, nullptr, rot, g, st);
+    (void)perm_dispatch<kInt ? kFmtMxInt : kFmtMx, kHad, kFloor, kRot>(s, perm, x, c, sc, nullptr,
+                                                                      rot, g, st);
     return;
   }
-  if constexpr (kUseMfma) {
+  // the butterfly variant quantizes MXFP4 only
+  if constexpr (kUseMfma || kInt) {
     const uint64_t tiles = ((uint64_t)g.nblk + 31) / 32;
     const uint64_t grid = (tiles + kWaves * kTiles - 1) / (kWaves * kTiles);
     if (flat)
-      hipLaunchKernelGGL((mx_rotq_stream_mfma_kernel<true, kHad, kFloor, kRot>), dim3((int)grid),
-                         dim3(kThreads), 0, st, x, c, sc, rot, g);
+      hipLaunchKernelGGL((mx_rotq_stream_mfma_kernel<true, kHad, kFloor, kRot, kInt>),
+                         dim3((int)grid), dim3(kThreads), 0, st, x, c, sc, rot, g);
     else
-      hipLaunchKernelGGL((mx_rotq_stream_mfma_kernel<false, kHad, kFloor, kRot>), dim3((int)grid),
-                         dim3(kThreads), 0, st, x, c, sc, rot, g);
+      hipLaunchKernelGGL((mx_rotq_stream_mfma_kernel<false, kHad, kFloor, kRot, kInt>),
+                         dim3((int)grid), dim3(kThreads), 0, st, x, c, sc, rot, g);
   } else {
     const uint64_t chunks = (uint64_t)g.nblk * 4;
     const uint64_t grid = (chunks + kThreads * 4 - 1) / (kThreads * 4);
@@ -572,24 +583,32 @@ static void rotq_dispatch(const Shape& s, const int32_t* perm, const uint16_t* x
   }
 }
 
+template <bool kInt>
+static void mx_rotq_variants(const Shape& s, const int32_t* perm, bool had, bool floor_rule,
+                             const uint16_t* xp, uint8_t* cp, uint8_t* sp, float* rot,
+                             const RotGeom& g, bool flat, hipStream_t st) {
+  const bool r = rot != nullptr;
+  if (had && !floor_rule && !r) rotq_dispatch<true, false, false, kInt>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (had && !floor_rule && r) rotq_dispatch<true, false, true, kInt>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (had && floor_rule && !r) rotq_dispatch<true, true, false, kInt>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (had && floor_rule && r) rotq_dispatch<true, true, true, kInt>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (!had && !floor_rule && !r) rotq_dispatch<false, false, false, kInt>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (!had && !floor_rule && r) rotq_dispatch<false, false, true, kInt>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (!had && floor_rule && !r) rotq_dispatch<false, true, false, kInt>(s, perm, xp, cp, sp, rot, g, flat, st);
+  if (!had && floor_rule && r) rotq_dispatch<false, true, true, kInt>(s, perm, xp, cp, sp, rot, g, flat, st);
+}
+
 void launch_mx_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, bool floor_rule,
-                            const void* x, void* codes, void* scales, float* rot, int64_t ld_rot,
-                            hipStream_t st) {
+                            bool mxint, const void* x, void* codes, void* scales, float* rot,
+                            int64_t ld_rot, hipStream_t st) {
   RotGeom g = rot_geom(s, ld_rot);
   auto xp = static_cast<const uint16_t*>(x);
   auto cp = static_cast<uint8_t*>(codes);
   auto sp = static_cast<uint8_t*>(scales);
-  const bool had = hadamard != 0, r = rot != nullptr;
   const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / 32 &&
-                    (!r || ld_rot == s.cols);
-  if (had && !floor_rule && !r) rotq_dispatch<true, false, false>(s, perm, xp, cp, sp, rot, g, flat, st);
-  if (had && !floor_rule && r) rotq_dispatch<true, false, true>(s, perm, xp, cp, sp, rot, g, flat, st);
-  if (had && floor_rule && !r) rotq_dispatch<true, true, false>(s, perm, xp, cp, sp, rot, g, flat, st);
-  if (had && floor_rule && r) rotq_dispatch<true, true, true>(s, perm, xp, cp, sp, rot, g, flat, st);
-  if (!had && !floor_rule && !r) rotq_dispatch<false, false, false>(s, perm, xp, cp, sp, rot, g, flat, st);
-  if (!had && !floor_rule && r) rotq_dispatch<false, false, true>(s, perm, xp, cp, sp, rot, g, flat, st);
-  if (!had && floor_rule && !r) rotq_dispatch<false, true, false>(s, perm, xp, cp, sp, rot, g, flat, st);
-  if (!had && floor_rule && r) rotq_dispatch<false, true, true>(s, perm, xp, cp, sp, rot, g, flat, st);
+                    (!rot || ld_rot == s.cols);
+  if (mxint) mx_rotq_variants<true>(s, perm, hadamard != 0, floor_rule, xp, cp, sp, rot, g, flat, st);
+  else mx_rotq_variants<false>(s, perm, hadamard != 0, floor_rule, xp, cp, sp, rot, g, flat, st);
 }
 
 template <bool kHad, bool kRazer, bool kRot, bool kAmax>

@@ -18,13 +18,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void widen8(u32x4_t d, float* v) {
-  v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
-  v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
-  v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z);
-  v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
-}
-
 __device__ __forceinline__ void store_rot8(float* rot, const float* y) {
   f32x4_t a = {y[0], y[1], y[2], y[3]};
   f32x4_t b = {y[4], y[5], y[6], y[7]};
@@ -124,6 +117,17 @@ __device__ __forceinline__ void mx_quant16_pair(const float* y, uint32_t& w0, ui
     w0 = cvt8_f32(y, s);
     w1 = cvt8_f32(y + 8, s);
   }
+}
+
+// MXINT4 of the lane's 16 outputs (block across lanes l and l ^ 32).
+template <bool kFloor, bool kMixed>
+__device__ __forceinline__ void mxint_quant16_pair(const float* y, uint32_t& w0, uint32_t& w1,
+                                                   uint32_t& byte) {
+  const uint32_t m = max_xor32(kMixed ? absmax16_mixed(y) : absmax_bits<16>(y));
+  byte = mxint_byte<kFloor>(m);
+  const int sh = 129 - (int)byte;
+  w0 = byte == 0xFFu ? 0u : int4x8_f32(y, sh);
+  w1 = byte == 0xFFu ? 0u : int4x8_f32(y + 8, sh);
 }
 
 // Largest magnitude of 16 fp32 values (a NaN operand may be dropped).
@@ -229,10 +233,10 @@ struct RotGeom {
   int64_t ld_x, ld_c, ld_s, ld_rot;
 };
 
-// Formats of the rotation kernels: MXFP4 (32-point transform), NVFP4
-// (16-point), and the NVFP4 pre-pass that only finds the largest rotated
-// magnitude (for a computed tensor scale).
-enum RotFmt : int { kFmtMx = 0, kFmtNv = 1, kFmtNvAmax = 2 };
+// Formats of the rotation kernels (the C ABI's format numbers): MXFP4 and
+// MXINT4 (32-point transform), NVFP4 (16-point), and the NVFP4 pre-pass that
+// only finds the largest rotated magnitude (for a computed tensor scale).
+enum RotFmt : int { kFmtMx = 0, kFmtNv = 1, kFmtMxInt = 2, kFmtNvAmax = 3 };
 
 inline RotGeom rot_geom(const Shape& s, int64_t ld_rot, int block = 32) {
   RotGeom g;

@@ -1,5 +1,6 @@
-// unrotate.hip -- MXFP4 dequantization with the inverse of the two-level
-// rotation, and the channel-energy statistic that calibrates the permutation.
+// unrotate.hip -- dequantization (MXFP4, MXINT4, NVFP4) with the inverse of
+// the two-level rotation, and the channel-energy statistic that calibrates
+// the permutation.
 //
 // "TORQ: Two-Level Orthogonal Rotation for MXFP4 Quantization", technical
 // summary sec. 2: the rotation is orthogonal, so decoding in the original
@@ -65,17 +66,23 @@ __device__ __forceinline__ void load_codes(const UnrotRsrc& q, const RotGeom& g,
   }
 }
 
-// bf16 outputs of one tile: decode, Hadamard (kHad), scale, round.
-template <bool kHad>
+// bf16 outputs of one MXFP4 (kInt: MXINT4) tile: decode (exact), Hadamard
+// (kHad), scale, round.
+template <bool kHad, bool kInt>
 __device__ __forceinline__ void unrotate_tile(u32x2_t c, uint32_t sbyte, const bf16x8_t& a0,
                                               const bf16x8_t& a1, u32x4_t& lo, u32x4_t& hi) {
-  const float s = e8m0_operand(sbyte & 0xFFu);
+  if constexpr (kInt) {
+    lo = int4x8_decode(c.x, sbyte & 0xFFu);
+    hi = int4x8_decode(c.y, sbyte & 0xFFu);
+  } else {
+    const float s = e8m0_operand(sbyte & 0xFFu);
 #define FP4_CVT2(w, k) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, k))
-  const uint32_t d[8] = {FP4_CVT2(c.x, 0), FP4_CVT2(c.x, 1), FP4_CVT2(c.x, 2), FP4_CVT2(c.x, 3),
-                         FP4_CVT2(c.y, 0), FP4_CVT2(c.y, 1), FP4_CVT2(c.y, 2), FP4_CVT2(c.y, 3)};
+    const uint32_t d[8] = {FP4_CVT2(c.x, 0), FP4_CVT2(c.x, 1), FP4_CVT2(c.x, 2), FP4_CVT2(c.x, 3),
+                           FP4_CVT2(c.y, 0), FP4_CVT2(c.y, 1), FP4_CVT2(c.y, 2), FP4_CVT2(c.y, 3)};
 #undef FP4_CVT2
-  lo = u32x4_t{d[0], d[1], d[2], d[3]};
-  hi = u32x4_t{d[4], d[5], d[6], d[7]};
+    lo = u32x4_t{d[0], d[1], d[2], d[3]};
+    hi = u32x4_t{d[4], d[5], d[6], d[7]};
+  }
   if (kHad) {
     float y[16];
     hadamard_mfma<32>(a0, a1, lo, hi, y);
@@ -173,10 +180,11 @@ struct UnrotCtx {
 // scatters into LDS buffer k % 2, waits at a barrier and writes the row out.
 // The loop runs whole groups of U = lcm(2, kAhead + 1) steps so every buffer
 // choice is a compile-time constant; a tail takes the last steps.
-// kNv: NVFP4 (kRazer: RaZeR codes) with the 16-point transform; else MXFP4
-// with the 32-point one.
-template <int G, int kTpw, int kAhead, bool kNv, bool kRazer, bool kHad, bool kPerm>
+// kFmt: the C ABI's format number; NVFP4 (kRazer: RaZeR codes) with the
+// 16-point transform, MXFP4 or MXINT4 with the 32-point one.
+template <int G, int kTpw, int kAhead, int kFmt, bool kRazer, bool kHad, bool kPerm>
 struct UnrotRows {
+  static constexpr bool kNv = kFmt == 1;
   using Ctx = UnrotCtx<kTpw, kAhead>;
   static constexpr int kCpl = 2 * kTpw;
   static constexpr uint32_t kBufBytes = 8192u * kTpw;
@@ -196,7 +204,7 @@ struct UnrotRows {
       if constexpr (kNv)
         nv_unrotate_tile<kHad, kRazer>(rc.c[i], rc.s[i], c.s_t, c.a0, c.a1, lo[i], hi[i]);
       else
-        unrotate_tile<kHad>(rc.c[i], rc.s[i], c.a0, c.a1, lo[i], hi[i]);
+        unrotate_tile<kHad, kFmt == 2>(rc.c[i], rc.s[i], c.a0, c.a1, lo[i], hi[i]);
     }
     load_codes<kTpw, kNv>(unrot_rsrc(c.codes, c.scales, c.out, r + kRing * G_, g), g, rc);
     const UnrotRsrc q = unrot_rsrc(c.codes, c.scales, c.out, r, g);
@@ -260,14 +268,15 @@ constexpr int unrot_wgs_per_cu() {
 #define FP4_UNROT_AHEAD 3
 #endif
 
-// kNv: NVFP4 blocks of 16 (scales 2 b + h, tensor scale *ts), the 16-point
-// transform; else MXFP4 blocks of 32 with the 32-point one.
-template <int kTpw, bool kNv, bool kRazer, bool kHad, bool kPerm>
+// kFmt 1 (NVFP4): blocks of 16 (scales 2 b + h, tensor scale *ts), the
+// 16-point transform; 0 (MXFP4) and 2 (MXINT4): blocks of 32, the 32-point one.
+template <int kTpw, int kFmt, bool kRazer, bool kHad, bool kPerm>
 __global__ __launch_bounds__(kThreads, 2) void dequant_unrotate_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ ts, const int32_t* __restrict__ perm, uint16_t* __restrict__ out,
     RotGeom g) {
   constexpr int kAhead = FP4_UNROT_AHEAD;
+  constexpr bool kNv = kFmt == 1;
   __shared__ __attribute__((aligned(16))) uint8_t sbuf[kPerm ? 2 * 8192 * kTpw : 16];
   i32x4_t v[kTpw][4];
   if (kPerm) load_lane_perm<kTpw>(perm, g, v);
@@ -289,15 +298,15 @@ __global__ __launch_bounds__(kThreads, 2) void dequant_unrotate_kernel(
                     : __syncthreads_and(lr >= 4) ? 4
                     : __syncthreads_and(lr >= 2) ? 2 : 1;
     if (run == 8)
-      UnrotRows<8, kTpw, kAhead, kNv, kRazer, kHad, true>::run(c);
+      UnrotRows<8, kTpw, kAhead, kFmt, kRazer, kHad, true>::run(c);
     else if (run == 4)
-      UnrotRows<4, kTpw, kAhead, kNv, kRazer, kHad, true>::run(c);
+      UnrotRows<4, kTpw, kAhead, kFmt, kRazer, kHad, true>::run(c);
     else if (run == 2)
-      UnrotRows<2, kTpw, kAhead, kNv, kRazer, kHad, true>::run(c);
+      UnrotRows<2, kTpw, kAhead, kFmt, kRazer, kHad, true>::run(c);
     else
-      UnrotRows<1, kTpw, kAhead, kNv, kRazer, kHad, true>::run(c);
+      UnrotRows<1, kTpw, kAhead, kFmt, kRazer, kHad, true>::run(c);
   } else {
-    UnrotRows<8, kTpw, kAhead, kNv, kRazer, kHad, false>::run(c);
+    UnrotRows<8, kTpw, kAhead, kFmt, kRazer, kHad, false>::run(c);
   }
 }
 
@@ -331,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void channel_energy_kernel(const uint16_t
 }
 
 // ================================ launchers =================================
-template <int kTpw, bool kNv, bool kRazer, bool kHad, bool kPerm>
+template <int kTpw, int kFmt, bool kRazer, bool kHad, bool kPerm>
 static void unrot_launch(const Shape& s, const int32_t* perm, const uint8_t* c, const uint8_t* sc,
                          const float* ts, uint16_t* o, const RotGeom& g, hipStream_t st) {
   // as for the forward kernel: pad LDS so that exactly kWgs work-groups fit per CU
@@ -346,35 +355,38 @@ static void unrot_launch(const Shape& s, const int32_t* perm, const uint8_t* c, 
   constexpr size_t kStatic = kPerm ? 2 * 8192 * kTpw : 16;
   const size_t share = (size_t)di.lds / kWgs;
   const size_t pad = share > kStatic + 1024 ? share - kStatic - 1024 : 0;
-  hipLaunchKernelGGL((dequant_unrotate_kernel<kTpw, kNv, kRazer, kHad, kPerm>), dim3(grid),
+  hipLaunchKernelGGL((dequant_unrotate_kernel<kTpw, kFmt, kRazer, kHad, kPerm>), dim3(grid),
                      dim3(kThreads), pad, st, c, sc, ts, perm, o, g);
 }
 
-template <bool kNv, bool kRazer, bool kHad, bool kPerm>
+template <int kFmt, bool kRazer, bool kHad, bool kPerm>
 static void unrot_dispatch(const Shape& s, const int32_t* perm, const uint8_t* c,
                            const uint8_t* sc, const float* ts, uint16_t* o, const RotGeom& g,
                            hipStream_t st) {
   const int64_t tpw = (s.cols + 32 * 32 * kWaves - 1) / (32 * 32 * kWaves);
-  if (tpw <= 1) unrot_launch<1, kNv, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
-  else if (tpw <= 2) unrot_launch<2, kNv, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
-  else if (tpw <= 3) unrot_launch<3, kNv, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
-  else unrot_launch<4, kNv, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
+  if (tpw <= 1) unrot_launch<1, kFmt, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
+  else if (tpw <= 2) unrot_launch<2, kFmt, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
+  else if (tpw <= 3) unrot_launch<3, kFmt, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
+  else unrot_launch<4, kFmt, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
 }
 
-template <bool kNv, bool kRazer>
+template <int kFmt, bool kRazer>
 static void unrot_variants(const Shape& s, const int32_t* perm, bool hadamard, const uint8_t* c,
                            const uint8_t* sc, const float* ts, uint16_t* o, const RotGeom& g,
                            hipStream_t st) {
-  if (hadamard && perm) unrot_dispatch<kNv, kRazer, true, true>(s, perm, c, sc, ts, o, g, st);
-  if (hadamard && !perm) unrot_dispatch<kNv, kRazer, true, false>(s, perm, c, sc, ts, o, g, st);
-  if (!hadamard && perm) unrot_dispatch<kNv, kRazer, false, true>(s, perm, c, sc, ts, o, g, st);
+  if (hadamard && perm) unrot_dispatch<kFmt, kRazer, true, true>(s, perm, c, sc, ts, o, g, st);
+  if (hadamard && !perm) unrot_dispatch<kFmt, kRazer, true, false>(s, perm, c, sc, ts, o, g, st);
+  if (!hadamard && perm) unrot_dispatch<kFmt, kRazer, false, true>(s, perm, c, sc, ts, o, g, st);
 }
 
-void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard,
+void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard, bool mxint,
                                 const void* codes, const void* scales, void* out, hipStream_t st) {
-  unrot_variants<false, false>(s, perm, hadamard != 0, static_cast<const uint8_t*>(codes),
-                               static_cast<const uint8_t*>(scales), nullptr,
-                               static_cast<uint16_t*>(out), rot_geom(s, 0), st);
+  auto c = static_cast<const uint8_t*>(codes);
+  auto sc = static_cast<const uint8_t*>(scales);
+  auto o = static_cast<uint16_t*>(out);
+  const RotGeom g = rot_geom(s, 0);
+  if (mxint) unrot_variants<2, false>(s, perm, hadamard != 0, c, sc, nullptr, o, g, st);
+  else unrot_variants<0, false>(s, perm, hadamard != 0, c, sc, nullptr, o, g, st);
 }
 
 void launch_nv_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard, bool razer,
@@ -384,8 +396,8 @@ void launch_nv_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamar
   auto c = static_cast<const uint8_t*>(codes);
   auto sc = static_cast<const uint8_t*>(scales);
   auto o = static_cast<uint16_t*>(out);
-  if (razer) unrot_variants<true, true>(s, perm, hadamard != 0, c, sc, ts, o, g, st);
-  else unrot_variants<true, false>(s, perm, hadamard != 0, c, sc, ts, o, g, st);
+  if (razer) unrot_variants<1, true>(s, perm, hadamard != 0, c, sc, ts, o, g, st);
+  else unrot_variants<1, false>(s, perm, hadamard != 0, c, sc, ts, o, g, st);
 }
 
 void launch_channel_energy(int64_t rows, int64_t cols, int64_t ld_x, const void* x, float* energy,

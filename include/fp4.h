@@ -1,5 +1,5 @@
 /*
- * fp4.h -- block-scaled 4-bit (MXFP4 / NVFP4) quantization on AMD Instinct
+ * fp4.h -- block-scaled 4-bit (MXFP4 / NVFP4 / MXINT4) quantization on AMD Instinct
  * MI355X (gfx950): C ABI of libfp4.so.
  *
  * Sources (web pages explaining the papers; cited by title and section):
@@ -13,16 +13,20 @@
  *          technical summary sec. 1 (32-element blocks sharing one exponent)
  *          and sec. 2 (an inter-block transform that evens out block variances,
  *          then a rotation inside each block; the scale maps the block maximum
- *          onto the largest code).
+ *          onto the largest code) and the generalisation remark of its results
+ *          (the rotation with NVFP4 and with an MXINT4 grid).
  *
  * Conventions shared by every entry point
  *  - Matrices are row-major. A block is `block` consecutive elements of one
- *    row (32 for MXFP4, 16 for NVFP4). `ld_*` is the row stride in elements
+ *    row (32 for MXFP4 and MXINT4, 16 for NVFP4). `ld_*` is the row stride in elements
  *    of that array (bytes for the uint8 code and scale arrays).
  *  - codes: uint8 [rows, ld_codes], element 2i of a row in the low nibble of
  *    byte i and element 2i+1 in the high nibble. FP4 E2M1 code =
  *    sign << 3 | magnitude index, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}.
- *  - scales: uint8 [rows, ld_scales], one byte per block. MXFP4: E8M0 byte,
+ *    MXINT4 code: a two's complement nibble k in [-8, 7], value k / 4 (the
+ *    4-bit microscaling integer element: two fraction bits; reading, the
+ *    pages name the format only).
+ *  - scales: uint8 [rows, ld_scales], one byte per block. MXFP4, MXINT4: E8M0 byte,
  *    scale 2^(byte-127), 0xFF = NaN. NVFP4: E4M3 (OCP "fn") byte; in RaZeR
  *    mode bit 7 holds the selector (0: code 0x8 means +5, 1: -5) and bits 0-6
  *    the positive scale.
@@ -52,13 +56,15 @@ extern "C" {
 
 #define FP4_VERSION 1
 
-enum fp4_format { FP4_MXFP4 = 0, FP4_NVFP4 = 1 };
+enum fp4_format { FP4_MXFP4 = 0, FP4_NVFP4 = 1, FP4_MXINT4 = 2 };
 enum fp4_mode { FP4_PLAIN = 0, FP4_RAZER = 1 };
 
 /* NVFP4: read tensor_scale as an input instead of computing it. */
 #define FP4_FLAG_TENSOR_SCALE_GIVEN 1u
 /* MXFP4: shared exponent floor(log2 amax) - 2 (elements above 6 * 2^e
- * saturate) instead of the default smallest e with amax <= 6 * 2^e. */
+ * saturate) instead of the default smallest e with amax <= 6 * 2^e.
+ * MXINT4: floor(log2 amax) (elements above 1.75 * 2^e saturate) instead of the
+ * default smallest e with amax <= 1.75 * 2^e. */
 #define FP4_FLAG_SCALE_OCP_FLOOR 2u
 
 enum fp4_status {
@@ -85,6 +91,12 @@ const char* fp4_status_string(int status);
  * or floor(log2 amax) - 2 with FP4_FLAG_SCALE_OCP_FLOOR. Elements are
  * x * 2^-e exactly. A block holding Inf or NaN gets scale byte 0xFF and codes 0.
  *
+ * MXINT4 ([TORQ] results, generalisation remark; the format as read in the
+ * header conventions): block 32, E8M0 exponent the smallest e in [-127, 127]
+ * with amax <= 1.75 * 2^e (capped at 127), or floor(log2 amax) with
+ * FP4_FLAG_SCALE_OCP_FLOOR; k = the integer nearest 4 x 2^-e, ties to even,
+ * clamped to [-7, 7] (-8 is never produced). Non-finite blocks as for MXFP4.
+ *
  * NVFP4 ([RaZeR] sec. 1): block 16. Each step is one fp32 operation rounded to
  * nearest-even: s_t = amax_tensor / 2688 (2688 = 6 * 448; 1.0 if the tensor is
  * all zero) unless FP4_FLAG_TENSOR_SCALE_GIVEN; s_b = E4M3 nearest to
@@ -99,15 +111,15 @@ const char* fp4_status_string(int status);
  *
  *  x_bf16       device, bf16 [rows, ld_x]; 16-byte aligned, ld_x % 8 == 0
  *  rows, cols   rows >= 0, cols >= 0, cols % block == 0; rows * cols / 8 < 2^31
- *  format       FP4_MXFP4 or FP4_NVFP4
- *  block        32 for MXFP4, 16 for NVFP4
+ *  format       FP4_MXFP4, FP4_NVFP4 or FP4_MXINT4
+ *  block        32 for MXFP4 and MXINT4, 16 for NVFP4
  *  mode         FP4_PLAIN, or FP4_RAZER with NVFP4
  *  flags        FP4_FLAG_* bits valid for the format
  *  codes        device, uint8 [rows, ld_codes]; 4-byte aligned, ld_codes % 4 == 0,
  *               ld_codes >= cols / 2
  *  scales       device, uint8 [rows, ld_scales], ld_scales >= cols / block
  *  tensor_scale NVFP4: device fp32[1], written (or read with the flag);
- *               MXFP4: ignored, may be NULL
+ *               MXFP4, MXINT4: ignored, may be NULL
  *  stream       hipStream_t
  * Returns FP4_OK or an fp4_status. With NVFP4 and a computed s_t, three
  * kernels are enqueued (tensor amax, s_t, quantize) and the codes array also
@@ -121,8 +133,8 @@ int fp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, i
 /*
  * fp4_dequantize -- decode codes and scales back to bf16.
  *
- * MXFP4: bf16(value * 2^e) (exact unless it overflows to Inf; scale 0xFF
- * gives NaN). NVFP4: bf16_rne(fp32(value * s_eff)); RaZeR mode decodes code
+ * MXFP4, MXINT4: bf16(value * 2^e) (exact unless it overflows to Inf; scale
+ * 0xFF gives NaN). NVFP4: bf16_rne(fp32(value * s_eff)); RaZeR mode decodes code
  * 0x8 to the block's special value, the decoder rebuilding it from the scale
  * byte's top bit ([RaZeR] sec. 2.3).
  * Optional inverse rotation so the result lies in the original basis: with
@@ -136,7 +148,7 @@ int fp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, i
  *  rows, cols, format, block, mode  as for fp4_quantize
  *  perm         NULL or device int32[cols], a permutation of 0..cols-1;
  *               requires cols <= 16384
- *  hadamard     0, or the block size (32 for MXFP4, 16 for NVFP4); with a
+ *  hadamard     0, or the block size (32 MXFP4/MXINT4, 16 NVFP4); with a
  *               rotation (perm or hadamard) cols % 32 == 0
  *  out_bf16     device, bf16 [rows, ld_out]; 16-byte aligned, ld_out % 8 == 0
  */
@@ -153,9 +165,10 @@ int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int6
  * e.g. by fp4_build_permutation from fp4_channel_energy, so that every block
  * receives a balanced share of channel energy). Level 2: the orthonormal
  * Sylvester-Hadamard matrix H[i][j] = (-1)^popcount(i & j) / sqrt(n) inside
- * each n-block (n = block: 32 for MXFP4, 16 for NVFP4), y = H x' in fp32.
+ * each n-block (n = block: 32 for MXFP4 and MXINT4, 16 for NVFP4), y = H x'
+ * in fp32.
  * Then quantization of y exactly as in fp4_quantize, with every amax taken
- * over the fp32 y: MXFP4's shared exponent; NVFP4's block scales, RaZeR
+ * over the fp32 y: the MX formats' shared exponent; NVFP4's block scales, RaZeR
  * choice and (unless FP4_FLAG_TENSOR_SCALE_GIVEN) s_t = amax(y) / 2688. With
  * a computed s_t three kernels are enqueued (rotation + amax partials held in
  * the code array, s_t, rotation + quantize); otherwise one.
@@ -165,8 +178,9 @@ int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int6
  *               cols <= 16384. A permutation made of aligned runs of 2, 4 or
  *               8 consecutive channels (fp4_build_permutation with group > 1)
  *               is detected and gathered with 4-, 8- or 16-byte LDS reads
- *  hadamard     the block size (32 MXFP4, 16 NVFP4) or 0 (none)
- *  format       FP4_MXFP4, or FP4_NVFP4 with mode FP4_PLAIN or FP4_RAZER
+ *  hadamard     the block size (32 MXFP4/MXINT4, 16 NVFP4) or 0 (none)
+ *  format       FP4_MXFP4, FP4_MXINT4, or FP4_NVFP4 with mode FP4_PLAIN or
+ *               FP4_RAZER
  *  cols         cols % 32 == 0
  *  rotated_out  NULL, or device fp32 [rows, ld_rot] receiving y; 16-byte
  *               aligned, ld_rot % 4 == 0 (for parity checks)

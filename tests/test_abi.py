@@ -51,7 +51,10 @@ TS = FAKE + 0x100
 
 
 @pytest.mark.parametrize("args,want", [
-    ((FAKE, 4, 64, 64, 2, 32, 0, 0, FAKE, 32, FAKE, 2, None), -4),      # bad format
+    ((FAKE, 4, 64, 64, 3, 32, 0, 0, FAKE, 32, FAKE, 2, None), -4),      # bad format
+    ((FAKE, 4, 64, 64, 2, 16, 0, 0, FAKE, 32, FAKE, 4, None), -4),      # MXINT4 block is 32
+    ((FAKE, 4, 64, 64, 2, 32, 1, 0, FAKE, 32, FAKE, 2, None), -4),      # RaZeR on MXINT4
+    ((FAKE, 4, 64, 64, 2, 32, 0, 1, FAKE, 32, FAKE, 2, None), -4),      # given s_t on MXINT4
     ((FAKE, 4, 64, 64, 0, 16, 0, 0, FAKE, 32, FAKE, 4, None), -4),      # MXFP4 needs block 32
     ((FAKE, 4, 64, 64, 1, 32, 0, 0, FAKE, 32, FAKE, 2, TS), -4),        # NVFP4 needs block 16
     ((FAKE, 4, 64, 64, 0, 32, 1, 0, FAKE, 32, FAKE, 2, None), -4),      # RaZeR needs NVFP4

@@ -84,10 +84,10 @@ def test_mx_exhaustive_bf16_patterns(orc, floor_rule):
     assert np.array_equal(np_u8(c), oc)
 
 
-@pytest.mark.parametrize("fmt,razer", [(0, False), (1, False), (1, True)])
+@pytest.mark.parametrize("fmt,razer", [(0, False), (1, False), (1, True), (2, False)])
 def test_dequant_every_code_and_scale(orc, fmt, razer):
     note(f"case: dequantize every code x scale byte fmt={fmt} razer={razer}")
-    blk = 32 if fmt == 0 else 16
+    blk = 16 if fmt == 1 else 32
     rows, cols = 256, 512
     codes = np.tile(np.arange(256, dtype=np.uint8), (rows, 1))
     scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], cols // blk, axis=1)
@@ -167,12 +167,12 @@ def test_nv_edge_cases(orc):
 
 
 # ------------------------------------------------------ layouts and shapes ---
-@pytest.mark.parametrize("fmt,razer", [(0, False), (1, False), (1, True)])
+@pytest.mark.parametrize("fmt,razer", [(0, False), (1, False), (1, True), (2, False)])
 @pytest.mark.parametrize("rows,cols", [(1, 32), (7, 96), (33, 160), (129, 4128)])
 def test_strided_ragged(orc, fmt, razer, rows, cols):
     """Row strides larger than the row, odd row counts, rows that are not a
     multiple of the work-group footprint."""
-    blk = 32 if fmt == 0 else 16
+    blk = 16 if fmt == 1 else 32
     if cols % blk:
         pytest.skip("cols not a multiple of the block")
     note(f"case: strided fmt={fmt} razer={razer} {rows}x{cols}")
@@ -190,6 +190,9 @@ def test_strided_ragged(orc, fmt, razer, rows, cols):
     if fmt == 0:
         oc, os_ = orc.mx_quantize(x)
         od = orc.dequantize(oc, os_, 0)
+    elif fmt == 2:
+        oc, os_ = orc.mxint4_quantize(x)
+        od = orc.dequantize(oc, os_, 2)
     else:
         oc, os_, ots = orc.nv_quantize(x, razer)
         assert float(ts.cpu()[0]) == ots
