@@ -46,7 +46,8 @@ B_NV = 2 + 0.5 + 1 / 16   # NVFP4 quantize (without the tensor-amax read)
 MFMA_PEAK_BF16_TFLOPS = 2500.0
 ROT_KERNEL = "rotq_perm_kernel"  # fused permutation + Hadamard + FP4 quantize
 ROT_INSTANCE = ROT_KERNEL + "<2, 0, true, false, false>"  # the MXFP4 instance timed at 16384x8192
-ROT_SOURCES = ["block_scaled_fp4_absmax_amd/csrc/rotate.hip",
+ROT_SOURCES = ["block_scaled_fp4_absmax_amd/csrc/rotate_kernels.hpp",
+               "block_scaled_fp4_absmax_amd/csrc/rotate_mx.hip",
                "block_scaled_fp4_absmax_amd/csrc/rotation.hpp",
                "block_scaled_fp4_absmax_amd/csrc/fp4_device.hpp",
                "block_scaled_fp4_absmax_amd/csrc/launch.hpp"]
@@ -295,7 +296,43 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
         c, sc, _, ts = fp4.rotate_quantize(xs[0], pm, had, fmt=fp4.NVFP4, mode=fp4.RAZER)
         xh = fp4.dequantize(c, sc, fp4.NVFP4, fp4.RAZER, ts, perm=pm, hadamard=had)
         out[f"c4_sqnr_db_nvfp4_razer_{name}"] = round(sqnr_db(torch, xf, xh.float()), 3)
-    del s16, xf
+    del s16
+
+    # MXINT4 (two's complement k/4 elements, E8M0 scale) on the same tensor
+    ms = timed(torch, lambda i: fp4.quantize(xs[i % n], fp4.MXINT4, codes=codes[i % n],
+                                             scales=scales[i % n]), 20, 3)
+    out["c4_mxint4_plain_quantize"] = gbs(ms, el, B_MX)
+    ms = timed(torch, lambda i: fp4.rotate_quantize(xs[i % n], perm, 32, codes=codes[i % n],
+                                                    scales=scales[i % n], fmt=fp4.MXINT4), 20, 3)
+    out["c4_mxint4_perm_h32_quantize"] = gbs(ms, el, B_MX)
+    ms = timed(torch, lambda i: fp4.dequantize(codes[i % n], scales[i % n], fp4.MXINT4, perm=perm,
+                                               hadamard=32, out=outb), 20, 3)
+    out["c4_mxint4_dequantize_unrotate"] = gbs(ms, el, B_MX)
+    for name, (pm, had) in {"perm_h32": (perm, 32), "h32": (None, 32),
+                            "plain": (None, 0)}.items():
+        c, sc, _ = fp4.rotate_quantize(xs[0], pm, had, fmt=fp4.MXINT4)
+        xh = fp4.dequantize(c, sc, fp4.MXINT4, perm=pm, hadamard=had)
+        out[f"c4_sqnr_db_mxint4_{name}"] = round(sqnr_db(torch, xf, xh.float()), 3)
+    del xf
+
+    # the heavy-tailed 8192 x 8192 activations: the Hadamard alone, every format
+    log("[bench] generating c3 for the rotation rows")
+    x3 = dev_copies(torch, inputs.gen_c3(), 1)[0]
+    r3, k3 = x3.shape
+    ms = timed(torch, lambda i: fp4.rotate_quantize(x3, None, 32), 20, 3)
+    out["c3_mxfp4_h32_quantize"] = gbs(ms, r3 * k3, B_MX)
+    x3f = x3.float()
+    q3 = {}
+    for fmt, mode, had, name in ((fp4.MXFP4, fp4.PLAIN, 32, "mxfp4"),
+                                 (fp4.MXINT4, fp4.PLAIN, 32, "mxint4"),
+                                 (fp4.NVFP4, fp4.RAZER, 16, "nvfp4_razer")):
+        for h in (0, had):
+            r = fp4.rotate_quantize(x3, None, h, fmt=fmt, mode=mode)
+            ts = r[3] if fmt == fp4.NVFP4 else None
+            xh = fp4.dequantize(r[0], r[1], fmt, mode, ts, hadamard=h)
+            q3[f"{name}_{'h%d' % h if h else 'plain'}"] = round(sqnr_db(torch, x3f, xh.float()), 3)
+    out["c3_sqnr_db"] = q3
+    del x3, x3f
 
     # NVFP4 + RaZeR on the 4096x4096 weight recipe, enough copies to defeat the cache
     log("[bench] generating c2 for the NVFP4 rows")

@@ -1,5 +1,6 @@
-// rotate.hip -- two-level rotation fused with FP4 quantize + pack (MXFP4,
-// MXINT4 and NVFP4).
+// rotate_kernels.hpp -- two-level rotation fused with FP4 quantize + pack
+// (MXFP4, MXINT4 and NVFP4): the kernels and their launch templates, compiled
+// per format in rotate_mx.hip, rotate_int.hip and rotate_nv.hip.
 //
 // "TORQ: Two-Level Orthogonal Rotation for MXFP4 Quantization", technical
 // summary sec. 2(a): an inter-block orthogonal transform that evens out the
@@ -22,15 +23,19 @@
 // A second implementation of the streaming (no permutation) kernel,
 // compile-time FP4_HADAMARD_MFMA=0, runs the transform as a radix-2 butterfly
 // in registers and DPP lane exchanges; it is kept for measuring one against
-// the other. (The inverse rotation, unrotate.hip, uses the butterfly.)
+// the other. (The inverse rotation runs on the MFMA as well.)
 //
 // The permutation x'[j] = x[perm[j]] is applied by staging whole rows in LDS.
 // A work-group alternates between two LDS row buffers: while its lanes gather
 // the permuted elements of one row from one buffer (LDS reads of 2 bytes, or
 // 4, 8, 16 when perm moves aligned runs of channels), the next row, fetched
 // with coalesced 16-byte loads, is written to the other.
+#ifndef FP4_ROTATE_KERNELS_HPP
+#define FP4_ROTATE_KERNELS_HPP
+
 #include <utility>
 
+#include "launch.hpp"
 #include "rotation.hpp"
 
 #ifndef FP4_HADAMARD_MFMA
@@ -598,72 +603,11 @@ static void mx_rotq_variants(const Shape& s, const int32_t* perm, bool had, bool
   if (!had && floor_rule && r) rotq_dispatch<false, true, true, kInt>(s, perm, xp, cp, sp, rot, g, flat, st);
 }
 
-void launch_mx_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, bool floor_rule,
-                            bool mxint, const void* x, void* codes, void* scales, float* rot,
-                            int64_t ld_rot, hipStream_t st) {
-  RotGeom g = rot_geom(s, ld_rot);
-  auto xp = static_cast<const uint16_t*>(x);
-  auto cp = static_cast<uint8_t*>(codes);
-  auto sp = static_cast<uint8_t*>(scales);
-  const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / 32 &&
-                    (!rot || ld_rot == s.cols);
-  if (mxint) mx_rotq_variants<true>(s, perm, hadamard != 0, floor_rule, xp, cp, sp, rot, g, flat, st);
-  else mx_rotq_variants<false>(s, perm, hadamard != 0, floor_rule, xp, cp, sp, rot, g, flat, st);
-}
-
-template <bool kHad, bool kRazer, bool kRot, bool kAmax>
-static int nv_stream_launch(const uint16_t* x, uint8_t* c, uint8_t* sc, const float* ts,
-                            float* rot, const RotGeom& g, bool flat, hipStream_t st) {
-  const uint64_t tiles = ((uint64_t)g.nblk + 31) / 32;
-  const int grid = (int)((tiles + kWaves * kTiles - 1) / (kWaves * kTiles));
-  if (flat)
-    hipLaunchKernelGGL((nv_rotq_stream_kernel<true, kHad, kRazer, kRot, kAmax>), dim3(grid),
-                       dim3(kThreads), 0, st, x, c, sc, ts, rot, g);
-  else
-    hipLaunchKernelGGL((nv_rotq_stream_kernel<false, kHad, kRazer, kRot, kAmax>), dim3(grid),
-                       dim3(kThreads), 0, st, x, c, sc, ts, rot, g);
-  return grid;
-}
-
-template <bool kHad, bool kRazer, bool kRot>
-static void nv_rotq(const Shape& s, const int32_t* perm, bool scale_given, const uint16_t* x,
-                    uint8_t* c, uint8_t* sc, float* ts, float* rot, const RotGeom& g, bool flat,
-                    hipStream_t st) {
-  if (!scale_given) {  // s_t from the largest rotated magnitude
-    const int nparts = perm ? perm_dispatch<kFmtNvAmax, kHad, false, false>(s, perm, x, c, sc,
-                                                                             nullptr, nullptr, g, st)
-                            : nv_stream_launch<kHad, false, false, true>(x, c, sc, nullptr,
-                                                                        nullptr, g, flat, st);
-    launch_nv_scale_from_partials(s, c, (uint32_t)nparts, ts, st);
-  }
-  if (perm)
-    (void)perm_dispatch<kFmtNv, kHad, kRazer, kRot>(s, perm, x, c, sc, ts, rot, g, st);
-  else
-    (void)nv_stream_launch<kHad, kRazer, kRot, false>(x, c, sc, ts, rot, g, flat, st);
-}
-
-void launch_nv_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, bool razer,
-                            bool scale_given, const void* x, void* codes, void* scales,
-                            float* ts, float* rot, int64_t ld_rot, hipStream_t st) {
-  if (s.rows == 0 || s.cols == 0) {  // nothing to quantize; a computed s_t is 1
-    if (!scale_given) launch_nv_scale_from_partials(s, codes, 0, ts, st);
-    return;
-  }
-  RotGeom g = rot_geom(s, ld_rot, 16);
-  auto xp = static_cast<const uint16_t*>(x);
-  auto cp = static_cast<uint8_t*>(codes);
-  auto sp = static_cast<uint8_t*>(scales);
-  const bool had = hadamard != 0, r = rot != nullptr;
-  const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / 16 &&
-                    (!r || ld_rot == s.cols);
-  if (had && razer && r) nv_rotq<true, true, true>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
-  if (had && razer && !r) nv_rotq<true, true, false>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
-  if (had && !razer && r) nv_rotq<true, false, true>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
-  if (had && !razer && !r) nv_rotq<true, false, false>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
-  if (!had && razer && r) nv_rotq<false, true, true>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
-  if (!had && razer && !r) nv_rotq<false, true, false>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
-  if (!had && !razer && r) nv_rotq<false, false, true>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
-  if (!had && !razer && !r) nv_rotq<false, false, false>(s, perm, scale_given, xp, cp, sp, ts, rot, g, flat, st);
-}
+// MXINT4 instances of the above, compiled in rotate_int.hip.
+void mxint_rotate_quant(const Shape& s, const int32_t* perm, bool had, bool floor_rule,
+                        const uint16_t* x, uint8_t* codes, uint8_t* scales, float* rot,
+                        const RotGeom& g, bool flat, hipStream_t st);
 
 }  // namespace fp4
+
+#endif  // FP4_ROTATE_KERNELS_HPP
