@@ -28,6 +28,9 @@ than itself (the pins live in ``tests/test_oracle_*.py``):
   scale pinned exhaustively by minimality over every bf16 magnitude; whole
   tensors by the nearest-grid property, the half-step error bound, scale
   invariance and sign symmetry.
+* ``gemm_f64``: pinned to an exact rational evaluation (Fraction) of the
+  block-scaled dot products on small operands, one-hot operands and the
+  bilinearity of the block scales.
 * ``razer_block``: pinned by exact Fraction SSE arg-min and exhaustive tiny-block
   enumeration.
 * ``rotate`` / ``unrotate_f64``: pinned to ``scipy.linalg.hadamard`` (orders 16
@@ -356,6 +359,20 @@ def rotate_quantize_mxint4(x_bf16: np.ndarray, perm: Optional[np.ndarray], hadam
     y = rotate(x_bf16, perm, hadamard)
     codes, scales = mxint4_quantize_f32(y, floor_rule)
     return codes, scales, y
+
+
+def gemm_f64(a_codes: np.ndarray, a_scales: np.ndarray, b_codes: np.ndarray,
+             b_scales: np.ndarray, fmt: int = 0, razer: bool = False, ts_a: float = 1.0,
+             ts_b: float = 1.0) -> np.ndarray:
+    """C = A B^T of two quantized operands, A [m, k] and B [n, k]: each decoded
+    exactly (dequantize_f64), then a float64 library matmul (the RaZeR page,
+    technical summary sec. 2.3: the GEMM consumes the quantized weights and
+    activations)."""
+    a = dequantize_f64(np.ascontiguousarray(a_codes), np.ascontiguousarray(a_scales), fmt, razer,
+                       ts_a)
+    b = dequantize_f64(np.ascontiguousarray(b_codes), np.ascontiguousarray(b_scales), fmt, razer,
+                       ts_b)
+    return a @ b.T
 
 
 def unrotate_f64(y: np.ndarray, perm: Optional[np.ndarray], hadamard: int) -> np.ndarray:
