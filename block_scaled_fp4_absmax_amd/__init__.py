@@ -16,13 +16,14 @@ from typing import Optional, Tuple
 __all__ = [
     "MXFP4", "NVFP4", "MXINT4", "PLAIN", "RAZER", "FLAG_TENSOR_SCALE_GIVEN", "FLAG_SCALE_OCP_FLOOR",
     "Fp4Error", "lib", "library_path", "quantize", "dequantize", "rotate_quantize",
-    "channel_energy", "build_permutation", "block_of",
+    "channel_energy", "build_permutation", "block_of", "gemm", "OUT_F32", "OUT_BF16",
 ]
 
 MXFP4, NVFP4, MXINT4 = 0, 1, 2
 PLAIN, RAZER = 0, 1
 FLAG_TENSOR_SCALE_GIVEN = 1
 FLAG_SCALE_OCP_FLOOR = 2
+OUT_F32, OUT_BF16 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfp4.so")
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
         "fp4_rotate_quantize": (i32, [vp, i64, i64, i64, vp, i32, i32, i32, i32, u32, vp, i64, vp,
                                       i64, vp, vp, i64, vp]),
         "fp4_channel_energy": (i32, [vp, i64, i64, i64, vp, vp]),
+        "fp4_gemm": (i32, [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, i32, i32, vp, i64,
+                           vp]),
         "fp4_build_permutation": (i32, [vp, i64, i32, i32, vp]),
     }
     for name, (res, args) in sig.items():
@@ -186,6 +189,27 @@ def rotate_quantize(x, perm=None, hadamard: Optional[int] = None, floor_rule: bo
     if fmt == NVFP4:
         return codes, scales, rotated, ts
     return codes, scales, rotated
+
+
+def gemm(a_codes, a_scales, b_codes, b_scales, k: Optional[int] = None, fmt: int = MXFP4,
+         out_dtype=None, out=None, stream=None):
+    """C = A B^T for quantized A [m, k] and B [n, k] (codes and scales as the
+    quantizer returns them); fp32 [m, n] unless ``out_dtype`` is bfloat16."""
+    import torch
+    m, ha, lda = _rows_ld(a_codes)
+    n, hb, ldb = _rows_ld(b_codes)
+    if k is None:
+        k = 2 * ha
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_codes.device)
+    od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    st = lib().fp4_gemm(_ptr(a_codes), lda, _ptr(a_scales), a_scales.stride(0), _ptr(b_codes),
+                        ldb, _ptr(b_scales), b_scales.stride(0), m, n, k, fmt, od, _ptr(out),
+                        out.stride(0), _stream(stream))
+    _check("fp4_gemm", st)
+    return out
 
 
 def channel_energy(x, out=None, stream=None):

@@ -151,6 +151,30 @@ int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t 
   return launch_status();
 }
 
+int fp4_gemm(const void* a_codes, int64_t ld_a, const void* a_scales, int64_t ld_sa,
+             const void* b_codes, int64_t ld_b, const void* b_scales, int64_t ld_sb, int64_t m,
+             int64_t n, int64_t k, int format, int out_dtype, void* c, int64_t ld_c,
+             void* stream) {
+  if (format != FP4_MXFP4) return FP4_ERR_UNSUPPORTED;
+  if (out_dtype != FP4_OUT_F32 && out_dtype != FP4_OUT_BF16) return FP4_ERR_UNSUPPORTED;
+  if (m < 0 || n < 0 || k < 0 || k % 32 != 0) return FP4_ERR_SHAPE;
+  if (m >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31) || k >= ((int64_t)1 << 31))
+    return FP4_ERR_UNSUPPORTED;
+  if (ld_a < k / 2 || ld_b < k / 2 || ld_sa < k / 32 || ld_sb < k / 32 || ld_c < n)
+    return FP4_ERR_SHAPE;
+  const int64_t lim = ((int64_t)1 << 31) / 128;
+  if (ld_a >= lim || ld_b >= lim || ld_sa >= lim || ld_sb >= lim) return FP4_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return FP4_OK;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return FP4_ERR_NULL;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || ld_a % 16 != 0 || ld_b % 16 != 0)
+    return FP4_ERR_ALIGN;
+  if (!aligned(c, out_dtype == FP4_OUT_F32 ? 4 : 2)) return FP4_ERR_ALIGN;
+  (void)hipGetLastError();
+  fp4::launch_mx_gemm(m, n, k, a_codes, ld_a, a_scales, ld_sa, b_codes, ld_b, b_scales, ld_sb, c,
+                      ld_c, out_dtype == FP4_OUT_BF16, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 int fp4_channel_energy(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                        float* energy, void* stream) {
   if (rows < 0 || cols < 0 || cols % 32 != 0 || ld_x < cols) return FP4_ERR_SHAPE;

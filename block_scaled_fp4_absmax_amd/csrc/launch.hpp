@@ -59,6 +59,11 @@ void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamar
 void launch_nv_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard, bool razer,
                                 const void* codes, const void* scales, const float* ts, void* out,
                                 hipStream_t st);
+// C = A B^T, MXFP4 operands (codes [rows, K/2], E8M0 scales [rows, K/32]);
+// fp32 or bf16 output.
+void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a, const void* sa,
+                    int64_t ld_sa, const void* b, int64_t ld_b, const void* sb, int64_t ld_sb,
+                    void* c, int64_t ld_c, bool bf16_out, hipStream_t st);
 void launch_channel_energy(int64_t rows, int64_t cols, int64_t ld_x, const void* x, float* energy,
                            hipStream_t st);
 
