@@ -29,6 +29,26 @@ FLAGS = [
 ]
 
 
+# Sources whose MFMA accumulators may live in the accumulation registers: the
+# GEMM's 256 accumulators per lane do not fit the ordinary VGPRs.
+ACC_REGISTER_SOURCES = {"gemm.hip"}
+
+
+def _source_flags(src, flags):
+    if src not in ACC_REGISTER_SOURCES:
+        return flags
+    out, skip = [], False
+    for i, f in enumerate(flags):
+        if skip:
+            skip = False
+            continue
+        if f == "-mllvm" and i + 1 < len(flags) and flags[i + 1] == "-amdgpu-mfma-vgpr-form":
+            skip = True
+            continue
+        out.append(f)
+    return out
+
+
 def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(ln for ln in res.stderr.splitlines()
@@ -44,8 +64,8 @@ def build(extra_flags=(), out=LIB, verbose=False) -> str:
     common = [HIPCC, *FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include")]
     with tempfile.TemporaryDirectory(prefix="fp4build") as tmpdir:
         objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
-        cmds = [[c for c in common if c != "-shared"] + ["-c", "-o", o, os.path.join(CSRC, s)]
-                for s, o in zip(SOURCES, objs)]
+        cmds = [_source_flags(s, [c for c in common if c != "-shared"]) +
+                ["-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)]
         with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
             errs = list(ex.map(_run, cmds))
         tmp = out + ".tmp%d" % os.getpid()

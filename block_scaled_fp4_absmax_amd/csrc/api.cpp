@@ -168,6 +168,8 @@ int fp4_gemm(const void* a_codes, int64_t ld_a, const void* a_scales, int64_t ld
   if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return FP4_ERR_NULL;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || ld_a % 16 != 0 || ld_b % 16 != 0)
     return FP4_ERR_ALIGN;
+  if (!aligned(a_scales, 4) || !aligned(b_scales, 4) || ld_sa % 4 != 0 || ld_sb % 4 != 0)
+    return FP4_ERR_ALIGN;
   if (!aligned(c, out_dtype == FP4_OUT_F32 ? 4 : 2)) return FP4_ERR_ALIGN;
   (void)hipGetLastError();
   fp4::launch_mx_gemm(m, n, k, a_codes, ld_a, a_scales, ld_sa, b_codes, ld_b, b_scales, ld_sb, c,

@@ -19,13 +19,14 @@
 // layout and the exactness of the products were confirmed on the GPU with an
 // in-bounds probe.
 //
-// Tiling: a work-group of four waves computes a 128 x 128 tile of C; wave
-// (wm, wn) owns the 64 x 64 quarter (wm, wn) as 2 x 2 MFMA tiles. K advances
-// 128 elements per stage: the work-group copies the stage's 128 rows x 64
-// code bytes of A and of B, and their 4 scale bytes per row, into one of two
-// LDS buffers (rows padded to 80 bytes so the 16-byte lane reads of 32
-// consecutive rows spread over all banks), while the waves multiply out of
-// the other. Loads past M, N or K read zeros through buffer-resource range
+// Tiling: a work-group of four waves computes a (64 WM) x (64 WN) tile of C
+// (256 x 256 for large products, 128 x 128 otherwise); wave (wm, wn) owns
+// the quarter (wm, wn) as WM x WN MFMA tiles. K advances 128 elements per
+// stage: the work-group copies the stage's rows of 64 code bytes of A and of
+// B, and their 4 scale bytes per row, into one of two LDS buffers (rows
+// padded to 80 bytes so the 16-byte lane reads of 32 consecutive rows spread
+// over all banks), while the waves multiply out of the other; the loads of
+// two stages are in flight at a time. Loads past M, N or K read zeros through buffer-resource range
 // checks (code 0 is +0), so any K that is a multiple of 32 works.
 #include "fp4_device.hpp"
 #include "launch.hpp"
@@ -37,11 +38,9 @@ namespace {
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 128;        // C tile of a work-group
-constexpr int kBK = 128;                   // K elements per stage
-constexpr int kRowBytes = kBK / 2;         // code bytes per row per stage
-constexpr int kLdsRow = kRowBytes + 16;    // padded LDS row
-constexpr int kTileBytes = kBM * kLdsRow;  // one operand, one stage
+constexpr int kBK = 128;                 // K elements per stage
+constexpr int kRowBytes = kBK / 2;       // code bytes per row per stage
+constexpr int kLdsRow = kRowBytes + 16;  // padded LDS row
 
 struct GemmArgs {
   const uint8_t* a;
@@ -53,68 +52,89 @@ struct GemmArgs {
   int32_t m, n, k;
 };
 
-// One operand's share of a stage, in flight in registers: two 16-byte code
-// chunks per lane, and (lanes 0..127 for A, 128..255 for B) one row's four
-// scale bytes.
-struct StageRegs {
-  u32x4_t a[2], b[2];
-  uint32_t s;
-};
-
 struct OperandRsrc {
   rsrc_t a, sa, b, sb;
 };
 
-__device__ __forceinline__ void load_stage(const OperandRsrc& q, const GemmArgs& g, int32_t k0,
-                                           StageRegs& r) {
-  const uint32_t t = threadIdx.x;
-  const uint32_t kb0 = (uint32_t)k0 / 2u, kbytes = (uint32_t)g.k / 2u;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t chunk = t + 256u * i, row = chunk >> 2, col = 16u * (chunk & 3u);
-    const bool in_k = kb0 + col < kbytes;
-    r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(
-        q.a, in_k ? row * (uint32_t)g.ld_a + kb0 + col : kOob, 0, 0);
-    r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(
-        q.b, in_k ? row * (uint32_t)g.ld_b + kb0 + col : kOob, 0, 0);
-  }
-  // scales: waves 0-1 read the rows of A, waves 2-3 those of B (lane t reads
-  // row t % 128); the choice is uniform per wave, so the resource stays scalar
-  const bool is_a = __builtin_amdgcn_readfirstlane(t >> 6) < 2u;
-  const rsrc_t rs = is_a ? q.sa : q.sb;
-  const uint32_t row = t & 127u, blk0 = (uint32_t)k0 / 32u, nblk = (uint32_t)g.k / 32u;
-  const uint32_t base = row * (uint32_t)(is_a ? g.ld_sa : g.ld_sb);
-  uint32_t s = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t off = blk0 + j < nblk ? base + blk0 + j : kOob;
-    s |= ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0) & 0xFFu) << (8 * j);
-  }
-  r.s = s;
-}
+// Work-group tile BM x BN = (64 WM) x (64 WN): four waves, wave (wm, wn) owns
+// WM x WN MFMA tiles of 32 x 32 at rows 32 WM wm.., columns 32 WN wn..
+template <int WM, int WN>
+struct Tile {
+  static constexpr int BM = 64 * WM, BN = 64 * WN;
+  static constexpr int kChunksA = BM * kRowBytes / 16 / 256;  // 16-byte chunks per lane
+  static constexpr int kChunksB = BN * kRowBytes / 16 / 256;
+  static constexpr int kScaleRows = (BM + BN) / 256;          // scale rows per lane
+  static constexpr int kLdsA = BM * kLdsRow, kLdsB = BN * kLdsRow;
 
-__device__ __forceinline__ void store_stage(uint8_t* lds_a, uint8_t* lds_b, uint32_t* lds_s,
-                                            const StageRegs& r) {
-  const uint32_t t = threadIdx.x;
+  // One stage in flight in registers: code chunks of A and B, and the four
+  // scale bytes of each scale row (one dword; scale rows are 4-byte aligned).
+  struct Regs {
+    u32x4_t a[kChunksA], b[kChunksB];
+    uint32_t s[kScaleRows];
+  };
+
+  static __device__ __forceinline__ void load(const OperandRsrc& q, const GemmArgs& g, int32_t k0,
+                                              Regs& r) {
+    const uint32_t t = threadIdx.x;
+    const uint32_t kb0 = (uint32_t)k0 / 2u, kbytes = (uint32_t)g.k / 2u;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t chunk = t + 256u * i, row = chunk >> 2, col = 16u * (chunk & 3u);
-    *reinterpret_cast<u32x4_t*>(lds_a + row * kLdsRow + col) = r.a[i];
-    *reinterpret_cast<u32x4_t*>(lds_b + row * kLdsRow + col) = r.b[i];
+    for (int i = 0; i < kChunksA; ++i) {
+      const uint32_t chunk = t + 256u * i, row = chunk >> 2, col = 16u * (chunk & 3u);
+      r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          q.a, kb0 + col < kbytes ? row * (uint32_t)g.ld_a + kb0 + col : kOob, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kChunksB; ++i) {
+      const uint32_t chunk = t + 256u * i, row = chunk >> 2, col = 16u * (chunk & 3u);
+      r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          q.b, kb0 + col < kbytes ? row * (uint32_t)g.ld_b + kb0 + col : kOob, 0, 0);
+    }
+    // scale row j of the stage: rows 0 .. BM-1 of A, then BM .. BM+BN-1 of B;
+    // lane t takes rows t + 256 i, whose operand is uniform across a wave
+    const uint32_t blk0 = (uint32_t)k0 / 32u, nblk = (uint32_t)g.k / 32u;
+#pragma unroll
+    for (int i = 0; i < kScaleRows; ++i) {
+      const uint32_t j = t + 256u * i;
+      const bool is_a = __builtin_amdgcn_readfirstlane(j >> 6) < (uint32_t)BM / 64u;
+      const rsrc_t rs = is_a ? q.sa : q.sb;
+      const uint32_t row = is_a ? j : j - BM;
+      const uint32_t base = row * (uint32_t)(is_a ? g.ld_sa : g.ld_sb);
+      // blk0 is a multiple of 4 below nblk <= ld_s (a multiple of 4), so the
+      // dword stays inside the row; bytes past K are cleared when stored
+      r.s[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, blk0 < nblk ? base + blk0 : kOob, 0, 0);
+    }
   }
-  lds_s[t] = r.s;  // A rows 0..127, then B rows 0..127
-}
 
-template <bool kBf16Out>
-__global__ __launch_bounds__(256, 2) void mx_gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kTileBytes];
-  __shared__ uint32_t lds_s[2][256];
+  static __device__ __forceinline__ void store(uint8_t* la, uint8_t* lb, uint32_t* ls,
+                                               const Regs& r, uint32_t smask) {
+    const uint32_t t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kChunksA; ++i) {
+      const uint32_t chunk = t + 256u * i, row = chunk >> 2, col = 16u * (chunk & 3u);
+      *reinterpret_cast<u32x4_t*>(la + row * kLdsRow + col) = r.a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kChunksB; ++i) {
+      const uint32_t chunk = t + 256u * i, row = chunk >> 2, col = 16u * (chunk & 3u);
+      *reinterpret_cast<u32x4_t*>(lb + row * kLdsRow + col) = r.b[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kScaleRows; ++i) ls[t + 256u * i] = r.s[i] & smask;
+  }
+};
 
-  const int32_t tiles_n = (g.n + kBN - 1) / kBN;
+template <int WM, int WN, bool kBf16Out>
+__global__ __launch_bounds__(256) void mx_gemm_kernel(GemmArgs g) {
+  using T = Tile<WM, WN>;
+  constexpr int BM = T::BM, BN = T::BN;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][T::kLdsA];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][T::kLdsB];
+  __shared__ uint32_t lds_s[2][BM + BN];
+
+  const int32_t tiles_n = (g.n + BN - 1) / BN;
   const int32_t bm = blockIdx.x / tiles_n, bn = blockIdx.x - bm * tiles_n;
-  const int32_t m0 = bm * kBM, n0 = bn * kBN;
-  const int32_t rows_a = min(kBM, g.m - m0), rows_b = min(kBN, g.n - n0);
+  const int32_t m0 = bm * BM, n0 = bn * BN;
+  const int32_t rows_a = min(BM, g.m - m0), rows_b = min(BN, g.n - n0);
   OperandRsrc q;
   q.a = make_rsrc(g.a + (int64_t)m0 * g.ld_a, (uint32_t)(rows_a * g.ld_a));
   q.b = make_rsrc(g.b + (int64_t)n0 * g.ld_b, (uint32_t)(rows_b * g.ld_b));
@@ -124,61 +144,90 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(GemmArgs g) {
   const uint32_t lane = threadIdx.x & 63u, r = lane & 31u, h = lane >> 5;
   const uint32_t w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1u;
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[WM][WN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int32_t stages = (g.k + kBK - 1) / kBK;
-  StageRegs st;
-  load_stage(q, g, 0, st);
-  store_stage(lds_a[0], lds_b[0], lds_s[0], st);
-  __syncthreads();
-
-  for (int32_t s = 0; s < stages; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < stages;
-    if (more) load_stage(q, g, (s + 1) * kBK, st);
+  // multiply out the stage held in LDS buffer buf: two 64-element K steps
+  auto mma = [&](int buf) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {  // two 64-element K steps per stage
-      i32x8_t fa[2], fb[2];
-      int32_t sa[2], sb[2];
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t koff = 32u * ks + 16u * h, sh = 8u * (2u * ks + h);
+      u32x4_t fa[WM], fb[WN];
+      int32_t sa[WM], sb[WN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint32_t ra = 64u * wm + 32u * i + r, rb = 64u * wn + 32u * i + r;
-        const u32x4_t va =
-            *reinterpret_cast<const u32x4_t*>(lds_a[buf] + ra * kLdsRow + 32u * ks + 16u * h);
-        const u32x4_t vb =
-            *reinterpret_cast<const u32x4_t*>(lds_b[buf] + rb * kLdsRow + 32u * ks + 16u * h);
-        fa[i] = i32x8_t{(int32_t)va.x, (int32_t)va.y, (int32_t)va.z, (int32_t)va.w, 0, 0, 0, 0};
-        fb[i] = i32x8_t{(int32_t)vb.x, (int32_t)vb.y, (int32_t)vb.z, (int32_t)vb.w, 0, 0, 0, 0};
-        sa[i] = (int32_t)((lds_s[buf][ra] >> (8u * (2u * ks + h))) & 0xFFu);
-        sb[i] = (int32_t)((lds_s[buf][128u + rb] >> (8u * (2u * ks + h))) & 0xFFu);
+      for (int i = 0; i < WM; ++i) {
+        const uint32_t ra = 32u * WM * wm + 32u * i + r;
+        fa[i] = *reinterpret_cast<const u32x4_t*>(lds_a[buf] + ra * kLdsRow + koff);
+        sa[i] = (int32_t)((lds_s[buf][ra] >> sh) & 0xFFu);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < WN; ++j) {
+        const uint32_t rb = 32u * WN * wn + 32u * j + r;
+        fb[j] = *reinterpret_cast<const u32x4_t*>(lds_b[buf] + rb * kLdsRow + koff);
+        sb[j] = (int32_t)((lds_s[buf][BM + rb] >> sh) & 0xFFu);
+      }
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[i], fb[j], acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const i32x8_t va{(int32_t)fa[i].x, (int32_t)fa[i].y, (int32_t)fa[i].z,
+                           (int32_t)fa[i].w, 0, 0, 0, 0};
+          const i32x8_t vb{(int32_t)fb[j].x, (int32_t)fb[j].y, (int32_t)fb[j].z,
+                           (int32_t)fb[j].w, 0, 0, 0, 0};
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc[i][j], 4, 4, 0,
+                                                                     sa[i], 0, sb[j]);
+        }
     }
-    if (more) store_stage(lds_a[buf ^ 1], lds_b[buf ^ 1], lds_s[buf ^ 1], st);
+  };
+
+  // Two stages in flight: while stage s is multiplied out of LDS buffer s % 2,
+  // register set s % 2 (whose stage is already in LDS) receives stage s + 2
+  // and register set (s + 1) % 2 holds stage s + 1, which is stored into the
+  // other LDS buffer afterwards. Loads are unconditional: past K they read
+  // zeros without touching memory, so every stage issues the same operations
+  // and each store waits for its own stage's loads only.
+  const int32_t stages = (g.k + kBK - 1) / kBK;
+  // scale bytes of a stage that lie past K (the last, partial stage) are
+  // cleared: their codes read as zero, and a stray 0xFF would make 0 * NaN
+  const uint32_t nblk = (uint32_t)g.k / 32u;
+  auto smask = [&](int32_t st) {
+    const uint32_t b0 = 4u * (uint32_t)st;
+    return b0 + 4u <= nblk ? 0xFFFFFFFFu : b0 >= nblk ? 0u : (1u << (8u * (nblk - b0))) - 1u;
+  };
+  typename T::Regs r0, r1;
+  T::load(q, g, 0, r0);
+  T::load(q, g, kBK, r1);
+  T::store(lds_a[0], lds_b[0], lds_s[0], r0, smask(0));
+  __syncthreads();
+  int32_t s = 0;
+  for (; s + 1 < stages; s += 2) {
+    T::load(q, g, (s + 2) * kBK, r0);
+    mma(0);
+    T::store(lds_a[1], lds_b[1], lds_s[1], r1, smask(s + 1));
+    __syncthreads();
+    T::load(q, g, (s + 3) * kBK, r1);
+    mma(1);
+    T::store(lds_a[0], lds_b[0], lds_s[0], r0, smask(s + 2));
     __syncthreads();
   }
+  if (s < stages) mma(0);  // an odd stage count ends in buffer 0
 
   // epilogue: lane (n, h) of tile (i, j) holds column n, rows 8 (e / 4) + 4 h + e % 4
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int32_t col = n0 + 64 * (int32_t)wn + 32 * j + (int32_t)r;
+    for (int j = 0; j < WN; ++j) {
+      const int32_t col = n0 + 32 * WN * (int32_t)wn + 32 * j + (int32_t)r;
       if (col >= g.n) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int32_t row = m0 + 64 * (int32_t)wm + 32 * i + 8 * (e / 4) + 4 * (int32_t)h + e % 4;
+        const int32_t row =
+            m0 + 32 * WM * (int32_t)wm + 32 * i + 8 * (e / 4) + 4 * (int32_t)h + e % 4;
         if (row >= g.m) continue;
         if constexpr (kBf16Out) {
           const uint32_t p = pack_bf16x2(acc[i][j][e], 0.0f);
@@ -190,6 +239,16 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(GemmArgs g) {
     }
 }
 
+template <int WM, int WN>
+void launch_tiles(const GemmArgs& g, bool bf16_out, hipStream_t st) {
+  const int64_t tiles = (((int64_t)g.m + 64 * WM - 1) / (64 * WM)) *
+                        (((int64_t)g.n + 64 * WN - 1) / (64 * WN));
+  if (bf16_out)
+    hipLaunchKernelGGL((mx_gemm_kernel<WM, WN, true>), dim3((unsigned)tiles), dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL((mx_gemm_kernel<WM, WN, false>), dim3((unsigned)tiles), dim3(256), 0, st, g);
+}
+
 }  // namespace
 
 void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a, const void* sa,
@@ -198,11 +257,17 @@ void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a
   GemmArgs g{static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(sa),
              static_cast<const uint8_t*>(b), static_cast<const uint8_t*>(sb), c,
              ld_a, ld_sa, ld_b, ld_sb, ld_c, (int32_t)m, (int32_t)n, (int32_t)k};
-  const int64_t tiles = ((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN);
-  if (bf16_out)
-    hipLaunchKernelGGL(mx_gemm_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, st, g);
+#ifdef FP4_GEMM_TILE
+  constexpr int kW = FP4_GEMM_TILE;
+  launch_tiles<kW, kW>(g, bf16_out, st);
+#else
+  // large products: 256 x 256 tiles (four 128 x 128 wave tiles) halve the
+  // operand traffic per flop; smaller ones keep 128 x 128 for more work-groups
+  if (m >= 2048 && n >= 2048)
+    launch_tiles<4, 4>(g, bf16_out, st);
   else
-    hipLaunchKernelGGL(mx_gemm_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, st, g);
+    launch_tiles<2, 2>(g, bf16_out, st);
+#endif
 }
 
 }  // namespace fp4

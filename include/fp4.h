@@ -208,7 +208,9 @@ int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t 
  *
  *  a_codes, b_codes     device, uint8; 16-byte aligned, ld % 16 == 0,
  *                       ld >= k / 2, 128 * ld < 2^31
- *  a_scales, b_scales   device, uint8; ld_s >= k / 32, 128 * ld_s < 2^31
+ *  a_scales, b_scales   device, uint8; 4-byte aligned, ld_s % 4 == 0,
+ *                       ld_s >= k / 32, 128 * ld_s < 2^31 (bytes of a row
+ *                       past k / 32 are never used)
  *  m, n, k              >= 0, < 2^31; k % 32 == 0 (m or n zero: no work;
  *                       k zero: C = 0)
  *  format               FP4_MXFP4 (others return FP4_ERR_UNSUPPORTED)

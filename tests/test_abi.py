@@ -104,6 +104,18 @@ def test_rotate_and_dequant_validation(L):
     assert D(FAKE, 32, FAKE, 4, None, 4, 64, 1, 16, 0, None, 0, FAKE, 64, None) == -1
     assert D(FAKE, 32, FAKE, 2, None, 4, 64, 0, 32, 0, None, 0, FAKE + 8, 64, None) == -3
     assert D(FAKE, 32, FAKE, 2, None, 0, 64, 0, 32, 0, None, 0, None, 64, None) == 0
+    # gemm(a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, m, n, k, fmt, out_dtype, c, ld_c, stream)
+    G = L.fp4_gemm
+    assert G(FAKE, 32, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 1, 0, FAKE, 8, None) == -4  # NVFP4
+    assert G(FAKE, 32, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 2, FAKE, 8, None) == -4  # dtype
+    assert G(FAKE, 32, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 48, 0, 0, FAKE, 8, None) == -2  # k % 32
+    assert G(FAKE, 16, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 0, FAKE, 8, None) == -2  # ld_a
+    assert G(FAKE, 32, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 0, FAKE, 4, None) == -2  # ld_c
+    assert G(FAKE, 40, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 0, FAKE, 8, None) == -3  # ld_a % 16
+    assert G(FAKE, 32, FAKE, 6, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 0, FAKE, 8, None) == -3  # ld_sa % 4
+    assert G(FAKE + 8, 32, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 0, FAKE, 8, None) == -3
+    assert G(None, 32, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 0, FAKE, 8, None) == -1
+    assert G(None, 32, None, 4, None, 32, None, 4, 0, 8, 64, 0, 0, None, 8, None) == 0  # m = 0
     E = L.fp4_channel_energy
     assert E(FAKE, 4, 48, 48, FAKE, None) == -2
     assert E(None, 4, 64, 64, FAKE, None) == -1
