@@ -23,11 +23,14 @@
 // (256 x 256 for large products, 128 x 128 otherwise); wave (wm, wn) owns
 // the quarter (wm, wn) as WM x WN MFMA tiles. K advances 128 elements per
 // stage: the work-group copies the stage's rows of 64 code bytes of A and of
-// B, and their 4 scale bytes per row, into one of two LDS buffers (rows
-// padded to 80 bytes so the 16-byte lane reads of 32 consecutive rows spread
-// over all banks), while the waves multiply out of the other; the loads of
-// two stages are in flight at a time. Loads past M, N or K read zeros through buffer-resource range
-// checks (code 0 is +0), so any K that is a multiple of 32 works.
+// B, and their 4 scale bytes per row, into one of two LDS buffers (16-byte
+// chunks swizzled within each row so that the lane writes and the MFMA
+// operand reads are free of bank conflicts), while the waves multiply out of
+// the other; the loads of three stages are in flight at a time. Loads past
+// M, N or K read zeros through buffer-resource range checks (code 0 is +0),
+// so any K that is a multiple of 32 works.
+#include <type_traits>
+
 #include "fp4_device.hpp"
 #include "launch.hpp"
 
@@ -40,7 +43,16 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 128;                 // K elements per stage
 constexpr int kRowBytes = kBK / 2;       // code bytes per row per stage
-constexpr int kLdsRow = kRowBytes + 16;  // padded LDS row
+constexpr int kLdsRow = kRowBytes;       // LDS row (16-byte chunks XOR-swizzled)
+
+// LDS byte offset of 16-byte chunk c (0..3) of row r: chunk c sits in slot
+// c ^ ((r / 2) % 4). A write pass of 8 lanes covers two rows (slots 0..3 of
+// each, 128 contiguous bytes); a read pass of 8 lanes takes one logical chunk
+// of 8 consecutive rows, which the swizzle spreads over all four slots of
+// both bank halves, so neither conflicts on 32 four-byte banks.
+__device__ __forceinline__ uint32_t lds_off(uint32_t r, uint32_t c) {
+  return r * kLdsRow + 16u * (c ^ ((r >> 1) & 3u));
+}
 
 struct GemmArgs {
   const uint8_t* a;
@@ -111,12 +123,12 @@ struct Tile {
 #pragma unroll
     for (int i = 0; i < kChunksA; ++i) {
       const uint32_t chunk = t + 256u * i, row = chunk >> 2, col = 16u * (chunk & 3u);
-      *reinterpret_cast<u32x4_t*>(la + row * kLdsRow + col) = r.a[i];
+      *reinterpret_cast<u32x4_t*>(la + lds_off(row, col / 16u)) = r.a[i];
     }
 #pragma unroll
     for (int i = 0; i < kChunksB; ++i) {
       const uint32_t chunk = t + 256u * i, row = chunk >> 2, col = 16u * (chunk & 3u);
-      *reinterpret_cast<u32x4_t*>(lb + row * kLdsRow + col) = r.b[i];
+      *reinterpret_cast<u32x4_t*>(lb + lds_off(row, col / 16u)) = r.b[i];
     }
 #pragma unroll
     for (int i = 0; i < kScaleRows; ++i) ls[t + 256u * i] = r.s[i] & smask;
@@ -156,19 +168,19 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmArgs g) {
   auto mma = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t koff = 32u * ks + 16u * h, sh = 8u * (2u * ks + h);
+      const uint32_t kc = 2u * ks + h, sh = 8u * kc;  // 16-byte chunk, scale byte
       u32x4_t fa[WM], fb[WN];
       int32_t sa[WM], sb[WN];
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
         const uint32_t ra = 32u * WM * wm + 32u * i + r;
-        fa[i] = *reinterpret_cast<const u32x4_t*>(lds_a[buf] + ra * kLdsRow + koff);
+        fa[i] = *reinterpret_cast<const u32x4_t*>(lds_a[buf] + lds_off(ra, kc));
         sa[i] = (int32_t)((lds_s[buf][ra] >> sh) & 0xFFu);
       }
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         const uint32_t rb = 32u * WN * wn + 32u * j + r;
-        fb[j] = *reinterpret_cast<const u32x4_t*>(lds_b[buf] + rb * kLdsRow + koff);
+        fb[j] = *reinterpret_cast<const u32x4_t*>(lds_b[buf] + lds_off(rb, kc));
         sb[j] = (int32_t)((lds_s[buf][BM + rb] >> sh) & 0xFFu);
       }
 #pragma unroll
@@ -185,12 +197,13 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmArgs g) {
     }
   };
 
-  // Two stages in flight: while stage s is multiplied out of LDS buffer s % 2,
-  // register set s % 2 (whose stage is already in LDS) receives stage s + 2
-  // and register set (s + 1) % 2 holds stage s + 1, which is stored into the
-  // other LDS buffer afterwards. Loads are unconditional: past K they read
-  // zeros without touching memory, so every stage issues the same operations
-  // and each store waits for its own stage's loads only.
+  // Three stages in flight: while stage s is multiplied out of LDS buffer
+  // s % 2, register set s % 3 (whose stage is already in LDS) receives stage
+  // s + 3, and register sets (s + 1) % 3, (s + 2) % 3 hold stages s + 1 and
+  // s + 2; stage s + 1 is stored into the other LDS buffer afterwards. Loads
+  // are unconditional: past K they read zeros without touching memory, so
+  // every stage issues the same operations and each store waits for its own
+  // stage's loads only.
   const int32_t stages = (g.k + kBK - 1) / kBK;
   // scale bytes of a stage that lie past K (the last, partial stage) are
   // cleared: their codes read as zero, and a stray 0xFF would make 0 * NaN
@@ -199,23 +212,29 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmArgs g) {
     const uint32_t b0 = 4u * (uint32_t)st;
     return b0 + 4u <= nblk ? 0xFFFFFFFFu : b0 >= nblk ? 0u : (1u << (8u * (nblk - b0))) - 1u;
   };
-  typename T::Regs r0, r1;
-  T::load(q, g, 0, r0);
-  T::load(q, g, kBK, r1);
-  T::store(lds_a[0], lds_b[0], lds_s[0], r0, smask(0));
+  typename T::Regs rs[3];
+  T::load(q, g, 0, rs[0]);
+  T::load(q, g, kBK, rs[1]);
+  T::load(q, g, 2 * kBK, rs[2]);
+  T::store(lds_a[0], lds_b[0], lds_s[0], rs[0], smask(0));
   __syncthreads();
+  // stage s with register set j = s % 3 (a compile-time index)
+  auto step = [&](auto J, int32_t s) {
+    constexpr int j = decltype(J)::value;
+    const int buf = s & 1;
+    T::load(q, g, (s + 3) * kBK, rs[j]);
+    mma(buf);
+    T::store(lds_a[buf ^ 1], lds_b[buf ^ 1], lds_s[buf ^ 1], rs[(j + 1) % 3], smask(s + 1));
+    __syncthreads();
+  };
   int32_t s = 0;
-  for (; s + 1 < stages; s += 2) {
-    T::load(q, g, (s + 2) * kBK, r0);
-    mma(0);
-    T::store(lds_a[1], lds_b[1], lds_s[1], r1, smask(s + 1));
-    __syncthreads();
-    T::load(q, g, (s + 3) * kBK, r1);
-    mma(1);
-    T::store(lds_a[0], lds_b[0], lds_s[0], r0, smask(s + 2));
-    __syncthreads();
+  for (; s + 2 < stages; s += 3) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+    step(std::integral_constant<int, 2>{}, s + 2);
   }
-  if (s < stages) mma(0);  // an odd stage count ends in buffer 0
+  if (s < stages) step(std::integral_constant<int, 0>{}, s);
+  if (s + 1 < stages) step(std::integral_constant<int, 1>{}, s + 1);
 
   // epilogue: lane (n, h) of tile (i, j) holds column n, rows 8 (e / 4) + 4 h + e % 4
 #pragma unroll
