@@ -333,6 +333,7 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
             q3[f"{name}_{'h%d' % h if h else 'plain'}"] = round(sqnr_db(torch, x3f, xh.float()), 3)
     out["c3_sqnr_db"] = q3
     del x3, x3f
+    out["gemm_mxfp4"] = gemm_rows(torch, fp4)
 
     # NVFP4 + RaZeR on the 4096x4096 weight recipe, enough copies to defeat the cache
     log("[bench] generating c2 for the NVFP4 rows")
@@ -367,6 +368,33 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     out["c2_sqnr_db_plain_nvfp4"] = round(sqnr_db(torch, ys[0].float(), xp.float()), 3)
     del ys, cs, ss
     return out
+
+
+MFMA_PEAK_FP4_TFLOPS = 10100.0
+
+
+def gemm_rows(torch, fp4):
+    """The consumer: C = A B^T on MXFP4 operands (activations [m, k], weights
+    [n, k] of the Llama-70B-shaped layer), bf16 out, on the scaled FP4 matrix
+    cores. Random codes and scale bytes: the time does not depend on values."""
+    log("[bench] MXFP4 GEMM rows")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    rows = {}
+    for m, n, k in ((4096, 8192, 8192), (4096, 28672, 8192), (4096, 8192, 28672),
+                    (16, 8192, 8192)):
+        a = torch.randint(0, 256, (m, k // 2), dtype=torch.uint8, device="cuda", generator=g)
+        sa = torch.randint(120, 131, (m, k // 32), dtype=torch.uint8, device="cuda", generator=g)
+        b = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device="cuda", generator=g)
+        sb = torch.randint(120, 131, (n, k // 32), dtype=torch.uint8, device="cuda", generator=g)
+        c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        ms = timed(torch, lambda i: fp4.gemm(a, sa, b, sb, out=c), 20, 3)
+        tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        by = (m + n) * (k / 2 + k / 32) + 2 * m * n
+        rows[f"{m}x{n}x{k}"] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
+                                "frac_fp4_mfma_peak": round(tf / MFMA_PEAK_FP4_TFLOPS, 4),
+                                "GBps": round(by / ms / 1e6, 1)}
+        del a, sa, b, sb, c
+    return rows
 
 
 def bench_c2(torch, fp4, inputs, args):
@@ -549,7 +577,7 @@ def trace_summary(trace_dir, bench_log):
            "", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
     fp4_total = 0.0
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        name = r["Name"].split("(")[0].replace("void ", "")
+        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         if not name.startswith("fp4::") and "copyBuffer" not in name:
             continue
         if name.startswith("fp4::"):
