@@ -361,17 +361,41 @@ def rotate_quantize_mxint4(x_bf16: np.ndarray, perm: Optional[np.ndarray], hadam
     return codes, scales, y
 
 
+def decode_exact(codes: np.ndarray, scales: np.ndarray, fmt: int, razer: bool = False,
+                 tensor_scale: float = 1.0) -> np.ndarray:
+    """float64 [rows, cols] of the exact element values (no rounding at all):
+    MXFP4 e2m1(code) 2^(e-127); NVFP4 e2m1(code) e4m3(scale) s_t, RaZeR code
+    0x8 reading +5 or -5 by the scale's top bit. Exact in float64: at most 3
+    significant bits times 4 times 24."""
+    codes = np.ascontiguousarray(codes)
+    rows, half = codes.shape
+    nib = np.empty((rows, 2 * half), np.int64)
+    nib[:, 0::2] = codes & 15
+    nib[:, 1::2] = codes >> 4
+    e2m1 = np.array([e2m1_value(c) for c in range(16)])
+    val = e2m1[nib]
+    if fmt == 0:
+        e = np.repeat(scales.astype(np.int64), 32, axis=1)[:, :2 * half] - 127
+        return np.ldexp(val, e)
+    assert fmt == 1
+    sb = np.repeat(scales.astype(np.int64), 16, axis=1)[:, :2 * half]
+    e4m3 = np.array([e4m3_value(b) for b in range(256)])
+    if razer:
+        special = np.where(sb & 0x80, -5.0, 5.0)
+        val = np.where(nib == 8, special, val)
+        sb = sb & 0x7F
+    return val * e4m3[sb] * float(tensor_scale)
+
+
 def gemm_f64(a_codes: np.ndarray, a_scales: np.ndarray, b_codes: np.ndarray,
              b_scales: np.ndarray, fmt: int = 0, razer: bool = False, ts_a: float = 1.0,
-             ts_b: float = 1.0) -> np.ndarray:
+             ts_b: float = 1.0, razer_b: Optional[bool] = None) -> np.ndarray:
     """C = A B^T of two quantized operands, A [m, k] and B [n, k]: each decoded
-    exactly (dequantize_f64), then a float64 library matmul (the RaZeR page,
+    exactly (decode_exact), then a float64 library matmul (the RaZeR page,
     technical summary sec. 2.3: the GEMM consumes the quantized weights and
-    activations)."""
-    a = dequantize_f64(np.ascontiguousarray(a_codes), np.ascontiguousarray(a_scales), fmt, razer,
-                       ts_a)
-    b = dequantize_f64(np.ascontiguousarray(b_codes), np.ascontiguousarray(b_scales), fmt, razer,
-                       ts_b)
+    activations). razer applies to A, and to B unless razer_b says otherwise."""
+    a = decode_exact(a_codes, a_scales, fmt, razer, ts_a)
+    b = decode_exact(b_codes, b_scales, fmt, razer if razer_b is None else razer_b, ts_b)
     return a @ b.T
 
 

@@ -83,3 +83,48 @@ def test_gemm_block_scale_bilinear(orc):
     b = orc.dequantize_f64(bc, bs, 0)
     part = a[:, 96:128] @ b[:, 96:128].T
     assert np.allclose(c2, c0 - 0.75 * part, rtol=0, atol=1e-9 * np.abs(c0).max())
+
+
+def _e4m3_exact(b):
+    """OCP E4M3 (fn): bias 7, subnormals m 2^-9, from the definition."""
+    e, m = (b >> 3) & 15, b & 7
+    if e == 0:
+        return Fraction(m, 512)
+    return (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+
+
+@pytest.mark.parametrize("razer_a,razer_b", [(False, False), (True, True), (True, False)])
+def test_nv_gemm_matches_exact_rational(orc, razer_a, razer_b):
+    """NVFP4 operands (E4M3 block scales, fp32 tensor scales, RaZeR code 0x8 =
+    +-5 by the scale's top bit) against exact rationals."""
+    rng = np.random.default_rng(21 + razer_a + 2 * razer_b)
+    m, n, k = 3, 4, 48
+    ac = rng.integers(0, 256, (m, k // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    as_ = rng.integers(0, 256 if razer_a else 127, (m, k // 16), dtype=np.uint8) & \
+        np.uint8(0xFF if razer_a else 0x7F)
+    bs = rng.integers(0, 256 if razer_b else 127, (n, k // 16), dtype=np.uint8) & \
+        np.uint8(0xFF if razer_b else 0x7F)
+    as_[as_ & 0x7F == 0x7F] -= 1  # no NaN scale
+    bs[bs & 0x7F == 0x7F] -= 1
+    ta, tb = float(np.float32(0.0123)), float(np.float32(3.75e-3))
+    c = orc.gemm_f64(ac, as_, bc, bs, 1, razer_a, ta, tb, razer_b=razer_b)
+
+    def val(codes, scales, r, j, rz, ts):
+        code = int(codes[r, j // 2]) >> (4 * (j % 2)) & 15
+        sbyte = int(scales[r, j // 16])
+        if rz and code == 8:
+            v = Fraction(-5 if sbyte & 0x80 else 5)
+        else:
+            v = _val(code)
+        return v * _e4m3_exact(sbyte & 0x7F if rz else sbyte) * Fraction(ts)
+
+    # the decoded values are exact in float64; their products need up to 62
+    # bits, so the float64 matmul rounds: k roundings of 2^-53 at most
+    for i in range(m):
+        for j in range(n):
+            terms = [val(ac, as_, i, t, razer_a, ta) * val(bc, bs, j, t, razer_b, tb)
+                     for t in range(k)]
+            want = sum(terms)
+            bound = k * Fraction(1, 2 ** 52) * sum(abs(x) for x in terms)
+            assert abs(Fraction(c[i, j]) - want) <= bound
