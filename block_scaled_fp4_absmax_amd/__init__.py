@@ -62,8 +62,8 @@ def lib() -> ctypes.CDLL:
         "fp4_rotate_quantize": (i32, [vp, i64, i64, i64, vp, i32, i32, i32, i32, u32, vp, i64, vp,
                                       i64, vp, vp, i64, vp]),
         "fp4_channel_energy": (i32, [vp, i64, i64, i64, vp, vp]),
-        "fp4_gemm": (i32, [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, i32, i32, vp, i64,
-                           vp]),
+        "fp4_gemm": (i32, [vp, i64, vp, i64, vp, i32, vp, i64, vp, i64, vp, i32, i64, i64, i64,
+                           i32, i32, vp, i64, vp]),
         "fp4_build_permutation": (i32, [vp, i64, i32, i32, vp]),
     }
     for name, (res, args) in sig.items():
@@ -192,9 +192,11 @@ def rotate_quantize(x, perm=None, hadamard: Optional[int] = None, floor_rule: bo
 
 
 def gemm(a_codes, a_scales, b_codes, b_scales, k: Optional[int] = None, fmt: int = MXFP4,
-         out_dtype=None, out=None, stream=None):
+         a_ts=None, b_ts=None, mode_a: int = PLAIN, mode_b: int = PLAIN, out_dtype=None,
+         out=None, stream=None):
     """C = A B^T for quantized A [m, k] and B [n, k] (codes and scales as the
-    quantizer returns them); fp32 [m, n] unless ``out_dtype`` is bfloat16."""
+    quantizer returns them; NVFP4 also takes the two tensor scales and a mode
+    per operand); fp32 [m, n] unless ``out_dtype`` is bfloat16."""
     import torch
     m, ha, lda = _rows_ld(a_codes)
     n, hb, ldb = _rows_ld(b_codes)
@@ -205,9 +207,10 @@ def gemm(a_codes, a_scales, b_codes, b_scales, k: Optional[int] = None, fmt: int
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a_codes.device)
     od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
-    st = lib().fp4_gemm(_ptr(a_codes), lda, _ptr(a_scales), a_scales.stride(0), _ptr(b_codes),
-                        ldb, _ptr(b_scales), b_scales.stride(0), m, n, k, fmt, od, _ptr(out),
-                        out.stride(0), _stream(stream))
+    st = lib().fp4_gemm(_ptr(a_codes), lda, _ptr(a_scales), a_scales.stride(0), _ptr(a_ts),
+                        mode_a, _ptr(b_codes), ldb, _ptr(b_scales), b_scales.stride(0),
+                        _ptr(b_ts), mode_b, m, n, k, fmt, od, _ptr(out), out.stride(0),
+                        _stream(stream))
     _check("fp4_gemm", st)
     return out
 

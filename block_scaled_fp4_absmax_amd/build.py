@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp4.so")
 SOURCES = ["quant.hip", "rotate_mx.hip", "rotate_int.hip", "rotate_nv.hip", "unrotate_mx.hip",
-           "unrotate_int.hip", "unrotate_nv.hip", "gemm.hip", "api.cpp", "perm.cpp", "device.cpp"]
+           "unrotate_int.hip", "unrotate_nv.hip", "gemm.hip", "gemm_nv.hip", "api.cpp", "perm.cpp", "device.cpp"]
 HEADERS = ["fp4_device.hpp", "launch.hpp", "rotation.hpp", "rotate_kernels.hpp",
            "unrotate_kernels.hpp"]
 
@@ -30,8 +30,8 @@ FLAGS = [
 
 
 # Sources whose MFMA accumulators may live in the accumulation registers: the
-# GEMM's 256 accumulators per lane do not fit the ordinary VGPRs.
-ACC_REGISTER_SOURCES = {"gemm.hip"}
+# GEMMs' 256 accumulators per lane do not fit the ordinary VGPRs.
+ACC_REGISTER_SOURCES = {"gemm.hip", "gemm_nv.hip"}
 
 
 def _source_flags(src, flags):

@@ -152,28 +152,44 @@ int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t 
 }
 
 int fp4_gemm(const void* a_codes, int64_t ld_a, const void* a_scales, int64_t ld_sa,
-             const void* b_codes, int64_t ld_b, const void* b_scales, int64_t ld_sb, int64_t m,
+             const float* a_ts, int mode_a, const void* b_codes, int64_t ld_b,
+             const void* b_scales, int64_t ld_sb, const float* b_ts, int mode_b, int64_t m,
              int64_t n, int64_t k, int format, int out_dtype, void* c, int64_t ld_c,
              void* stream) {
-  if (format != FP4_MXFP4) return FP4_ERR_UNSUPPORTED;
+  if (format != FP4_MXFP4 && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
   if (out_dtype != FP4_OUT_F32 && out_dtype != FP4_OUT_BF16) return FP4_ERR_UNSUPPORTED;
+  if (mode_a != FP4_PLAIN && mode_a != FP4_RAZER) return FP4_ERR_UNSUPPORTED;
+  if (mode_b != FP4_PLAIN && mode_b != FP4_RAZER) return FP4_ERR_UNSUPPORTED;
+  if (format == FP4_MXFP4 && (mode_a != FP4_PLAIN || mode_b != FP4_PLAIN))
+    return FP4_ERR_UNSUPPORTED;
+  const int blk = block_of(format);
   if (m < 0 || n < 0 || k < 0 || k % 32 != 0) return FP4_ERR_SHAPE;
   if (m >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31) || k >= ((int64_t)1 << 31))
     return FP4_ERR_UNSUPPORTED;
-  if (ld_a < k / 2 || ld_b < k / 2 || ld_sa < k / 32 || ld_sb < k / 32 || ld_c < n)
+  if (ld_a < k / 2 || ld_b < k / 2 || ld_sa < k / blk || ld_sb < k / blk || ld_c < n)
     return FP4_ERR_SHAPE;
-  const int64_t lim = ((int64_t)1 << 31) / 128;
+  const int64_t lim = ((int64_t)1 << 31) / 256;
   if (ld_a >= lim || ld_b >= lim || ld_sa >= lim || ld_sb >= lim) return FP4_ERR_UNSUPPORTED;
   if (m == 0 || n == 0) return FP4_OK;
   if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return FP4_ERR_NULL;
+  if (format == FP4_NVFP4 && (!a_ts || !b_ts)) return FP4_ERR_NULL;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || ld_a % 16 != 0 || ld_b % 16 != 0)
     return FP4_ERR_ALIGN;
-  if (!aligned(a_scales, 4) || !aligned(b_scales, 4) || ld_sa % 4 != 0 || ld_sb % 4 != 0)
+  // scale rows are read as dwords (MXFP4) or 16-bit pairs (NVFP4)
+  const int sal = format == FP4_MXFP4 ? 4 : 2;
+  if (!aligned(a_scales, sal) || !aligned(b_scales, sal) || ld_sa % sal != 0 || ld_sb % sal != 0)
     return FP4_ERR_ALIGN;
+  if (format == FP4_NVFP4 && (!aligned(a_ts, 4) || !aligned(b_ts, 4))) return FP4_ERR_ALIGN;
   if (!aligned(c, out_dtype == FP4_OUT_F32 ? 4 : 2)) return FP4_ERR_ALIGN;
   (void)hipGetLastError();
-  fp4::launch_mx_gemm(m, n, k, a_codes, ld_a, a_scales, ld_sa, b_codes, ld_b, b_scales, ld_sb, c,
-                      ld_c, out_dtype == FP4_OUT_BF16, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (format == FP4_MXFP4)
+    fp4::launch_mx_gemm(m, n, k, a_codes, ld_a, a_scales, ld_sa, b_codes, ld_b, b_scales, ld_sb,
+                        c, ld_c, out_dtype == FP4_OUT_BF16, st);
+  else
+    fp4::launch_nv_gemm(m, n, k, a_codes, ld_a, a_scales, ld_sa, a_ts, mode_a == FP4_RAZER,
+                        b_codes, ld_b, b_scales, ld_sb, b_ts, mode_b == FP4_RAZER, c, ld_c,
+                        out_dtype == FP4_OUT_BF16, st);
   return launch_status();
 }
 

@@ -1,0 +1,260 @@
+// gemm_nv.hip -- C = s_a s_b (A B^T) with NVFP4 operands, optionally RaZeR,
+// on the bf16 matrix cores.
+//
+// "RaZeR: Pushing the Limits of NVFP4 Quantization with Redundant Zero
+// Remapping", technical summary sec. 2.3: GEMM kernels that take the
+// quantized weights and activations, the special value rebuilt from the
+// scale's metadata bit. A is [M, K], B is [N, K], each as fp4_quantize writes
+// NVFP4: codes [rows, K/2], E4M3 scale bytes [rows, K/16] (RaZeR: selector in
+// bit 7) and an fp32 tensor scale s.
+//
+// gfx950's block-scaled FP4 matrix instructions take E8M0 scales per 32
+// elements; NVFP4's are E4M3 per 16, so they cannot be fed to it. Instead
+// each element is decoded exactly: an E2M1 value (or the block's +-5) has at
+// most 3 significant bits and an E4M3 scale 4, so value x scale has at most 7
+// and is a bf16, between 2^-10 and 2688. The work-group decodes each stage
+// once, on its way into LDS, and the waves run v_mfma_f32_32x32x16_bf16 on the
+// decoded tiles (products of bf16 are exact in fp32); the tensor scales
+// multiply once in the epilogue. RaZeR needs no second pass: code 0x8 simply
+// decodes to the block's special value.
+//
+// Tiling as in the MXFP4 GEMM: four waves, a (64 WM) x (64 WN) work-group
+// tile, WM x WN MFMA tiles of 32 x 32 per wave; K advances 64 elements per
+// stage (32 code bytes and 4 scale bytes of each row), decoded into one of two
+// LDS buffers of bf16 rows (128 bytes per row, 16-byte chunks XOR-swizzled by
+// row) while the waves multiply out of the other.
+#include <type_traits>
+
+#include "fp4_device.hpp"
+#include "launch.hpp"
+
+namespace fp4 {
+
+namespace {
+
+typedef __bf16 nbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float nf32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kBK = 64;         // K elements per stage
+constexpr int kRowB = 2 * kBK;  // bf16 bytes per row per stage in LDS
+
+// LDS byte offset of 16-byte chunk c (0..7, eight elements) of row r: slot
+// c ^ (r % 8), so the lane reads of one chunk of 8 consecutive rows fall on
+// eight different slots (all 32 banks).
+__device__ __forceinline__ uint32_t nv_lds_off(uint32_t r, uint32_t c) {
+  return r * kRowB + 16u * (c ^ (r & 7u));
+}
+
+struct NvGemmArgs {
+  const uint8_t* a;
+  const uint8_t* sa;
+  const uint8_t* b;
+  const uint8_t* sb;
+  const float* ta;
+  const float* tb;
+  void* c;
+  int64_t ld_a, ld_sa, ld_b, ld_sb, ld_c;
+  int32_t m, n, k;
+};
+
+struct NvRsrc {
+  rsrc_t a, sa, b, sb;
+};
+
+// One operand chunk: 16 code bytes (32 elements, two NVFP4 blocks) and the
+// blocks' two scale bytes; lane t of the work-group takes chunk t + 256 i of
+// the stage, i.e. row (t + 256 i) / 2, half (t + 256 i) % 2 of its 64 elements.
+template <int kRows>
+struct NvOperand {
+  static constexpr int kChunks = kRows * 2 / 256;
+  u32x4_t w[kChunks];
+  uint32_t s[kChunks];
+
+  __device__ __forceinline__ void load(rsrc_t q, rsrc_t qs, int64_t ld, int64_t ld_s, int32_t k0,
+                                       int32_t k) {
+    const uint32_t t = threadIdx.x, kb0 = (uint32_t)k0 / 2u, kbytes = (uint32_t)k / 2u;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const uint32_t chunk = t + 256u * i, row = chunk >> 1, half = chunk & 1u;
+      const bool in_k = kb0 + 16u * half < kbytes;  // k is a multiple of 32: whole chunks
+      w[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          q, in_k ? row * (uint32_t)ld + kb0 + 16u * half : kOob, 0, 0);
+      s[i] = __builtin_amdgcn_raw_buffer_load_b16(
+          qs, in_k ? row * (uint32_t)ld_s + (uint32_t)k0 / 16u + 2u * half : kOob, 0, 0);
+    }
+  }
+
+  // decode to bf16 and write the chunk's four 16-byte LDS chunks
+  template <bool kRazer>
+  __device__ __forceinline__ void store(uint8_t* lds) const {
+    const uint32_t t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const uint32_t chunk = t + 256u * i, row = chunk >> 1, half = chunk & 1u;
+      const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // eight elements: block j / 2 of the chunk
+        const uint32_t sbyte = (s[i] >> (8 * (j / 2))) & 0xFFu;
+        const float sc = e4m3_decode(kRazer ? (sbyte & 0x7Fu) : sbyte);
+        const float special = (sbyte & 0x80u) ? -5.0f : 5.0f;
+        float v[8];
+#define FP4_NV_DEC2(sel)                                                              \
+  {                                                                                   \
+    const float2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[j], 1.0f, sel);    \
+    v[2 * sel] = p.x;                                                                 \
+    v[2 * sel + 1] = p.y;                                                             \
+  }
+        FP4_NV_DEC2(0) FP4_NV_DEC2(1) FP4_NV_DEC2(2) FP4_NV_DEC2(3)
+#undef FP4_NV_DEC2
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // RaZeR: code 0x8, the only code that decodes to -0.0, is the special
+          if (kRazer && __float_as_uint(v[e]) == 0x80000000u) v[e] = special;
+          v[e] *= sc;  // exact: at most 7 significant bits
+        }
+        const u32x4_t o{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+        *reinterpret_cast<u32x4_t*>(lds + nv_lds_off(row, 4u * half + (uint32_t)j)) = o;
+      }
+    }
+  }
+};
+
+template <int WM, int WN, bool kRazerA, bool kRazerB, bool kBf16Out>
+__global__ __launch_bounds__(256) void nv_gemm_kernel(NvGemmArgs g) {
+  constexpr int BM = 64 * WM, BN = 64 * WN;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * kRowB];
+
+  const int32_t tiles_n = (g.n + BN - 1) / BN;
+  const int32_t bm = blockIdx.x / tiles_n, bn = blockIdx.x - bm * tiles_n;
+  const int32_t m0 = bm * BM, n0 = bn * BN;
+  const int32_t rows_a = min(BM, g.m - m0), rows_b = min(BN, g.n - n0);
+  NvRsrc q;
+  q.a = make_rsrc(g.a + (int64_t)m0 * g.ld_a, (uint32_t)(rows_a * g.ld_a));
+  q.b = make_rsrc(g.b + (int64_t)n0 * g.ld_b, (uint32_t)(rows_b * g.ld_b));
+  q.sa = make_rsrc(g.sa + (int64_t)m0 * g.ld_sa, (uint32_t)(rows_a * g.ld_sa));
+  q.sb = make_rsrc(g.sb + (int64_t)n0 * g.ld_sb, (uint32_t)(rows_b * g.ld_sb));
+
+  const uint32_t lane = threadIdx.x & 63u, r = lane & 31u, h = lane >> 5;
+  const uint32_t w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1u;
+
+  nf32x16_t acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // multiply out the stage in LDS buffer buf: four 16-element K steps; lane
+  // (r, h) supplies elements 8h .. 8h + 7 of the step (chunk 2 ks + h)
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t c = 2u * ks + h;
+      nbf16x8_t fa[WM], fb[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+        fa[i] = *reinterpret_cast<const nbf16x8_t*>(
+            lds_a[buf] + nv_lds_off(32u * WM * wm + 32u * i + r, c));
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+        fb[j] = *reinterpret_cast<const nbf16x8_t*>(
+            lds_b[buf] + nv_lds_off(32u * WN * wn + 32u * j + r, c));
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // two stages of loads in flight, as in the MXFP4 GEMM; loads past K read
+  // zeros (code 0 decodes to +0 whatever the scale byte)
+  const int32_t stages = (g.k + kBK - 1) / kBK;
+  NvOperand<BM> a0, a1;
+  NvOperand<BN> b0, b1;
+  a0.load(q.a, q.sa, g.ld_a, g.ld_sa, 0, g.k);
+  b0.load(q.b, q.sb, g.ld_b, g.ld_sb, 0, g.k);
+  a1.load(q.a, q.sa, g.ld_a, g.ld_sa, kBK, g.k);
+  b1.load(q.b, q.sb, g.ld_b, g.ld_sb, kBK, g.k);
+  a0.template store<kRazerA>(lds_a[0]);
+  b0.template store<kRazerB>(lds_b[0]);
+  __syncthreads();
+  int32_t s = 0;
+  for (; s + 1 < stages; s += 2) {
+    a0.load(q.a, q.sa, g.ld_a, g.ld_sa, (s + 2) * kBK, g.k);
+    b0.load(q.b, q.sb, g.ld_b, g.ld_sb, (s + 2) * kBK, g.k);
+    mma(0);
+    a1.template store<kRazerA>(lds_a[1]);
+    b1.template store<kRazerB>(lds_b[1]);
+    __syncthreads();
+    a1.load(q.a, q.sa, g.ld_a, g.ld_sa, (s + 3) * kBK, g.k);
+    b1.load(q.b, q.sb, g.ld_b, g.ld_sb, (s + 3) * kBK, g.k);
+    mma(1);
+    a0.template store<kRazerA>(lds_a[0]);
+    b0.template store<kRazerB>(lds_b[0]);
+    __syncthreads();
+  }
+  if (s < stages) mma(0);
+
+  const float ts = *g.ta * *g.tb;
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int32_t col = n0 + 32 * WN * (int32_t)wn + 32 * j + (int32_t)r;
+      if (col >= g.n) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int32_t row =
+            m0 + 32 * WM * (int32_t)wm + 32 * i + 8 * (e / 4) + 4 * (int32_t)h + e % 4;
+        if (row >= g.m) continue;
+        const float v = acc[i][j][e] * ts;
+        if constexpr (kBf16Out) {
+          const uint32_t p = pack_bf16x2(v, 0.0f);
+          static_cast<uint16_t*>(g.c)[(int64_t)row * g.ld_c + col] = (uint16_t)(p & 0xFFFFu);
+        } else {
+          static_cast<float*>(g.c)[(int64_t)row * g.ld_c + col] = v;
+        }
+      }
+    }
+}
+
+template <int WM, int WN, bool kRa, bool kRb>
+void nv_launch(const NvGemmArgs& g, bool bf16_out, hipStream_t st) {
+  const int64_t tiles = (((int64_t)g.m + 64 * WM - 1) / (64 * WM)) *
+                        (((int64_t)g.n + 64 * WN - 1) / (64 * WN));
+  if (bf16_out)
+    hipLaunchKernelGGL((nv_gemm_kernel<WM, WN, kRa, kRb, true>), dim3((unsigned)tiles), dim3(256),
+                       0, st, g);
+  else
+    hipLaunchKernelGGL((nv_gemm_kernel<WM, WN, kRa, kRb, false>), dim3((unsigned)tiles),
+                       dim3(256), 0, st, g);
+}
+
+template <bool kRa, bool kRb>
+void nv_tiles(const NvGemmArgs& g, bool bf16_out, hipStream_t st) {
+  if (g.m >= 2048 && g.n >= 2048)
+    nv_launch<4, 4, kRa, kRb>(g, bf16_out, st);
+  else
+    nv_launch<2, 2, kRa, kRb>(g, bf16_out, st);
+}
+
+}  // namespace
+
+void launch_nv_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a, const void* sa,
+                    int64_t ld_sa, const float* ta, bool razer_a, const void* b, int64_t ld_b,
+                    const void* sb, int64_t ld_sb, const float* tb, bool razer_b, void* c,
+                    int64_t ld_c, bool bf16_out, hipStream_t st) {
+  NvGemmArgs g{static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(sa),
+               static_cast<const uint8_t*>(b), static_cast<const uint8_t*>(sb), ta, tb, c,
+               ld_a, ld_sa, ld_b, ld_sb, ld_c, (int32_t)m, (int32_t)n, (int32_t)k};
+  if (razer_a && razer_b) nv_tiles<true, true>(g, bf16_out, st);
+  if (razer_a && !razer_b) nv_tiles<true, false>(g, bf16_out, st);
+  if (!razer_a && razer_b) nv_tiles<false, true>(g, bf16_out, st);
+  if (!razer_a && !razer_b) nv_tiles<false, false>(g, bf16_out, st);
+}
+
+}  // namespace fp4

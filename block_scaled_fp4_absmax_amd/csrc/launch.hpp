@@ -64,6 +64,12 @@ void launch_nv_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamar
 void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a, const void* sa,
                     int64_t ld_sa, const void* b, int64_t ld_b, const void* sb, int64_t ld_sb,
                     void* c, int64_t ld_c, bool bf16_out, hipStream_t st);
+// C = ta tb (A B^T), NVFP4 operands (codes [rows, K/2], E4M3 scales
+// [rows, K/16], RaZeR per operand), decoded exactly to bf16 for the MFMA.
+void launch_nv_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a, const void* sa,
+                    int64_t ld_sa, const float* ta, bool razer_a, const void* b, int64_t ld_b,
+                    const void* sb, int64_t ld_sb, const float* tb, bool razer_b, void* c,
+                    int64_t ld_c, bool bf16_out, hipStream_t st);
 void launch_channel_energy(int64_t rows, int64_t cols, int64_t ld_x, const void* x, float* energy,
                            hipStream_t st);
 

@@ -195,31 +195,39 @@ int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t 
 /*
  * fp4_gemm -- C = A B^T on the quantized operands, the consumer of the path
  * ([RaZeR] sec. 2.3: GEMM kernels that take quantized weights and
- * activations).
+ * activations, the special value rebuilt from the scale's metadata bit).
  *
  * A is [m, k] (e.g. activations) and B is [n, k] (e.g. weights, one row per
- * output channel), both MXFP4 exactly as fp4_quantize / fp4_rotate_quantize
- * write them: codes [rows, ld] (element 2i in the low nibble of byte i) and
- * E8M0 scales [rows, ld_s], one per 32 consecutive k. Computed on gfx950's
- * scaled FP4 matrix instructions: every product of two elements is exact, the
- * block scales 2^(e_a + e_b) are applied per 32-element block pair, and sums
- * accumulate in fp32 (64 k at a time). A scale byte 0xFF (NaN) gives NaN in
- * every output it reaches.
+ * output channel), each exactly as fp4_quantize / fp4_rotate_quantize write
+ * it: codes [rows, ld] (element 2i in the low nibble of byte i) and scale
+ * bytes [rows, ld_s], one per block of k.
+ *  - MXFP4: gfx950's scaled FP4 matrix instructions; every product of two
+ *    elements is exact, the block scales 2^(e_a + e_b) apply per 32-element
+ *    block pair, sums accumulate in fp32 (64 k at a time). A scale byte 0xFF
+ *    (NaN) gives NaN in every output it reaches.
+ *  - NVFP4 (mode_a / mode_b FP4_PLAIN or FP4_RAZER per operand): each element
+ *    e2m1(code) * e4m3(scale) (RaZeR code 0x8: +-5 by the scale's bit 7) is
+ *    decoded exactly to bf16 and multiplied on the bf16 matrix instructions
+ *    (exact products, fp32 sums 16 k at a time); C = (ts_a ts_b) * sum, one
+ *    fp32 rounding of the tensor-scale product and one of the result.
  *
  *  a_codes, b_codes     device, uint8; 16-byte aligned, ld % 16 == 0,
- *                       ld >= k / 2, 128 * ld < 2^31
- *  a_scales, b_scales   device, uint8; 4-byte aligned, ld_s % 4 == 0,
- *                       ld_s >= k / 32, 128 * ld_s < 2^31 (bytes of a row
- *                       past k / 32 are never used)
+ *                       ld >= k / 2, 256 * ld < 2^31
+ *  a_scales, b_scales   device, uint8; ld_s >= k / block, 256 * ld_s < 2^31;
+ *                       MXFP4: 4-byte aligned, ld_s % 4 == 0; NVFP4: 2-byte
+ *                       aligned, ld_s % 2 == 0 (bytes past k / block unused)
+ *  a_ts, b_ts           NVFP4: device fp32[1] tensor scales; MXFP4: ignored
+ *  mode_a, mode_b       FP4_PLAIN, or FP4_RAZER (NVFP4 only)
  *  m, n, k              >= 0, < 2^31; k % 32 == 0 (m or n zero: no work;
  *                       k zero: C = 0)
- *  format               FP4_MXFP4 (others return FP4_ERR_UNSUPPORTED)
+ *  format               FP4_MXFP4 or FP4_NVFP4
  *  out_dtype            FP4_OUT_F32 (c fp32) or FP4_OUT_BF16 (c bf16, RNE)
  *  c, ld_c              device, [m, ld_c], ld_c >= n, aligned to its element
  */
 enum fp4_out_dtype { FP4_OUT_F32 = 0, FP4_OUT_BF16 = 1 };
 int fp4_gemm(const void* a_codes, int64_t ld_a, const void* a_scales, int64_t ld_sa,
-             const void* b_codes, int64_t ld_b, const void* b_scales, int64_t ld_sb, int64_t m,
+             const float* a_ts, int mode_a, const void* b_codes, int64_t ld_b,
+             const void* b_scales, int64_t ld_sb, const float* b_ts, int mode_b, int64_t m,
              int64_t n, int64_t k, int format, int out_dtype, void* c, int64_t ld_c,
              void* stream);
 

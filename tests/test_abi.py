@@ -104,18 +104,25 @@ def test_rotate_and_dequant_validation(L):
     assert D(FAKE, 32, FAKE, 4, None, 4, 64, 1, 16, 0, None, 0, FAKE, 64, None) == -1
     assert D(FAKE, 32, FAKE, 2, None, 4, 64, 0, 32, 0, None, 0, FAKE + 8, 64, None) == -3
     assert D(FAKE, 32, FAKE, 2, None, 0, 64, 0, 32, 0, None, 0, None, 64, None) == 0
-    # gemm(a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, m, n, k, fmt, out_dtype, c, ld_c, stream)
-    G = L.fp4_gemm
-    assert G(FAKE, 32, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 1, 0, FAKE, 8, None) == -4  # NVFP4
-    assert G(FAKE, 32, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 2, FAKE, 8, None) == -4  # dtype
-    assert G(FAKE, 32, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 48, 0, 0, FAKE, 8, None) == -2  # k % 32
-    assert G(FAKE, 16, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 0, FAKE, 8, None) == -2  # ld_a
-    assert G(FAKE, 32, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 0, FAKE, 4, None) == -2  # ld_c
-    assert G(FAKE, 40, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 0, FAKE, 8, None) == -3  # ld_a % 16
-    assert G(FAKE, 32, FAKE, 6, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 0, FAKE, 8, None) == -3  # ld_sa % 4
-    assert G(FAKE + 8, 32, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 0, FAKE, 8, None) == -3
-    assert G(None, 32, FAKE, 4, FAKE, 32, FAKE, 4, 8, 8, 64, 0, 0, FAKE, 8, None) == -1
-    assert G(None, 32, None, 4, None, 32, None, 4, 0, 8, 64, 0, 0, None, 8, None) == 0  # m = 0
+    # gemm(a, ld_a, sa, ld_sa, ta, mode_a, b, ld_b, sb, ld_sb, tb, mode_b, m, n, k, fmt,
+    #      out_dtype, c, ld_c, stream)
+    def G(a=FAKE, lda=32, sa=FAKE, ldsa=4, ta=None, ma=0, b=FAKE, ldb=32, sb=FAKE, ldsb=4,
+          tb=None, mb=0, m=8, n=8, k=64, fmt=0, od=0, c=FAKE, ldc=8):
+        return L.fp4_gemm(a, lda, sa, ldsa, ta, ma, b, ldb, sb, ldsb, tb, mb, m, n, k, fmt, od,
+                          c, ldc, None)
+    assert G(fmt=2) == -4                        # MXINT4 has no GEMM
+    assert G(od=2) == -4                         # output type
+    assert G(ma=1) == -4                         # RaZeR needs NVFP4
+    assert G(k=48) == -2                         # k % 32
+    assert G(lda=16) == -2                       # ld_a < k / 2
+    assert G(ldc=4) == -2                        # ld_c < n
+    assert G(lda=40) == -3                       # ld_a % 16
+    assert G(ldsa=6) == -3                       # MXFP4 scale rows: ld_s % 4
+    assert G(a=FAKE + 8) == -3
+    assert G(a=None) == -1
+    assert G(a=None, sa=None, b=None, sb=None, c=None, m=0) == 0
+    assert G(fmt=1, ldsa=4, ldsb=4) == -1        # NVFP4 needs both tensor scales
+    assert G(fmt=1, ta=TS, tb=TS, ldsa=5, ldsb=4) == -3  # NVFP4 scale rows: ld_s % 2
     E = L.fp4_channel_energy
     assert E(FAKE, 4, 48, 48, FAKE, None) == -2
     assert E(None, 4, 64, 64, FAKE, None) == -1

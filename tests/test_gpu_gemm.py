@@ -143,3 +143,73 @@ def test_gemm_of_quantized_layer(orc, rot):
     ref = inputs.bf16_bits_to_f32(xa).astype(np.float64) @ \
         inputs.bf16_bits_to_f32(xw).astype(np.float64).T
     note(f"  GEMM SQNR vs the unquantized product: {orc.sqnr_db(ref, want):.2f} dB")
+
+
+# ------------------------------------------------------------------ NVFP4 --
+# Each element decodes exactly to bf16 and the bf16 products are exact; sums
+# accumulate in fp32 16 values of k per instruction, then one multiplication
+# by the rounded tensor-scale product:
+#     |C_gpu - C| <= 2^-22 (k / 16 + 1) S + 2^-22 |C|
+def _rand_nv(rng, rows, k, razer):
+    codes = rng.integers(0, 256, (rows, k // 2), dtype=np.uint8)
+    scales = rng.integers(1, 127, (rows, k // 16), dtype=np.uint8)  # finite E4M3
+    if razer:
+        scales |= (rng.integers(0, 2, scales.shape, dtype=np.uint8) << 7)
+    return codes, scales
+
+
+def _check_nv(orc, ac, as_, ta, ra, bc, bs, tb, rb, k, bf16=False):
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    m, n = ac.shape[0], bc.shape[0]
+    tat = torch.tensor([ta], dtype=torch.float32, device="cuda")
+    tbt = torch.tensor([tb], dtype=torch.float32, device="cuda")
+    out = torch.empty((m, n), dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
+    fp4.gemm(dev(ac), _scales_dev(as_, 2), dev(bc), _scales_dev(bs, 0), k=k, fmt=fp4.NVFP4,
+             a_ts=tat, b_ts=tbt, mode_a=fp4.RAZER if ra else fp4.PLAIN,
+             mode_b=fp4.RAZER if rb else fp4.PLAIN, out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    want = orc.gemm_f64(ac, as_, bc, bs, 1, ra, ta, tb, razer_b=rb)
+    a = np.abs(orc.decode_exact(ac, as_, 1, ra, ta))
+    b = np.abs(orc.decode_exact(bc, bs, 1, rb, tb))
+    tol = 2.0 ** -22 * (k / 16 + 1) * (a @ b.T) + 2.0 ** -22 * np.abs(want)
+    if bf16:
+        tol += 2.0 ** -8 * np.abs(want)
+    err = np.abs(got - want)
+    assert np.all(err <= tol), f"max err {err.max()} at {np.unravel_index(err.argmax(), err.shape)}"
+
+
+@pytest.mark.parametrize("m,n,k,ra,rb", [
+    (128, 128, 128, False, False), (128, 128, 128, True, True), (37, 45, 96, True, False),
+    (200, 300, 4160, False, True), (1, 512, 8192, True, True), (2048, 2304, 1024, True, True),
+    (2100, 2050, 544, False, False)])
+def test_nv_gemm_random_codes(orc, m, n, k, ra, rb):
+    note(f"case: NVFP4 GEMM {m}x{n}x{k} razer A={ra} B={rb}")
+    rng = np.random.default_rng(m + 3 * n + k + ra + 2 * rb)
+    ac, as_ = _rand_nv(rng, m, k, ra)
+    bc, bs = _rand_nv(rng, n, k, rb)
+    _check_nv(orc, ac, as_, float(np.float32(0.0371)), ra, bc, bs, float(np.float32(2.5e-3)), rb,
+              k, bf16=(m == 37))
+
+
+def test_nv_gemm_of_quantized_layer(orc):
+    """Activations and weights quantized on the GPU with NVFP4 + RaZeR (tensor
+    scales computed), then the GEMM on them."""
+    note("case: NVFP4+RaZeR quantize activations 256x2048, weights 384x2048, then GEMM")
+    xa = inputs.gen_c3(rows=256, cols=2048)
+    xw = inputs.gen_c5(0, rows=384, cols=2048)
+    ca, sa, ta = fp4.quantize(to_dev(xa), fp4.NVFP4, fp4.RAZER)
+    cw, sw, tw = fp4.quantize(to_dev(xw), fp4.NVFP4, fp4.RAZER)
+    c = fp4.gemm(ca, sa, cw, sw, fmt=fp4.NVFP4, a_ts=ta, b_ts=tw, mode_a=fp4.RAZER,
+                 mode_b=fp4.RAZER)
+    torch.cuda.synchronize()
+    ac, as_, bc, bs = (t.cpu().numpy() for t in (ca, sa, cw, sw))
+    fa, fb = float(ta.cpu()[0]), float(tw.cpu()[0])
+    want = orc.gemm_f64(ac, as_, bc, bs, 1, True, fa, fb)
+    a = np.abs(orc.decode_exact(ac, as_, 1, True, fa))
+    b = np.abs(orc.decode_exact(bc, bs, 1, True, fb))
+    tol = 2.0 ** -22 * (2048 / 16 + 1) * (a @ b.T) + 2.0 ** -22 * np.abs(want)
+    assert np.all(np.abs(c.cpu().numpy() - want) <= tol)
+    ref = inputs.bf16_bits_to_f32(xa).astype(np.float64) @ \
+        inputs.bf16_bits_to_f32(xw).astype(np.float64).T
+    note(f"  GEMM SQNR vs the unquantized product: {orc.sqnr_db(ref, want):.2f} dB")
