@@ -333,7 +333,8 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
             q3[f"{name}_{'h%d' % h if h else 'plain'}"] = round(sqnr_db(torch, x3f, xh.float()), 3)
     out["c3_sqnr_db"] = q3
     del x3, x3f
-    out["gemm_mxfp4"] = gemm_rows(torch, fp4)
+    out["gemm_mxfp4"] = gemm_rows(torch, fp4, fp4.MXFP4)
+    out["gemm_nvfp4_razer"] = gemm_rows(torch, fp4, fp4.NVFP4)
 
     # NVFP4 + RaZeR on the 4096x4096 weight recipe, enough copies to defeat the cache
     log("[bench] generating c2 for the NVFP4 rows")
@@ -373,25 +374,32 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
 MFMA_PEAK_FP4_TFLOPS = 10100.0
 
 
-def gemm_rows(torch, fp4):
-    """The consumer: C = A B^T on MXFP4 operands (activations [m, k], weights
-    [n, k] of the Llama-70B-shaped layer), bf16 out, on the scaled FP4 matrix
-    cores. Random codes and scale bytes: the time does not depend on values."""
-    log("[bench] MXFP4 GEMM rows")
+def gemm_rows(torch, fp4, fmt):
+    """The consumer: C = A B^T on quantized operands (activations [m, k],
+    weights [n, k] of the Llama-70B-shaped layer), bf16 out. MXFP4 runs on the
+    scaled FP4 matrix cores (peak 10.1 PFLOP/s); NVFP4 + RaZeR on both sides is
+    decoded exactly to bf16 and runs on the bf16 ones (peak 2.5 PFLOP/s).
+    Random codes and finite scale bytes: the time does not depend on values."""
+    nv = fmt == fp4.NVFP4
+    blk, lo, hi = (16, 40, 60) if nv else (32, 120, 131)
+    peak = MFMA_PEAK_BF16_TFLOPS if nv else MFMA_PEAK_FP4_TFLOPS
+    log(f"[bench] {'NVFP4+RaZeR' if nv else 'MXFP4'} GEMM rows")
     g = torch.Generator(device="cuda").manual_seed(5)
+    ts = torch.ones(1, dtype=torch.float32, device="cuda")
+    kw = dict(fmt=fp4.NVFP4, a_ts=ts, b_ts=ts, mode_a=fp4.RAZER, mode_b=fp4.RAZER) if nv else {}
     rows = {}
     for m, n, k in ((4096, 8192, 8192), (4096, 28672, 8192), (4096, 8192, 28672),
                     (16, 8192, 8192)):
         a = torch.randint(0, 256, (m, k // 2), dtype=torch.uint8, device="cuda", generator=g)
-        sa = torch.randint(120, 131, (m, k // 32), dtype=torch.uint8, device="cuda", generator=g)
+        sa = torch.randint(lo, hi, (m, k // blk), dtype=torch.uint8, device="cuda", generator=g)
         b = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device="cuda", generator=g)
-        sb = torch.randint(120, 131, (n, k // 32), dtype=torch.uint8, device="cuda", generator=g)
+        sb = torch.randint(lo, hi, (n, k // blk), dtype=torch.uint8, device="cuda", generator=g)
         c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-        ms = timed(torch, lambda i: fp4.gemm(a, sa, b, sb, out=c), 20, 3)
+        ms = timed(torch, lambda i: fp4.gemm(a, sa, b, sb, out=c, **kw), 10, 2)
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
-        by = (m + n) * (k / 2 + k / 32) + 2 * m * n
+        by = (m + n) * (k / 2 + k / blk) + 2 * m * n
         rows[f"{m}x{n}x{k}"] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
-                                "frac_fp4_mfma_peak": round(tf / MFMA_PEAK_FP4_TFLOPS, 4),
+                                "frac_mfma_peak": round(tf / peak, 4),
                                 "GBps": round(by / ms / 1e6, 1)}
         del a, sa, b, sb, c
     return rows
