@@ -111,8 +111,14 @@ def _load():
         "orc_nv_quantize_f32": (None, [vp, i64, i64, i64, i32, f32, vp, i64, vp, i64]),
         "orc_nv_tensor_amax_f32": (f32, [vp, i64, i64, i64]),
         "orc_razer_block": (i32, [vp, i32, vp, vp, vp]),
-        "orc_dequantize": (None, [vp, i64, vp, i64, f32, i64, i64, i32, i32, vp, i64]),
-        "orc_dequantize_f64": (None, [vp, i64, vp, i64, f32, i64, i64, i32, i32, vp, i64]),
+        "orc_dequantize": (None, [vp, i64, vp, i64, f32, i64, i64, i32, i32, f64, vp, i64]),
+        "orc_dequantize_f64": (None, [vp, i64, vp, i64, f32, i64, i64, i32, i32, f64, vp, i64]),
+        "orc_e3m3_value": (f64, [i32]),
+        "orc_e3m3_encode": (i32, [f64]),
+        "orc_nvw_tensor_scale": (f32, [f32]),
+        "orc_razer_block_set": (i32, [vp, i32, vp, i32, vp]),
+        "orc_nvw_quantize_bf16": (None, [vp, i64, i64, i64, f32, f64, vp, i64, vp, i64]),
+        "orc_nvw_value": (f64, [i32, i32, f64]),
         "orc_rotate": (None, [vp, i64, i64, i64, vp, i32, vp, i64]),
         "orc_unrotate_f64": (None, [vp, i64, i64, i64, vp, i32, vp, i64]),
         "orc_channel_energy": (None, [vp, i64, i64, i64, vp]),
@@ -280,27 +286,65 @@ def razer_block(y: np.ndarray) -> Tuple[np.ndarray, int, float, float]:
     return codes, int(sel), float(sse[0]), float(sse0[0])
 
 
-def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: int, razer: bool = False,
-               tensor_scale: float = 1.0) -> np.ndarray:
-    """bf16 bits [rows, cols] of the decoded values (fmt 0 = MXFP4, 1 = NVFP4, 2 = MXINT4)."""
+def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: int, razer: int = 0,
+               tensor_scale: float = 1.0, pair: float = 0.0) -> np.ndarray:
+    """bf16 bits [rows, cols] of the decoded values (fmt 0 = MXFP4, 1 = NVFP4,
+    2 = MXINT4; NVFP4 razer 1 = RaZeR, 2 = the weight variant with second
+    special pair +-pair)."""
     rows = codes.shape[0]
     cols = codes.shape[1] * 2
     out = np.zeros((rows, cols), np.uint16)
     _load().orc_dequantize(_ptr(codes), _ld(codes), _ptr(scales), _ld(scales),
-                           float(tensor_scale), rows, cols, int(fmt), int(razer),
+                           float(tensor_scale), rows, cols, int(fmt), int(razer), float(pair),
                            _ptr(out), cols)
     return out
 
 
-def dequantize_f64(codes: np.ndarray, scales: np.ndarray, fmt: int, razer: bool = False,
-                   tensor_scale: float = 1.0) -> np.ndarray:
+def dequantize_f64(codes: np.ndarray, scales: np.ndarray, fmt: int, razer: int = 0,
+                   tensor_scale: float = 1.0, pair: float = 0.0) -> np.ndarray:
     rows = codes.shape[0]
     cols = codes.shape[1] * 2
     out = np.zeros((rows, cols), np.float64)
     _load().orc_dequantize_f64(_ptr(codes), _ld(codes), _ptr(scales), _ld(scales),
                                float(tensor_scale), rows, cols, int(fmt), int(razer),
-                               _ptr(out), cols)
+                               float(pair), _ptr(out), cols)
     return out
+
+
+# ---- RaZeR for weights: E3M3 block scale, four special values --------------
+def e3m3_value(code: int) -> float:
+    return _load().orc_e3m3_value(int(code))
+
+
+def e3m3_encode(v: float) -> int:
+    return _load().orc_e3m3_encode(float(v))
+
+
+def nvw_tensor_scale(amax: float) -> float:
+    return float(_load().orc_nvw_tensor_scale(float(amax)))
+
+
+def razer_block_set(y: np.ndarray, specials) -> Tuple[np.ndarray, int]:
+    y = np.ascontiguousarray(y, np.float32)
+    sp = np.ascontiguousarray(specials, np.float64)
+    codes = np.zeros(y.size, np.uint8)
+    sel = _load().orc_razer_block_set(_ptr(y), y.size, _ptr(sp), sp.size, _ptr(codes))
+    return codes, int(sel)
+
+
+def nvw_quantize(x_bf16: np.ndarray, pair: float, tensor_scale: Optional[float] = None
+                 ) -> Tuple[np.ndarray, np.ndarray, float]:
+    """RaZeR weight quantization: codes, scale bytes (E3M3 | selector << 6), s_t."""
+    assert x_bf16.dtype == np.uint16
+    rows, cols = x_bf16.shape
+    assert cols % 16 == 0
+    if tensor_scale is None:
+        tensor_scale = nvw_tensor_scale(nv_tensor_amax(x_bf16))
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 16), np.uint8)
+    _load().orc_nvw_quantize_bf16(_ptr(x_bf16), rows, cols, _ld(x_bf16), float(tensor_scale),
+                                  float(pair), _ptr(codes), cols // 2, _ptr(scales), cols // 16)
+    return codes, scales, float(tensor_scale)
 
 
 def nv_tensor_amax_f32(y: np.ndarray) -> float:
@@ -361,12 +405,13 @@ def rotate_quantize_mxint4(x_bf16: np.ndarray, perm: Optional[np.ndarray], hadam
     return codes, scales, y
 
 
-def decode_exact(codes: np.ndarray, scales: np.ndarray, fmt: int, razer: bool = False,
-                 tensor_scale: float = 1.0) -> np.ndarray:
+def decode_exact(codes: np.ndarray, scales: np.ndarray, fmt: int, razer: int = 0,
+                 tensor_scale: float = 1.0, pair: float = 0.0) -> np.ndarray:
     """float64 [rows, cols] of the exact element values (no rounding at all):
     MXFP4 e2m1(code) 2^(e-127); NVFP4 e2m1(code) e4m3(scale) s_t, RaZeR code
     0x8 reading +5 or -5 by the scale's top bit. Exact in float64: at most 3
-    significant bits times 4 times 24."""
+    significant bits times 4 times 24. razer 2: the weight variant (E3M3
+    scale, special {+5, -5, +pair, -pair}[selector])."""
     codes = np.ascontiguousarray(codes)
     rows, half = codes.shape
     nib = np.empty((rows, 2 * half), np.int64)
@@ -379,6 +424,11 @@ def decode_exact(codes: np.ndarray, scales: np.ndarray, fmt: int, razer: bool = 
         return np.ldexp(val, e)
     assert fmt == 1
     sb = np.repeat(scales.astype(np.int64), 16, axis=1)[:, :2 * half]
+    if razer == 2:
+        sp = np.array([5.0, -5.0, pair, -pair])
+        val = np.where(nib == 8, sp[(sb >> 6) & 3], val)
+        e3m3 = np.array([e3m3_value(b) for b in range(64)])
+        return val * e3m3[sb & 63] * float(tensor_scale)
     e4m3 = np.array([e4m3_value(b) for b in range(256)])
     if razer:
         special = np.where(sb & 0x80, -5.0, 5.0)
@@ -388,14 +438,14 @@ def decode_exact(codes: np.ndarray, scales: np.ndarray, fmt: int, razer: bool = 
 
 
 def gemm_f64(a_codes: np.ndarray, a_scales: np.ndarray, b_codes: np.ndarray,
-             b_scales: np.ndarray, fmt: int = 0, razer: bool = False, ts_a: float = 1.0,
-             ts_b: float = 1.0, razer_b: Optional[bool] = None) -> np.ndarray:
+             b_scales: np.ndarray, fmt: int = 0, razer: int = 0, ts_a: float = 1.0,
+             ts_b: float = 1.0, razer_b: Optional[int] = None, pair: float = 0.0) -> np.ndarray:
     """C = A B^T of two quantized operands, A [m, k] and B [n, k]: each decoded
     exactly (decode_exact), then a float64 library matmul (the RaZeR page,
     technical summary sec. 2.3: the GEMM consumes the quantized weights and
     activations). razer applies to A, and to B unless razer_b says otherwise."""
-    a = decode_exact(a_codes, a_scales, fmt, razer, ts_a)
-    b = decode_exact(b_codes, b_scales, fmt, razer if razer_b is None else razer_b, ts_b)
+    a = decode_exact(a_codes, a_scales, fmt, razer, ts_a, pair)
+    b = decode_exact(b_codes, b_scales, fmt, razer if razer_b is None else razer_b, ts_b, pair)
     return a @ b.T
 
 

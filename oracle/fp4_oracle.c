@@ -471,6 +471,115 @@ float orc_nv_tensor_amax_f32(const float* x, int64_t rows, int64_t cols, int64_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* RaZeR for weights ([RaZeR] sec. 2.1 and 2.2): weights tolerate a coarser  */
+/* block scale, E3M3 (6 bits) instead of E4M3, which frees 2 bits per block; */
+/* they select one of four special values, two +- pairs computed offline,    */
+/* for the redundant code 0x8, the block taking the one of least squared     */
+/* error. Readings where the pages are silent: E3M3 "fn"-style, bias 3,      */
+/* subnormals m 2^-5, largest 30, no Inf or NaN; the tensor scale maps the   */
+/* largest block onto 6 * 30, s_t = amax_t / 180; selector i picks           */
+/* {+5, -5, +p, -p}[i] (the pages give +-5; p is the second pair); the scale  */
+/* byte is e3m3 | i << 6. Ties: the lowest selector; an element takes the    */
+/* special code only when strictly closer to it than to every standard value.*/
+/* ------------------------------------------------------------------------ */
+double orc_e3m3_value(int code) {
+  int e = (code >> 3) & 7, m = code & 7;
+  if (e == 0) return ldexp((double)m, -5);
+  return ldexp(1.0 + m / 8.0, e - 3);
+}
+
+int orc_e3m3_encode(double v) {
+  if (v > 30.0) return 63;
+  int best = 0;
+  double bestd = fabs(v - orc_e3m3_value(0));
+  for (int c = 1; c < 64; ++c) {
+    double d = fabs(v - orc_e3m3_value(c));
+    if (d < bestd || (d == bestd && (c % 2 == 0) && (best % 2 != 0))) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return best;
+}
+
+float orc_nvw_tensor_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  return amax / 180.0f;
+}
+
+/* Index of the special value (of ns) whose code book gives the least squared
+ * error on y[0..n): the error of an element differs between candidates only
+ * where it takes code 0x8, so the candidates are ranked by their total gain
+ * over plain E2M1, exact in double (see orc_razer_block). */
+int orc_razer_block_set(const float* y, int n, const double* specials, int ns, uint8_t* codes) {
+  double best_gain = -1.0;
+  int best = 0;
+  for (int i = 0; i < ns; ++i) {
+    double gain = 0.0;
+    for (int j = 0; j < n; ++j) {
+      double v = (double)y[j];
+      int c = orc_e2m1_nearest_razer(v, specials[i]);
+      if (c == 8) {
+        double vs = orc_e2m1_value(orc_e2m1_nearest(v));
+        gain += (v - vs) * (v - vs) - (v - specials[i]) * (v - specials[i]);
+      }
+    }
+    if (gain > best_gain) {
+      best_gain = gain;
+      best = i;
+    }
+  }
+  for (int j = 0; j < n; ++j) codes[j] = (uint8_t)orc_e2m1_nearest_razer((double)y[j], specials[best]);
+  return best;
+}
+
+static void nvw_block(const float* xv, float s_t, double p, uint8_t* rc, int64_t b,
+                      uint8_t* scale) {
+  const double specials[4] = {5.0, -5.0, p, -p};
+  const float d = 6.0f * s_t;
+  float amax = 0.0f;
+  for (int i = 0; i < 16; ++i)
+    if (fabsf(xv[i]) > amax) amax = fabsf(xv[i]);
+  float s_raw = amax / d;
+  int sb = orc_e3m3_encode((double)s_raw);
+  if (sb == 0) {
+    for (int i = 0; i < 16; ++i) put_nibble(rc, 16 * b + i, 0);
+    *scale = 0;
+    return;
+  }
+  float s_eff = (float)orc_e3m3_value(sb) * s_t;
+  float rcp = 1.0f / s_eff;
+  float y[16];
+  uint8_t c[16];
+  for (int i = 0; i < 16; ++i) y[i] = xv[i] * rcp;
+  int sel = orc_razer_block_set(y, 16, specials, 4, c);
+  for (int i = 0; i < 16; ++i) put_nibble(rc, 16 * b + i, c[i]);
+  *scale = (uint8_t)(sb | (sel << 6));
+}
+
+void orc_nvw_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                           float tensor_scale, double p, uint8_t* codes, int64_t ld_codes,
+                           uint8_t* scales, int64_t ld_scales) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < cols / 16; ++b) {
+      float xv[16];
+      for (int i = 0; i < 16; ++i) xv[i] = orc_bf16_to_f32(x[r * ld_x + 16 * b + i]);
+      nvw_block(xv, tensor_scale, p, codes + r * ld_codes, b, scales + r * ld_scales + b);
+    }
+  }
+}
+
+/* Value of a weight-RaZeR element before the tensor scale: e2m1 or special,
+ * times e3m3(scale). */
+double orc_nvw_value(int code, int byte, double p) {
+  const double specials[4] = {5.0, -5.0, p, -p};
+  double v = code == 8 ? specials[(byte >> 6) & 3] : orc_e2m1_value(code);
+  return v * orc_e3m3_value(byte & 63);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dequantization. MXFP4 and MXINT4: value * 2^e, exact before the final   */
 /* rounding.                                                                 */
 /* NVFP4: fp32 product value * s_eff. RaZeR: code 0x8 decodes to the block's */
@@ -480,7 +589,7 @@ float orc_nv_tensor_amax_f32(const float* x, int64_t rows, int64_t cols, int64_t
 /* ------------------------------------------------------------------------ */
 static double dq_value(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                        int64_t ld_scales, float s_t, int64_t r, int64_t j, int format,
-                       int razer) {
+                       int razer, double p) {
   int c = get_nibble(codes + r * ld_codes, j);
   if (format == 0 || format == 2) {
     int byte = scales[r * ld_scales + j / 32];
@@ -490,36 +599,40 @@ static double dq_value(const uint8_t* codes, int64_t ld_codes, const uint8_t* sc
   int byte = scales[r * ld_scales + j / 16];
   double v;
   float s_eff;
-  if (razer) {
+  if (razer == 2) { /* weights: E3M3 scale, four specials */
+    const double specials[4] = {5.0, -5.0, p, -p};
+    s_eff = (float)orc_e3m3_value(byte & 63) * s_t;
+    v = (c == 8) ? specials[(byte >> 6) & 3] : orc_e2m1_value(c);
+  } else if (razer) {
     s_eff = (float)orc_e4m3_value(byte & 0x7F) * s_t;
     v = (c == 8) ? ((byte & 0x80) ? -5.0 : 5.0) : orc_e2m1_value(c);
   } else {
     s_eff = (float)orc_e4m3_value(byte) * s_t;
     v = orc_e2m1_value(c);
   }
-  float p = (float)v * s_eff;
-  return (double)p;
+  float prod = (float)v * s_eff;
+  return (double)prod;
 }
 
 void orc_dequantize_f64(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                         int64_t ld_scales, float tensor_scale, int64_t rows, int64_t cols,
-                        int format, int razer, double* out, int64_t ld_out) {
+                        int format, int razer, double p, double* out, int64_t ld_out) {
   int64_t r;
 #pragma omp parallel for schedule(static) num_threads(g_threads)
   for (r = 0; r < rows; ++r)
     for (int64_t j = 0; j < cols; ++j)
       out[r * ld_out + j] =
-          dq_value(codes, ld_codes, scales, ld_scales, tensor_scale, r, j, format, razer);
+          dq_value(codes, ld_codes, scales, ld_scales, tensor_scale, r, j, format, razer, p);
 }
 
 void orc_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                     int64_t ld_scales, float tensor_scale, int64_t rows, int64_t cols,
-                    int format, int razer, uint16_t* out, int64_t ld_out) {
+                    int format, int razer, double p, uint16_t* out, int64_t ld_out) {
   int64_t r;
 #pragma omp parallel for schedule(static) num_threads(g_threads)
   for (r = 0; r < rows; ++r)
     for (int64_t j = 0; j < cols; ++j) {
-      double v = dq_value(codes, ld_codes, scales, ld_scales, tensor_scale, r, j, format, razer);
+      double v = dq_value(codes, ld_codes, scales, ld_scales, tensor_scale, r, j, format, razer, p);
       out[r * ld_out + j] = orc_f32_to_bf16((float)v); /* exact or already fp32 */
     }
 }

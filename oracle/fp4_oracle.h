@@ -65,13 +65,24 @@ float orc_nv_tensor_amax_f32(const float* x, int64_t rows, int64_t cols, int64_t
 int orc_razer_block(const float* y, int n, uint8_t* codes, double* sse_chosen,
                     double* sse_plain);
 
-/* dequantization; format 0 = MXFP4, 1 = NVFP4, 2 = MXINT4 */
+/* RaZeR for weights: E3M3 block scale, selector over {+5, -5, +p, -p} */
+double orc_e3m3_value(int code);
+int orc_e3m3_encode(double v);
+float orc_nvw_tensor_scale(float amax);
+int orc_razer_block_set(const float* y, int n, const double* specials, int ns, uint8_t* codes);
+void orc_nvw_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                           float tensor_scale, double p, uint8_t* codes, int64_t ld_codes,
+                           uint8_t* scales, int64_t ld_scales);
+double orc_nvw_value(int code, int byte, double p);
+
+/* dequantization; format 0 = MXFP4, 1 = NVFP4, 2 = MXINT4; razer 2 = the
+ * weight variant (second special pair +-p) */
 void orc_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                     int64_t ld_scales, float tensor_scale, int64_t rows, int64_t cols,
-                    int format, int razer, uint16_t* out, int64_t ld_out);
+                    int format, int razer, double p, uint16_t* out, int64_t ld_out);
 void orc_dequantize_f64(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                         int64_t ld_scales, float tensor_scale, int64_t rows, int64_t cols,
-                        int format, int razer, double* out, int64_t ld_out);
+                        int format, int razer, double p, double* out, int64_t ld_out);
 
 /* two-level rotation: permutation across blocks, Hadamard inside each block */
 void orc_rotate(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
