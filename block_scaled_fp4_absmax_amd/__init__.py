@@ -14,13 +14,13 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "MXFP4", "NVFP4", "MXINT4", "PLAIN", "RAZER", "FLAG_TENSOR_SCALE_GIVEN", "FLAG_SCALE_OCP_FLOOR",
+    "MXFP4", "NVFP4", "MXINT4", "PLAIN", "RAZER", "RAZER_W", "FLAG_TENSOR_SCALE_GIVEN", "FLAG_SCALE_OCP_FLOOR",
     "Fp4Error", "lib", "library_path", "quantize", "dequantize", "rotate_quantize",
     "channel_energy", "build_permutation", "block_of", "gemm", "OUT_F32", "OUT_BF16",
 ]
 
 MXFP4, NVFP4, MXINT4 = 0, 1, 2
-PLAIN, RAZER = 0, 1
+PLAIN, RAZER, RAZER_W = 0, 1, 2
 FLAG_TENSOR_SCALE_GIVEN = 1
 FLAG_SCALE_OCP_FLOOR = 2
 OUT_F32, OUT_BF16 = 0, 1

@@ -23,8 +23,8 @@ int check_quant_args(const void* x, int64_t rows, int64_t cols, int64_t ld_x, in
                      const void* scales, int64_t ld_scales, const float* tensor_scale) {
   if (!known_format(format)) return FP4_ERR_UNSUPPORTED;
   if (block != block_of(format)) return FP4_ERR_UNSUPPORTED;
-  if (mode != FP4_PLAIN && mode != FP4_RAZER) return FP4_ERR_UNSUPPORTED;
-  if (mode == FP4_RAZER && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;  // E8M0 has no sign bit
+  if (mode != FP4_PLAIN && mode != FP4_RAZER && mode != FP4_RAZER_W) return FP4_ERR_UNSUPPORTED;
+  if (mode != FP4_PLAIN && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;  // E8M0 has no free bit
   if (flags & ~(FP4_FLAG_TENSOR_SCALE_GIVEN | FP4_FLAG_SCALE_OCP_FLOOR)) return FP4_ERR_UNSUPPORTED;
   if ((flags & FP4_FLAG_TENSOR_SCALE_GIVEN) && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
   if ((flags & FP4_FLAG_SCALE_OCP_FLOOR) && format == FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
@@ -80,8 +80,10 @@ int fp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, i
       fp4::launch_mx_quant(s, (flags & FP4_FLAG_SCALE_OCP_FLOOR) != 0, format == FP4_MXINT4, x_bf16,
                            codes, scales, st);
   } else {
-    if (need_scale) fp4::launch_nv_tensor_scale(s, x_bf16, codes, tensor_scale, st);
-    if (!empty) fp4::launch_nv_quant(s, mode == FP4_RAZER, x_bf16, codes, scales, tensor_scale, st);
+    if (need_scale)
+      fp4::launch_nv_tensor_scale(s, x_bf16, codes, mode == FP4_RAZER_W ? 180.0f : 2688.0f,
+                                  tensor_scale, st);
+    if (!empty) fp4::launch_nv_quant(s, mode, x_bf16, codes, scales, tensor_scale, st);
   }
   return launch_status();
 }
@@ -92,9 +94,10 @@ int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int6
                    void* stream) {
   if (!known_format(format)) return FP4_ERR_UNSUPPORTED;
   if (block != block_of(format)) return FP4_ERR_UNSUPPORTED;
-  if (mode != FP4_PLAIN && mode != FP4_RAZER) return FP4_ERR_UNSUPPORTED;
-  if (mode == FP4_RAZER && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
+  if (mode != FP4_PLAIN && mode != FP4_RAZER && mode != FP4_RAZER_W) return FP4_ERR_UNSUPPORTED;
+  if (mode != FP4_PLAIN && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
   if (hadamard != 0 && hadamard != block) return FP4_ERR_UNSUPPORTED;
+  if (mode == FP4_RAZER_W && (hadamard || perm)) return FP4_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 0 || cols % block != 0) return FP4_ERR_SHAPE;
   if ((hadamard || perm) && cols % 32 != 0) return FP4_ERR_SHAPE;  // 32-element segments
   if (ld_out < cols || ld_codes < cols / 2 || ld_scales < cols / block) return FP4_ERR_SHAPE;
@@ -117,7 +120,7 @@ int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int6
     fp4::launch_nv_dequant_unrotate(s, perm, hadamard, mode == FP4_RAZER, codes, scales,
                                     tensor_scale, out_bf16, st);
   else
-    fp4::launch_dequant(s, format, mode == FP4_RAZER, codes, scales, tensor_scale, out_bf16, st);
+    fp4::launch_dequant(s, format, mode, codes, scales, tensor_scale, out_bf16, st);
   return launch_status();
 }
 
@@ -129,6 +132,7 @@ int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t 
   int rc = check_quant_args(x_bf16, rows, cols, ld_x, format, block, mode, flags, codes, ld_codes,
                             scales, ld_scales, tensor_scale);
   if (rc != FP4_OK) return rc;
+  if (mode == FP4_RAZER_W) return FP4_ERR_UNSUPPORTED;  // a weight format; rotation is online
   if (hadamard != 0 && hadamard != block) return FP4_ERR_UNSUPPORTED;
   if (cols % 32 != 0) return FP4_ERR_SHAPE;  // the kernels work on 32-element segments
   if (perm && cols > fp4::kMaxPermCols) return FP4_ERR_UNSUPPORTED;
@@ -159,7 +163,8 @@ int fp4_gemm(const void* a_codes, int64_t ld_a, const void* a_scales, int64_t ld
   if (format != FP4_MXFP4 && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
   if (out_dtype != FP4_OUT_F32 && out_dtype != FP4_OUT_BF16) return FP4_ERR_UNSUPPORTED;
   if (mode_a != FP4_PLAIN && mode_a != FP4_RAZER) return FP4_ERR_UNSUPPORTED;
-  if (mode_b != FP4_PLAIN && mode_b != FP4_RAZER) return FP4_ERR_UNSUPPORTED;
+  if (mode_b != FP4_PLAIN && mode_b != FP4_RAZER && mode_b != FP4_RAZER_W)
+    return FP4_ERR_UNSUPPORTED;
   if (format == FP4_MXFP4 && (mode_a != FP4_PLAIN || mode_b != FP4_PLAIN))
     return FP4_ERR_UNSUPPORTED;
   const int blk = block_of(format);
@@ -187,8 +192,8 @@ int fp4_gemm(const void* a_codes, int64_t ld_a, const void* a_scales, int64_t ld
     fp4::launch_mx_gemm(m, n, k, a_codes, ld_a, a_scales, ld_sa, b_codes, ld_b, b_scales, ld_sb,
                         c, ld_c, out_dtype == FP4_OUT_BF16, st);
   else
-    fp4::launch_nv_gemm(m, n, k, a_codes, ld_a, a_scales, ld_sa, a_ts, mode_a == FP4_RAZER,
-                        b_codes, ld_b, b_scales, ld_sb, b_ts, mode_b == FP4_RAZER, c, ld_c,
+    fp4::launch_nv_gemm(m, n, k, a_codes, ld_a, a_scales, ld_sa, a_ts, mode_a, b_codes, ld_b,
+                        b_scales, ld_sb, b_ts, mode_b, c, ld_c,
                         out_dtype == FP4_OUT_BF16, st);
   return launch_status();
 }

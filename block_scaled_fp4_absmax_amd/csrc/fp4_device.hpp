@@ -278,4 +278,63 @@ __device__ __forceinline__ uint32_t razer_flag(float g, int k) {
   return ((__float_as_uint(g) + 0x7FFFFFFFu) >> 31) << (4 * k + 3);
 }
 
+// ---- RaZeR for weights --------------------------------------------------------
+// Weights take a 6-bit E3M3 block scale ("fn"-style: bias 3, subnormals
+// m 2^-5, largest 30), freeing two bits that select the special value of code
+// 0x8 among {+5, -5, +2.5, -2.5} (selector 0..3 in bits 6-7 of the scale byte;
+// +-2.5 is the second pair, chosen offline). s_t = amax_t / 180 maps the
+// largest block onto 6 * 30.
+constexpr float kWeightPair = 2.5f;
+
+// Nearest E3M3 code to s >= 0, ties to the even code, saturating at 30: as
+// e4m3_encode with 3 exponent bits (subnormals below 2^-2, rebias 127 -> 3).
+__device__ __forceinline__ uint32_t e3m3_encode(float s) {
+  const uint32_t sub = (uint32_t)__builtin_rintf(s * 32.0f);
+  uint32_t u = __float_as_uint(s);
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  const uint32_t nrm = (u >> 20) - (124u << 3);
+  const uint32_t c = s < 0x1p-2f ? sub : nrm;
+  return s <= 30.0f ? c : 63u;
+}
+
+__device__ __forceinline__ float e3m3_decode(uint32_t c) {
+  const uint32_t mag = c & 63u;
+  const float nrm = __uint_as_float((((mag >> 3) + 124u) << 23) | ((mag & 7u) << 20));
+  const float sub = (float)mag * 0x1p-5f;
+  return mag >= 8u ? nrm : sub;
+}
+
+// E3M3 block code of a block maximum (the quotient as in nv_block_code).
+__device__ __forceinline__ uint32_t nvw_block_code(float amax, const NvScale& n) {
+  float s_raw;
+  if (__builtin_expect(n.rcp_quotient, 1)) {
+    const float q = amax * n.y6;
+    s_raw = __builtin_fmaf(__builtin_fmaf(-q, n.d6, amax), n.y6, q);
+  } else {
+    s_raw = amax / n.d6;
+  }
+  return e3m3_encode(s_raw);
+}
+
+// r[c] = RN(1 / RN(e3m3(c) * s_t)) for the 64 codes (threads 0..63).
+__device__ __forceinline__ void nvw_rcp_table(float* tab, float s_t) {
+  if (threadIdx.x < 64) tab[threadIdx.x] = 1.0f / (e3m3_decode(threadIdx.x) * s_t);
+}
+
+// Squared-error gain of the special value 2.5 (same sign): its standard
+// neighbours 2 and 3 are 0.5 away, so with d = |y| - 2.5 the gain is
+// 0.25 - |d| on |d| < 0.25 and none outside. Exact in fp32: where it is
+// positive |y| lies in [2, 4) (d a multiple of 2^-22, Sterbenz), and a block
+// sum of 16 (at most 4, on the 2^-22 grid) is exact too.
+__device__ __forceinline__ float razer_gain_pair2(float y) {
+  const float d = __builtin_fabsf(y) - kWeightPair;
+  return __builtin_amdgcn_fmed3f(0.25f - __builtin_fabsf(d), 0.0f, 0.25f);
+}
+
+__device__ __forceinline__ float weight_special(uint32_t byte) {
+  const uint32_t sel = (byte >> 6) & 3u;
+  const float mag = sel >= 2u ? kWeightPair : 5.0f;
+  return (sel & 1u) ? -mag : mag;
+}
+
 }  // namespace fp4

@@ -1,5 +1,5 @@
-// gemm_nv.hip -- C = s_a s_b (A B^T) with NVFP4 operands, optionally RaZeR,
-// on the bf16 matrix cores.
+// gemm_nv.hip -- C = s_a s_b (A B^T) with NVFP4 operands, optionally RaZeR
+// (and, for the weights B, RaZeR's weight variant), on the bf16 matrix cores.
 //
 // "RaZeR: Pushing the Limits of NVFP4 Quantization with Redundant Zero
 // Remapping", technical summary sec. 2.3: GEMM kernels that take the
@@ -10,9 +10,9 @@
 //
 // gfx950's block-scaled FP4 matrix instructions take E8M0 scales per 32
 // elements; NVFP4's are E4M3 per 16, so they cannot be fed to it. Instead
-// each element is decoded exactly: an E2M1 value (or the block's +-5) has at
-// most 3 significant bits and an E4M3 scale 4, so value x scale has at most 7
-// and is a bf16, between 2^-10 and 2688. The work-group decodes each stage
+// each element is decoded exactly: an E2M1 value (or the block's +-5, +-2.5)
+// has at most 3 significant bits and an E4M3 or E3M3 scale 4, so value x
+// scale has at most 7 and is a bf16, between 2^-10 and 2688. The work-group decodes each stage
 // once, on its way into LDS, and the waves run v_mfma_f32_32x32x16_bf16 on the
 // decoded tiles (products of bf16 are exact in fp32); the tensor scales
 // multiply once in the epilogue. RaZeR needs no second pass: code 0x8 simply
@@ -84,8 +84,10 @@ struct NvOperand {
     }
   }
 
-  // decode to bf16 and write the chunk's four 16-byte LDS chunks
-  template <bool kRazer>
+  // decode to bf16 and write the chunk's four 16-byte LDS chunks; kMode 0
+  // plain, 1 RaZeR (E4M3 scale, +-5), 2 RaZeR for weights (E3M3 scale,
+  // {+5, -5, +2.5, -2.5})
+  template <int kMode>
   __device__ __forceinline__ void store(uint8_t* lds) const {
     const uint32_t t = threadIdx.x;
 #pragma unroll
@@ -95,8 +97,10 @@ struct NvOperand {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {  // eight elements: block j / 2 of the chunk
         const uint32_t sbyte = (s[i] >> (8 * (j / 2))) & 0xFFu;
-        const float sc = e4m3_decode(kRazer ? (sbyte & 0x7Fu) : sbyte);
-        const float special = (sbyte & 0x80u) ? -5.0f : 5.0f;
+        const float sc =
+            kMode == 2 ? e3m3_decode(sbyte) : e4m3_decode(kMode ? (sbyte & 0x7Fu) : sbyte);
+        const float special =
+            kMode == 2 ? weight_special(sbyte) : (sbyte & 0x80u) ? -5.0f : 5.0f;
         float v[8];
 #define FP4_NV_DEC2(sel)                                                              \
   {                                                                                   \
@@ -109,7 +113,7 @@ struct NvOperand {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           // RaZeR: code 0x8, the only code that decodes to -0.0, is the special
-          if (kRazer && __float_as_uint(v[e]) == 0x80000000u) v[e] = special;
+          if (kMode && __float_as_uint(v[e]) == 0x80000000u) v[e] = special;
           v[e] *= sc;  // exact: at most 7 significant bits
         }
         const u32x4_t o{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
@@ -120,7 +124,7 @@ struct NvOperand {
   }
 };
 
-template <int WM, int WN, bool kRazerA, bool kRazerB, bool kBf16Out>
+template <int WM, int WN, int kModeA, int kModeB, bool kBf16Out>
 __global__ __launch_bounds__(256) void nv_gemm_kernel(NvGemmArgs g) {
   constexpr int BM = 64 * WM, BN = 64 * WN;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kRowB];
@@ -179,22 +183,22 @@ __global__ __launch_bounds__(256) void nv_gemm_kernel(NvGemmArgs g) {
   b0.load(q.b, q.sb, g.ld_b, g.ld_sb, 0, g.k);
   a1.load(q.a, q.sa, g.ld_a, g.ld_sa, kBK, g.k);
   b1.load(q.b, q.sb, g.ld_b, g.ld_sb, kBK, g.k);
-  a0.template store<kRazerA>(lds_a[0]);
-  b0.template store<kRazerB>(lds_b[0]);
+  a0.template store<kModeA>(lds_a[0]);
+  b0.template store<kModeB>(lds_b[0]);
   __syncthreads();
   int32_t s = 0;
   for (; s + 1 < stages; s += 2) {
     a0.load(q.a, q.sa, g.ld_a, g.ld_sa, (s + 2) * kBK, g.k);
     b0.load(q.b, q.sb, g.ld_b, g.ld_sb, (s + 2) * kBK, g.k);
     mma(0);
-    a1.template store<kRazerA>(lds_a[1]);
-    b1.template store<kRazerB>(lds_b[1]);
+    a1.template store<kModeA>(lds_a[1]);
+    b1.template store<kModeB>(lds_b[1]);
     __syncthreads();
     a1.load(q.a, q.sa, g.ld_a, g.ld_sa, (s + 3) * kBK, g.k);
     b1.load(q.b, q.sb, g.ld_b, g.ld_sb, (s + 3) * kBK, g.k);
     mma(1);
-    a0.template store<kRazerA>(lds_a[0]);
-    b0.template store<kRazerB>(lds_b[0]);
+    a0.template store<kModeA>(lds_a[0]);
+    b0.template store<kModeB>(lds_b[0]);
     __syncthreads();
   }
   if (s < stages) mma(0);
@@ -222,39 +226,44 @@ __global__ __launch_bounds__(256) void nv_gemm_kernel(NvGemmArgs g) {
     }
 }
 
-template <int WM, int WN, bool kRa, bool kRb>
+template <int WM, int WN, int kMa, int kMb>
 void nv_launch(const NvGemmArgs& g, bool bf16_out, hipStream_t st) {
   const int64_t tiles = (((int64_t)g.m + 64 * WM - 1) / (64 * WM)) *
                         (((int64_t)g.n + 64 * WN - 1) / (64 * WN));
   if (bf16_out)
-    hipLaunchKernelGGL((nv_gemm_kernel<WM, WN, kRa, kRb, true>), dim3((unsigned)tiles), dim3(256),
+    hipLaunchKernelGGL((nv_gemm_kernel<WM, WN, kMa, kMb, true>), dim3((unsigned)tiles), dim3(256),
                        0, st, g);
   else
-    hipLaunchKernelGGL((nv_gemm_kernel<WM, WN, kRa, kRb, false>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((nv_gemm_kernel<WM, WN, kMa, kMb, false>), dim3((unsigned)tiles),
                        dim3(256), 0, st, g);
 }
 
-template <bool kRa, bool kRb>
+template <int kMa, int kMb>
 void nv_tiles(const NvGemmArgs& g, bool bf16_out, hipStream_t st) {
   if (g.m >= 2048 && g.n >= 2048)
-    nv_launch<4, 4, kRa, kRb>(g, bf16_out, st);
+    nv_launch<4, 4, kMa, kMb>(g, bf16_out, st);
   else
-    nv_launch<2, 2, kRa, kRb>(g, bf16_out, st);
+    nv_launch<2, 2, kMa, kMb>(g, bf16_out, st);
+}
+
+template <int kMa>
+void nv_modes_b(const NvGemmArgs& g, int mode_b, bool bf16_out, hipStream_t st) {
+  if (mode_b == 2) nv_tiles<kMa, 2>(g, bf16_out, st);
+  else if (mode_b == 1) nv_tiles<kMa, 1>(g, bf16_out, st);
+  else nv_tiles<kMa, 0>(g, bf16_out, st);
 }
 
 }  // namespace
 
 void launch_nv_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a, const void* sa,
-                    int64_t ld_sa, const float* ta, bool razer_a, const void* b, int64_t ld_b,
-                    const void* sb, int64_t ld_sb, const float* tb, bool razer_b, void* c,
+                    int64_t ld_sa, const float* ta, int mode_a, const void* b, int64_t ld_b,
+                    const void* sb, int64_t ld_sb, const float* tb, int mode_b, void* c,
                     int64_t ld_c, bool bf16_out, hipStream_t st) {
   NvGemmArgs g{static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(sa),
                static_cast<const uint8_t*>(b), static_cast<const uint8_t*>(sb), ta, tb, c,
                ld_a, ld_sa, ld_b, ld_sb, ld_c, (int32_t)m, (int32_t)n, (int32_t)k};
-  if (razer_a && razer_b) nv_tiles<true, true>(g, bf16_out, st);
-  if (razer_a && !razer_b) nv_tiles<true, false>(g, bf16_out, st);
-  if (!razer_a && razer_b) nv_tiles<false, true>(g, bf16_out, st);
-  if (!razer_a && !razer_b) nv_tiles<false, false>(g, bf16_out, st);
+  if (mode_a == 1) nv_modes_b<1>(g, mode_b, bf16_out, st);
+  else nv_modes_b<0>(g, mode_b, bf16_out, st);
 }
 
 }  // namespace fp4

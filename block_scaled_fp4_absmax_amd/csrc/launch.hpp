@@ -32,15 +32,17 @@ struct Shape {
 void launch_mx_quant(const Shape& s, bool floor_rule, bool mxint, const void* x, void* codes,
                      void* scales, hipStream_t st);
 // Writes s_t; uses the code buffer as scratch for per-work-group partial maxima.
-void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float* ts,
+// top: 2688 (E4M3 scales) or 180 (E3M3 scales of RaZeR for weights).
+void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float top, float* ts,
                             hipStream_t st);
 // s_t from nparts amax partials, partial i in the code slot of chunk i (row-major
 // chunks of 8 elements, 4 code bytes each).
 void launch_nv_scale_from_partials(const Shape& s, void* codes, uint32_t nparts, float* ts,
                                    hipStream_t st);
-void launch_nv_quant(const Shape& s, bool razer, const void* x, void* codes, void* scales,
+// mode: 0 plain, 1 RaZeR, 2 RaZeR for weights (E3M3 scale, four specials).
+void launch_nv_quant(const Shape& s, int mode, const void* x, void* codes, void* scales,
                      const float* ts, hipStream_t st);
-void launch_dequant(const Shape& s, int format, bool razer, const void* codes, const void* scales,
+void launch_dequant(const Shape& s, int format, int mode, const void* codes, const void* scales,
                     const float* ts, void* out, hipStream_t st);
 // MXFP4, or MXINT4 with mxint.
 void launch_mx_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, bool floor_rule,
@@ -66,9 +68,10 @@ void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a
                     void* c, int64_t ld_c, bool bf16_out, hipStream_t st);
 // C = ta tb (A B^T), NVFP4 operands (codes [rows, K/2], E4M3 scales
 // [rows, K/16], RaZeR per operand), decoded exactly to bf16 for the MFMA.
+// mode_a: 0 plain or 1 RaZeR; mode_b: 0, 1 or 2 (RaZeR for weights).
 void launch_nv_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a, const void* sa,
-                    int64_t ld_sa, const float* ta, bool razer_a, const void* b, int64_t ld_b,
-                    const void* sb, int64_t ld_sb, const float* tb, bool razer_b, void* c,
+                    int64_t ld_sa, const float* ta, int mode_a, const void* b, int64_t ld_b,
+                    const void* sb, int64_t ld_sb, const float* tb, int mode_b, void* c,
                     int64_t ld_c, bool bf16_out, hipStream_t st);
 void launch_channel_energy(int64_t rows, int64_t cols, int64_t ld_x, const void* x, float* energy,
                            hipStream_t st);

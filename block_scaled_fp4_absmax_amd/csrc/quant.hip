@@ -138,9 +138,12 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint16_t* __res
 // single round trip.
 constexpr int kScaleThreads = 1024;
 
+// top: the largest scaled block maximum, 6 * 448 = 2688 (E4M3 scales) or
+// 6 * 30 = 180 (E3M3 scales of RaZeR for weights).
 template <bool kFlat>
 __global__ __launch_bounds__(kScaleThreads) void nv_tensor_scale_kernel(
-    const uint8_t* __restrict__ codes, uint32_t nparts, Geom g, float* __restrict__ ts) {
+    const uint8_t* __restrict__ codes, uint32_t nparts, Geom g, float top,
+    float* __restrict__ ts) {
   __shared__ uint32_t red[kScaleThreads / 64];
   uint32_t m = 0;
   for (uint32_t i0 = threadIdx.x; i0 < nparts; i0 += 16 * kScaleThreads) {
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(kScaleThreads) void nv_tensor_scale_kernel(
     uint32_t r = red[0];
     for (int i = 1; i < kScaleThreads / 64; ++i) r = max(r, red[i]);
     const float amax = __uint_as_float(r);
-    *ts = amax == 0.0f ? 1.0f : amax / 2688.0f;
+    *ts = amax == 0.0f ? 1.0f : amax / top;
   }
 }
 
@@ -175,12 +178,15 @@ __global__ void nv_unit_scale_kernel(float* ts) { *ts = 1.0f; }
 
 // One NVFP4 chunk (half a block; the block spans lanes l and l ^ 1): the scale
 // arithmetic is in fp4_device.hpp (nv_block_code, nv_rcp_table).
-template <bool kRazer>
+// kMode: 0 plain NVFP4, 1 RaZeR (E4M3 scale, +-5 by the scale's sign bit),
+// 2 RaZeR for weights (E3M3 scale, {+5, -5, +2.5, -2.5} by bits 6-7).
+template <int kMode>
 __device__ __forceinline__ void nv_quant_chunk(u32x4_t d, const NvScale& ns, const float* rcp_tab,
                                                uint32_t& w, uint32_t& byte) {
   uint32_t m = absmax8_bf16(d);
   m = max(m, dpp_xor1(m));
-  const uint32_t sb = nv_block_code(__uint_as_float(m << 16), ns);
+  const float amax = __uint_as_float(m << 16);
+  const uint32_t sb = kMode == 2 ? nvw_block_code(amax, ns) : nv_block_code(amax, ns);
   w = 0;
   byte = 0;
   if (sb != 0u) {
@@ -192,7 +198,7 @@ __device__ __forceinline__ void nv_quant_chunk(u32x4_t d, const NvScale& ns, con
     y[6] = bf16_lo(d.w) * r; y[7] = bf16_hi(d.w) * r;
     w = cvt8_f32(y, 1.0f);
     byte = sb;
-    if (kRazer) {
+    if constexpr (kMode == 1) {
       // selector = [gains of negative elements exceed those of positive ones]
       float dsum = 0.0f;
       uint32_t cm = 0;
@@ -206,13 +212,38 @@ __device__ __forceinline__ void nv_quant_chunk(u32x4_t d, const NvScale& ns, con
       const uint32_t sel = dsum > 0.0f ? 1u : 0u;
       w = razer_apply(w, cm, sel);
       byte |= sel << 7;
+    } else if constexpr (kMode == 2) {
+      // block gains of the four specials (exact sums); the largest wins,
+      // ties to the lower selector
+      float g[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // +5, -5, +2.5, -2.5
+      uint32_t cm5 = 0, cm2 = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float g5 = razer_gain(y[k]), g2 = razer_gain_pair2(y[k]);
+        const bool neg = __float_as_uint(y[k]) >> 31;
+        g[0] += neg ? 0.0f : g5;
+        g[1] += neg ? g5 : 0.0f;
+        g[2] += neg ? 0.0f : g2;
+        g[3] += neg ? g2 : 0.0f;
+        cm5 |= razer_flag(g5, k);
+        cm2 |= razer_flag(g2, k);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g[i] += dpp_xor1f(g[i]);
+      uint32_t sel = 0;
+      float best = g[0];
+      if (g[1] > best) { best = g[1]; sel = 1; }
+      if (g[2] > best) { best = g[2]; sel = 2; }
+      if (g[3] > best) { sel = 3; }
+      w = razer_apply(w, sel >= 2u ? cm2 : cm5, sel & 1u);
+      byte |= sel << 6;
     }
   }
 }
 
 // kFull: the work-group's kThreads * kUnroll chunks all exist (every
 // work-group but the last), so loads and stores need no bounds check.
-template <bool kFlat, bool kRazer, bool kFull>
+template <bool kFlat, int kMode, bool kFull>
 __device__ __forceinline__ void nv_quant_pass(const uint16_t* __restrict__ x,
                                               uint8_t* __restrict__ codes,
                                               uint8_t* __restrict__ scales, const float* rcp_tab,
@@ -224,13 +255,13 @@ __device__ __forceinline__ void nv_quant_pass(const uint16_t* __restrict__ x,
   for (int u = 0; u < kUnroll; ++u) {
     if (!kFull && base + u * kThreads >= g.n) continue;
     uint32_t w, byte;
-    nv_quant_chunk<kRazer>(d[u], ns, rcp_tab, w, byte);
+    nv_quant_chunk<kMode>(d[u], ns, rcp_tab, w, byte);
     __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + co[u]));
     if (leader) scales[so[u]] = (uint8_t)byte;
   }
 }
 
-template <bool kFlat, bool kRazer>
+template <bool kFlat, int kMode>
 __global__ __launch_bounds__(kThreads) void nv_quant_kernel(const uint16_t* __restrict__ x,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
@@ -257,12 +288,15 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(const uint16_t* __re
   }
   const float s_t = *ts;
   const NvScale ns = nv_scale_setup(s_t);
-  nv_rcp_table(rcp_tab, s_t);
+  if (kMode == 2)
+    nvw_rcp_table(rcp_tab, s_t);
+  else
+    nv_rcp_table(rcp_tab, s_t);
   __syncthreads();
   if (full)
-    nv_quant_pass<kFlat, kRazer, true>(x, codes, scales, rcp_tab, ns, g, d, co, so);
+    nv_quant_pass<kFlat, kMode, true>(x, codes, scales, rcp_tab, ns, g, d, co, so);
   else
-    nv_quant_pass<kFlat, kRazer, false>(x, codes, scales, rcp_tab, ns, g, d, co, so);
+    nv_quant_pass<kFlat, kMode, false>(x, codes, scales, rcp_tab, ns, g, d, co, so);
 }
 
 // ------------------------------------------------------------ dequantize ----
@@ -303,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __r
   }
 }
 
-template <bool kFlat, bool kRazer>
+template <bool kFlat, int kMode>
 __global__ __launch_bounds__(kThreads) void nv_dequant_kernel(const uint8_t* __restrict__ codes,
                                                               const uint8_t* __restrict__ scales,
                                                               const float* __restrict__ ts,
@@ -328,8 +362,8 @@ __global__ __launch_bounds__(kThreads) void nv_dequant_kernel(const uint8_t* __r
       uint32_t v = base + u * stride;
       if (v >= g.n) continue;
       const uint32_t byte = sb[u];
-      const float s_eff = e4m3_decode(kRazer ? (byte & 0x7Fu) : byte) * s_t;
-      const float special = (byte & 0x80u) ? -5.0f : 5.0f;
+      const float s_eff = (kMode == 2 ? e3m3_decode(byte) : e4m3_decode(kMode ? (byte & 0x7Fu) : byte)) * s_t;
+      const float special = kMode == 2 ? weight_special(byte) : (byte & 0x80u) ? -5.0f : 5.0f;
       float val[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -341,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void nv_dequant_kernel(const uint8_t* __r
         val[2 * k] = p.x;
         val[2 * k + 1] = p.y;
       }
-      if (kRazer) {  // code 8 is the only code that decodes to -0.0
+      if (kMode) {  // code 8 is the only code that decodes to -0.0
 #pragma unroll
         for (int k = 0; k < 8; ++k)
           if (__float_as_uint(val[k]) == 0x80000000u) val[k] = special;
@@ -399,7 +433,7 @@ void launch_mx_quant(const Shape& s, bool floor_rule, bool mxint, const void* x,
   else mx_quant_variants<false>(s, floor_rule, x, codes, scales, st);
 }
 
-void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float* ts,
+void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float top, float* ts,
                             hipStream_t st) {
   Geom g = make_geom(s, 16);
   if (g.n == 0) {
@@ -414,11 +448,11 @@ void launch_nv_tensor_scale(const Shape& s, const void* x, void* codes, float* t
   if (flat) {
     FP4_LAUNCH((nv_amax_kernel<true>), grid, st, xp, cp, g);
     hipLaunchKernelGGL((nv_tensor_scale_kernel<true>), dim3(1), dim3(kScaleThreads), 0, st, cp,
-                       (uint32_t)grid, g, ts);
+                       (uint32_t)grid, g, top, ts);
   } else {
     FP4_LAUNCH((nv_amax_kernel<false>), grid, st, xp, cp, g);
     hipLaunchKernelGGL((nv_tensor_scale_kernel<false>), dim3(1), dim3(kScaleThreads), 0, st, cp,
-                       (uint32_t)grid, g, ts);
+                       (uint32_t)grid, g, top, ts);
   }
 }
 
@@ -430,24 +464,30 @@ void launch_nv_scale_from_partials(const Shape& s, void* codes, uint32_t nparts,
   }
   Geom g = make_geom(s, 16);
   hipLaunchKernelGGL((nv_tensor_scale_kernel<false>), dim3(1), dim3(kScaleThreads), 0, st,
-                     static_cast<const uint8_t*>(codes), nparts, g, ts);
+                     static_cast<const uint8_t*>(codes), nparts, g, 2688.0f, ts);
 }
 
-void launch_nv_quant(const Shape& s, bool razer, const void* x, void* codes, void* scales,
-                     const float* ts, hipStream_t st) {
+template <int kMode>
+static void nv_quant_variants(const Shape& s, const void* x, void* codes, void* scales,
+                              const float* ts, hipStream_t st) {
   Geom g = make_geom(s, 16);
   const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / 16;
   const int grid = grid_for(g.n);
   auto xp = static_cast<const uint16_t*>(x);
   auto cp = static_cast<uint8_t*>(codes);
   auto sp = static_cast<uint8_t*>(scales);
-  if (flat && razer) FP4_LAUNCH((nv_quant_kernel<true, true>), grid, st, xp, cp, sp, ts, g);
-  if (flat && !razer) FP4_LAUNCH((nv_quant_kernel<true, false>), grid, st, xp, cp, sp, ts, g);
-  if (!flat && razer) FP4_LAUNCH((nv_quant_kernel<false, true>), grid, st, xp, cp, sp, ts, g);
-  if (!flat && !razer) FP4_LAUNCH((nv_quant_kernel<false, false>), grid, st, xp, cp, sp, ts, g);
+  if (flat) FP4_LAUNCH((nv_quant_kernel<true, kMode>), grid, st, xp, cp, sp, ts, g);
+  else FP4_LAUNCH((nv_quant_kernel<false, kMode>), grid, st, xp, cp, sp, ts, g);
 }
 
-void launch_dequant(const Shape& s, int format, bool razer, const void* codes, const void* scales,
+void launch_nv_quant(const Shape& s, int mode, const void* x, void* codes, void* scales,
+                     const float* ts, hipStream_t st) {
+  if (mode == 2) nv_quant_variants<2>(s, x, codes, scales, ts, st);
+  else if (mode == 1) nv_quant_variants<1>(s, x, codes, scales, ts, st);
+  else nv_quant_variants<0>(s, x, codes, scales, ts, st);
+}
+
+void launch_dequant(const Shape& s, int format, int mode, const void* codes, const void* scales,
                     const float* ts, void* out, hipStream_t st) {
   const int block = format == 1 ? 16 : 32;
   Geom g = make_geom(s, block);
@@ -464,10 +504,13 @@ void launch_dequant(const Shape& s, int format, bool razer, const void* codes, c
     if (flat) FP4_LAUNCH((mx_dequant_kernel<true, true>), grid, st, cp, sp, op, g);
     else FP4_LAUNCH((mx_dequant_kernel<false, true>), grid, st, cp, sp, op, g);
   } else {
-    if (flat && razer) FP4_LAUNCH((nv_dequant_kernel<true, true>), grid, st, cp, sp, ts, op, g);
-    if (flat && !razer) FP4_LAUNCH((nv_dequant_kernel<true, false>), grid, st, cp, sp, ts, op, g);
-    if (!flat && razer) FP4_LAUNCH((nv_dequant_kernel<false, true>), grid, st, cp, sp, ts, op, g);
-    if (!flat && !razer) FP4_LAUNCH((nv_dequant_kernel<false, false>), grid, st, cp, sp, ts, op, g);
+#define FP4_NV_DQ(M)                                                                   \
+  if (mode == M) {                                                                     \
+    if (flat) FP4_LAUNCH((nv_dequant_kernel<true, M>), grid, st, cp, sp, ts, op, g);   \
+    else FP4_LAUNCH((nv_dequant_kernel<false, M>), grid, st, cp, sp, ts, op, g);       \
+  }
+    FP4_NV_DQ(0) FP4_NV_DQ(1) FP4_NV_DQ(2)
+#undef FP4_NV_DQ
   }
 }
 

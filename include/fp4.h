@@ -57,7 +57,7 @@ extern "C" {
 #define FP4_VERSION 1
 
 enum fp4_format { FP4_MXFP4 = 0, FP4_NVFP4 = 1, FP4_MXINT4 = 2 };
-enum fp4_mode { FP4_PLAIN = 0, FP4_RAZER = 1 };
+enum fp4_mode { FP4_PLAIN = 0, FP4_RAZER = 1, FP4_RAZER_W = 2 };
 
 /* NVFP4: read tensor_scale as an input instead of computing it. */
 #define FP4_FLAG_TENSOR_SCALE_GIVEN 1u
@@ -109,11 +109,20 @@ const char* fp4_status_string(int status);
  * the block takes the one with the smaller sum of squared errors in y (equal:
  * +5), an element takes the special code only when strictly closer to it.
  *
+ * RaZeR for weights (FP4_RAZER_W; [RaZeR] sec. 2.1 and 2.2; NVFP4 only):
+ * the block scale is E3M3 (6 bits: bias 3, subnormals m 2^-5, largest 30,
+ * no Inf/NaN; reading, the pages give the width only), s_t = amax / 180 (6 *
+ * 30) unless given, and the two freed bits (scale byte bits 6-7) select code
+ * 0x8's value among {+5, -5, +2.5, -2.5}; +-2.5, the second pair, is not on
+ * the pages and was chosen offline as the best multiple of 0.5 on synthetic
+ * LLM weights. The block takes the special of least squared error (ties: the
+ * lower selector). Not available with rotation.
+ *
  *  x_bf16       device, bf16 [rows, ld_x]; 16-byte aligned, ld_x % 8 == 0
  *  rows, cols   rows >= 0, cols >= 0, cols % block == 0; rows * cols / 8 < 2^31
  *  format       FP4_MXFP4, FP4_NVFP4 or FP4_MXINT4
  *  block        32 for MXFP4 and MXINT4, 16 for NVFP4
- *  mode         FP4_PLAIN, or FP4_RAZER with NVFP4
+ *  mode         FP4_PLAIN, or FP4_RAZER / FP4_RAZER_W with NVFP4
  *  flags        FP4_FLAG_* bits valid for the format
  *  codes        device, uint8 [rows, ld_codes]; 4-byte aligned, ld_codes % 4 == 0,
  *               ld_codes >= cols / 2
@@ -143,6 +152,8 @@ int fp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, i
  * The inverse-rotated values are computed in fp32 and rounded once to bf16:
  * the transform of the decoded grid values is exact, and the block scale
  * (MXFP4 2^e, NVFP4 s_eff) multiplies once, after it.
+ * FP4_RAZER_W: s_eff = e3m3(byte & 63) * s_t and code 0x8 decodes to
+ * {+5, -5, +2.5, -2.5}[byte >> 6] (no inverse rotation).
  *
  *  codes, scales, tensor_scale  as produced by fp4_quantize / fp4_rotate_quantize
  *  rows, cols, format, block, mode  as for fp4_quantize
@@ -217,7 +228,8 @@ int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t 
  *                       MXFP4: 4-byte aligned, ld_s % 4 == 0; NVFP4: 2-byte
  *                       aligned, ld_s % 2 == 0 (bytes past k / block unused)
  *  a_ts, b_ts           NVFP4: device fp32[1] tensor scales; MXFP4: ignored
- *  mode_a, mode_b       FP4_PLAIN, or FP4_RAZER (NVFP4 only)
+ *  mode_a, mode_b       FP4_PLAIN, or (NVFP4 only) FP4_RAZER; mode_b may also
+ *                       be FP4_RAZER_W (E3M3 scale, four specials: weights)
  *  m, n, k              >= 0, < 2^31; k % 32 == 0 (m or n zero: no work;
  *                       k zero: C = 0)
  *  format               FP4_MXFP4 or FP4_NVFP4
