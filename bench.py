@@ -364,6 +364,13 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     ms = timed(torch, lambda i: fp4.dequantize(cs[i % m], ss[i % m], fp4.NVFP4, fp4.RAZER,
                                                tss[i % m], out=ob), 40, 5)
     out["c2_nvfp4_razer_dequantize"] = gbs(ms, el2, B_NV)
+    ms = timed(torch, lambda i: fp4.quantize(ys[i % m], fp4.NVFP4, fp4.RAZER_W,
+                                             tensor_scale=tss[i % m], codes=cs[i % m],
+                                             scales=ss[i % m]), 40, 5)
+    out["c2_nvfp4_razer_w_quantize_scale_given"] = gbs(ms, el2, B_NV)
+    cw, sw, tw = fp4.quantize(ys[0], fp4.NVFP4, fp4.RAZER_W)
+    xw = fp4.dequantize(cw, sw, fp4.NVFP4, fp4.RAZER_W, tw)
+    out["c2_sqnr_db_razer_w"] = round(sqnr_db(torch, ys[0].float(), xw.float()), 3)
     cp, sp, tp = fp4.quantize(ys[0], fp4.NVFP4, fp4.PLAIN)
     xp = fp4.dequantize(cp, sp, fp4.NVFP4, fp4.PLAIN, tp)
     out["c2_sqnr_db_plain_nvfp4"] = round(sqnr_db(torch, ys[0].float(), xp.float()), 3)
@@ -459,11 +466,35 @@ def bench_c5(torch, fp4, inputs, args):
             fp4.dequantize(cs[k], ss[k], fp4.NVFP4, fp4.RAZER, ts[k], out=outs[k])
 
     ms = timed(torch, step, args.steps, args.warmup)
-    num = sum(float((xs[k].double() ** 2).sum()) for k in range(len(xs)))
-    den = sum(float(((xs[k].double() - outs[k].double()) ** 2).sum()) for k in range(len(xs)))
     import math
+
+    def layer_sqnr():
+        num = sum(float((xs[k].double() ** 2).sum()) for k in range(len(xs)))
+        den = sum(float(((xs[k].double() - outs[k].double()) ** 2).sum())
+                  for k in range(len(xs)))
+        return 10 * math.log10(num / den)
+
+    sqnr = layer_sqnr()
+
+    # the same layer with RaZeR for weights (E3M3 scales, four special values)
+    def step_w(i):
+        for k in range(len(xs)):
+            fp4.quantize(xs[k], fp4.NVFP4, fp4.RAZER_W, tensor_scale=ts[k], scale_given=False,
+                         codes=cs[k], scales=ss[k])
+            fp4.dequantize(cs[k], ss[k], fp4.NVFP4, fp4.RAZER_W, ts[k], out=outs[k])
+
+    ms_w = timed(torch, step_w, max(3, args.steps // 2), 1)
+    extras = {"razer_w_layer_round_trip": {"ms": round(ms_w, 4),
+                                           "algorithmic_GBps": round(el * (2 * B_NV + 2) / ms_w
+                                                                     / 1e6, 1),
+                                           "sqnr_db": round(layer_sqnr(), 3)}}
+    for k in range(len(xs)):
+        fp4.quantize(xs[k], fp4.NVFP4, fp4.PLAIN, tensor_scale=ts[k], scale_given=False,
+                     codes=cs[k], scales=ss[k])
+        fp4.dequantize(cs[k], ss[k], fp4.NVFP4, fp4.PLAIN, ts[k], out=outs[k])
+    extras["plain_nvfp4_sqnr_db"] = round(layer_sqnr(), 3)
     per_el = (B_NV + 2) + B_NV
-    res = {"ms": ms, "value": el * 2 / ms / 1e6, "elems": el, "sqnr": 10 * math.log10(num / den),
+    res = {"ms": ms, "value": el * 2 / ms / 1e6, "elems": el, "sqnr": sqnr,
            "config": {"workload": "c5: Llama-70B-shaped decoder-layer weights q,k,v,o,gate,up,"
                                   "down (855,638,016 bf16), NVFP4+RaZeR quantize with tensor "
                                   "amax, then dequantize to bf16", "tensors": 7,
@@ -472,7 +503,7 @@ def bench_c5(torch, fp4, inputs, args):
                         "unit": "GB/s", "frac": el * per_el / ms / 1e6 / HBM_PEAK_GBS,
                         "traffic": None, "kernel": "nv_amax + nv_quant + nv_dequant (7 tensors)",
                         "bytes_per_launch": int(el * per_el)},
-           "extras": {}}
+           "extras": extras}
     return res, None, None
 
 
