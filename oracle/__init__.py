@@ -122,6 +122,9 @@ def _load():
         "orc_rotate": (None, [vp, i64, i64, i64, vp, i32, vp, i64]),
         "orc_unrotate_f64": (None, [vp, i64, i64, i64, vp, i32, vp, i64]),
         "orc_channel_energy": (None, [vp, i64, i64, i64, vp]),
+        "orc_rotate_r": (None, [vp, i64, i64, i64, vp, vp, vp, i64]),
+        "orc_unrotate_r_f64": (None, [vp, i64, i64, i64, vp, vp, vp, i64]),
+        "orc_occupancy": (f64, [vp, i64, i64, i64, vp]),
         "orc_build_perm": (None, [vp, i64, i32, i32, vp]),
         "orc_hadamard_entry": (f64, [i32, i32, i32]),
     }
@@ -447,6 +450,47 @@ def gemm_f64(a_codes: np.ndarray, a_scales: np.ndarray, b_codes: np.ndarray,
     a = decode_exact(a_codes, a_scales, fmt, razer, ts_a, pair)
     b = decode_exact(b_codes, b_scales, fmt, razer if razer_b is None else razer_b, ts_b, pair)
     return a @ b.T
+
+
+def rotate_r(x_bf16: np.ndarray, perm: Optional[np.ndarray], R: np.ndarray) -> np.ndarray:
+    """fp32 [rows, cols]: permute channels, then y_b = R x'_b in every 32-block."""
+    rows, cols = x_bf16.shape
+    R = np.ascontiguousarray(R, np.float64)
+    assert R.shape == (32, 32) and cols % 32 == 0
+    if perm is not None:
+        perm = np.ascontiguousarray(perm, np.int32)
+    out = np.zeros((rows, cols), np.float32)
+    _load().orc_rotate_r(_ptr(x_bf16), rows, cols, _ld(x_bf16), _ptr(perm), _ptr(R), _ptr(out),
+                         cols)
+    return out
+
+
+def rotate_quantize_r(x_bf16: np.ndarray, perm: Optional[np.ndarray], R: np.ndarray):
+    """Permutation and block matrix R, then MXFP4 quantization of the fp32 y."""
+    y = rotate_r(x_bf16, perm, R)
+    codes, scales = mx_quantize_f32(y)
+    return codes, scales, y
+
+
+def unrotate_r_f64(y: np.ndarray, perm: Optional[np.ndarray], R: np.ndarray) -> np.ndarray:
+    y = np.ascontiguousarray(y, np.float64)
+    rows, cols = y.shape
+    R = np.ascontiguousarray(R, np.float64)
+    if perm is not None:
+        perm = np.ascontiguousarray(perm, np.int32)
+    out = np.zeros((rows, cols), np.float64)
+    _load().orc_unrotate_r_f64(_ptr(y), rows, cols, cols, _ptr(perm), _ptr(R), _ptr(out), cols)
+    return out
+
+
+def occupancy(y: np.ndarray) -> Tuple[np.ndarray, float]:
+    """MXFP4 code-book occupancy of fp32 values (fractions per E2M1 magnitude
+    index) and the occupancy-equilibrium loss (squared distance from 1/8)."""
+    y = np.ascontiguousarray(y, np.float32)
+    rows, cols = y.shape
+    hist = np.zeros(8, np.float64)
+    loss = _load().orc_occupancy(_ptr(y), rows, cols, cols, _ptr(hist))
+    return hist, float(loss)
 
 
 def unrotate_f64(y: np.ndarray, perm: Optional[np.ndarray], hadamard: int) -> np.ndarray:

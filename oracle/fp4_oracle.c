@@ -705,6 +705,68 @@ void orc_unrotate_f64(const double* y, int64_t rows, int64_t cols, int64_t ld_y,
 /* Per-channel energy E_c = sum over rows of x_rc^2, in double, row order.
  * It is the diagonal of the (uncentred) activation second-moment matrix whose
  * 32x32 diagonal blocks carry the block variances in [TORQ] sec. 2(a). */
+/* A general orthogonal rotation inside each 32-block ([TORQ] sec. 2(b): the
+ * intra-block rotation is learned): y_b = R x'_b with R [32][32] row-major,
+ * as a dense product in double rounded once to fp32; x' is the permuted row. */
+void orc_rotate_r(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                  const int32_t* perm, const double* R, float* out, int64_t ld_out) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r) {
+    double xp[32];
+    for (int64_t b0 = 0; b0 < cols; b0 += 32) {
+      for (int j = 0; j < 32; ++j) {
+        int64_t src = perm ? perm[b0 + j] : b0 + j;
+        xp[j] = (double)orc_bf16_to_f32(x[r * ld_x + src]);
+      }
+      for (int i = 0; i < 32; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < 32; ++j) acc += R[32 * i + j] * xp[j];
+        out[r * ld_out + b0 + i] = (float)acc;
+      }
+    }
+  }
+}
+
+/* Inverse: x'_b = R^T y_b, then element j of the row goes to column perm[j]. */
+void orc_unrotate_r_f64(const double* y, int64_t rows, int64_t cols, int64_t ld_y,
+                        const int32_t* perm, const double* R, double* out, int64_t ld_out) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r)
+    for (int64_t b0 = 0; b0 < cols; b0 += 32)
+      for (int j = 0; j < 32; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < 32; ++i) acc += R[32 * i + j] * y[r * ld_y + b0 + i];
+        out[r * ld_out + (perm ? perm[b0 + j] : b0 + j)] = acc;
+      }
+}
+
+/* Code-book occupancy ([TORQ] sec. 2(b), the occupancy-equilibrium loss):
+ * quantize every 32-block of y to MXFP4 (default scale rule) and count the
+ * elements per E2M1 magnitude index 0..7; hist receives the 8 fractions.
+ * The loss is their squared distance from the uniform 1/8 (returned). */
+double orc_occupancy(const float* y, int64_t rows, int64_t cols, int64_t ld, double* hist) {
+  double cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b0 = 0; b0 < cols; b0 += 32) {
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        double a = fabs((double)y[r * ld + b0 + i]);
+        if (a > amax) amax = a;
+      }
+      int e = orc_e8m0_scale(amax, 0) - 127;
+      for (int i = 0; i < 32; ++i)
+        cnt[nearest_mag(fabs(ldexp((double)y[r * ld + b0 + i], -e)))] += 1.0;
+    }
+  double n = (double)(rows * (cols / 32) * 32), loss = 0.0;
+  for (int c = 0; c < 8; ++c) {
+    hist[c] = n > 0 ? cnt[c] / n : 0.0;
+    loss += (hist[c] - 0.125) * (hist[c] - 0.125);
+  }
+  return loss;
+}
+
 void orc_channel_energy(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                         double* energy) {
   for (int64_t j = 0; j < cols; ++j) energy[j] = 0.0;

@@ -89,6 +89,11 @@ void orc_rotate(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                 const int32_t* perm, int hadamard, float* out, int64_t ld_out);
 void orc_unrotate_f64(const double* y, int64_t rows, int64_t cols, int64_t ld_y,
                       const int32_t* perm, int hadamard, double* out, int64_t ld_out);
+void orc_rotate_r(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                  const int32_t* perm, const double* R, float* out, int64_t ld_out);
+void orc_unrotate_r_f64(const double* y, int64_t rows, int64_t cols, int64_t ld_y,
+                        const int32_t* perm, const double* R, double* out, int64_t ld_out);
+double orc_occupancy(const float* y, int64_t rows, int64_t cols, int64_t ld, double* hist);
 void orc_channel_energy(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                         double* energy);
 void orc_build_perm(const float* energy, int64_t cols, int block, int group, int32_t* perm);

@@ -1,0 +1,121 @@
+"""Pins for the oracle's learned block rotation and code-book occupancy (CPU).
+
+"TORQ: Two-Level Orthogonal Rotation for MXFP4 Quantization", technical
+summary sec. 2(b): a learned orthogonal matrix inside each 32-element block,
+trained on the code-book occupancy equilibrium loss (the deviation of the
+empirical use of the MXFP4 codes from uniform). Reading (the pages give no
+formula): occupancy = fraction of elements per E2M1 magnitude index after the
+default MXFP4 scale rule, loss = sum over the 8 indices of (fraction - 1/8)^2.
+"""
+from fractions import Fraction
+
+import numpy as np
+import scipy.linalg
+import scipy.stats
+
+from block_scaled_fp4_absmax_amd import inputs
+
+E2M1 = [Fraction(v) for v in ("0", "1/2", "1", "3/2", "2", "3", "4", "6")]
+
+
+def _ortho(seed):
+    return scipy.stats.ortho_group.rvs(32, random_state=seed)
+
+
+def test_rotate_r_special_matrices(orc):
+    x = inputs.gen_c3(rows=6, cols=256)
+    xf = inputs.bf16_bits_to_f32(x).astype(np.float64)
+    perm = np.random.default_rng(2).permutation(256).astype(np.int32)
+    xp = xf[:, perm]
+    # the identity and a permutation matrix move values exactly
+    assert np.array_equal(orc.rotate_r(x, perm, np.eye(32)), xp.astype(np.float32))
+    q = np.random.default_rng(3).permutation(32)
+    P = np.eye(32)[q]  # (P v)[i] = v[q[i]]
+    want = xp.reshape(6, 8, 32)[:, :, q].reshape(6, 256)
+    assert np.array_equal(orc.rotate_r(x, perm, P), want.astype(np.float32))
+    # the orthonormal Sylvester-Hadamard matrix gives the Hadamard rotation
+    H = scipy.linalg.hadamard(32) / np.sqrt(32)
+    ref = (xp.reshape(6, 8, 32) @ H.T).reshape(6, 256).astype(np.float32)
+    got = orc.rotate_r(x, perm, H)
+    assert np.abs(got.astype(np.float64) - ref).max() <= 2.0 ** -24 * np.abs(ref).max()
+    assert np.mean(got == ref) > 0.999
+    # a single Givens rotation of coordinates 3 and 17
+    th = 0.3
+    G = np.eye(32)
+    G[3, 3] = G[17, 17] = np.cos(th)
+    G[3, 17], G[17, 3] = -np.sin(th), np.sin(th)
+    y = orc.rotate_r(x, None, G).astype(np.float64).reshape(6, 8, 32)
+    xb = xf.reshape(6, 8, 32)
+    assert np.allclose(y[..., 3], np.cos(th) * xb[..., 3] - np.sin(th) * xb[..., 17], rtol=1e-6,
+                       atol=1e-30)
+    assert np.allclose(y[..., 17], np.sin(th) * xb[..., 3] + np.cos(th) * xb[..., 17], rtol=1e-6,
+                       atol=1e-30)
+    others = [k for k in range(32) if k not in (3, 17)]
+    assert np.array_equal(y[..., others], xb[..., others])
+
+
+def test_rotate_r_general_matrix_and_inverse(orc):
+    """A random orthogonal (non-symmetric) matrix: rotate_r against a dense
+    product, and unrotate_r_f64 (which applies R^T) inverts it, so a
+    transposed operand on either side fails."""
+    x = inputs.gen_c4(rows=8, cols=512)
+    perm = np.random.default_rng(4).permutation(512).astype(np.int32)
+    R = _ortho(5)
+    assert np.abs(R - R.T).max() > 0.1
+    xp = inputs.bf16_bits_to_f32(x).astype(np.float64)[:, perm]
+    ref = (xp.reshape(8, 16, 32) @ R.T).reshape(8, 512)
+    y = orc.rotate_r(x, perm, R)
+    assert np.abs(y - ref).max() <= 2.0 ** -23 * np.abs(ref).max()
+    back = orc.unrotate_r_f64(ref, perm, R)
+    xf = inputs.bf16_bits_to_f32(x).astype(np.float64)
+    assert np.abs(back - xf).max() <= 1e-12 * np.abs(xf).max()
+    # the norm of every block is kept
+    assert np.allclose(np.linalg.norm(ref.reshape(-1, 32), axis=1),
+                       np.linalg.norm(xp.reshape(-1, 32), axis=1), rtol=1e-12)
+
+
+def _exact_hist(y):
+    """Occupancy by exact search: the smallest E8M0 exponent with
+    amax <= 6 * 2^e, then the nearest E2M1 magnitude (ties: even index)."""
+    cnt = [0] * 8
+    for blk in y.reshape(-1, 32):
+        fb = [abs(Fraction(float(v))) for v in blk]
+        amax = max(fb)
+        e = -127
+        while amax > 6 * Fraction(2) ** e and e < 127:
+            e += 1
+        for v in fb:
+            a = v / Fraction(2) ** e
+            cnt[min(range(8), key=lambda i: (abs(a - E2M1[i]), i % 2))] += 1
+    n = sum(cnt)
+    return [Fraction(c, n) for c in cnt]
+
+
+def test_occupancy_against_exact_search(orc):
+    rng = np.random.default_rng(9)
+    y = (rng.standard_normal((4, 128)) * np.exp(rng.normal(0, 2, (4, 1)))).astype(np.float32)
+    # midpoints between magnitudes, exactly, at a block scale of 2^1
+    mids = np.float32([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]) * 2
+    y[0, :8] = mids
+    y[0, 8:32] = 0.0
+    y[1, 32:64] = -y[1, 32:64]
+    hist, loss = orc.occupancy(y)
+    want = _exact_hist(y)
+    assert [Fraction(h) for h in hist] == want
+    assert Fraction(loss).limit_denominator(1 << 40) == sum((w - Fraction(1, 8)) ** 2 for w in want)
+
+
+def test_occupancy_uniform_and_degenerate(orc):
+    # every block holds each E2M1 magnitude four times (signs mixed) at a
+    # random power-of-two scale: all fractions are 1/8 and the loss is 0
+    rng = np.random.default_rng(11)
+    mags = np.float64([0, .5, 1, 1.5, 2, 3, 4, 6])
+    blocks = []
+    for _ in range(64):
+        b = np.repeat(mags, 4) * rng.choice([-1.0, 1.0], 32)
+        blocks.append(rng.permutation(b) * 2.0 ** rng.integers(-20, 20))
+    hist, loss = orc.occupancy(np.float32(blocks).reshape(16, 128))
+    assert np.array_equal(hist, np.full(8, 0.125)) and loss == 0.0
+    # all zeros: everything in bin 0
+    hist, loss = orc.occupancy(np.zeros((2, 64), np.float32))
+    assert hist[0] == 1.0 and not hist[1:].any() and loss == 0.875
