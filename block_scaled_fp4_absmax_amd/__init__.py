@@ -17,6 +17,7 @@ __all__ = [
     "MXFP4", "NVFP4", "MXINT4", "PLAIN", "RAZER", "RAZER_W", "FLAG_TENSOR_SCALE_GIVEN", "FLAG_SCALE_OCP_FLOOR",
     "Fp4Error", "lib", "library_path", "quantize", "dequantize", "rotate_quantize",
     "channel_energy", "build_permutation", "block_of", "gemm", "OUT_F32", "OUT_BF16",
+    "rotate_quantize_r", "dequantize_r", "calibrate_block_rotation",
 ]
 
 MXFP4, NVFP4, MXINT4 = 0, 1, 2
@@ -65,6 +66,10 @@ def lib() -> ctypes.CDLL:
         "fp4_gemm": (i32, [vp, i64, vp, i64, vp, i32, vp, i64, vp, i64, vp, i32, i64, i64, i64,
                            i32, i32, vp, i64, vp]),
         "fp4_build_permutation": (i32, [vp, i64, i32, i32, vp]),
+        "fp4_rotate_quantize_r": (i32, [vp, i64, i64, i64, vp, vp, vp, i64, vp, i64, vp, i64,
+                                        vp]),
+        "fp4_dequantize_r": (i32, [vp, i64, vp, i64, i64, i64, vp, vp, vp, i64, vp]),
+        "fp4_calibrate_block_rotation": (i32, [vp, i64, i64, i64, vp, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -235,3 +240,56 @@ def build_permutation(energy, block: int = 32, group: int = 1):
     st = lib().fp4_build_permutation(_ptr(e), e.numel(), block, group, _ptr(perm))
     _check("fp4_build_permutation", st)
     return perm
+
+
+def rotate_quantize_r(x, perm, rotation, want_rotated: bool = False, codes=None, scales=None,
+                      rotated=None, stream=None):
+    """Permutation + learned 32x32 block matrix (fp32 [32, 32] device tensor,
+    R row-major) fused with MXFP4 quantize + pack. Returns (codes, scales,
+    rotated fp32 [rows, cols] or None)."""
+    import torch
+    rows, cols, ld = _rows_ld(x)
+    codes, scales = _outputs(rows, cols, MXFP4, x.device, codes, scales)
+    if want_rotated and rotated is None:
+        rotated = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+    st = lib().fp4_rotate_quantize_r(_ptr(x), rows, cols, ld, _ptr(perm), _ptr(rotation),
+                                     _ptr(codes), codes.stride(0), _ptr(scales),
+                                     scales.stride(0), _ptr(rotated),
+                                     rotated.stride(0) if rotated is not None else 0,
+                                     _stream(stream))
+    _check("fp4_rotate_quantize_r", st)
+    return codes, scales, rotated
+
+
+def dequantize_r(codes, scales, perm, rotation, out=None, stream=None):
+    """Inverse of :func:`rotate_quantize_r`: decode, R^T per block, undo the
+    permutation; bf16 [rows, cols]."""
+    import torch
+    rows, half, ldc = _rows_ld(codes)
+    cols = half * 2
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
+    st = lib().fp4_dequantize_r(_ptr(codes), ldc, _ptr(scales), scales.stride(0), rows, cols,
+                                _ptr(perm), _ptr(rotation), _ptr(out), out.stride(0),
+                                _stream(stream))
+    _check("fp4_dequantize_r", st)
+    return out
+
+
+def calibrate_block_rotation(x, perm=None, iters: int = 200, angles: int = 64):
+    """Learn the block matrix R on a bf16 calibration sample (host code).
+
+    ``x`` is a bf16 tensor (any device; copied to the host) and ``perm`` the
+    permutation that will be used online (host or device int32, or None).
+    Returns (R fp32 [32, 32] host tensor, (loss of H / sqrt(32), loss of R)).
+    """
+    import torch
+    xh = x.detach().to("cpu").contiguous()
+    rows, cols, ld = _rows_ld(xh)
+    ph = None if perm is None else perm.detach().to("cpu", torch.int32).contiguous()
+    R = torch.empty((32, 32), dtype=torch.float32)
+    loss = (ctypes.c_double * 2)()
+    st = lib().fp4_calibrate_block_rotation(_ptr(xh), rows, cols, ld, _ptr(ph), iters, angles,
+                                            _ptr(R), ctypes.cast(loss, ctypes.c_void_p))
+    _check("fp4_calibrate_block_rotation", st)
+    return R, (loss[0], loss[1])

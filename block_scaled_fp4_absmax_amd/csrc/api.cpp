@@ -155,6 +155,45 @@ int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t 
   return launch_status();
 }
 
+int fp4_rotate_quantize_r(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                          const int32_t* perm, const float* rotation, void* codes,
+                          int64_t ld_codes, void* scales, int64_t ld_scales, float* rotated_out,
+                          int64_t ld_rot, void* stream) {
+  int rc = check_quant_args(x_bf16, rows, cols, ld_x, FP4_MXFP4, 32, FP4_PLAIN, 0, codes, ld_codes,
+                            scales, ld_scales, nullptr);
+  if (rc != FP4_OK) return rc;
+  if (cols > fp4::kMaxPermCols) return FP4_ERR_UNSUPPORTED;
+  if (rotated_out && ld_rot < cols) return FP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (!perm || !rotation) return FP4_ERR_NULL;
+  if (!aligned(perm, 4) || !aligned(rotation, 4)) return FP4_ERR_ALIGN;
+  if (rotated_out && (!aligned(rotated_out, 16) || ld_rot % 4 != 0)) return FP4_ERR_ALIGN;
+  (void)hipGetLastError();
+  fp4::launch_mx_matrix_rotate_quant(Shape{rows, cols, ld_x, ld_codes, ld_scales}, perm, rotation,
+                                     x_bf16, codes, scales, rotated_out, ld_rot,
+                                     static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int fp4_dequantize_r(const void* codes, int64_t ld_codes, const void* scales, int64_t ld_scales,
+                     int64_t rows, int64_t cols, const int32_t* perm, const float* rotation,
+                     void* out_bf16, int64_t ld_out, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return FP4_ERR_SHAPE;
+  if (ld_out < cols || ld_codes < cols / 2 || ld_scales < cols / 32) return FP4_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && rows * cols / 8 >= (int64_t)1 << 31) return FP4_ERR_UNSUPPORTED;
+  if (cols > fp4::kMaxPermCols) return FP4_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (!codes || !scales || !out_bf16 || !perm || !rotation) return FP4_ERR_NULL;
+  if (!aligned(out_bf16, 16) || ld_out % 8 != 0) return FP4_ERR_ALIGN;
+  if (!aligned(codes, 4) || ld_codes % 4 != 0) return FP4_ERR_ALIGN;
+  if (!aligned(perm, 4) || !aligned(rotation, 4)) return FP4_ERR_ALIGN;
+  (void)hipGetLastError();
+  fp4::launch_mx_matrix_dequant_unrotate(Shape{rows, cols, ld_out, ld_codes, ld_scales}, perm,
+                                         rotation, codes, scales, out_bf16,
+                                         static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 int fp4_gemm(const void* a_codes, int64_t ld_a, const void* a_scales, int64_t ld_sa,
              const float* a_ts, int mode_a, const void* b_codes, int64_t ld_b,
              const void* b_scales, int64_t ld_sb, const float* b_ts, int mode_b, int64_t m,

@@ -73,6 +73,15 @@ void launch_nv_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a
                     int64_t ld_sa, const float* ta, int mode_a, const void* b, int64_t ld_b,
                     const void* sb, int64_t ld_sb, const float* tb, int mode_b, void* c,
                     int64_t ld_c, bool bf16_out, hipStream_t st);
+// MXFP4 after the permutation and a learned 32x32 block matrix (rmat, device,
+// row-major fp32) in place of the Hadamard; and the inverse on decode
+// (rmat^T, then the inverse permutation). perm must be given.
+void launch_mx_matrix_rotate_quant(const Shape& s, const int32_t* perm, const float* rmat,
+                                   const void* x, void* codes, void* scales, float* rot,
+                                   int64_t ld_rot, hipStream_t st);
+void launch_mx_matrix_dequant_unrotate(const Shape& s, const int32_t* perm, const float* rmat,
+                                       const void* codes, const void* scales, void* out,
+                                       hipStream_t st);
 void launch_channel_energy(int64_t rows, int64_t cols, int64_t ld_x, const void* x, float* energy,
                            hipStream_t st);
 

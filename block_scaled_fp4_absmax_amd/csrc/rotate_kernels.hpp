@@ -251,6 +251,7 @@ struct PermCtx {
   uint8_t* sbuf;                       // two LDS row buffers
   uint32_t (*off)[8];                  // the lane's gather offsets, per tile
   bf16x8_t a0, a1;                     // Hadamard MFMA operands
+  bf16x8_t m[3][2];                    // kFmtMxMat: the learned block matrix
   uint8_t* __restrict__ codes;
   uint8_t* __restrict__ scales;
   float* __restrict__ rot;
@@ -298,7 +299,10 @@ struct PermRows {
       gather_tile<G, kBuf * kBufBytes>(c.sbuf, c.off[i], lo, hi);
       float y[16];
       if (kHad) {
-        hadamard_mfma<kFmt == kFmtMx || kFmt == kFmtMxInt ? 32 : 16>(c.a0, c.a1, lo, hi, y);
+        if constexpr (kFmt == kFmtMxMat)
+          matrix_mfma(c.m, lo, hi, y);
+        else
+          hadamard_mfma<kFmt == kFmtMx || kFmt == kFmtMxInt ? 32 : 16>(c.a0, c.a1, lo, hi, y);
       } else {
         widen8(lo, y);
         widen8(hi, y + 8);
@@ -307,8 +311,9 @@ struct PermRows {
         if (ok) *c.amax = __builtin_fmaxf(*c.amax, absmax16f(y));
       } else {
         uint32_t w0, w1, byte, so;
-        if constexpr (kFmt == kFmtMx || kFmt == kFmtMxInt) {  // kOpt: OCP floor rule
-          if constexpr (kFmt == kFmtMx)
+        if constexpr (kFmt == kFmtMx || kFmt == kFmtMxInt || kFmt == kFmtMxMat) {
+          // kOpt: OCP floor rule
+          if constexpr (kFmt != kFmtMxInt)
             mx_quant16_pair<kOpt, kHad>(y, w0, w1, byte);
           else
             mxint_quant16_pair<kOpt, kHad>(y, w0, w1, byte);
@@ -388,7 +393,8 @@ constexpr int perm_waves_cap() {
 #define FP4_PERM_AHEAD perm_ahead<kTpw>()
 #endif
 
-// kFmt: kFmtMx or kFmtMxInt (kOpt = OCP floor rule), kFmtNv (kOpt = RaZeR; ts
+// kFmt: kFmtMx or kFmtMxInt (kOpt = OCP floor rule), kFmtMxMat (MXFP4 after
+// the 32x32 block matrix at ts, row-major fp32), kFmtNv (kOpt = RaZeR; ts
 // holds s_t),
 // kFmtNvAmax (no stores; work-group i leaves its largest rotated magnitude in
 // the code slot of chunk i).
@@ -420,8 +426,11 @@ __global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void rotq_perm_kernel(
   }
   uint32_t off[kTpw][8];
   const int lr = pack_lane_perm<kTpw>(v, g, off);
-  bf16x8_t a0, a1;
-  hadamard_operands<kFmt == kFmtMx || kFmt == kFmtMxInt ? 32 : 16>(a0, a1);
+  bf16x8_t a0, a1, m[3][2];
+  if constexpr (kFmt == kFmtMxMat)
+    matrix_operands(ts, false, m);
+  else
+    hadamard_operands<kFmt == kFmtMx || kFmt == kFmtMxInt ? 32 : 16>(a0, a1);
   put_row<kCpl>(sbuf, cpr, first);
   // run length agreed by the whole work-group (this also publishes row r0 and
   // the reciprocal table)
@@ -429,7 +438,9 @@ __global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void rotq_perm_kernel(
                   : __syncthreads_and(lr >= 4) ? 4
                   : __syncthreads_and(lr >= 2) ? 2 : 1;
   float amax = 0.0f;
-  PermCtx<kTpw, kAhead> c{x, sbuf, off, a0, a1, codes, scales, rot, g, pre, ns, rcp_tab, &amax};
+  PermCtx<kTpw, kAhead> c{x, sbuf, off, a0, a1, {{m[0][0], m[0][1]}, {m[1][0], m[1][1]},
+                                                 {m[2][0], m[2][1]}},
+                          codes, scales, rot, g, pre, ns, rcp_tab, &amax};
   if (run == 8)
     PermRows<8, kTpw, kAhead, kFmt, kHad, kOpt, kRot>::run(c);
   else if (run == 4)

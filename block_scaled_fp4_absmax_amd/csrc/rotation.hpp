@@ -84,9 +84,60 @@ __device__ __forceinline__ void hadamard_mfma(const bf16x8_t& a0, const bf16x8_t
   for (int r = 0; r < 16; ++r) y[r] = acc[r] * kScale;
 }
 
+// A general 32x32 block matrix M (row-major fp32 in device memory), for the
+// learned intra-block rotation: lane l holds M[tau(l % 32)][16 (l / 32) + j],
+// j = 0..15 (tau = out_index_of_row, the operand order of hadamard_operands),
+// as three bf16 terms t0 + t1 + t2 = M exactly (each term takes the next 8
+// significant bits; the differences are exact in fp32); with transpose, M^T.
+__device__ __forceinline__ void matrix_operands(const float* __restrict__ M, bool transpose,
+                                                bf16x8_t (&a)[3][2]) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t row = out_index_of_row(lane & 31u), k0 = 16u * (lane >> 5);
+  uint32_t w[3][8];
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    float t[3][2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t k = k0 + (uint32_t)(j + e);
+      const float v = transpose ? M[32u * k + row] : M[32u * row + k];
+      const float t0 = __uint_as_float(pack_bf16x2(v, 0.0f) << 16);
+      const float r1 = v - t0;
+      const float t1 = __uint_as_float(pack_bf16x2(r1, 0.0f) << 16);
+      t[0][e] = t0;
+      t[1][e] = t1;
+      t[2][e] = r1 - t1;  // at most 8 significant bits: exact in bf16
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) w[q][j / 2] = pack_bf16x2(t[q][0], t[q][1]);
+  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    a[q][0] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[q][0], w[q][1], w[q][2], w[q][3]});
+    a[q][1] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[q][4], w[q][5], w[q][6], w[q][7]});
+  }
+}
+
+// y[0..15] = (M x)[16h .. 16h + 15] for the lane's segment: products of bf16
+// are exact, so the only rounding is the fp32 accumulation of the six MFMAs.
+__device__ __forceinline__ void matrix_mfma(const bf16x8_t (&a)[3][2], u32x4_t lo, u32x4_t hi,
+                                            float* y) {
+  f32x16_t acc = {};
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[q][0], __builtin_bit_cast(bf16x8_t, lo), acc,
+                                                  0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[q][1], __builtin_bit_cast(bf16x8_t, hi), acc,
+                                                  0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) y[r] = acc[r];
+}
+
 // Largest |y| of 16 fp32 values as a bit pattern, for values that are the
-// Hadamard transform of a block: a NaN or Inf input makes every output of the
-// block NaN or +-Inf, so a float maximum of magnitudes (which may drop a NaN
+// Hadamard transform or a learned-matrix product of a block: a NaN or Inf
+// input makes every output of the block NaN or +-Inf (0 * Inf and 0 * NaN are
+// NaN), so a float maximum of magnitudes (which may drop a NaN
 // operand in favour of another) still yields a non-finite result for such a
 // block, and for finite values its bits order like the magnitudes.
 __device__ __forceinline__ uint32_t absmax16_mixed(const float* y) {
@@ -234,9 +285,10 @@ struct RotGeom {
 };
 
 // Formats of the rotation kernels (the C ABI's format numbers): MXFP4 and
-// MXINT4 (32-point transform), NVFP4 (16-point), and the NVFP4 pre-pass that
-// only finds the largest rotated magnitude (for a computed tensor scale).
-enum RotFmt : int { kFmtMx = 0, kFmtNv = 1, kFmtMxInt = 2, kFmtNvAmax = 3 };
+// MXINT4 (32-point transform), NVFP4 (16-point), the NVFP4 pre-pass that
+// only finds the largest rotated magnitude (for a computed tensor scale), and
+// MXFP4 after a learned 32x32 block matrix instead of the Hadamard.
+enum RotFmt : int { kFmtMx = 0, kFmtNv = 1, kFmtMxInt = 2, kFmtNvAmax = 3, kFmtMxMat = 4 };
 
 inline RotGeom rot_geom(const Shape& s, int64_t ld_rot, int block = 32) {
   RotGeom g;

@@ -95,6 +95,24 @@ __device__ __forceinline__ void unrotate_tile(u32x2_t c, uint32_t sbyte, const b
   }
 }
 
+// MXFP4 after a learned block matrix M: decode (exact in bf16), multiply by
+// M^T (m holds its operands), round to bf16.
+__device__ __forceinline__ void unrotate_tile_mat(u32x2_t c, uint32_t sbyte,
+                                                  const bf16x8_t (&m)[3][2], u32x4_t& lo,
+                                                  u32x4_t& hi) {
+  const float s = e8m0_operand(sbyte & 0xFFu);
+#define FP4_CVT2(w, k) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, k))
+  const uint32_t d[8] = {FP4_CVT2(c.x, 0), FP4_CVT2(c.x, 1), FP4_CVT2(c.x, 2), FP4_CVT2(c.x, 3),
+                         FP4_CVT2(c.y, 0), FP4_CVT2(c.y, 1), FP4_CVT2(c.y, 2), FP4_CVT2(c.y, 3)};
+#undef FP4_CVT2
+  float y[16];
+  matrix_mfma(m, u32x4_t{d[0], d[1], d[2], d[3]}, u32x4_t{d[4], d[5], d[6], d[7]}, y);
+  lo = u32x4_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+               pack_bf16x2(y[6], y[7])};
+  hi = u32x4_t{pack_bf16x2(y[8], y[9]), pack_bf16x2(y[10], y[11]), pack_bf16x2(y[12], y[13]),
+               pack_bf16x2(y[14], y[15])};
+}
+
 // NVFP4: one whole 16-element block per lane. The E2M1 values (RaZeR: code 8
 // is the block's +-5) are exact in bf16 and the 16-point transform of them is
 // exact (sums of at most 16 multiples of 0.5 below 100, then times 1/4); the
@@ -171,6 +189,7 @@ struct UnrotCtx {
   uint8_t* sbuf;        // two LDS row buffers (with a permutation)
   uint32_t (*off)[8];   // the lane's scatter offsets, per tile
   bf16x8_t a0, a1;      // Hadamard MFMA operands
+  bf16x8_t m[3][2];     // kFmt 3: the learned block matrix, transposed
   RotGeom g;
   RowCodes<kTpw>* rc;   // kAhead + 1 register buffers: rows k .. k + kAhead
   float s_t;            // NVFP4 tensor scale
@@ -205,6 +224,8 @@ struct UnrotRows {
     for (int i = 0; i < kTpw; ++i) {
       if constexpr (kNv)
         nv_unrotate_tile<kHad, kRazer>(rc.c[i], rc.s[i], c.s_t, c.a0, c.a1, lo[i], hi[i]);
+      else if constexpr (kFmt == 3)
+        unrotate_tile_mat(rc.c[i], rc.s[i], c.m, lo[i], hi[i]);
       else
         unrotate_tile<kHad, kFmt == 2>(rc.c[i], rc.s[i], c.a0, c.a1, lo[i], hi[i]);
     }
@@ -271,13 +292,15 @@ constexpr int unrot_wgs_per_cu() {
 #endif
 
 // kFmt 1 (NVFP4): blocks of 16 (scales 2 b + h, tensor scale *ts), the
-// 16-point transform; 0 (MXFP4) and 2 (MXINT4): blocks of 32, the 32-point one.
+// 16-point transform; 0 (MXFP4) and 2 (MXINT4): blocks of 32, the 32-point
+// one; 3: MXFP4 with the transpose of the learned 32x32 matrix at ts.
 template <int kTpw, int kFmt, bool kRazer, bool kHad, bool kPerm>
 __global__ __launch_bounds__(kThreads, 2) void dequant_unrotate_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ ts, const int32_t* __restrict__ perm, uint16_t* __restrict__ out,
     RotGeom g) {
-  constexpr int kAhead = FP4_UNROT_AHEAD;
+  // the learned matrix holds 24 more registers: less look-ahead on wide rows
+  constexpr int kAhead = kFmt == 3 && kTpw >= 3 ? 1 : FP4_UNROT_AHEAD;
   constexpr bool kNv = kFmt == 1;
   __shared__ __attribute__((aligned(16))) uint8_t sbuf[kPerm ? 2 * 8192 * kTpw : 16];
   i32x4_t v[kTpw][4];
@@ -290,10 +313,23 @@ __global__ __launch_bounds__(kThreads, 2) void dequant_unrotate_kernel(
   uint32_t off[kTpw][8];
   int lr = 8;
   if (kPerm) lr = pack_lane_perm<kTpw>(v, g, off);
-  bf16x8_t a0, a1;
-  hadamard_operands<kNv ? 16 : 32>(a0, a1);
+  bf16x8_t a0, a1, m[3][2];
+  if constexpr (kFmt == 3)
+    matrix_operands(ts, true, m);
+  else
+    hadamard_operands<kNv ? 16 : 32>(a0, a1);
   const float s_t = kNv ? *ts : 1.0f;
-  UnrotCtx<kTpw, kAhead> c{codes, scales, out, sbuf, off, a0, a1, g, rc, s_t};
+  UnrotCtx<kTpw, kAhead> c{codes,
+                           scales,
+                           out,
+                           sbuf,
+                           off,
+                           a0,
+                           a1,
+                           {{m[0][0], m[0][1]}, {m[1][0], m[1][1]}, {m[2][0], m[2][1]}},
+                           g,
+                           rc,
+                           s_t};
   if constexpr (kPerm) {
     // run length agreed by the whole work-group
     const int run = __syncthreads_and(lr >= 8) ? 8

@@ -204,6 +204,41 @@ int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t 
                         int64_t ld_rot, void* stream);
 
 /*
+ * fp4_rotate_quantize_r -- the two-level rotation with a learned block matrix
+ * in place of the Hadamard, fused with MXFP4 quantize + pack ([TORQ] sec.
+ * 2(b): the rotation inside each block is learned, see
+ * fp4_calibrate_block_rotation).
+ *
+ * x'[r, j] = x[r, perm[j]], then y = R x' on every 32-element block of x',
+ * R the same 32x32 matrix for all blocks (fp32, products exact, sums in fp32),
+ * then MXFP4 quantization of y as in fp4_quantize (default scale rule).
+ *
+ *  perm         device int32[cols], a permutation of 0..cols-1 (entries
+ *               clamped to cols-1); required: pass the identity for none;
+ *               cols <= 16384
+ *  rotation     device fp32[32 * 32], R row-major (R[i][j] at 32 i + j),
+ *               4-byte aligned; read once per work-group. Any matrix is
+ *               accepted; fp4_dequantize_r inverts it only if orthogonal
+ *  rotated_out  NULL, or device fp32 [rows, ld_rot] receiving y; 16-byte
+ *               aligned, ld_rot % 4 == 0 (for parity checks)
+ *  others       as for fp4_quantize with format FP4_MXFP4 (cols % 32 == 0)
+ */
+int fp4_rotate_quantize_r(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                          const int32_t* perm, const float* rotation, void* codes,
+                          int64_t ld_codes, void* scales, int64_t ld_scales, float* rotated_out,
+                          int64_t ld_rot, void* stream);
+
+/*
+ * fp4_dequantize_r -- inverse of fp4_rotate_quantize_r: MXFP4 decode (exact
+ * in bf16), x' = R^T y per 32-element block (fp32 sums), then
+ * out[r, perm[j]] = x'[r, j], rounded to bf16 (RNE). Arguments as for
+ * fp4_dequantize with format FP4_MXFP4 and as for fp4_rotate_quantize_r.
+ */
+int fp4_dequantize_r(const void* codes, int64_t ld_codes, const void* scales, int64_t ld_scales,
+                     int64_t rows, int64_t cols, const int32_t* perm, const float* rotation,
+                     void* out_bf16, int64_t ld_out, void* stream);
+
+/*
  * fp4_gemm -- C = A B^T on the quantized operands, the consumer of the path
  * ([RaZeR] sec. 2.3: GEMM kernels that take quantized weights and
  * activations, the special value rebuilt from the scale's metadata bit).
@@ -277,6 +312,40 @@ int fp4_channel_energy(const void* x_bf16, int64_t rows, int64_t cols, int64_t l
  */
 int fp4_build_permutation(const float* energy_host, int64_t cols, int block, int group,
                           int32_t* perm_host);
+
+/*
+ * fp4_calibrate_block_rotation -- host-side, synchronous. Learns the 32x32
+ * block matrix R of fp4_rotate_quantize_r on a calibration sample ([TORQ]
+ * sec. 2(b)): alternating coordinate descent on the code-book occupancy
+ * equilibrium loss L(R) = sum over the 8 E2M1 magnitudes c of
+ * (p_c - 1/8)^2, p_c the fraction of elements of R x' (every block of every
+ * row) that round to magnitude c under their block's MXFP4 scale.
+ *  - start: R = H / sqrt(32), the orthonormal Sylvester-Hadamard matrix;
+ *  - S-step: every block's shared exponent by the default MXFP4 rule, so the
+ *    block maximum lands in the top binade of the code book;
+ *  - R-step: one Givens rotation of output coordinates (i, j), i the
+ *    coordinate whose own occupancy is farthest from uniform (largest sum of
+ *    squared deviations), j the most complementary partner (smallest dot
+ *    product of the two deviation vectors; ties: lowest index); the angle is
+ *    the best of theta = k pi / (2 angles), k = 1 .. angles - 1 (the loss is
+ *    piecewise constant in theta); taken only if it lowers the loss, else the
+ *    pair is barred until the next accepted step.
+ * `iters` R-steps are tried (fewer if every pair is barred). The result is
+ * orthogonal up to fp64 rounding, then stored as fp32; the sample is
+ * evaluated in fp64 (bf16 inputs are exact).
+ *
+ *  x_host       host bf16 [rows, ld_x]; rows * cols <= 2^26
+ *  cols         cols % 32 == 0
+ *  perm_host    NULL (identity) or host int32[cols], the permutation that
+ *               will be used online
+ *  iters        >= 0 R-steps
+ *  angles       2 .. 4096
+ *  rotation_out host fp32[32 * 32], R row-major
+ *  loss_out     NULL or host double[2]: L(H / sqrt(32)) and L(R)
+ */
+int fp4_calibrate_block_rotation(const uint16_t* x_host, int64_t rows, int64_t cols,
+                                 int64_t ld_x, const int32_t* perm_host, int iters, int angles,
+                                 float* rotation_out, double* loss_out);
 
 #ifdef __cplusplus
 }

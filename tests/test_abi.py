@@ -123,6 +123,23 @@ def test_rotate_and_dequant_validation(L):
     assert G(a=None, sa=None, b=None, sb=None, c=None, m=0) == 0
     assert G(fmt=1, ldsa=4, ldsb=4) == -1        # NVFP4 needs both tensor scales
     assert G(fmt=1, ta=TS, tb=TS, ldsa=5, ldsb=4) == -3  # NVFP4 scale rows: ld_s % 2
+    # rotate_quantize_r(x, rows, cols, ld, perm, rotation, codes, ldc, scales, lds, rot, ld_rot,
+    #                   stream)
+    Q = L.fp4_rotate_quantize_r
+    assert Q(FAKE, 4, 48, 48, FAKE, FAKE, FAKE, 24, FAKE, 2, None, 0, None) == -2  # cols % 32
+    assert Q(FAKE, 4, 64, 64, None, FAKE, FAKE, 32, FAKE, 2, None, 0, None) == -1  # perm needed
+    assert Q(FAKE, 4, 64, 64, FAKE, None, FAKE, 32, FAKE, 2, None, 0, None) == -1  # matrix needed
+    assert Q(FAKE, 4, 64, 64, FAKE, FAKE + 2, FAKE, 32, FAKE, 2, None, 0, None) == -3
+    assert Q(FAKE, 4, 64, 64, FAKE, FAKE, FAKE, 32, FAKE, 2, FAKE, 32, None) == -2  # ld_rot
+    assert Q(FAKE, 4, 32768, 32768, FAKE, FAKE, FAKE, 16384, FAKE, 1024, None, 0, None) == -4
+    assert Q(None, 0, 64, 64, None, None, None, 32, None, 2, None, 0, None) == 0
+    # dequantize_r(codes, ldc, scales, lds, rows, cols, perm, rotation, out, ldo, stream)
+    U = L.fp4_dequantize_r
+    assert U(FAKE, 24, FAKE, 2, 4, 48, FAKE, FAKE, FAKE, 48, None) == -2
+    assert U(FAKE, 32, FAKE, 2, 4, 64, None, FAKE, FAKE, 64, None) == -1
+    assert U(FAKE, 32, FAKE, 2, 4, 64, FAKE, FAKE, FAKE + 8, 64, None) == -3
+    assert U(FAKE, 32, FAKE, 2, 4, 64, FAKE, FAKE + 1, FAKE, 64, None) == -3
+    assert U(None, 32, None, 2, 0, 64, None, None, None, 64, None) == 0
     E = L.fp4_channel_energy
     assert E(FAKE, 4, 48, 48, FAKE, None) == -2
     assert E(None, 4, 64, 64, FAKE, None) == -1
