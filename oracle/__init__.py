@@ -35,6 +35,20 @@ than itself (the pins live in ``tests/test_oracle_*.py``):
   enumeration.
 * ``rotate`` / ``unrotate_f64``: pinned to ``scipy.linalg.hadamard`` (orders 16
   and 32) and norm preservation.
+* ``e3m3_value`` / ``e3m3_encode`` / ``razer_block_set`` / ``nvw_quantize``:
+  decoder pinned to its closed form; encoder at every midpoint and one ulp
+  either side; the block choice to an exact Fraction arg-min and exhaustive
+  tiny-block enumeration; whole tensors by the block-choice consistency, sign
+  symmetry and the tensor-scale rule. The second special-value pair is not on
+  the pages: parity unpinned for that value (an offline search picks it).
+* ``rotate_r`` / ``unrotate_r_f64``: pinned by special matrices (identity,
+  permutation, Sylvester-Hadamard from scipy, one Givens rotation in closed
+  form), a random orthogonal matrix against numpy's product, and the inverse.
+* ``occupancy``: pinned to an exact Fraction search of the scale and the
+  nearest magnitude, and to uniform and all-zero cases.
+* ``apply_givens``: pinned to a dense product of the Givens matrices (numpy),
+  closed forms for one rotation and for angles 0 and pi/2 (a swap with a sign),
+  norm preservation and the inverse (the transposed rotations in reverse).
 * ``build_perm``: pinned by bijectivity, block-energy balancing, a replay of the
   greedy invariant (every unit goes to an open block of least load) and, for
   aligned channel runs, the run structure.
@@ -123,6 +137,7 @@ def _load():
         "orc_unrotate_f64": (None, [vp, i64, i64, i64, vp, i32, vp, i64]),
         "orc_channel_energy": (None, [vp, i64, i64, i64, vp]),
         "orc_rotate_r": (None, [vp, i64, i64, i64, vp, vp, vp, i64]),
+        "orc_apply_givens": (None, [vp, i64, i64, i64, vp, i64, vp, vp, vp, i64]),
         "orc_unrotate_r_f64": (None, [vp, i64, i64, i64, vp, vp, vp, i64]),
         "orc_occupancy": (f64, [vp, i64, i64, i64, vp]),
         "orc_build_perm": (None, [vp, i64, i32, i32, vp]),
@@ -480,6 +495,23 @@ def unrotate_r_f64(y: np.ndarray, perm: Optional[np.ndarray], R: np.ndarray) -> 
         perm = np.ascontiguousarray(perm, np.int32)
     out = np.zeros((rows, cols), np.float64)
     _load().orc_unrotate_r_f64(_ptr(y), rows, cols, cols, _ptr(perm), _ptr(R), _ptr(out), cols)
+    return out
+
+
+def apply_givens(x_bf16: np.ndarray, perm: Optional[np.ndarray], pairs: np.ndarray,
+                 cs: np.ndarray) -> np.ndarray:
+    """fp64 [rows, cols]: permute channels, then the Givens rotations in order
+    (pairs int [n, 2] = (i, j), cs [n, 2] = (c, s))."""
+    rows, cols = x_bf16.shape
+    pairs = np.ascontiguousarray(pairs, np.int32).reshape(-1, 2)
+    cs = np.ascontiguousarray(cs, np.float64).reshape(-1, 2)
+    assert pairs.shape == cs.shape
+    assert pairs.size == 0 or (pairs.min() >= 0 and pairs.max() < cols)
+    if perm is not None:
+        perm = np.ascontiguousarray(perm, np.int32)
+    out = np.zeros((rows, cols), np.float64)
+    _load().orc_apply_givens(_ptr(x_bf16), rows, cols, _ld(x_bf16), _ptr(perm), len(pairs),
+                             _ptr(pairs), _ptr(cs), _ptr(out), cols)
     return out
 
 

@@ -767,6 +767,30 @@ double orc_occupancy(const float* y, int64_t rows, int64_t cols, int64_t ld, dou
   return loss;
 }
 
+/* [TORQ] sec. 2(a): the inter-block transform built from Givens rotations.
+ * x'[j] = x[perm[j]] (perm NULL: identity), then for k = 0 .. n-1 in order,
+ * with (i, j) = pairs[2k], pairs[2k+1] and (c, s) = cs[2k], cs[2k+1]:
+ *   (x'_i, x'_j) <- (c x'_i - s x'_j, s x'_i + c x'_j).
+ * fp64 throughout (the written definition, one rotation after another). */
+void orc_apply_givens(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                      const int32_t* perm, int64_t n, const int32_t* pairs, const double* cs,
+                      double* out, int64_t ld_out) {
+  int64_t r;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (r = 0; r < rows; ++r) {
+    double* z = out + r * ld_out;
+    for (int64_t j = 0; j < cols; ++j)
+      z[j] = (double)orc_bf16_to_f32(x[r * ld_x + (perm ? perm[j] : j)]);
+    for (int64_t k = 0; k < n; ++k) {
+      const int32_t i = pairs[2 * k], j = pairs[2 * k + 1];
+      const double c = cs[2 * k], s = cs[2 * k + 1];
+      const double zi = z[i], zj = z[j];
+      z[i] = c * zi - s * zj;
+      z[j] = s * zi + c * zj;
+    }
+  }
+}
+
 void orc_channel_energy(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                         double* energy) {
   for (int64_t j = 0; j < cols; ++j) energy[j] = 0.0;

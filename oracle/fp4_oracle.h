@@ -93,6 +93,9 @@ void orc_rotate_r(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                   const int32_t* perm, const double* R, float* out, int64_t ld_out);
 void orc_unrotate_r_f64(const double* y, int64_t rows, int64_t cols, int64_t ld_y,
                         const int32_t* perm, const double* R, double* out, int64_t ld_out);
+void orc_apply_givens(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                      const int32_t* perm, int64_t n, const int32_t* pairs, const double* cs,
+                      double* out, int64_t ld_out);
 double orc_occupancy(const float* y, int64_t rows, int64_t cols, int64_t ld, double* hist);
 void orc_channel_energy(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                         double* energy);

@@ -119,3 +119,58 @@ def test_occupancy_uniform_and_degenerate(orc):
     # all zeros: everything in bin 0
     hist, loss = orc.occupancy(np.zeros((2, 64), np.float32))
     assert hist[0] == 1.0 and not hist[1:].any() and loss == 0.875
+
+
+def _givens_matrix(n, i, j, c, s):
+    G = np.eye(n)
+    G[i, i], G[i, j], G[j, i], G[j, j] = c, -s, s, c
+    return G
+
+
+def test_apply_givens_against_dense_product(orc):
+    """The rotations in order equal the product G_n ... G_1 of their dense
+    matrices (numpy), after the permutation."""
+    rows, cols = 5, 96
+    x = inputs.gen_c3(rows=rows, cols=cols)
+    perm = np.random.default_rng(6).permutation(cols).astype(np.int32)
+    rng = np.random.default_rng(7)
+    pairs, cs = [], []
+    for _ in range(40):  # overlapping pairs: the order matters
+        i, j = rng.choice(cols, 2, replace=False)
+        th = rng.uniform(-np.pi, np.pi)
+        pairs.append((i, j))
+        cs.append((np.cos(th), np.sin(th)))
+    Q = np.eye(cols)
+    for (i, j), (c, s) in zip(pairs, cs):
+        Q = _givens_matrix(cols, i, j, c, s) @ Q
+    xp = inputs.bf16_bits_to_f32(x).astype(np.float64)[:, perm]
+    want = xp @ Q.T
+    got = orc.apply_givens(x, perm, np.array(pairs), np.array(cs))
+    assert np.abs(got - want).max() <= 1e-13 * np.abs(xp).max()
+    assert np.allclose(np.linalg.norm(got, axis=1), np.linalg.norm(xp, axis=1), rtol=1e-13)
+    # reversed order gives a different result (the sequence is not commutative)
+    rev = orc.apply_givens(x, perm, np.array(pairs[::-1]), np.array(cs[::-1]))
+    assert np.abs(rev - got).max() > 1e-3 * np.abs(xp).max()
+
+
+def test_apply_givens_closed_forms_and_inverse(orc):
+    x = inputs.gen_c4(rows=3, cols=64)
+    xf = inputs.bf16_bits_to_f32(x).astype(np.float64)
+    # angle 0: nothing moves; pi / 2 (c = 0, s = 1): x_i <- -x_j, x_j <- x_i
+    same = orc.apply_givens(x, None, np.array([[3, 40]]), np.array([[1.0, 0.0]]))
+    assert np.array_equal(same, xf)
+    sw = orc.apply_givens(x, None, np.array([[3, 40]]), np.array([[0.0, 1.0]]))
+    want = xf.copy()
+    want[:, 3], want[:, 40] = -xf[:, 40], xf[:, 3]
+    assert np.array_equal(sw, want)
+    # the inverse is the transposed rotations (s -> -s) in reverse order
+    rng = np.random.default_rng(8)
+    pairs = np.array([rng.choice(64, 2, replace=False) for _ in range(30)])
+    th = rng.uniform(0, np.pi / 2, 30)
+    cs = np.stack([np.cos(th), np.sin(th)], 1)
+    fwd = orc.apply_givens(x, None, pairs, cs)
+    cur = fwd.copy()
+    for (i, j), (c, s) in zip(pairs[::-1], cs[::-1]):
+        zi, zj = cur[:, i].copy(), cur[:, j].copy()
+        cur[:, i], cur[:, j] = c * zi + s * zj, -s * zi + c * zj
+    assert np.abs(cur - xf).max() <= 1e-13 * np.abs(xf).max()
