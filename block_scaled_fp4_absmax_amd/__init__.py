@@ -18,6 +18,7 @@ __all__ = [
     "Fp4Error", "lib", "library_path", "quantize", "dequantize", "rotate_quantize",
     "channel_energy", "build_permutation", "block_of", "gemm", "OUT_F32", "OUT_BF16",
     "rotate_quantize_r", "dequantize_r", "calibrate_block_rotation",
+    "calibrate_macro_rotation", "apply_channel_rotation", "MacroRotation",
 ]
 
 MXFP4, NVFP4, MXINT4 = 0, 1, 2
@@ -70,6 +71,10 @@ def lib() -> ctypes.CDLL:
                                         vp]),
         "fp4_dequantize_r": (i32, [vp, i64, vp, i64, i64, i64, vp, vp, vp, i64, vp]),
         "fp4_calibrate_block_rotation": (i32, [vp, i64, i64, i64, vp, i32, i32, vp, vp]),
+        "fp4_calibrate_macro_rotation": (i32, [vp, i64, i64, i64, vp, i32, ctypes.c_double, i32,
+                                               vp, vp, vp, vp, vp, vp]),
+        "fp4_apply_channel_rotation": (i32, [vp, i64, i64, i64, vp, vp, vp, vp, i32, i32, vp,
+                                             i64, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -293,3 +298,67 @@ def calibrate_block_rotation(x, perm=None, iters: int = 200, angles: int = 64):
                                             _ptr(R), ctypes.cast(loss, ctypes.c_void_p))
     _check("fp4_calibrate_block_rotation", st)
     return R, (loss[0], loss[1])
+
+
+class MacroRotation:
+    """The inter-block Givens transform: ``pairs`` int32 [n, 2], ``cs`` fp32
+    [n, 2] (cos, sin), ``layer_start`` int32 [layers + 1] (host tensors), and
+    the relative block-variance spread before and after."""
+
+    def __init__(self, pairs, cs, layer_start, spread):
+        self.pairs, self.cs, self.layer_start, self.spread = pairs, cs, layer_start, spread
+
+    @property
+    def n_rot(self) -> int:
+        return int(self.pairs.shape[0])
+
+    @property
+    def n_layers(self) -> int:
+        return int(self.layer_start.numel()) - 1
+
+    def to(self, device):
+        return MacroRotation(self.pairs.to(device), self.cs.to(device),
+                             self.layer_start.to(device), self.spread)
+
+
+def calibrate_macro_rotation(x, perm=None, block: int = 32, tol: float = 1e-6,
+                             max_rot: Optional[int] = None) -> MacroRotation:
+    """Givens rotations that equalise the block variances of the bf16 sample
+    ``x`` after ``perm`` (host code; x is copied to the host)."""
+    import torch
+    xh = x.detach().to("cpu").contiguous()
+    rows, cols, ld = _rows_ld(xh)
+    if max_rot is None:
+        max_rot = 4 * (cols // block)
+    ph = None if perm is None else perm.detach().to("cpu", torch.int32).contiguous()
+    pairs = torch.empty((max_rot, 2), dtype=torch.int32)
+    cs = torch.empty((max_rot, 2), dtype=torch.float32)
+    starts = torch.empty(max_rot + 1, dtype=torch.int32)
+    n_rot, n_layers = ctypes.c_int(0), ctypes.c_int(0)
+    spread = (ctypes.c_double * 2)()
+    st = lib().fp4_calibrate_macro_rotation(
+        _ptr(xh), rows, cols, ld, _ptr(ph), block, float(tol), max_rot, _ptr(pairs), _ptr(cs),
+        _ptr(starts), ctypes.byref(n_rot), ctypes.byref(n_layers),
+        ctypes.cast(spread, ctypes.c_void_p))
+    _check("fp4_calibrate_macro_rotation", st)
+    n, nl = n_rot.value, n_layers.value
+    return MacroRotation(pairs[:n].clone(), cs[:n].clone(), starts[:nl + 1].clone(),
+                         (spread[0], spread[1]))
+
+
+def apply_channel_rotation(x, macro: MacroRotation, perm=None, out=None, stream=None):
+    """bf16 [rows, cols]: permutation, then the Givens layers of ``macro``
+    (device tensors, see :meth:`MacroRotation.to`), on every row."""
+    import torch
+    rows, cols, ld = _rows_ld(x)
+    for t in (perm, macro.pairs, macro.cs, macro.layer_start):
+        if t is not None and t.numel() and t.device != x.device:
+            raise ValueError("the permutation and the rotation tables must be on x's device")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device)
+    st = lib().fp4_apply_channel_rotation(_ptr(x), rows, cols, ld, _ptr(perm), _ptr(macro.pairs),
+                                          _ptr(macro.cs), _ptr(macro.layer_start),
+                                          macro.n_layers, macro.n_rot, _ptr(out),
+                                          out.stride(0), _stream(stream))
+    _check("fp4_apply_channel_rotation", st)
+    return out

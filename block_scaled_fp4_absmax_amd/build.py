@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp4.so")
 SOURCES = ["quant.hip", "rotate_mx.hip", "rotate_int.hip", "rotate_nv.hip", "rotate_mat.hip",
-           "unrotate_mx.hip", "unrotate_int.hip", "unrotate_nv.hip", "unrotate_mat.hip", "gemm.hip", "gemm_nv.hip", "api.cpp", "perm.cpp", "calib.cpp", "device.cpp"]
+           "unrotate_mx.hip", "unrotate_int.hip", "unrotate_nv.hip", "unrotate_mat.hip", "givens.hip", "gemm.hip", "gemm_nv.hip", "api.cpp", "perm.cpp", "calib.cpp", "device.cpp"]
 HEADERS = ["fp4_device.hpp", "launch.hpp", "rotation.hpp", "rotate_kernels.hpp",
            "unrotate_kernels.hpp"]
 

@@ -194,6 +194,29 @@ int fp4_dequantize_r(const void* codes, int64_t ld_codes, const void* scales, in
   return launch_status();
 }
 
+int fp4_apply_channel_rotation(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                               const int32_t* perm, const int32_t* pairs, const float* cs,
+                               const int32_t* layer_start, int n_layers, int n_rot,
+                               void* out_bf16, int64_t ld_out, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 8 != 0 || ld_x < cols || ld_out < cols) return FP4_ERR_SHAPE;
+  if (n_layers < 0 || n_rot < 0) return FP4_ERR_SHAPE;
+  if (cols > fp4::kMaxPermCols || rows >= ((int64_t)1 << 31)) return FP4_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (!x_bf16 || !out_bf16) return FP4_ERR_NULL;
+  if (n_layers > 0 && !layer_start) return FP4_ERR_NULL;
+  if (n_rot > 0 && (!pairs || !cs || n_layers == 0)) return FP4_ERR_NULL;
+  if (!aligned(x_bf16, 16) || ld_x % 8 != 0 || !aligned(out_bf16, 16) || ld_out % 8 != 0)
+    return FP4_ERR_ALIGN;
+  if ((perm && !aligned(perm, 4)) || (pairs && !aligned(pairs, 4)) || (cs && !aligned(cs, 4)) ||
+      (layer_start && !aligned(layer_start, 4)))
+    return FP4_ERR_ALIGN;
+  if (x_bf16 == out_bf16 && ld_x != ld_out) return FP4_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  fp4::launch_givens_rows(rows, cols, x_bf16, ld_x, perm, pairs, cs, layer_start, n_layers,
+                          n_rot, out_bf16, ld_out, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 int fp4_gemm(const void* a_codes, int64_t ld_a, const void* a_scales, int64_t ld_sa,
              const float* a_ts, int mode_a, const void* b_codes, int64_t ld_b,
              const void* b_scales, int64_t ld_sb, const float* b_ts, int mode_b, int64_t m,

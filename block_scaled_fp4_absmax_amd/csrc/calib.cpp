@@ -246,3 +246,178 @@ extern "C" int fp4_calibrate_block_rotation(const uint16_t* x_host, int64_t rows
   if (loss_out) loss_out[1] = loss;
   return FP4_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Inter-block transform ("TORQ: Two-Level Orthogonal Rotation for MXFP4
+// Quantization", technical summary sec. 2(a)): an orthogonal transform that
+// makes every block's variance the same, built by iterated Givens rotations.
+// Reading: block variance = sum over the block's channels of the second
+// moment sum_r x[r, j]^2 on the sample (after the permutation). Each step
+// takes the block p of largest and q of smallest variance and moves
+// t = min(V_p - mean, mean - V_q) from p to q with one rotation of channel i
+// (largest second moment in p) and channel j (smallest in q), whose angle
+// solves the exact transfer equation with the pair's cross moment; a step
+// that cannot move all of t (the pair is too weak) moves what it can. So each
+// full step brings one block to the mean: at most (blocks - 1) full steps.
+// Channels are used once per layer, so the rotations of one layer are
+// disjoint and can be applied in parallel.
+namespace {
+
+struct Macro {
+  int64_t rows, cols;
+  int block;
+  std::vector<double> X;  // [cols][rows], the permuted sample, column-major
+  std::vector<double> E;  // [cols] second moments
+  std::vector<double> V;  // [blocks]
+
+  double* col(int64_t j) { return &X[j * rows]; }
+  void moment(int64_t j) {
+    const double* c = col(j);
+    double e = 0.0;
+    for (int64_t r = 0; r < rows; ++r) e += c[r] * c[r];
+    E[j] = e;
+  }
+  void block_sum(int64_t b) {
+    double v = 0.0;
+    for (int k = 0; k < block; ++k) v += E[b * block + k];
+    V[b] = v;
+  }
+  void rotate(int64_t i, int64_t j, double c, double s) {
+    double* xi = col(i);
+    double* xj = col(j);
+    for (int64_t r = 0; r < rows; ++r) {
+      const double a = xi[r], b = xj[r];
+      xi[r] = c * a - s * b;
+      xj[r] = s * a + c * b;
+    }
+    moment(i);
+    moment(j);
+  }
+  double spread() const {
+    double lo = V[0], hi = V[0], sum = 0.0;
+    for (double v : V) {
+      lo = std::min(lo, v);
+      hi = std::max(hi, v);
+      sum += v;
+    }
+    const double mean = sum / (double)V.size();
+    return mean > 0.0 ? (hi - lo) / mean : 0.0;
+  }
+};
+
+void load_sample(Macro& m, const uint16_t* x, int64_t ld_x, const int32_t* perm) {
+  m.X.assign(m.cols * m.rows, 0.0);
+  for (int64_t r = 0; r < m.rows; ++r)
+    for (int64_t j = 0; j < m.cols; ++j)
+      m.X[j * m.rows + r] = (double)bf16_to_f32(x[r * ld_x + (perm ? perm[j] : j)]);
+  m.E.assign(m.cols, 0.0);
+  for (int64_t j = 0; j < m.cols; ++j) m.moment(j);
+  m.V.assign(m.cols / m.block, 0.0);
+  for (int64_t b = 0; b < (int64_t)m.V.size(); ++b) m.block_sum(b);
+}
+
+}  // namespace
+
+extern "C" int fp4_calibrate_macro_rotation(const uint16_t* x_host, int64_t rows, int64_t cols,
+                                            int64_t ld_x, const int32_t* perm_host, int block,
+                                            double tol, int max_rot, int32_t* pairs_out,
+                                            float* cs_out, int32_t* layer_start_out,
+                                            int* n_rot_out, int* n_layers_out,
+                                            double* spread_out) {
+  if (!x_host || !n_rot_out || !n_layers_out || !layer_start_out) return FP4_ERR_NULL;
+  if (max_rot > 0 && (!pairs_out || !cs_out)) return FP4_ERR_NULL;
+  if (block != 16 && block != 32) return FP4_ERR_UNSUPPORTED;
+  if (rows <= 0 || cols <= 0 || cols % block != 0 || ld_x < cols) return FP4_ERR_SHAPE;
+  if (max_rot < 0 || !(tol >= 0.0)) return FP4_ERR_UNSUPPORTED;
+  if (rows * cols > ((int64_t)1 << 26)) return FP4_ERR_UNSUPPORTED;  // a sample, not a model
+  if (perm_host)
+    for (int64_t j = 0; j < cols; ++j)
+      if (perm_host[j] < 0 || perm_host[j] >= cols) return FP4_ERR_SHAPE;
+
+  Macro m;
+  m.rows = rows;
+  m.cols = cols;
+  m.block = block;
+  load_sample(m, x_host, ld_x, perm_host);
+  const int64_t nb = cols / block;
+  if (spread_out) spread_out[0] = m.spread();
+
+  std::vector<uint8_t> used(cols, 0);
+  int n = 0, layers = 0;
+  layer_start_out[0] = 0;
+  bool layer_open = false;
+  while (n < max_rot && m.spread() > tol) {
+    // the mean is taken afresh: the fp32 (cos, sin) kept below are orthogonal
+    // only to about 2^-24, so the total moves a little with every step
+    double total = 0.0;
+    int64_t p = 0, q = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+      total += m.V[b];
+      if (m.V[b] > m.V[p]) p = b;
+      if (m.V[b] < m.V[q]) q = b;
+    }
+    const double mean = total / (double)nb;
+    const double t_want = std::min(m.V[p] - mean, mean - m.V[q]);
+    // the pair: free channels of p (largest moment) and q (smallest); if
+    // they cannot move all of t, or none is free, a new layer frees them all
+    int64_t i = -1, j = -1;
+    double C = 0.0, A = 0.0, rad = 0.0, t_max = 0.0;
+    auto pick = [&]() {
+      i = j = -1;
+      for (int k = 0; k < block; ++k) {
+        const int64_t a = p * block + k, b = q * block + k;
+        if (!used[a] && (i < 0 || m.E[a] > m.E[i])) i = a;
+        if (!used[b] && (j < 0 || m.E[b] < m.E[j])) j = b;
+      }
+      if (i < 0 || j < 0) return;
+      // moment moved into j by the rotation of angle phi / 2:
+      //   A (1 - cos phi) + C sin phi = A - rad cos(phi + beta),
+      // A = (E_i - E_j) / 2, C = cross moment, rad = |(A, C)|, beta = atan2(C, A);
+      // at most A + rad
+      const double* xi = m.col(i);
+      const double* xj = m.col(j);
+      C = 0.0;
+      for (int64_t r = 0; r < rows; ++r) C += xi[r] * xj[r];
+      A = 0.5 * (m.E[i] - m.E[j]);
+      rad = std::hypot(A, C);
+      t_max = A + rad;
+    };
+    pick();
+    if ((i < 0 || j < 0 || t_max < t_want) && layer_open && n > layer_start_out[layers]) {
+      std::fill(used.begin(), used.end(), 0);
+      layer_start_out[++layers] = n;
+      pick();
+    }
+    if (i < 0 || j < 0 || !(t_max > 0.0)) break;  // no pair can move anything
+    layer_open = true;
+    const double t = std::min(t_want, t_max);
+    const double beta = std::atan2(C, A);
+    const double arg = std::max(-1.0, std::min(1.0, (A - t) / rad));
+    const double phi = std::acos(arg) - beta;
+    // the sample follows the rotation exactly as returned (fp32 cos, sin)
+    const float c = (float)std::cos(0.5 * phi), s = (float)std::sin(0.5 * phi);
+    m.rotate(i, j, (double)c, (double)s);
+    m.block_sum(p);
+    m.block_sum(q);
+    used[i] = used[j] = 1;
+    pairs_out[2 * n] = (int32_t)i;
+    pairs_out[2 * n + 1] = (int32_t)j;
+    cs_out[2 * n] = c;
+    cs_out[2 * n + 1] = s;
+    ++n;
+  }
+  if (layer_open && layer_start_out[layers] < n) ++layers;  // close the last, non-empty layer
+  layer_start_out[layers] = n;
+  *n_rot_out = n;
+  *n_layers_out = layers;
+  if (spread_out) {  // the spread the returned (fp32) rotations reach, evaluated afresh
+    load_sample(m, x_host, ld_x, perm_host);
+    for (int k = 0; k < n; ++k) {
+      m.rotate(pairs_out[2 * k], pairs_out[2 * k + 1], (double)cs_out[2 * k],
+               (double)cs_out[2 * k + 1]);
+    }
+    for (int64_t b = 0; b < nb; ++b) m.block_sum(b);
+    spread_out[1] = m.spread();
+  }
+  return FP4_OK;
+}

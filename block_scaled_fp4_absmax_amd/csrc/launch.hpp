@@ -85,4 +85,12 @@ void launch_mx_matrix_dequant_unrotate(const Shape& s, const int32_t* perm, cons
 void launch_channel_energy(int64_t rows, int64_t cols, int64_t ld_x, const void* x, float* energy,
                            hipStream_t st);
 
+// Rows of bf16: permutation (perm may be NULL), then n_layers layers of
+// disjoint Givens rotations (layer L = rotations layer_start[L] ..
+// layer_start[L + 1] - 1), in fp32, rounded to bf16 once. out may be x.
+void launch_givens_rows(int64_t rows, int64_t cols, const void* x, int64_t ld_x,
+                        const int32_t* perm, const int32_t* pairs, const float* cs,
+                        const int32_t* layer_start, int n_layers, int n_rot, void* out,
+                        int64_t ld_out, hipStream_t st);
+
 }  // namespace fp4

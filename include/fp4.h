@@ -347,6 +347,67 @@ int fp4_calibrate_block_rotation(const uint16_t* x_host, int64_t rows, int64_t c
                                  int64_t ld_x, const int32_t* perm_host, int iters, int angles,
                                  float* rotation_out, double* loss_out);
 
+/*
+ * fp4_calibrate_macro_rotation -- host-side, synchronous. The inter-block
+ * transform of [TORQ] sec. 2(a): an orthogonal transform, built from Givens
+ * rotations, after which every block has the same variance. Readings: the
+ * variance of a block is the sum over its channels of the second moment
+ * sum_r x[r, j]^2 of the sample (after perm); the start is the permutation
+ * (e.g. fp4_build_permutation's, which already balances most of it).
+ * Each step takes the block p of largest and q of smallest variance
+ * (ties: lowest index), moves t = min(V_p - mean, mean - V_q) from p to q with
+ * one rotation (x_i, x_j) <- (c x_i - s x_j, s x_i + c x_j) of the channel i
+ * of p with the largest second moment and the channel j of q with the
+ * smallest (both not yet used in the current layer; ties: lowest index),
+ * angle from the exact transfer equation with the pair's cross moment (the
+ * whole of t, or as much as the pair can move). The sample is kept rotated in
+ * fp64, so every step sees exact moments. Stops once
+ * (max V - min V) <= tol * mean V, or after max_rot rotations. A full step
+ * brings a block to the mean, so blocks - 1 steps suffice when no pair is
+ * too weak. Rotations are grouped in layers of disjoint channel pairs.
+ *
+ *  x_host           host bf16 [rows, ld_x]; rows * cols <= 2^26
+ *  perm_host        NULL (identity) or host int32[cols]
+ *  block            32 or 16; cols % block == 0
+ *  tol              >= 0, relative spread to reach
+ *  max_rot          >= 0
+ *  pairs_out        host int32[2 * max_rot]: (i, j) per rotation, in order
+ *  cs_out           host fp32[2 * max_rot]: (cos, sin) per rotation
+ *  layer_start_out  host int32[max_rot + 1]: layer L = rotations
+ *                   layer_start[L] .. layer_start[L + 1] - 1
+ *  n_rot_out, n_layers_out  host: counts written
+ *  spread_out       NULL or host double[2]: (max V - min V) / mean V before,
+ *                   and after the returned (fp32) rotations
+ */
+int fp4_calibrate_macro_rotation(const uint16_t* x_host, int64_t rows, int64_t cols,
+                                 int64_t ld_x, const int32_t* perm_host, int block, double tol,
+                                 int max_rot, int32_t* pairs_out, float* cs_out,
+                                 int32_t* layer_start_out, int* n_rot_out, int* n_layers_out,
+                                 double* spread_out);
+
+/*
+ * fp4_apply_channel_rotation -- the inter-block transform on every row of a
+ * bf16 matrix ([TORQ] sec. 2(a)): z = x[r, perm[.]] in fp32, then each layer
+ * of Givens rotations (x_i, x_j) <- (c x_i - s x_j, s x_i + c x_j), then
+ * out[r, .] = bf16(z) (RNE). Rotations within a layer must touch disjoint
+ * channels (as fp4_calibrate_macro_rotation writes them); they run in
+ * parallel. For activations this yields the input of fp4_rotate_quantize /
+ * fp4_rotate_quantize_r with perm = identity; for a consumer's weights W
+ * [n, cols] (one row per output) the same call gives W' with W' z = W x, the
+ * offline folding the pages describe.
+ *
+ *  x_bf16, out_bf16  device bf16 [rows, ld]; 16-byte aligned, ld % 8 == 0;
+ *                    out may be x (in place) when ld_out == ld_x
+ *  cols              cols % 8 == 0, cols <= 16384
+ *  perm              NULL or device int32[cols] (entries clamped into the row)
+ *  pairs, cs         device int32[2 n_rot], fp32[2 n_rot] (indices clamped)
+ *  layer_start       device int32[n_layers + 1] (clamped to 0 .. n_rot)
+ */
+int fp4_apply_channel_rotation(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                               const int32_t* perm, const int32_t* pairs, const float* cs,
+                               const int32_t* layer_start, int n_layers, int n_rot,
+                               void* out_bf16, int64_t ld_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -140,6 +140,19 @@ def test_rotate_and_dequant_validation(L):
     assert U(FAKE, 32, FAKE, 2, 4, 64, FAKE, FAKE, FAKE + 8, 64, None) == -3
     assert U(FAKE, 32, FAKE, 2, 4, 64, FAKE, FAKE + 1, FAKE, 64, None) == -3
     assert U(None, 32, None, 2, 0, 64, None, None, None, 64, None) == 0
+    # apply_channel_rotation(x, rows, cols, ld, perm, pairs, cs, layer_start, n_layers, n_rot,
+    #                        out, ld_out, stream)
+    A = L.fp4_apply_channel_rotation
+    assert A(FAKE, 4, 60, 64, None, FAKE, FAKE, FAKE, 1, 2, FAKE, 64, None) == -2  # cols % 8
+    assert A(FAKE, 4, 64, 64, None, FAKE, FAKE, FAKE, -1, 2, FAKE, 64, None) == -2
+    assert A(FAKE, 4, 32768, 32768, None, FAKE, FAKE, FAKE, 1, 2, FAKE, 32768, None) == -4
+    assert A(FAKE, 4, 64, 64, None, None, FAKE, FAKE, 1, 2, FAKE, 64, None) == -1  # pairs
+    assert A(FAKE, 4, 64, 64, None, FAKE, FAKE, None, 1, 2, FAKE, 64, None) == -1  # layers
+    assert A(FAKE, 4, 64, 64, None, FAKE, FAKE, FAKE, 0, 2, FAKE, 64, None) == -1  # no layer
+    assert A(FAKE + 2, 4, 64, 64, None, FAKE, FAKE, FAKE, 1, 2, FAKE, 64, None) == -3
+    assert A(FAKE, 4, 64, 64, FAKE + 1, FAKE, FAKE, FAKE, 1, 2, FAKE, 64, None) == -3
+    assert A(FAKE, 4, 64, 64, None, FAKE, FAKE, FAKE, 1, 2, FAKE, 72, None) == -4  # in place
+    assert A(None, 0, 64, 64, None, None, None, None, 0, 0, None, 64, None) == 0
     E = L.fp4_channel_energy
     assert E(FAKE, 4, 48, 48, FAKE, None) == -2
     assert E(None, 4, 64, 64, FAKE, None) == -1

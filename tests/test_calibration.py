@@ -7,6 +7,8 @@ step: a Givens rotation of a badly balanced, complementary coordinate pair at
 the best of a finite set of angles) on the code-book occupancy equilibrium
 loss, started from the Hadamard.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -135,3 +137,97 @@ def test_calibration_validation(L):
     loss = np.zeros(2)
     assert C(x.ctypes.data, 4, 64, 64, None, 5, 8, R.ctypes.data, loss.ctypes.data) == 0
     assert np.array_equal(R, _h0()) and loss[0] == loss[1] == 0.875
+
+
+# ------------------------------------------------- inter-block transform --
+def _macro(L, x, perm, block=32, tol=1e-6, max_rot=None):
+    rows, cols = x.shape
+    if max_rot is None:
+        max_rot = 4 * (cols // block)
+    pairs = np.zeros((max_rot, 2), np.int32)
+    cs = np.zeros((max_rot, 2), np.float32)
+    starts = np.zeros(max_rot + 1, np.int32)
+    n, nl = ctypes.c_int(0), ctypes.c_int(0)
+    spread = np.zeros(2)
+    p = None if perm is None else np.ascontiguousarray(perm, np.int32).ctypes.data
+    st = L.fp4_calibrate_macro_rotation(x.ctypes.data, rows, cols, cols, p, block, tol, max_rot,
+                                        pairs.ctypes.data, cs.ctypes.data, starts.ctypes.data,
+                                        ctypes.byref(n), ctypes.byref(nl), spread.ctypes.data)
+    assert st == 0
+    return pairs[:n.value], cs[:n.value], starts[:nl.value + 1], spread
+
+
+def _block_spread(z, block):
+    v = (z.astype(np.float64) ** 2).sum(0).reshape(-1, block).sum(1)
+    return (v.max() - v.min()) / v.mean(), v
+
+
+@pytest.mark.parametrize("block,use_perm", [(32, True), (32, False), (16, True)])
+def test_macro_rotation_equalises_block_variances(L, orc, block, use_perm):
+    x = inputs.gen_c4(rows=256, cols=2048)
+    perm = orc.build_perm(orc.channel_energy(x).astype(np.float32), block) if use_perm else None
+    pairs, cs, starts, spread = _macro(L, x, perm, block)
+    nb = 2048 // block
+    s0, _ = _block_spread(orc.apply_givens(x, perm, pairs[:0], cs[:0]), block)
+    z = orc.apply_givens(x, perm, pairs, cs.astype(np.float64))
+    s1, _ = _block_spread(z, block)
+    assert abs(spread[0] - s0) <= 1e-12 * s0 and abs(spread[1] - s1) <= 1e-9
+    assert s1 <= 1e-5 < s0
+    # after the permutation every step here is a full one: one per block but
+    # the last; from the identity some pairs are too weak and steps are split
+    assert len(pairs) <= (nb - 1 if use_perm else 4 * nb)
+    # layers: consecutive, and the channels of a layer are disjoint
+    assert starts[0] == 0 and starts[-1] == len(pairs) and np.all(np.diff(starts) > 0)
+    for a, b in zip(starts[:-1], starts[1:]):
+        ch = pairs[a:b].reshape(-1)
+        assert len(np.unique(ch)) == len(ch)
+    assert np.allclose(cs[:, 0] ** 2 + cs[:, 1] ** 2, 1.0, atol=1e-6)
+    # every pair joins two different blocks
+    assert np.all(pairs[:, 0] // block != pairs[:, 1] // block)
+
+
+def test_macro_rotation_first_step(L, orc):
+    """The first rotation pairs the strongest channel of the heaviest block
+    with the weakest channel of the lightest, and brings one of the two
+    blocks to the mean."""
+    x = inputs.gen_c4(rows=256, cols=2048)
+    perm = orc.build_perm(orc.channel_energy(x).astype(np.float32), 32)
+    pairs, cs, _, _ = _macro(L, x, perm)
+    xp = inputs.bf16_bits_to_f32(x).astype(np.float64)[:, perm]
+    e = (xp ** 2).sum(0)
+    v = e.reshape(-1, 32).sum(1)
+    p, q = int(np.argmax(v)), int(np.argmin(v))
+    i = 32 * p + int(np.argmax(e[32 * p:32 * p + 32]))
+    j = 32 * q + int(np.argmin(e[32 * q:32 * q + 32]))
+    assert tuple(pairs[0]) == (i, j)
+    _, v1 = _block_spread(orc.apply_givens(x, perm, pairs[:1], cs[:1].astype(np.float64)), 32)
+    mean = v.mean()
+    assert min(abs(v1[p] - mean), abs(v1[q] - mean)) <= 1e-6 * mean
+    assert abs(v1.sum() - v.sum()) <= 1e-9 * v.sum()
+
+
+def test_macro_rotation_validation(L):
+    x = np.zeros((4, 64), np.uint16)
+    out = np.zeros(16, np.int32)
+    cs = np.zeros(16, np.float32)
+    n = ctypes.c_int(0)
+    C = L.fp4_calibrate_macro_rotation
+    args = [x.ctypes.data, 4, 64, 64, None, 32, 1e-6, 8, out.ctypes.data, cs.ctypes.data,
+            out.ctypes.data, ctypes.byref(n), ctypes.byref(n), None]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return C(*a)
+
+    assert call(a0=None) == -1
+    assert call(a5=24) == -4          # block
+    assert call(a2=48, a3=48) == -2   # cols % block
+    assert call(a6=-1.0) == -4        # tol
+    assert call(a7=-1) == -4          # max_rot
+    assert call(a8=None) == -1
+    bad = np.full(64, 99, np.int32)
+    assert call(a4=bad.ctypes.data) == -2
+    # an all-zero sample: nothing to move
+    assert call() == 0 and n.value == 0
