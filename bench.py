@@ -315,6 +315,49 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
         out[f"c4_sqnr_db_mxint4_{name}"] = round(sqnr_db(torch, xf, xh.float()), 3)
     del xf
 
+    # the full two-level rotation: the inter-block Givens layers (calibrated on
+    # 256 rows after the permutation) applied on the GPU, then the learned block
+    # matrix (calibrated on 256 rows of their output) fused with MXFP4
+    log("[bench] two-level rotation rows (Givens layers, learned block matrix)")
+    t0 = time.perf_counter()
+    macro = fp4.calibrate_macro_rotation(xs[0][:256], perm.cpu())
+    macro_ms = (time.perf_counter() - t0) * 1e3
+    md = macro.to("cuda")
+    zs = [torch.empty_like(xs[0]) for _ in range(n)]
+    ms = timed(torch, lambda i: fp4.apply_channel_rotation(xs[i % n], md, perm, out=zs[i % n]),
+               20, 3)
+    out["c4_givens_layers_apply"] = gbs(ms, el, 4)
+    t0 = time.perf_counter()
+    R, rloss = fp4.calibrate_block_rotation(zs[0][:256], None, iters=30, angles=32)
+    block_ms = (time.perf_counter() - t0) * 1e3
+    rt = R.cuda()
+    ident = torch.arange(cols, dtype=torch.int32, device="cuda")
+    ms = timed(torch, lambda i: fp4.rotate_quantize_r(zs[i % n], ident, rt, codes=codes[i % n],
+                                                      scales=scales[i % n]), 20, 3)
+    out["c4_mxfp4_learned_r_quantize"] = gbs(ms, el, B_MX)
+    ms = timed(torch, lambda i: fp4.dequantize_r(codes[i % n], scales[i % n], ident, rt,
+                                                 out=outb), 20, 3)
+    out["c4_mxfp4_learned_r_dequantize"] = gbs(ms, el, B_MX)
+    xf, zf = xs[0].float(), zs[0].float()
+    c, sc, _ = fp4.rotate_quantize_r(zs[0], ident, rt)
+    q_gr = sqnr_db(torch, zf, fp4.dequantize_r(c, sc, ident, rt).float())
+    c, sc, _ = fp4.rotate_quantize(zs[0], None, 32)
+    q_gh = sqnr_db(torch, zf, fp4.dequantize(c, sc, fp4.MXFP4, hadamard=32).float())
+    Rp, _ = fp4.calibrate_block_rotation(xs[0][:256], perm.cpu(), iters=30, angles=32)
+    c, sc, _ = fp4.rotate_quantize_r(xs[0], perm, Rp.cuda())
+    q_pr = sqnr_db(torch, xf, fp4.dequantize_r(c, sc, perm, Rp.cuda()).float())
+    out["c4_two_level"] = {
+        "givens_rotations": macro.n_rot, "givens_layers": macro.n_layers,
+        "block_variance_spread_before_after": [round(v, 9) for v in macro.spread],
+        "givens_calibration_ms": round(macro_ms, 1),
+        "block_matrix_calibration_ms": round(block_ms, 1),
+        "occupancy_loss_hadamard_learned": [round(v, 6) for v in rloss],
+        # round trip in the rotated basis (the transforms are orthogonal)
+        "sqnr_db_perm_learned_r": round(q_pr, 3),
+        "sqnr_db_perm_givens_h32": round(q_gh, 3),
+        "sqnr_db_perm_givens_learned_r": round(q_gr, 3)}
+    del zs, xf, zf
+
     # the heavy-tailed 8192 x 8192 activations: the Hadamard alone, every format
     log("[bench] generating c3 for the rotation rows")
     x3 = dev_copies(torch, inputs.gen_c3(), 1)[0]
