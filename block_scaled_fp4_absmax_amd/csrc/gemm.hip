@@ -258,6 +258,165 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmArgs g) {
     }
 }
 
+// Decode-shaped products (m <= 32): a work-group of eight waves computes one
+// 32 x 32 tile of C (rows of A past m read as zeros), so an n-wide product
+// launches n / 32 work-groups; wave w takes the 256-K super-steps w, w + 8,
+// ... (the waves of a work-group read neighbouring pieces of each row) and
+// the partial tiles are added in LDS in wave order (deterministic). A
+// super-step of an operand is 32 rows x 128 code bytes: it is loaded with
+// each 128-byte row piece read by eight consecutive lanes (whole lines per
+// instruction; one row per lane measured 1.5x slower), kept in registers
+// while later steps load, then passed through the wave's own LDS buffer
+// (16-byte chunks XOR-swizzled by row, so that the writes and the reads are
+// free of bank conflicts) to the MFMA layout: lane (r, h) takes the 64 bytes
+// 64 h .. 64 h + 63 of row r (blocks 4 h .. 4 h + 3), with the dword of their
+// four scale bytes; MFMA c of the step takes block 4 h + c in lane half h for
+// both operands, which pairs the same K block of A and B in every lane.
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnySets = 4;  // super-steps of loads in flight per wave
+
+struct SkinnyStep {
+  u32x4_t a[4], b[4];  // row 8 c + lane / 8, 16-byte chunk lane % 8
+  uint32_t sa, sb;     // row lane % 32, blocks 4 (lane / 32) .. + 3
+};
+
+// LDS byte offset of 16-byte chunk j (0..7) of row r in a 32 x 128-byte
+// operand piece.
+__device__ __forceinline__ uint32_t skinny_off(uint32_t r, uint32_t j) {
+  return 128u * r + 16u * (j ^ (r & 7u));
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(64 * kSkinnyWaves) void mx_gemm_skinny_kernel(GemmArgs g) {
+  // per wave: the A piece, then the B piece, of the step being multiplied;
+  // afterwards the same memory holds the partial tiles of waves 1..7
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSkinnyWaves * 8192];
+  const int32_t n0 = blockIdx.x * 32;
+  const int32_t rows_b = min(32, g.n - n0);
+  const rsrc_t ra = make_rsrc(g.a, (uint32_t)(g.m * g.ld_a));
+  const rsrc_t rsa = make_rsrc(g.sa, (uint32_t)(g.m * g.ld_sa));
+  const rsrc_t rb = make_rsrc(g.b + (int64_t)n0 * g.ld_b, (uint32_t)(rows_b * g.ld_b));
+  const rsrc_t rsb = make_rsrc(g.sb + (int64_t)n0 * g.ld_sb, (uint32_t)(rows_b * g.ld_sb));
+  const uint32_t lane = threadIdx.x & 63u, r = lane & 31u, h = lane >> 5;
+  const int32_t w = (int32_t)(threadIdx.x >> 6);
+  uint8_t* const la = smem + 8192u * (uint32_t)w;
+  uint8_t* const lb = la + 4096u;
+  const uint32_t kbytes = (uint32_t)g.k / 2u, nblk = (uint32_t)g.k / 32u;
+  const int32_t steps = (g.k + 255) / 256;
+  const int32_t cnt = steps > w ? (steps - w + kSkinnyWaves - 1) / kSkinnyWaves : 0;
+
+  // loads of the wave's i-th super-step s = w + 8 i (i >= cnt or past K:
+  // offsets out of range, which read zeros without touching memory)
+  auto load = [&](int32_t i, SkinnyStep& t) {
+    const int32_t s = w + kSkinnyWaves * i;
+    const bool live = i < cnt;
+    const uint32_t off = 128u * (uint32_t)s + 16u * (lane & 7u);
+    const bool ok = live && off < kbytes;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t row = 8u * c + (lane >> 3);
+      t.a[c] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? row * (uint32_t)g.ld_a + off : kOob,
+                                                     0, 0);
+      t.b[c] = __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? row * (uint32_t)g.ld_b + off : kOob,
+                                                     0, 0);
+    }
+    // blk is a multiple of 4 below nblk <= ld_s (a multiple of 4): the dword
+    // stays inside the row; bytes past K are cleared before use
+    const uint32_t blk = 8u * (uint32_t)s + 4u * h;
+    const bool oks = live && blk < nblk;
+    t.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, oks ? r * (uint32_t)g.ld_sa + blk : kOob, 0, 0);
+    t.sb = __builtin_amdgcn_raw_buffer_load_b32(rsb, oks ? r * (uint32_t)g.ld_sb + blk : kOob, 0, 0);
+  };
+
+  f32x16_t acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  auto mma = [&](int32_t i, const SkinnyStep& t) {
+    const int32_t s = w + kSkinnyWaves * i;
+    const uint32_t blk = 8u * (uint32_t)s + 4u * h;
+    const uint32_t keep = blk + 4u <= nblk ? 0xFFFFFFFFu
+                          : blk >= nblk   ? 0u
+                                          : (1u << (8u * (nblk - blk))) - 1u;
+    const uint32_t sa = t.sa & keep, sb = t.sb & keep;
+    // through the wave's LDS buffer into the MFMA layout
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t o = skinny_off(8u * c + (lane >> 3), lane & 7u);
+      *reinterpret_cast<u32x4_t*>(la + o) = t.a[c];
+      *reinterpret_cast<u32x4_t*>(lb + o) = t.b[c];
+    }
+    wave_sync();
+    u32x4_t fa[4], fb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t o = skinny_off(r, 4u * h + c);
+      fa[c] = *reinterpret_cast<const u32x4_t*>(la + o);
+      fb[c] = *reinterpret_cast<const u32x4_t*>(lb + o);
+    }
+    wave_sync();  // the buffer is written again by the next step
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const i32x8_t va{(int32_t)fa[c].x, (int32_t)fa[c].y, (int32_t)fa[c].z, (int32_t)fa[c].w,
+                       0, 0, 0, 0};
+      const i32x8_t vb{(int32_t)fb[c].x, (int32_t)fb[c].y, (int32_t)fb[c].z, (int32_t)fb[c].w,
+                       0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          va, vb, acc, 4, 4, 0, (int32_t)((sa >> (8 * c)) & 0xFFu), 0,
+          (int32_t)((sb >> (8 * c)) & 0xFFu));
+    }
+  };
+  SkinnyStep t[kSkinnySets];
+#pragma unroll
+  for (int j = 0; j < kSkinnySets; ++j) load(j, t[j]);
+  auto step = [&](auto J, int32_t i) {
+    constexpr int j = decltype(J)::value;
+    mma(i, t[j]);
+    load(i + kSkinnySets, t[j]);
+  };
+  int32_t i = 0;
+  for (; i + kSkinnySets - 1 < cnt; i += kSkinnySets) {
+    step(std::integral_constant<int, 0>{}, i);
+    step(std::integral_constant<int, 1>{}, i + 1);
+    step(std::integral_constant<int, 2>{}, i + 2);
+    step(std::integral_constant<int, 3>{}, i + 3);
+  }
+  if (i < cnt) step(std::integral_constant<int, 0>{}, i);
+  if (i + 1 < cnt) step(std::integral_constant<int, 1>{}, i + 1);
+  if (i + 2 < cnt) step(std::integral_constant<int, 2>{}, i + 2);
+
+  __syncthreads();  // every wave is done with its operand buffer
+  f32x16_t* part = reinterpret_cast<f32x16_t*>(smem);  // [kSkinnyWaves - 1][64]
+  if (w > 0) part[64 * (w - 1) + lane] = acc;
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int v = 0; v < kSkinnyWaves - 1; ++v) {
+    const f32x16_t p = part[64 * v + lane];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] += p[e];
+  }
+  // lane (n, h) holds column n, rows 8 (e / 4) + 4 h + e % 4
+  const int32_t col = n0 + (int32_t)r;
+  if (col >= g.n) return;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int32_t row = 8 * (e / 4) + 4 * (int32_t)h + e % 4;
+    if (row >= g.m) continue;
+    if constexpr (kBf16Out) {
+      const uint32_t p = pack_bf16x2(acc[e], 0.0f);
+      static_cast<uint16_t*>(g.c)[(int64_t)row * g.ld_c + col] = (uint16_t)(p & 0xFFFFu);
+    } else {
+      static_cast<float*>(g.c)[(int64_t)row * g.ld_c + col] = acc[e];
+    }
+  }
+}
+
 template <int WM, int WN>
 void launch_tiles(const GemmArgs& g, bool bf16_out, hipStream_t st) {
   const int64_t tiles = (((int64_t)g.m + 64 * WM - 1) / (64 * WM)) *
@@ -276,6 +435,14 @@ void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a
   GemmArgs g{static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(sa),
              static_cast<const uint8_t*>(b), static_cast<const uint8_t*>(sb), c,
              ld_a, ld_sa, ld_b, ld_sb, ld_c, (int32_t)m, (int32_t)n, (int32_t)k};
+  if (m <= 32) {  // decode-shaped: one 32 x 32 tile of C per work-group
+    const unsigned grid = (unsigned)((n + 31) / 32);
+    if (bf16_out)
+      hipLaunchKernelGGL((mx_gemm_skinny_kernel<true>), dim3(grid), dim3(64 * kSkinnyWaves), 0, st, g);
+    else
+      hipLaunchKernelGGL((mx_gemm_skinny_kernel<false>), dim3(grid), dim3(64 * kSkinnyWaves), 0, st, g);
+    return;
+  }
 #ifdef FP4_GEMM_TILE
   constexpr int kW = FP4_GEMM_TILE;
   launch_tiles<kW, kW>(g, bf16_out, st);

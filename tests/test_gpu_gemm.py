@@ -79,7 +79,11 @@ def _check(orc, ac, as_, bc, bs, k, bf16=False, pad=0):
 # the 256 x 256 work-group tiles
 @pytest.mark.parametrize("m,n,k", [(128, 128, 128), (1, 1, 32), (37, 45, 96), (200, 300, 4160),
                                    (1, 512, 8192), (256, 384, 8192), (513, 129, 1024),
-                                   (2048, 2304, 1024), (2100, 2050, 544)])
+                                   (2048, 2304, 1024), (2100, 2050, 544),
+                                   # m <= 32 takes the decode-shaped kernel (K split over
+                                   # eight waves, a 32 x 32 tile per work-group)
+                                   (16, 2048, 8192), (32, 1000, 4160), (7, 300, 96),
+                                   (1, 33, 544), (31, 64, 28672), (16, 96, 256)])
 def test_gemm_random_codes(orc, m, n, k):
     note(f"case: MXFP4 GEMM {m}x{n}x{k} random codes and scales")
     rng = np.random.default_rng(m + 7 * n + k)
@@ -95,6 +99,21 @@ def test_gemm_bf16_out_and_strides(orc):
     bc, bs = _rand_operand(rng, 70, 544)
     _check(orc, ac, as_, bc, bs, 544, bf16=True, pad=32)
     _check(orc, ac, as_, bc, bs, 544, bf16=False, pad=16)
+
+
+def test_gemm_decode_shaped_strides_and_nan(orc):
+    note("case: MXFP4 GEMM m <= 32: padded strides, bf16 out, NaN scale in one block")
+    rng = np.random.default_rng(13)
+    ac, as_ = _rand_operand(rng, 20, 544)
+    bc, bs = _rand_operand(rng, 70, 544)
+    _check(orc, ac, as_, bc, bs, 544, bf16=True, pad=32)
+    _check(orc, ac, as_, bc, bs, 544, bf16=False, pad=16)
+    as_[5, 2] = 0xFF
+    out = fp4.gemm(torch.from_numpy(ac).cuda(), _scales_dev(as_, 0), torch.from_numpy(bc).cuda(),
+                   _scales_dev(bs, 0), k=544)
+    torch.cuda.synchronize()
+    c = out.cpu().numpy()
+    assert np.all(np.isnan(c[5])) and not np.isnan(np.delete(c, 5, 0)).any()
 
 
 def test_gemm_k_zero_and_empty(orc):
