@@ -226,6 +226,185 @@ __global__ __launch_bounds__(256) void nv_gemm_kernel(NvGemmArgs g) {
     }
 }
 
+// Decode-shaped products (m <= 32), as the MXFP4 decode kernel: a
+// work-group of eight waves computes one 32 x 32 tile of C, wave w takes the
+// 256-K super-steps w, w + 8, ..., each operand's 32 rows x 128 code bytes
+// are loaded with eight consecutive lanes per 128-byte row piece and passed
+// through the wave's XOR-swizzled LDS buffer, so that lane (r, h) holds the
+// 128 elements 128 h .. 128 h + 127 of row r of the step (16 dwords) and their
+// 8 scale bytes. MFMA q (0..15) of the step takes dword q, eight elements,
+// from both operands in both lane halves (the same K values of A and B in
+// every lane), decoded exactly to bf16 with the block scale of that dword
+// (byte q / 2). Partial tiles are added in LDS in wave order.
+constexpr int kNvSkinnyWaves = 8;
+constexpr int kNvSkinnySets = 3;
+
+struct NvSkinnyStep {
+  u32x4_t a[4], b[4];  // row 8 c + lane / 8, 16-byte chunk lane % 8
+  uint32_t sa[2], sb[2];  // row lane % 32: scale bytes 8 h .. 8 h + 7 of the step
+};
+
+__device__ __forceinline__ uint32_t nv_skinny_off(uint32_t r, uint32_t j) {
+  return 128u * r + 16u * (j ^ (r & 7u));
+}
+
+__device__ __forceinline__ void nv_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Eight E2M1 codes of one dword, decoded with scale byte sbyte (kMode as for
+// NvOperand::store), as four bf16 pairs.
+template <int kMode>
+__device__ __forceinline__ nbf16x8_t nv_decode8(uint32_t wd, uint32_t sbyte) {
+  const float sc = kMode == 2 ? e3m3_decode(sbyte) : e4m3_decode(kMode ? (sbyte & 0x7Fu) : sbyte);
+  const float special = kMode == 2 ? weight_special(sbyte) : (sbyte & 0x80u) ? -5.0f : 5.0f;
+  float v[8];
+#define FP4_NV_DEC2(sel)                                                          \
+  {                                                                               \
+    const float2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, sel);   \
+    v[2 * sel] = p.x;                                                             \
+    v[2 * sel + 1] = p.y;                                                         \
+  }
+  FP4_NV_DEC2(0) FP4_NV_DEC2(1) FP4_NV_DEC2(2) FP4_NV_DEC2(3)
+#undef FP4_NV_DEC2
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (kMode && __float_as_uint(v[e]) == 0x80000000u) v[e] = special;
+    v[e] *= sc;  // exact: at most 7 significant bits
+  }
+  const u32x4_t o{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                  pack_bf16x2(v[6], v[7])};
+  return __builtin_bit_cast(nbf16x8_t, o);
+}
+
+template <int kModeA, int kModeB, bool kBf16Out>
+__global__ __launch_bounds__(64 * kNvSkinnyWaves) void nv_gemm_skinny_kernel(NvGemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kNvSkinnyWaves * 8192];
+  const int32_t n0 = blockIdx.x * 32;
+  const int32_t rows_b = min(32, g.n - n0);
+  const rsrc_t ra = make_rsrc(g.a, (uint32_t)(g.m * g.ld_a));
+  const rsrc_t rsa = make_rsrc(g.sa, (uint32_t)(g.m * g.ld_sa));
+  const rsrc_t rb = make_rsrc(g.b + (int64_t)n0 * g.ld_b, (uint32_t)(rows_b * g.ld_b));
+  const rsrc_t rsb = make_rsrc(g.sb + (int64_t)n0 * g.ld_sb, (uint32_t)(rows_b * g.ld_sb));
+  const uint32_t lane = threadIdx.x & 63u, r = lane & 31u, h = lane >> 5;
+  const int32_t w = (int32_t)(threadIdx.x >> 6);
+  uint8_t* const la = smem + 8192u * (uint32_t)w;
+  uint8_t* const lb = la + 4096u;
+  const uint32_t kbytes = (uint32_t)g.k / 2u, nblk = (uint32_t)g.k / 16u;
+  const int32_t steps = (g.k + 255) / 256;
+  const int32_t cnt = steps > w ? (steps - w + kNvSkinnyWaves - 1) / kNvSkinnyWaves : 0;
+
+  // loads of the wave's i-th super-step (past the list or past K: offsets out
+  // of range, which read zeros without touching memory; code 0 decodes to +0
+  // whatever the scale byte)
+  auto load = [&](int32_t i, NvSkinnyStep& t) __attribute__((always_inline)) {
+    const int32_t s = w + kNvSkinnyWaves * i;
+    const bool live = i < cnt;
+    const uint32_t off = 128u * (uint32_t)s + 16u * (lane & 7u);
+    const bool ok = live && off < kbytes;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t row = 8u * c + (lane >> 3);
+      t.a[c] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? row * (uint32_t)g.ld_a + off : kOob,
+                                                     0, 0);
+      t.b[c] = __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? row * (uint32_t)g.ld_b + off : kOob,
+                                                     0, 0);
+    }
+    // scale bytes in 16-bit pieces (rows are 2-byte aligned); an even block
+    // index below nblk (even, as k % 32 == 0) covers both of its blocks
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t blk = 16u * (uint32_t)s + 8u * h + 2u * q;
+      const bool oks = live && blk < nblk;
+      const uint32_t va = __builtin_amdgcn_raw_buffer_load_b16(
+          rsa, oks ? r * (uint32_t)g.ld_sa + blk : kOob, 0, 0);
+      const uint32_t vb = __builtin_amdgcn_raw_buffer_load_b16(
+          rsb, oks ? r * (uint32_t)g.ld_sb + blk : kOob, 0, 0);
+      if (q % 2 == 0) {
+        t.sa[q / 2] = va;
+        t.sb[q / 2] = vb;
+      } else {
+        t.sa[q / 2] |= va << 16;
+        t.sb[q / 2] |= vb << 16;
+      }
+    }
+  };
+
+  nf32x16_t acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  auto mma = [&](const NvSkinnyStep& t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t o = nv_skinny_off(8u * c + (lane >> 3), lane & 7u);
+      *reinterpret_cast<u32x4_t*>(la + o) = t.a[c];
+      *reinterpret_cast<u32x4_t*>(lb + o) = t.b[c];
+    }
+    nv_wave_sync();
+    u32x4_t fa[4], fb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t o = nv_skinny_off(r, 4u * h + c);
+      fa[c] = *reinterpret_cast<const u32x4_t*>(la + o);
+      fb[c] = *reinterpret_cast<const u32x4_t*>(lb + o);
+    }
+    nv_wave_sync();  // the buffer is written again by the next step
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t sba = (t.sa[q / 8] >> (8 * ((q / 2) % 4))) & 0xFFu;
+      const uint32_t sbb = (t.sb[q / 8] >> (8 * ((q / 2) % 4))) & 0xFFu;
+      const nbf16x8_t da = nv_decode8<kModeA>(fa[q / 4][q % 4], sba);
+      const nbf16x8_t db = nv_decode8<kModeB>(fb[q / 4][q % 4], sbb);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, db, acc, 0, 0, 0);
+    }
+  };
+  NvSkinnyStep t[kNvSkinnySets];
+#pragma unroll
+  for (int j = 0; j < kNvSkinnySets; ++j) load(j, t[j]);
+  auto step = [&](auto J, int32_t i) __attribute__((always_inline)) {
+    constexpr int j = decltype(J)::value;
+    mma(t[j]);
+    load(i + kNvSkinnySets, t[j]);
+  };
+  int32_t i = 0;
+  for (; i + kNvSkinnySets - 1 < cnt; i += kNvSkinnySets) {
+    step(std::integral_constant<int, 0>{}, i);
+    step(std::integral_constant<int, 1>{}, i + 1);
+    step(std::integral_constant<int, 2>{}, i + 2);
+  }
+  if (i < cnt) step(std::integral_constant<int, 0>{}, i);
+  if (i + 1 < cnt) step(std::integral_constant<int, 1>{}, i + 1);
+
+  __syncthreads();  // every wave is done with its operand buffer
+  nf32x16_t* part = reinterpret_cast<nf32x16_t*>(smem);  // [kNvSkinnyWaves - 1][64]
+  if (w > 0) part[64 * (w - 1) + lane] = acc;
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int v = 0; v < kNvSkinnyWaves - 1; ++v) {
+    const nf32x16_t p = part[64 * v + lane];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] += p[e];
+  }
+  const float ts = *g.ta * *g.tb;
+  const int32_t col = n0 + (int32_t)r;
+  if (col >= g.n) return;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int32_t row = 8 * (e / 4) + 4 * (int32_t)h + e % 4;
+    if (row >= g.m) continue;
+    const float v = acc[e] * ts;
+    if constexpr (kBf16Out) {
+      const uint32_t p = pack_bf16x2(v, 0.0f);
+      static_cast<uint16_t*>(g.c)[(int64_t)row * g.ld_c + col] = (uint16_t)(p & 0xFFFFu);
+    } else {
+      static_cast<float*>(g.c)[(int64_t)row * g.ld_c + col] = v;
+    }
+  }
+}
+
 template <int WM, int WN, int kMa, int kMb>
 void nv_launch(const NvGemmArgs& g, bool bf16_out, hipStream_t st) {
   const int64_t tiles = (((int64_t)g.m + 64 * WM - 1) / (64 * WM)) *
@@ -240,6 +419,16 @@ void nv_launch(const NvGemmArgs& g, bool bf16_out, hipStream_t st) {
 
 template <int kMa, int kMb>
 void nv_tiles(const NvGemmArgs& g, bool bf16_out, hipStream_t st) {
+  if (g.m <= 32) {  // decode-shaped: one 32 x 32 tile of C per work-group
+    const unsigned grid = (unsigned)((g.n + 31) / 32);
+    if (bf16_out)
+      hipLaunchKernelGGL((nv_gemm_skinny_kernel<kMa, kMb, true>), dim3(grid),
+                         dim3(64 * kNvSkinnyWaves), 0, st, g);
+    else
+      hipLaunchKernelGGL((nv_gemm_skinny_kernel<kMa, kMb, false>), dim3(grid),
+                         dim3(64 * kNvSkinnyWaves), 0, st, g);
+    return;
+  }
   if (g.m >= 2048 && g.n >= 2048)
     nv_launch<4, 4, kMa, kMb>(g, bf16_out, st);
   else

@@ -201,14 +201,17 @@ def _check_nv(orc, ac, as_, ta, ra, bc, bs, tb, rb, k, bf16=False):
 @pytest.mark.parametrize("m,n,k,ra,rb", [
     (128, 128, 128, False, False), (128, 128, 128, True, True), (37, 45, 96, True, False),
     (200, 300, 4160, False, True), (1, 512, 8192, True, True), (2048, 2304, 1024, True, True),
-    (2100, 2050, 544, False, False)])
+    (2100, 2050, 544, False, False),
+    # m <= 32: the decode-shaped kernel
+    (16, 2048, 8192, True, True), (32, 1000, 4160, False, True), (7, 300, 96, True, False),
+    (1, 33, 544, False, False), (31, 64, 28672, True, True), (20, 70, 1056, False, False)])
 def test_nv_gemm_random_codes(orc, m, n, k, ra, rb):
     note(f"case: NVFP4 GEMM {m}x{n}x{k} razer A={ra} B={rb}")
     rng = np.random.default_rng(m + 3 * n + k + ra + 2 * rb)
     ac, as_ = _rand_nv(rng, m, k, ra)
     bc, bs = _rand_nv(rng, n, k, rb)
     _check_nv(orc, ac, as_, float(np.float32(0.0371)), ra, bc, bs, float(np.float32(2.5e-3)), rb,
-              k, bf16=(m == 37))
+              k, bf16=(m in (37, 20)))
 
 
 def test_nv_gemm_of_quantized_layer(orc):

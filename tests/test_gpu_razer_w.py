@@ -108,7 +108,7 @@ def test_razer_w_zero_tensor(orc):
     assert float(ts.cpu()[0]) == 1.0 and not np_u8(c).any() and not np_u8(s).any()
 
 
-@pytest.mark.parametrize("m,n,k", [(128, 256, 1024), (2048, 2048, 512)])
+@pytest.mark.parametrize("m,n,k", [(128, 256, 1024), (2048, 2048, 512), (16, 512, 2048)])
 def test_gemm_razer_activations_razer_w_weights(orc, m, n, k):
     """The pages' weight-and-activation setting: activations NVFP4 + RaZeR,
     weights RaZeR for weights, both quantized on the GPU, then the GEMM."""
