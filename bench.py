@@ -439,7 +439,7 @@ def gemm_rows(torch, fp4, fmt):
     kw = dict(fmt=fp4.NVFP4, a_ts=ts, b_ts=ts, mode_a=fp4.RAZER, mode_b=fp4.RAZER) if nv else {}
     rows = {}
     for m, n, k in ((4096, 8192, 8192), (4096, 28672, 8192), (4096, 8192, 28672),
-                    (16, 8192, 8192)):
+                    (16, 8192, 8192), (32, 28672, 8192)):
         a = torch.randint(0, 256, (m, k // 2), dtype=torch.uint8, device="cuda", generator=g)
         sa = torch.randint(lo, hi, (m, k // blk), dtype=torch.uint8, device="cuda", generator=g)
         b = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device="cuda", generator=g)
