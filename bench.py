@@ -327,6 +327,9 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     ms = timed(torch, lambda i: fp4.apply_channel_rotation(xs[i % n], md, perm, out=zs[i % n]),
                20, 3)
     out["c4_givens_layers_apply"] = gbs(ms, el, 4)
+    ms = timed(torch, lambda i: fp4.apply_channel_rotation(xs[i % n], md, None, out=zs[i % n]),
+               20, 3)
+    out["c4_givens_layers_apply_no_perm"] = gbs(ms, el, 4)
     t0 = time.perf_counter()
     R, rloss = fp4.calibrate_block_rotation(zs[0][:256], None, iters=30, angles=32)
     block_ms = (time.perf_counter() - t0) * 1e3
