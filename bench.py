@@ -118,6 +118,22 @@ def timed(torch, fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def step_distribution(torch, fn, n):
+    """p10 / p50 / p90 of single-step times (us): an event pair around each of n
+    back-to-back steps; the queue stays ahead of the GPU, so each pair brackets
+    that step's kernels only."""
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record(st)
+        fn(i)
+        b.record(st)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    return [round(t[n // 10], 2), round(t[n // 2], 2), round(t[(9 * n) // 10], 2)]
+
+
 def dev_copies(torch, x_u16, n):
     import numpy as np
     t = torch.from_numpy(x_u16.view(np.int16)).cuda().view(torch.bfloat16)
@@ -173,9 +189,17 @@ def cpu_baseline(workload, x, perm, target_s):
     dt = run(probe)
     rows = int(min(x.shape[0], max(probe, probe * target_s / max(dt, 1e-6))))
     dt = run(rows)
-    return {"value": rows * cols * 2 / dt / 1e9, "unit": "GB/s", "cores": th, "kind": "oracle",
-            "sample": f"first {rows} rows x {cols} cols of the same tensor "
-                      f"({rows * cols} elements), {dt:.1f} s on {th} threads"}
+    out = {"value": rows * cols * 2 / dt / 1e9, "unit": "GB/s", "cores": th, "kind": "oracle",
+           "sample": f"first {rows} rows x {cols} cols of the same tensor "
+                     f"({rows * cols} elements), {dt:.1f} s on {th} threads"}
+    # the same on one thread, on a sample of about a quarter of that time
+    oracle.set_threads(1)
+    r1 = max(1, min(rows, int(probe * target_s / 4 / max(run(probe), 1e-6))))
+    dt1 = run(r1)
+    oracle.set_threads(th)
+    out["one_thread"] = {"value": r1 * cols * 2 / dt1 / 1e9, "unit": "GB/s",
+                         "sample": f"first {r1} rows, {dt1:.1f} s on 1 thread"}
+    return out
 
 
 def bench_c4(torch, fp4, inputs, args):
@@ -204,6 +228,7 @@ def bench_c4(torch, fp4, inputs, args):
 
     log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
     ms = timed(torch, step, args.steps, args.warmup)
+    dist = step_distribution(torch, step, 200)
     elems = rows * cols
     value = elems * 2 / (ms * 1e-3) / 1e9
     achieved = elems * B_MX / (ms * 1e-3) / 1e9
@@ -213,7 +238,8 @@ def bench_c4(torch, fp4, inputs, args):
     c_pl, s_pl, _ = fp4.quantize(xs[0], fp4.MXFP4)
     q_plain = sqnr_db(torch, xs[0].float(), fp4.dequantize(c_pl, s_pl, fp4.MXFP4).float())
 
-    extras = {"calibration_ms": round(calib_ms, 3), "channel_energy_ms": round(e_ms, 4),
+    extras = {"step_us_p10_p50_p90": dist,
+              "calibration_ms": round(calib_ms, 3), "channel_energy_ms": round(e_ms, 4),
               "sqnr_db_plain_mxfp4": round(q_plain, 3), "device_copy": device_copy(torch)}
     if not args.no_extras:
         extras.update(extra_rows(torch, fp4, inputs, xs, perm, codes, scales))
@@ -619,6 +645,17 @@ def pmc_summary(dirs):
         _, c = pick(cu, ROT_INSTANCE)
         lines += [f"MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES = "
                   f"{med(b) / max(med(c), 1):.4f} (median dispatch).", ""]
+        # instruction mix: wave instructions per 64 elements (one per lane
+        # and element for a VALU op that every lane issues once per element)
+        mix = []
+        for ctr in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+            got = _pmc_rows(dirs[2], ctr)
+            if any(ROT_INSTANCE in k for k in got):
+                _, v = pick(got, ROT_INSTANCE)
+                mix.append(f"{ctr} {med(v) / (rows * cols / 64):.3f}")
+        if mix:
+            lines += ["Instructions per element (wave instructions x 64 / elements, median "
+                      "dispatch): " + ", ".join(mix) + ".", ""]
     lines += [
         "Commands (from the repository root, TMPDIR=/tmp):",
         "",
@@ -627,8 +664,9 @@ def pmc_summary(dirs):
         "-- python3 bench.py --steps 3 --warmup 1 --no-extras --no-cpu",
         "rocprofv3 --pmc WRITE_SIZE --kernel-trace -d <write_dir> -o run --output-format csv "
         "-- python3 bench.py --steps 3 --warmup 1 --no-extras --no-cpu",
-        "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES --kernel-trace -d <mfma_dir> "
-        "-o run --output-format csv -- python3 bench.py --steps 3 --warmup 1 --no-extras --no-cpu",
+        "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
+        "SQ_INSTS_LDS SQ_INSTS_SALU --kernel-trace -d <mfma_dir> -o run --output-format csv "
+        "-- python3 bench.py --steps 3 --warmup 1 --no-extras --no-cpu",
         "python3 bench.py --pmc-summary <fetch_dir> <write_dir> <mfma_dir>",
         "```",
         "",
