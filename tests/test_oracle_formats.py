@@ -181,3 +181,37 @@ def test_bf16_rounding_matches_torch(orc):
             assert (got & 0x7F80) == 0x7F80 and (got & 0x7F)
         else:
             assert got == ref[i], hex(int(bits[i]))
+
+
+def test_e2m1_all_bf16_all_exponents_through_the_block_quantizer(orc):
+    """Every finite bf16 pattern at every E8M0 exponent a finite block can
+    reach, e in [-127, 126] (about 8 M elements): blocks of 31 test values and
+    one pin element, 6 * 2^e (for e = 126, where that overflows fp32, the
+    largest finite fp32, which also needs e = 126), so the ceiling rule
+    chooses exactly e; the oracle's MXFP4 quantizer must give the
+    round-half-even code of x * 2^-e (exact in float64) and the scale byte
+    e + 127."""
+    pats = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        f32 = (pats << 16).view(np.float32)
+    f32 = f32[np.isfinite(f32)]
+    total = 0
+    for e in range(-127, 127):
+        top = np.float32(np.ldexp(6.0, e)) if e < 126 else np.finfo(np.float32).max
+        x = f32[np.abs(f32.astype(np.float64)) <= float(top)]
+        nb = -(-x.size // 31)
+        blocks = np.zeros((nb, 32), np.float32)
+        vals = np.zeros(nb * 31, np.float32)
+        vals[:x.size] = x
+        blocks[:, :31] = vals.reshape(nb, 31)
+        blocks[:, 31] = top
+        codes, scales = orc.mx_quantize_f32(blocks)
+        assert np.all(scales == e + 127), e
+        nib = np.empty((nb, 32), np.uint8)
+        nib[:, 0::2], nib[:, 1::2] = codes & 15, codes >> 4
+        got = nib[:, :31].reshape(-1)[:x.size].astype(np.int64)
+        y = np.ldexp(x.astype(np.float64), -e)
+        want = (np.signbit(y).astype(np.int64) << 3) | _rint_rule(np.abs(y))
+        assert np.array_equal(got, want), e
+        total += x.size
+    assert total > 8_000_000
