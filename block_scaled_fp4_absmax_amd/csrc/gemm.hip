@@ -19,14 +19,15 @@
 // layout and the exactness of the products were confirmed on the GPU with an
 // in-bounds probe.
 //
-// Tiling: a work-group of four waves computes a (64 WM) x (64 WN) tile of C
-// (256 x 256 for large products, 128 x 128 otherwise); wave (wm, wn) owns
-// the quarter (wm, wn) as WM x WN MFMA tiles. K advances 128 elements per
-// stage: the work-group copies the stage's rows of 64 code bytes of A and of
-// B, and their 4 scale bytes per row, into one of two LDS buffers (16-byte
-// chunks swizzled within each row so that the lane writes and the MFMA
-// operand reads are free of bank conflicts), while the waves multiply out of
-// the other; the loads of three stages are in flight at a time. Loads past
+// Tiling: a work-group of VM x VN waves computes a (32 WM VM) x (32 WN VN)
+// tile of C (256 x 256 from eight waves for large products, 128 x 128 from
+// four otherwise); wave (wm, wn) owns WM x WN MFMA tiles. K advances 128
+// elements per stage: the work-group copies the stage's rows of 64 code bytes
+// of A and of B, and their 4 scale bytes per row, into one of two LDS buffers
+// (16-byte chunks swizzled within each row so that the lane writes and the
+// MFMA operand reads are free of bank conflicts), while the waves multiply
+// out of the other; the loads of two or three stages are held in registers
+// meanwhile. Loads past
 // M, N or K read zeros through buffer-resource range checks (code 0 is +0),
 // so any K that is a multiple of 32 works.
 #include <type_traits>
@@ -68,14 +69,19 @@ struct OperandRsrc {
   rsrc_t a, sa, b, sb;
 };
 
-// Work-group tile BM x BN = (64 WM) x (64 WN): four waves, wave (wm, wn) owns
-// WM x WN MFMA tiles of 32 x 32 at rows 32 WM wm.., columns 32 WN wn..
-template <int WM, int WN>
+// Work-group tile BM x BN = (32 WM VM) x (32 WN VN): VM x VN waves, wave
+// (wm, wn) owns WM x WN MFMA tiles of 32 x 32 at rows 32 WM wm..,
+// columns 32 WN wn..
+template <int WM, int WN, int VM, int VN>
 struct Tile {
-  static constexpr int BM = 64 * WM, BN = 64 * WN;
-  static constexpr int kChunksA = BM * kRowBytes / 16 / 256;  // 16-byte chunks per lane
-  static constexpr int kChunksB = BN * kRowBytes / 16 / 256;
-  static constexpr int kScaleRows = (BM + BN) / 256;          // scale rows per lane
+  static constexpr int BM = 32 * WM * VM, BN = 32 * WN * VN;
+  static constexpr int kT = 64 * VM * VN;                     // threads
+  static constexpr int kChunksA = BM * kRowBytes / 16 / kT;   // 16-byte chunks per lane
+  static constexpr int kChunksB = BN * kRowBytes / 16 / kT;
+  static constexpr int kScaleRows = (BM + BN) / kT;           // scale rows per lane
+  static_assert(kChunksA * kT * 16 == BM * kRowBytes && kChunksB * kT * 16 == BN * kRowBytes &&
+                    kScaleRows * kT == BM + BN && BM % 64 == 0,
+                "the stage divides evenly over the lanes");
   static constexpr int kLdsA = BM * kLdsRow, kLdsB = BN * kLdsRow;
 
   // One stage in flight in registers: code chunks of A and B, and the four
@@ -91,22 +97,22 @@ struct Tile {
     const uint32_t kb0 = (uint32_t)k0 / 2u, kbytes = (uint32_t)g.k / 2u;
 #pragma unroll
     for (int i = 0; i < kChunksA; ++i) {
-      const uint32_t chunk = t + 256u * i, row = chunk >> 2, col = 16u * (chunk & 3u);
+      const uint32_t chunk = t + (uint32_t)kT * i, row = chunk >> 2, col = 16u * (chunk & 3u);
       r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(
           q.a, kb0 + col < kbytes ? row * (uint32_t)g.ld_a + kb0 + col : kOob, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kChunksB; ++i) {
-      const uint32_t chunk = t + 256u * i, row = chunk >> 2, col = 16u * (chunk & 3u);
+      const uint32_t chunk = t + (uint32_t)kT * i, row = chunk >> 2, col = 16u * (chunk & 3u);
       r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(
           q.b, kb0 + col < kbytes ? row * (uint32_t)g.ld_b + kb0 + col : kOob, 0, 0);
     }
     // scale row j of the stage: rows 0 .. BM-1 of A, then BM .. BM+BN-1 of B;
-    // lane t takes rows t + 256 i, whose operand is uniform across a wave
+    // lane t takes rows t + kT i, whose operand is uniform across a wave
     const uint32_t blk0 = (uint32_t)k0 / 32u, nblk = (uint32_t)g.k / 32u;
 #pragma unroll
     for (int i = 0; i < kScaleRows; ++i) {
-      const uint32_t j = t + 256u * i;
+      const uint32_t j = t + (uint32_t)kT * i;
       const bool is_a = __builtin_amdgcn_readfirstlane(j >> 6) < (uint32_t)BM / 64u;
       const rsrc_t rs = is_a ? q.sa : q.sb;
       const uint32_t row = is_a ? j : j - BM;
@@ -122,22 +128,22 @@ struct Tile {
     const uint32_t t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < kChunksA; ++i) {
-      const uint32_t chunk = t + 256u * i, row = chunk >> 2, col = 16u * (chunk & 3u);
+      const uint32_t chunk = t + (uint32_t)kT * i, row = chunk >> 2, col = 16u * (chunk & 3u);
       *reinterpret_cast<u32x4_t*>(la + lds_off(row, col / 16u)) = r.a[i];
     }
 #pragma unroll
     for (int i = 0; i < kChunksB; ++i) {
-      const uint32_t chunk = t + 256u * i, row = chunk >> 2, col = 16u * (chunk & 3u);
+      const uint32_t chunk = t + (uint32_t)kT * i, row = chunk >> 2, col = 16u * (chunk & 3u);
       *reinterpret_cast<u32x4_t*>(lb + lds_off(row, col / 16u)) = r.b[i];
     }
 #pragma unroll
-    for (int i = 0; i < kScaleRows; ++i) ls[t + 256u * i] = r.s[i] & smask;
+    for (int i = 0; i < kScaleRows; ++i) ls[t + (uint32_t)kT * i] = r.s[i] & smask;
   }
 };
 
-template <int WM, int WN, bool kBf16Out>
-__global__ __launch_bounds__(256) void mx_gemm_kernel(GemmArgs g) {
-  using T = Tile<WM, WN>;
+template <int WM, int WN, int VM, int VN, int kSets, bool kBf16Out>
+__global__ __launch_bounds__(64 * VM * VN) void mx_gemm_kernel(GemmArgs g) {
+  using T = Tile<WM, WN, VM, VN>;
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][T::kLdsA];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][T::kLdsB];
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmArgs g) {
   q.sb = make_rsrc(g.sb + (int64_t)n0 * g.ld_sb, (uint32_t)(rows_b * g.ld_sb));
 
   const uint32_t lane = threadIdx.x & 63u, r = lane & 31u, h = lane >> 5;
-  const uint32_t w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1u;
+  const uint32_t w = threadIdx.x >> 6, wm = w / VN, wn = w % VN;
 
   f32x16_t acc[WM][WN];
 #pragma unroll
@@ -197,13 +203,13 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmArgs g) {
     }
   };
 
-  // Three stages in flight: while stage s is multiplied out of LDS buffer
-  // s % 2, register set s % 3 (whose stage is already in LDS) receives stage
-  // s + 3, and register sets (s + 1) % 3, (s + 2) % 3 hold stages s + 1 and
-  // s + 2; stage s + 1 is stored into the other LDS buffer afterwards. Loads
-  // are unconditional: past K they read zeros without touching memory, so
-  // every stage issues the same operations and each store waits for its own
-  // stage's loads only.
+  // kSets stages in flight in registers: while stage s is multiplied out of
+  // LDS buffer s % 2, register set s % kSets (whose stage is already in LDS)
+  // receives stage s + kSets, and the other sets hold stages s + 1 ..
+  // s + kSets - 1; stage s + 1 is stored into the other LDS buffer
+  // afterwards. Loads are unconditional: past K they read zeros without
+  // touching memory, so every stage issues the same operations and each
+  // store waits for its own stage's loads only.
   const int32_t stages = (g.k + kBK - 1) / kBK;
   // scale bytes of a stage that lie past K (the last, partial stage) are
   // cleared: their codes read as zero, and a stray 0xFF would make 0 * NaN
@@ -212,29 +218,30 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmArgs g) {
     const uint32_t b0 = 4u * (uint32_t)st;
     return b0 + 4u <= nblk ? 0xFFFFFFFFu : b0 >= nblk ? 0u : (1u << (8u * (nblk - b0))) - 1u;
   };
-  typename T::Regs rs[3];
-  T::load(q, g, 0, rs[0]);
-  T::load(q, g, kBK, rs[1]);
-  T::load(q, g, 2 * kBK, rs[2]);
+  typename T::Regs rs[kSets];
+#pragma unroll
+  for (int j = 0; j < kSets; ++j) T::load(q, g, j * kBK, rs[j]);
   T::store(lds_a[0], lds_b[0], lds_s[0], rs[0], smask(0));
   __syncthreads();
-  // stage s with register set j = s % 3 (a compile-time index)
+  // stage s with register set j = s % kSets (a compile-time index)
   auto step = [&](auto J, int32_t s) {
     constexpr int j = decltype(J)::value;
     const int buf = s & 1;
-    T::load(q, g, (s + 3) * kBK, rs[j]);
+    T::load(q, g, (s + kSets) * kBK, rs[j]);
     mma(buf);
-    T::store(lds_a[buf ^ 1], lds_b[buf ^ 1], lds_s[buf ^ 1], rs[(j + 1) % 3], smask(s + 1));
+    T::store(lds_a[buf ^ 1], lds_b[buf ^ 1], lds_s[buf ^ 1], rs[(j + 1) % kSets], smask(s + 1));
     __syncthreads();
   };
+  auto group = [&]<int... js>(int32_t s0, std::integer_sequence<int, js...>) {
+    (step(std::integral_constant<int, js>{}, s0 + js), ...);
+  };
+  auto tail = [&]<int... js>(int32_t s0, std::integer_sequence<int, js...>) {
+    (void)((s0 + js < stages ? (step(std::integral_constant<int, js>{}, s0 + js), true) : false) &&
+           ...);
+  };
   int32_t s = 0;
-  for (; s + 2 < stages; s += 3) {
-    step(std::integral_constant<int, 0>{}, s);
-    step(std::integral_constant<int, 1>{}, s + 1);
-    step(std::integral_constant<int, 2>{}, s + 2);
-  }
-  if (s < stages) step(std::integral_constant<int, 0>{}, s);
-  if (s + 1 < stages) step(std::integral_constant<int, 1>{}, s + 1);
+  for (; s + kSets - 1 < stages; s += kSets) group(s, std::make_integer_sequence<int, kSets>{});
+  tail(s, std::make_integer_sequence<int, kSets - 1>{});
 
   // epilogue: lane (n, h) of tile (i, j) holds column n, rows 8 (e / 4) + 4 h + e % 4
 #pragma unroll
@@ -417,14 +424,16 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void mx_gemm_skinny_kernel(GemmA
   }
 }
 
-template <int WM, int WN>
+template <int WM, int WN, int VM, int VN, int kSets>
 void launch_tiles(const GemmArgs& g, bool bf16_out, hipStream_t st) {
-  const int64_t tiles = (((int64_t)g.m + 64 * WM - 1) / (64 * WM)) *
-                        (((int64_t)g.n + 64 * WN - 1) / (64 * WN));
+  constexpr int BM = 32 * WM * VM, BN = 32 * WN * VN;
+  const int64_t tiles = (((int64_t)g.m + BM - 1) / BM) * (((int64_t)g.n + BN - 1) / BN);
   if (bf16_out)
-    hipLaunchKernelGGL((mx_gemm_kernel<WM, WN, true>), dim3((unsigned)tiles), dim3(256), 0, st, g);
+    hipLaunchKernelGGL((mx_gemm_kernel<WM, WN, VM, VN, kSets, true>), dim3((unsigned)tiles),
+                       dim3(64 * VM * VN), 0, st, g);
   else
-    hipLaunchKernelGGL((mx_gemm_kernel<WM, WN, false>), dim3((unsigned)tiles), dim3(256), 0, st, g);
+    hipLaunchKernelGGL((mx_gemm_kernel<WM, WN, VM, VN, kSets, false>), dim3((unsigned)tiles),
+                       dim3(64 * VM * VN), 0, st, g);
 }
 
 }  // namespace
@@ -443,17 +452,17 @@ void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a
       hipLaunchKernelGGL((mx_gemm_skinny_kernel<false>), dim3(grid), dim3(64 * kSkinnyWaves), 0, st, g);
     return;
   }
-#ifdef FP4_GEMM_TILE
-  constexpr int kW = FP4_GEMM_TILE;
-  launch_tiles<kW, kW>(g, bf16_out, st);
-#else
-  // large products: 256 x 256 tiles (four 128 x 128 wave tiles) halve the
-  // operand traffic per flop; smaller ones keep 128 x 128 for more work-groups
+  // large products: 256 x 256 tiles halve the operand traffic per flop;
+  // smaller ones keep 128 x 128 for more work-groups
+  // 256 x 256: eight waves (2 x 4) of 4 x 2 MFMA tiles, two per SIMD, so one
+  // wave's MFMAs overlap the other's LDS reads and barrier; two stages of
+  // loads in registers (the accumulators take half the register file).
+  // Measured against four waves of 4 x 4 tiles (one per SIMD, accumulators
+  // in AGPRs): 4-20% faster on the layer shapes, bit-identical results.
   if (m >= 2048 && n >= 2048)
-    launch_tiles<4, 4>(g, bf16_out, st);
+    launch_tiles<4, 2, 2, 4, 2>(g, bf16_out, st);
   else
-    launch_tiles<2, 2>(g, bf16_out, st);
-#endif
+    launch_tiles<2, 2, 2, 2, 3>(g, bf16_out, st);
 }
 
 }  // namespace fp4
