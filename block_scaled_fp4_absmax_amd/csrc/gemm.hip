@@ -21,9 +21,10 @@
 //
 // Tiling: a work-group of VM x VN waves computes a (32 WM VM) x (32 WN VN)
 // tile of C (256 x 256 from eight waves for large products, 128 x 128 from
-// four otherwise); wave (wm, wn) owns WM x WN MFMA tiles. K advances 128
-// elements per stage: the work-group copies the stage's rows of 64 code bytes
-// of A and of B, and their 4 scale bytes per row, into one of two LDS buffers
+// four otherwise); wave (wm, wn) owns WM x WN MFMA tiles. K advances KB (256
+// or 128) elements per stage: the work-group copies the stage's rows of KB / 2
+// code bytes of A and of B, and their KB / 32 scale bytes per row, into one of
+// two LDS buffers
 // (16-byte chunks swizzled within each row so that the lane writes and the
 // MFMA operand reads are free of bank conflicts), while the waves multiply
 // out of the other; the loads of two or three stages are held in registers
@@ -42,17 +43,20 @@ namespace {
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 128;                 // K elements per stage
-constexpr int kRowBytes = kBK / 2;       // code bytes per row per stage
-constexpr int kLdsRow = kRowBytes;       // LDS row (16-byte chunks XOR-swizzled)
-
-// LDS byte offset of 16-byte chunk c (0..3) of row r: chunk c sits in slot
-// c ^ ((r / 2) % 4). A write pass of 8 lanes covers two rows (slots 0..3 of
-// each, 128 contiguous bytes); a read pass of 8 lanes takes one logical chunk
+// LDS byte offset of 16-byte chunk c of row r in a stage of KB K values
+// (KB / 32 chunks per row). KB = 128: chunk c (0..3) sits in slot
+// c ^ ((r / 2) % 4); a write pass of 8 lanes covers two rows (slots 0..3 of
+// each, 128 contiguous bytes), a read pass of 8 lanes takes one logical chunk
 // of 8 consecutive rows, which the swizzle spreads over all four slots of
-// both bank halves, so neither conflicts on 32 four-byte banks.
+// both bank halves, so neither conflicts on 32 four-byte banks. KB = 256:
+// chunk c (0..7) in slot c ^ (r % 8), one row per write pass, eight rows
+// over the eight slots per read pass.
+template <int KB>
 __device__ __forceinline__ uint32_t lds_off(uint32_t r, uint32_t c) {
-  return r * kLdsRow + 16u * (c ^ ((r >> 1) & 3u));
+  if constexpr (KB == 128)
+    return r * 64u + 16u * (c ^ ((r >> 1) & 3u));
+  else
+    return r * 128u + 16u * (c ^ (r & 7u));
 }
 
 struct GemmArgs {
@@ -72,20 +76,23 @@ struct OperandRsrc {
 // Work-group tile BM x BN = (32 WM VM) x (32 WN VN): VM x VN waves, wave
 // (wm, wn) owns WM x WN MFMA tiles of 32 x 32 at rows 32 WM wm..,
 // columns 32 WN wn..
-template <int WM, int WN, int VM, int VN>
+template <int WM, int WN, int VM, int VN, int KB>
 struct Tile {
   static constexpr int BM = 32 * WM * VM, BN = 32 * WN * VN;
   static constexpr int kT = 64 * VM * VN;                     // threads
+  static constexpr int kRowBytes = KB / 2;                    // code bytes per row per stage
+  static constexpr int kCpr = kRowBytes / 16;                 // 16-byte chunks per row
+  static constexpr int kSW = KB / 128;                        // scale dwords per row
   static constexpr int kChunksA = BM * kRowBytes / 16 / kT;   // 16-byte chunks per lane
   static constexpr int kChunksB = BN * kRowBytes / 16 / kT;
-  static constexpr int kScaleRows = (BM + BN) / kT;           // scale rows per lane
+  static constexpr int kScaleRows = (BM + BN) * kSW / kT;     // scale dwords per lane
   static_assert(kChunksA * kT * 16 == BM * kRowBytes && kChunksB * kT * 16 == BN * kRowBytes &&
-                    kScaleRows * kT == BM + BN && BM % 64 == 0,
+                    kScaleRows * kT == (BM + BN) * kSW && BM % 64 == 0,
                 "the stage divides evenly over the lanes");
-  static constexpr int kLdsA = BM * kLdsRow, kLdsB = BN * kLdsRow;
+  static constexpr int kLdsA = BM * kRowBytes, kLdsB = BN * kRowBytes;
 
-  // One stage in flight in registers: code chunks of A and B, and the four
-  // scale bytes of each scale row (one dword; scale rows are 4-byte aligned).
+  // One stage in flight in registers: code chunks of A and B, and the KB / 32
+  // scale bytes of each scale row (kSW dwords; scale rows are 4-byte aligned).
   struct Regs {
     u32x4_t a[kChunksA], b[kChunksB];
     uint32_t s[kScaleRows];
@@ -97,57 +104,65 @@ struct Tile {
     const uint32_t kb0 = (uint32_t)k0 / 2u, kbytes = (uint32_t)g.k / 2u;
 #pragma unroll
     for (int i = 0; i < kChunksA; ++i) {
-      const uint32_t chunk = t + (uint32_t)kT * i, row = chunk >> 2, col = 16u * (chunk & 3u);
+      const uint32_t chunk = t + (uint32_t)kT * i, row = chunk / kCpr, col = 16u * (chunk % kCpr);
       r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(
           q.a, kb0 + col < kbytes ? row * (uint32_t)g.ld_a + kb0 + col : kOob, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kChunksB; ++i) {
-      const uint32_t chunk = t + (uint32_t)kT * i, row = chunk >> 2, col = 16u * (chunk & 3u);
+      const uint32_t chunk = t + (uint32_t)kT * i, row = chunk / kCpr, col = 16u * (chunk % kCpr);
       r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(
           q.b, kb0 + col < kbytes ? row * (uint32_t)g.ld_b + kb0 + col : kOob, 0, 0);
     }
-    // scale row j of the stage: rows 0 .. BM-1 of A, then BM .. BM+BN-1 of B;
-    // lane t takes rows t + kT i, whose operand is uniform across a wave
+    // scale dword e of the stage: row e / kSW (rows 0 .. BM-1 of A, then
+    // BM .. BM+BN-1 of B), dword e % kSW of its KB / 32 bytes; lane t takes
+    // dwords t + kT i, whose operand is uniform across a wave
     const uint32_t blk0 = (uint32_t)k0 / 32u, nblk = (uint32_t)g.k / 32u;
 #pragma unroll
     for (int i = 0; i < kScaleRows; ++i) {
-      const uint32_t j = t + (uint32_t)kT * i;
-      const bool is_a = __builtin_amdgcn_readfirstlane(j >> 6) < (uint32_t)BM / 64u;
+      const uint32_t e = t + (uint32_t)kT * i, j = e / kSW;
+      const uint32_t blk = blk0 + 4u * (e % kSW);
+      const bool is_a = __builtin_amdgcn_readfirstlane(e >> 6) < (uint32_t)(BM * kSW) / 64u;
       const rsrc_t rs = is_a ? q.sa : q.sb;
       const uint32_t row = is_a ? j : j - BM;
       const uint32_t base = row * (uint32_t)(is_a ? g.ld_sa : g.ld_sb);
-      // blk0 is a multiple of 4 below nblk <= ld_s (a multiple of 4), so the
+      // blk is a multiple of 4 below nblk <= ld_s (a multiple of 4), so the
       // dword stays inside the row; bytes past K are cleared when stored
-      r.s[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, blk0 < nblk ? base + blk0 : kOob, 0, 0);
+      r.s[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, blk < nblk ? base + blk : kOob, 0, 0);
     }
   }
 
+  // smask(d): which bytes of scale dword d (0 .. kSW - 1) of the stage lie
+  // before the end of K
+  template <typename Mask>
   static __device__ __forceinline__ void store(uint8_t* la, uint8_t* lb, uint32_t* ls,
-                                               const Regs& r, uint32_t smask) {
+                                               const Regs& r, Mask smask) {
     const uint32_t t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < kChunksA; ++i) {
-      const uint32_t chunk = t + (uint32_t)kT * i, row = chunk >> 2, col = 16u * (chunk & 3u);
-      *reinterpret_cast<u32x4_t*>(la + lds_off(row, col / 16u)) = r.a[i];
+      const uint32_t chunk = t + (uint32_t)kT * i, row = chunk / kCpr, c = chunk % kCpr;
+      *reinterpret_cast<u32x4_t*>(la + lds_off<KB>(row, c)) = r.a[i];
     }
 #pragma unroll
     for (int i = 0; i < kChunksB; ++i) {
-      const uint32_t chunk = t + (uint32_t)kT * i, row = chunk >> 2, col = 16u * (chunk & 3u);
-      *reinterpret_cast<u32x4_t*>(lb + lds_off(row, col / 16u)) = r.b[i];
+      const uint32_t chunk = t + (uint32_t)kT * i, row = chunk / kCpr, c = chunk % kCpr;
+      *reinterpret_cast<u32x4_t*>(lb + lds_off<KB>(row, c)) = r.b[i];
     }
 #pragma unroll
-    for (int i = 0; i < kScaleRows; ++i) ls[t + (uint32_t)kT * i] = r.s[i] & smask;
+    for (int i = 0; i < kScaleRows; ++i) {
+      const uint32_t e = t + (uint32_t)kT * i;
+      ls[e] = r.s[i] & smask(e % kSW);
+    }
   }
 };
 
-template <int WM, int WN, int VM, int VN, int kSets, bool kBf16Out>
+template <int WM, int WN, int VM, int VN, int KB, int kSets, bool kBf16Out>
 __global__ __launch_bounds__(64 * VM * VN) void mx_gemm_kernel(GemmArgs g) {
-  using T = Tile<WM, WN, VM, VN>;
-  constexpr int BM = T::BM, BN = T::BN;
+  using T = Tile<WM, WN, VM, VN, KB>;
+  constexpr int BM = T::BM, BN = T::BN, kSW = T::kSW, kBK = KB;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][T::kLdsA];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][T::kLdsB];
-  __shared__ uint32_t lds_s[2][BM + BN];
+  __shared__ uint32_t lds_s[2][(BM + BN) * kSW];
 
   const int32_t tiles_n = (g.n + BN - 1) / BN;
   const int32_t bm = blockIdx.x / tiles_n, bn = blockIdx.x - bm * tiles_n;
@@ -170,24 +185,25 @@ __global__ __launch_bounds__(64 * VM * VN) void mx_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // multiply out the stage held in LDS buffer buf: two 64-element K steps
+  // multiply out the stage held in LDS buffer buf: KB / 64 K steps of 64
   auto mma = [&](int buf) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t kc = 2u * ks + h, sh = 8u * kc;  // 16-byte chunk, scale byte
+    for (int ks = 0; ks < KB / 64; ++ks) {
+      // 16-byte chunk kc of the row; its scale byte kc of the row's KB / 32
+      const uint32_t kc = 2u * ks + h, sd = kc / 4u, sh = 8u * (kc % 4u);
       u32x4_t fa[WM], fb[WN];
       int32_t sa[WM], sb[WN];
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
         const uint32_t ra = 32u * WM * wm + 32u * i + r;
-        fa[i] = *reinterpret_cast<const u32x4_t*>(lds_a[buf] + lds_off(ra, kc));
-        sa[i] = (int32_t)((lds_s[buf][ra] >> sh) & 0xFFu);
+        fa[i] = *reinterpret_cast<const u32x4_t*>(lds_a[buf] + lds_off<KB>(ra, kc));
+        sa[i] = (int32_t)((lds_s[buf][ra * kSW + sd] >> sh) & 0xFFu);
       }
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         const uint32_t rb = 32u * WN * wn + 32u * j + r;
-        fb[j] = *reinterpret_cast<const u32x4_t*>(lds_b[buf] + lds_off(rb, kc));
-        sb[j] = (int32_t)((lds_s[buf][BM + rb] >> sh) & 0xFFu);
+        fb[j] = *reinterpret_cast<const u32x4_t*>(lds_b[buf] + lds_off<KB>(rb, kc));
+        sb[j] = (int32_t)((lds_s[buf][(BM + rb) * kSW + sd] >> sh) & 0xFFu);
       }
 #pragma unroll
       for (int i = 0; i < WM; ++i)
@@ -215,8 +231,10 @@ __global__ __launch_bounds__(64 * VM * VN) void mx_gemm_kernel(GemmArgs g) {
   // cleared: their codes read as zero, and a stray 0xFF would make 0 * NaN
   const uint32_t nblk = (uint32_t)g.k / 32u;
   auto smask = [&](int32_t st) {
-    const uint32_t b0 = 4u * (uint32_t)st;
-    return b0 + 4u <= nblk ? 0xFFFFFFFFu : b0 >= nblk ? 0u : (1u << (8u * (nblk - b0))) - 1u;
+    return [=](uint32_t d) {
+      const uint32_t b0 = (uint32_t)(KB / 32) * (uint32_t)st + 4u * d;
+      return b0 + 4u <= nblk ? 0xFFFFFFFFu : b0 >= nblk ? 0u : (1u << (8u * (nblk - b0))) - 1u;
+    };
   };
   typename T::Regs rs[kSets];
 #pragma unroll
@@ -424,15 +442,15 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void mx_gemm_skinny_kernel(GemmA
   }
 }
 
-template <int WM, int WN, int VM, int VN, int kSets>
+template <int WM, int WN, int VM, int VN, int KB, int kSets>
 void launch_tiles(const GemmArgs& g, bool bf16_out, hipStream_t st) {
   constexpr int BM = 32 * WM * VM, BN = 32 * WN * VN;
   const int64_t tiles = (((int64_t)g.m + BM - 1) / BM) * (((int64_t)g.n + BN - 1) / BN);
   if (bf16_out)
-    hipLaunchKernelGGL((mx_gemm_kernel<WM, WN, VM, VN, kSets, true>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((mx_gemm_kernel<WM, WN, VM, VN, KB, kSets, true>), dim3((unsigned)tiles),
                        dim3(64 * VM * VN), 0, st, g);
   else
-    hipLaunchKernelGGL((mx_gemm_kernel<WM, WN, VM, VN, kSets, false>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((mx_gemm_kernel<WM, WN, VM, VN, KB, kSets, false>), dim3((unsigned)tiles),
                        dim3(64 * VM * VN), 0, st, g);
 }
 
@@ -455,14 +473,16 @@ void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a
   // large products: 256 x 256 tiles halve the operand traffic per flop;
   // smaller ones keep 128 x 128 for more work-groups
   // 256 x 256: eight waves (2 x 4) of 4 x 2 MFMA tiles, two per SIMD, so one
-  // wave's MFMAs overlap the other's LDS reads and barrier; two stages of
-  // loads in registers (the accumulators take half the register file).
-  // Measured against four waves of 4 x 4 tiles (one per SIMD, accumulators
-  // in AGPRs): 4-20% faster on the layer shapes, bit-identical results.
+  // wave's MFMAs overlap the other's LDS reads and barrier (the accumulators
+  // take half the register file). Measured against four waves of 4 x 4
+  // tiles (one per SIMD, accumulators in AGPRs): 4-20% faster on the layer
+  // shapes, bit-identical results. Stages of 256 K (whole 128-byte lines of
+  // each row; 136 KB of LDS), the next stage in registers while one is
+  // multiplied: up to 8% faster again than 128-K stages with two in flight.
   if (m >= 2048 && n >= 2048)
-    launch_tiles<4, 2, 2, 4, 2>(g, bf16_out, st);
+    launch_tiles<4, 2, 2, 4, 256, 1>(g, bf16_out, st);
   else
-    launch_tiles<2, 2, 2, 2, 3>(g, bf16_out, st);
+    launch_tiles<2, 2, 2, 2, 128, 3>(g, bf16_out, st);
 }
 
 }  // namespace fp4
