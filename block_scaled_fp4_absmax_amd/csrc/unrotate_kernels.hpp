@@ -294,8 +294,10 @@ constexpr int unrot_wgs_per_cu() {
 // kFmt 1 (NVFP4): blocks of 16 (scales 2 b + h, tensor scale *ts), the
 // 16-point transform; 0 (MXFP4) and 2 (MXINT4): blocks of 32, the 32-point
 // one; 3: MXFP4 with the transpose of the learned 32x32 matrix at ts.
+// Wide rows (three or four tiles per wave) run one work-group per CU, one
+// wave per SIMD, so they may use the whole register file.
 template <int kTpw, int kFmt, bool kRazer, bool kHad, bool kPerm>
-__global__ __launch_bounds__(kThreads, 2) void dequant_unrotate_kernel(
+__global__ __launch_bounds__(kThreads, kTpw >= 3 ? 1 : 2) void dequant_unrotate_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ ts, const int32_t* __restrict__ perm, uint16_t* __restrict__ out,
     RotGeom g) {
