@@ -332,7 +332,10 @@ int fp4_build_permutation(const float* energy_host, int64_t cols, int block, int
  *    pair is barred until the next accepted step.
  * `iters` R-steps are tried (fewer if every pair is barred). The result is
  * orthogonal up to fp64 rounding, then stored as fp32; the sample is
- * evaluated in fp64 (bf16 inputs are exact).
+ * evaluated in fp64 (bf16 inputs are exact). Cost: about iters * angles *
+ * rows * cols / 32 block evaluations on one host thread (30 steps of 32
+ * angles on a 256 x 8192 sample take a few seconds), so calibrate on a
+ * sample of rows.
  *
  *  x_host       host bf16 [rows, ld_x]; rows * cols <= 2^26
  *  cols         cols % 32 == 0
