@@ -281,12 +281,14 @@ def dequantize_r(codes, scales, perm, rotation, out=None, stream=None):
     return out
 
 
-def calibrate_block_rotation(x, perm=None, iters: int = 200, angles: int = 64):
+def calibrate_block_rotation(x, perm=None, iters: int = 60, angles: int = 32):
     """Learn the block matrix R on a bf16 calibration sample (host code).
 
     ``x`` is a bf16 tensor (any device; copied to the host) and ``perm`` the
     permutation that will be used online (host or device int32, or None).
-    Returns (R fp32 [32, 32] host tensor, (loss of H / sqrt(32), loss of R)).
+    The cost grows as iters * angles * x.numel() / 32: pass a sample of rows
+    (a few hundred rows of 8192 take seconds). Returns (R fp32 [32, 32] host
+    tensor, (loss of H / sqrt(32), loss of R)).
     """
     import torch
     xh = x.detach().to("cpu").contiguous()
