@@ -24,6 +24,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <thread>
 #include <vector>
 
 #include "../../include/fp4.h"
@@ -200,14 +201,27 @@ extern "C" int fp4_calibrate_block_rotation(const uint16_t* x_host, int64_t rows
         if (k != bi && k != bj) m = std::max(m, fabs(st.y[b * kN + k]));
       omax[b] = m;
     }
+    // the angles are independent: evaluated on several host threads (each
+    // loss is a sum of integer counts, so the result does not depend on the
+    // split), then the first strictly best one is taken in angle order
+    std::vector<double> la(angles, 0.0);
+    const int nth = (int)std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    std::vector<std::thread> pool;
+    for (int t = 0; t < nth; ++t)
+      pool.emplace_back([&, t]() {
+        for (int a = 1 + t; a < angles; a += nth) {
+          const double th = a * (M_PI / 2.0) / angles;
+          la[a] = trial_loss(st, bi, bj, cos(th), sin(th), omax);
+        }
+      });
+    for (auto& th : pool) th.join();
     double best_loss = loss, bc = 1.0, bs = 0.0;
     for (int a = 1; a < angles; ++a) {
-      const double th = a * (M_PI / 2.0) / angles, c = cos(th), s = sin(th);
-      const double l = trial_loss(st, bi, bj, c, s, omax);
-      if (l < best_loss) {
-        best_loss = l;
-        bc = c;
-        bs = s;
+      if (la[a] < best_loss) {
+        const double th = a * (M_PI / 2.0) / angles;
+        best_loss = la[a];
+        bc = cos(th);
+        bs = sin(th);
       }
     }
     if (!(best_loss < loss)) {
