@@ -337,4 +337,20 @@ __device__ __forceinline__ float weight_special(uint32_t byte) {
   return (sel & 1u) ? -mag : mag;
 }
 
+// Work-group -> (column tile x, row tile y) of a skinny product with gx x gy
+// tiles of 32 x 32 on a grid of skinny_grid(gx, gy) work-groups. Work-groups
+// are dealt to the 8 XCDs in turn, so the ids of one column tile are made
+// congruent mod 8: all row tiles of a column tile run on one XCD and read
+// their shared B rows through one L2. x >= gx marks a padding work-group.
+struct SkinnyTile {
+  int32_t x, y;
+};
+__device__ __forceinline__ SkinnyTile skinny_tile(uint32_t id, int32_t gy) {
+  const int32_t q = (int32_t)(id >> 3);
+  return SkinnyTile{(q / gy) * 8 + (int32_t)(id & 7u), q % gy};
+}
+inline unsigned skinny_grid(int64_t gx, int64_t gy) {
+  return (unsigned)(((gx + 7) / 8) * 8 * gy);
+}
+
 }  // namespace fp4

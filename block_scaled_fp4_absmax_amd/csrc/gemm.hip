@@ -283,9 +283,9 @@ __global__ __launch_bounds__(64 * VM * VN) void mx_gemm_kernel(GemmArgs g) {
     }
 }
 
-// Decode-shaped products (m <= 32): a work-group of eight waves computes one
-// 32 x 32 tile of C (rows of A past m read as zeros), so an n-wide product
-// launches n / 32 work-groups; wave w takes the 256-K super-steps w, w + 8,
+// Decode-shaped products (m <= kSkinnyMaxM): a work-group of eight waves
+// computes one 32 x 32 tile of C (rows of A past m read as zeros), so an
+// m x n product launches (m / 32) x (n / 32) work-groups; wave w takes the 256-K super-steps w, w + 8,
 // ... (the waves of a work-group read neighbouring pieces of each row) and
 // the partial tiles are added in LDS in wave order (deterministic). A
 // super-step of an operand is 32 rows x 128 code bytes: it is loaded with
@@ -299,6 +299,11 @@ __global__ __launch_bounds__(64 * VM * VN) void mx_gemm_kernel(GemmArgs g) {
 // both operands, which pairs the same K block of A and B in every lane.
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnySets = 4;  // super-steps of loads in flight per wave
+// Up to this many rows of A the product takes this kernel, one work-group
+// per 32 x 32 tile of C (row tiles of one column tile on one XCD). Measured
+// at n = k = 8192: 19 us against 32 us for the 128 x 128 tiles at m = 48-64,
+// 28 against 33 at m = 96, 36 against 34 at m = 128.
+constexpr int kSkinnyMaxM = 96;
 
 struct SkinnyStep {
   u32x4_t a[4], b[4];  // row 8 c + lane / 8, 16-byte chunk lane % 8
@@ -322,10 +327,12 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void mx_gemm_skinny_kernel(GemmA
   // per wave: the A piece, then the B piece, of the step being multiplied;
   // afterwards the same memory holds the partial tiles of waves 1..7
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSkinnyWaves * 8192];
-  const int32_t n0 = blockIdx.x * 32;
-  const int32_t rows_b = min(32, g.n - n0);
-  const rsrc_t ra = make_rsrc(g.a, (uint32_t)(g.m * g.ld_a));
-  const rsrc_t rsa = make_rsrc(g.sa, (uint32_t)(g.m * g.ld_sa));
+  const SkinnyTile tile = skinny_tile(blockIdx.x, (g.m + 31) / 32);
+  const int32_t n0 = tile.x * 32, m0 = tile.y * 32;
+  if (n0 >= g.n) return;  // padding of the grid to whole XCD rounds
+  const int32_t rows_a = min(32, g.m - m0), rows_b = min(32, g.n - n0);
+  const rsrc_t ra = make_rsrc(g.a + (int64_t)m0 * g.ld_a, (uint32_t)(rows_a * g.ld_a));
+  const rsrc_t rsa = make_rsrc(g.sa + (int64_t)m0 * g.ld_sa, (uint32_t)(rows_a * g.ld_sa));
   const rsrc_t rb = make_rsrc(g.b + (int64_t)n0 * g.ld_b, (uint32_t)(rows_b * g.ld_b));
   const rsrc_t rsb = make_rsrc(g.sb + (int64_t)n0 * g.ld_sb, (uint32_t)(rows_b * g.ld_sb));
   const uint32_t lane = threadIdx.x & 63u, r = lane & 31u, h = lane >> 5;
@@ -431,7 +438,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void mx_gemm_skinny_kernel(GemmA
   if (col >= g.n) return;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int32_t row = 8 * (e / 4) + 4 * (int32_t)h + e % 4;
+    const int32_t row = m0 + 8 * (e / 4) + 4 * (int32_t)h + e % 4;
     if (row >= g.m) continue;
     if constexpr (kBf16Out) {
       const uint32_t p = pack_bf16x2(acc[e], 0.0f);
@@ -462,8 +469,8 @@ void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a
   GemmArgs g{static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(sa),
              static_cast<const uint8_t*>(b), static_cast<const uint8_t*>(sb), c,
              ld_a, ld_sa, ld_b, ld_sb, ld_c, (int32_t)m, (int32_t)n, (int32_t)k};
-  if (m <= 32) {  // decode-shaped: one 32 x 32 tile of C per work-group
-    const unsigned grid = (unsigned)((n + 31) / 32);
+  if (m <= kSkinnyMaxM) {  // decode-shaped: K split over the waves of a work-group
+    const unsigned grid = skinny_grid((n + 31) / 32, (m + 31) / 32);
     if (bf16_out)
       hipLaunchKernelGGL((mx_gemm_skinny_kernel<true>), dim3(grid), dim3(64 * kSkinnyWaves), 0, st, g);
     else

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(64 * VM * VN) void nv_gemm_kernel(NvGemmArgs g) {
     }
 }
 
-// Decode-shaped products (m <= 32), as the MXFP4 decode kernel: a
+// Decode-shaped products (m <= kNvSkinnyMaxM), as the MXFP4 decode kernel: a
 // work-group of eight waves computes one 32 x 32 tile of C, wave w takes the
 // 256-K super-steps w, w + 8, ..., each operand's 32 rows x 128 code bytes
 // are loaded with eight consecutive lanes per 128-byte row piece and passed
@@ -240,6 +240,11 @@ __global__ __launch_bounds__(64 * VM * VN) void nv_gemm_kernel(NvGemmArgs g) {
 // (byte q / 2). Partial tiles are added in LDS in wave order.
 constexpr int kNvSkinnyWaves = 8;
 constexpr int kNvSkinnySets = 3;
+// Up to this many rows of A the product takes this kernel, one work-group
+// per 32 x 32 tile of C (row tiles of one column tile on one XCD). Measured
+// at n = k = 8192: 42 us against 107 us for the 128 x 128 tiles at m = 64,
+// 99 against 108 at m = 160, 116 against 108 at m = 192.
+constexpr int kNvSkinnyMaxM = 160;
 
 struct NvSkinnyStep {
   u32x4_t a[4], b[4];  // row 8 c + lane / 8, 16-byte chunk lane % 8
@@ -284,10 +289,12 @@ __device__ __forceinline__ nbf16x8_t nv_decode8(uint32_t wd, uint32_t sbyte) {
 template <int kModeA, int kModeB, bool kBf16Out>
 __global__ __launch_bounds__(64 * kNvSkinnyWaves) void nv_gemm_skinny_kernel(NvGemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kNvSkinnyWaves * 8192];
-  const int32_t n0 = blockIdx.x * 32;
-  const int32_t rows_b = min(32, g.n - n0);
-  const rsrc_t ra = make_rsrc(g.a, (uint32_t)(g.m * g.ld_a));
-  const rsrc_t rsa = make_rsrc(g.sa, (uint32_t)(g.m * g.ld_sa));
+  const SkinnyTile tile = skinny_tile(blockIdx.x, (g.m + 31) / 32);
+  const int32_t n0 = tile.x * 32, m0 = tile.y * 32;
+  if (n0 >= g.n) return;  // padding of the grid to whole XCD rounds
+  const int32_t rows_a = min(32, g.m - m0), rows_b = min(32, g.n - n0);
+  const rsrc_t ra = make_rsrc(g.a + (int64_t)m0 * g.ld_a, (uint32_t)(rows_a * g.ld_a));
+  const rsrc_t rsa = make_rsrc(g.sa + (int64_t)m0 * g.ld_sa, (uint32_t)(rows_a * g.ld_sa));
   const rsrc_t rb = make_rsrc(g.b + (int64_t)n0 * g.ld_b, (uint32_t)(rows_b * g.ld_b));
   const rsrc_t rsb = make_rsrc(g.sb + (int64_t)n0 * g.ld_sb, (uint32_t)(rows_b * g.ld_sb));
   const uint32_t lane = threadIdx.x & 63u, r = lane & 31u, h = lane >> 5;
@@ -395,7 +402,7 @@ __global__ __launch_bounds__(64 * kNvSkinnyWaves) void nv_gemm_skinny_kernel(NvG
   if (col >= g.n) return;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int32_t row = 8 * (e / 4) + 4 * (int32_t)h + e % 4;
+    const int32_t row = m0 + 8 * (e / 4) + 4 * (int32_t)h + e % 4;
     if (row >= g.m) continue;
     const float v = acc[e] * ts;
     if constexpr (kBf16Out) {
@@ -421,8 +428,8 @@ void nv_launch(const NvGemmArgs& g, bool bf16_out, hipStream_t st) {
 
 template <int kMa, int kMb>
 void nv_tiles(const NvGemmArgs& g, bool bf16_out, hipStream_t st) {
-  if (g.m <= 32) {  // decode-shaped: one 32 x 32 tile of C per work-group
-    const unsigned grid = (unsigned)((g.n + 31) / 32);
+  if (g.m <= kNvSkinnyMaxM) {  // decode-shaped: K split over the waves of a work-group
+    const unsigned grid = skinny_grid((g.n + 31) / 32, (g.m + 31) / 32);
     if (bf16_out)
       hipLaunchKernelGGL((nv_gemm_skinny_kernel<kMa, kMb, true>), dim3(grid),
                          dim3(64 * kNvSkinnyWaves), 0, st, g);

@@ -80,10 +80,13 @@ def _check(orc, ac, as_, bc, bs, k, bf16=False, pad=0):
 @pytest.mark.parametrize("m,n,k", [(128, 128, 128), (1, 1, 32), (37, 45, 96), (200, 300, 4160),
                                    (1, 512, 8192), (256, 384, 8192), (513, 129, 1024),
                                    (2048, 2304, 1024), (2100, 2050, 544),
-                                   # m <= 32 takes the decode-shaped kernel (K split over
-                                   # eight waves, a 32 x 32 tile per work-group)
+                                   # m <= 96 takes the decode-shaped kernel (K split over
+                                   # eight waves, a 32 x 32 tile per work-group; column
+                                   # tiles padded to multiples of 8)
                                    (16, 2048, 8192), (32, 1000, 4160), (7, 300, 96),
-                                   (1, 33, 544), (31, 64, 28672), (16, 96, 256)])
+                                   (1, 33, 544), (31, 64, 28672), (16, 96, 256),
+                                   (33, 520, 4160), (64, 257, 1056), (96, 1000, 544),
+                                   (97, 64, 256)])
 def test_gemm_random_codes(orc, m, n, k):
     note(f"case: MXFP4 GEMM {m}x{n}x{k} random codes and scales")
     rng = np.random.default_rng(m + 7 * n + k)
@@ -202,9 +205,10 @@ def _check_nv(orc, ac, as_, ta, ra, bc, bs, tb, rb, k, bf16=False):
     (128, 128, 128, False, False), (128, 128, 128, True, True), (37, 45, 96, True, False),
     (200, 300, 4160, False, True), (1, 512, 8192, True, True), (2048, 2304, 1024, True, True),
     (2100, 2050, 544, False, False),
-    # m <= 32: the decode-shaped kernel
+    # m <= 160: the decode-shaped kernel
     (16, 2048, 8192, True, True), (32, 1000, 4160, False, True), (7, 300, 96, True, False),
-    (1, 33, 544, False, False), (31, 64, 28672, True, True), (20, 70, 1056, False, False)])
+    (1, 33, 544, False, False), (31, 64, 28672, True, True), (20, 70, 1056, False, False),
+    (65, 520, 1056, True, False), (160, 300, 544, False, True), (161, 96, 512, True, True)])
 def test_nv_gemm_random_codes(orc, m, n, k, ra, rb):
     note(f"case: NVFP4 GEMM {m}x{n}x{k} razer A={ra} B={rb}")
     rng = np.random.default_rng(m + 3 * n + k + ra + 2 * rb)
