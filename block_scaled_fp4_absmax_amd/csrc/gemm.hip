@@ -283,31 +283,33 @@ __global__ __launch_bounds__(64 * VM * VN) void mx_gemm_kernel(GemmArgs g) {
     }
 }
 
-// Decode-shaped products (m <= kSkinnyMaxM): a work-group of eight waves
-// computes one 32 x 32 tile of C (rows of A past m read as zeros), so an
-// m x n product launches (m / 32) x (n / 32) work-groups; wave w takes the 256-K super-steps w, w + 8,
-// ... (the waves of a work-group read neighbouring pieces of each row) and
-// the partial tiles are added in LDS in wave order (deterministic). A
-// super-step of an operand is 32 rows x 128 code bytes: it is loaded with
-// each 128-byte row piece read by eight consecutive lanes (whole lines per
-// instruction; one row per lane measured 1.5x slower), kept in registers
-// while later steps load, then passed through the wave's own LDS buffer
-// (16-byte chunks XOR-swizzled by row, so that the writes and the reads are
-// free of bank conflicts) to the MFMA layout: lane (r, h) takes the 64 bytes
-// 64 h .. 64 h + 63 of row r (blocks 4 h .. 4 h + 3), with the dword of their
-// four scale bytes; MFMA c of the step takes block 4 h + c in lane half h for
-// both operands, which pairs the same K block of A and B in every lane.
+// Split-K products, for few rows of A (decode and small batches) and for
+// products with few 128 x 128 tiles: a work-group of eight waves computes
+// MT x NT tiles of 32 x 32 of C (rows past m or n read as zeros); wave w
+// takes the 256-K super-steps w, w + 8, ... (the waves of a work-group read
+// neighbouring pieces of each row) and the partial tiles are added in LDS in
+// wave order (deterministic). A super-step of an operand piece is 32 rows x
+// 128 code bytes: it is loaded with each 128-byte row piece read by eight
+// consecutive lanes (whole lines per instruction; one row per lane measured
+// 1.5x slower), kept in registers while later steps load, then passed
+// through the wave's own LDS buffer (16-byte chunks XOR-swizzled by row, so
+// that the writes and the reads are free of bank conflicts) to the MFMA
+// layout: lane (r, h) takes the 64 bytes 64 h .. 64 h + 63 of row r (blocks
+// 4 h .. 4 h + 3), with the dword of their four scale bytes; MFMA c of a tile
+// pair takes block 4 h + c in lane half h for both operands, which pairs the
+// same K block of A and B in every lane. The operand bytes each CU streams
+// bound these products, so the tile shape (1 x 1, 1 x 2 or 2 x 2) is chosen
+// per product by skinny_shape; at n = k = 8192 (1 x 2 and 2 x 2 tiles):
+// m = 64 in 11.4 us and m = 128 in 16.2 us, against 32-34 us for one 32 x 32
+// tile per work-group or the 128 x 128 tiles.
 constexpr int kSkinnyWaves = 8;
-constexpr int kSkinnySets = 4;  // super-steps of loads in flight per wave
-// Up to this many rows of A the product takes this kernel, one work-group
-// per 32 x 32 tile of C (row tiles of one column tile on one XCD). Measured
-// at n = k = 8192: 19 us against 32 us for the 128 x 128 tiles at m = 48-64,
-// 28 against 33 at m = 96, 36 against 34 at m = 128.
-constexpr int kSkinnyMaxM = 96;
+constexpr int kSkinnyMaxM = 256;  // larger m always takes the 128 x 128 or 256 x 256 tiles
 
+// A work-group's operand pieces: MT pieces of A (32 rows each) and NT of B.
+template <int MT, int NT>
 struct SkinnyStep {
-  u32x4_t a[4], b[4];  // row 8 c + lane / 8, 16-byte chunk lane % 8
-  uint32_t sa, sb;     // row lane % 32, blocks 4 (lane / 32) .. + 3
+  u32x4_t v[MT + NT][4];  // row 8 c + lane / 8 of the piece, 16-byte chunk lane % 8
+  uint32_t s[MT + NT];    // row lane % 32 of the piece, blocks 4 (lane / 32) .. + 3
 };
 
 // LDS byte offset of 16-byte chunk j (0..7) of row r in a 32 x 128-byte
@@ -322,131 +324,175 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <bool kBf16Out>
+template <int MT, int NT, int kSets, bool kBf16Out>
 __global__ __launch_bounds__(64 * kSkinnyWaves) void mx_gemm_skinny_kernel(GemmArgs g) {
-  // per wave: the A piece, then the B piece, of the step being multiplied;
-  // afterwards the same memory holds the partial tiles of waves 1..7
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSkinnyWaves * 8192];
-  const SkinnyTile tile = skinny_tile(blockIdx.x, (g.m + 31) / 32);
-  const int32_t n0 = tile.x * 32, m0 = tile.y * 32;
+  constexpr int kP = MT + NT;
+  constexpr int kOps = kSkinnyWaves * kP * 4096;                  // operand pieces
+  constexpr int kRed = kSkinnyWaves * 64 * MT * NT * 64;          // partial tiles
+  // per wave: the pieces of the step being multiplied; afterwards the same
+  // memory holds the partial tiles of all waves
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kOps > kRed ? kOps : kRed];
+  const SkinnyTile tile = skinny_tile(blockIdx.x, (g.m + 32 * MT - 1) / (32 * MT));
+  const int32_t n0 = tile.x * 32 * NT, m0 = tile.y * 32 * MT;
   if (n0 >= g.n) return;  // padding of the grid to whole XCD rounds
-  const int32_t rows_a = min(32, g.m - m0), rows_b = min(32, g.n - n0);
+  const int32_t rows_a = min(32 * MT, g.m - m0), rows_b = min(32 * NT, g.n - n0);
   const rsrc_t ra = make_rsrc(g.a + (int64_t)m0 * g.ld_a, (uint32_t)(rows_a * g.ld_a));
   const rsrc_t rsa = make_rsrc(g.sa + (int64_t)m0 * g.ld_sa, (uint32_t)(rows_a * g.ld_sa));
   const rsrc_t rb = make_rsrc(g.b + (int64_t)n0 * g.ld_b, (uint32_t)(rows_b * g.ld_b));
   const rsrc_t rsb = make_rsrc(g.sb + (int64_t)n0 * g.ld_sb, (uint32_t)(rows_b * g.ld_sb));
   const uint32_t lane = threadIdx.x & 63u, r = lane & 31u, h = lane >> 5;
   const int32_t w = (int32_t)(threadIdx.x >> 6);
-  uint8_t* const la = smem + 8192u * (uint32_t)w;
-  uint8_t* const lb = la + 4096u;
+  uint8_t* const lw = smem + kP * 4096u * (uint32_t)w;
   const uint32_t kbytes = (uint32_t)g.k / 2u, nblk = (uint32_t)g.k / 32u;
   const int32_t steps = (g.k + 255) / 256;
   const int32_t cnt = steps > w ? (steps - w + kSkinnyWaves - 1) / kSkinnyWaves : 0;
 
   // loads of the wave's i-th super-step s = w + 8 i (i >= cnt or past K:
   // offsets out of range, which read zeros without touching memory)
-  auto load = [&](int32_t i, SkinnyStep& t) {
+  auto load = [&](int32_t i, SkinnyStep<MT, NT>& t) {
     const int32_t s = w + kSkinnyWaves * i;
     const bool live = i < cnt;
     const uint32_t off = 128u * (uint32_t)s + 16u * (lane & 7u);
     const bool ok = live && off < kbytes;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t row = 8u * c + (lane >> 3);
-      t.a[c] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? row * (uint32_t)g.ld_a + off : kOob,
-                                                     0, 0);
-      t.b[c] = __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? row * (uint32_t)g.ld_b + off : kOob,
-                                                     0, 0);
-    }
     // blk is a multiple of 4 below nblk <= ld_s (a multiple of 4): the dword
     // stays inside the row; bytes past K are cleared before use
     const uint32_t blk = 8u * (uint32_t)s + 4u * h;
     const bool oks = live && blk < nblk;
-    t.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, oks ? r * (uint32_t)g.ld_sa + blk : kOob, 0, 0);
-    t.sb = __builtin_amdgcn_raw_buffer_load_b32(rsb, oks ? r * (uint32_t)g.ld_sb + blk : kOob, 0, 0);
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+      const bool pa = p < MT;
+      const uint32_t base = 32u * (uint32_t)(pa ? p : p - MT);
+      const uint32_t ld = (uint32_t)(pa ? g.ld_a : g.ld_b);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t row = base + 8u * c + (lane >> 3);
+        t.v[p][c] = __builtin_amdgcn_raw_buffer_load_b128(pa ? ra : rb,
+                                                          ok ? row * ld + off : kOob, 0, 0);
+      }
+      const uint32_t lds_ = (uint32_t)(pa ? g.ld_sa : g.ld_sb);
+      t.s[p] = __builtin_amdgcn_raw_buffer_load_b32(pa ? rsa : rsb,
+                                                    oks ? (base + r) * lds_ + blk : kOob, 0, 0);
+    }
   };
 
-  f32x16_t acc;
+  f32x16_t acc[MT][NT];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-  auto mma = [&](int32_t i, const SkinnyStep& t) {
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto mma = [&](int32_t i, const SkinnyStep<MT, NT>& t) {
     const int32_t s = w + kSkinnyWaves * i;
     const uint32_t blk = 8u * (uint32_t)s + 4u * h;
     const uint32_t keep = blk + 4u <= nblk ? 0xFFFFFFFFu
                           : blk >= nblk   ? 0u
                                           : (1u << (8u * (nblk - blk))) - 1u;
-    const uint32_t sa = t.sa & keep, sb = t.sb & keep;
-    // through the wave's LDS buffer into the MFMA layout
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t o = skinny_off(8u * c + (lane >> 3), lane & 7u);
-      *reinterpret_cast<u32x4_t*>(la + o) = t.a[c];
-      *reinterpret_cast<u32x4_t*>(lb + o) = t.b[c];
-    }
+    // through the wave's LDS buffer into the MFMA layout (the previous
+    // step's reads are done first)
     wave_sync();
-    u32x4_t fa[4], fb[4];
+#pragma unroll
+    for (int p = 0; p < kP; ++p)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<u32x4_t*>(lw + 4096u * p + skinny_off(8u * c + (lane >> 3), lane & 7u)) =
+            t.v[p][c];
+    wave_sync();
+    // MFMA c of every tile pair takes chunk c of each piece: operands are
+    // read from LDS per chunk (each one a whole 8-register MFMA operand)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t o = skinny_off(r, 4u * h + c);
-      fa[c] = *reinterpret_cast<const u32x4_t*>(la + o);
-      fb[c] = *reinterpret_cast<const u32x4_t*>(lb + o);
-    }
-    wave_sync();  // the buffer is written again by the next step
+      i32x8_t va[MT], vb[NT];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const i32x8_t va{(int32_t)fa[c].x, (int32_t)fa[c].y, (int32_t)fa[c].z, (int32_t)fa[c].w,
-                       0, 0, 0, 0};
-      const i32x8_t vb{(int32_t)fb[c].x, (int32_t)fb[c].y, (int32_t)fb[c].z, (int32_t)fb[c].w,
-                       0, 0, 0, 0};
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          va, vb, acc, 4, 4, 0, (int32_t)((sa >> (8 * c)) & 0xFFu), 0,
-          (int32_t)((sb >> (8 * c)) & 0xFFu));
+      for (int p = 0; p < kP; ++p) {
+        const u32x4_t f =
+            *reinterpret_cast<const u32x4_t*>(lw + 4096u * p + skinny_off(r, 4u * h + c));
+        const i32x8_t v{(int32_t)f.x, (int32_t)f.y, (int32_t)f.z, (int32_t)f.w, 0, 0, 0, 0};
+        if (p < MT) va[p] = v;
+        else vb[p - MT] = v;
+      }
+#pragma unroll
+      for (int ti = 0; ti < MT; ++ti)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[ti][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              va[ti], vb[j], acc[ti][j], 4, 4, 0,
+              (int32_t)(((t.s[ti] & keep) >> (8 * c)) & 0xFFu), 0,
+              (int32_t)(((t.s[MT + j] & keep) >> (8 * c)) & 0xFFu));
     }
   };
-  SkinnyStep t[kSkinnySets];
+  SkinnyStep<MT, NT> t[kSets];
 #pragma unroll
-  for (int j = 0; j < kSkinnySets; ++j) load(j, t[j]);
-  auto step = [&](auto J, int32_t i) {
-    constexpr int j = decltype(J)::value;
-    mma(i, t[j]);
-    load(i + kSkinnySets, t[j]);
-  };
+  for (int j = 0; j < kSets; ++j) load(j, t[j]);
   int32_t i = 0;
-  for (; i + kSkinnySets - 1 < cnt; i += kSkinnySets) {
-    step(std::integral_constant<int, 0>{}, i);
-    step(std::integral_constant<int, 1>{}, i + 1);
-    step(std::integral_constant<int, 2>{}, i + 2);
-    step(std::integral_constant<int, 3>{}, i + 3);
-  }
-  if (i < cnt) step(std::integral_constant<int, 0>{}, i);
-  if (i + 1 < cnt) step(std::integral_constant<int, 1>{}, i + 1);
-  if (i + 2 < cnt) step(std::integral_constant<int, 2>{}, i + 2);
-
-  __syncthreads();  // every wave is done with its operand buffer
-  f32x16_t* part = reinterpret_cast<f32x16_t*>(smem);  // [kSkinnyWaves - 1][64]
-  if (w > 0) part[64 * (w - 1) + lane] = acc;
-  __syncthreads();
-  if (w != 0) return;
+  for (; i + kSets - 1 < cnt; i += kSets) {
 #pragma unroll
-  for (int v = 0; v < kSkinnyWaves - 1; ++v) {
-    const f32x16_t p = part[64 * v + lane];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] += p[e];
-  }
-  // lane (n, h) holds column n, rows 8 (e / 4) + 4 h + e % 4
-  const int32_t col = n0 + (int32_t)r;
-  if (col >= g.n) return;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int32_t row = m0 + 8 * (e / 4) + 4 * (int32_t)h + e % 4;
-    if (row >= g.m) continue;
-    if constexpr (kBf16Out) {
-      const uint32_t p = pack_bf16x2(acc[e], 0.0f);
-      static_cast<uint16_t*>(g.c)[(int64_t)row * g.ld_c + col] = (uint16_t)(p & 0xFFFFu);
-    } else {
-      static_cast<float*>(g.c)[(int64_t)row * g.ld_c + col] = acc[e];
+    for (int j = 0; j < kSets; ++j) {
+      mma(i + j, t[j]);
+      load(i + j + kSets, t[j]);
     }
   }
+#pragma unroll
+  for (int j = 0; j < kSets - 1; ++j)
+    if (i + j < cnt) mma(i + j, t[j]);
+
+  // Partial tiles to LDS, four accumulator elements (one row group) per
+  // 16-byte slot, lanes contiguous; then wave w adds up the items (tile, row
+  // group) w, w + 8, ... over the waves in order 0..7 (deterministic) and
+  // writes them. Lane (n, h) of a tile holds column n, rows 8 (e / 4) + 4 h +
+  // e % 4.
+  constexpr int kT = MT * NT;
+  __syncthreads();  // every wave is done with its operand buffers
+  f32x4_t* part = reinterpret_cast<f32x4_t*>(smem);  // [kSkinnyWaves][kT][4][64]
+#pragma unroll
+  for (int ti = 0; ti < MT; ++ti)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        part[64 * ((w * kT + ti * NT + j) * 4 + q) + lane] =
+            f32x4_t{acc[ti][j][4 * q], acc[ti][j][4 * q + 1], acc[ti][j][4 * q + 2],
+                    acc[ti][j][4 * q + 3]};
+  __syncthreads();
+  for (int item = w; item < kT * 4; item += kSkinnyWaves) {
+    f32x4_t sum = part[64 * item + lane];
+#pragma unroll
+    for (int v = 1; v < kSkinnyWaves; ++v) {
+      const f32x4_t p = part[64 * (v * kT * 4 + item) + lane];
+      sum.x += p.x;
+      sum.y += p.y;
+      sum.z += p.z;
+      sum.w += p.w;
+    }
+    const int32_t tq = item / 4, q = item % 4;
+    const int32_t col = n0 + 32 * (tq % NT) + (int32_t)r;
+    const int32_t row0 = m0 + 32 * (tq / NT) + 8 * q + 4 * (int32_t)h;
+    if (col >= g.n) continue;
+    const float vals[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int32_t row = row0 + e;
+      if (row >= g.m) continue;
+      if constexpr (kBf16Out) {
+        const uint32_t pk = pack_bf16x2(vals[e], 0.0f);
+        static_cast<uint16_t*>(g.c)[(int64_t)row * g.ld_c + col] = (uint16_t)(pk & 0xFFFFu);
+      } else {
+        static_cast<float*>(g.c)[(int64_t)row * g.ld_c + col] = vals[e];
+      }
+    }
+  }
+}
+
+template <int MT, int NT, int kSets>
+void launch_skinny(const GemmArgs& g, bool bf16_out, hipStream_t st) {
+  const unsigned grid =
+      skinny_grid((g.n + 32 * NT - 1) / (32 * NT), (g.m + 32 * MT - 1) / (32 * MT));
+  if (bf16_out)
+    hipLaunchKernelGGL((mx_gemm_skinny_kernel<MT, NT, kSets, true>), dim3(grid),
+                       dim3(64 * kSkinnyWaves), 0, st, g);
+  else
+    hipLaunchKernelGGL((mx_gemm_skinny_kernel<MT, NT, kSets, false>), dim3(grid),
+                       dim3(64 * kSkinnyWaves), 0, st, g);
 }
 
 template <int WM, int WN, int VM, int VN, int KB, int kSets>
@@ -469,14 +515,13 @@ void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a
   GemmArgs g{static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(sa),
              static_cast<const uint8_t*>(b), static_cast<const uint8_t*>(sb), c,
              ld_a, ld_sa, ld_b, ld_sb, ld_c, (int32_t)m, (int32_t)n, (int32_t)k};
-  if (m <= kSkinnyMaxM) {  // decode-shaped: K split over the waves of a work-group
-    const unsigned grid = skinny_grid((n + 31) / 32, (m + 31) / 32);
-    if (bf16_out)
-      hipLaunchKernelGGL((mx_gemm_skinny_kernel<true>), dim3(grid), dim3(64 * kSkinnyWaves), 0, st, g);
-    else
-      hipLaunchKernelGGL((mx_gemm_skinny_kernel<false>), dim3(grid), dim3(64 * kSkinnyWaves), 0, st, g);
-    return;
-  }
+  // split-K tiles: two super-steps in flight per wave for 1 x 1 (7.6 us at
+  // 16 x 8192 x 8192 against 9.8 with four), one for the wider tiles (their
+  // larger steps already fill the caches' queues; two measured no faster)
+  const SkinnyShape sh = skinny_shape(m, n, device_info().cus, kSkinnyMaxM, 8);
+  if (sh.mt == 1 && sh.nt == 1) return launch_skinny<1, 1, 2>(g, bf16_out, st);
+  if (sh.mt == 1 && sh.nt == 2) return launch_skinny<1, 2, 1>(g, bf16_out, st);
+  if (sh.mt == 2 && sh.nt == 2) return launch_skinny<2, 2, 1>(g, bf16_out, st);
   // large products: 256 x 256 tiles halve the operand traffic per flop;
   // smaller ones keep 128 x 128 for more work-groups
   // 256 x 256: eight waves (2 x 4) of 4 x 2 MFMA tiles, two per SIMD, so one

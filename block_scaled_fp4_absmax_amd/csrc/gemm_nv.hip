@@ -228,27 +228,24 @@ __global__ __launch_bounds__(64 * VM * VN) void nv_gemm_kernel(NvGemmArgs g) {
     }
 }
 
-// Decode-shaped products (m <= kNvSkinnyMaxM), as the MXFP4 decode kernel: a
-// work-group of eight waves computes one 32 x 32 tile of C, wave w takes the
-// 256-K super-steps w, w + 8, ..., each operand's 32 rows x 128 code bytes
-// are loaded with eight consecutive lanes per 128-byte row piece and passed
+// Split-K products, as the MXFP4 split-K kernel: a work-group of eight
+// waves computes MT x NT tiles of 32 x 32 of C, wave w takes the 256-K
+// super-steps w, w + 8, ...; each operand piece (32 rows x 128 code bytes)
+// is loaded with eight consecutive lanes per 128-byte row piece and passed
 // through the wave's XOR-swizzled LDS buffer, so that lane (r, h) holds the
-// 128 elements 128 h .. 128 h + 127 of row r of the step (16 dwords) and their
-// 8 scale bytes. MFMA q (0..15) of the step takes dword q, eight elements,
-// from both operands in both lane halves (the same K values of A and B in
-// every lane), decoded exactly to bf16 with the block scale of that dword
-// (byte q / 2). Partial tiles are added in LDS in wave order.
+// 128 elements 128 h .. 128 h + 127 of row r of the step (16 dwords) and
+// their 8 scale bytes. MFMA q (0..15) of a tile pair takes dword q, eight
+// elements, from both operands in both lane halves (the same K values of A
+// and B in every lane), decoded exactly to bf16 with the block scale of that
+// dword (byte q / 2); each decoded dword serves every tile pair it belongs
+// to. Partial tiles are added in LDS in wave order.
 constexpr int kNvSkinnyWaves = 8;
-constexpr int kNvSkinnySets = 3;
-// Up to this many rows of A the product takes this kernel, one work-group
-// per 32 x 32 tile of C (row tiles of one column tile on one XCD). Measured
-// at n = k = 8192: 42 us against 107 us for the 128 x 128 tiles at m = 64,
-// 99 against 108 at m = 160, 116 against 108 at m = 192.
-constexpr int kNvSkinnyMaxM = 160;
+constexpr int kNvSkinnyMaxM = 256;  // larger m always takes the 128 x 128 or 256 x 256 tiles
 
+template <int MT, int NT>
 struct NvSkinnyStep {
-  u32x4_t a[4], b[4];  // row 8 c + lane / 8, 16-byte chunk lane % 8
-  uint32_t sa[2], sb[2];  // row lane % 32: scale bytes 8 h .. 8 h + 7 of the step
+  u32x4_t v[MT + NT][4];  // row 8 c + lane / 8 of the piece, 16-byte chunk lane % 8
+  uint32_t s[MT + NT][2];  // row lane % 32 of the piece: scale bytes 8 h .. 8 h + 7 of the step
 };
 
 __device__ __forceinline__ uint32_t nv_skinny_off(uint32_t r, uint32_t j) {
@@ -286,21 +283,23 @@ __device__ __forceinline__ nbf16x8_t nv_decode8(uint32_t wd, uint32_t sbyte) {
   return __builtin_bit_cast(nbf16x8_t, o);
 }
 
-template <int kModeA, int kModeB, bool kBf16Out>
+template <int MT, int NT, int kSets, int kModeA, int kModeB, bool kBf16Out>
 __global__ __launch_bounds__(64 * kNvSkinnyWaves) void nv_gemm_skinny_kernel(NvGemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kNvSkinnyWaves * 8192];
-  const SkinnyTile tile = skinny_tile(blockIdx.x, (g.m + 31) / 32);
-  const int32_t n0 = tile.x * 32, m0 = tile.y * 32;
+  constexpr int kP = MT + NT, kT = MT * NT;
+  constexpr int kOps = kNvSkinnyWaves * kP * 4096;   // operand pieces
+  constexpr int kRed = kNvSkinnyWaves * 64 * kT * 64;  // partial tiles
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kOps > kRed ? kOps : kRed];
+  const SkinnyTile tile = skinny_tile(blockIdx.x, (g.m + 32 * MT - 1) / (32 * MT));
+  const int32_t n0 = tile.x * 32 * NT, m0 = tile.y * 32 * MT;
   if (n0 >= g.n) return;  // padding of the grid to whole XCD rounds
-  const int32_t rows_a = min(32, g.m - m0), rows_b = min(32, g.n - n0);
+  const int32_t rows_a = min(32 * MT, g.m - m0), rows_b = min(32 * NT, g.n - n0);
   const rsrc_t ra = make_rsrc(g.a + (int64_t)m0 * g.ld_a, (uint32_t)(rows_a * g.ld_a));
   const rsrc_t rsa = make_rsrc(g.sa + (int64_t)m0 * g.ld_sa, (uint32_t)(rows_a * g.ld_sa));
   const rsrc_t rb = make_rsrc(g.b + (int64_t)n0 * g.ld_b, (uint32_t)(rows_b * g.ld_b));
   const rsrc_t rsb = make_rsrc(g.sb + (int64_t)n0 * g.ld_sb, (uint32_t)(rows_b * g.ld_sb));
   const uint32_t lane = threadIdx.x & 63u, r = lane & 31u, h = lane >> 5;
   const int32_t w = (int32_t)(threadIdx.x >> 6);
-  uint8_t* const la = smem + 8192u * (uint32_t)w;
-  uint8_t* const lb = la + 4096u;
+  uint8_t* const lw = smem + kP * 4096u * (uint32_t)w;
   const uint32_t kbytes = (uint32_t)g.k / 2u, nblk = (uint32_t)g.k / 16u;
   const int32_t steps = (g.k + 255) / 256;
   const int32_t cnt = steps > w ? (steps - w + kNvSkinnyWaves - 1) / kNvSkinnyWaves : 0;
@@ -308,110 +307,150 @@ __global__ __launch_bounds__(64 * kNvSkinnyWaves) void nv_gemm_skinny_kernel(NvG
   // loads of the wave's i-th super-step (past the list or past K: offsets out
   // of range, which read zeros without touching memory; code 0 decodes to +0
   // whatever the scale byte)
-  auto load = [&](int32_t i, NvSkinnyStep& t) __attribute__((always_inline)) {
+  auto load = [&](int32_t i, NvSkinnyStep<MT, NT>& t) __attribute__((always_inline)) {
     const int32_t s = w + kNvSkinnyWaves * i;
     const bool live = i < cnt;
     const uint32_t off = 128u * (uint32_t)s + 16u * (lane & 7u);
     const bool ok = live && off < kbytes;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t row = 8u * c + (lane >> 3);
-      t.a[c] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? row * (uint32_t)g.ld_a + off : kOob,
-                                                     0, 0);
-      t.b[c] = __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? row * (uint32_t)g.ld_b + off : kOob,
-                                                     0, 0);
-    }
-    // scale bytes in 16-bit pieces (rows are 2-byte aligned); an even block
-    // index below nblk (even, as k % 32 == 0) covers both of its blocks
+    for (int p = 0; p < kP; ++p) {
+      const bool pa = p < MT;
+      const uint32_t base = 32u * (uint32_t)(pa ? p : p - MT);
+      const uint32_t ld = (uint32_t)(pa ? g.ld_a : g.ld_b);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t blk = 16u * (uint32_t)s + 8u * h + 2u * q;
-      const bool oks = live && blk < nblk;
-      const uint32_t va = __builtin_amdgcn_raw_buffer_load_b16(
-          rsa, oks ? r * (uint32_t)g.ld_sa + blk : kOob, 0, 0);
-      const uint32_t vb = __builtin_amdgcn_raw_buffer_load_b16(
-          rsb, oks ? r * (uint32_t)g.ld_sb + blk : kOob, 0, 0);
-      if (q % 2 == 0) {
-        t.sa[q / 2] = va;
-        t.sb[q / 2] = vb;
-      } else {
-        t.sa[q / 2] |= va << 16;
-        t.sb[q / 2] |= vb << 16;
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t row = base + 8u * c + (lane >> 3);
+        t.v[p][c] = __builtin_amdgcn_raw_buffer_load_b128(pa ? ra : rb,
+                                                          ok ? row * ld + off : kOob, 0, 0);
+      }
+      // scale bytes in 16-bit pieces (rows are 2-byte aligned); an even block
+      // index below nblk (even, as k % 32 == 0) covers both of its blocks
+      const uint32_t lds_ = (uint32_t)(pa ? g.ld_sa : g.ld_sb);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t blk = 16u * (uint32_t)s + 8u * h + 2u * q;
+        const bool oks = live && blk < nblk;
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b16(
+            pa ? rsa : rsb, oks ? (base + r) * lds_ + blk : kOob, 0, 0);
+        if (q % 2 == 0) t.s[p][q / 2] = v;
+        else t.s[p][q / 2] |= v << 16;
       }
     }
   };
 
-  nf32x16_t acc;
+  nf32x16_t acc[MT][NT];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-  auto mma = [&](const NvSkinnyStep& t) __attribute__((always_inline)) {
+  for (int ti = 0; ti < MT; ++ti)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t o = nv_skinny_off(8u * c + (lane >> 3), lane & 7u);
-      *reinterpret_cast<u32x4_t*>(la + o) = t.a[c];
-      *reinterpret_cast<u32x4_t*>(lb + o) = t.b[c];
-    }
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[ti][j][e] = 0.0f;
+  auto mma = [&](const NvSkinnyStep<MT, NT>& t) __attribute__((always_inline)) {
+    nv_wave_sync();  // the previous step's reads of the buffer are done
+#pragma unroll
+    for (int p = 0; p < kP; ++p)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<u32x4_t*>(lw + 4096u * p +
+                                    nv_skinny_off(8u * c + (lane >> 3), lane & 7u)) = t.v[p][c];
     nv_wave_sync();
-    u32x4_t fa[4], fb[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t o = nv_skinny_off(r, 4u * h + c);
-      fa[c] = *reinterpret_cast<const u32x4_t*>(la + o);
-      fb[c] = *reinterpret_cast<const u32x4_t*>(lb + o);
-    }
-    nv_wave_sync();  // the buffer is written again by the next step
+      u32x4_t f[kP];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const uint32_t sba = (t.sa[q / 8] >> (8 * ((q / 2) % 4))) & 0xFFu;
-      const uint32_t sbb = (t.sb[q / 8] >> (8 * ((q / 2) % 4))) & 0xFFu;
-      const nbf16x8_t da = nv_decode8<kModeA>(fa[q / 4][q % 4], sba);
-      const nbf16x8_t db = nv_decode8<kModeB>(fb[q / 4][q % 4], sbb);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, db, acc, 0, 0, 0);
+      for (int p = 0; p < kP; ++p)
+        f[p] = *reinterpret_cast<const u32x4_t*>(lw + 4096u * p + nv_skinny_off(r, 4u * h + c));
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int q = 4 * c + d;
+        nbf16x8_t da[MT], db[NT];
+#pragma unroll
+        for (int ti = 0; ti < MT; ++ti)
+          da[ti] = nv_decode8<kModeA>(f[ti][d], (t.s[ti][q / 8] >> (8 * ((q / 2) % 4))) & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          db[j] = nv_decode8<kModeB>(f[MT + j][d],
+                                     (t.s[MT + j][q / 8] >> (8 * ((q / 2) % 4))) & 0xFFu);
+#pragma unroll
+        for (int ti = 0; ti < MT; ++ti)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[ti][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ti], db[j], acc[ti][j], 0, 0, 0);
+      }
     }
   };
-  NvSkinnyStep t[kNvSkinnySets];
+  NvSkinnyStep<MT, NT> t[kSets];
 #pragma unroll
-  for (int j = 0; j < kNvSkinnySets; ++j) load(j, t[j]);
-  auto step = [&](auto J, int32_t i) __attribute__((always_inline)) {
-    constexpr int j = decltype(J)::value;
-    mma(t[j]);
-    load(i + kNvSkinnySets, t[j]);
-  };
+  for (int j = 0; j < kSets; ++j) load(j, t[j]);
   int32_t i = 0;
-  for (; i + kNvSkinnySets - 1 < cnt; i += kNvSkinnySets) {
-    step(std::integral_constant<int, 0>{}, i);
-    step(std::integral_constant<int, 1>{}, i + 1);
-    step(std::integral_constant<int, 2>{}, i + 2);
-  }
-  if (i < cnt) step(std::integral_constant<int, 0>{}, i);
-  if (i + 1 < cnt) step(std::integral_constant<int, 1>{}, i + 1);
-
-  __syncthreads();  // every wave is done with its operand buffer
-  nf32x16_t* part = reinterpret_cast<nf32x16_t*>(smem);  // [kNvSkinnyWaves - 1][64]
-  if (w > 0) part[64 * (w - 1) + lane] = acc;
-  __syncthreads();
-  if (w != 0) return;
+  for (; i + kSets - 1 < cnt; i += kSets) {
 #pragma unroll
-  for (int v = 0; v < kNvSkinnyWaves - 1; ++v) {
-    const nf32x16_t p = part[64 * v + lane];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] += p[e];
-  }
-  const float ts = *g.ta * *g.tb;
-  const int32_t col = n0 + (int32_t)r;
-  if (col >= g.n) return;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int32_t row = m0 + 8 * (e / 4) + 4 * (int32_t)h + e % 4;
-    if (row >= g.m) continue;
-    const float v = acc[e] * ts;
-    if constexpr (kBf16Out) {
-      const uint32_t p = pack_bf16x2(v, 0.0f);
-      static_cast<uint16_t*>(g.c)[(int64_t)row * g.ld_c + col] = (uint16_t)(p & 0xFFFFu);
-    } else {
-      static_cast<float*>(g.c)[(int64_t)row * g.ld_c + col] = v;
+    for (int j = 0; j < kSets; ++j) {
+      mma(t[j]);
+      load(i + j + kSets, t[j]);
     }
   }
+#pragma unroll
+  for (int j = 0; j < kSets - 1; ++j)
+    if (i + j < cnt) mma(t[j]);
+
+  // Partial tiles to LDS, four accumulator elements (one row group) per
+  // 16-byte slot, lanes contiguous; then wave w adds up the items (tile, row
+  // group) w, w + 8, ... over the waves in order 0..7 (deterministic), scales
+  // them by the two tensor scales and writes them. Lane (n, h) of a tile
+  // holds column n, rows 8 (e / 4) + 4 h + e % 4.
+  __syncthreads();  // every wave is done with its operand buffers
+  f32x4_t* part = reinterpret_cast<f32x4_t*>(smem);  // [kNvSkinnyWaves][kT][4][64]
+#pragma unroll
+  for (int ti = 0; ti < MT; ++ti)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        part[64 * ((w * kT + ti * NT + j) * 4 + q) + lane] =
+            f32x4_t{acc[ti][j][4 * q], acc[ti][j][4 * q + 1], acc[ti][j][4 * q + 2],
+                    acc[ti][j][4 * q + 3]};
+  __syncthreads();
+  const float ts = *g.ta * *g.tb;
+  for (int item = w; item < kT * 4; item += kNvSkinnyWaves) {
+    f32x4_t sum = part[64 * item + lane];
+#pragma unroll
+    for (int v = 1; v < kNvSkinnyWaves; ++v) {
+      const f32x4_t p = part[64 * (v * kT * 4 + item) + lane];
+      sum.x += p.x;
+      sum.y += p.y;
+      sum.z += p.z;
+      sum.w += p.w;
+    }
+    const int32_t tq = item / 4, q = item % 4;
+    const int32_t col = n0 + 32 * (tq % NT) + (int32_t)r;
+    const int32_t row0 = m0 + 32 * (tq / NT) + 8 * q + 4 * (int32_t)h;
+    if (col >= g.n) continue;
+    const float vals[4] = {sum.x * ts, sum.y * ts, sum.z * ts, sum.w * ts};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int32_t row = row0 + e;
+      if (row >= g.m) continue;
+      if constexpr (kBf16Out) {
+        const uint32_t pk = pack_bf16x2(vals[e], 0.0f);
+        static_cast<uint16_t*>(g.c)[(int64_t)row * g.ld_c + col] = (uint16_t)(pk & 0xFFFFu);
+      } else {
+        static_cast<float*>(g.c)[(int64_t)row * g.ld_c + col] = vals[e];
+      }
+    }
+  }
+}
+
+template <int MT, int NT, int kSets, int kMa, int kMb>
+void nv_launch_skinny(const NvGemmArgs& g, bool bf16_out, hipStream_t st) {
+  const unsigned grid =
+      skinny_grid((g.n + 32 * NT - 1) / (32 * NT), (g.m + 32 * MT - 1) / (32 * MT));
+  if (bf16_out)
+    hipLaunchKernelGGL((nv_gemm_skinny_kernel<MT, NT, kSets, kMa, kMb, true>), dim3(grid),
+                       dim3(64 * kNvSkinnyWaves), 0, st, g);
+  else
+    hipLaunchKernelGGL((nv_gemm_skinny_kernel<MT, NT, kSets, kMa, kMb, false>), dim3(grid),
+                       dim3(64 * kNvSkinnyWaves), 0, st, g);
 }
 
 template <int WM, int WN, int VM, int VN, int kMa, int kMb>
@@ -428,16 +467,10 @@ void nv_launch(const NvGemmArgs& g, bool bf16_out, hipStream_t st) {
 
 template <int kMa, int kMb>
 void nv_tiles(const NvGemmArgs& g, bool bf16_out, hipStream_t st) {
-  if (g.m <= kNvSkinnyMaxM) {  // decode-shaped: K split over the waves of a work-group
-    const unsigned grid = skinny_grid((g.n + 31) / 32, (g.m + 31) / 32);
-    if (bf16_out)
-      hipLaunchKernelGGL((nv_gemm_skinny_kernel<kMa, kMb, true>), dim3(grid),
-                         dim3(64 * kNvSkinnyWaves), 0, st, g);
-    else
-      hipLaunchKernelGGL((nv_gemm_skinny_kernel<kMa, kMb, false>), dim3(grid),
-                         dim3(64 * kNvSkinnyWaves), 0, st, g);
-    return;
-  }
+  const SkinnyShape sh = skinny_shape(g.m, g.n, device_info().cus, kNvSkinnyMaxM, 10);
+  if (sh.mt == 1 && sh.nt == 1) return nv_launch_skinny<1, 1, 2, kMa, kMb>(g, bf16_out, st);
+  if (sh.mt == 1 && sh.nt == 2) return nv_launch_skinny<1, 2, 1, kMa, kMb>(g, bf16_out, st);
+  if (sh.mt == 2 && sh.nt == 2) return nv_launch_skinny<2, 2, 1, kMa, kMb>(g, bf16_out, st);
   // 256 x 256 from eight waves (two per SIMD) of 4 x 2 MFMA tiles: 17-24%
   // faster than four waves of 4 x 4 on the layer shapes, bit-identical
   if (g.m >= 2048 && g.n >= 2048)

@@ -80,13 +80,16 @@ def _check(orc, ac, as_, bc, bs, k, bf16=False, pad=0):
 @pytest.mark.parametrize("m,n,k", [(128, 128, 128), (1, 1, 32), (37, 45, 96), (200, 300, 4160),
                                    (1, 512, 8192), (256, 384, 8192), (513, 129, 1024),
                                    (2048, 2304, 1024), (2100, 2050, 544),
-                                   # m <= 96 takes the decode-shaped kernel (K split over
-                                   # eight waves, a 32 x 32 tile per work-group; column
-                                   # tiles padded to multiples of 8)
+                                   # split-K kernel (K over eight waves): one 32 x 32 tile
+                                   # per work-group (most shapes up to m = 256 with few
+                                   # tiles), 32 x 64 (20 x 8300, 30 x 9000) or 64 x 64
+                                   # (40 x 9000, 128 x 8192); column tiles padded to
+                                   # multiples of 8
                                    (16, 2048, 8192), (32, 1000, 4160), (7, 300, 96),
                                    (1, 33, 544), (31, 64, 28672), (16, 96, 256),
                                    (33, 520, 4160), (64, 257, 1056), (96, 1000, 544),
-                                   (97, 64, 256)])
+                                   (97, 64, 256), (20, 8300, 544), (30, 9000, 256),
+                                   (40, 9000, 256), (128, 8192, 96)])
 def test_gemm_random_codes(orc, m, n, k):
     note(f"case: MXFP4 GEMM {m}x{n}x{k} random codes and scales")
     rng = np.random.default_rng(m + 7 * n + k)
@@ -205,17 +208,19 @@ def _check_nv(orc, ac, as_, ta, ra, bc, bs, tb, rb, k, bf16=False):
     (128, 128, 128, False, False), (128, 128, 128, True, True), (37, 45, 96, True, False),
     (200, 300, 4160, False, True), (1, 512, 8192, True, True), (2048, 2304, 1024, True, True),
     (2100, 2050, 544, False, False),
-    # m <= 160: the decode-shaped kernel
+    # the split-K kernel, 32 x 32, 32 x 64 (20 x 8300) and 64 x 64 (40 x 9000,
+    # 128 x 8192) tiles per work-group
     (16, 2048, 8192, True, True), (32, 1000, 4160, False, True), (7, 300, 96, True, False),
     (1, 33, 544, False, False), (31, 64, 28672, True, True), (20, 70, 1056, False, False),
-    (65, 520, 1056, True, False), (160, 300, 544, False, True), (161, 96, 512, True, True)])
+    (65, 520, 1056, True, False), (160, 300, 544, False, True), (161, 96, 512, True, True),
+    (20, 8300, 544, True, False), (40, 9000, 256, True, True), (128, 8192, 96, False, True)])
 def test_nv_gemm_random_codes(orc, m, n, k, ra, rb):
     note(f"case: NVFP4 GEMM {m}x{n}x{k} razer A={ra} B={rb}")
     rng = np.random.default_rng(m + 3 * n + k + ra + 2 * rb)
     ac, as_ = _rand_nv(rng, m, k, ra)
     bc, bs = _rand_nv(rng, n, k, rb)
     _check_nv(orc, ac, as_, float(np.float32(0.0371)), ra, bc, bs, float(np.float32(2.5e-3)), rb,
-              k, bf16=(m in (37, 20)))
+              k, bf16=(m in (37, 20, 40)))
 
 
 def test_nv_gemm_of_quantized_layer(orc):
