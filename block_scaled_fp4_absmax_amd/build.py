@@ -14,7 +14,7 @@ LIB = os.path.join(HERE, "libfp4.so")
 SOURCES = ["quant.hip", "rotate_mx.hip", "rotate_int.hip", "rotate_nv.hip", "rotate_mat.hip",
            "unrotate_mx.hip", "unrotate_int.hip", "unrotate_nv.hip", "unrotate_mat.hip", "givens.hip", "gemm.hip", "gemm_nv.hip", "api.cpp", "perm.cpp", "calib.cpp", "device.cpp"]
 HEADERS = ["fp4_device.hpp", "launch.hpp", "rotation.hpp", "rotate_kernels.hpp",
-           "unrotate_kernels.hpp"]
+           "unrotate_kernels.hpp", "split_k.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

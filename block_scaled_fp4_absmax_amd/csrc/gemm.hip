@@ -35,6 +35,7 @@
 
 #include "fp4_device.hpp"
 #include "launch.hpp"
+#include "split_k.hpp"
 
 namespace fp4 {
 

@@ -27,6 +27,7 @@
 
 #include "fp4_device.hpp"
 #include "launch.hpp"
+#include "split_k.hpp"
 
 namespace fp4 {
 
