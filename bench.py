@@ -118,6 +118,36 @@ def timed(torch, fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def graph_us(torch, fn, calls=20, replays=5):
+    """us per call of fn() replayed from a HIP graph of `calls` calls: the
+    GPU-side time of launches too short for the Python binding to keep the
+    queue ahead of them (the library records no allocation and no memset, so
+    the calls capture as they run)."""
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        fn()  # warm-up on the capture stream
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(cur)
+    for _ in range(replays):
+        g.replay()
+    b.record(cur)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (calls * replays)
+    del g
+    return us
+
+
 def step_distribution(torch, fn, n):
     """p10 / p50 / p90 of single-step times (us): an event pair around each of n
     back-to-back steps; the queue stays ahead of the GPU, so each pair brackets
@@ -480,6 +510,11 @@ def gemm_rows(torch, fp4, fmt):
         rows[f"{m}x{n}x{k}"] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
                                 "frac_mfma_peak": round(tf / peak, 4),
                                 "GBps": round(by / ms / 1e6, 1)}
+        if m <= 32:  # µs-scale launches: also their time replayed from a graph
+            us = graph_us(torch, lambda: fp4.gemm(a, sa, b, sb, out=c, **kw))
+            rows[f"{m}x{n}x{k}"]["graph_us_per_call"] = round(us, 2)
+            rows[f"{m}x{n}x{k}"]["graph_frac_mfma_peak"] = round(
+                2.0 * m * n * k / (us * 1e-6) / 1e12 / peak, 4)
         del a, sa, b, sb, c
     return rows
 

@@ -26,7 +26,7 @@ def _gpu():
 
 def test_graph_replays_match_eager():
     note("case: HIP graph of rotate+quantize (MXFP4), NVFP4 RaZeR with computed s_t, "
-         "dequantize with inverse rotation, and the GEMM; 4 replays")
+         "dequantize with inverse rotation, and the GEMM (tiles and split-K); 4 replays")
     x = to_dev(inputs.gen_c4(rows=512, cols=4096))
     w = to_dev(inputs.gen_c5(0, rows=256, cols=4096))
     perm = fp4.build_permutation(fp4.channel_energy(x)).cuda()
@@ -40,6 +40,7 @@ def test_graph_replays_match_eager():
     cw = torch.empty((256, 2048), dtype=torch.uint8, device="cuda")
     sw = torch.empty((256, 128), dtype=torch.uint8, device="cuda")
     out = torch.empty((512, 256), dtype=torch.float32, device="cuda")
+    out16 = torch.empty((16, 256), dtype=torch.bfloat16, device="cuda")  # split-K GEMM
 
     def work():
         fp4.rotate_quantize(x, perm, 32, codes=c, scales=s)
@@ -48,10 +49,11 @@ def test_graph_replays_match_eager():
                      scales=sn)
         fp4.rotate_quantize(w, None, 32, codes=cw, scales=sw)
         fp4.gemm(c, s, cw, sw, out=out)
+        fp4.gemm(c[:16], s[:16], cw, sw, out=out16)
 
     work()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (c, s, d, cn, sn, tn, cw, sw, out)]
+    ref = [t.clone() for t in (c, s, d, cn, sn, tn, cw, sw, out, out16)]
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -62,10 +64,10 @@ def test_graph_replays_match_eager():
     with torch.cuda.graph(g):
         work()
     for rep in range(4):
-        for t in (c, s, d, cn, sn, tn, cw, sw, out):
+        for t in (c, s, d, cn, sn, tn, cw, sw, out, out16):
             t.zero_()  # eager work between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for a, b in zip((c, s, d, cn, sn, tn, cw, sw, out), ref):
+        for a, b in zip((c, s, d, cn, sn, tn, cw, sw, out, out16), ref):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}"
