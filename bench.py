@@ -119,7 +119,7 @@ def timed(torch, fn, steps, warmup):
 
 
 def graph_us(torch, fn, calls=20, replays=5):
-    """us per call of fn() replayed from a HIP graph of `calls` calls: the
+    """us per call of fn(i) replayed from a HIP graph of calls i = 0..calls-1: the
     GPU-side time of launches too short for the Python binding to keep the
     queue ahead of them (the library records no allocation and no memset, so
     the calls capture as they run)."""
@@ -127,13 +127,14 @@ def graph_us(torch, fn, calls=20, replays=5):
     side = torch.cuda.Stream()
     side.wait_stream(cur)
     with torch.cuda.stream(side):
-        fn()  # warm-up on the capture stream
+        for i in range(calls):
+            fn(i)  # warm-up on the capture stream
     cur.wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _ in range(calls):
-            fn()
+        for i in range(calls):
+            fn(i)
     g.replay()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
@@ -448,6 +449,12 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     ss = [torch.empty((r2, c2 // 16), dtype=torch.uint8, device="cuda") for _ in range(m)]
     tss = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(m)]
     el2 = r2 * c2
+
+    def graph_row(key, fn, per_el):
+        # the same calls replayed from a HIP graph (host submission removed)
+        us = graph_us(torch, fn, calls=2 * m)
+        out[key]["graph_us_per_call"] = round(us, 2)
+        out[key]["graph_algorithmic_GBps"] = round(el2 * per_el / us / 1e3, 1)
     ms = timed(torch, lambda i: fp4.quantize(ys[i % m], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[i % m],
                                              scale_given=False, codes=cs[i % m],
                                              scales=ss[i % m]), 40, 5)
@@ -457,15 +464,23 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     ms = timed(torch, lambda i: fp4.quantize(ys[i % m], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[i % m],
                                              codes=cs[i % m], scales=ss[i % m]), 40, 5)
     out["c2_nvfp4_razer_quantize_scale_given"] = gbs(ms, el2, B_NV)
+    graph_row("c2_nvfp4_razer_quantize_scale_given", lambda i: fp4.quantize(
+        ys[i % m], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[i % m], codes=cs[i % m],
+        scales=ss[i % m]), B_NV)
     ms = timed(torch, lambda i: fp4.quantize(ys[i % m], fp4.NVFP4, fp4.PLAIN, tensor_scale=tss[i % m],
                                              codes=cs[i % m], scales=ss[i % m]), 40, 5)
     out["c2_nvfp4_plain_quantize_scale_given"] = gbs(ms, el2, B_NV)
+    graph_row("c2_nvfp4_plain_quantize_scale_given", lambda i: fp4.quantize(
+        ys[i % m], fp4.NVFP4, fp4.PLAIN, tensor_scale=tss[i % m], codes=cs[i % m],
+        scales=ss[i % m]), B_NV)
     for k in range(m):
         fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[k], codes=cs[k], scales=ss[k])
     ob = torch.empty_like(ys[0])
     ms = timed(torch, lambda i: fp4.dequantize(cs[i % m], ss[i % m], fp4.NVFP4, fp4.RAZER,
                                                tss[i % m], out=ob), 40, 5)
     out["c2_nvfp4_razer_dequantize"] = gbs(ms, el2, B_NV)
+    graph_row("c2_nvfp4_razer_dequantize", lambda i: fp4.dequantize(
+        cs[i % m], ss[i % m], fp4.NVFP4, fp4.RAZER, tss[i % m], out=ob), B_NV)
     ms = timed(torch, lambda i: fp4.quantize(ys[i % m], fp4.NVFP4, fp4.RAZER_W,
                                              tensor_scale=tss[i % m], codes=cs[i % m],
                                              scales=ss[i % m]), 40, 5)
@@ -511,7 +526,7 @@ def gemm_rows(torch, fp4, fmt):
                                 "frac_mfma_peak": round(tf / peak, 4),
                                 "GBps": round(by / ms / 1e6, 1)}
         if m <= 32:  # µs-scale launches: also their time replayed from a graph
-            us = graph_us(torch, lambda: fp4.gemm(a, sa, b, sb, out=c, **kw))
+            us = graph_us(torch, lambda i: fp4.gemm(a, sa, b, sb, out=c, **kw))
             rows[f"{m}x{n}x{k}"]["graph_us_per_call"] = round(us, 2)
             rows[f"{m}x{n}x{k}"]["graph_frac_mfma_peak"] = round(
                 2.0 * m * n * k / (us * 1e-6) / 1e12 / peak, 4)
