@@ -272,10 +272,14 @@ __device__ __forceinline__ uint32_t razer_apply(uint32_t w, uint32_t cm, uint32_
   return (w & ~((spm >> 3) * 0xFu)) | spm;
 }
 
-// Gain flag of one element in nibble k (see razer_gain): bit 31 of
-// bits(g) + 0x7FFFFFFF is set iff g > 0.
-__device__ __forceinline__ uint32_t razer_flag(float g, int k) {
-  return ((__float_as_uint(g) + 0x7FFFFFFFu) >> 31) << (4 * k + 3);
+// Gain flags of eight elements (see razer_gain): bit 3 of nibble k is set iff
+// g[k] > 0. The gains lie in [+0, 1] and the positive ones are multiples of
+// 2^-22, so the FP4 conversion at scale 2^-100 sends each positive gain far
+// past 6, which saturates to code 7, and +0 to code 0 (checked on the GPU):
+// bit 2 of each nibble is the flag. Four conversions for eight elements, in
+// place of three integer instructions per element.
+__device__ __forceinline__ uint32_t razer_flags8(const float* g) {
+  return (cvt8_f32(g, 0x1p-100f) & 0x44444444u) << 1;
 }
 
 // ---- RaZeR for weights --------------------------------------------------------

@@ -201,13 +201,13 @@ __device__ __forceinline__ void nv_quant_chunk(u32x4_t d, const NvScale& ns, con
     if constexpr (kMode == 1) {
       // selector = [gains of negative elements exceed those of positive ones]
       float dsum = 0.0f;
-      uint32_t cm = 0;
+      float gk[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float gk = razer_gain(y[k]);  // in [0, 1]
-        dsum -= __builtin_copysignf(gk, y[k]);
-        cm |= razer_flag(gk, k);
+        gk[k] = razer_gain(y[k]);  // in [0, 1]
+        dsum -= __builtin_copysignf(gk[k], y[k]);
       }
+      const uint32_t cm = razer_flags8(gk);
       dsum += dpp_xor1f(dsum);
       const uint32_t sel = dsum > 0.0f ? 1u : 0u;
       w = razer_apply(w, cm, sel);
@@ -216,18 +216,18 @@ __device__ __forceinline__ void nv_quant_chunk(u32x4_t d, const NvScale& ns, con
       // block gains of the four specials (exact sums); the largest wins,
       // ties to the lower selector
       float g[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // +5, -5, +2.5, -2.5
-      uint32_t cm5 = 0, cm2 = 0;
+      float g5[8], g2[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float g5 = razer_gain(y[k]), g2 = razer_gain_pair2(y[k]);
+        g5[k] = razer_gain(y[k]);
+        g2[k] = razer_gain_pair2(y[k]);
         const bool neg = __float_as_uint(y[k]) >> 31;
-        g[0] += neg ? 0.0f : g5;
-        g[1] += neg ? g5 : 0.0f;
-        g[2] += neg ? 0.0f : g2;
-        g[3] += neg ? g2 : 0.0f;
-        cm5 |= razer_flag(g5, k);
-        cm2 |= razer_flag(g2, k);
+        g[0] += neg ? 0.0f : g5[k];
+        g[1] += neg ? g5[k] : 0.0f;
+        g[2] += neg ? 0.0f : g2[k];
+        g[3] += neg ? g2[k] : 0.0f;
       }
+      const uint32_t cm5 = razer_flags8(g5), cm2 = razer_flags8(g2);
 #pragma unroll
       for (int i = 0; i < 4; ++i) g[i] += dpp_xor1f(g[i]);
       uint32_t sel = 0;

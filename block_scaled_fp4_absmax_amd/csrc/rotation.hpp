@@ -209,15 +209,15 @@ __device__ __forceinline__ void nv_quant16(const float* y, const NvScale& ns, co
     byte = sb;
     if (kRazer) {
       float dsum = 0.0f;
-      uint32_t cm0 = 0, cm1 = 0;
+      float g[16];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float g0 = razer_gain(v[k]), g1 = razer_gain(v[k + 8]);
-        dsum -= __builtin_copysignf(g0, v[k]);
-        dsum -= __builtin_copysignf(g1, v[k + 8]);
-        cm0 |= razer_flag(g0, k);
-        cm1 |= razer_flag(g1, k);
+        g[k] = razer_gain(v[k]);
+        g[k + 8] = razer_gain(v[k + 8]);
+        dsum -= __builtin_copysignf(g[k], v[k]);
+        dsum -= __builtin_copysignf(g[k + 8], v[k + 8]);
       }
+      const uint32_t cm0 = razer_flags8(g), cm1 = razer_flags8(g + 8);
       const uint32_t sel = dsum > 0.0f ? 1u : 0u;
       w0 = razer_apply(w0, cm0, sel);
       w1 = razer_apply(w1, cm1, sel);
