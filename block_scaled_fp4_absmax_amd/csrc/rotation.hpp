@@ -50,6 +50,8 @@ __device__ __forceinline__ uint32_t out_index_of_row(uint32_t m) {
 // Walsh mask W(row & 15) is parity(row & j). For 16-point blocks A is
 // diag(H16, H16) on each 32-element segment: entries couple an output row
 // only to inputs of the same half (row / 16 == l / 32), with sign W(row & 15).
+// The 16-point entries are +-1/4 (exact in bf16), which carries the transform's
+// 1/sqrt(16) into the MFMA; the 32-point ones are +-1 (1/sqrt(32) is not exact).
 template <int kN>
 __device__ __forceinline__ void hadamard_operands(bf16x8_t& a0, bf16x8_t& a1) {
   static_assert(kN == 16 || kN == 32, "block Hadamard of 16 or 32 points");
@@ -58,11 +60,12 @@ __device__ __forceinline__ void hadamard_operands(bf16x8_t& a0, bf16x8_t& a1) {
   uint32_t m = ((row & 1u) ? 0xAAAAu : 0u) ^ ((row & 2u) ? 0xCCCCu : 0u) ^
                ((row & 4u) ? 0xF0F0u : 0u) ^ ((row & 8u) ? 0xFF00u : 0u);
   if (kN == 32 && ((lane >> 5) & (row >> 4))) m ^= 0xFFFFu;
-  const uint32_t one = (kN == 16 && (row >> 4) != (lane >> 5)) ? 0u : 0x3F803F80u;
+  constexpr uint32_t kUnit = kN == 16 ? 0x3E803E80u : 0x3F803F80u;  // bf16 pair 1/4 or 1
+  const uint32_t one = (kN == 16 && (row >> 4) != (lane >> 5)) ? 0u : kUnit;
   u32x4_t v0, v1;
   uint32_t w[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)  // bf16 pair: +-1 = 0x3F80 with the sign bit from the mask
+  for (int i = 0; i < 8; ++i)  // bf16 pair: the unit with the sign bit from the mask
     w[i] = one ? (one | (((m >> (2 * i)) & 1u) << 15) | (((m >> (2 * i + 1)) & 1u) << 31)) : 0u;
   v0 = u32x4_t{w[0], w[1], w[2], w[3]};
   v1 = u32x4_t{w[4], w[5], w[6], w[7]};
@@ -72,16 +75,16 @@ __device__ __forceinline__ void hadamard_operands(bf16x8_t& a0, bf16x8_t& a1) {
 
 // y[0..15] = (A x)[16h .. 16h+15] / sqrt(kN) for this lane's segment, from
 // the lane's 16 inputs x[16h .. 16h+15] (bf16 pairs in lo/hi); for kN = 16
-// these are the 16 outputs of one 16-element block, and 1/4 is exact.
+// these are the 16 outputs of one 16-element block, scaled by the operand's
+// exact 1/4 (every product and partial sum is the unscaled one times 1/4).
 template <int kN>
 __device__ __forceinline__ void hadamard_mfma(const bf16x8_t& a0, const bf16x8_t& a1,
                                               u32x4_t lo, u32x4_t hi, float* y) {
   f32x16_t acc = {};
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, __builtin_bit_cast(bf16x8_t, lo), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, __builtin_bit_cast(bf16x8_t, hi), acc, 0, 0, 0);
-  constexpr float kScale = kN == 32 ? kInvSqrt32 : 0.25f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) y[r] = acc[r] * kScale;
+  for (int r = 0; r < 16; ++r) y[r] = kN == 32 ? acc[r] * kInvSqrt32 : acc[r];
 }
 
 // A general 32x32 block matrix M (row-major fp32 in device memory), for the
