@@ -98,6 +98,17 @@ def test_gemm_random_codes(orc, m, n, k):
     _check(orc, ac, as_, bc, bs, k)
 
 
+@pytest.mark.parametrize("m,n,k,pad", [(20, 8300, 544, 16), (40, 9000, 256, 32)])
+def test_gemm_split_k_tiles_strides(orc, m, n, k, pad):
+    # 32 x 64 and 64 x 64 split-K tiles with padded code rows (never read)
+    # and bf16 output; the column tiles are padded to whole XCD rounds
+    note(f"case: MXFP4 split-K GEMM {m}x{n}x{k}, bf16 output, row pad {pad}")
+    rng = np.random.default_rng(m * n + pad)
+    ac, as_ = _rand_operand(rng, m, k)
+    bc, bs = _rand_operand(rng, n, k)
+    _check(orc, ac, as_, bc, bs, k, bf16=True, pad=pad)
+
+
 def test_gemm_bf16_out_and_strides(orc):
     note("case: MXFP4 GEMM 130x70x544, bf16 output, padded row strides")
     rng = np.random.default_rng(9)
