@@ -165,6 +165,15 @@ __device__ __forceinline__ u32x4_t int4x8_decode(uint32_t w, uint32_t byte) {
                  pack_bf16x2(v[6], v[7])};
 }
 
+// Eight nibbles -> bf16 pairs of k itself (exact), for a scale applied later.
+__device__ __forceinline__ u32x4_t int4x8_decode_unit(uint32_t w) {
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = (float)((int32_t)(w << (28 - 4 * k)) >> 28);
+  return u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                 pack_bf16x2(v[6], v[7])};
+}
+
 __device__ __forceinline__ void widen8(u32x4_t d, float* v) {
   v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
   v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);

@@ -73,18 +73,21 @@ __device__ __forceinline__ void hadamard_operands(bf16x8_t& a0, bf16x8_t& a1) {
   a1 = __builtin_bit_cast(bf16x8_t, v1);
 }
 
-// y[0..15] = (A x)[16h .. 16h+15] / sqrt(kN) for this lane's segment, from
+// y[0..15] = (A x)[16h .. 16h+15] / sqrt(kN) for this lane's segment (for
+// kN = 32, times `scale` in place of 1/sqrt(32) where the caller folds a
+// power of two into it), from
 // the lane's 16 inputs x[16h .. 16h+15] (bf16 pairs in lo/hi); for kN = 16
 // these are the 16 outputs of one 16-element block, scaled by the operand's
 // exact 1/4 (every product and partial sum is the unscaled one times 1/4).
 template <int kN>
 __device__ __forceinline__ void hadamard_mfma(const bf16x8_t& a0, const bf16x8_t& a1,
-                                              u32x4_t lo, u32x4_t hi, float* y) {
+                                              u32x4_t lo, u32x4_t hi, float* y,
+                                              float scale = kInvSqrt32) {
   f32x16_t acc = {};
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, __builtin_bit_cast(bf16x8_t, lo), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, __builtin_bit_cast(bf16x8_t, hi), acc, 0, 0, 0);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) y[r] = kN == 32 ? acc[r] * kInvSqrt32 : acc[r];
+  for (int r = 0; r < 16; ++r) y[r] = kN == 32 ? acc[r] * scale : acc[r];
 }
 
 // A general 32x32 block matrix M (row-major fp32 in device memory), for the

@@ -73,7 +73,34 @@ __device__ __forceinline__ void load_codes(const UnrotRsrc& q, const RotGeom& g,
 template <bool kHad, bool kInt>
 __device__ __forceinline__ void unrotate_tile(u32x2_t c, uint32_t sbyte, const bf16x8_t& a0,
                                               const bf16x8_t& a1, u32x4_t& lo, u32x4_t& hi) {
-  if constexpr (kInt) {
+  if constexpr (kInt && kHad) {
+    // The block scale 2^(e - 2) is a power of two, so it can follow the
+    // Hadamard: k decodes to bf16 as is, and one multiply by 2^(e - 2) / sqrt(32)
+    // gives the same real value, hence the same rounding, as scaling first,
+    // while that factor is a normal float (byte >= 6) and the scaled sums
+    // (at most 256 * 2^(e - 2)) stay finite (byte <= 248). Other bytes (tiny
+    // or huge scales, NaN) decode scaled.
+    // The MFMA combines lanes, so it runs on every lane outside the choice;
+    // the two lanes of a block share its byte and so its choice.
+    const uint32_t byte = sbyte & 0xFFu;
+    const bool fast = byte >= 6u && byte <= 248u;
+    u32x4_t dl, dh;
+    if (fast) {
+      dl = int4x8_decode_unit(c.x);
+      dh = int4x8_decode_unit(c.y);
+    } else {
+      dl = int4x8_decode(c.x, byte);
+      dh = int4x8_decode(c.y, byte);
+    }
+    float y[16];
+    hadamard_mfma<32>(a0, a1, dl, dh, y,
+                      fast ? __builtin_amdgcn_ldexpf(kInvSqrt32, (int)byte - 129) : kInvSqrt32);
+    lo = u32x4_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                 pack_bf16x2(y[6], y[7])};
+    hi = u32x4_t{pack_bf16x2(y[8], y[9]), pack_bf16x2(y[10], y[11]), pack_bf16x2(y[12], y[13]),
+                 pack_bf16x2(y[14], y[15])};
+    return;
+  } else if constexpr (kInt) {
     lo = int4x8_decode(c.x, sbyte & 0xFFu);
     hi = int4x8_decode(c.y, sbyte & 0xFFu);
   } else {

@@ -199,3 +199,26 @@ def test_mxint4_dequant_unrotate(orc, rows, cols, kind, had):
         sq = orc.sqnr_db(inputs.bf16_bits_to_f32(x), got)
         note(f"  round-trip SQNR {sq:.2f} dB")
         assert sq > 15
+
+
+def test_mxint4_dequant_hadamard_all_scale_bytes(orc):
+    # Every finite scale byte 0..240 on its own block: the bytes 6..248 take
+    # the scale after the Hadamard, the others before it; both must agree with
+    # the oracle (random codes in [-7, 7], the grid the quantizer writes).
+    note("case: MXINT4 dequantize + H32, scale bytes 0..240, random codes")
+    rng = np.random.default_rng(241)
+    nbytes = 241
+    rows, cols = 4, 32 * nbytes
+    k = rng.integers(-7, 8, size=(rows, cols))
+    nib = (k & 0xF).astype(np.uint8)
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.tile(np.arange(nbytes, dtype=np.uint8), (rows, 1))
+    d = fp4.dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                       fp4.MXINT4, perm=None, hadamard=32)
+    torch.cuda.synchronize()
+    want = orc.unrotate_f64(orc.dequantize_f64(codes, scales, 2), None, 32)
+    got = inputs.bf16_bits_to_f32(bf16_bits(d)).astype(np.float64)
+    blockmax = np.repeat(np.abs(want).reshape(rows, nbytes, 32).max(2), 32, axis=1)
+    tol = 2.0 ** -8 * np.abs(want) + 2.0 ** -20 * blockmax + 2.0 ** -133
+    err = np.abs(got - want)
+    assert np.all(err <= tol), f"max err at {np.unravel_index((err - tol).argmax(), err.shape)}"
