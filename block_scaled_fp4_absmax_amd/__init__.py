@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Tuple
+from typing import Optional
 
 __all__ = [
     "MXFP4", "NVFP4", "MXINT4", "PLAIN", "RAZER", "RAZER_W", "FLAG_TENSOR_SCALE_GIVEN", "FLAG_SCALE_OCP_FLOOR",
@@ -103,9 +103,61 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _rows_ld(t) -> Tuple[int, int, int]:
-    assert t.dim() == 2 and t.stride(1) == 1, "expects a 2-D tensor with contiguous rows"
+# ---- argument checks --------------------------------------------------------
+# The C ABI sees pointers, sizes and strides only, so a tensor of the wrong
+# dtype, device or size would be read or written out of bounds. Every
+# argument is checked here before its pointer is passed: dtype, 2-D with
+# contiguous rows (or a contiguous vector), enough rows and columns, and the
+# device of the call.
+
+
+def _mat(t, name, dtype, device, rows=None, min_cols=0, exact_rows=True):
+    """Check a 2-D argument; returns (rows, cols, row stride)."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1) or t.stride(0) < 0:
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    if rows is not None and (t.shape[0] != rows if exact_rows else t.shape[0] < rows):
+        raise ValueError(f"{name} has {t.shape[0]} rows, {rows} needed")
+    if t.shape[1] < min_cols:
+        raise ValueError(f"{name} has {t.shape[1]} columns, at least {min_cols} needed")
+    _on(t, name, device)
     return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _vec(t, name, dtype, n, device):
+    """Check a contiguous vector argument of at least n elements."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < n:
+        raise ValueError(f"{name} has {t.numel()} elements, at least {n} needed")
+    _on(t, name, device)
+
+
+def _on(t, name, device):
+    if device is None:  # host argument
+        if t.device.type != "cpu":
+            raise ValueError(f"{name} must be a host tensor")
+        return
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+
+
+def _device_of(x):
+    """The device of the call: the first tensor argument's (checked to be a
+    HIP device by the first _mat / _vec on it)."""
+    return x.device
+
+
+def _check_fmt(fmt, mode):
+    if fmt not in (MXFP4, NVFP4, MXINT4):
+        raise ValueError(f"unknown format {fmt}")
+    if mode not in (PLAIN, RAZER, RAZER_W):
+        raise ValueError(f"unknown mode {mode}")
 
 
 def _outputs(rows, cols, fmt, device, codes=None, scales=None):
@@ -114,7 +166,17 @@ def _outputs(rows, cols, fmt, device, codes=None, scales=None):
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
     if scales is None:
         scales = torch.empty((rows, cols // block_of(fmt)), dtype=torch.uint8, device=device)
+    _mat(codes, "codes", torch.uint8, device, rows, cols // 2)
+    _mat(scales, "scales", torch.uint8, device, rows, cols // block_of(fmt))
     return codes, scales
+
+
+def _tensor_scale(tensor_scale, device):
+    import torch
+    if tensor_scale is None:
+        return torch.empty(1, dtype=torch.float32, device=device)
+    _vec(tensor_scale, "tensor_scale", torch.float32, 1, device)
+    return tensor_scale
 
 
 def quantize(x, fmt: int = MXFP4, mode: int = PLAIN, floor_rule: bool = False,
@@ -129,17 +191,20 @@ def quantize(x, fmt: int = MXFP4, mode: int = PLAIN, floor_rule: bool = False,
     (allocated when None).
     """
     import torch
-    rows, cols, ld = _rows_ld(x)
-    codes, scales = _outputs(rows, cols, fmt, x.device, codes, scales)
+    _check_fmt(fmt, mode)
+    dev = _device_of(x)
+    rows, cols, ld = _mat(x, "x", torch.bfloat16, dev)
+    codes, scales = _outputs(rows, cols, fmt, dev, codes, scales)
     flags = FLAG_SCALE_OCP_FLOOR if floor_rule else 0
     ts = None
     if fmt == NVFP4:
         if scale_given is None:
             scale_given = tensor_scale is not None
         if scale_given:
+            if tensor_scale is None:
+                raise ValueError("scale_given needs a tensor_scale")
             flags |= FLAG_TENSOR_SCALE_GIVEN
-        ts = tensor_scale if tensor_scale is not None else torch.empty(
-            1, dtype=torch.float32, device=x.device)
+        ts = _tensor_scale(tensor_scale, dev)
     st = lib().fp4_quantize(_ptr(x), rows, cols, ld, fmt, block_of(fmt), mode, flags,
                             _ptr(codes), codes.stride(0), _ptr(scales), scales.stride(0),
                             _ptr(ts), _stream(stream))
@@ -151,10 +216,20 @@ def dequantize(codes, scales, fmt: int = MXFP4, mode: int = PLAIN, tensor_scale=
                perm=None, hadamard: int = 0, out=None, stream=None):
     """Decode to a bf16 [rows, cols] tensor (optionally undoing a rotation)."""
     import torch
-    rows, half, ldc = _rows_ld(codes)
+    _check_fmt(fmt, mode)
+    dev = _device_of(codes)
+    rows, half, ldc = _mat(codes, "codes", torch.uint8, dev)
     cols = half * 2
+    _mat(scales, "scales", torch.uint8, dev, rows, cols // block_of(fmt))
+    if fmt == NVFP4:
+        if tensor_scale is None:
+            raise ValueError("NVFP4 needs its tensor_scale")
+        _vec(tensor_scale, "tensor_scale", torch.float32, 1, dev)
+    if perm is not None:
+        _vec(perm, "perm", torch.int32, cols, dev)
     if out is None:
-        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    _mat(out, "out", torch.bfloat16, dev, rows, cols)
     st = lib().fp4_dequantize(_ptr(codes), ldc, _ptr(scales), scales.stride(0),
                               _ptr(tensor_scale), rows, cols, fmt, block_of(fmt), mode,
                               _ptr(perm), hadamard, _ptr(out), out.stride(0), _stream(stream))
@@ -175,21 +250,28 @@ def rotate_quantize(x, perm=None, hadamard: Optional[int] = None, floor_rule: bo
     tensor_scale) for NVFP4.
     """
     import torch
-    rows, cols, ld = _rows_ld(x)
+    _check_fmt(fmt, mode)
+    dev = _device_of(x)
+    rows, cols, ld = _mat(x, "x", torch.bfloat16, dev)
     if hadamard is None:
         hadamard = block_of(fmt)
-    codes, scales = _outputs(rows, cols, fmt, x.device, codes, scales)
+    if perm is not None:
+        _vec(perm, "perm", torch.int32, cols, dev)
+    codes, scales = _outputs(rows, cols, fmt, dev, codes, scales)
     if want_rotated and rotated is None:
-        rotated = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+        rotated = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    if rotated is not None:
+        _mat(rotated, "rotated", torch.float32, dev, rows, cols)
     flags = FLAG_SCALE_OCP_FLOOR if floor_rule else 0
     ts = None
     if fmt == NVFP4:
         if scale_given is None:
             scale_given = tensor_scale is not None
         if scale_given:
+            if tensor_scale is None:
+                raise ValueError("scale_given needs a tensor_scale")
             flags |= FLAG_TENSOR_SCALE_GIVEN
-        ts = tensor_scale if tensor_scale is not None else torch.empty(
-            1, dtype=torch.float32, device=x.device)
+        ts = _tensor_scale(tensor_scale, dev)
     st = lib().fp4_rotate_quantize(_ptr(x), rows, cols, ld, _ptr(perm), hadamard, fmt,
                                    block_of(fmt), mode, flags, _ptr(codes), codes.stride(0),
                                    _ptr(scales), scales.stride(0), _ptr(ts), _ptr(rotated),
@@ -208,15 +290,33 @@ def gemm(a_codes, a_scales, b_codes, b_scales, k: Optional[int] = None, fmt: int
     quantizer returns them; NVFP4 also takes the two tensor scales and a mode
     per operand); fp32 [m, n] unless ``out_dtype`` is bfloat16."""
     import torch
-    m, ha, lda = _rows_ld(a_codes)
-    n, hb, ldb = _rows_ld(b_codes)
-    if k is None:
-        k = 2 * ha
+    if fmt not in (MXFP4, NVFP4):
+        raise ValueError(f"fp4_gemm takes MXFP4 or NVFP4, got format {fmt}")
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"out_dtype must be torch.float32 or torch.bfloat16, got {out_dtype}")
+    dev = _device_of(a_codes)
+    m, ha, lda = _mat(a_codes, "a_codes", torch.uint8, dev)
+    n, hb, ldb = _mat(b_codes, "b_codes", torch.uint8, dev)
+    if k is None:
+        k = 2 * ha
+    if k > 2 * ha or k > 2 * hb:
+        raise ValueError(f"k = {k} exceeds the code rows ({2 * ha}, {2 * hb} elements)")
+    blk = block_of(fmt)
+    _mat(a_scales, "a_scales", torch.uint8, dev, m, k // blk)
+    _mat(b_scales, "b_scales", torch.uint8, dev, n, k // blk)
+    if fmt == NVFP4:
+        if a_ts is None or b_ts is None:
+            raise ValueError("NVFP4 needs both tensor scales")
+        _vec(a_ts, "a_ts", torch.float32, 1, dev)
+        _vec(b_ts, "b_ts", torch.float32, 1, dev)
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a_codes.device)
-    od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    if out.dtype != out_dtype:
+        raise ValueError(f"out is {out.dtype}, out_dtype is {out_dtype}")
+    _mat(out, "out", out_dtype, dev, m, n)
+    od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
     st = lib().fp4_gemm(_ptr(a_codes), lda, _ptr(a_scales), a_scales.stride(0), _ptr(a_ts),
                         mode_a, _ptr(b_codes), ldb, _ptr(b_scales), b_scales.stride(0),
                         _ptr(b_ts), mode_b, m, n, k, fmt, od, _ptr(out), out.stride(0),
@@ -228,9 +328,11 @@ def gemm(a_codes, a_scales, b_codes, b_scales, k: Optional[int] = None, fmt: int
 def channel_energy(x, out=None, stream=None):
     """fp32 [cols]: sum over rows of x^2 per channel (fp64 accumulation)."""
     import torch
-    rows, cols, ld = _rows_ld(x)
+    dev = _device_of(x)
+    rows, cols, ld = _mat(x, "x", torch.bfloat16, dev)
     if out is None:
-        out = torch.empty(cols, dtype=torch.float32, device=x.device)
+        out = torch.empty(cols, dtype=torch.float32, device=dev)
+    _vec(out, "out", torch.float32, cols, dev)
     st = lib().fp4_channel_energy(_ptr(x), rows, cols, ld, _ptr(out), _stream(stream))
     _check("fp4_channel_energy", st)
     return out
@@ -253,10 +355,15 @@ def rotate_quantize_r(x, perm, rotation, want_rotated: bool = False, codes=None,
     R row-major) fused with MXFP4 quantize + pack. Returns (codes, scales,
     rotated fp32 [rows, cols] or None)."""
     import torch
-    rows, cols, ld = _rows_ld(x)
-    codes, scales = _outputs(rows, cols, MXFP4, x.device, codes, scales)
+    dev = _device_of(x)
+    rows, cols, ld = _mat(x, "x", torch.bfloat16, dev)
+    _vec(perm, "perm", torch.int32, cols, dev)
+    _vec(rotation, "rotation", torch.float32, 32 * 32, dev)
+    codes, scales = _outputs(rows, cols, MXFP4, dev, codes, scales)
     if want_rotated and rotated is None:
-        rotated = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+        rotated = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    if rotated is not None:
+        _mat(rotated, "rotated", torch.float32, dev, rows, cols)
     st = lib().fp4_rotate_quantize_r(_ptr(x), rows, cols, ld, _ptr(perm), _ptr(rotation),
                                      _ptr(codes), codes.stride(0), _ptr(scales),
                                      scales.stride(0), _ptr(rotated),
@@ -270,10 +377,15 @@ def dequantize_r(codes, scales, perm, rotation, out=None, stream=None):
     """Inverse of :func:`rotate_quantize_r`: decode, R^T per block, undo the
     permutation; bf16 [rows, cols]."""
     import torch
-    rows, half, ldc = _rows_ld(codes)
+    dev = _device_of(codes)
+    rows, half, ldc = _mat(codes, "codes", torch.uint8, dev)
     cols = half * 2
+    _mat(scales, "scales", torch.uint8, dev, rows, cols // 32)
+    _vec(perm, "perm", torch.int32, cols, dev)
+    _vec(rotation, "rotation", torch.float32, 32 * 32, dev)
     if out is None:
-        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    _mat(out, "out", torch.bfloat16, dev, rows, cols)
     st = lib().fp4_dequantize_r(_ptr(codes), ldc, _ptr(scales), scales.stride(0), rows, cols,
                                 _ptr(perm), _ptr(rotation), _ptr(out), out.stride(0),
                                 _stream(stream))
@@ -292,8 +404,10 @@ def calibrate_block_rotation(x, perm=None, iters: int = 60, angles: int = 32):
     """
     import torch
     xh = x.detach().to("cpu").contiguous()
-    rows, cols, ld = _rows_ld(xh)
+    rows, cols, ld = _mat(xh, "x", torch.bfloat16, None)
     ph = None if perm is None else perm.detach().to("cpu", torch.int32).contiguous()
+    if ph is not None and ph.numel() != cols:
+        raise ValueError(f"perm has {ph.numel()} entries, {cols} needed")
     R = torch.empty((32, 32), dtype=torch.float32)
     loss = (ctypes.c_double * 2)()
     st = lib().fp4_calibrate_block_rotation(_ptr(xh), rows, cols, ld, _ptr(ph), iters, angles,
@@ -329,10 +443,12 @@ def calibrate_macro_rotation(x, perm=None, block: int = 32, tol: float = 1e-6,
     ``x`` after ``perm`` (host code; x is copied to the host)."""
     import torch
     xh = x.detach().to("cpu").contiguous()
-    rows, cols, ld = _rows_ld(xh)
+    rows, cols, ld = _mat(xh, "x", torch.bfloat16, None)
     if max_rot is None:
         max_rot = 4 * (cols // block)
     ph = None if perm is None else perm.detach().to("cpu", torch.int32).contiguous()
+    if ph is not None and ph.numel() != cols:
+        raise ValueError(f"perm has {ph.numel()} entries, {cols} needed")
     pairs = torch.empty((max_rot, 2), dtype=torch.int32)
     cs = torch.empty((max_rot, 2), dtype=torch.float32)
     starts = torch.empty(max_rot + 1, dtype=torch.int32)
@@ -352,12 +468,16 @@ def apply_channel_rotation(x, macro: MacroRotation, perm=None, out=None, stream=
     """bf16 [rows, cols]: permutation, then the Givens layers of ``macro``
     (device tensors, see :meth:`MacroRotation.to`), on every row."""
     import torch
-    rows, cols, ld = _rows_ld(x)
-    for t in (perm, macro.pairs, macro.cs, macro.layer_start):
-        if t is not None and t.numel() and t.device != x.device:
-            raise ValueError("the permutation and the rotation tables must be on x's device")
+    dev = _device_of(x)
+    rows, cols, ld = _mat(x, "x", torch.bfloat16, dev)
+    if perm is not None:
+        _vec(perm, "perm", torch.int32, cols, dev)
+    _vec(macro.pairs, "pairs", torch.int32, 2 * macro.n_rot, dev)
+    _vec(macro.cs, "cs", torch.float32, 2 * macro.n_rot, dev)
+    _vec(macro.layer_start, "layer_start", torch.int32, macro.n_layers + 1, dev)
     if out is None:
-        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device)
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    _mat(out, "out", torch.bfloat16, dev, rows, cols)
     st = lib().fp4_apply_channel_rotation(_ptr(x), rows, cols, ld, _ptr(perm), _ptr(macro.pairs),
                                           _ptr(macro.cs), _ptr(macro.layer_start),
                                           macro.n_layers, macro.n_rot, _ptr(out),

@@ -75,15 +75,17 @@ __device__ __forceinline__ void unrotate_tile(u32x2_t c, uint32_t sbyte, const b
                                               const bf16x8_t& a1, u32x4_t& lo, u32x4_t& hi) {
   if constexpr (kInt && kHad) {
     // The block scale 2^(e - 2) is a power of two, so it can follow the
-    // Hadamard: k decodes to bf16 as is, and one multiply by 2^(e - 2) / sqrt(32)
-    // gives the same real value, hence the same rounding, as scaling first,
-    // while that factor is a normal float (byte >= 6) and the scaled sums
-    // (at most 256 * 2^(e - 2)) stay finite (byte <= 248). Other bytes (tiny
-    // or huge scales, NaN) decode scaled.
+    // Hadamard: k decodes to bf16 as is, the integer sums (at most 256 in
+    // magnitude) are exact, and one multiply by 2^(e - 2) / sqrt(32) rounds
+    // the exact real result once, as scaling first would, while that factor
+    // is a normal float (byte >= 6). It also keeps large scales right: scaled
+    // first, k 2^(e - 2) overflows bf16 for byte 254 (k = -8) and partial sums
+    // overflow fp32 from byte 249 on, where the transformed value may still
+    // be finite. Tiny scales (bytes 0..5) and NaN (255) decode scaled.
     // The MFMA combines lanes, so it runs on every lane outside the choice;
     // the two lanes of a block share its byte and so its choice.
     const uint32_t byte = sbyte & 0xFFu;
-    const bool fast = byte >= 6u && byte <= 248u;
+    const bool fast = byte >= 6u && byte != 0xFFu;
     u32x4_t dl, dh;
     if (fast) {
       dl = int4x8_decode_unit(c.x);

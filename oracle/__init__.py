@@ -17,11 +17,19 @@ than itself (the pins live in ``tests/test_oracle_*.py``):
   encoder pinned at every midpoint and one ulp either side.
 * ``e8m0_scale``: pinned exhaustively by the minimality property; decoder pinned
   to ``torch.float8_e8m0fnu``.
-* ``mx_quantize*``, ``nv_quantize``, ``dequantize*``: pinned by the nearest-grid
-  property, scale invariance, sign symmetry and idempotence.
-* ``nv_quantize_f32`` / ``nv_tensor_amax_f32``: pinned by an element-wise
-  restatement of the NVFP4 steps with an independent brute-force code search
-  on fp32 inputs, and by the nearest-grid and error-bound properties.
+* ``mx_quantize*``, ``dequantize*``: pinned by the nearest-grid property,
+  scale invariance, sign symmetry and idempotence.
+* ``nv_quantize``, ``nv_quantize_f32``, ``nvw_quantize``, ``nv_tensor_scale``,
+  ``nvw_tensor_scale``: every scale byte and code pinned to a restatement of
+  the per-block fp32 steps (tensor scale, RN(6 s_t), the block quotient, the
+  E4M3 / E3M3 code, s_eff, its reciprocal, the scaled elements, the nearest
+  code and the RaZeR choice) in exact rational arithmetic with its own fp32
+  rounding, E4M3 values from ``torch.float8_e4m3fn``, on random blocks and on
+  blocks that sit on every rounding edge of the sequence; those blocks are
+  shown to separate the plausible slips (x / s_eff, amax / 6 / s_t, an
+  unrounded s_eff), and each slip planted in a copy of the C source is
+  rejected. Also by error bounds, scale invariance and sign symmetry.
+* ``nv_tensor_amax_f32``: pinned to numpy's maximum of magnitudes.
 * ``int4_value`` / ``int4_nearest`` / ``mxint4_scale`` / ``mxint4_quantize*``:
   decoder pinned to numpy's two's complement sign extension; nearest search
   to ``np.rint`` (round half to even) and exact Fraction brute force; the
@@ -35,12 +43,12 @@ than itself (the pins live in ``tests/test_oracle_*.py``):
   enumeration.
 * ``rotate`` / ``unrotate_f64``: pinned to ``scipy.linalg.hadamard`` (orders 16
   and 32) and norm preservation.
-* ``e3m3_value`` / ``e3m3_encode`` / ``razer_block_set`` / ``nvw_quantize``:
-  decoder pinned to its closed form; encoder at every midpoint and one ulp
-  either side; the block choice to an exact Fraction arg-min and exhaustive
-  tiny-block enumeration; whole tensors by the block-choice consistency, sign
-  symmetry and the tensor-scale rule. The second special-value pair is not on
-  the pages: parity unpinned for that value (an offline search picks it).
+* ``e3m3_value`` / ``e3m3_encode`` / ``razer_block_set``: decoder pinned to
+  its closed form; encoder at every midpoint and one ulp either side; the
+  block choice to an exact Fraction arg-min and exhaustive tiny-block
+  enumeration (``nvw_quantize``: see the NVFP4 entry above). The second
+  special-value pair is not on the pages: parity unpinned for that value (an
+  offline search picks it).
 * ``rotate_r`` / ``unrotate_r_f64``: pinned by special matrices (identity,
   permutation, Sylvester-Hadamard from scipy, one Givens rotation in closed
   form), a random orthogonal matrix against numpy's product, and the inverse.

@@ -702,9 +702,6 @@ void orc_unrotate_f64(const double* y, int64_t rows, int64_t cols, int64_t ld_y,
   }
 }
 
-/* Per-channel energy E_c = sum over rows of x_rc^2, in double, row order.
- * It is the diagonal of the (uncentred) activation second-moment matrix whose
- * 32x32 diagonal blocks carry the block variances in [TORQ] sec. 2(a). */
 /* A general orthogonal rotation inside each 32-block ([TORQ] sec. 2(b): the
  * intra-block rotation is learned): y_b = R x'_b with R [32][32] row-major,
  * as a dense product in double rounded once to fp32; x' is the permuted row. */
@@ -791,6 +788,9 @@ void orc_apply_givens(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_
   }
 }
 
+/* Per-channel energy E_c = sum over rows of x_rc^2, in double, row order.
+ * It is the diagonal of the (uncentred) activation second-moment matrix whose
+ * 32x32 diagonal blocks carry the block variances in [TORQ] sec. 2(a). */
 void orc_channel_energy(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                         double* energy) {
   for (int64_t j = 0; j < cols; ++j) energy[j] = 0.0;

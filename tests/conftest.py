@@ -19,8 +19,18 @@ def pytest_configure(config):
 def orc():
     import oracle
     oracle.build(force=False)
-    oracle.set_threads(min(8, os.cpu_count() or 1))
+    oracle.set_threads(host_threads())
     return oracle
+
+
+def host_threads():
+    """Host threads for the oracle: the cores this process may run on,
+    at most OMP_NUM_THREADS when that is set."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n or 1)
 
 
 def read_golden(name):

@@ -48,6 +48,33 @@ def same_bf16(a, b):
 
 def check_rotated(y_gpu, y_orc, codes_gpu, scales_gpu, codes_orc, scales_orc):
     """Apply the rotated-path tolerance; returns a dict of counts."""
+    r = rotated_counts(y_gpu, y_orc, codes_gpu, scales_gpu, codes_orc, scales_orc)
+    n_bad = r["codes_differ"] + 32 * r["scales_differ"]
+    assert n_bad <= ROT_CODE_FRAC * r["total"], f"{n_bad} of {r['total']} codes differ"
+    return r
+
+
+def check_rotated_rows(y_gpu_dev, y_orc, codes_gpu, scales_gpu, codes_orc, scales_orc,
+                       chunk=1024):
+    """check_rotated over a whole tensor in chunks of rows (bounded host
+    memory): every element and block condition on every chunk, the fraction
+    of differing codes over the whole tensor. y_gpu_dev: device fp32."""
+    rows = y_orc.shape[0]
+    tot = {"codes_differ": 0, "scales_differ": 0, "total": 0}
+    for r0 in range(0, rows, chunk):
+        r1 = min(rows, r0 + chunk)
+        r = rotated_counts(y_gpu_dev[r0:r1].cpu().numpy(), y_orc[r0:r1], codes_gpu[r0:r1],
+                           scales_gpu[r0:r1], codes_orc[r0:r1], scales_orc[r0:r1])
+        for k in tot:
+            tot[k] += r[k]
+    n_bad = tot["codes_differ"] + 32 * tot["scales_differ"]
+    assert n_bad <= ROT_CODE_FRAC * tot["total"], f"{n_bad} of {tot['total']} codes differ"
+    return tot
+
+
+def rotated_counts(y_gpu, y_orc, codes_gpu, scales_gpu, codes_orc, scales_orc):
+    """The per-element and per-block conditions of the rotated-path tolerance
+    (asserted); returns the counts of differing codes and scale bytes."""
     rows, cols = y_orc.shape
     yo = y_orc.astype(np.float64).reshape(rows, cols // 32, 32)
     yg = y_gpu.astype(np.float64).reshape(rows, cols // 32, 32)
@@ -87,7 +114,4 @@ def check_rotated(y_gpu, y_orc, codes_gpu, scales_gpu, codes_orc, scales_orc):
         amax_e = (amax[..., None] * np.ones_like(mg))[sel]
         assert np.all(np.abs(np.abs(yo[sel]) - mid) <= ROT_REL * amax_e), \
             "a code differs away from a rounding midpoint"
-    total = rows * cols
-    n_bad = n_diff + 32 * int(bad_scale.sum())
-    assert n_bad <= ROT_CODE_FRAC * total, f"{n_bad} of {total} codes differ"
-    return {"codes_differ": n_diff, "scales_differ": int(bad_scale.sum()), "total": total}
+    return {"codes_differ": n_diff, "scales_differ": int(bad_scale.sum()), "total": rows * cols}

@@ -163,6 +163,41 @@ def test_binding_raises_without_gpu_work():
         fp4._check("fp4_quantize", -2)
 
 
+def test_binding_argument_checks():
+    """The binding rejects wrong dtypes, host tensors, short outputs and
+    unsupported output dtypes before any pointer reaches the library (the
+    device-side cases are in test_gpu_binding.py)."""
+    import torch
+    bf = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="bfloat16"):
+        fp4.quantize(bf.float())
+    with pytest.raises(ValueError, match="CUDA"):
+        fp4.quantize(bf)
+    with pytest.raises(ValueError, match="contiguous rows"):
+        fp4.quantize(bf.t())
+    with pytest.raises(ValueError, match="format"):
+        fp4.quantize(bf, fmt=7)
+    u8 = torch.zeros(4, 32, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="out_dtype"):
+        fp4.gemm(u8, u8, u8, u8, out_dtype=torch.float16)
+    with pytest.raises(ValueError, match="out_dtype"):
+        fp4.gemm(u8, u8, u8, u8, out=torch.zeros(4, 4, dtype=torch.float16))
+    with pytest.raises(ValueError, match="uint8"):
+        fp4.dequantize(u8.to(torch.int8), u8)
+    # the helpers on host tensors (device None)
+    with pytest.raises(ValueError, match="rows"):
+        fp4._mat(u8, "codes", torch.uint8, None, rows=5)
+    with pytest.raises(ValueError, match="columns"):
+        fp4._mat(u8, "codes", torch.uint8, None, rows=4, min_cols=33)
+    assert fp4._mat(u8, "codes", torch.uint8, None, rows=4, min_cols=32) == (4, 32, 32)
+    with pytest.raises(ValueError, match="elements"):
+        fp4._vec(torch.zeros(63, dtype=torch.int32), "perm", torch.int32, 64, None)
+    with pytest.raises(ValueError, match="int32"):
+        fp4._vec(torch.zeros(64, dtype=torch.int64), "perm", torch.int32, 64, None)
+    with pytest.raises(ValueError, match="contiguous"):
+        fp4._vec(torch.zeros(128, dtype=torch.int32)[::2], "perm", torch.int32, 64, None)
+
+
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_host_permutation_matches_oracle(L, orc, group):
     rng = np.random.default_rng(3 + group)

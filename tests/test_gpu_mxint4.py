@@ -202,23 +202,41 @@ def test_mxint4_dequant_unrotate(orc, rows, cols, kind, had):
 
 
 def test_mxint4_dequant_hadamard_all_scale_bytes(orc):
-    # Every finite scale byte 0..240 on its own block: the bytes 6..248 take
-    # the scale after the Hadamard, the others before it; both must agree with
-    # the oracle (random codes in [-7, 7], the grid the quantizer writes).
-    note("case: MXINT4 dequantize + H32, scale bytes 0..240, random codes")
+    # Every scale byte 0..255 on its own blocks, with every code -8..7 (the
+    # quantizer writes -7..7; -8 is a valid code): the bytes 6..254 take the
+    # scale after the Hadamard, 0..5 before it, 255 is NaN. Compared with the
+    # oracle's exact result rounded to bf16 (fp32, then bf16, nearest-even):
+    # where that overflows the GPU value must be the same infinity, elsewhere
+    # finite and within one bf16 rounding (plus fp32 rounding of tiny sums).
+    note("case: MXINT4 dequantize + H32, scale bytes 0..255, codes -8..7")
     rng = np.random.default_rng(241)
-    nbytes = 241
-    rows, cols = 4, 32 * nbytes
-    k = rng.integers(-7, 8, size=(rows, cols))
+    nbytes = 256
+    rows, cols = 6, 32 * nbytes
+    k = rng.integers(-8, 8, size=(rows, cols))
+    k[0, :] = np.where(np.arange(cols) % 32 == 0, -8, 0)  # a lone -8 per block
+    k[1, :] = 7      # constant blocks: the largest sums
     nib = (k & 0xF).astype(np.uint8)
     codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
     scales = np.tile(np.arange(nbytes, dtype=np.uint8), (rows, 1))
     d = fp4.dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
                        fp4.MXINT4, perm=None, hadamard=32)
     torch.cuda.synchronize()
-    want = orc.unrotate_f64(orc.dequantize_f64(codes, scales, 2), None, 32)
-    got = inputs.bf16_bits_to_f32(bf16_bits(d)).astype(np.float64)
-    blockmax = np.repeat(np.abs(want).reshape(rows, nbytes, 32).max(2), 32, axis=1)
-    tol = 2.0 ** -8 * np.abs(want) + 2.0 ** -20 * blockmax + 2.0 ** -133
-    err = np.abs(got - want)
-    assert np.all(err <= tol), f"max err at {np.unravel_index((err - tol).argmax(), err.shape)}"
+    fin = np.arange(cols) < 32 * 255
+    vals = np.ldexp(k.astype(np.float64), np.repeat(np.arange(nbytes), 32)[None, :] - 129)
+    want = orc.unrotate_f64(np.where(fin, vals, 0.0), None, 32)
+    gb = bf16_bits(d)
+    got = inputs.bf16_bits_to_f32(gb).astype(np.float64)
+    assert np.all(np.isnan(got[:, ~fin])), "scale byte 0xFF decodes to NaN"
+    with np.errstate(over="ignore"):
+        want_b = inputs.bf16_bits_to_f32(inputs.f64_to_bf16_bits(want)).astype(np.float64)
+    g, w, wb = got[:, fin], want[:, fin], want_b[:, fin]
+    inf = np.isinf(wb)
+    assert inf.sum() > 0 and (~inf).sum() > 0
+    assert np.array_equal(g[inf], wb[inf]), "an overflowing result is not the same infinity"
+    assert np.all(np.isfinite(g[~inf])), "a finite result came out infinite"
+    blockmax = np.repeat(np.abs(w).reshape(rows, 255, 32).max(2), 32, axis=1)
+    tol = 2.0 ** -8 * np.abs(w) + 2.0 ** -20 * np.where(np.isinf(blockmax), 0, blockmax) \
+        + 2.0 ** -133
+    err = np.abs(g - w)
+    ok = err[~inf] <= tol[~inf]
+    assert np.all(ok), f"{(~ok).sum()} results off by more than one bf16 rounding"

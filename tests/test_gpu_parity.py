@@ -10,7 +10,8 @@ torch = pytest.importorskip("torch")
 
 import block_scaled_fp4_absmax_amd as fp4
 from block_scaled_fp4_absmax_amd import inputs
-from parity_util import bf16_bits, check_rotated, note, same_bf16, to_dev, unpack
+from parity_util import (bf16_bits, check_rotated, check_rotated_rows, note, same_bf16,
+                         to_dev, unpack)
 
 pytestmark = pytest.mark.gpu
 
@@ -342,24 +343,30 @@ def test_dequant_unrotate_shapes(orc, rows, cols, kind, had):
 
 
 # ------------------------------------------------------- full-size configs --
-def _sample_rows(rows, k, seed):
-    return np.sort(np.random.default_rng(seed).choice(rows, size=min(k, rows), replace=False))
+# Whole tensors against the oracle. The rotated configurations are launched
+# twice: with the rotated values written out (for the value tolerance) and in
+# the configuration that bench.py times (codes and scales only); the two must
+# agree bit for bit, and their codes meet the rotated-path tolerance.
 
 
-def test_c3_full_size_sampled(orc):
-    note("case: C3 full 8192x8192 MXFP4 + H32, sampled rows vs oracle")
+@pytest.mark.timeout(900)
+def test_c3_full_size(orc):
+    note("case: C3 full 8192x8192 MXFP4 + H32, whole tensor vs oracle")
     x = inputs.gen_c3()
-    c, s, y = fp4.rotate_quantize(to_dev(x), None, 32, want_rotated=True)
+    xt = to_dev(x)
+    c, s, y = fp4.rotate_quantize(xt, None, 32, want_rotated=True)
+    c0, s0, _ = fp4.rotate_quantize(xt, None, 32)
     sync()
-    rows = _sample_rows(x.shape[0], 48, 7)
-    xs = np.ascontiguousarray(x[rows])
-    oc, os_, oy = orc.rotate_quantize(xs, None, 32)
-    ri = torch.from_numpy(rows).cuda()
-    check_rotated(y[ri].cpu().numpy(), oy, np_u8(c[ri]), np_u8(s[ri]), oc, os_)
+    assert torch.equal(c, c0) and torch.equal(s, s0)
+    del xt, c0, s0
+    oc, os_, oy = orc.rotate_quantize(x, None, 32)
+    r = check_rotated_rows(y, oy, np_u8(c), np_u8(s), oc, os_)
+    note(f"  {r}")
 
 
-def test_c4_full_size_sampled(orc):
-    note("case: C4 full 16384x8192 energy + permutation + H32, sampled rows vs oracle")
+@pytest.mark.timeout(900)
+def test_c4_full_size(orc):
+    note("case: C4 full 16384x8192 energy + permutation + H32, whole tensor vs oracle")
     x = inputs.gen_c4()
     xt = to_dev(x)
     e_gpu = fp4.channel_energy(xt)
@@ -367,28 +374,35 @@ def test_c4_full_size_sampled(orc):
     e_orc = orc.channel_energy(x)
     assert np.allclose(e_gpu.cpu().numpy(), e_orc, rtol=1e-6, atol=0)
     perm = fp4.build_permutation(e_gpu).numpy()
-    c, s, y = fp4.rotate_quantize(xt, torch.from_numpy(perm).cuda(), 32, want_rotated=True)
+    pt = torch.from_numpy(perm).cuda()
+    c, s, y = fp4.rotate_quantize(xt, pt, 32, want_rotated=True)
+    c0, s0, _ = fp4.rotate_quantize(xt, pt, 32)
     sync()
-    rows = _sample_rows(x.shape[0], 48, 8)
-    xs = np.ascontiguousarray(x[rows])
-    oc, os_, oy = orc.rotate_quantize(xs, perm, 32)
-    ri = torch.from_numpy(rows).cuda()
-    check_rotated(y[ri].cpu().numpy(), oy, np_u8(c[ri]), np_u8(s[ri]), oc, os_)
+    assert torch.equal(c, c0) and torch.equal(s, s0)
+    del xt, c0, s0
+    oc, os_, oy = orc.rotate_quantize(x, perm, 32)
+    r = check_rotated_rows(y, oy, np_u8(c), np_u8(s), oc, os_)
+    note(f"  {r}")
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("t", range(7))
-def test_c5_layer_sweep_sampled(orc, t):
+def test_c5_layer_sweep_full(orc, t):
+    """Every tensor of the layer bit for bit: codes, scale bytes, s_t and the
+    decoded bf16, with s_t computed (amax pass) and with s_t given."""
     name, R, C = inputs.C5_SHAPES[t]
-    note(f"case: C5 {name} {R}x{C} NVFP4+RaZeR round trip, sampled rows vs oracle")
+    note(f"case: C5 {name} {R}x{C} NVFP4+RaZeR round trip, whole tensor vs oracle")
     x = inputs.gen_c5(t)
-    c, s, ts = fp4.quantize(to_dev(x), fp4.NVFP4, fp4.RAZER)
+    xt = to_dev(x)
+    c, s, ts = fp4.quantize(xt, fp4.NVFP4, fp4.RAZER)
     d = fp4.dequantize(c, s, fp4.NVFP4, fp4.RAZER, ts)
+    c2, s2, _ = fp4.quantize(xt, fp4.NVFP4, fp4.RAZER, tensor_scale=ts.clone())
     sync()
+    del xt
     ots = orc.nv_tensor_scale(orc.nv_tensor_amax(x))
     assert float(ts.cpu()[0]) == ots
-    rows = _sample_rows(R, 32, t)
-    xs = np.ascontiguousarray(x[rows])
-    oc, os_, _ = orc.nv_quantize(xs, True, ots)
-    ri = torch.from_numpy(rows).cuda()
-    assert np.array_equal(np_u8(c[ri]), oc) and np.array_equal(np_u8(s[ri]), os_)
-    assert np.array_equal(bf16_bits(d[ri]), orc.dequantize(oc, os_, 1, True, ots))
+    oc, os_, _ = orc.nv_quantize(x, True, ots)
+    assert np.array_equal(np_u8(s), os_) and np.array_equal(np_u8(c), oc)
+    assert np.array_equal(np_u8(s2), os_) and np.array_equal(np_u8(c2), oc)
+    del c2, s2
+    assert np.array_equal(bf16_bits(d), orc.dequantize(oc, os_, 1, True, ots))
