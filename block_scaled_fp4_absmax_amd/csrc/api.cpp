@@ -102,7 +102,7 @@ int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int6
   if ((hadamard || perm) && cols % 32 != 0) return FP4_ERR_SHAPE;  // 32-element segments
   if (ld_out < cols || ld_codes < cols / 2 || ld_scales < cols / block) return FP4_ERR_SHAPE;
   if (rows > 0 && cols > 0 && rows * cols / 8 >= (int64_t)1 << 31) return FP4_ERR_UNSUPPORTED;
-  if (perm && cols > fp4::kMaxPermCols) return FP4_ERR_UNSUPPORTED;
+  if (perm && cols > fp4::kMaxUnpermCols) return FP4_ERR_UNSUPPORTED;
   if (format == FP4_NVFP4 && !tensor_scale) return FP4_ERR_NULL;
   if (rows == 0 || cols == 0) return FP4_OK;
   if (!codes || !scales || !out_bf16) return FP4_ERR_NULL;
@@ -181,7 +181,7 @@ int fp4_dequantize_r(const void* codes, int64_t ld_codes, const void* scales, in
   if (rows < 0 || cols < 0 || cols % 32 != 0) return FP4_ERR_SHAPE;
   if (ld_out < cols || ld_codes < cols / 2 || ld_scales < cols / 32) return FP4_ERR_SHAPE;
   if (rows > 0 && cols > 0 && rows * cols / 8 >= (int64_t)1 << 31) return FP4_ERR_UNSUPPORTED;
-  if (cols > fp4::kMaxPermCols) return FP4_ERR_UNSUPPORTED;
+  if (cols > fp4::kMaxUnpermCols) return FP4_ERR_UNSUPPORTED;
   if (rows == 0 || cols == 0) return FP4_OK;
   if (!codes || !scales || !out_bf16 || !perm || !rotation) return FP4_ERR_NULL;
   if (!aligned(out_bf16, 16) || ld_out % 8 != 0) return FP4_ERR_ALIGN;
@@ -200,7 +200,7 @@ int fp4_apply_channel_rotation(const void* x_bf16, int64_t rows, int64_t cols, i
                                void* out_bf16, int64_t ld_out, void* stream) {
   if (rows < 0 || cols < 0 || cols % 8 != 0 || ld_x < cols || ld_out < cols) return FP4_ERR_SHAPE;
   if (n_layers < 0 || n_rot < 0) return FP4_ERR_SHAPE;
-  if (cols > fp4::kMaxPermCols || rows >= ((int64_t)1 << 31)) return FP4_ERR_UNSUPPORTED;
+  if (cols > fp4::kMaxUnpermCols || rows >= ((int64_t)1 << 31)) return FP4_ERR_UNSUPPORTED;
   if (rows == 0 || cols == 0) return FP4_OK;
   if (!x_bf16 || !out_bf16) return FP4_ERR_NULL;
   if (n_layers > 0 && !layer_start) return FP4_ERR_NULL;

@@ -6,9 +6,12 @@
 
 namespace fp4 {
 
-// Largest row length that the permuting kernels stage in LDS (row + indices,
-// 4 bytes per column).
-constexpr int64_t kMaxPermCols = 16384;
+// Largest row length that the forward permuting kernels stage in LDS (their
+// gather offsets are 16-bit byte offsets into the row), and that the inverse
+// permutation and the Givens-layer kernels stage (row + indices, 4 bytes per
+// column).
+constexpr int64_t kMaxPermCols = 32768;
+constexpr int64_t kMaxUnpermCols = 16384;
 // Work-groups of the row-at-a-time (LDS-staged) kernels.
 #ifndef FP4_PERM_GRID
 #define FP4_PERM_GRID 1024

@@ -42,6 +42,7 @@
 #define FP4_HADAMARD_MFMA 1
 #endif
 
+
 namespace fp4 {
 
 constexpr bool kUseMfma = FP4_HADAMARD_MFMA != 0;
@@ -262,6 +263,67 @@ struct PermCtx {
   float* amax;                         // NVFP4 pre-pass: the lane's running maximum
 };
 
+// Gather, transform, quantize and store row r, staged in LDS at buf + kOff
+// (G: the gather run length). Per tile the lane issues one 8-byte code store
+// and one scale-byte store (plus four 16-byte stores of the rotated values
+// with kRot), whether or not it holds a block: the count of memory
+// operations per row is fixed.
+template <int G, uint32_t kOff, int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot, class Ctx>
+__device__ __forceinline__ void perm_row(const Ctx& c, const uint8_t* buf, int32_t r) {
+    // Cache policy of the code stores, measured on MI355X at 16384 x 8192:
+    // plain write-back stores ran the MX formats 6% faster than nontemporal
+    // ones (55.9 against 59.8 us), and NVFP4 2% slower (65.2 against 63.7).
+    constexpr int kCodeAux = kFmt == kFmtNv ? kNt : 0;
+    const RotGeom& g = c.g;
+    const RowRsrc q = row_rsrc<kRot>(c.x, c.codes, c.scales, c.rot, r, g);
+    const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < kTpw; ++i) {
+      const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kWaves * i) + (int32_t)n;
+      const bool ok = b < g.bpr;
+      u32x4_t lo, hi;
+      gather_tile<G, kOff>(buf, c.off[i], lo, hi);
+      float y[16];
+      if (kHad) {
+        if constexpr (kFmt == kFmtMxMat)
+          matrix_mfma(c.m, lo, hi, y);
+        else
+          hadamard_mfma<kFmt == kFmtMx || kFmt == kFmtMxInt ? 32 : 16>(c.a0, c.a1, lo, hi, y);
+      } else {
+        widen8(lo, y);
+        widen8(hi, y + 8);
+      }
+      if constexpr (kFmt == kFmtNvAmax) {
+        if (ok) *c.amax = __builtin_fmaxf(*c.amax, absmax16f(y));
+      } else {
+        uint32_t w0, w1, byte, so;
+        if constexpr (kFmt == kFmtMx || kFmt == kFmtMxInt || kFmt == kFmtMxMat) {
+          // kOpt: OCP floor rule
+          if constexpr (kFmt != kFmtMxInt)
+            mx_quant16_pair<kOpt, kHad>(y, w0, w1, byte);
+          else
+            mxint_quant16_pair<kOpt, kHad>(y, w0, w1, byte);
+          so = ok && h == 0 ? (uint32_t)b : kOob;
+        } else {  // kOpt: RaZeR; lane h holds block 2 b + h
+          nv_quant16<kOpt>(y, c.ns, c.rcp_tab, w0, w1, byte);
+          so = ok ? 2u * b + h : kOob;
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w0, w1}, q.c,
+                                              ok ? 16u * b + 8u * h : kOob, 0, kCodeAux);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, q.s, so, 0, 0);
+        if (kRot) {
+          const uint32_t o = ok ? 4u * (32u * b + 16u * h) : kOob;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t,
+                                   f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]}),
+                q.rot, o == kOob ? kOob : o + 16u * k, 0, kNt);
+        }
+      }
+    }
+}
+
 // Rows r0 + k G (G = grid size), k < K. Row k is gathered from LDS buffer
 // k % 2; during its step, rows k + 1 .. k + kAhead are in flight in register
 // buffers (row j in buffer j % kAhead). A step stages row k + 1 into the other
@@ -289,53 +351,7 @@ struct PermRows {
     load_row<kCpl>(row_rsrc<kRot>(c.x, c.codes, c.scales, c.rot,
                                   r + (1 + kAhead) * (int32_t)gridDim.x, g).x,
                    cpr, pre);
-    const RowRsrc q = row_rsrc<kRot>(c.x, c.codes, c.scales, c.rot, r, g);
-    const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < kTpw; ++i) {
-      const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kWaves * i) + (int32_t)n;
-      const bool ok = b < g.bpr;
-      u32x4_t lo, hi;
-      gather_tile<G, kBuf * kBufBytes>(c.sbuf, c.off[i], lo, hi);
-      float y[16];
-      if (kHad) {
-        if constexpr (kFmt == kFmtMxMat)
-          matrix_mfma(c.m, lo, hi, y);
-        else
-          hadamard_mfma<kFmt == kFmtMx || kFmt == kFmtMxInt ? 32 : 16>(c.a0, c.a1, lo, hi, y);
-      } else {
-        widen8(lo, y);
-        widen8(hi, y + 8);
-      }
-      if constexpr (kFmt == kFmtNvAmax) {
-        if (ok) *c.amax = __builtin_fmaxf(*c.amax, absmax16f(y));
-      } else {
-        uint32_t w0, w1, byte, so;
-        if constexpr (kFmt == kFmtMx || kFmt == kFmtMxInt || kFmt == kFmtMxMat) {
-          // kOpt: OCP floor rule
-          if constexpr (kFmt != kFmtMxInt)
-            mx_quant16_pair<kOpt, kHad>(y, w0, w1, byte);
-          else
-            mxint_quant16_pair<kOpt, kHad>(y, w0, w1, byte);
-          so = ok && h == 0 ? (uint32_t)b : kOob;
-        } else {  // kOpt: RaZeR; lane h holds block 2 b + h
-          nv_quant16<kOpt>(y, c.ns, c.rcp_tab, w0, w1, byte);
-          so = ok ? 2u * b + h : kOob;
-        }
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w0, w1}, q.c,
-                                              ok ? 16u * b + 8u * h : kOob, 0, kNt);
-        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, q.s, so, 0, 0);
-        if (kRot) {
-          const uint32_t o = ok ? 4u * (32u * b + 16u * h) : kOob;
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(u32x4_t,
-                                   f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]}),
-                q.rot, o == kOob ? kOob : o + 16u * k, 0, kNt);
-        }
-      }
-    }
+    perm_row<G, kBuf * kBufBytes, kTpw, kFmt, kHad, kOpt, kRot>(c, c.sbuf, r);
     __syncthreads();
   }
 
@@ -375,7 +391,7 @@ struct PermRows {
 // CU slower. A second row of look-ahead gained about 1%, more none.
 template <int kTpw>
 constexpr int perm_wgs_per_cu() {
-  return kTpw == 1 ? 4 : 2;
+  return kTpw == 1 ? 4 : kTpw <= 4 ? 2 : 1;
 }
 template <int kTpw>
 constexpr int perm_ahead() {
@@ -383,7 +399,7 @@ constexpr int perm_ahead() {
 }
 template <int kTpw>
 constexpr int perm_waves_cap() {
-  return kTpw == 1 ? 4 : 2;
+  return kTpw == 1 ? 4 : kTpw <= 4 ? 2 : 1;
 }
 
 #ifndef FP4_PERM_WAVES
@@ -452,6 +468,185 @@ __global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void rotq_perm_kernel(
   if constexpr (kFmt == kFmtNvAmax) {
     const float m = block_max(amax, rcp_tab);
     if (threadIdx.x == 0) *amax_partial_slot(codes, blockIdx.x, g) = __float_as_uint(m);
+  }
+}
+
+// ========= permuting kernel, rows staged by direct-to-LDS loads ============
+// The same row computation as rotq_perm_kernel, with the rows brought into
+// LDS by buffer_load_dwordx4 ... lds (gfx950), which writes each lane's 16
+// bytes straight into LDS: no registers hold rows in flight and no LDS stores
+// copy them in, so a work-group keeps a ring of kNB row buffers and kNB - 1
+// rows in flight. Step k (row r0 + k G, G the grid size):
+//   wait until this wave's loads of row k are done (vmcnt), barrier (every
+//   wave's share of row k is in LDS, and every wave has finished reading the
+//   buffer of row k - 1), issue the loads of row k + kNB - 1 into that freed
+//   buffer, then gather, transform, quantize and store row k.
+// Each step issues a fixed number of memory operations in a fixed order
+// (kCpl loads, then kS stores; a scheduling barrier keeps them apart), so the
+// loads of row k are exactly those with more than (kNB - 2) kCpl + (steps
+// since) kS operations after them. The barrier is a bare s_barrier: a
+// work-group fence would wait for every load in flight.
+// The ring buffers are separate LDS objects so that the compiler sees which
+// buffer each read touches and does not wait for loads into the others.
+template <int kTpw, int kSlot>
+__device__ __forceinline__ uint8_t* ring_buf() {
+  __shared__ __attribute__((aligned(16))) uint8_t b[8192 * kTpw];
+  return b;
+}
+
+// s_waitcnt vmcnt(n) (n < 64) leaving the other counters alone (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int m = n < 63 ? n : 63;
+  __builtin_amdgcn_s_waitcnt((m & 0xF) | ((m >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait for this wave's LDS operations, then meet the work-group, with no wait
+// on vector memory (compiler-only fences keep memory accesses on their side).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// This wave's share of a row: operation u moves chunk c = u kThreads + 64 w +
+// lane (16 bytes) of the row to buf + 16 c; chunks past the row read nothing.
+template <int kCpl>
+__device__ __forceinline__ void dma_row(rsrc_t src, uint8_t* buf, int32_t cpr) {
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int u = 0; u < kCpl; ++u) {
+    const int32_t c = threadIdx.x + u * kThreads;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src, (__attribute__((address_space(3))) void*)(buf + 16 * (u * kThreads + 64 * w)), 16,
+        c < cpr ? 16u * (uint32_t)c : kOob, 0, 0, kNt);
+  }
+}
+
+// Rows of a work-group: row(k) = g + k G for k < count (g its index, G the
+// grid size), past the end otherwise, so that all work-groups work on one
+// window of consecutive rows at a time (measured on MI355X: a contiguous range
+// of rows per work-group ran 8-12% slower); every work-group runs `steps`
+// steps, the largest count.
+struct RowMap {
+  int32_t base, stride, count, steps;
+  __device__ __forceinline__ int32_t row(int32_t k) const {
+    return k < count ? base + k * stride : 0x7FFFFFFF;
+  }
+};
+
+__device__ __forceinline__ RowMap row_map(int32_t rows) {
+  const int32_t G_ = gridDim.x, g = blockIdx.x;
+  return RowMap{g, G_, (rows - g + G_ - 1) / G_, (rows + G_ - 1) / G_};
+}
+
+template <int G, int kTpw, int kNB, int kFmt, bool kHad, bool kOpt, bool kRot>
+struct DmaRows {
+  using Ctx = PermCtx<kTpw, 1>;
+  static constexpr int kCpl = 2 * kTpw;
+  // vector-memory stores per step
+  static constexpr int kS = kFmt == kFmtNvAmax ? 0 : kTpw * (2 + (kRot ? 4 : 0));
+
+  // step k with kSt = k mod kNB; kFirst: the first kNB steps (fewer stores
+  // issued since the prologue's loads)
+  template <int kSt, bool kFirst>
+  static __device__ __forceinline__ void step(const Ctx& c, const RowMap& m, int32_t k) {
+    constexpr int kSince = kFirst ? kSt : kNB - 1;
+    wait_vmcnt<(kNB - 2) * kCpl + kSince * kS>();
+    lds_barrier();
+    dma_row<kCpl>(row_rsrc<false>(c.x, c.codes, c.scales, c.rot, m.row(k + kNB - 1), c.g).x,
+                  ring_buf<kTpw, (kSt + kNB - 1) % kNB>(), c.g.cols / 8);
+    __builtin_amdgcn_sched_barrier(0);
+    perm_row<G, 0, kTpw, kFmt, kHad, kOpt, kRot>(c, ring_buf<kTpw, kSt>(), m.row(k));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  template <bool kFirst, int... us>
+  static __device__ __forceinline__ void group(const Ctx& c, const RowMap& m, int32_t k,
+                                               std::integer_sequence<int, us...>) {
+    (step<us, kFirst>(c, m, k + us), ...);
+  }
+
+  // Whole groups of kNB steps; rows past the end run with empty resources.
+  static __device__ __forceinline__ void run(const Ctx& c, const RowMap& m) {
+    group<true>(c, m, 0, std::make_integer_sequence<int, kNB>{});
+    for (int32_t k = kNB; k < m.steps; k += kNB)
+      group<false>(c, m, k, std::make_integer_sequence<int, kNB>{});
+    wait_vmcnt<0>();  // no load into LDS outlives the work-group
+  }
+};
+
+template <int kTpw, int kNB, int j>
+__device__ __forceinline__ void dma_prologue(const uint16_t* x, const RotGeom& g,
+                                             const RowMap& m) {
+  if constexpr (j < kNB - 1) {
+    dma_row<2 * kTpw>(row_rsrc<false>(x, nullptr, nullptr, nullptr, m.row(j), g).x,
+                      ring_buf<kTpw, j>(), g.cols / 8);
+    dma_prologue<kTpw, kNB, j + 1>(x, g, m);
+  }
+}
+
+
+template <int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot>
+__global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void rotq_perm_dma_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, const float* __restrict__ ts, float* __restrict__ rot,
+    RotGeom g) {
+  // as many row buffers as fit in 152 KB of LDS, at most four
+  constexpr int kNBmax = (152 * 1024) / (8192 * kTpw);
+  constexpr int kNB = kNBmax < 4 ? kNBmax : 4;
+  static_assert(kNB >= 2, "two row buffers at least");
+  __shared__ float rcp_tab[128];
+  __shared__ uint32_t vote[kWaves];
+  // perm entries first, then the first kNB - 1 rows, so the row loads are in
+  // flight while the entries are unpacked
+  i32x4_t v[kTpw][4];
+  load_lane_perm<kTpw>(perm, g, v);
+  const RowMap rm = row_map(g.rows);
+  dma_prologue<kTpw, kNB, 0>(x, g, rm);
+  NvScale ns{1.0f, 1.0f, true};
+  if constexpr (kFmt == kFmtNv) {
+    const float s_t = *ts;
+    ns = nv_scale_setup(s_t);
+    nv_rcp_table(rcp_tab, s_t);
+  }
+  uint32_t off[kTpw][8];
+  const int lr = pack_lane_perm<kTpw>(v, g, off);
+  bf16x8_t a0, a1, m[3][2];
+  if constexpr (kFmt == kFmtMxMat)
+    matrix_operands(ts, false, m);
+  else
+    hadamard_operands<kFmt == kFmtMx || kFmt == kFmtMxInt ? 32 : 16>(a0, a1);
+  // run length agreed by the whole work-group (the barrier also publishes
+  // the reciprocal table); bit i of a wave's vote: every lane has runs >= 2^i
+  const uint32_t mine = (lr >= 2 ? 1u : 0u) | (lr >= 4 ? 2u : 0u) | (lr >= 8 ? 4u : 0u);
+  uint32_t wv = mine;
+#pragma unroll
+  for (int off_ = 32; off_ >= 1; off_ >>= 1) wv &= (uint32_t)__shfl_xor((int)wv, off_, 64);
+  if ((threadIdx.x & 63) == 0) vote[threadIdx.x >> 6] = wv;
+  lds_barrier();
+  uint32_t all = vote[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) all &= vote[i];
+  const int run = (all & 4u) ? 8 : (all & 2u) ? 4 : (all & 1u) ? 2 : 1;
+  float amax = 0.0f;
+  PermCtx<kTpw, 1> c{x, nullptr, off, a0, a1, {{m[0][0], m[0][1]}, {m[1][0], m[1][1]},
+                                               {m[2][0], m[2][1]}},
+                     codes, scales, rot, g, nullptr, ns, rcp_tab, &amax};
+  if (run == 8)
+    DmaRows<8, kTpw, kNB, kFmt, kHad, kOpt, kRot>::run(c, rm);
+  else if (run == 4)
+    DmaRows<4, kTpw, kNB, kFmt, kHad, kOpt, kRot>::run(c, rm);
+  else if (run == 2)
+    DmaRows<2, kTpw, kNB, kFmt, kHad, kOpt, kRot>::run(c, rm);
+  else
+    DmaRows<1, kTpw, kNB, kFmt, kHad, kOpt, kRot>::run(c, rm);
+  if constexpr (kFmt == kFmtNvAmax) {
+    __syncthreads();  // vote[] is reused by block_max
+    const float mx = block_max(amax, reinterpret_cast<float*>(vote));
+    if (threadIdx.x == 0) *amax_partial_slot(codes, blockIdx.x, g) = __float_as_uint(mx);
   }
 }
 
@@ -551,8 +746,13 @@ static int perm_launch(const Shape& s, const int32_t* perm, const uint16_t* x, u
   constexpr size_t kStatic = 2 * 8192 * kTpw;
   const size_t share = (size_t)ci.lds / kWgs;  // > lds / (kWgs + 1), so kWgs fit, not more
   const size_t pad = share > kStatic + 1024 ? share - kStatic - 1024 : 0;
-  hipLaunchKernelGGL((rotq_perm_kernel<kTpw, kFmt, kHad, kOpt, kRot>), dim3(grid), dim3(kThreads),
-                     pad, st, x, perm, c, sc, ts, rot, g);
+  if constexpr (kTpw > 4) {  // wide rows: staged by direct-to-LDS loads, one work-group per CU
+    hipLaunchKernelGGL((rotq_perm_dma_kernel<kTpw, kFmt, kHad, kOpt, kRot>), dim3(grid),
+                       dim3(kThreads), 0, st, x, perm, c, sc, ts, rot, g);
+  } else {
+    hipLaunchKernelGGL((rotq_perm_kernel<kTpw, kFmt, kHad, kOpt, kRot>), dim3(grid),
+                       dim3(kThreads), pad, st, x, perm, c, sc, ts, rot, g);
+  }
   return grid;
 }
 
@@ -566,7 +766,10 @@ static int perm_dispatch(const Shape& s, const int32_t* perm, const uint16_t* x,
   if (tpw <= 1) return perm_launch<1, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
   if (tpw <= 2) return perm_launch<2, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
   if (tpw <= 3) return perm_launch<3, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
-  return perm_launch<4, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
+  if (tpw <= 4) return perm_launch<4, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
+  if (tpw <= 6) return perm_launch<6, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
+  if (tpw <= 7) return perm_launch<7, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
+  return perm_launch<8, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
 }
 
 template <bool kHad, bool kFloor, bool kRot, bool kInt>

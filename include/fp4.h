@@ -186,8 +186,10 @@ int fp4_dequantize(const void* codes, int64_t ld_codes, const void* scales, int6
  *
  *  perm         NULL (identity) or device int32[cols], a permutation of
  *               0..cols-1 (entries are clamped to cols-1); requires
- *               cols <= 16384. A permutation made of aligned runs of 2, 4 or
- *               8 consecutive channels (fp4_build_permutation with group > 1)
+ *               cols <= 32768 (rows up to 16384 wide are staged through
+ *               registers, wider ones straight into LDS, one work-group per
+ *               CU). A permutation made of aligned runs of 2, 4 or 8
+ *               consecutive channels (fp4_build_permutation with group > 1)
  *               is detected and gathered with 4-, 8- or 16-byte LDS reads
  *  hadamard     the block size (32 MXFP4/MXINT4, 16 NVFP4) or 0 (none)
  *  format       FP4_MXFP4, FP4_MXINT4, or FP4_NVFP4 with mode FP4_PLAIN or
@@ -215,7 +217,7 @@ int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t 
  *
  *  perm         device int32[cols], a permutation of 0..cols-1 (entries
  *               clamped to cols-1); required: pass the identity for none;
- *               cols <= 16384
+ *               cols <= 32768
  *  rotation     device fp32[32 * 32], R row-major (R[i][j] at 32 i + j),
  *               4-byte aligned; read once per work-group. Any matrix is
  *               accepted; fp4_dequantize_r inverts it only if orthogonal

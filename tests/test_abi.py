@@ -90,8 +90,8 @@ def test_rotate_and_dequant_validation(L):
     assert R(FAKE, 4, 64, 64, None, 32, 1, 16, 0, 0, FAKE, 32, FAKE, 4, TS, None, 0, None) == -4
     # NVFP4 rotation works on 32-element segments: cols % 32
     assert R(FAKE, 4, 48, 48, None, 16, 1, 16, 1, 0, FAKE, 24, FAKE, 3, TS, None, 0, None) == -2
-    assert R(FAKE, 4, 32768, 32768, FAKE, 32, 0, 32, 0, 0, FAKE, 16384, FAKE, 1024, None, None,
-             0, None) == -4  # permutation wider than the LDS row buffer
+    assert R(FAKE, 4, 32800, 32800, FAKE, 32, 0, 32, 0, 0, FAKE, 16400, FAKE, 1025, None, None,
+             0, None) == -4  # permutation wider than the LDS row buffer (32768)
     assert R(FAKE, 4, 64, 64, None, 32, 0, 32, 0, 0, FAKE, 32, FAKE, 2, None, FAKE, 32,
              None) == -2
     assert R(FAKE, 4, 64, 64, None, 32, 0, 32, 0, 0, FAKE, 32, FAKE, 2, None, FAKE + 4, 64,
@@ -131,7 +131,7 @@ def test_rotate_and_dequant_validation(L):
     assert Q(FAKE, 4, 64, 64, FAKE, None, FAKE, 32, FAKE, 2, None, 0, None) == -1  # matrix needed
     assert Q(FAKE, 4, 64, 64, FAKE, FAKE + 2, FAKE, 32, FAKE, 2, None, 0, None) == -3
     assert Q(FAKE, 4, 64, 64, FAKE, FAKE, FAKE, 32, FAKE, 2, FAKE, 32, None) == -2  # ld_rot
-    assert Q(FAKE, 4, 32768, 32768, FAKE, FAKE, FAKE, 16384, FAKE, 1024, None, 0, None) == -4
+    assert Q(FAKE, 4, 32800, 32800, FAKE, FAKE, FAKE, 16400, FAKE, 1025, None, 0, None) == -4
     assert Q(None, 0, 64, 64, None, None, None, 32, None, 2, None, 0, None) == 0
     # dequantize_r(codes, ldc, scales, lds, rows, cols, perm, rotation, out, ldo, stream)
     U = L.fp4_dequantize_r

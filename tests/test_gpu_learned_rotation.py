@@ -98,6 +98,17 @@ def test_learned_rotation_shapes(orc, rows, cols):
     _unrotate_check(orc, c, s, perm, R, pt, rt)
 
 
+@pytest.mark.parametrize("rows,cols", [(5, 28672), (300, 24576)])
+def test_learned_rotation_wide_rows(orc, rows, cols):
+    """Rows wider than 16384 (forward only: the inverse permutation is
+    limited to 16384 columns)."""
+    note(f"case: learned block matrix, wide rows {rows}x{cols}")
+    x = inputs.gen_c3(rows=rows, cols=cols)
+    perm = np.random.default_rng(cols + rows).permutation(cols).astype(np.int32)
+    r, _ = _case(orc, x, perm, _random_rotation(cols))
+    note(f"  {r}")
+
+
 @pytest.mark.parametrize("kind", [2, 8])
 def test_learned_rotation_channel_runs(orc, learned, kind):
     note(f"case: learned R with a permutation of {kind}-channel runs, 300x8192")

@@ -162,7 +162,7 @@ def test_mxint4_grouped_permutation(orc, group):
 
 @pytest.mark.parametrize("rows,cols,use_perm", [
     (3, 96, True), (37, 2080, True), (5, 16384, True), (6, 8224, True), (1537, 8192, True),
-    (2500, 1024, True), (37, 2080, False), (1, 32, False)])
+    (2500, 1024, True), (37, 2080, False), (1, 32, False), (9, 28672, True)])
 def test_mxint4_rotation_ragged(orc, rows, cols, use_perm):
     note(f"case: MXINT4 rotate ragged {rows}x{cols} perm={use_perm} H32")
     x = inputs.gen_c3(rows=rows, cols=cols)

@@ -143,7 +143,8 @@ def test_nv_rotation_grouped_permutation(orc, group):
 # unequal row counts per work-group (1537, 2500), both kernels (perm / none)
 @pytest.mark.parametrize("rows,cols,use_perm", [
     (3, 96, True), (37, 2080, True), (5, 16384, True), (6, 8224, True), (4, 12288, True),
-    (1537, 8192, True), (2500, 1024, True), (37, 2080, False), (1, 32, False), (3, 96, False)])
+    (1537, 8192, True), (2500, 1024, True), (37, 2080, False), (1, 32, False), (3, 96, False),
+    (7, 28672, True), (300, 20480, True), (2, 32768, True)])
 def test_nv_rotation_ragged(orc, rows, cols, use_perm):
     note(f"case: NVFP4 rotate ragged {rows}x{cols} perm={use_perm} H16 RaZeR")
     x = inputs.gen_c3(rows=rows, cols=cols)

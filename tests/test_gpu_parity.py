@@ -293,6 +293,43 @@ def test_rotate_ragged(orc, rows, cols):
     _rot_case(orc, x, perm8, 32)
 
 
+# rows wider than 16384 take the kernel that stages rows straight into LDS:
+# 6, 7 and 8 MFMA tiles per wave (16416 and 20480 run as 6, with idle tiles),
+# one work-group per CU, row counts below, at and above the grid
+@pytest.mark.parametrize("rows,cols", [(3, 16416), (37, 20480), (5, 24576), (6, 28672),
+                                       (2, 32768), (300, 28672), (1100, 28704)])
+def test_rotate_wide_rows(orc, rows, cols):
+    note(f"case: rotate wide rows {rows}x{cols}")
+    x = inputs.gen_c4(rows=rows, cols=cols)
+    perm = np.random.default_rng(cols + rows).permutation(cols).astype(np.int32)
+    r = _rot_case(orc, x, perm, 32)
+    note(f"  {r}")
+    runs = np.random.default_rng(cols + 1).permutation(cols // 8).astype(np.int32)
+    perm8 = (8 * runs[:, None] + np.arange(8)[None, :]).reshape(-1).astype(np.int32)
+    _rot_case(orc, x, perm8, 32)
+    _rot_case(orc, x, perm, 0)
+
+
+@pytest.mark.timeout(900)
+def test_rotate_down_projection_input_full(orc):
+    """The two-level rotation on activations entering the 28672-wide down
+    projection: 8192 tokens x 28672 channels with log-normal block variances,
+    permutation from the tensor's own channel energies, whole tensor."""
+    note("case: permutation + H32 + MXFP4, 8192x28672 activations, whole tensor vs oracle")
+    x = inputs.gen_c4(rows=8192, cols=28672)
+    xt = to_dev(x)
+    perm = fp4.build_permutation(fp4.channel_energy(xt)).numpy()
+    pt = torch.from_numpy(perm).cuda()
+    c, s, y = fp4.rotate_quantize(xt, pt, 32, want_rotated=True)
+    c0, s0, _ = fp4.rotate_quantize(xt, pt, 32)
+    sync()
+    assert torch.equal(c, c0) and torch.equal(s, s0)
+    del xt, c0, s0
+    oc, os_, oy = orc.rotate_quantize(x, perm, 32)
+    r = check_rotated_rows(y, oy, np_u8(c), np_u8(s), oc, os_)
+    note(f"  {r}")
+
+
 def _unrotate_case(orc, x, perm, had):
     pt = None if perm is None else torch.from_numpy(perm).cuda()
     c, s, _ = fp4.rotate_quantize(to_dev(x), pt, had)
