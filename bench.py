@@ -29,6 +29,7 @@ output directories.
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -89,7 +90,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default="c4", choices=["c4", "c2", "c5"])
+    p.add_argument("--workload", default="c4", choices=["c4", "c1", "c2", "c3", "c5"])
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -190,6 +191,18 @@ def sqnr_db(torch, x, xh):
     return float(10 * torch.log10((x * x).sum() / (d * d).sum()))
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_threads():
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     env = os.environ.get("OMP_NUM_THREADS")
@@ -221,6 +234,7 @@ def cpu_baseline(workload, x, perm, target_s):
     rows = int(min(x.shape[0], max(probe, probe * target_s / max(dt, 1e-6))))
     dt = run(rows)
     out = {"value": rows * cols * 2 / dt / 1e9, "unit": "GB/s", "cores": th, "kind": "oracle",
+           "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
            "sample": f"first {rows} rows x {cols} cols of the same tensor "
                      f"({rows * cols} elements), {dt:.1f} s on {th} threads"}
     # the same on one thread, on a sample of about a quarter of that time
@@ -492,7 +506,100 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     xp = fp4.dequantize(cp, sp, fp4.NVFP4, fp4.PLAIN, tp)
     out["c2_sqnr_db_plain_nvfp4"] = round(sqnr_db(torch, ys[0].float(), xp.float()), 3)
     del ys, cs, ss
+    out["c1_mxfp4"] = c1_rows(torch, fp4, inputs)
+    out["c5_layer_nvfp4_razer"] = c5_rows(torch, fp4, inputs)
     return out
+
+
+def c1_rows(torch, fp4, inputs):
+    """C1: MXFP4 quantize and dequantize of the 256 x 4096 tensor (2 MB in,
+    launch-bound: also timed from a HIP graph replay), bit-exactness aside
+    (the tests cover it) and the round-trip SQNR."""
+    log("[bench] c1 MXFP4 256x4096")
+    x = inputs.gen_c1()
+    xt = dev_copies(torch, x, 1)[0]
+    r, c = x.shape
+    el = r * c
+    codes = torch.empty((r, c // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((r, c // 32), dtype=torch.uint8, device="cuda")
+    outb = torch.empty_like(xt)
+    q = lambda i: fp4.quantize(xt, fp4.MXFP4, codes=codes, scales=scales)
+    d = lambda i: fp4.dequantize(codes, scales, fp4.MXFP4, out=outb)
+    res = {}
+    for name, fn in (("quantize", q), ("dequantize", d)):
+        ms = timed(torch, fn, 200, 20)
+        us = graph_us(torch, fn, calls=50)
+        res[name] = {"us": round(ms * 1e3, 2), "graph_us_per_call": round(us, 2),
+                     "graph_algorithmic_GBps": round(el * B_MX / us / 1e3, 1)}
+    q(0)
+    d(0)
+    res["sqnr_db"] = round(sqnr_db(torch, xt.float(), outb.float()), 3)
+    return res
+
+
+def c5_rows(torch, fp4, inputs, steps=5, warmup=1, razer_w=False):
+    """C5: the Llama-70B-shaped decoder layer's seven weights (855,638,016
+    bf16), NVFP4 + RaZeR: quantize with the tensor amax pass, quantize with s_t
+    given, dequantize to bf16, and the round trip (amax + quantize +
+    dequantize); per-tensor and layer SQNR. One copy of each weight: the 1.7 GB
+    layer is several times the 256 MB Infinity Cache, so every pass reads HBM."""
+    xs, cs, ss, ts, outs, names = [], [], [], [], [], []
+    el = 0
+    for t, (name, r, c) in enumerate(inputs.C5_SHAPES):
+        log(f"[bench] generating c5 {name} {r}x{c}")
+        x = inputs.gen_c5(t)
+        xs.append(dev_copies(torch, x, 1)[0])
+        cs.append(torch.empty((r, c // 2), dtype=torch.uint8, device="cuda"))
+        ss.append(torch.empty((r, c // 16), dtype=torch.uint8, device="cuda"))
+        ts.append(torch.empty(1, dtype=torch.float32, device="cuda"))
+        outs.append(torch.empty_like(xs[-1]))
+        names.append(name)
+        el += r * c
+        del x
+    n = len(xs)
+    mode = fp4.RAZER_W if razer_w else fp4.RAZER
+
+    def quant_amax(i):
+        for k in range(n):
+            fp4.quantize(xs[k], fp4.NVFP4, mode, tensor_scale=ts[k], scale_given=False,
+                         codes=cs[k], scales=ss[k])
+
+    def quant_given(i):
+        for k in range(n):
+            fp4.quantize(xs[k], fp4.NVFP4, mode, tensor_scale=ts[k], codes=cs[k], scales=ss[k])
+
+    def dequant(i):
+        for k in range(n):
+            fp4.dequantize(cs[k], ss[k], fp4.NVFP4, mode, ts[k], out=outs[k])
+
+    def round_trip(i):
+        quant_amax(i)
+        dequant(i)
+
+    res = {"elements": el}
+    for name, fn, per in (("quantize_with_amax", quant_amax, B_NV + 2),
+                          ("quantize_scale_given", quant_given, B_NV),
+                          ("dequantize", dequant, B_NV),
+                          ("round_trip", round_trip, 2 * B_NV + 2)):
+        ms = timed(torch, fn, steps, warmup)
+        res[name] = {"ms": round(ms, 4), "input_GBps": round(el * 2 / ms / 1e6, 1),
+                     "algorithmic_GBps": round(el * per / ms / 1e6, 1),
+                     "frac_hbm": round(el * per / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    round_trip(0)
+    torch.cuda.synchronize()
+    num = den = 0.0
+    per_t = {}
+    for k in range(n):
+        xd = xs[k].double()
+        e = float(((xd - outs[k].double()) ** 2).sum())
+        s2 = float((xd * xd).sum())
+        per_t[names[k]] = round(10 * math.log10(s2 / e), 3)
+        num += s2
+        den += e
+    res["sqnr_db_per_tensor"] = per_t
+    res["sqnr_db_layer"] = round(10 * math.log10(num / den), 3)
+    del xs, cs, ss, ts, outs
+    return res
 
 
 MFMA_PEAK_FP4_TFLOPS = 10100.0
@@ -532,6 +639,65 @@ def gemm_rows(torch, fp4, fmt):
                 2.0 * m * n * k / (us * 1e-6) / 1e12 / peak, 4)
         del a, sa, b, sb, c
     return rows
+
+
+def bench_c1(torch, fp4, inputs, args):
+    """C1: MXFP4 quantize + dequantize of the 256 x 4096 tensor, one step =
+    both calls (launch-bound at this size)."""
+    x = inputs.gen_c1()
+    xt = dev_copies(torch, x, 1)[0]
+    r, c = x.shape
+    codes = torch.empty((r, c // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((r, c // 32), dtype=torch.uint8, device="cuda")
+    outb = torch.empty_like(xt)
+
+    def step(i):
+        fp4.quantize(xt, fp4.MXFP4, codes=codes, scales=scales)
+        fp4.dequantize(codes, scales, fp4.MXFP4, out=outb)
+
+    ms = timed(torch, step, args.steps, args.warmup)
+    el = r * c
+    return {"ms": ms, "value": el * 2 / ms / 1e6, "elems": el,
+            "sqnr": sqnr_db(torch, xt.float(), outb.float()),
+            "config": {"workload": "c1: 256x4096 bf16 N(0,0.02) + 0.1% outliers x20; MXFP4 "
+                                   "(E8M0, block 32) quantize then dequantize", "rows": r,
+                       "cols": c, "format": "mxfp4", "block": 32},
+            "roofline": {"bound": "hbm", "achieved": el * 2 * B_MX / ms / 1e6,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": el * 2 * B_MX / ms / 1e6 / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "mx_quant_kernel + mx_dequant_kernel (launch-bound)",
+                         "bytes_per_launch": int(el * B_MX)},
+            "extras": {"graph": c1_rows(torch, fp4, inputs)}}, x, None
+
+
+def bench_c3(torch, fp4, inputs, args):
+    """C3: 32-point block Hadamard + MXFP4 on the 8192 x 8192 heavy-tailed
+    activations (one fused launch per step, two input copies)."""
+    x = inputs.gen_c3()
+    xs = dev_copies(torch, x, copies_for(x.nbytes))
+    n = len(xs)
+    r, c = x.shape
+    codes = [torch.empty((r, c // 2), dtype=torch.uint8, device="cuda") for _ in range(n)]
+    scales = [torch.empty((r, c // 32), dtype=torch.uint8, device="cuda") for _ in range(n)]
+
+    def step(i):
+        k = i % n
+        fp4.rotate_quantize(xs[k], None, 32, codes=codes[k], scales=scales[k])
+
+    ms = timed(torch, step, args.steps, args.warmup)
+    el = r * c
+    xh = fp4.dequantize(codes[0], scales[0], fp4.MXFP4, hadamard=32)
+    return {"ms": ms, "value": el * 2 / ms / 1e6, "elems": el,
+            "sqnr": sqnr_db(torch, xs[0].float(), xh.float()),
+            "config": {"workload": "c3: 8192x8192 bf16 activations 0.5 Student-t(3), 16 "
+                                   "channels x50; block Hadamard-32 + MXFP4 quantize + pack",
+                       "rows": r, "cols": c, "format": "mxfp4", "block": 32,
+                       "rotation": "hadamard32", "input_copies": n},
+            "roofline": {"bound": "hbm", "achieved": el * B_MX / ms / 1e6, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": el * B_MX / ms / 1e6 / HBM_PEAK_GBS,
+                         "traffic": None, "kernel": "mx_rotq_stream_mfma_kernel",
+                         "bytes_per_launch": int(el * B_MX)},
+            "extras": {"step_us_p10_p50_p90": step_distribution(torch, step, 200)}}, None, None
 
 
 def bench_c2(torch, fp4, inputs, args):
@@ -615,6 +781,11 @@ def bench_c5(torch, fp4, inputs, args):
                      codes=cs[k], scales=ss[k])
         fp4.dequantize(cs[k], ss[k], fp4.NVFP4, fp4.PLAIN, ts[k], out=outs[k])
     extras["plain_nvfp4_sqnr_db"] = round(layer_sqnr(), 3)
+    # the kernels of one timed step and their launches per step (for the
+    # per-step sum of a kernel trace: other passes above launch some of them too)
+    extras["step_kernel_calls"] = {"nv_amax_kernel<": len(xs), "nv_tensor_scale_kernel<": len(xs),
+                                   "nv_quant_kernel<true, 1>": len(xs),
+                                   "nv_dequant_kernel<true, 1>": len(xs)}
     per_el = (B_NV + 2) + B_NV
     res = {"ms": ms, "value": el * 2 / ms / 1e6, "elems": el, "sqnr": sqnr,
            "config": {"workload": "c5: Llama-70B-shaped decoder-layer weights q,k,v,o,gate,up,"
@@ -748,13 +919,10 @@ def trace_summary(trace_dir, bench_log):
     args = f"--workload {wl}" if wl != "c4" else ""
     out = [f"# Kernel times of one profiled bench.py run ({line['config']['workload'] if line else wl})",
            "", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
-    fp4_total = 0.0
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         if not name.startswith("fp4::") and "copyBuffer" not in name:
             continue
-        if name.startswith("fp4::"):
-            fp4_total += float(r["TotalDurationNs"])
         out.append(f"| `{name[:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     out.append("")
@@ -765,12 +933,20 @@ def trace_summary(trace_dir, bench_log):
         out += [f"The fused kernel `{ROT_INSTANCE}` averages {avg:.2f} us per launch here (warm-up "
                 f"launches included); the same run's HIP-event time per step is {ev:.2f} us "
                 f"({ev / avg:.3f}x), one launch per step.", ""]
-    elif line:
-        n = line["steps"] + line["warmup"]
+    elif line and line.get("extras", {}).get("step_kernel_calls"):
+        calls = line["extras"]["step_kernel_calls"]
         ev = line["ms_per_step"] * 1e3
-        out += [f"All fp4 kernels together take {fp4_total / 1e3 / n:.1f} us per step here "
-                f"(total over the {n} warm-up and timed steps); the same run's HIP-event time per "
-                f"step is {ev:.1f} us.", ""]
+        per_step, parts = 0.0, []
+        for pat, k in calls.items():
+            hit = [r for r in rows if pat in r["Name"]]
+            if not hit:
+                continue
+            avg = sum(float(r["TotalDurationNs"]) for r in hit) / sum(int(r["Calls"]) for r in hit)
+            per_step += k * avg / 1e3
+            parts.append(f"{k} x `{pat.rstrip('<')}` {avg / 1e3:.2f} us")
+        out += [f"One timed step launches " + ", ".join(parts) + f": {per_step:.1f} us of kernel "
+                f"time per step (average durations over every launch in the trace); the same "
+                f"run's HIP-event time per step is {ev:.1f} us.", ""]
     out += ["Command (from the repository root, TMPDIR=/tmp):", "", "```",
             "rocprofv3 --kernel-trace --stats -d <trace_dir> -o run --output-format csv "
             f"-- python3 bench.py {args + ' ' if args else ''}"
@@ -799,7 +975,8 @@ def main():
 
     fp4.lib()  # fails loudly if the HIP library is not built
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    fn = {"c4": bench_c4, "c2": bench_c2, "c5": bench_c5}[args.workload]
+    fn = {"c4": bench_c4, "c1": bench_c1, "c2": bench_c2, "c3": bench_c3,
+          "c5": bench_c5}[args.workload]
     res, x_host, perm = fn(torch, fp4, inputs, args)
 
     cpu = None

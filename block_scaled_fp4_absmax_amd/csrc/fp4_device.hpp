@@ -183,17 +183,17 @@ __device__ __forceinline__ void widen8(u32x4_t d, float* v) {
 
 // ---- E4M3 block scale (NVFP4) ---------------------------------------------
 // OCP E4M3 "fn": bias 7, subnormals m * 2^-9, largest finite 448, 0x7F NaN.
-// Nearest code to s >= 0 with ties to the even code, saturating at 448;
-// branch-free (both the subnormal and the normal candidate are computed).
+// Nearest code to s >= 0 with ties to the even code, saturating at 448:
+// gfx950's v_cvt_pk_fp8_f32 rounds to the OCP E4M3 code this way (checked on
+// MI355X against an integer-arithmetic encoder -- subnormals m 2^-9 by an
+// exact rescale and round half even, normals by rounding the 20 dropped
+// mantissa bits with ties to even -- for every non-negative fp32 bit pattern
+// up to +Inf) except that it gives NaN (0x7F) where the value rounds past
+// 448, so the value is first clamped to 448 (a NaN s, which fminf drops, also
+// gives 0x7E).
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  // subnormals m * 2^-9: exact rescale, round half even
-  const uint32_t sub = (uint32_t)__builtin_rintf(s * 512.0f);
-  // normals: round the 20 dropped mantissa bits (ties even), rebias 127 -> 7
-  uint32_t u = __float_as_uint(s);
-  u += 0x7FFFFu + ((u >> 20) & 1u);
-  const uint32_t nrm = (u >> 20) - (120u << 3);
-  const uint32_t c = s < 0x1p-6f ? sub : nrm;
-  return s <= 448.0f ? c : 0x7Eu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(s, 448.0f), 0.0f, 0, false) &
+         0xFFu;
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
@@ -278,7 +278,9 @@ __device__ __forceinline__ void nv_rcp_table(float* tab, float s_t) {
 __device__ __forceinline__ uint32_t razer_apply(uint32_t w, uint32_t cm, uint32_t sel) {
   const uint32_t spm = cm & ~(w ^ (sel ? 0x88888888u : 0u));
   w = canonical_zero(w);
-  return (w & ~((spm >> 3) * 0xFu)) | spm;
+  // nibble mask 0xF where spm has bit 3: 15 b 16^k summed = (spm << 1) -
+  // (spm >> 3) modulo 2^32 (full-rate shifts in place of a 32-bit multiply)
+  return (w & ~((spm << 1) - (spm >> 3))) | spm;
 }
 
 // Gain flags of eight elements (see razer_gain): bit 3 of nibble k is set iff
@@ -299,8 +301,10 @@ __device__ __forceinline__ uint32_t razer_flags8(const float* g) {
 // largest block onto 6 * 30.
 constexpr float kWeightPair = 2.5f;
 
-// Nearest E3M3 code to s >= 0, ties to the even code, saturating at 30: as
-// e4m3_encode with 3 exponent bits (subnormals below 2^-2, rebias 127 -> 3).
+// Nearest E3M3 code to s >= 0, ties to the even code, saturating at 30 (no
+// hardware format has this layout): subnormals m 2^-5 (below 2^-2) by an exact
+// rescale and round half even; normals by rounding the 20 dropped mantissa
+// bits with ties to even and rebiasing 127 -> 3.
 __device__ __forceinline__ uint32_t e3m3_encode(float s) {
   const uint32_t sub = (uint32_t)__builtin_rintf(s * 32.0f);
   uint32_t u = __float_as_uint(s);
