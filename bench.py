@@ -54,6 +54,10 @@ ROT_SOURCES = ["block_scaled_fp4_absmax_amd/csrc/rotate_kernels.hpp",
                "block_scaled_fp4_absmax_amd/csrc/launch.hpp"]
 TRAFFIC_FILE = "profiles/traffic_perm_rotate_quantize_c4.md"
 COPY_BYTES = 1 << 30  # torch device copy in device_copy(): 1 GiB read, 1 GiB written
+# steps of the informational rows: the first hundred or so launches on freshly
+# allocated output buffers run up to 30% slower on MI355X, so each row warms up
+# longer than a few launches before it is timed
+ROW_STEPS, ROW_WARMUP = 50, 30
 
 
 def log(msg):
@@ -103,8 +107,28 @@ def parse():
     return p.parse_args()
 
 
+_SETTLE = {}
+
+
+def settle(torch, ms=30.0):
+    """Keep the GPU busy for about ms milliseconds (device fills of a 256 MiB
+    buffer, untimed) and wait: after host-side work the GPU idles, and on
+    MI355X the first ~10 ms of work after an idle second run up to 30% slower
+    while the clocks come back up. Settling first makes a timed region see the
+    clocks of sustained operation."""
+    if "buf" not in _SETTLE:
+        _SETTLE["buf"] = torch.empty(1 << 26, dtype=torch.float32, device="cuda")
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(16):  # about 1 ms of back-to-back fills per wait
+            _SETTLE["buf"].fill_(1.0)
+        torch.cuda.synchronize()
+
+
 def timed(torch, fn, steps, warmup):
-    """ms per call of fn(i), measured with events on the current stream."""
+    """ms per call of fn(i), measured with events on the current stream, after
+    settle() and the warm-up calls."""
+    settle(torch)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -124,6 +148,7 @@ def graph_us(torch, fn, calls=20, replays=5):
     GPU-side time of launches too short for the Python binding to keep the
     queue ahead of them (the library records no allocation and no memset, so
     the calls capture as they run)."""
+    settle(torch)
     cur = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     side.wait_stream(cur)
@@ -154,6 +179,7 @@ def step_distribution(torch, fn, n):
     """p10 / p50 / p90 of single-step times (us): an event pair around each of n
     back-to-back steps; the queue stays ahead of the GPU, so each pair brackets
     that step's kernels only."""
+    settle(torch)
     st = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
@@ -267,9 +293,13 @@ def bench_c4(torch, fp4, inputs, args):
     calib_ms = (time.perf_counter() - t0) * 1e3
     e_ms = timed(torch, lambda i: fp4.channel_energy(xs[i % n]), 5, 1)
 
+    # one prepared library call per input copy: the arguments are checked once,
+    # each step enqueues the fused kernel straight through the C ABI
+    plans = [fp4.rotate_quantize(xs[k], perm, 32, codes=codes[k], scales=scales[k], prepare=True)
+             for k in range(n)]
+
     def step(i):
-        k = i % n
-        fp4.rotate_quantize(xs[k], perm, 32, codes=codes[k], scales=scales[k])
+        plans[i % n].run()
 
     log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
     ms = timed(torch, step, args.steps, args.warmup)
@@ -328,18 +358,25 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
         return {"ms": round(ms, 5), "input_GBps": round(elems * 2 / ms / 1e6, 1),
                 "algorithmic_GBps": round(elems * per_el / ms / 1e6, 1)}
 
-    ms = timed(torch, lambda i: fp4.quantize(xs[i % n], fp4.MXFP4, codes=codes[i % n],
-                                             scales=scales[i % n]), 20, 3)
+    def per_copy(make):
+        """A step over the input copies from prepared calls (one per copy)."""
+        ps = [make(k) for k in range(n)]
+        return lambda i: ps[i % n].run()
+
+    ms = timed(torch, per_copy(lambda k: fp4.quantize(xs[k], fp4.MXFP4, codes=codes[k],
+                                                      scales=scales[k], prepare=True)), ROW_STEPS, ROW_WARMUP)
     out["c4_mxfp4_plain_quantize"] = gbs(ms, el, B_MX)
-    ms = timed(torch, lambda i: fp4.rotate_quantize(xs[i % n], None, 32, codes=codes[i % n],
-                                                    scales=scales[i % n]), 20, 3)
+    ms = timed(torch, per_copy(lambda k: fp4.rotate_quantize(xs[k], None, 32, codes=codes[k],
+                                                             scales=scales[k], prepare=True)),
+               ROW_STEPS, ROW_WARMUP)
     out["c4_mxfp4_hadamard_only"] = gbs(ms, el, B_MX)
     outb = torch.empty_like(xs[0])
-    ms = timed(torch, lambda i: fp4.dequantize(codes[i % n], scales[i % n], fp4.MXFP4, out=outb),
-               20, 3)
+    ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], scales[k], fp4.MXFP4, out=outb,
+                                                        prepare=True)), ROW_STEPS, ROW_WARMUP)
     out["c4_mxfp4_dequantize"] = gbs(ms, el, B_MX)
-    ms = timed(torch, lambda i: fp4.dequantize(codes[i % n], scales[i % n], fp4.MXFP4, perm=perm,
-                                               hadamard=32, out=outb), 20, 3)
+    ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], scales[k], fp4.MXFP4, perm=perm,
+                                                        hadamard=32, out=outb, prepare=True)),
+               ROW_STEPS, ROW_WARMUP)
     out["c4_mxfp4_dequantize_unrotate"] = gbs(ms, el, B_MX)
 
     # NVFP4 + RaZeR after the two-level rotation on the same tensor (permutation
@@ -348,18 +385,18 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     s16 = [torch.empty((rows, cols // 16), dtype=torch.uint8, device="cuda") for _ in range(n)]
     t16 = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(n)]
 
-    def nv_rot(i, given):
-        k = i % n
-        fp4.rotate_quantize(xs[k], perm16, 16, codes=codes[k], scales=s16[k], fmt=fp4.NVFP4,
-                            mode=fp4.RAZER, tensor_scale=t16[k], scale_given=given)
+    def nv_rot(given):
+        return per_copy(lambda k: fp4.rotate_quantize(
+            xs[k], perm16, 16, codes=codes[k], scales=s16[k], fmt=fp4.NVFP4, mode=fp4.RAZER,
+            tensor_scale=t16[k], scale_given=given, prepare=True))
 
-    ms = timed(torch, lambda i: nv_rot(i, False), 20, 3)
+    ms = timed(torch, nv_rot(False), ROW_STEPS, ROW_WARMUP)
     out["c4_nvfp4_razer_perm_h16_with_amax"] = gbs(ms, el, B_NV + 2)
-    ms = timed(torch, lambda i: nv_rot(i, True), 20, 3)
+    ms = timed(torch, nv_rot(True), ROW_STEPS, ROW_WARMUP)
     out["c4_nvfp4_razer_perm_h16_scale_given"] = gbs(ms, el, B_NV)
-    ms = timed(torch, lambda i: fp4.dequantize(codes[i % n], s16[i % n], fp4.NVFP4, fp4.RAZER,
-                                               t16[i % n], perm=perm16, hadamard=16, out=outb),
-               20, 3)
+    ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], s16[k], fp4.NVFP4, fp4.RAZER,
+                                                        t16[k], perm=perm16, hadamard=16,
+                                                        out=outb, prepare=True)), ROW_STEPS, ROW_WARMUP)
     out["c4_nvfp4_razer_dequantize_unrotate"] = gbs(ms, el, B_NV)
     xf = xs[0].float()
     for name, (pm, had) in {"perm_h16": (perm16, 16), "h16": (None, 16),
@@ -370,14 +407,16 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     del s16
 
     # MXINT4 (two's complement k/4 elements, E8M0 scale) on the same tensor
-    ms = timed(torch, lambda i: fp4.quantize(xs[i % n], fp4.MXINT4, codes=codes[i % n],
-                                             scales=scales[i % n]), 20, 3)
+    ms = timed(torch, per_copy(lambda k: fp4.quantize(xs[k], fp4.MXINT4, codes=codes[k],
+                                                      scales=scales[k], prepare=True)), ROW_STEPS, ROW_WARMUP)
     out["c4_mxint4_plain_quantize"] = gbs(ms, el, B_MX)
-    ms = timed(torch, lambda i: fp4.rotate_quantize(xs[i % n], perm, 32, codes=codes[i % n],
-                                                    scales=scales[i % n], fmt=fp4.MXINT4), 20, 3)
+    ms = timed(torch, per_copy(lambda k: fp4.rotate_quantize(xs[k], perm, 32, codes=codes[k],
+                                                             scales=scales[k], fmt=fp4.MXINT4,
+                                                             prepare=True)), ROW_STEPS, ROW_WARMUP)
     out["c4_mxint4_perm_h32_quantize"] = gbs(ms, el, B_MX)
-    ms = timed(torch, lambda i: fp4.dequantize(codes[i % n], scales[i % n], fp4.MXINT4, perm=perm,
-                                               hadamard=32, out=outb), 20, 3)
+    ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], scales[k], fp4.MXINT4, perm=perm,
+                                                        hadamard=32, out=outb, prepare=True)),
+               ROW_STEPS, ROW_WARMUP)
     out["c4_mxint4_dequantize_unrotate"] = gbs(ms, el, B_MX)
     for name, (pm, had) in {"perm_h32": (perm, 32), "h32": (None, 32),
                             "plain": (None, 0)}.items():
@@ -395,22 +434,23 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     macro_ms = (time.perf_counter() - t0) * 1e3
     md = macro.to("cuda")
     zs = [torch.empty_like(xs[0]) for _ in range(n)]
-    ms = timed(torch, lambda i: fp4.apply_channel_rotation(xs[i % n], md, perm, out=zs[i % n]),
-               20, 3)
+    ms = timed(torch, per_copy(lambda k: fp4.apply_channel_rotation(xs[k], md, perm, out=zs[k],
+                                                                    prepare=True)), ROW_STEPS, ROW_WARMUP)
     out["c4_givens_layers_apply"] = gbs(ms, el, 4)
-    ms = timed(torch, lambda i: fp4.apply_channel_rotation(xs[i % n], md, None, out=zs[i % n]),
-               20, 3)
+    ms = timed(torch, per_copy(lambda k: fp4.apply_channel_rotation(xs[k], md, None, out=zs[k],
+                                                                    prepare=True)), ROW_STEPS, ROW_WARMUP)
     out["c4_givens_layers_apply_no_perm"] = gbs(ms, el, 4)
     t0 = time.perf_counter()
     R, rloss = fp4.calibrate_block_rotation(zs[0][:256], None, iters=30, angles=32)
     block_ms = (time.perf_counter() - t0) * 1e3
     rt = R.cuda()
     ident = torch.arange(cols, dtype=torch.int32, device="cuda")
-    ms = timed(torch, lambda i: fp4.rotate_quantize_r(zs[i % n], ident, rt, codes=codes[i % n],
-                                                      scales=scales[i % n]), 20, 3)
+    ms = timed(torch, per_copy(lambda k: fp4.rotate_quantize_r(zs[k], ident, rt, codes=codes[k],
+                                                               scales=scales[k], prepare=True)),
+               ROW_STEPS, ROW_WARMUP)
     out["c4_mxfp4_learned_r_quantize"] = gbs(ms, el, B_MX)
-    ms = timed(torch, lambda i: fp4.dequantize_r(codes[i % n], scales[i % n], ident, rt,
-                                                 out=outb), 20, 3)
+    ms = timed(torch, per_copy(lambda k: fp4.dequantize_r(codes[k], scales[k], ident, rt, out=outb,
+                                                          prepare=True)), ROW_STEPS, ROW_WARMUP)
     out["c4_mxfp4_learned_r_dequantize"] = gbs(ms, el, B_MX)
     xf, zf = xs[0].float(), zs[0].float()
     c, sc, _ = fp4.rotate_quantize_r(zs[0], ident, rt)
@@ -434,10 +474,15 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
 
     # the heavy-tailed 8192 x 8192 activations: the Hadamard alone, every format
     log("[bench] generating c3 for the rotation rows")
-    x3 = dev_copies(torch, inputs.gen_c3(), 1)[0]
+    x3h = inputs.gen_c3()
+    x3s = dev_copies(torch, x3h, copies_for(x3h.nbytes))  # beyond the Infinity Cache
+    del x3h
+    x3 = x3s[0]
     r3, k3 = x3.shape
-    ms = timed(torch, lambda i: fp4.rotate_quantize(x3, None, 32), 20, 3)
+    p3 = [fp4.rotate_quantize(t, None, 32, prepare=True) for t in x3s]
+    ms = timed(torch, lambda i: p3[i % len(p3)].run(), ROW_STEPS, ROW_WARMUP)
     out["c3_mxfp4_h32_quantize"] = gbs(ms, r3 * k3, B_MX)
+    del p3, x3s
     x3f = x3.float()
     q3 = {}
     for fmt, mode, had, name in ((fp4.MXFP4, fp4.PLAIN, 32, "mxfp4"),
@@ -469,35 +514,37 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
         us = graph_us(torch, fn, calls=2 * m)
         out[key]["graph_us_per_call"] = round(us, 2)
         out[key]["graph_algorithmic_GBps"] = round(el2 * per_el / us / 1e3, 1)
-    ms = timed(torch, lambda i: fp4.quantize(ys[i % m], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[i % m],
-                                             scale_given=False, codes=cs[i % m],
-                                             scales=ss[i % m]), 40, 5)
+    def plan(fn, **kw):
+        ps = [fn(k, **kw) for k in range(m)]
+        return lambda i: ps[i % m].run()
+    q_amax = plan(lambda k: fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[k],
+                                         scale_given=False, codes=cs[k], scales=ss[k],
+                                         prepare=True))
+    ms = timed(torch, q_amax, 2 * ROW_STEPS, ROW_WARMUP)
     out["c2_nvfp4_razer_quantize_with_amax"] = gbs(ms, el2, B_NV + 2)
     xh = fp4.dequantize(cs[0], ss[0], fp4.NVFP4, fp4.RAZER, tss[0])
     out["c2_sqnr_db_razer"] = round(sqnr_db(torch, ys[0].float(), xh.float()), 3)
-    ms = timed(torch, lambda i: fp4.quantize(ys[i % m], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[i % m],
-                                             codes=cs[i % m], scales=ss[i % m]), 40, 5)
+    q_razer = plan(lambda k: fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[k],
+                                          codes=cs[k], scales=ss[k], prepare=True))
+    ms = timed(torch, q_razer, 2 * ROW_STEPS, ROW_WARMUP)
     out["c2_nvfp4_razer_quantize_scale_given"] = gbs(ms, el2, B_NV)
-    graph_row("c2_nvfp4_razer_quantize_scale_given", lambda i: fp4.quantize(
-        ys[i % m], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[i % m], codes=cs[i % m],
-        scales=ss[i % m]), B_NV)
-    ms = timed(torch, lambda i: fp4.quantize(ys[i % m], fp4.NVFP4, fp4.PLAIN, tensor_scale=tss[i % m],
-                                             codes=cs[i % m], scales=ss[i % m]), 40, 5)
+    graph_row("c2_nvfp4_razer_quantize_scale_given", q_razer, B_NV)
+    q_plain = plan(lambda k: fp4.quantize(ys[k], fp4.NVFP4, fp4.PLAIN, tensor_scale=tss[k],
+                                          codes=cs[k], scales=ss[k], prepare=True))
+    ms = timed(torch, q_plain, 2 * ROW_STEPS, ROW_WARMUP)
     out["c2_nvfp4_plain_quantize_scale_given"] = gbs(ms, el2, B_NV)
-    graph_row("c2_nvfp4_plain_quantize_scale_given", lambda i: fp4.quantize(
-        ys[i % m], fp4.NVFP4, fp4.PLAIN, tensor_scale=tss[i % m], codes=cs[i % m],
-        scales=ss[i % m]), B_NV)
+    graph_row("c2_nvfp4_plain_quantize_scale_given", q_plain, B_NV)
     for k in range(m):
         fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[k], codes=cs[k], scales=ss[k])
     ob = torch.empty_like(ys[0])
-    ms = timed(torch, lambda i: fp4.dequantize(cs[i % m], ss[i % m], fp4.NVFP4, fp4.RAZER,
-                                               tss[i % m], out=ob), 40, 5)
+    dq = plan(lambda k: fp4.dequantize(cs[k], ss[k], fp4.NVFP4, fp4.RAZER, tss[k], out=ob,
+                                       prepare=True))
+    ms = timed(torch, dq, 2 * ROW_STEPS, ROW_WARMUP)
     out["c2_nvfp4_razer_dequantize"] = gbs(ms, el2, B_NV)
-    graph_row("c2_nvfp4_razer_dequantize", lambda i: fp4.dequantize(
-        cs[i % m], ss[i % m], fp4.NVFP4, fp4.RAZER, tss[i % m], out=ob), B_NV)
-    ms = timed(torch, lambda i: fp4.quantize(ys[i % m], fp4.NVFP4, fp4.RAZER_W,
-                                             tensor_scale=tss[i % m], codes=cs[i % m],
-                                             scales=ss[i % m]), 40, 5)
+    graph_row("c2_nvfp4_razer_dequantize", dq, B_NV)
+    ms = timed(torch, plan(lambda k: fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER_W,
+                                                  tensor_scale=tss[k], codes=cs[k], scales=ss[k],
+                                                  prepare=True)), 2 * ROW_STEPS, ROW_WARMUP)
     out["c2_nvfp4_razer_w_quantize_scale_given"] = gbs(ms, el2, B_NV)
     cw, sw, tw = fp4.quantize(ys[0], fp4.NVFP4, fp4.RAZER_W)
     xw = fp4.dequantize(cw, sw, fp4.NVFP4, fp4.RAZER_W, tw)
@@ -523,8 +570,10 @@ def c1_rows(torch, fp4, inputs):
     codes = torch.empty((r, c // 2), dtype=torch.uint8, device="cuda")
     scales = torch.empty((r, c // 32), dtype=torch.uint8, device="cuda")
     outb = torch.empty_like(xt)
-    q = lambda i: fp4.quantize(xt, fp4.MXFP4, codes=codes, scales=scales)
-    d = lambda i: fp4.dequantize(codes, scales, fp4.MXFP4, out=outb)
+    pq = fp4.quantize(xt, fp4.MXFP4, codes=codes, scales=scales, prepare=True)
+    pd = fp4.dequantize(codes, scales, fp4.MXFP4, out=outb, prepare=True)
+    q = lambda i: pq.run()
+    d = lambda i: pd.run()
     res = {}
     for name, fn in (("quantize", q), ("dequantize", d)):
         ms = timed(torch, fn, 200, 20)
@@ -537,7 +586,7 @@ def c1_rows(torch, fp4, inputs):
     return res
 
 
-def c5_rows(torch, fp4, inputs, steps=5, warmup=1, razer_w=False):
+def c5_rows(torch, fp4, inputs, steps=5, warmup=3, razer_w=False):
     """C5: the Llama-70B-shaped decoder layer's seven weights (855,638,016
     bf16), NVFP4 + RaZeR: quantize with the tensor amax pass, quantize with s_t
     given, dequantize to bf16, and the round trip (amax + quantize +
@@ -626,14 +675,15 @@ def gemm_rows(torch, fp4, fmt):
         b = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device="cuda", generator=g)
         sb = torch.randint(lo, hi, (n, k // blk), dtype=torch.uint8, device="cuda", generator=g)
         c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-        ms = timed(torch, lambda i: fp4.gemm(a, sa, b, sb, out=c, **kw), 10, 2)
+        pg = fp4.gemm(a, sa, b, sb, out=c, prepare=True, **kw)
+        ms = timed(torch, lambda i: pg.run(), 10, 2)
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         by = (m + n) * (k / 2 + k / blk) + 2 * m * n
         rows[f"{m}x{n}x{k}"] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
                                 "frac_mfma_peak": round(tf / peak, 4),
                                 "GBps": round(by / ms / 1e6, 1)}
         if m <= 32:  # µs-scale launches: also their time replayed from a graph
-            us = graph_us(torch, lambda i: fp4.gemm(a, sa, b, sb, out=c, **kw))
+            us = graph_us(torch, lambda i: pg.run())
             rows[f"{m}x{n}x{k}"]["graph_us_per_call"] = round(us, 2)
             rows[f"{m}x{n}x{k}"]["graph_frac_mfma_peak"] = round(
                 2.0 * m * n * k / (us * 1e-6) / 1e12 / peak, 4)
@@ -651,9 +701,12 @@ def bench_c1(torch, fp4, inputs, args):
     scales = torch.empty((r, c // 32), dtype=torch.uint8, device="cuda")
     outb = torch.empty_like(xt)
 
+    pq = fp4.quantize(xt, fp4.MXFP4, codes=codes, scales=scales, prepare=True)
+    pd = fp4.dequantize(codes, scales, fp4.MXFP4, out=outb, prepare=True)
+
     def step(i):
-        fp4.quantize(xt, fp4.MXFP4, codes=codes, scales=scales)
-        fp4.dequantize(codes, scales, fp4.MXFP4, out=outb)
+        pq.run()
+        pd.run()
 
     ms = timed(torch, step, args.steps, args.warmup)
     el = r * c
@@ -680,9 +733,11 @@ def bench_c3(torch, fp4, inputs, args):
     codes = [torch.empty((r, c // 2), dtype=torch.uint8, device="cuda") for _ in range(n)]
     scales = [torch.empty((r, c // 32), dtype=torch.uint8, device="cuda") for _ in range(n)]
 
+    plans = [fp4.rotate_quantize(xs[k], None, 32, codes=codes[k], scales=scales[k], prepare=True)
+             for k in range(n)]
+
     def step(i):
-        k = i % n
-        fp4.rotate_quantize(xs[k], None, 32, codes=codes[k], scales=scales[k])
+        plans[i % n].run()
 
     ms = timed(torch, step, args.steps, args.warmup)
     el = r * c
@@ -709,10 +764,11 @@ def bench_c2(torch, fp4, inputs, args):
     ss = [torch.empty((r, c // 16), dtype=torch.uint8, device="cuda") for _ in range(m)]
     tss = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(m)]
 
+    plans = [fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[k], scale_given=False,
+                          codes=cs[k], scales=ss[k], prepare=True) for k in range(m)]
+
     def step(i):
-        k = i % m
-        fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[k], scale_given=False,
-                     codes=cs[k], scales=ss[k])
+        plans[i % m].run()
 
     ms = timed(torch, step, args.steps, args.warmup)
     el = r * c

@@ -18,7 +18,7 @@ __all__ = [
     "Fp4Error", "lib", "library_path", "quantize", "dequantize", "rotate_quantize",
     "channel_energy", "build_permutation", "block_of", "gemm", "OUT_F32", "OUT_BF16",
     "rotate_quantize_r", "dequantize_r", "calibrate_block_rotation",
-    "calibrate_macro_rotation", "apply_channel_rotation", "MacroRotation",
+    "calibrate_macro_rotation", "apply_channel_rotation", "MacroRotation", "Prepared",
 ]
 
 MXFP4, NVFP4, MXINT4 = 0, 1, 2
@@ -87,6 +87,41 @@ def lib() -> ctypes.CDLL:
 def _check(fn: str, status: int) -> None:
     if status != 0:
         raise Fp4Error(fn, status, lib().fp4_status_string(status).decode())
+
+
+class Prepared:
+    """A checked library call bound to its tensors, for loops that repeat the
+    same call (serving, benchmarks): ``run()`` enqueues it again with no
+    argument checks and no allocation and returns the same output tensors.
+    It runs on the stream given when it was prepared, else on the caller's
+    current stream at each run (so it can be captured in a graph). The
+    tensors must stay alive and unchanged in shape and storage."""
+
+    def __init__(self, name: str, args: tuple, outputs, stream_given: bool):
+        fn = getattr(lib(), name)
+        # arguments converted to their ctypes types once (the stream is last)
+        self._fn = fn
+        self._args = [a if a is None or isinstance(a, ctypes._SimpleCData) else t(a)
+                      for t, a in zip(fn.argtypes, args)]
+        self._name = name
+        self._fixed_stream = stream_given
+        self.outputs = outputs
+
+    def run(self, stream=None):
+        if stream is not None or not self._fixed_stream:
+            self._args[-1] = _stream(stream)
+        st = self._fn(*self._args)
+        if st:
+            _check(self._name, st)
+        return self.outputs
+
+
+def _call(name: str, args: tuple, outputs, prepare: bool, stream=None):
+    """Run a checked call now, or return it as a Prepared call."""
+    if prepare:
+        return Prepared(name, args, outputs, stream is not None)
+    _check(name, getattr(lib(), name)(*args))
+    return outputs
 
 
 def block_of(fmt: int) -> int:
@@ -181,14 +216,15 @@ def _tensor_scale(tensor_scale, device):
 
 def quantize(x, fmt: int = MXFP4, mode: int = PLAIN, floor_rule: bool = False,
              tensor_scale=None, scale_given: Optional[bool] = None, codes=None, scales=None,
-             stream=None):
+             stream=None, prepare: bool = False):
     """Quantize a bf16 [rows, cols] CUDA tensor.
 
     Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/block],
     tensor_scale fp32 [1] for NVFP4 else None). For NVFP4, ``tensor_scale`` is
     a 1-element fp32 device tensor: read as s_t when ``scale_given`` (the
     default when it is passed), otherwise it receives the computed s_t
-    (allocated when None).
+    (allocated when None). ``prepare=True`` returns a :class:`Prepared` call
+    instead of running it (so does every other entry point that enqueues work).
     """
     import torch
     _check_fmt(fmt, mode)
@@ -205,15 +241,14 @@ def quantize(x, fmt: int = MXFP4, mode: int = PLAIN, floor_rule: bool = False,
                 raise ValueError("scale_given needs a tensor_scale")
             flags |= FLAG_TENSOR_SCALE_GIVEN
         ts = _tensor_scale(tensor_scale, dev)
-    st = lib().fp4_quantize(_ptr(x), rows, cols, ld, fmt, block_of(fmt), mode, flags,
-                            _ptr(codes), codes.stride(0), _ptr(scales), scales.stride(0),
-                            _ptr(ts), _stream(stream))
-    _check("fp4_quantize", st)
-    return codes, scales, ts
+    return _call("fp4_quantize",
+                 (_ptr(x), rows, cols, ld, fmt, block_of(fmt), mode, flags, _ptr(codes),
+                  codes.stride(0), _ptr(scales), scales.stride(0), _ptr(ts), _stream(stream)),
+                 (codes, scales, ts), prepare, stream)
 
 
 def dequantize(codes, scales, fmt: int = MXFP4, mode: int = PLAIN, tensor_scale=None,
-               perm=None, hadamard: int = 0, out=None, stream=None):
+               perm=None, hadamard: int = 0, out=None, stream=None, prepare: bool = False):
     """Decode to a bf16 [rows, cols] tensor (optionally undoing a rotation)."""
     import torch
     _check_fmt(fmt, mode)
@@ -230,17 +265,16 @@ def dequantize(codes, scales, fmt: int = MXFP4, mode: int = PLAIN, tensor_scale=
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
     _mat(out, "out", torch.bfloat16, dev, rows, cols)
-    st = lib().fp4_dequantize(_ptr(codes), ldc, _ptr(scales), scales.stride(0),
-                              _ptr(tensor_scale), rows, cols, fmt, block_of(fmt), mode,
-                              _ptr(perm), hadamard, _ptr(out), out.stride(0), _stream(stream))
-    _check("fp4_dequantize", st)
-    return out
+    return _call("fp4_dequantize",
+                 (_ptr(codes), ldc, _ptr(scales), scales.stride(0), _ptr(tensor_scale), rows,
+                  cols, fmt, block_of(fmt), mode, _ptr(perm), hadamard, _ptr(out), out.stride(0),
+                  _stream(stream)), out, prepare, stream)
 
 
 def rotate_quantize(x, perm=None, hadamard: Optional[int] = None, floor_rule: bool = False,
                     want_rotated: bool = False, codes=None, scales=None, rotated=None,
                     fmt: int = MXFP4, mode: int = PLAIN, tensor_scale=None,
-                    scale_given: Optional[bool] = None, stream=None):
+                    scale_given: Optional[bool] = None, stream=None, prepare: bool = False):
     """Permutation + block Hadamard fused with FP4 quantize + pack.
 
     ``hadamard`` defaults to the format's block size (32 MXFP4, 16 NVFP4); 0
@@ -272,20 +306,18 @@ def rotate_quantize(x, perm=None, hadamard: Optional[int] = None, floor_rule: bo
                 raise ValueError("scale_given needs a tensor_scale")
             flags |= FLAG_TENSOR_SCALE_GIVEN
         ts = _tensor_scale(tensor_scale, dev)
-    st = lib().fp4_rotate_quantize(_ptr(x), rows, cols, ld, _ptr(perm), hadamard, fmt,
-                                   block_of(fmt), mode, flags, _ptr(codes), codes.stride(0),
-                                   _ptr(scales), scales.stride(0), _ptr(ts), _ptr(rotated),
-                                   rotated.stride(0) if rotated is not None else 0,
-                                   _stream(stream))
-    _check("fp4_rotate_quantize", st)
-    if fmt == NVFP4:
-        return codes, scales, rotated, ts
-    return codes, scales, rotated
+    return _call("fp4_rotate_quantize",
+                 (_ptr(x), rows, cols, ld, _ptr(perm), hadamard, fmt, block_of(fmt), mode, flags,
+                  _ptr(codes), codes.stride(0), _ptr(scales), scales.stride(0), _ptr(ts),
+                  _ptr(rotated), rotated.stride(0) if rotated is not None else 0,
+                  _stream(stream)),
+                 (codes, scales, rotated, ts) if fmt == NVFP4 else (codes, scales, rotated),
+                 prepare, stream)
 
 
 def gemm(a_codes, a_scales, b_codes, b_scales, k: Optional[int] = None, fmt: int = MXFP4,
          a_ts=None, b_ts=None, mode_a: int = PLAIN, mode_b: int = PLAIN, out_dtype=None,
-         out=None, stream=None):
+         out=None, stream=None, prepare: bool = False):
     """C = A B^T for quantized A [m, k] and B [n, k] (codes and scales as the
     quantizer returns them; NVFP4 also takes the two tensor scales and a mode
     per operand); fp32 [m, n] unless ``out_dtype`` is bfloat16."""
@@ -317,15 +349,13 @@ def gemm(a_codes, a_scales, b_codes, b_scales, k: Optional[int] = None, fmt: int
         raise ValueError(f"out is {out.dtype}, out_dtype is {out_dtype}")
     _mat(out, "out", out_dtype, dev, m, n)
     od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
-    st = lib().fp4_gemm(_ptr(a_codes), lda, _ptr(a_scales), a_scales.stride(0), _ptr(a_ts),
-                        mode_a, _ptr(b_codes), ldb, _ptr(b_scales), b_scales.stride(0),
-                        _ptr(b_ts), mode_b, m, n, k, fmt, od, _ptr(out), out.stride(0),
-                        _stream(stream))
-    _check("fp4_gemm", st)
-    return out
+    return _call("fp4_gemm",
+                 (_ptr(a_codes), lda, _ptr(a_scales), a_scales.stride(0), _ptr(a_ts), mode_a,
+                  _ptr(b_codes), ldb, _ptr(b_scales), b_scales.stride(0), _ptr(b_ts), mode_b,
+                  m, n, k, fmt, od, _ptr(out), out.stride(0), _stream(stream)), out, prepare, stream)
 
 
-def channel_energy(x, out=None, stream=None):
+def channel_energy(x, out=None, stream=None, prepare: bool = False):
     """fp32 [cols]: sum over rows of x^2 per channel (fp64 accumulation)."""
     import torch
     dev = _device_of(x)
@@ -333,9 +363,8 @@ def channel_energy(x, out=None, stream=None):
     if out is None:
         out = torch.empty(cols, dtype=torch.float32, device=dev)
     _vec(out, "out", torch.float32, cols, dev)
-    st = lib().fp4_channel_energy(_ptr(x), rows, cols, ld, _ptr(out), _stream(stream))
-    _check("fp4_channel_energy", st)
-    return out
+    return _call("fp4_channel_energy", (_ptr(x), rows, cols, ld, _ptr(out), _stream(stream)),
+                 out, prepare, stream)
 
 
 def build_permutation(energy, block: int = 32, group: int = 1):
@@ -350,7 +379,7 @@ def build_permutation(energy, block: int = 32, group: int = 1):
 
 
 def rotate_quantize_r(x, perm, rotation, want_rotated: bool = False, codes=None, scales=None,
-                      rotated=None, stream=None):
+                      rotated=None, stream=None, prepare: bool = False):
     """Permutation + learned 32x32 block matrix (fp32 [32, 32] device tensor,
     R row-major) fused with MXFP4 quantize + pack. Returns (codes, scales,
     rotated fp32 [rows, cols] or None)."""
@@ -364,16 +393,14 @@ def rotate_quantize_r(x, perm, rotation, want_rotated: bool = False, codes=None,
         rotated = torch.empty((rows, cols), dtype=torch.float32, device=dev)
     if rotated is not None:
         _mat(rotated, "rotated", torch.float32, dev, rows, cols)
-    st = lib().fp4_rotate_quantize_r(_ptr(x), rows, cols, ld, _ptr(perm), _ptr(rotation),
-                                     _ptr(codes), codes.stride(0), _ptr(scales),
-                                     scales.stride(0), _ptr(rotated),
-                                     rotated.stride(0) if rotated is not None else 0,
-                                     _stream(stream))
-    _check("fp4_rotate_quantize_r", st)
-    return codes, scales, rotated
+    return _call("fp4_rotate_quantize_r",
+                 (_ptr(x), rows, cols, ld, _ptr(perm), _ptr(rotation), _ptr(codes),
+                  codes.stride(0), _ptr(scales), scales.stride(0), _ptr(rotated),
+                  rotated.stride(0) if rotated is not None else 0, _stream(stream)),
+                 (codes, scales, rotated), prepare, stream)
 
 
-def dequantize_r(codes, scales, perm, rotation, out=None, stream=None):
+def dequantize_r(codes, scales, perm, rotation, out=None, stream=None, prepare: bool = False):
     """Inverse of :func:`rotate_quantize_r`: decode, R^T per block, undo the
     permutation; bf16 [rows, cols]."""
     import torch
@@ -386,11 +413,9 @@ def dequantize_r(codes, scales, perm, rotation, out=None, stream=None):
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
     _mat(out, "out", torch.bfloat16, dev, rows, cols)
-    st = lib().fp4_dequantize_r(_ptr(codes), ldc, _ptr(scales), scales.stride(0), rows, cols,
-                                _ptr(perm), _ptr(rotation), _ptr(out), out.stride(0),
-                                _stream(stream))
-    _check("fp4_dequantize_r", st)
-    return out
+    return _call("fp4_dequantize_r",
+                 (_ptr(codes), ldc, _ptr(scales), scales.stride(0), rows, cols, _ptr(perm),
+                  _ptr(rotation), _ptr(out), out.stride(0), _stream(stream)), out, prepare, stream)
 
 
 def calibrate_block_rotation(x, perm=None, iters: int = 60, angles: int = 32):
@@ -464,7 +489,8 @@ def calibrate_macro_rotation(x, perm=None, block: int = 32, tol: float = 1e-6,
                          (spread[0], spread[1]))
 
 
-def apply_channel_rotation(x, macro: MacroRotation, perm=None, out=None, stream=None):
+def apply_channel_rotation(x, macro: MacroRotation, perm=None, out=None, stream=None,
+                           prepare: bool = False):
     """bf16 [rows, cols]: permutation, then the Givens layers of ``macro``
     (device tensors, see :meth:`MacroRotation.to`), on every row."""
     import torch
@@ -478,9 +504,7 @@ def apply_channel_rotation(x, macro: MacroRotation, perm=None, out=None, stream=
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
     _mat(out, "out", torch.bfloat16, dev, rows, cols)
-    st = lib().fp4_apply_channel_rotation(_ptr(x), rows, cols, ld, _ptr(perm), _ptr(macro.pairs),
-                                          _ptr(macro.cs), _ptr(macro.layer_start),
-                                          macro.n_layers, macro.n_rot, _ptr(out),
-                                          out.stride(0), _stream(stream))
-    _check("fp4_apply_channel_rotation", st)
-    return out
+    return _call("fp4_apply_channel_rotation",
+                 (_ptr(x), rows, cols, ld, _ptr(perm), _ptr(macro.pairs), _ptr(macro.cs),
+                  _ptr(macro.layer_start), macro.n_layers, macro.n_rot, _ptr(out), out.stride(0),
+                  _stream(stream)), out, prepare, stream)

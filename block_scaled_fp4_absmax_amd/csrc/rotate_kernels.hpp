@@ -388,7 +388,9 @@ struct PermRows {
 // registers, and the waves per SIMD the register allocation is held to. Two
 // row buffers of 8 KB kTpw each bound the work-groups a CU can hold; two per
 // CU (32 rows each at 16384 rows) ran faster than three or four, and one per
-// CU slower. A second row of look-ahead gained about 1%, more none.
+// CU slower. A second row of look-ahead gained about 1%, more none. The NVFP4
+// variants, with more arithmetic per element, also ran slowest at three or
+// four per CU.
 template <int kTpw>
 constexpr int perm_wgs_per_cu() {
   return kTpw == 1 ? 4 : kTpw <= 4 ? 2 : 1;

@@ -25,8 +25,9 @@ def _gpu():
 
 
 def test_graph_replays_match_eager():
-    note("case: HIP graph of rotate+quantize (MXFP4), NVFP4 RaZeR with computed s_t, "
-         "dequantize with inverse rotation, and the GEMM (tiles and split-K); 4 replays")
+    note("case: HIP graph of rotate+quantize (MXFP4) and dequantize with inverse rotation "
+         "(prepared calls), NVFP4 RaZeR with computed s_t, and the GEMM (tiles and split-K); "
+         "4 replays")
     x = to_dev(inputs.gen_c4(rows=512, cols=4096))
     w = to_dev(inputs.gen_c5(0, rows=256, cols=4096))
     perm = fp4.build_permutation(fp4.channel_energy(x)).cuda()
@@ -41,10 +42,13 @@ def test_graph_replays_match_eager():
     sw = torch.empty((256, 128), dtype=torch.uint8, device="cuda")
     out = torch.empty((512, 256), dtype=torch.float32, device="cuda")
     out16 = torch.empty((16, 256), dtype=torch.bfloat16, device="cuda")  # split-K GEMM
+    # prepared calls follow the stream current at each run, the capture stream included
+    p_rot = fp4.rotate_quantize(x, perm, 32, codes=c, scales=s, prepare=True)
+    p_deq = fp4.dequantize(c, s, fp4.MXFP4, perm=perm, hadamard=32, out=d, prepare=True)
 
     def work():
-        fp4.rotate_quantize(x, perm, 32, codes=c, scales=s)
-        fp4.dequantize(c, s, fp4.MXFP4, perm=perm, hadamard=32, out=d)
+        p_rot.run()
+        p_deq.run()
         fp4.quantize(w, fp4.NVFP4, fp4.RAZER, tensor_scale=tn, scale_given=False, codes=cn,
                      scales=sn)
         fp4.rotate_quantize(w, None, 32, codes=cw, scales=sw)
