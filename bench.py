@@ -101,6 +101,12 @@ def parse():
     p.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
                    help="write the kernel-time summary from a rocprofv3 --kernel-trace --stats "
                         "directory and the JSON line that the profiled run printed, and exit")
+    p.add_argument("--kernel-op", choices=sorted(KERNEL_OPS),
+                   help="time one kernel on its own (the run that rocprofv3 counter passes "
+                        "profile) and print its JSON line")
+    p.add_argument("--counter-summary", nargs="+", metavar=("OP_LOG", "DIR"),
+                   help="write the counter summary of a --kernel-op run from its JSON line and "
+                        "rocprofv3 --pmc output directories, and exit")
     p.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                    help="write the traffic summary from rocprofv3 --pmc output directories "
                         "(FETCH_SIZE run, WRITE_SIZE run[, MFMA busy run]) and exit")
@@ -803,11 +809,14 @@ def bench_c5(torch, fp4, inputs, args):
         el += r * c
         del x
 
+    plans = [p for k in range(len(xs)) for p in (
+        fp4.quantize(xs[k], fp4.NVFP4, fp4.RAZER, tensor_scale=ts[k], scale_given=False,
+                     codes=cs[k], scales=ss[k], prepare=True),
+        fp4.dequantize(cs[k], ss[k], fp4.NVFP4, fp4.RAZER, ts[k], out=outs[k], prepare=True))]
+
     def step(i):
-        for k in range(len(xs)):
-            fp4.quantize(xs[k], fp4.NVFP4, fp4.RAZER, tensor_scale=ts[k], scale_given=False,
-                         codes=cs[k], scales=ss[k])
-            fp4.dequantize(cs[k], ss[k], fp4.NVFP4, fp4.RAZER, ts[k], out=outs[k])
+        for p in plans:
+            p.run()
 
     ms = timed(torch, step, args.steps, args.warmup)
     import math
@@ -856,21 +865,240 @@ def bench_c5(torch, fp4, inputs, args):
     return res, None, None
 
 
-def _pmc_rows(d, counter):
-    """{kernel name: [per-dispatch counter value]} from a rocprofv3 --pmc CSV directory."""
+KERNEL_OPS = {
+    "c4_perm_mxfp4": "fused permutation + Hadamard-32 + MXFP4 quantize, 16384x8192 bf16 (c4)",
+    "c4_perm_nvfp4_razer": "fused permutation + Hadamard-16 + NVFP4 + RaZeR quantize, tensor "
+                           "scale given, 16384x8192 bf16 (c4)",
+    "c2_nvfp4_plain": "NVFP4 quantize, tensor scale given, 4096x4096 bf16 (c2)",
+    "c2_nvfp4_razer": "NVFP4 + RaZeR quantize, tensor scale given, 4096x4096 bf16 (c2)",
+    "gemm_mxfp4": "MXFP4 x MXFP4 GEMM, m=4096 n=8192 k=8192, bf16 out",
+}
+
+
+def kernel_op(torch, fp4, inputs, args):
+    """One kernel on its own: args.warmup untimed launches, then args.steps
+    timed ones, over enough input copies to read from HBM. Prints one JSON line
+    naming the kernel, the units one launch processes and the ms per launch,
+    which --counter-summary reads beside the counter directories."""
+    op = args.kernel_op
+    if op.startswith("c4_"):
+        rows, cols = inputs.FULL_SHAPES["c4"]
+        x = inputs.gen_c4()
+        xs = dev_copies(torch, x, copies_for(x.nbytes))
+        del x
+        n = len(xs)
+        nv = op == "c4_perm_nvfp4_razer"
+        blk = 16 if nv else 32
+        perm = fp4.build_permutation(fp4.channel_energy(xs[0]), blk).cuda()
+        codes = [torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda") for _ in range(n)]
+        scales = [torch.empty((rows, cols // blk), dtype=torch.uint8, device="cuda")
+                  for _ in range(n)]
+        kw = {}
+        if nv:
+            ts = [fp4.rotate_quantize(xs[k], perm, 16, fmt=fp4.NVFP4, mode=fp4.RAZER)[3]
+                  for k in range(n)]
+            kw = lambda k: dict(fmt=fp4.NVFP4, mode=fp4.RAZER, tensor_scale=ts[k])
+        else:
+            kw = lambda k: {}
+        ps = [fp4.rotate_quantize(xs[k], perm, blk, codes=codes[k], scales=scales[k],
+                                  prepare=True, **kw(k)) for k in range(n)]
+        kernel = ROT_KERNEL + ("<2, 1, true, true, false>" if nv else "<2, 0, true, false, false>")
+        units, unit = rows * cols, "element"
+    elif op.startswith("c2_"):
+        x = inputs.gen_c2()
+        r, c = x.shape
+        xs = dev_copies(torch, x, copies_for(x.nbytes))
+        del x
+        n = len(xs)
+        mode = fp4.RAZER if op == "c2_nvfp4_razer" else fp4.PLAIN
+        ps = []
+        for k in range(n):
+            cq, sq, tq = fp4.quantize(xs[k], fp4.NVFP4, mode)  # tensor scale, untimed
+            ps.append(fp4.quantize(xs[k], fp4.NVFP4, mode, tensor_scale=tq, codes=cq, scales=sq,
+                                   prepare=True))
+        kernel = f"nv_quant_kernel<true, {1 if mode == fp4.RAZER else 0}>"
+        units, unit = r * c, "element"
+    else:
+        m, nn, k = 4096, 8192, 8192
+        g = torch.Generator(device="cuda").manual_seed(5)
+        a = torch.randint(0, 256, (m, k // 2), dtype=torch.uint8, device="cuda", generator=g)
+        sa = torch.randint(120, 131, (m, k // 32), dtype=torch.uint8, device="cuda", generator=g)
+        b = torch.randint(0, 256, (nn, k // 2), dtype=torch.uint8, device="cuda", generator=g)
+        sb = torch.randint(120, 131, (nn, k // 32), dtype=torch.uint8, device="cuda", generator=g)
+        cm = torch.empty((m, nn), dtype=torch.bfloat16, device="cuda")
+        ps = [fp4.gemm(a, sa, b, sb, out=cm, prepare=True)]
+        kernel = "mx_gemm_kernel<"
+        units, unit = 2 * m * nn * k, "flop"
+    ms = timed(torch, lambda i: ps[i % len(ps)].run(), args.steps, args.warmup)
+    print(json.dumps({"kernel_op": op, "what": KERNEL_OPS[op], "kernel": kernel,
+                      "units_per_launch": units, "unit": unit, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_launch": round(ms, 5)}), flush=True)
+
+
+# counters whose ratio the summary reports, when a pass holds both
+def _pearson(a, b):
+    n = len(a)
+    ma, mb = sum(a) / n, sum(b) / n
+    sab = sum((x - ma) * (y - mb) for x, y in zip(a, b))
+    saa = sum((x - ma) ** 2 for x in a)
+    sbb = sum((y - mb) ** 2 for y in b)
+    return sab / math.sqrt(saa * sbb) if saa > 0 and sbb > 0 else float("nan")
+
+
+COUNTER_RATIOS = [
+    ("LDS bank-conflict cycles per indexed-LDS active cycle", "SQ_LDS_BANK_CONFLICT",
+     "SQ_LDS_IDX_ACTIVE"),
+    ("mean HBM read latency, cycles (outstanding reads per read request)",
+     "TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_RDREQ_sum"),
+    ("mean HBM write latency, cycles", "TCC_EA0_WRREQ_LEVEL_sum", "TCC_EA0_WRREQ_sum"),
+    ("waves waiting on any instruction per wave cycle", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+    ("L2 hit rate", "TCC_HIT_sum", "TCC_REQ_sum"),
+]
+
+
+def counter_summary(op_log, dirs):
+    """Markdown counter summary of a --kernel-op run: per counter, the median
+    over the kernel's dispatches, the value per unit of work (wave instructions
+    x 64 per element for SQ_INSTS_*), and the means over the fastest and the
+    slowest third of the dispatches (durations from the counter runs' own
+    timestamps), to show what separates slow launches from fast ones."""
+    import csv
+    import glob
+    line = None
+    with open(op_log) as fh:
+        for ln in fh:
+            if ln.startswith("{") and '"kernel_op"' in ln:
+                line = json.loads(ln)
+    if line is None:
+        raise SystemExit(f"no --kernel-op line in {op_log}")
+    pat, units, unit = line["kernel"], line["units_per_launch"], line["unit"]
+    per, dur, passes, name = {}, {}, [], None
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        ctrs = set()
+        for f in files:
+            for row in csv.DictReader(open(f)):
+                if pat not in row["Kernel_Name"]:
+                    continue
+                name = name or row["Kernel_Name"]
+                key = (d, row["Dispatch_Id"])
+                c = row["Counter_Name"]
+                ctrs.add(c)
+                per.setdefault(key, {})
+                per[key][c] = per[key].get(c, 0.0) + float(row["Counter_Value"])
+                t = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+                if t > 0:
+                    dur[key] = t
+        passes.append(sorted(ctrs))
+    if not per:
+        raise SystemExit(f"no dispatch of {pat!r} in the counter output")
+    med = lambda v: sorted(v)[len(v) // 2]
+    mean = lambda v: sum(v) / len(v) if v else float("nan")
+    counters = sorted({c for v in per.values() for c in v})
+    short = (name or pat).replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+    out = [f"# Counters of `{short}`", "",
+           f"Workload: {line['what']}; {units:,} {unit}s per launch; {line['ms_per_launch'] * 1e3:.2f} us "
+           f"per launch by HIP events over the profiled run's timed launches ({line['steps']} after "
+           f"{line['warmup']} warm-up; counter collection serialises launches, so this is not "
+           f"the kernel's time). Durations below are the dispatches' own timestamps.", "",
+           "| counter | dispatches | median per launch | per " + unit + " | mean, fastest third | "
+           "mean, slowest third |", "|---|---|---|---|---|---|"]
+    ratio_rows = []
+    for c in counters:
+        keys = [k for k, v in per.items() if c in v]
+        vals = [per[k][c] for k in keys]
+        timed_keys = sorted((k for k in keys if k in dur), key=lambda k: dur[k])
+        third = max(1, len(timed_keys) // 3)
+        fast = [per[k][c] for k in timed_keys[:third]]
+        slow = [per[k][c] for k in timed_keys[-third:]]
+        pu = med(vals) * (64 if c.startswith("SQ_INSTS_") else 1) / units
+        out.append(f"| `{c}` | {len(vals)} | {med(vals):.6g} | {pu:.4g} | {mean(fast):.6g} | "
+                   f"{mean(slow):.6g} |")
+    out.append("")
+    dur_rows = []
+    for ps in passes:
+        keys = sorted((k for k in dur if all(c in per[k] for c in ps)), key=lambda k: dur[k])
+        if keys:
+            third = max(1, len(keys) // 3)
+            dur_rows.append((", ".join(f"`{c}`" for c in ps), len(keys), med([dur[k] for k in keys]),
+                             mean([dur[k] for k in keys[:third]]),
+                             mean([dur[k] for k in keys[-third:]])))
+    out += ["Launch durations under each counter pass (us):", "",
+            "| pass | dispatches | median | mean, fastest third | mean, slowest third |",
+            "|---|---|---|---|---|"]
+    out += [f"| {p} | {n} | {m:.2f} | {f:.2f} | {s_:.2f} |" for p, n, m, f, s_ in dur_rows]
+    out.append("")
+    for c in ("GRBM_COUNT", "GRBM_GUI_ACTIVE"):
+        # counted cycles per us of launch: a falling rate in longer launches
+        # means the clock, not the work, changed between them
+        keys = sorted((k for k, v in per.items() if c in v and k in dur), key=lambda k: dur[k])
+        if len(keys) < 3:
+            continue
+        third = len(keys) // 3
+        rate = [per[k][c] / dur[k] for k in keys]
+        ds = [dur[k] for k in keys]
+        ratio_rows.append(f"| `{c}` per us of launch (rate of the counted clock; Pearson r "
+                          f"with duration {_pearson(ds, rate):+.2f}, of the count itself "
+                          f"{_pearson(ds, [per[k][c] for k in keys]):+.2f}) | `{c}` / duration | "
+                          f"{med(rate):.5g} | {mean(rate[:third]):.5g} | {mean(rate[-third:]):.5g} |")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
+        # busy cycles are counted per SIMD: 1024 SIMDs, clocked at 2.4 GHz
+        keys = sorted((k for k, v in per.items() if "SQ_VALU_MFMA_BUSY_CYCLES" in v and k in dur),
+                      key=lambda k: dur[k])
+        if keys:
+            third = max(1, len(keys) // 3)
+            fr = [per[k]["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * dur[k] * 2400.0) for k in keys]
+            ratio_rows.append(f"| MFMA busy per SIMD cycle (1024 SIMDs at 2.4 GHz over the "
+                              f"launch) | `SQ_VALU_MFMA_BUSY_CYCLES` / (1024 x 2400 x us) | "
+                              f"{med(fr):.4g} | {mean(fr[:third]):.4g} | {mean(fr[-third:]):.4g} |")
+    for label, a, b in COUNTER_RATIOS:
+        keys = [k for k, v in per.items() if a in v and b in v and v[b] > 0]
+        if not keys:
+            continue
+        r = [per[k][a] / per[k][b] for k in keys]
+        tk = sorted((k for k in keys if k in dur), key=lambda k: dur[k])
+        third = max(1, len(tk) // 3)
+        ratio_rows.append(f"| {label} | `{a}` / `{b}` | {med(r):.4g} | "
+                          f"{mean([per[k][a] / per[k][b] for k in tk[:third]]):.4g} | "
+                          f"{mean([per[k][a] / per[k][b] for k in tk[-third:]]):.4g} |")
+    if ratio_rows:
+        out += ["| ratio | counters | median | mean, fastest third | mean, slowest third |",
+                "|---|---|---|---|---|"] + ratio_rows + [""]
+    op = line["kernel_op"]
+    out += ["Commands (from the repository root, TMPDIR=/tmp; one rocprofv3 run per counter "
+            "pass):", "", "```"]
+    for i, ps in enumerate(passes):
+        out.append(f"rocprofv3 --pmc {' '.join(ps)} --kernel-trace -d <dir{i + 1}> -o run "
+                   f"--output-format csv -- python3 bench.py --kernel-op {op} --steps "
+                   f"{line['steps']} --warmup {line['warmup']} > <op_log{i + 1}>")
+    out += [f"python3 bench.py --counter-summary <op_log1> "
+            + " ".join(f"<dir{i + 1}>" for i in range(len(passes))), "```"]
+    print("\n".join(out))
+
+
+def _pmc_rows(d, counter, per_us=False):
+    """{kernel name: [per-dispatch counter value]} from a rocprofv3 --pmc CSV
+    directory; with per_us, each value divided by its dispatch's duration (us)."""
     import csv
     import glob
     out = {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-        per = {}
+        per, dur = {}, {}
         with open(f) as fh:
             for row in csv.DictReader(fh):
                 if row["Counter_Name"] != counter:
                     continue
                 key = (row["Kernel_Name"], row["Dispatch_Id"])
                 per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
-        for (k, _), v in per.items():
-            out.setdefault(k, []).append(v)
+                dur[key] = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+        for key, v in per.items():
+            if per_us:
+                if dur[key] <= 0:
+                    continue
+                v /= dur[key]
+            out.setdefault(key[0], []).append(v)
     return out
 
 
@@ -916,12 +1144,10 @@ def pmc_summary(dirs):
         "",
     ]
     if len(dirs) > 2:
-        busy = _pmc_rows(dirs[2], "SQ_VALU_MFMA_BUSY_CYCLES")
-        cu = _pmc_rows(dirs[2], "SQ_BUSY_CU_CYCLES")
-        _, b = pick(busy, ROT_INSTANCE)
-        _, c = pick(cu, ROT_INSTANCE)
-        lines += [f"MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES = "
-                  f"{med(b) / max(med(c), 1):.4f} (median dispatch).", ""]
+        # busy cycles are counted per SIMD: 1024 SIMDs at 2.4 GHz over the launch
+        _, b = pick(_pmc_rows(dirs[2], "SQ_VALU_MFMA_BUSY_CYCLES", per_us=True), ROT_INSTANCE)
+        lines += [f"MFMA busy per SIMD cycle: SQ_VALU_MFMA_BUSY_CYCLES / (1024 x 2400 x launch "
+                  f"us) = {med(b) / (1024 * 2400.0):.4f} (median dispatch).", ""]
         # instruction mix: wave instructions per 64 elements (one per lane
         # and element for a VALU op that every lane issues once per element)
         mix = []
@@ -941,7 +1167,7 @@ def pmc_summary(dirs):
         "-- python3 bench.py --steps 3 --warmup 1 --no-extras --no-cpu",
         "rocprofv3 --pmc WRITE_SIZE --kernel-trace -d <write_dir> -o run --output-format csv "
         "-- python3 bench.py --steps 3 --warmup 1 --no-extras --no-cpu",
-        "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
+        "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
         "SQ_INSTS_LDS SQ_INSTS_SALU --kernel-trace -d <mfma_dir> -o run --output-format csv "
         "-- python3 bench.py --steps 3 --warmup 1 --no-extras --no-cpu",
         "python3 bench.py --pmc-summary <fetch_dir> <write_dir> <mfma_dir>",
@@ -1020,6 +1246,9 @@ def main():
     if args.pmc_summary:
         pmc_summary(args.pmc_summary)
         return
+    if args.counter_summary:
+        counter_summary(args.counter_summary[0], args.counter_summary[1:])
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on one MI355X and has no "
               "multi-GPU mode (rows shard with no communication); run with --gpus 1",
@@ -1031,6 +1260,9 @@ def main():
 
     fp4.lib()  # fails loudly if the HIP library is not built
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.kernel_op:
+        kernel_op(torch, fp4, inputs, args)
+        return
     fn = {"c4": bench_c4, "c1": bench_c1, "c2": bench_c2, "c3": bench_c3,
           "c5": bench_c5}[args.workload]
     res, x_host, perm = fn(torch, fp4, inputs, args)
