@@ -54,10 +54,11 @@ ROT_SOURCES = ["block_scaled_fp4_absmax_amd/csrc/rotate_kernels.hpp",
                "block_scaled_fp4_absmax_amd/csrc/launch.hpp"]
 TRAFFIC_FILE = "profiles/traffic_perm_rotate_quantize_c4.md"
 COPY_BYTES = 1 << 30  # torch device copy in device_copy(): 1 GiB read, 1 GiB written
-# steps of the informational rows: the first hundred or so launches on freshly
-# allocated output buffers run up to 30% slower on MI355X, so each row warms up
-# longer than a few launches before it is timed
-ROW_STEPS, ROW_WARMUP = 50, 30
+# steps of the informational rows. On MI355X a kernel reaches its sustained
+# speed only after some 25 ms of its own launches (the first launches of a
+# new kernel, or on freshly allocated buffers, run up to 30% slower), so each
+# row warms up for ROW_WARM_MS of its own calls before it is timed
+ROW_STEPS, ROW_WARMUP, ROW_WARM_MS = 50, 30, 40.0
 
 
 def log(msg):
@@ -65,11 +66,19 @@ def log(msg):
 
 
 def rot_source_hash():
+    """sha256 (first 16 hex) of the fused kernel's sources with comments and
+    blank lines removed: a change to the code invalidates the committed
+    counters, a change to a comment does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ROT_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for ln in text.splitlines():
+            ln = re.sub(r"//.*", "", ln).rstrip()
+            if ln:
+                h.update(ln.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -114,16 +123,21 @@ def parse():
 
 
 _SETTLE = {}
+SETTLE_REST_S = float(os.environ.get("FP4_BENCH_REST_S", "0.5"))
 
 
-def settle(torch, ms=30.0):
-    """Keep the GPU busy for about ms milliseconds (device fills of a 256 MiB
-    buffer, untimed) and wait: after host-side work the GPU idles, and on
+def settle(torch, ms=30.0, rest_s=SETTLE_REST_S):
+    """Let the GPU rest for rest_s seconds, then keep it busy for about ms
+    milliseconds (device fills of a 256 MiB buffer, untimed) and wait. On
     MI355X the first ~10 ms of work after an idle second run up to 30% slower
-    while the clocks come back up. Settling first makes a timed region see the
-    clocks of sustained operation."""
+    while the clocks come back up, and kernels timed right after long
+    stretches of other full-bandwidth work run up to 15% slower than the same
+    kernels on their own. The rest and the fills make every timed region start
+    from the same state: the clocks of sustained operation, no backlog."""
     if "buf" not in _SETTLE:
         _SETTLE["buf"] = torch.empty(1 << 26, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    time.sleep(rest_s)
     t0 = time.perf_counter()
     while (time.perf_counter() - t0) * 1e3 < ms:
         for _ in range(16):  # about 1 ms of back-to-back fills per wait
@@ -131,13 +145,19 @@ def settle(torch, ms=30.0):
         torch.cuda.synchronize()
 
 
-def timed(torch, fn, steps, warmup):
+def timed(torch, fn, steps, warmup, warm_ms=0.0):
     """ms per call of fn(i), measured with events on the current stream, after
-    settle() and the warm-up calls."""
+    settle() and the warm-up calls: warmup calls, continued until the warm-up
+    has run for at least warm_ms milliseconds."""
     settle(torch)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for _ in range(8):
+            fn(warmup)
+        torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
@@ -213,7 +233,7 @@ def device_copy(torch):
     """Reference: torch's device-to-device copy of 1 GiB (read + write bytes / time)."""
     src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
     dst = torch.empty_like(src)
-    ms = timed(torch, lambda i: dst.copy_(src), 10, 2)
+    ms = timed(torch, lambda i: dst.copy_(src), 10, 2, ROW_WARM_MS)
     return {"bytes_moved": 2 << 30, "ms": round(ms, 4), "GBps": round(2 * (1 << 30) / ms / 1e6, 1)}
 
 
@@ -310,6 +330,9 @@ def bench_c4(torch, fp4, inputs, args):
     log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
     ms = timed(torch, step, args.steps, args.warmup)
     dist = step_distribution(torch, step, 200)
+    # the same step at its sustained speed: 500 steps timed after warm-up steps
+    # have run for ROW_WARM_MS (informational; value keeps the protocol above)
+    sustained_us = timed(torch, step, 500, args.warmup, ROW_WARM_MS) * 1e3
     elems = rows * cols
     value = elems * 2 / (ms * 1e-3) / 1e9
     achieved = elems * B_MX / (ms * 1e-3) / 1e9
@@ -319,7 +342,8 @@ def bench_c4(torch, fp4, inputs, args):
     c_pl, s_pl, _ = fp4.quantize(xs[0], fp4.MXFP4)
     q_plain = sqnr_db(torch, xs[0].float(), fp4.dequantize(c_pl, s_pl, fp4.MXFP4).float())
 
-    extras = {"step_us_p10_p50_p90": dist,
+    extras = {"step_us_p10_p50_p90": dist, "step_us_sustained": round(sustained_us, 2),
+              "sustained_frac_hbm": round(elems * B_MX / sustained_us / 1e3 / HBM_PEAK_GBS, 4),
               "calibration_ms": round(calib_ms, 3), "channel_energy_ms": round(e_ms, 4),
               "sqnr_db_plain_mxfp4": round(q_plain, 3), "device_copy": device_copy(torch)}
     if not args.no_extras:
@@ -370,19 +394,19 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
         return lambda i: ps[i % n].run()
 
     ms = timed(torch, per_copy(lambda k: fp4.quantize(xs[k], fp4.MXFP4, codes=codes[k],
-                                                      scales=scales[k], prepare=True)), ROW_STEPS, ROW_WARMUP)
+                                                      scales=scales[k], prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxfp4_plain_quantize"] = gbs(ms, el, B_MX)
     ms = timed(torch, per_copy(lambda k: fp4.rotate_quantize(xs[k], None, 32, codes=codes[k],
                                                              scales=scales[k], prepare=True)),
-               ROW_STEPS, ROW_WARMUP)
+               ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxfp4_hadamard_only"] = gbs(ms, el, B_MX)
     outb = torch.empty_like(xs[0])
     ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], scales[k], fp4.MXFP4, out=outb,
-                                                        prepare=True)), ROW_STEPS, ROW_WARMUP)
+                                                        prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxfp4_dequantize"] = gbs(ms, el, B_MX)
     ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], scales[k], fp4.MXFP4, perm=perm,
                                                         hadamard=32, out=outb, prepare=True)),
-               ROW_STEPS, ROW_WARMUP)
+               ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxfp4_dequantize_unrotate"] = gbs(ms, el, B_MX)
 
     # NVFP4 + RaZeR after the two-level rotation on the same tensor (permutation
@@ -396,13 +420,13 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
             xs[k], perm16, 16, codes=codes[k], scales=s16[k], fmt=fp4.NVFP4, mode=fp4.RAZER,
             tensor_scale=t16[k], scale_given=given, prepare=True))
 
-    ms = timed(torch, nv_rot(False), ROW_STEPS, ROW_WARMUP)
+    ms = timed(torch, nv_rot(False), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_nvfp4_razer_perm_h16_with_amax"] = gbs(ms, el, B_NV + 2)
-    ms = timed(torch, nv_rot(True), ROW_STEPS, ROW_WARMUP)
+    ms = timed(torch, nv_rot(True), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_nvfp4_razer_perm_h16_scale_given"] = gbs(ms, el, B_NV)
     ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], s16[k], fp4.NVFP4, fp4.RAZER,
                                                         t16[k], perm=perm16, hadamard=16,
-                                                        out=outb, prepare=True)), ROW_STEPS, ROW_WARMUP)
+                                                        out=outb, prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_nvfp4_razer_dequantize_unrotate"] = gbs(ms, el, B_NV)
     xf = xs[0].float()
     for name, (pm, had) in {"perm_h16": (perm16, 16), "h16": (None, 16),
@@ -414,15 +438,15 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
 
     # MXINT4 (two's complement k/4 elements, E8M0 scale) on the same tensor
     ms = timed(torch, per_copy(lambda k: fp4.quantize(xs[k], fp4.MXINT4, codes=codes[k],
-                                                      scales=scales[k], prepare=True)), ROW_STEPS, ROW_WARMUP)
+                                                      scales=scales[k], prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxint4_plain_quantize"] = gbs(ms, el, B_MX)
     ms = timed(torch, per_copy(lambda k: fp4.rotate_quantize(xs[k], perm, 32, codes=codes[k],
                                                              scales=scales[k], fmt=fp4.MXINT4,
-                                                             prepare=True)), ROW_STEPS, ROW_WARMUP)
+                                                             prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxint4_perm_h32_quantize"] = gbs(ms, el, B_MX)
     ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], scales[k], fp4.MXINT4, perm=perm,
                                                         hadamard=32, out=outb, prepare=True)),
-               ROW_STEPS, ROW_WARMUP)
+               ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxint4_dequantize_unrotate"] = gbs(ms, el, B_MX)
     for name, (pm, had) in {"perm_h32": (perm, 32), "h32": (None, 32),
                             "plain": (None, 0)}.items():
@@ -441,10 +465,10 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     md = macro.to("cuda")
     zs = [torch.empty_like(xs[0]) for _ in range(n)]
     ms = timed(torch, per_copy(lambda k: fp4.apply_channel_rotation(xs[k], md, perm, out=zs[k],
-                                                                    prepare=True)), ROW_STEPS, ROW_WARMUP)
+                                                                    prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_givens_layers_apply"] = gbs(ms, el, 4)
     ms = timed(torch, per_copy(lambda k: fp4.apply_channel_rotation(xs[k], md, None, out=zs[k],
-                                                                    prepare=True)), ROW_STEPS, ROW_WARMUP)
+                                                                    prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_givens_layers_apply_no_perm"] = gbs(ms, el, 4)
     t0 = time.perf_counter()
     R, rloss = fp4.calibrate_block_rotation(zs[0][:256], None, iters=30, angles=32)
@@ -453,10 +477,10 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     ident = torch.arange(cols, dtype=torch.int32, device="cuda")
     ms = timed(torch, per_copy(lambda k: fp4.rotate_quantize_r(zs[k], ident, rt, codes=codes[k],
                                                                scales=scales[k], prepare=True)),
-               ROW_STEPS, ROW_WARMUP)
+               ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxfp4_learned_r_quantize"] = gbs(ms, el, B_MX)
     ms = timed(torch, per_copy(lambda k: fp4.dequantize_r(codes[k], scales[k], ident, rt, out=outb,
-                                                          prepare=True)), ROW_STEPS, ROW_WARMUP)
+                                                          prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxfp4_learned_r_dequantize"] = gbs(ms, el, B_MX)
     xf, zf = xs[0].float(), zs[0].float()
     c, sc, _ = fp4.rotate_quantize_r(zs[0], ident, rt)
@@ -486,7 +510,7 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     x3 = x3s[0]
     r3, k3 = x3.shape
     p3 = [fp4.rotate_quantize(t, None, 32, prepare=True) for t in x3s]
-    ms = timed(torch, lambda i: p3[i % len(p3)].run(), ROW_STEPS, ROW_WARMUP)
+    ms = timed(torch, lambda i: p3[i % len(p3)].run(), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c3_mxfp4_h32_quantize"] = gbs(ms, r3 * k3, B_MX)
     del p3, x3s
     x3f = x3.float()
@@ -526,18 +550,18 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     q_amax = plan(lambda k: fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[k],
                                          scale_given=False, codes=cs[k], scales=ss[k],
                                          prepare=True))
-    ms = timed(torch, q_amax, 2 * ROW_STEPS, ROW_WARMUP)
+    ms = timed(torch, q_amax, 2 * ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c2_nvfp4_razer_quantize_with_amax"] = gbs(ms, el2, B_NV + 2)
     xh = fp4.dequantize(cs[0], ss[0], fp4.NVFP4, fp4.RAZER, tss[0])
     out["c2_sqnr_db_razer"] = round(sqnr_db(torch, ys[0].float(), xh.float()), 3)
     q_razer = plan(lambda k: fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[k],
                                           codes=cs[k], scales=ss[k], prepare=True))
-    ms = timed(torch, q_razer, 2 * ROW_STEPS, ROW_WARMUP)
+    ms = timed(torch, q_razer, 2 * ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c2_nvfp4_razer_quantize_scale_given"] = gbs(ms, el2, B_NV)
     graph_row("c2_nvfp4_razer_quantize_scale_given", q_razer, B_NV)
     q_plain = plan(lambda k: fp4.quantize(ys[k], fp4.NVFP4, fp4.PLAIN, tensor_scale=tss[k],
                                           codes=cs[k], scales=ss[k], prepare=True))
-    ms = timed(torch, q_plain, 2 * ROW_STEPS, ROW_WARMUP)
+    ms = timed(torch, q_plain, 2 * ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c2_nvfp4_plain_quantize_scale_given"] = gbs(ms, el2, B_NV)
     graph_row("c2_nvfp4_plain_quantize_scale_given", q_plain, B_NV)
     for k in range(m):
@@ -545,12 +569,12 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     ob = torch.empty_like(ys[0])
     dq = plan(lambda k: fp4.dequantize(cs[k], ss[k], fp4.NVFP4, fp4.RAZER, tss[k], out=ob,
                                        prepare=True))
-    ms = timed(torch, dq, 2 * ROW_STEPS, ROW_WARMUP)
+    ms = timed(torch, dq, 2 * ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c2_nvfp4_razer_dequantize"] = gbs(ms, el2, B_NV)
     graph_row("c2_nvfp4_razer_dequantize", dq, B_NV)
     ms = timed(torch, plan(lambda k: fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER_W,
                                                   tensor_scale=tss[k], codes=cs[k], scales=ss[k],
-                                                  prepare=True)), 2 * ROW_STEPS, ROW_WARMUP)
+                                                  prepare=True)), 2 * ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c2_nvfp4_razer_w_quantize_scale_given"] = gbs(ms, el2, B_NV)
     cw, sw, tw = fp4.quantize(ys[0], fp4.NVFP4, fp4.RAZER_W)
     xw = fp4.dequantize(cw, sw, fp4.NVFP4, fp4.RAZER_W, tw)
@@ -582,7 +606,7 @@ def c1_rows(torch, fp4, inputs):
     d = lambda i: pd.run()
     res = {}
     for name, fn in (("quantize", q), ("dequantize", d)):
-        ms = timed(torch, fn, 200, 20)
+        ms = timed(torch, fn, 200, 20, ROW_WARM_MS)
         us = graph_us(torch, fn, calls=50)
         res[name] = {"us": round(ms * 1e3, 2), "graph_us_per_call": round(us, 2),
                      "graph_algorithmic_GBps": round(el * B_MX / us / 1e3, 1)}
@@ -636,7 +660,7 @@ def c5_rows(torch, fp4, inputs, steps=5, warmup=3, razer_w=False):
                           ("quantize_scale_given", quant_given, B_NV),
                           ("dequantize", dequant, B_NV),
                           ("round_trip", round_trip, 2 * B_NV + 2)):
-        ms = timed(torch, fn, steps, warmup)
+        ms = timed(torch, fn, steps, warmup, ROW_WARM_MS)
         res[name] = {"ms": round(ms, 4), "input_GBps": round(el * 2 / ms / 1e6, 1),
                      "algorithmic_GBps": round(el * per / ms / 1e6, 1),
                      "frac_hbm": round(el * per / ms / 1e6 / HBM_PEAK_GBS, 4)}
@@ -682,7 +706,7 @@ def gemm_rows(torch, fp4, fmt):
         sb = torch.randint(lo, hi, (n, k // blk), dtype=torch.uint8, device="cuda", generator=g)
         c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
         pg = fp4.gemm(a, sa, b, sb, out=c, prepare=True, **kw)
-        ms = timed(torch, lambda i: pg.run(), 10, 2)
+        ms = timed(torch, lambda i: pg.run(), 10, 2, ROW_WARM_MS)
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         by = (m + n) * (k / 2 + k / blk) + 2 * m * n
         rows[f"{m}x{n}x{k}"] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
@@ -1173,7 +1197,8 @@ def pmc_summary(dirs):
         "python3 bench.py --pmc-summary <fetch_dir> <write_dir> <mfma_dir>",
         "```",
         "",
-        "Values read by bench.py (source_hash: sha256 of the kernel sources, first 16 hex):",
+        "Values read by bench.py (source_hash: sha256 of the kernel sources without comments, "
+        "first 16 hex):",
         "",
         f"- source_hash: `{rot_source_hash()}`",
         f"- traffic_bytes_per_launch: {int(round(rd + wr))}",

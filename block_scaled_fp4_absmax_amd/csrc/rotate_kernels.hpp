@@ -271,8 +271,9 @@ struct PermCtx {
 template <int G, uint32_t kOff, int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot, class Ctx>
 __device__ __forceinline__ void perm_row(const Ctx& c, const uint8_t* buf, int32_t r) {
     // Cache policy of the code stores, measured on MI355X at 16384 x 8192:
-    // plain write-back stores ran the MX formats 6% faster than nontemporal
-    // ones (55.9 against 59.8 us), and NVFP4 2% slower (65.2 against 63.7).
+    // plain write-back stores ran the MX formats faster than nontemporal ones
+    // (MXFP4 55.9 against 59.8 us, MXINT4 60.8 against 62.4), and NVFP4 2%
+    // slower (65.2 against 63.7).
     constexpr int kCodeAux = kFmt == kFmtNv ? kNt : 0;
     const RotGeom& g = c.g;
     const RowRsrc q = row_rsrc<kRot>(c.x, c.codes, c.scales, c.rot, r, g);
