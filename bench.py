@@ -638,32 +638,44 @@ def c5_rows(torch, fp4, inputs, steps=5, warmup=3, razer_w=False):
     n = len(xs)
     mode = fp4.RAZER_W if razer_w else fp4.RAZER
 
-    def quant_amax(i):
-        for k in range(n):
-            fp4.quantize(xs[k], fp4.NVFP4, mode, tensor_scale=ts[k], scale_given=False,
-                         codes=cs[k], scales=ss[k])
+    def layer(make):
+        """One pass over the seven tensors from prepared calls."""
+        ps = [make(k) for k in range(n)]
 
-    def quant_given(i):
-        for k in range(n):
-            fp4.quantize(xs[k], fp4.NVFP4, mode, tensor_scale=ts[k], codes=cs[k], scales=ss[k])
+        def run(i):
+            for p in ps:
+                p.run()
+        return run
 
-    def dequant(i):
-        for k in range(n):
-            fp4.dequantize(cs[k], ss[k], fp4.NVFP4, mode, ts[k], out=outs[k])
+    def quant(m, given):
+        return layer(lambda k: fp4.quantize(xs[k], fp4.NVFP4, m, tensor_scale=ts[k],
+                                            scale_given=given, codes=cs[k], scales=ss[k],
+                                            prepare=True))
+
+    quant_amax, quant_given = quant(mode, False), quant(mode, True)
+    dequant = layer(lambda k: fp4.dequantize(cs[k], ss[k], fp4.NVFP4, mode, ts[k], out=outs[k],
+                                             prepare=True))
 
     def round_trip(i):
         quant_amax(i)
         dequant(i)
 
     res = {"elements": el}
-    for name, fn, per in (("quantize_with_amax", quant_amax, B_NV + 2),
-                          ("quantize_scale_given", quant_given, B_NV),
-                          ("dequantize", dequant, B_NV),
-                          ("round_trip", round_trip, 2 * B_NV + 2)):
+
+    def row(name, fn, per):
         ms = timed(torch, fn, steps, warmup, ROW_WARM_MS)
         res[name] = {"ms": round(ms, 4), "input_GBps": round(el * 2 / ms / 1e6, 1),
                      "algorithmic_GBps": round(el * per / ms / 1e6, 1),
                      "frac_hbm": round(el * per / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+    row("quantize_with_amax", quant_amax, B_NV + 2)
+    row("quantize_scale_given", quant_given, B_NV)
+    row("dequantize", dequant, B_NV)
+    row("round_trip", round_trip, 2 * B_NV + 2)
+    if not razer_w:
+        # the same quantize passes in plain NVFP4: what RaZeR's choice costs
+        row("plain_quantize_with_amax", quant(fp4.PLAIN, False), B_NV + 2)
+        row("plain_quantize_scale_given", quant(fp4.PLAIN, True), B_NV)
     round_trip(0)
     torch.cuda.synchronize()
     num = den = 0.0
