@@ -62,7 +62,8 @@ def _check(orc, x, macro, perm, got):
 
 @pytest.mark.parametrize("rows,cols,use_perm", [(3, 96, True), (37, 2080, True),
                                                 (1537, 8192, True), (5, 16384, False),
-                                                (2500, 1024, False)])
+                                                (7, 16384, True), (2500, 1024, False),
+                                                (2500, 1024, True)])
 def test_random_layers(orc, rows, cols, use_perm):
     note(f"case: Givens layers, random disjoint pairs, {rows}x{cols} perm={use_perm}")
     x = inputs.gen_c3(rows=rows, cols=cols)
@@ -71,6 +72,34 @@ def test_random_layers(orc, rows, cols, use_perm):
     md = macro.to("cuda")
     pt = None if perm is None else torch.from_numpy(perm).cuda()
     z = fp4.apply_channel_rotation(to_dev(x), md, pt)
+    sync()
+    _check(orc, x, macro, perm, bf16_bits(z))
+
+
+def test_gather_with_repeats(orc):
+    """An index vector that is not a permutation (repeated and missing
+    channels) is a gather: every output channel reads its own source."""
+    note("case: Givens layers after a gather with repeats, 37x2080")
+    rows, cols = 37, 2080
+    x = inputs.gen_c3(rows=rows, cols=cols)
+    idx = np.random.default_rng(11).integers(0, cols, cols).astype(np.int32)
+    macro = _random_layers(cols, 4, 200, 12)
+    z = fp4.apply_channel_rotation(to_dev(x), macro.to("cuda"), torch.from_numpy(idx).cuda())
+    sync()
+    _check(orc, x, macro, idx, bf16_bits(z))
+
+
+@pytest.mark.parametrize("n_layers,per_layer", [(1, 0), (8, 500)])
+def test_rotation_table_sizes(orc, n_layers, per_layer):
+    """No rotation at all (a pure permutation), and 4000 rotations over
+    16384 columns, whose tables leave no room for the compact kernel (the
+    row-wide kernel runs them)."""
+    rows, cols = 9, 16384
+    note(f"case: Givens layers, {n_layers} x {per_layer} rotations, {rows}x{cols} with perm")
+    x = inputs.gen_c4(rows=rows, cols=cols)
+    perm = np.random.default_rng(5).permutation(cols).astype(np.int32)
+    macro = _random_layers(cols, n_layers, per_layer, 13)
+    z = fp4.apply_channel_rotation(to_dev(x), macro.to("cuda"), torch.from_numpy(perm).cuda())
     sync()
     _check(orc, x, macro, perm, bf16_bits(z))
 
