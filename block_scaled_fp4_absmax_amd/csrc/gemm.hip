@@ -45,19 +45,21 @@ typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // LDS byte offset of 16-byte chunk c of row r in a stage of KB K values
-// (KB / 32 chunks per row). KB = 128: chunk c (0..3) sits in slot
-// c ^ ((r / 2) % 4); a write pass of 8 lanes covers two rows (slots 0..3 of
-// each, 128 contiguous bytes), a read pass of 8 lanes takes one logical chunk
-// of 8 consecutive rows, which the swizzle spreads over all four slots of
-// both bank halves, so neither conflicts on 32 four-byte banks. KB = 256:
-// chunk c (0..7) in slot c ^ (r % 8), one row per write pass, eight rows
-// over the eight slots per read pass.
+// (KB / 32 chunks per row). gfx950's LDS has 64 four-byte banks (256 bytes):
+// a 16-byte access pass of 16 lanes is free of conflicts when its 16 chunks
+// fall on 16 different 16-byte bank groups. KB = 256 (128-byte rows, two rows
+// per bank cycle): chunk c (0..7) sits in slot c ^ ((r / 2) % 8), so a read
+// pass (one logical chunk of 16 consecutive rows) covers both row parities
+// times eight slots, and a write pass (two whole rows) covers them too.
+// KB = 128 (64-byte rows, four per bank cycle): slot c ^ ((r / 4) % 4). The
+// earlier XOR by r % 8 (or (r / 2) % 4), right for 32 banks, measured 0.35
+// bank-conflict cycles per LDS-active cycle here; this one 0.
 template <int KB>
 __device__ __forceinline__ uint32_t lds_off(uint32_t r, uint32_t c) {
   if constexpr (KB == 128)
-    return r * 64u + 16u * (c ^ ((r >> 1) & 3u));
+    return r * 64u + 16u * (c ^ ((r >> 2) & 3u));
   else
-    return r * 128u + 16u * (c ^ (r & 7u));
+    return r * 128u + 16u * (c ^ ((r >> 1) & 7u));
 }
 
 struct GemmArgs {
@@ -314,9 +316,9 @@ struct SkinnyStep {
 };
 
 // LDS byte offset of 16-byte chunk j (0..7) of row r in a 32 x 128-byte
-// operand piece.
+// operand piece (slot j ^ ((r / 2) % 8): see lds_off for the 64 banks).
 __device__ __forceinline__ uint32_t skinny_off(uint32_t r, uint32_t j) {
-  return 128u * r + 16u * (j ^ (r & 7u));
+  return 128u * r + 16u * (j ^ ((r >> 1) & 7u));
 }
 
 __device__ __forceinline__ void wave_sync() {

@@ -40,10 +40,11 @@ constexpr int kBK = 64;         // K elements per stage
 constexpr int kRowB = 2 * kBK;  // bf16 bytes per row per stage in LDS
 
 // LDS byte offset of 16-byte chunk c (0..7, eight elements) of row r: slot
-// c ^ (r % 8), so the lane reads of one chunk of 8 consecutive rows fall on
-// eight different slots (all 32 banks).
+// c ^ ((r / 2) % 8). gfx950's LDS has 64 four-byte banks, two 128-byte rows
+// per bank cycle, so the lane reads of one chunk of 16 consecutive rows fall
+// on 16 different 16-byte bank groups (both row parities, eight slots).
 __device__ __forceinline__ uint32_t nv_lds_off(uint32_t r, uint32_t c) {
-  return r * kRowB + 16u * (c ^ (r & 7u));
+  return r * kRowB + 16u * (c ^ ((r >> 1) & 7u));
 }
 
 struct NvGemmArgs {
@@ -250,7 +251,7 @@ struct NvSkinnyStep {
 };
 
 __device__ __forceinline__ uint32_t nv_skinny_off(uint32_t r, uint32_t j) {
-  return 128u * r + 16u * (j ^ (r & 7u));
+  return 128u * r + 16u * (j ^ ((r >> 1) & 7u));  // as nv_lds_off
 }
 
 __device__ __forceinline__ void nv_wave_sync() {
