@@ -154,6 +154,80 @@ __device__ __forceinline__ uint32_t absmax16_mixed(const float* y) {
   return __float_as_uint(m);
 }
 
+// ---- the 32-point transform as two 16x16x32 MFMAs (streaming layout) ----
+// A tile is 16 consecutive blocks (1 KB of bf16): lane l = 16 q + n loads the
+// 16 bytes of elements 8q .. 8q + 7 of block n, so the 64 lanes of one load
+// cover the whole kilobyte. As the B operand of v_mfma_f32_16x16x32_bf16
+// (column l % 16, k = 8 (l / 16) .. + 7) that is column n = block n with
+// k = element, so both MFMAs below transform all 16 blocks at once. The C
+// output gives lane l rows 4 (l / 16) .. + 3 of column l % 16; row m of the
+// first A operand is output 8 (m / 4) + m % 4 of H32 and of the second
+// output 8 (m / 4) + 4 + m % 4, so lane (n, q) receives the 8 consecutive
+// outputs 8q .. 8q + 7 of block n, whose codes are 4 consecutive bytes.
+// Operand entries are +-1 (the 1/sqrt(32) follows as one multiply).
+__device__ __forceinline__ void hadamard32_spread_operands(bf16x8_t& a0, bf16x8_t& a1) {
+  const uint32_t lane = threadIdx.x & 63u, m = lane & 15u, k0 = 8u * (lane >> 4);
+  const uint32_t o0 = 8u * (m >> 2) + (m & 3u), o1 = o0 + 4u;
+  uint32_t w0[4], w1[4];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const uint32_t k = k0 + (uint32_t)j;
+    w0[j / 2] = 0x3F803F80u | (((uint32_t)__builtin_popcount(o0 & k) & 1u) << 15) |
+                (((uint32_t)__builtin_popcount(o0 & (k + 1u)) & 1u) << 31);
+    w1[j / 2] = 0x3F803F80u | (((uint32_t)__builtin_popcount(o1 & k) & 1u) << 15) |
+                (((uint32_t)__builtin_popcount(o1 & (k + 1u)) & 1u) << 31);
+  }
+  a0 = __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w0[2], w0[3]});
+  a1 = __builtin_bit_cast(bf16x8_t, u32x4_t{w1[0], w1[1], w1[2], w1[3]});
+}
+
+// y[0..7] = outputs 8q .. 8q + 7 of H32 x / sqrt(32) for the lane's block,
+// from its 8 inputs (elements 8q .. 8q + 7): see hadamard32_spread_operands.
+__device__ __forceinline__ void hadamard32_spread(const bf16x8_t& a0, const bf16x8_t& a1,
+                                                  u32x4_t x, float* y) {
+  const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+  const bf16x8_t b = __builtin_bit_cast(bf16x8_t, x);
+  const f32x4_t c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, z, 0, 0, 0);
+  const f32x4_t c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, z, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    y[i] = c0[i] * kInvSqrt32;
+    y[4 + i] = c1[i] * kInvSqrt32;
+  }
+}
+
+// Largest |y| of 8 fp32 values as a bit pattern, for Hadamard outputs (the
+// reasoning of absmax16_mixed: a non-finite block makes all 8 non-finite).
+__device__ __forceinline__ uint32_t absmax8_mixed(const float* y) {
+  float m = __builtin_fmaxf(__builtin_fabsf(y[0]), __builtin_fabsf(y[1]));
+#pragma unroll
+  for (int k = 2; k < 8; k += 2)
+    m = __builtin_fmaxf(__builtin_fmaxf(m, __builtin_fabsf(y[k])), __builtin_fabsf(y[k + 1]));
+  return __float_as_uint(m);
+}
+
+// Largest of v over the lanes l, l ^ 16, l ^ 32, l ^ 48 (one block of the
+// streaming layout), by gfx950's row and lane-half swaps.
+__device__ __forceinline__ uint32_t max_spread4(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((uint32_t)r[0], (uint32_t)r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)q[0], (uint32_t)q[1]);
+}
+
+// MXFP4 / MXINT4 of the lane's 8 outputs, the block spread over 4 lanes.
+template <bool kFloor, bool kMixed>
+__device__ __forceinline__ void mx_quant8_spread(const float* y, uint32_t& w, uint32_t& byte) {
+  byte = e8m0_byte<kFloor>(max_spread4(kMixed ? absmax8_mixed(y) : absmax_bits<8>(y)));
+  w = byte == 0xFFu ? 0u : cvt8_f32(y, e8m0_operand(byte));
+}
+
+template <bool kFloor, bool kMixed>
+__device__ __forceinline__ void mxint_quant8_spread(const float* y, uint32_t& w, uint32_t& byte) {
+  byte = mxint_byte<kFloor>(max_spread4(kMixed ? absmax8_mixed(y) : absmax_bits<8>(y)));
+  w = byte == 0xFFu ? 0u : int4x8_f32(y, 129 - (int)byte);
+}
+
 // Larger of v in lanes l and l ^ 32 (gfx950 lane-half swap).
 __device__ __forceinline__ uint32_t max_xor32(uint32_t v) {
   const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
