@@ -905,6 +905,12 @@ KERNEL_OPS = {
     "c4_perm_mxfp4": "fused permutation + Hadamard-32 + MXFP4 quantize, 16384x8192 bf16 (c4)",
     "c4_perm_nvfp4_razer": "fused permutation + Hadamard-16 + NVFP4 + RaZeR quantize, tensor "
                            "scale given, 16384x8192 bf16 (c4)",
+    "c4_unrot_mxfp4": "MXFP4 dequantize + inverse Hadamard-32 and permutation, 16384x8192 "
+                      "(c4), bf16 out",
+    "c4_unrot_mxint4": "MXINT4 dequantize + inverse Hadamard-32 and permutation, 16384x8192 "
+                       "(c4), bf16 out",
+    "c4_unrot_nvfp4_razer": "NVFP4 + RaZeR dequantize + inverse Hadamard-16 and permutation, "
+                            "16384x8192 (c4), bf16 out",
     "c2_nvfp4_plain": "NVFP4 quantize, tensor scale given, 4096x4096 bf16 (c2)",
     "c2_nvfp4_razer": "NVFP4 + RaZeR quantize, tensor scale given, 4096x4096 bf16 (c2)",
     "gemm_mxfp4": "MXFP4 x MXFP4 GEMM, m=4096 n=8192 k=8192, bf16 out",
@@ -923,7 +929,7 @@ def kernel_op(torch, fp4, inputs, args):
         xs = dev_copies(torch, x, copies_for(x.nbytes))
         del x
         n = len(xs)
-        nv = op == "c4_perm_nvfp4_razer"
+        nv = op in ("c4_perm_nvfp4_razer", "c4_unrot_nvfp4_razer")
         blk = 16 if nv else 32
         perm = fp4.build_permutation(fp4.channel_energy(xs[0]), blk).cuda()
         codes = [torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda") for _ in range(n)]
@@ -936,9 +942,24 @@ def kernel_op(torch, fp4, inputs, args):
             kw = lambda k: dict(fmt=fp4.NVFP4, mode=fp4.RAZER, tensor_scale=ts[k])
         else:
             kw = lambda k: {}
-        ps = [fp4.rotate_quantize(xs[k], perm, blk, codes=codes[k], scales=scales[k],
-                                  prepare=True, **kw(k)) for k in range(n)]
-        kernel = ROT_KERNEL + ("<2, 1, true, true, false>" if nv else "<2, 0, true, false, false>")
+        if op.startswith("c4_unrot_"):
+            fmt = {"mxfp4": fp4.MXFP4, "mxint4": fp4.MXINT4, "nvfp4_razer": fp4.NVFP4}[op[9:]]
+            mode = fp4.RAZER if nv else fp4.PLAIN
+            outs = [torch.empty_like(xs[k]) for k in range(n)]
+            ps = []
+            for k in range(n):
+                r = fp4.rotate_quantize(xs[k], perm, blk, codes=codes[k], scales=scales[k],
+                                        fmt=fmt, mode=mode)
+                ts_k = r[3] if nv else None
+                ps.append(fp4.dequantize(codes[k], scales[k], fmt, mode, ts_k, perm=perm,
+                                         hadamard=blk, out=outs[k], prepare=True))
+            kernel = "dequant_unrotate_kernel<2, " + {fp4.MXFP4: "0,", fp4.NVFP4: "1,",
+                                                       fp4.MXINT4: "2,"}[fmt]
+        else:
+            ps = [fp4.rotate_quantize(xs[k], perm, blk, codes=codes[k], scales=scales[k],
+                                      prepare=True, **kw(k)) for k in range(n)]
+            kernel = ROT_KERNEL + ("<2, 1, true, true, false>" if nv
+                                   else "<2, 0, true, false, false>")
         units, unit = rows * cols, "element"
     elif op.startswith("c2_"):
         x = inputs.gen_c2()
