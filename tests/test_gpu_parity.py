@@ -293,6 +293,40 @@ def test_rotate_ragged(orc, rows, cols):
     _rot_case(orc, x, perm8, 32)
 
 
+# the Hadamard without a permutation streams tiles of 16 blocks, four lanes per
+# block: strided rows (the non-flat block geometry), block counts that are not
+# a multiple of 16, padded outputs whose guard bytes must stay untouched, both
+# scale rules and both MX element grids
+@pytest.mark.parametrize("fmt", [fp4.MXFP4, fp4.MXINT4])
+@pytest.mark.parametrize("rows,cols,floor_rule", [(7, 96, False), (33, 160, True),
+                                                  (129, 4128, False), (5, 8224, True)])
+def test_rotate_hadamard_strided(orc, fmt, rows, cols, floor_rule):
+    note(f"case: H32 streaming fmt={fmt} strided {rows}x{cols} floor={floor_rule}")
+    x_full = inputs.gen_c3(rows=rows, cols=cols + 40, seed=cols)
+    xt = to_dev(x_full)[:, :cols]
+    x = np.ascontiguousarray(x_full[:, :cols])
+    cbuf = torch.full((rows, cols // 2 + 16), 0xAB, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((rows, cols // 32 + 7), 0xCD, dtype=torch.uint8, device="cuda")
+    rbuf = torch.full((rows, cols + 8), 7.0, dtype=torch.float32, device="cuda")
+    c, s, y = fp4.rotate_quantize(xt, None, 32, floor_rule=floor_rule, fmt=fmt,
+                                  codes=cbuf[:, :cols // 2], scales=sbuf[:, :cols // 32],
+                                  rotated=rbuf[:, :cols])[:3]
+    sync()
+    if fmt == fp4.MXFP4:
+        oc, os_, oy = orc.rotate_quantize(x, None, 32, floor_rule)
+    else:
+        oc, os_, oy = orc.rotate_quantize_mxint4(x, None, 32, floor_rule)
+    r = check_rotated(y.cpu().numpy(), oy, np_u8(c), np_u8(s), oc, os_)
+    note(f"  {r}")
+    assert np.all(np_u8(cbuf)[:, cols // 2:] == 0xAB)
+    assert np.all(np_u8(sbuf)[:, cols // 32:] == 0xCD)
+    assert torch.all(rbuf[:, cols:] == 7.0)
+    # the launch without the rotated output gives the same bytes
+    c2, s2 = fp4.rotate_quantize(xt, None, 32, floor_rule=floor_rule, fmt=fmt)[:2]
+    sync()
+    assert torch.equal(c2, c.contiguous()) and torch.equal(s2, s.contiguous())
+
+
 # rows wider than 16384 take the kernel that stages rows straight into LDS:
 # 6, 7 and 8 MFMA tiles per wave (16416 and 20480 run as 6, with idle tiles),
 # one work-group per CU, row counts below, at and above the grid
