@@ -729,8 +729,32 @@ def gemm_rows(torch, fp4, fmt):
             rows[f"{m}x{n}x{k}"]["graph_us_per_call"] = round(us, 2)
             rows[f"{m}x{n}x{k}"]["graph_frac_mfma_peak"] = round(
                 2.0 * m * n * k / (us * 1e-6) / 1e12 / peak, 4)
+        if not nv and m >= 256:
+            rows[f"{m}x{n}x{k}"]["library"] = library_mx_gemm(torch, a, sa, b, sb, peak)
         del a, sa, b, sb, c
     return rows
+
+
+def library_mx_gemm(torch, a, sa, b, sb, peak):
+    """The same MXFP4 product through torch._scaled_mm (the ROCm math
+    library's block-scaled FP4 GEMM), timed with the same protocol: a
+    reference point for the hand-written kernel, not part of the path. Timing
+    only (the operands are random bytes; the library's scale layout is not
+    checked against ours)."""
+    try:
+        A = a.view(torch.float4_e2m1fn_x2)
+        B = b.view(torch.float4_e2m1fn_x2)
+        SA, SB = sa.view(torch.float8_e8m0fnu), sb.view(torch.float8_e8m0fnu)
+        fn = lambda i: torch._scaled_mm(A, B.t(), SA, SB, out_dtype=torch.bfloat16)
+        fn(0)
+        ms = timed(torch, fn, 10, 2, ROW_WARM_MS)
+    except Exception as ex:  # not available in this torch build
+        return {"error": f"{type(ex).__name__}: {str(ex)[:120]}"}
+    m, k = a.shape[0], 2 * a.shape[1]
+    n = b.shape[0]
+    tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    return {"call": "torch._scaled_mm", "ms": round(ms, 4), "TFLOPs": round(tf, 1),
+            "frac_mfma_peak": round(tf / peak, 4)}
 
 
 def bench_c1(torch, fp4, inputs, args):
