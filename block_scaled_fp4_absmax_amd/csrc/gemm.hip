@@ -265,6 +265,60 @@ __global__ __launch_bounds__(64 * VM * VN) void mx_gemm_kernel(GemmArgs g) {
   tail(s, std::make_integer_sequence<int, kSets - 1>{});
 
   // epilogue: lane (n, h) of tile (i, j) holds column n, rows 8 (e / 4) + 4 h + e % 4
+  if constexpr (kBf16Out && VM == 2 && KB >= BN) {
+    // bf16 through LDS (free after the last stage's barrier): the waves of
+    // row half wm write their tiles into lds_a (wm = 0) or lds_b (wm = 1),
+    // BM / 2 rows of BN bf16, then every thread copies 16-byte pieces of
+    // whole rows out. 16-byte piece p of row rl sits in slot p ^ 4 ((rl / 4)
+    // % 2), so that the two lane halves of a write (rows 4 apart) use
+    // different banks. Needs ld_c % 8 == 0 and a 16-byte aligned C;
+    // otherwise the direct stores below run.
+    const bool via_lds = g.ld_c % 8 == 0 && reinterpret_cast<uintptr_t>(g.c) % 16 == 0;
+    if (via_lds) {
+      constexpr int kHalf = BM / 2;
+      static_assert(2 * kHalf * BN <= 2 * T::kLdsA && 2 * kHalf * BN <= 2 * T::kLdsB,
+                    "a row half of the bf16 tile fits each operand buffer pair");
+      uint8_t* half = wm == 0 ? &lds_a[0][0] : &lds_b[0][0];
+      auto slot = [](uint32_t rl, uint32_t p) { return p ^ (4u * ((rl >> 2) & 1u)); };
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const uint32_t cl = 32u * WN * wn + 32u * j + r;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t rl = 32u * i + 8u * (e / 4) + 4u * h + (e % 4);
+            const uint32_t off = rl * (2u * BN) + 16u * slot(rl, cl / 8u) + 2u * (cl % 8u);
+            *reinterpret_cast<uint16_t*>(half + off) =
+                (uint16_t)(pack_bf16x2(acc[i][j][e], 0.0f) & 0xFFFFu);
+          }
+        }
+      __syncthreads();
+      constexpr int kPieces = BM * BN / 8;  // 16-byte pieces of the tile
+      constexpr int kPpr = BN / 8;          // per row
+#pragma unroll
+      for (int u = 0; u < kPieces / T::kT; ++u) {
+        const uint32_t pc = threadIdx.x + (uint32_t)T::kT * u;
+        const uint32_t row = pc / kPpr, p = pc % kPpr;
+        const uint32_t rl = row % kHalf;
+        const uint8_t* src = (row < (uint32_t)kHalf ? &lds_a[0][0] : &lds_b[0][0]) +
+                             rl * (2u * BN) + 16u * slot(rl, p);
+        const int32_t grow = m0 + (int32_t)row, gcol = n0 + 8 * (int32_t)p;
+        if (grow >= g.m || gcol >= g.n) continue;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src);
+        uint16_t* dst = static_cast<uint16_t*>(g.c) + (int64_t)grow * g.ld_c + gcol;
+        if (gcol + 8 <= g.n) {
+          *reinterpret_cast<u32x4_t*>(dst) = v;
+        } else {
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if (gcol + t < g.n) dst[t] = (uint16_t)(w4[t / 2] >> (16 * (t % 2)));
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < WM; ++i)
 #pragma unroll
