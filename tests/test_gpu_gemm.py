@@ -51,7 +51,7 @@ def _scales_dev(sc, extra):
     return torch.from_numpy(buf).cuda()[:, :nb]
 
 
-def _check(orc, ac, as_, bc, bs, k, bf16=False, pad=0):
+def _check(orc, ac, as_, bc, bs, k, bf16=False, pad=0, out_pad=5):
     m, n = ac.shape[0], bc.shape[0]
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
     if pad:  # code row strides beyond the row (16-byte multiples)
@@ -62,10 +62,12 @@ def _check(orc, ac, as_, bc, bs, k, bf16=False, pad=0):
     else:
         A, B = dev(ac), dev(bc)
     SA, SB = _scales_dev(as_, 4 if pad else 0), _scales_dev(bs, 4 if pad else 0)
-    out = torch.full((m, n + 5), 7.0, dtype=torch.bfloat16 if bf16 else torch.float32,
-                     device="cuda")[:, :n]
+    full = torch.full((m, n + out_pad), 7.0, dtype=torch.bfloat16 if bf16 else torch.float32,
+                      device="cuda")
+    out = full[:, :n]
     fp4.gemm(A, SA, B, SB, k=k, out=out)
     torch.cuda.synchronize()
+    assert torch.all(full[:, n:] == 7.0), "the kernel wrote past n"
     got = out.float().cpu().numpy().astype(np.float64)
     want = orc.gemm_f64(ac, as_, bc, bs)
     tol = _bound(orc, ac, as_, bc, bs, k) + (2.0 ** -8 * np.abs(want) if bf16 else 0)
@@ -107,6 +109,20 @@ def test_gemm_split_k_tiles_strides(orc, m, n, k, pad):
     ac, as_ = _rand_operand(rng, m, k)
     bc, bs = _rand_operand(rng, n, k)
     _check(orc, ac, as_, bc, bs, k, bf16=True, pad=pad)
+
+
+# bf16 output of the tiled kernels, whose epilogue goes through LDS when the
+# row stride of C is a multiple of 8 elements (row strides n + 3 .. n + 13 with
+# n ragged, so both that path with partial 16-byte pieces and the direct
+# stores run), for both tile sizes
+@pytest.mark.parametrize("m,n,k", [(513, 129, 1024), (2048, 2304, 1024), (2100, 2050, 544)])
+def test_gemm_bf16_tiles(orc, m, n, k):
+    rng = np.random.default_rng(m + n + k)
+    ac, as_ = _rand_operand(rng, m, k)
+    bc, bs = _rand_operand(rng, n, k)
+    for out_pad in sorted({(-n) % 8 + 8, (-n) % 8 + 3}):
+        note(f"case: MXFP4 GEMM {m}x{n}x{k}, bf16 output, C row stride n + {out_pad}")
+        _check(orc, ac, as_, bc, bs, k, bf16=True, out_pad=out_pad)
 
 
 def test_gemm_bf16_out_and_strides(orc):

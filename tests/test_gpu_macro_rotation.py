@@ -89,12 +89,16 @@ def test_gather_with_repeats(orc):
     _check(orc, x, macro, idx, bf16_bits(z))
 
 
-@pytest.mark.parametrize("n_layers,per_layer", [(1, 0), (8, 500)])
-def test_rotation_table_sizes(orc, n_layers, per_layer):
-    """No rotation at all (a pure permutation), and 4000 rotations over
-    16384 columns, whose tables leave no room for the compact kernel (the
-    row-wide kernel runs them)."""
-    rows, cols = 9, 16384
+@pytest.mark.parametrize("n_layers,per_layer,cols", [(1, 0, 16384), (8, 500, 16384),
+                                                     (2, 100, 8192), (16, 12, 8192),
+                                                     (17, 10, 8192)])
+def test_rotation_table_sizes(orc, n_layers, per_layer, cols):
+    """Table sizes around the compact kernel's limits: no rotation at all (a
+    pure permutation); 4000 rotations over 16384 columns, whose tables leave
+    no room for it (the row-wide kernel runs them); layers of 100 rotations
+    (two register rounds each); 16 rounds, the most wave 0 holds in
+    registers, and 17 (its LDS loop)."""
+    rows = 9
     note(f"case: Givens layers, {n_layers} x {per_layer} rotations, {rows}x{cols} with perm")
     x = inputs.gen_c4(rows=rows, cols=cols)
     perm = np.random.default_rng(5).permutation(cols).astype(np.int32)
