@@ -345,7 +345,9 @@ __device__ __forceinline__ void nvw_rcp_table(float* tab, float s_t) {
 // sum of 16 (at most 4, on the 2^-22 grid) is exact too.
 __device__ __forceinline__ float razer_gain_pair2(float y) {
   const float d = __builtin_fabsf(y) - kWeightPair;
-  return __builtin_amdgcn_fmed3f(0.25f - __builtin_fabsf(d), 0.0f, 0.25f);
+  // 0.25 - |d| <= 0.25, so clamping to [0, 1] (the instruction's clamp bit)
+  // is clamping to [0, 0.25]
+  return __builtin_amdgcn_fmed3f(0.25f - __builtin_fabsf(d), 0.0f, 1.0f);
 }
 
 __device__ __forceinline__ float weight_special(uint32_t byte) {

@@ -213,23 +213,30 @@ __device__ __forceinline__ void nv_quant_chunk(u32x4_t d, const NvScale& ns, con
       w = razer_apply(w, cm, sel);
       byte |= sel << 7;
     } else if constexpr (kMode == 2) {
-      // block gains of the four specials (exact sums); the largest wins,
-      // ties to the lower selector
-      float g[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // +5, -5, +2.5, -2.5
+      // block gains of the four specials; the largest wins, ties to the
+      // lower selector. Per pair, s = G+ + G- and d = G+ - G- (the sign of y
+      // as a +-1 factor of one fma), then G+- = (s +- d) / 2: every sum is
+      // exact (multiples of 2^-20 or 2^-22, at most 16 or 4), and s +- d is
+      // the exact 2 G+-, so the gains equal the separate sums bit for bit.
+      float s5 = 0.0f, d5 = 0.0f, s2 = 0.0f, d2 = 0.0f;
       float g5[8], g2[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         g5[k] = razer_gain(y[k]);
         g2[k] = razer_gain_pair2(y[k]);
-        const bool neg = __float_as_uint(y[k]) >> 31;
-        g[0] += neg ? 0.0f : g5[k];
-        g[1] += neg ? g5[k] : 0.0f;
-        g[2] += neg ? 0.0f : g2[k];
-        g[3] += neg ? g2[k] : 0.0f;
+        const float sg = __builtin_copysignf(1.0f, y[k]);
+        s5 += g5[k];
+        d5 = __builtin_fmaf(sg, g5[k], d5);
+        s2 += g2[k];
+        d2 = __builtin_fmaf(sg, g2[k], d2);
       }
       const uint32_t cm5 = razer_flags8(g5), cm2 = razer_flags8(g2);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) g[i] += dpp_xor1f(g[i]);
+      s5 += dpp_xor1f(s5);
+      d5 += dpp_xor1f(d5);
+      s2 += dpp_xor1f(s2);
+      d2 += dpp_xor1f(d2);
+      const float g[4] = {0.5f * (s5 + d5), 0.5f * (s5 - d5), 0.5f * (s2 + d2),
+                          0.5f * (s2 - d2)};  // +5, -5, +2.5, -2.5
       uint32_t sel = 0;
       float best = g[0];
       if (g[1] > best) { best = g[1]; sel = 1; }
