@@ -159,6 +159,85 @@ struct Tile {
   }
 };
 
+// Epilogue of a work-group tile: lane (n, h) of MFMA tile (i, j) holds
+// column n and rows 8 (e / 4) + 4 h + e % 4, e = 0..15. bf16 goes through LDS
+// (kLds: the two operand buffer pairs la, lb are free after the last stage's
+// barrier and hold a row half each): the waves of row half wm write their
+// tiles into la (wm = 0) or lb (wm = 1), BM / 2 rows of BN bf16, then every
+// thread copies 16-byte pieces of whole rows out. 16-byte piece p of row rl
+// sits in slot p ^ 4 ((rl / 4) % 2), so that the two lane halves of a write
+// (rows 4 apart) use different banks. That needs ld_c % 8 == 0 and a 16-byte
+// aligned C; otherwise, and for fp32, each element is stored directly.
+template <int WM, int WN, int VM, int VN, bool kBf16Out, bool kLds>
+__device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[WM][WN], const GemmArgs& g,
+                                              int32_t m0, int32_t n0, uint32_t wm, uint32_t wn,
+                                              uint32_t r, uint32_t h, uint8_t* la, uint8_t* lb) {
+  constexpr int BM = 32 * WM * VM, BN = 32 * WN * VN, kT = 64 * VM * VN;
+  if constexpr (kBf16Out && kLds && VM == 2) {
+    const bool via_lds = g.ld_c % 8 == 0 && reinterpret_cast<uintptr_t>(g.c) % 16 == 0;
+    if (via_lds) {
+      constexpr int kHalf = BM / 2;
+      uint8_t* half = wm == 0 ? la : lb;
+      auto slot = [](uint32_t rl, uint32_t p) { return p ^ (4u * ((rl >> 2) & 1u)); };
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const uint32_t cl = 32u * WN * wn + 32u * j + r;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t rl = 32u * i + 8u * (e / 4) + 4u * h + (e % 4);
+            const uint32_t off = rl * (2u * BN) + 16u * slot(rl, cl / 8u) + 2u * (cl % 8u);
+            *reinterpret_cast<uint16_t*>(half + off) =
+                (uint16_t)(pack_bf16x2(acc[i][j][e], 0.0f) & 0xFFFFu);
+          }
+        }
+      __syncthreads();
+      constexpr int kPieces = BM * BN / 8;  // 16-byte pieces of the tile
+      constexpr int kPpr = BN / 8;          // per row
+#pragma unroll
+      for (int u = 0; u < kPieces / kT; ++u) {
+        const uint32_t pc = threadIdx.x + (uint32_t)kT * u;
+        const uint32_t row = pc / kPpr, p = pc % kPpr;
+        const uint32_t rl = row % kHalf;
+        const uint8_t* src = (row < (uint32_t)kHalf ? la : lb) + rl * (2u * BN) + 16u * slot(rl, p);
+        const int32_t grow = m0 + (int32_t)row, gcol = n0 + 8 * (int32_t)p;
+        if (grow >= g.m || gcol >= g.n) continue;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src);
+        uint16_t* dst = static_cast<uint16_t*>(g.c) + (int64_t)grow * g.ld_c + gcol;
+        if (gcol + 8 <= g.n) {
+          *reinterpret_cast<u32x4_t*>(dst) = v;
+        } else {
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if (gcol + t < g.n) dst[t] = (uint16_t)(w4[t / 2] >> (16 * (t % 2)));
+        }
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int32_t col = n0 + 32 * WN * (int32_t)wn + 32 * j + (int32_t)r;
+      if (col >= g.n) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int32_t row =
+            m0 + 32 * WM * (int32_t)wm + 32 * i + 8 * (e / 4) + 4 * (int32_t)h + e % 4;
+        if (row >= g.m) continue;
+        if constexpr (kBf16Out) {
+          const uint32_t pv = pack_bf16x2(acc[i][j][e], 0.0f);
+          static_cast<uint16_t*>(g.c)[(int64_t)row * g.ld_c + col] = (uint16_t)(pv & 0xFFFFu);
+        } else {
+          static_cast<float*>(g.c)[(int64_t)row * g.ld_c + col] = acc[i][j][e];
+        }
+      }
+    }
+}
+
 template <int WM, int WN, int VM, int VN, int KB, int kSets, bool kBf16Out>
 __global__ __launch_bounds__(64 * VM * VN) void mx_gemm_kernel(GemmArgs g) {
   using T = Tile<WM, WN, VM, VN, KB>;
@@ -264,80 +343,8 @@ __global__ __launch_bounds__(64 * VM * VN) void mx_gemm_kernel(GemmArgs g) {
   for (; s + kSets - 1 < stages; s += kSets) group(s, std::make_integer_sequence<int, kSets>{});
   tail(s, std::make_integer_sequence<int, kSets - 1>{});
 
-  // epilogue: lane (n, h) of tile (i, j) holds column n, rows 8 (e / 4) + 4 h + e % 4
-  if constexpr (kBf16Out && VM == 2 && KB >= BN) {
-    // bf16 through LDS (free after the last stage's barrier): the waves of
-    // row half wm write their tiles into lds_a (wm = 0) or lds_b (wm = 1),
-    // BM / 2 rows of BN bf16, then every thread copies 16-byte pieces of
-    // whole rows out. 16-byte piece p of row rl sits in slot p ^ 4 ((rl / 4)
-    // % 2), so that the two lane halves of a write (rows 4 apart) use
-    // different banks. Needs ld_c % 8 == 0 and a 16-byte aligned C;
-    // otherwise the direct stores below run.
-    const bool via_lds = g.ld_c % 8 == 0 && reinterpret_cast<uintptr_t>(g.c) % 16 == 0;
-    if (via_lds) {
-      constexpr int kHalf = BM / 2;
-      static_assert(2 * kHalf * BN <= 2 * T::kLdsA && 2 * kHalf * BN <= 2 * T::kLdsB,
-                    "a row half of the bf16 tile fits each operand buffer pair");
-      uint8_t* half = wm == 0 ? &lds_a[0][0] : &lds_b[0][0];
-      auto slot = [](uint32_t rl, uint32_t p) { return p ^ (4u * ((rl >> 2) & 1u)); };
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          const uint32_t cl = 32u * WN * wn + 32u * j + r;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const uint32_t rl = 32u * i + 8u * (e / 4) + 4u * h + (e % 4);
-            const uint32_t off = rl * (2u * BN) + 16u * slot(rl, cl / 8u) + 2u * (cl % 8u);
-            *reinterpret_cast<uint16_t*>(half + off) =
-                (uint16_t)(pack_bf16x2(acc[i][j][e], 0.0f) & 0xFFFFu);
-          }
-        }
-      __syncthreads();
-      constexpr int kPieces = BM * BN / 8;  // 16-byte pieces of the tile
-      constexpr int kPpr = BN / 8;          // per row
-#pragma unroll
-      for (int u = 0; u < kPieces / T::kT; ++u) {
-        const uint32_t pc = threadIdx.x + (uint32_t)T::kT * u;
-        const uint32_t row = pc / kPpr, p = pc % kPpr;
-        const uint32_t rl = row % kHalf;
-        const uint8_t* src = (row < (uint32_t)kHalf ? &lds_a[0][0] : &lds_b[0][0]) +
-                             rl * (2u * BN) + 16u * slot(rl, p);
-        const int32_t grow = m0 + (int32_t)row, gcol = n0 + 8 * (int32_t)p;
-        if (grow >= g.m || gcol >= g.n) continue;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src);
-        uint16_t* dst = static_cast<uint16_t*>(g.c) + (int64_t)grow * g.ld_c + gcol;
-        if (gcol + 8 <= g.n) {
-          *reinterpret_cast<u32x4_t*>(dst) = v;
-        } else {
-          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-            if (gcol + t < g.n) dst[t] = (uint16_t)(w4[t / 2] >> (16 * (t % 2)));
-        }
-      }
-      return;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < WM; ++i)
-#pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      const int32_t col = n0 + 32 * WN * (int32_t)wn + 32 * j + (int32_t)r;
-      if (col >= g.n) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int32_t row =
-            m0 + 32 * WM * (int32_t)wm + 32 * i + 8 * (e / 4) + 4 * (int32_t)h + e % 4;
-        if (row >= g.m) continue;
-        if constexpr (kBf16Out) {
-          const uint32_t p = pack_bf16x2(acc[i][j][e], 0.0f);
-          static_cast<uint16_t*>(g.c)[(int64_t)row * g.ld_c + col] = (uint16_t)(p & 0xFFFFu);
-        } else {
-          static_cast<float*>(g.c)[(int64_t)row * g.ld_c + col] = acc[i][j][e];
-        }
-      }
-    }
+  tile_epilogue<WM, WN, VM, VN, kBf16Out, KB >= BN>(acc, g, m0, n0, wm, wn, r, h, &lds_a[0][0],
+                                                  &lds_b[0][0]);
 }
 
 // Split-K products, for few rows of A (decode and small batches) and for
@@ -588,6 +595,9 @@ void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a
   // shapes, bit-identical results. Stages of 256 K (whole 128-byte lines of
   // each row; 136 KB of LDS), the next stage in registers while one is
   // multiplied: up to 8% faster again than 128-K stages with two in flight.
+  // Loading the stages straight into LDS (buffer loads with the LDS as
+  // destination, four 128-K stages in flight, one barrier per stage or per
+  // two) gave the same results 20-40% slower on the layer shapes.
   if (m >= 2048 && n >= 2048)
     launch_tiles<4, 2, 2, 4, 256, 1>(g, bf16_out, st);
   else
