@@ -1134,6 +1134,16 @@ def counter_summary(op_log, dirs):
             ratio_rows.append(f"| MFMA busy per SIMD cycle (1024 SIMDs at 2.4 GHz over the "
                               f"launch) | `SQ_VALU_MFMA_BUSY_CYCLES` / (1024 x 2400 x us) | "
                               f"{med(fr):.4g} | {mean(fr[:third]):.4g} | {mean(fr[-third:]):.4g} |")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in counters and "GRBM_COUNT" in counters:
+        # against the counted clock instead (GRBM_COUNT sums the eight XCDs'
+        # cycles); the two counters come from different passes, so only the
+        # ratio of their medians is given
+        busy = med([v["SQ_VALU_MFMA_BUSY_CYCLES"] for v in per.values()
+                    if "SQ_VALU_MFMA_BUSY_CYCLES" in v])
+        clk = med([v["GRBM_COUNT"] for v in per.values() if "GRBM_COUNT" in v])
+        ratio_rows.append(f"| MFMA busy per SIMD cycle of the counted clock (medians) | "
+                          f"(`SQ_VALU_MFMA_BUSY_CYCLES` / 1024) / (`GRBM_COUNT` / 8) | "
+                          f"{busy / 1024 / (clk / 8):.4g} | - | - |")
     for label, a, b in COUNTER_RATIOS:
         keys = [k for k, v in per.items() if a in v and b in v and v[b] > 0]
         if not keys:
