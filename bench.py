@@ -699,9 +699,11 @@ MFMA_PEAK_FP4_TFLOPS = 10100.0
 def gemm_rows(torch, fp4, fmt):
     """The consumer: C = A B^T on quantized operands (activations [m, k],
     weights [n, k] of the Llama-70B-shaped layer), bf16 out. MXFP4 runs on the
-    scaled FP4 matrix cores (peak 10.1 PFLOP/s); NVFP4 + RaZeR on both sides is
-    decoded exactly to bf16 and runs on the bf16 ones (peak 2.5 PFLOP/s).
-    Random codes and finite scale bytes: the time does not depend on values."""
+    scaled FP4 matrix cores (peak 10.1 PFLOP/s), with both operands' scales in
+    the GEMM order (the quantizers' FP4_FLAG_SCALES_GEMM output; the row-major
+    time is given beside it); NVFP4 + RaZeR on both sides is decoded exactly
+    to bf16 and runs on the bf16 ones (peak 2.5 PFLOP/s). Random codes and
+    finite scale bytes: the time does not depend on values."""
     nv = fmt == fp4.NVFP4
     blk, lo, hi = (16, 40, 60) if nv else (32, 120, 131)
     peak = MFMA_PEAK_BF16_TFLOPS if nv else MFMA_PEAK_FP4_TFLOPS
@@ -717,13 +719,29 @@ def gemm_rows(torch, fp4, fmt):
         b = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device="cuda", generator=g)
         sb = torch.randint(lo, hi, (n, k // blk), dtype=torch.uint8, device="cuda", generator=g)
         c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-        pg = fp4.gemm(a, sa, b, sb, out=c, prepare=True, **kw)
+        row_major = None
+        if not nv:
+            p0 = fp4.gemm(a, sa, b, sb, out=c, prepare=True)
+            ms0 = timed(torch, lambda i: p0.run(), 10, 2, ROW_WARM_MS)
+            row_major = {"ms": round(ms0, 4), "frac_mfma_peak": round(
+                2.0 * m * n * k / (ms0 * 1e-3) / 1e12 / peak, 4)}
+            ga = torch.randint(lo, hi, fp4.gemm_scale_shape(m, k), dtype=torch.uint8,
+                               device="cuda", generator=g)
+            gb = torch.randint(lo, hi, fp4.gemm_scale_shape(n, k), dtype=torch.uint8,
+                               device="cuda", generator=g)
+            pg = fp4.gemm(a, ga, b, gb, out=c, prepare=True, a_gemm_scales=True,
+                          b_gemm_scales=True)
+        else:
+            pg = fp4.gemm(a, sa, b, sb, out=c, prepare=True, **kw)
         ms = timed(torch, lambda i: pg.run(), 10, 2, ROW_WARM_MS)
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         by = (m + n) * (k / 2 + k / blk) + 2 * m * n
         rows[f"{m}x{n}x{k}"] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
                                 "frac_mfma_peak": round(tf / peak, 4),
                                 "GBps": round(by / ms / 1e6, 1)}
+        if row_major is not None:
+            rows[f"{m}x{n}x{k}"]["scales"] = "GEMM order"
+            rows[f"{m}x{n}x{k}"]["row_major_scales"] = row_major
         if m <= 32:  # µs-scale launches: also their time replayed from a graph
             us = graph_us(torch, lambda i: pg.run())
             rows[f"{m}x{n}x{k}"]["graph_us_per_call"] = round(us, 2)
@@ -938,6 +956,8 @@ KERNEL_OPS = {
     "c2_nvfp4_plain": "NVFP4 quantize, tensor scale given, 4096x4096 bf16 (c2)",
     "c2_nvfp4_razer": "NVFP4 + RaZeR quantize, tensor scale given, 4096x4096 bf16 (c2)",
     "gemm_mxfp4": "MXFP4 x MXFP4 GEMM, m=4096 n=8192 k=8192, bf16 out",
+    "gemm_mxfp4_gemm_scales": "MXFP4 x MXFP4 GEMM, m=4096 n=8192 k=8192, bf16 out, both "
+                              "operands' scales in the GEMM order",
 }
 
 
@@ -1007,7 +1027,13 @@ def kernel_op(torch, fp4, inputs, args):
         b = torch.randint(0, 256, (nn, k // 2), dtype=torch.uint8, device="cuda", generator=g)
         sb = torch.randint(120, 131, (nn, k // 32), dtype=torch.uint8, device="cuda", generator=g)
         cm = torch.empty((m, nn), dtype=torch.bfloat16, device="cuda")
-        ps = [fp4.gemm(a, sa, b, sb, out=cm, prepare=True)]
+        if op == "gemm_mxfp4_gemm_scales":  # random scale bytes, laid out in the GEMM order
+            sa = torch.randint(120, 131, fp4.gemm_scale_shape(m, k), dtype=torch.uint8,
+                               device="cuda", generator=g)
+            sb = torch.randint(120, 131, fp4.gemm_scale_shape(nn, k), dtype=torch.uint8,
+                               device="cuda", generator=g)
+        gs = op == "gemm_mxfp4_gemm_scales"
+        ps = [fp4.gemm(a, sa, b, sb, out=cm, prepare=True, a_gemm_scales=gs, b_gemm_scales=gs)]
         kernel = "mx_gemm_kernel<"
         units, unit = 2 * m * nn * k, "flop"
     ms = timed(torch, lambda i: ps[i % len(ps)].run(), args.steps, args.warmup)

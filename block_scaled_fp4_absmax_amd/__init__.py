@@ -15,6 +15,7 @@ from typing import Optional
 
 __all__ = [
     "MXFP4", "NVFP4", "MXINT4", "PLAIN", "RAZER", "RAZER_W", "FLAG_TENSOR_SCALE_GIVEN", "FLAG_SCALE_OCP_FLOOR",
+    "FLAG_SCALES_GEMM", "gemm_scale_shape",
     "Fp4Error", "lib", "library_path", "quantize", "dequantize", "rotate_quantize",
     "channel_energy", "build_permutation", "block_of", "gemm", "OUT_F32", "OUT_BF16",
     "rotate_quantize_r", "dequantize_r", "calibrate_block_rotation",
@@ -25,6 +26,7 @@ MXFP4, NVFP4, MXINT4 = 0, 1, 2
 PLAIN, RAZER, RAZER_W = 0, 1, 2
 FLAG_TENSOR_SCALE_GIVEN = 1
 FLAG_SCALE_OCP_FLOOR = 2
+FLAG_SCALES_GEMM = 0x100
 OUT_F32, OUT_BF16 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -195,14 +197,23 @@ def _check_fmt(fmt, mode):
         raise ValueError(f"unknown mode {mode}")
 
 
-def _outputs(rows, cols, fmt, device, codes=None, scales=None):
+def gemm_scale_shape(rows: int, cols: int):
+    """Shape of an MXFP4 scale array in the GEMM order (FLAG_SCALES_GEMM):
+    one row of 256-byte steps per group of 32 rows, a step per 256 columns."""
+    return ((rows + 31) // 32, 256 * ((cols + 255) // 256))
+
+
+def _outputs(rows, cols, fmt, device, codes=None, scales=None, gemm_scales=False):
     import torch
+    if gemm_scales and fmt != MXFP4:
+        raise ValueError("scales in the GEMM order are MXFP4 only")
+    sshape = gemm_scale_shape(rows, cols) if gemm_scales else (rows, cols // block_of(fmt))
     if codes is None:
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
     if scales is None:
-        scales = torch.empty((rows, cols // block_of(fmt)), dtype=torch.uint8, device=device)
+        scales = torch.empty(sshape, dtype=torch.uint8, device=device)
     _mat(codes, "codes", torch.uint8, device, rows, cols // 2)
-    _mat(scales, "scales", torch.uint8, device, rows, cols // block_of(fmt))
+    _mat(scales, "scales", torch.uint8, device, *sshape)
     return codes, scales
 
 
@@ -216,11 +227,13 @@ def _tensor_scale(tensor_scale, device):
 
 def quantize(x, fmt: int = MXFP4, mode: int = PLAIN, floor_rule: bool = False,
              tensor_scale=None, scale_given: Optional[bool] = None, codes=None, scales=None,
-             stream=None, prepare: bool = False):
+             stream=None, prepare: bool = False, gemm_scales: bool = False):
     """Quantize a bf16 [rows, cols] CUDA tensor.
 
     Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/block],
-    tensor_scale fp32 [1] for NVFP4 else None). For NVFP4, ``tensor_scale`` is
+    tensor_scale fp32 [1] for NVFP4 else None); with ``gemm_scales`` (MXFP4)
+    the scales come in the GEMM order, shape :func:`gemm_scale_shape`. For
+    NVFP4, ``tensor_scale`` is
     a 1-element fp32 device tensor: read as s_t when ``scale_given`` (the
     default when it is passed), otherwise it receives the computed s_t
     (allocated when None). ``prepare=True`` returns a :class:`Prepared` call
@@ -230,8 +243,8 @@ def quantize(x, fmt: int = MXFP4, mode: int = PLAIN, floor_rule: bool = False,
     _check_fmt(fmt, mode)
     dev = _device_of(x)
     rows, cols, ld = _mat(x, "x", torch.bfloat16, dev)
-    codes, scales = _outputs(rows, cols, fmt, dev, codes, scales)
-    flags = FLAG_SCALE_OCP_FLOOR if floor_rule else 0
+    codes, scales = _outputs(rows, cols, fmt, dev, codes, scales, gemm_scales)
+    flags = (FLAG_SCALE_OCP_FLOOR if floor_rule else 0) | (FLAG_SCALES_GEMM if gemm_scales else 0)
     ts = None
     if fmt == NVFP4:
         if scale_given is None:
@@ -274,14 +287,16 @@ def dequantize(codes, scales, fmt: int = MXFP4, mode: int = PLAIN, tensor_scale=
 def rotate_quantize(x, perm=None, hadamard: Optional[int] = None, floor_rule: bool = False,
                     want_rotated: bool = False, codes=None, scales=None, rotated=None,
                     fmt: int = MXFP4, mode: int = PLAIN, tensor_scale=None,
-                    scale_given: Optional[bool] = None, stream=None, prepare: bool = False):
+                    scale_given: Optional[bool] = None, stream=None, prepare: bool = False,
+                    gemm_scales: bool = False):
     """Permutation + block Hadamard fused with FP4 quantize + pack.
 
     ``hadamard`` defaults to the format's block size (32 MXFP4, 16 NVFP4); 0
     turns the transform off. NVFP4 takes ``mode`` (PLAIN or RAZER) and a
     tensor scale as in :func:`quantize`. Returns (codes, scales, rotated fp32
     [rows, cols] or None) for MXFP4 and MXINT4, and (codes, scales, rotated,
-    tensor_scale) for NVFP4.
+    tensor_scale) for NVFP4. ``gemm_scales`` (MXFP4): scales in the GEMM
+    order, as for :func:`quantize`.
     """
     import torch
     _check_fmt(fmt, mode)
@@ -291,12 +306,12 @@ def rotate_quantize(x, perm=None, hadamard: Optional[int] = None, floor_rule: bo
         hadamard = block_of(fmt)
     if perm is not None:
         _vec(perm, "perm", torch.int32, cols, dev)
-    codes, scales = _outputs(rows, cols, fmt, dev, codes, scales)
+    codes, scales = _outputs(rows, cols, fmt, dev, codes, scales, gemm_scales)
     if want_rotated and rotated is None:
         rotated = torch.empty((rows, cols), dtype=torch.float32, device=dev)
     if rotated is not None:
         _mat(rotated, "rotated", torch.float32, dev, rows, cols)
-    flags = FLAG_SCALE_OCP_FLOOR if floor_rule else 0
+    flags = (FLAG_SCALE_OCP_FLOOR if floor_rule else 0) | (FLAG_SCALES_GEMM if gemm_scales else 0)
     ts = None
     if fmt == NVFP4:
         if scale_given is None:
@@ -317,10 +332,13 @@ def rotate_quantize(x, perm=None, hadamard: Optional[int] = None, floor_rule: bo
 
 def gemm(a_codes, a_scales, b_codes, b_scales, k: Optional[int] = None, fmt: int = MXFP4,
          a_ts=None, b_ts=None, mode_a: int = PLAIN, mode_b: int = PLAIN, out_dtype=None,
-         out=None, stream=None, prepare: bool = False):
+         out=None, stream=None, prepare: bool = False, a_gemm_scales: bool = False,
+         b_gemm_scales: bool = False):
     """C = A B^T for quantized A [m, k] and B [n, k] (codes and scales as the
     quantizer returns them; NVFP4 also takes the two tensor scales and a mode
-    per operand); fp32 [m, n] unless ``out_dtype`` is bfloat16."""
+    per operand); fp32 [m, n] unless ``out_dtype`` is bfloat16.
+    ``a_gemm_scales`` / ``b_gemm_scales`` (MXFP4): that operand's scales are
+    in the GEMM order (a quantizer called with ``gemm_scales=True``)."""
     import torch
     if fmt not in (MXFP4, NVFP4):
         raise ValueError(f"fp4_gemm takes MXFP4 or NVFP4, got format {fmt}")
@@ -336,8 +354,14 @@ def gemm(a_codes, a_scales, b_codes, b_scales, k: Optional[int] = None, fmt: int
     if k > 2 * ha or k > 2 * hb:
         raise ValueError(f"k = {k} exceeds the code rows ({2 * ha}, {2 * hb} elements)")
     blk = block_of(fmt)
-    _mat(a_scales, "a_scales", torch.uint8, dev, m, k // blk)
-    _mat(b_scales, "b_scales", torch.uint8, dev, n, k // blk)
+    if (a_gemm_scales or b_gemm_scales) and fmt != MXFP4:
+        raise ValueError("scales in the GEMM order are MXFP4 only")
+    _mat(a_scales, "a_scales", torch.uint8, dev,
+         *(gemm_scale_shape(m, k) if a_gemm_scales else (m, k // blk)))
+    _mat(b_scales, "b_scales", torch.uint8, dev,
+         *(gemm_scale_shape(n, k) if b_gemm_scales else (n, k // blk)))
+    mode_a |= FLAG_SCALES_GEMM if a_gemm_scales else 0
+    mode_b |= FLAG_SCALES_GEMM if b_gemm_scales else 0
     if fmt == NVFP4:
         if a_ts is None or b_ts is None:
             raise ValueError("NVFP4 needs both tensor scales")

@@ -17,6 +17,12 @@ bool known_format(int format) {
   return format == FP4_MXFP4 || format == FP4_NVFP4 || format == FP4_MXINT4;
 }
 
+// Stride check of an MXFP4 scale array in the GEMM order (FP4_FLAG_SCALES_GEMM):
+// ld is the 32-row group stride, whole 256-byte steps covering `len` elements.
+bool gemm_scale_ld_ok(int64_t ld, int64_t len) {
+  return ld % 256 == 0 && ld >= 256 * ((len + 255) / 256);
+}
+
 // Checks shared by the quantizing entry points.
 int check_quant_args(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int format,
                      int block, int mode, uint32_t flags, const void* codes, int64_t ld_codes,
@@ -25,11 +31,15 @@ int check_quant_args(const void* x, int64_t rows, int64_t cols, int64_t ld_x, in
   if (block != block_of(format)) return FP4_ERR_UNSUPPORTED;
   if (mode != FP4_PLAIN && mode != FP4_RAZER && mode != FP4_RAZER_W) return FP4_ERR_UNSUPPORTED;
   if (mode != FP4_PLAIN && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;  // E8M0 has no free bit
-  if (flags & ~(FP4_FLAG_TENSOR_SCALE_GIVEN | FP4_FLAG_SCALE_OCP_FLOOR)) return FP4_ERR_UNSUPPORTED;
+  if (flags & ~(FP4_FLAG_TENSOR_SCALE_GIVEN | FP4_FLAG_SCALE_OCP_FLOOR | FP4_FLAG_SCALES_GEMM))
+    return FP4_ERR_UNSUPPORTED;
   if ((flags & FP4_FLAG_TENSOR_SCALE_GIVEN) && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
   if ((flags & FP4_FLAG_SCALE_OCP_FLOOR) && format == FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
+  const bool s_gemm = (flags & FP4_FLAG_SCALES_GEMM) != 0;
+  if (s_gemm && format != FP4_MXFP4) return FP4_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 0 || cols % block != 0) return FP4_ERR_SHAPE;
-  if (ld_x < cols || ld_codes < cols / 2 || ld_scales < cols / block) return FP4_ERR_SHAPE;
+  if (ld_x < cols || ld_codes < cols / 2) return FP4_ERR_SHAPE;
+  if (s_gemm ? !gemm_scale_ld_ok(ld_scales, cols) : ld_scales < cols / block) return FP4_ERR_SHAPE;
   if (rows > 0 && cols > 0 && rows * cols / 8 >= (int64_t)1 << 31) return FP4_ERR_UNSUPPORTED;
   if (format == FP4_NVFP4 && !tensor_scale) return FP4_ERR_NULL;
   if (rows == 0 || cols == 0) return FP4_OK;
@@ -70,7 +80,7 @@ int fp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, i
                             scales, ld_scales, tensor_scale);
   if (rc != FP4_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  Shape s{rows, cols, ld_x, ld_codes, ld_scales};
+  Shape s{rows, cols, ld_x, ld_codes, ld_scales, (flags & FP4_FLAG_SCALES_GEMM) != 0};
   const bool empty = rows == 0 || cols == 0;
   const bool need_scale = format == FP4_NVFP4 && !(flags & FP4_FLAG_TENSOR_SCALE_GIVEN);
   if (empty && !need_scale) return FP4_OK;  // nothing to enqueue
@@ -143,7 +153,7 @@ int fp4_rotate_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t 
   if (!empty && perm && !aligned(perm, 4)) return FP4_ERR_ALIGN;
   if (!empty && rotated_out && (!aligned(rotated_out, 16) || ld_rot % 4 != 0)) return FP4_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  Shape s{rows, cols, ld_x, ld_codes, ld_scales};
+  Shape s{rows, cols, ld_x, ld_codes, ld_scales, (flags & FP4_FLAG_SCALES_GEMM) != 0};
   (void)hipGetLastError();
   if (format != FP4_NVFP4)
     fp4::launch_mx_rotate_quant(s, perm, hadamard, (flags & FP4_FLAG_SCALE_OCP_FLOOR) != 0,
@@ -224,6 +234,11 @@ int fp4_gemm(const void* a_codes, int64_t ld_a, const void* a_scales, int64_t ld
              void* stream) {
   if (format != FP4_MXFP4 && format != FP4_NVFP4) return FP4_ERR_UNSUPPORTED;
   if (out_dtype != FP4_OUT_F32 && out_dtype != FP4_OUT_BF16) return FP4_ERR_UNSUPPORTED;
+  // MXFP4 scale order per operand: row-major, or the GEMM order
+  const bool sg_a = format == FP4_MXFP4 && (mode_a & (int)FP4_FLAG_SCALES_GEMM) != 0;
+  const bool sg_b = format == FP4_MXFP4 && (mode_b & (int)FP4_FLAG_SCALES_GEMM) != 0;
+  if (sg_a) mode_a &= ~(int)FP4_FLAG_SCALES_GEMM;
+  if (sg_b) mode_b &= ~(int)FP4_FLAG_SCALES_GEMM;
   if (mode_a != FP4_PLAIN && mode_a != FP4_RAZER) return FP4_ERR_UNSUPPORTED;
   if (mode_b != FP4_PLAIN && mode_b != FP4_RAZER && mode_b != FP4_RAZER_W)
     return FP4_ERR_UNSUPPORTED;
@@ -233,8 +248,9 @@ int fp4_gemm(const void* a_codes, int64_t ld_a, const void* a_scales, int64_t ld
   if (m < 0 || n < 0 || k < 0 || k % 32 != 0) return FP4_ERR_SHAPE;
   if (m >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31) || k >= ((int64_t)1 << 31))
     return FP4_ERR_UNSUPPORTED;
-  if (ld_a < k / 2 || ld_b < k / 2 || ld_sa < k / blk || ld_sb < k / blk || ld_c < n)
-    return FP4_ERR_SHAPE;
+  if (ld_a < k / 2 || ld_b < k / 2 || ld_c < n) return FP4_ERR_SHAPE;
+  if (sg_a ? !gemm_scale_ld_ok(ld_sa, k) : ld_sa < k / blk) return FP4_ERR_SHAPE;
+  if (sg_b ? !gemm_scale_ld_ok(ld_sb, k) : ld_sb < k / blk) return FP4_ERR_SHAPE;
   const int64_t lim = ((int64_t)1 << 31) / 256;
   if (ld_a >= lim || ld_b >= lim || ld_sa >= lim || ld_sb >= lim) return FP4_ERR_UNSUPPORTED;
   if (m == 0 || n == 0) return FP4_OK;
@@ -252,7 +268,7 @@ int fp4_gemm(const void* a_codes, int64_t ld_a, const void* a_scales, int64_t ld
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (format == FP4_MXFP4)
     fp4::launch_mx_gemm(m, n, k, a_codes, ld_a, a_scales, ld_sa, b_codes, ld_b, b_scales, ld_sb,
-                        c, ld_c, out_dtype == FP4_OUT_BF16, st);
+                        c, ld_c, out_dtype == FP4_OUT_BF16, sg_a, sg_b, st);
   else
     fp4::launch_nv_gemm(m, n, k, a_codes, ld_a, a_scales, ld_sa, a_ts, mode_a, b_codes, ld_b,
                         b_scales, ld_sb, b_ts, mode_b, c, ld_c,

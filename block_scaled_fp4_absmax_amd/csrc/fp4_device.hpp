@@ -41,6 +41,18 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            0x00020000);
 }
 
+// ---- scale byte placement --------------------------------------------------
+// Row-major: row r at r * ld_s, block b at b. GEMM order (MXFP4): rows in
+// groups of 32 at stride ld_s; inside a group, the 8 blocks of each
+// 256-element step of the row are 256 contiguous bytes, row r % 32 at
+// 8 (r % 32), block b at 256 (b / 8) + b % 8. Row and block parts add.
+__device__ __forceinline__ int64_t scale_row_off(int64_t r, int64_t ld_s, bool gemm) {
+  return gemm ? (r >> 5) * ld_s + 8 * (r & 31) : r * ld_s;
+}
+__device__ __forceinline__ uint32_t scale_col_off(uint32_t b, bool gemm) {
+  return gemm ? ((b >> 3) << 8) | (b & 7u) : b;
+}
+
 // Bit casts take a scalar by value: clang's __builtin_bit_cast applied
 // directly to an ext-vector element (v.y) reads element 0 instead.
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }

@@ -70,7 +70,27 @@ struct GemmArgs {
   void* c;
   int64_t ld_a, ld_sa, ld_b, ld_sb, ld_c;  // bytes (codes, scales), elements (C)
   int32_t m, n, k;
+  bool sg_a, sg_b;  // scale bytes in the GEMM order (ld_s: 32-row group stride)
 };
+
+// Scale bytes of an operand tile of `rows` rows from row r0 (a multiple of
+// 32), row-major or in the GEMM order (scale_row_off).
+__device__ __forceinline__ rsrc_t scale_rsrc(const uint8_t* s, int64_t ld, bool gemm, int32_t r0,
+                                             int32_t rows) {
+  return make_rsrc(s + scale_row_off(r0, ld, gemm),
+                   (uint32_t)(gemm ? (int64_t)((rows + 31) / 32) * ld : (int64_t)rows * ld));
+}
+
+// Offset in that tile of the scale dword of row `row`, blocks blk .. blk + 3
+// (blk % 4 == 0, so the dword never crosses a row or an 8-block step). Both
+// offsets are computed and one is kept by a mask: a select on the flag
+// becomes a branch inside the K loop, which splits the loop's schedule.
+__device__ __forceinline__ uint32_t scale_dword_off(uint32_t row, uint32_t blk, uint32_t ld,
+                                                    bool gemm) {
+  const uint32_t rm = row * ld + blk;
+  const uint32_t go = (row >> 5) * ld + 8u * (row & 31u) + scale_col_off(blk, true);
+  return rm ^ ((rm ^ go) & (0u - (uint32_t)gemm));
+}
 
 struct OperandRsrc {
   rsrc_t a, sa, b, sb;
@@ -128,10 +148,11 @@ struct Tile {
       const bool is_a = __builtin_amdgcn_readfirstlane(e >> 6) < (uint32_t)(BM * kSW) / 64u;
       const rsrc_t rs = is_a ? q.sa : q.sb;
       const uint32_t row = is_a ? j : j - BM;
-      const uint32_t base = row * (uint32_t)(is_a ? g.ld_sa : g.ld_sb);
-      // blk is a multiple of 4 below nblk <= ld_s (a multiple of 4), so the
-      // dword stays inside the row; bytes past K are cleared when stored
-      r.s[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, blk < nblk ? base + blk : kOob, 0, 0);
+      const uint32_t off =
+          scale_dword_off(row, blk, (uint32_t)(is_a ? g.ld_sa : g.ld_sb), is_a ? g.sg_a : g.sg_b);
+      // blk is a multiple of 4 below nblk <= k / 32, so the dword stays
+      // inside the row; bytes past K are cleared when stored
+      r.s[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, blk < nblk ? off : kOob, 0, 0);
     }
   }
 
@@ -253,8 +274,8 @@ __global__ __launch_bounds__(64 * VM * VN) void mx_gemm_kernel(GemmArgs g) {
   OperandRsrc q;
   q.a = make_rsrc(g.a + (int64_t)m0 * g.ld_a, (uint32_t)(rows_a * g.ld_a));
   q.b = make_rsrc(g.b + (int64_t)n0 * g.ld_b, (uint32_t)(rows_b * g.ld_b));
-  q.sa = make_rsrc(g.sa + (int64_t)m0 * g.ld_sa, (uint32_t)(rows_a * g.ld_sa));
-  q.sb = make_rsrc(g.sb + (int64_t)n0 * g.ld_sb, (uint32_t)(rows_b * g.ld_sb));
+  q.sa = scale_rsrc(g.sa, g.ld_sa, g.sg_a, m0, rows_a);
+  q.sb = scale_rsrc(g.sb, g.ld_sb, g.sg_b, n0, rows_b);
 
   const uint32_t lane = threadIdx.x & 63u, r = lane & 31u, h = lane >> 5;
   const uint32_t w = threadIdx.x >> 6, wm = w / VN, wn = w % VN;
@@ -401,9 +422,9 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void mx_gemm_skinny_kernel(GemmA
   if (n0 >= g.n) return;  // padding of the grid to whole XCD rounds
   const int32_t rows_a = min(32 * MT, g.m - m0), rows_b = min(32 * NT, g.n - n0);
   const rsrc_t ra = make_rsrc(g.a + (int64_t)m0 * g.ld_a, (uint32_t)(rows_a * g.ld_a));
-  const rsrc_t rsa = make_rsrc(g.sa + (int64_t)m0 * g.ld_sa, (uint32_t)(rows_a * g.ld_sa));
+  const rsrc_t rsa = scale_rsrc(g.sa, g.ld_sa, g.sg_a, m0, rows_a);
   const rsrc_t rb = make_rsrc(g.b + (int64_t)n0 * g.ld_b, (uint32_t)(rows_b * g.ld_b));
-  const rsrc_t rsb = make_rsrc(g.sb + (int64_t)n0 * g.ld_sb, (uint32_t)(rows_b * g.ld_sb));
+  const rsrc_t rsb = scale_rsrc(g.sb, g.ld_sb, g.sg_b, n0, rows_b);
   const uint32_t lane = threadIdx.x & 63u, r = lane & 31u, h = lane >> 5;
   const int32_t w = (int32_t)(threadIdx.x >> 6);
   uint8_t* const lw = smem + kP * 4096u * (uint32_t)w;
@@ -418,8 +439,8 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void mx_gemm_skinny_kernel(GemmA
     const bool live = i < cnt;
     const uint32_t off = 128u * (uint32_t)s + 16u * (lane & 7u);
     const bool ok = live && off < kbytes;
-    // blk is a multiple of 4 below nblk <= ld_s (a multiple of 4): the dword
-    // stays inside the row; bytes past K are cleared before use
+    // blk is a multiple of 4 below nblk <= k / 32: the dword stays inside
+    // the row; bytes past K are cleared before use
     const uint32_t blk = 8u * (uint32_t)s + 4u * h;
     const bool oks = live && blk < nblk;
 #pragma unroll
@@ -434,8 +455,8 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void mx_gemm_skinny_kernel(GemmA
                                                           ok ? row * ld + off : kOob, 0, 0);
       }
       const uint32_t lds_ = (uint32_t)(pa ? g.ld_sa : g.ld_sb);
-      t.s[p] = __builtin_amdgcn_raw_buffer_load_b32(pa ? rsa : rsb,
-                                                    oks ? (base + r) * lds_ + blk : kOob, 0, 0);
+      const uint32_t so = scale_dword_off(base + r, blk, lds_, pa ? g.sg_a : g.sg_b);
+      t.s[p] = __builtin_amdgcn_raw_buffer_load_b32(pa ? rsa : rsb, oks ? so : kOob, 0, 0);
     }
   };
 
@@ -575,10 +596,11 @@ void launch_tiles(const GemmArgs& g, bool bf16_out, hipStream_t st) {
 
 void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a, const void* sa,
                     int64_t ld_sa, const void* b, int64_t ld_b, const void* sb, int64_t ld_sb,
-                    void* c, int64_t ld_c, bool bf16_out, hipStream_t st) {
+                    void* c, int64_t ld_c, bool bf16_out, bool sg_a, bool sg_b,
+                    hipStream_t st) {
   GemmArgs g{static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(sa),
              static_cast<const uint8_t*>(b), static_cast<const uint8_t*>(sb), c,
-             ld_a, ld_sa, ld_b, ld_sb, ld_c, (int32_t)m, (int32_t)n, (int32_t)k};
+             ld_a, ld_sa, ld_b, ld_sb, ld_c, (int32_t)m, (int32_t)n, (int32_t)k, sg_a, sg_b};
   // split-K tiles: two super-steps in flight per wave for 1 x 1 (7.6 us at
   // 16 x 8192 x 8192 against 9.8 with four), one for the wider tiles (their
   // larger steps already fill the caches' queues; two measured no faster)

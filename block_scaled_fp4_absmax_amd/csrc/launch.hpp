@@ -28,7 +28,8 @@ struct Shape {
   int64_t rows, cols;
   int64_t ld_x;  // bf16 input (or output, for dequantize) row stride, elements
   int64_t ld_c;  // code row stride, bytes
-  int64_t ld_s;  // scale row stride, bytes
+  int64_t ld_s;  // scale row stride, bytes (GEMM order: 32-row group stride)
+  bool s_gemm = false;  // MXFP4 scale bytes in the GEMM order (FP4_FLAG_SCALES_GEMM)
 };
 
 // MXFP4, or MXINT4 with mxint.
@@ -64,11 +65,11 @@ void launch_mx_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamar
 void launch_nv_dequant_unrotate(const Shape& s, const int32_t* perm, int hadamard, bool razer,
                                 const void* codes, const void* scales, const float* ts, void* out,
                                 hipStream_t st);
-// C = A B^T, MXFP4 operands (codes [rows, K/2], E8M0 scales [rows, K/32]);
-// fp32 or bf16 output.
+// C = A B^T, MXFP4 operands (codes [rows, K/2], E8M0 scales [rows, K/32], or
+// in the GEMM order with sg_a / sg_b); fp32 or bf16 output.
 void launch_mx_gemm(int64_t m, int64_t n, int64_t k, const void* a, int64_t ld_a, const void* sa,
                     int64_t ld_sa, const void* b, int64_t ld_b, const void* sb, int64_t ld_sb,
-                    void* c, int64_t ld_c, bool bf16_out, hipStream_t st);
+                    void* c, int64_t ld_c, bool bf16_out, bool sg_a, bool sg_b, hipStream_t st);
 // C = ta tb (A B^T), NVFP4 operands (codes [rows, K/2], E4M3 scales
 // [rows, K/16], RaZeR per operand), decoded exactly to bf16 for the MFMA.
 // mode_a: 0 plain or 1 RaZeR; mode_b: 0, 1 or 2 (RaZeR for weights).

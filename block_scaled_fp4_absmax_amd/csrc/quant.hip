@@ -28,6 +28,7 @@ struct Geom {
   uint32_t n;    // number of chunks = rows * cols / 8
   uint32_t cpr;  // chunks per row
   int64_t ld_x, ld_c, ld_s;
+  bool s_gemm;   // scale bytes in the GEMM order (never with kFlat)
 };
 
 template <bool kFlat, int kBlock>
@@ -41,7 +42,7 @@ __device__ __forceinline__ void locate(const Geom& g, uint32_t v, int64_t& xo, i
     uint32_t r = v / g.cpr, c = v - r * g.cpr;
     xo = r * g.ld_x + 8 * (int64_t)c;
     co = r * g.ld_c + 4 * (int64_t)c;
-    so = r * g.ld_s + (int64_t)(c / (kBlock / 8));
+    so = scale_row_off(r, g.ld_s, g.s_gemm) + scale_col_off(c / (kBlock / 8), g.s_gemm);
   }
 }
 
@@ -412,6 +413,7 @@ static inline Geom make_geom(const Shape& s, int block) {
   g.ld_x = s.ld_x;
   g.ld_c = s.ld_c;
   g.ld_s = s.ld_s;
+  g.s_gemm = s.s_gemm;
   (void)block;
   return g;
 }
@@ -423,7 +425,8 @@ template <bool kInt>
 static void mx_quant_variants(const Shape& s, bool floor_rule, const void* x, void* codes,
                               void* scales, hipStream_t st) {
   Geom g = make_geom(s, 32);
-  const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / 32;
+  const bool flat =
+      s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / 32 && !s.s_gemm;
   const int grid = grid_for(g.n);
   auto xp = static_cast<const uint16_t*>(x);
   auto cp = static_cast<uint8_t*>(codes);

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void mx_rotq_stream_mfma_kernel(
       const uint32_t r = kFlat ? 0u : b / (uint32_t)g.bpr;
       const uint32_t cb = kFlat ? b : b - r * (uint32_t)g.bpr;
       co[u] = r * g.ld_c + 16 * (int64_t)cb + 4 * q;
-      so[u] = r * g.ld_s + cb;
+      so[u] = scale_row_off(r, g.ld_s, g.s_gemm) + scale_col_off(cb, g.s_gemm);
       ro[u] = r * g.ld_rot + 32 * (int64_t)cb + 8 * q;
       d[u] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4_t*>(x + r * g.ld_x + 32 * (int64_t)cb + 8 * q));
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void mx_rotq_stream_bfly_kernel(
       uint32_t c = kFlat ? v : v - r * cpr;
       xo[u] = r * g.ld_x + 8 * (int64_t)c;
       co[u] = r * g.ld_c + 4 * (int64_t)c;
-      so[u] = r * g.ld_s + c / 4;
+      so[u] = scale_row_off(r, g.ld_s, g.s_gemm) + scale_col_off(c / 4, g.s_gemm);
       ro[u] = r * g.ld_rot + 8 * (int64_t)c;
       d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xo[u]));
     }
@@ -183,7 +183,7 @@ __device__ __forceinline__ RowRsrc row_rsrc(const uint16_t* x, uint8_t* codes, u
   RowRsrc q;
   q.x = make_rsrc(x + rr * g.ld_x, in ? 2u * (uint32_t)g.cols : 0u);
   q.c = make_rsrc(codes + rr * g.ld_c, in ? (uint32_t)g.cols / 2u : 0u);
-  q.s = make_rsrc(scales + rr * g.ld_s, in ? (uint32_t)g.spr : 0u);
+  q.s = make_rsrc(scales + scale_row_off(rr, g.ld_s, g.s_gemm), in ? (uint32_t)g.s_ext : 0u);
   if (kRot) q.rot = make_rsrc(rot + rr * g.ld_rot, in ? 4u * (uint32_t)g.cols : 0u);
   return q;
 }
@@ -299,7 +299,7 @@ __device__ __forceinline__ void perm_row(const Ctx& c, const uint8_t* buf, int32
             mx_quant16_pair<kOpt, kHad>(y, w0, w1, byte);
           else
             mxint_quant16_pair<kOpt, kHad>(y, w0, w1, byte);
-          so = ok && h == 0 ? (uint32_t)b : kOob;
+          so = ok && h == 0 ? scale_col_off((uint32_t)b, g.s_gemm) : kOob;
         } else {  // kOpt: RaZeR; lane h holds block 2 b + h
           nv_quant16<kOpt>(y, c.ns, c.rcp_tab, w0, w1, byte);
           so = ok ? 2u * b + h : kOob;

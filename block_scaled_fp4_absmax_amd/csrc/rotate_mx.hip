@@ -12,7 +12,7 @@ void launch_mx_rotate_quant(const Shape& s, const int32_t* perm, int hadamard, b
   auto cp = static_cast<uint8_t*>(codes);
   auto sp = static_cast<uint8_t*>(scales);
   const bool flat = s.ld_x == s.cols && s.ld_c == s.cols / 2 && s.ld_s == s.cols / 32 &&
-                    (!rot || ld_rot == s.cols);
+                    !s.s_gemm && (!rot || ld_rot == s.cols);
   if (mxint)
     mxint_rotate_quant(s, perm, hadamard != 0, floor_rule, xp, cp, sp, rot, g, flat, st);
   else

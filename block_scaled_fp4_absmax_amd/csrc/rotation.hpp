@@ -361,6 +361,8 @@ struct RotGeom {
   int32_t bpr;   // 32-element segments per row (MXFP4 blocks; two NVFP4 blocks each)
   uint32_t nblk; // rows * bpr
   int32_t spr;   // scale bytes per row: cols / block
+  int32_t s_ext; // bytes from a row's first scale byte past its last one
+  bool s_gemm;   // MXFP4 scale bytes in the GEMM order
   int64_t ld_x, ld_c, ld_s, ld_rot;
 };
 
@@ -377,6 +379,9 @@ inline RotGeom rot_geom(const Shape& s, int64_t ld_rot, int block = 32) {
   g.bpr = (int32_t)(s.cols / 32);
   g.nblk = (uint32_t)(s.rows * (s.cols / 32));
   g.spr = (int32_t)(s.cols / block);
+  g.s_gemm = s.s_gemm;
+  // GEMM order: block b of a row at 256 (b / 8) + b % 8
+  g.s_ext = !s.s_gemm ? g.spr : g.spr == 0 ? 0 : 256 * ((g.spr + 7) / 8 - 1) + 8;
   g.ld_x = s.ld_x;
   g.ld_c = s.ld_c;
   g.ld_s = s.ld_s;

@@ -66,6 +66,20 @@ enum fp4_mode { FP4_PLAIN = 0, FP4_RAZER = 1, FP4_RAZER_W = 2 };
  * MXINT4: floor(log2 amax) (elements above 1.75 * 2^e saturate) instead of the
  * default smallest e with amax <= 1.75 * 2^e. */
 #define FP4_FLAG_SCALE_OCP_FLOOR 2u
+/* MXFP4 only: scale bytes in the GEMM's order instead of [rows, ld_scales]
+ * (the scale layout that fp4_gemm reads fastest; [RaZeR] sec. 2.3, GEMM
+ * kernels fed by the quantizer's own output). Rows form groups of 32, and a
+ * group's scales are kept in steps of 256 elements of the row (8 blocks):
+ * the byte of row r, block b sits at
+ *     (r / 32) * ld_scales + (b / 8) * 256 + (r % 32) * 8 + b % 8,
+ * so each 256-element step of a 32-row group is 256 contiguous bytes. Here
+ * ld_scales is the stride between row groups: a multiple of 256, at least
+ * 256 * ceil(cols / 256); the array holds ceil(rows / 32) * ld_scales bytes.
+ * Bytes of rows past `rows` and of blocks past cols / 32 are never written
+ * and do not affect fp4_gemm's results. Taken by fp4_quantize and
+ * fp4_rotate_quantize in `flags`, and by fp4_gemm OR-ed into mode_a or
+ * mode_b (per operand). fp4_dequantize reads [rows, ld_scales] only. */
+#define FP4_FLAG_SCALES_GEMM 0x100u
 
 enum fp4_status {
   FP4_OK = 0,
@@ -126,7 +140,8 @@ const char* fp4_status_string(int status);
  *  flags        FP4_FLAG_* bits valid for the format
  *  codes        device, uint8 [rows, ld_codes]; 4-byte aligned, ld_codes % 4 == 0,
  *               ld_codes >= cols / 2
- *  scales       device, uint8 [rows, ld_scales], ld_scales >= cols / block
+ *  scales       device, uint8 [rows, ld_scales], ld_scales >= cols / block;
+ *               with FP4_FLAG_SCALES_GEMM the GEMM order above (MXFP4)
  *  tensor_scale NVFP4: device fp32[1], written (or read with the flag);
  *               MXFP4, MXINT4: ignored, may be NULL
  *  stream       hipStream_t
@@ -263,10 +278,16 @@ int fp4_dequantize_r(const void* codes, int64_t ld_codes, const void* scales, in
  *                       ld >= k / 2, 256 * ld < 2^31
  *  a_scales, b_scales   device, uint8; ld_s >= k / block, 256 * ld_s < 2^31;
  *                       MXFP4: 4-byte aligned, ld_s % 4 == 0; NVFP4: 2-byte
- *                       aligned, ld_s % 2 == 0 (bytes past k / block unused)
+ *                       aligned, ld_s % 2 == 0 (bytes past k / block unused).
+ *                       MXFP4 with FP4_FLAG_SCALES_GEMM in the operand's mode:
+ *                       the GEMM order (ld_s the 32-row group stride, a
+ *                       multiple of 256, >= 256 * ceil(k / 256)); each step of
+ *                       256 k then reads 256 contiguous bytes per 32 rows
+ *                       instead of 8 bytes from each of 32 rows
  *  a_ts, b_ts           NVFP4: device fp32[1] tensor scales; MXFP4: ignored
  *  mode_a, mode_b       FP4_PLAIN, or (NVFP4 only) FP4_RAZER; mode_b may also
- *                       be FP4_RAZER_W (E3M3 scale, four specials: weights)
+ *                       be FP4_RAZER_W (E3M3 scale, four specials: weights);
+ *                       MXFP4: FP4_PLAIN, optionally | FP4_FLAG_SCALES_GEMM
  *  m, n, k              >= 0, < 2^31; k % 32 == 0 (m or n zero: no work;
  *                       k zero: C = 0)
  *  format               FP4_MXFP4 or FP4_NVFP4

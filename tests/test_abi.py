@@ -158,6 +158,52 @@ def test_rotate_and_dequant_validation(L):
     assert E(None, 4, 64, 64, FAKE, None) == -1
 
 
+def test_gemm_scale_order_validation(L):
+    """FP4_FLAG_SCALES_GEMM: MXFP4 only, ld_scales a multiple of 256 covering
+    ceil(cols / 256) steps; in fp4_gemm it is OR-ed into an operand's mode."""
+    Fg = 0x100
+    Q = L.fp4_quantize
+    assert Q(FAKE, 4, 64, 64, 1, 16, 0, Fg, FAKE, 32, FAKE, 256, TS, None) == -4   # NVFP4
+    assert Q(FAKE, 4, 64, 64, 2, 32, 0, Fg, FAKE, 32, FAKE, 256, None, None) == -4  # MXINT4
+    assert Q(FAKE, 4, 64, 64, 0, 32, 0, Fg, FAKE, 32, FAKE, 2, None, None) == -2    # < 256
+    assert Q(FAKE, 4, 64, 64, 0, 32, 0, Fg, FAKE, 32, FAKE, 300, None, None) == -2  # % 256
+    assert Q(FAKE, 4, 512, 512, 0, 32, 0, Fg, FAKE, 256, FAKE, 256, None, None) == -2  # 2 steps
+    assert Q(None, 0, 512, 512, 0, 32, 0, Fg, None, 256, None, 512, None, None) == 0
+    assert Q(None, 0, 544, 544, 0, 32, 0, Fg | 2, None, 272, None, 768, None, None) == 0
+    R = L.fp4_rotate_quantize
+    assert R(FAKE, 4, 64, 64, None, 16, 1, 16, 0, Fg, FAKE, 32, FAKE, 256, TS, None, 0,
+             None) == -4
+    assert R(FAKE, 4, 64, 64, None, 32, 0, 32, 0, Fg, FAKE, 32, FAKE, 2, None, None, 0,
+             None) == -2
+    assert R(None, 0, 64, 64, None, 32, 0, 32, 0, Fg, None, 32, None, 256, None, None, 0,
+             None) == 0
+
+    def G(ma=0, mb=0, ldsa=4, ldsb=4, k=64, fmt=0, m=8, ta=None, tb=None):
+        return L.fp4_gemm(FAKE, 512, FAKE, ldsa, ta, ma, FAKE, 512, FAKE, ldsb, tb, mb, m, 8, k,
+                          fmt, 0, FAKE, 8, None)
+    assert G(ma=Fg, fmt=1, ta=TS, tb=TS) == -4   # NVFP4 scales have no GEMM order
+    assert G(ma=Fg) == -2                        # ld_sa must be a 256-byte step multiple
+    assert G(mb=Fg, ldsb=260) == -2
+    assert G(ma=Fg, ldsa=256, k=512) == -2       # two steps of 256 k need 512
+    assert G(ma=Fg | 1, ldsa=256) == -4          # RaZeR needs NVFP4
+    assert G(ma=Fg, mb=Fg, ldsa=512, ldsb=512, k=512, m=0) == 0
+
+
+def test_gemm_scale_shape_and_binding():
+    import torch
+    assert fp4.gemm_scale_shape(100, 8192) == (4, 8192)
+    assert fp4.gemm_scale_shape(32, 544) == (1, 768)
+    assert fp4.gemm_scale_shape(0, 0) == (0, 0)
+    with pytest.raises(ValueError, match="MXFP4"):
+        fp4._outputs(4, 64, fp4.NVFP4, None, gemm_scales=True)
+    c, s = fp4._outputs(33, 512, fp4.MXFP4, None, torch.zeros(33, 256, dtype=torch.uint8),
+                        torch.zeros(2, 512, dtype=torch.uint8), gemm_scales=True)
+    assert tuple(s.shape) == (2, 512)
+    with pytest.raises(ValueError, match="rows"):
+        fp4._outputs(33, 512, fp4.MXFP4, None, torch.zeros(33, 256, dtype=torch.uint8),
+                     torch.zeros(1, 512, dtype=torch.uint8), gemm_scales=True)
+
+
 def test_binding_raises_without_gpu_work():
     with pytest.raises(fp4.Fp4Error):
         fp4._check("fp4_quantize", -2)
