@@ -46,7 +46,7 @@ B_NV = 2 + 0.5 + 1 / 16   # NVFP4 quantize (without the tensor-amax read)
 
 MFMA_PEAK_BF16_TFLOPS = 2500.0
 ROT_KERNEL = "rotq_perm_kernel"  # fused permutation + Hadamard + FP4 quantize
-ROT_INSTANCE = ROT_KERNEL + "<2, 0, true, false, false>"  # the MXFP4 instance timed at 16384x8192
+ROT_INSTANCE = ROT_KERNEL + "<1, 0, true, false, false, 8>"  # the MXFP4 instance timed at 16384x8192
 ROT_SOURCES = ["block_scaled_fp4_absmax_amd/csrc/rotate_kernels.hpp",
                "block_scaled_fp4_absmax_amd/csrc/rotate_mx.hip",
                "block_scaled_fp4_absmax_amd/csrc/rotation.hpp",
@@ -367,7 +367,7 @@ def roofline_c4(elems, ms):
     r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
          "frac": round(achieved / HBM_PEAK_GBS, 4),
          "traffic": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1),
-         "kernel": ROT_KERNEL + "<2,0,true,false,false> (MXFP4; 2 MFMA tiles per wave per row)",
+         "kernel": ROT_KERNEL + "<1,0,true,false,false,8> (MXFP4; eight waves, one MFMA tile per wave per row)",
          "bytes_per_launch": int(elems * B_MX),
          "traffic_bytes_per_launch": traffic, "traffic_source": src,
          # the block Hadamard as a dense contraction: 2 x (32x32x16) MFMAs per 32 blocks
@@ -1002,8 +1002,8 @@ def kernel_op(torch, fp4, inputs, args):
         else:
             ps = [fp4.rotate_quantize(xs[k], perm, blk, codes=codes[k], scales=scales[k],
                                       prepare=True, **kw(k)) for k in range(n)]
-            kernel = ROT_KERNEL + ("<2, 1, true, true, false>" if nv
-                                   else "<2, 0, true, false, false>")
+            kernel = ROT_KERNEL + ("<1, 1, true, true, false, 8>" if nv
+                                   else "<1, 0, true, false, false, 8>")
         units, unit = rows * cols, "element"
     elif op.startswith("c2_"):
         x = inputs.gen_c2()

@@ -60,6 +60,7 @@ constexpr bool kUseMfma = FP4_HADAMARD_MFMA != 0;
 #define FP4_TILES 1
 #endif
 constexpr int kTiles = FP4_TILES;
+
 constexpr int kSpreadTiles = 2;
 
 // kInt: MXINT4 elements instead of E2M1.
@@ -154,12 +155,13 @@ __global__ __launch_bounds__(kThreads) void mx_rotq_stream_bfly_kernel(
 }
 
 // ================== permuting kernel (rows staged in LDS) ===================
-// A work-group walks rows r0 + k G (G = grid size) and stages each row in one
-// of two LDS buffers of 8192 kTpw bytes (cols <= 4096 kTpw), so a single
+// A work-group of kW waves walks rows r0 + k G (G = grid size) and stages
+// each row in one of two LDS buffers of 2048 kW kTpw bytes (cols <= 1024 kW
+// kTpw), so a single
 // barrier per row suffices: row k + 1 is written to one buffer while row k is
 // gathered from the other. Global loads run one row ahead in registers.
 //
-// Lane (n, h) of wave w handles, for i < kTpw, tile t = w + kWaves i: block
+// Lane (n, h) of wave w handles, for i < kTpw, tile t = w + kW i (kW waves): block
 // b = 32 t + n, elements e0 .. e0 + 15 with e0 = 32 b + 16 h, gathered from
 // row positions perm[e0 .. e0 + 15]. Those positions are the same for every
 // row, so each lane loads them once and keeps them in registers as LDS byte
@@ -188,20 +190,20 @@ __device__ __forceinline__ RowRsrc row_rsrc(const uint16_t* x, uint8_t* codes, u
   return q;
 }
 
-template <int kCpl>
+template <int kCpl, int kW = kWaves>
 __device__ __forceinline__ void load_row(rsrc_t src, int32_t cpr, u32x4_t* pre) {
 #pragma unroll
   for (int i = 0; i < kCpl; ++i) {
-    const int32_t c = threadIdx.x + i * kThreads;
+    const int32_t c = threadIdx.x + i * 64 * kW;
     pre[i] = __builtin_amdgcn_raw_buffer_load_b128(src, c < cpr ? 16u * c : kOob, 0, kNt);
   }
 }
 
-template <int kCpl>
+template <int kCpl, int kW = kWaves>
 __device__ __forceinline__ void put_row(uint8_t* buf, int32_t cpr, const u32x4_t* pre) {
 #pragma unroll
   for (int i = 0; i < kCpl; ++i) {
-    int32_t c = threadIdx.x + i * kThreads;
+    int32_t c = threadIdx.x + i * 64 * kW;
     if (c < cpr) reinterpret_cast<u32x4_t*>(buf)[c] = pre[i];
   }
 }
@@ -263,7 +265,8 @@ struct PermCtx {
 // and one scale-byte store (plus four 16-byte stores of the rotated values
 // with kRot), whether or not it holds a block: the count of memory
 // operations per row is fixed.
-template <int G, uint32_t kOff, int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot, class Ctx>
+template <int G, uint32_t kOff, int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot, class Ctx,
+          int kW = kWaves>
 __device__ __forceinline__ void perm_row(const Ctx& c, const uint8_t* buf, int32_t r) {
     // Cache policy of the code stores, measured on MI355X at 16384 x 8192:
     // plain write-back stores ran the MX formats faster than nontemporal ones
@@ -275,7 +278,7 @@ __device__ __forceinline__ void perm_row(const Ctx& c, const uint8_t* buf, int32
     const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
 #pragma unroll
     for (int i = 0; i < kTpw; ++i) {
-      const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kWaves * i) + (int32_t)n;
+      const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kW * i) + (int32_t)n;
       const bool ok = b < g.bpr;
       u32x4_t lo, hi;
       gather_tile<G, kOff>(buf, c.off[i], lo, hi);
@@ -329,11 +332,11 @@ __device__ __forceinline__ void perm_row(const Ctx& c, const uint8_t* buf, int32
 // so both buffer choices are compile-time constants and every path into a
 // step's wait has at least the steady state's memory operations after the
 // loads it waits for; a tail takes the last steps.
-template <int G, int kTpw, int kAhead, int kFmt, bool kHad, bool kOpt, bool kRot>
+template <int G, int kTpw, int kAhead, int kFmt, bool kHad, bool kOpt, bool kRot, int kW>
 struct PermRows {
   using Ctx = PermCtx<kTpw, kAhead>;
   static constexpr int kCpl = 2 * kTpw;
-  static constexpr uint32_t kBufBytes = 8192u * kTpw;
+  static constexpr uint32_t kBufBytes = 2048u * kW * kTpw;
   static constexpr int U = kAhead % 2 == 0 ? kAhead : 2 * kAhead;
 
   // kS = k mod U for the step of row k
@@ -343,11 +346,10 @@ struct PermRows {
     u32x4_t* pre = c.pre[(kS + 1) % kAhead];
     const RotGeom& g = c.g;
     const int32_t cpr = g.cols / 8;
-    if (has_next) put_row<kCpl>(c.sbuf + (1 - kBuf) * kBufBytes, cpr, pre);
-    load_row<kCpl>(row_rsrc<kRot>(c.x, c.codes, c.scales, c.rot,
-                                  r + (1 + kAhead) * (int32_t)gridDim.x, g).x,
-                   cpr, pre);
-    perm_row<G, kBuf * kBufBytes, kTpw, kFmt, kHad, kOpt, kRot>(c, c.sbuf, r);
+    if (has_next) put_row<kCpl, kW>(c.sbuf + (1 - kBuf) * kBufBytes, cpr, pre);
+    const int32_t ra = r + (1 + kAhead) * (int32_t)gridDim.x;
+    load_row<kCpl, kW>(row_rsrc<kRot>(c.x, c.codes, c.scales, c.rot, ra, g).x, cpr, pre);
+    perm_row<G, kBuf * kBufBytes, kTpw, kFmt, kHad, kOpt, kRot, Ctx, kW>(c, c.sbuf, r);
     __syncthreads();
   }
 
@@ -355,53 +357,63 @@ struct PermRows {
   template <int... us>
   static __device__ __forceinline__ void group(const Ctx& c, int32_t k, int32_t K,
                                                std::integer_sequence<int, us...>) {
-    const int32_t G_ = gridDim.x, r0 = blockIdx.x;
-    (step<(1 + us) % U>(c, r0 + (k + us) * G_, k + us + 1 < K), ...);
+    (step<(1 + us) % U>(c, row_of(k + us), k + us + 1 < K), ...);
   }
 
   // Steps k .. K - 1, fewer than U.
   template <int... us>
   static __device__ __forceinline__ void tail(const Ctx& c, int32_t k, int32_t K,
                                               std::integer_sequence<int, us...>) {
-    const int32_t G_ = gridDim.x, r0 = blockIdx.x;
-    (void)((k + us < K ? (step<(1 + us) % U>(c, r0 + (k + us) * G_, k + us + 1 < K), true)
+    (void)((k + us < K ? (step<(1 + us) % U>(c, row_of(k + us), k + us + 1 < K), true)
                        : false) &&
            ...);
+  }
+
+  // row of step k of this work-group
+  static __device__ __forceinline__ int32_t row_of(int32_t k) {
+    return (int32_t)blockIdx.x + k * (int32_t)gridDim.x;
   }
 
   static __device__ __forceinline__ void run(const Ctx& c) {
     const int32_t G_ = gridDim.x, r0 = blockIdx.x;
     const int32_t K = (c.g.rows - r0 + G_ - 1) / G_;
-    step<0>(c, r0, K > 1);
+    step<0>(c, row_of(0), K > 1);
     int32_t k = 1;
     for (; k + U - 1 < K; k += U) group(c, k, K, std::make_integer_sequence<int, U>{});
     tail(c, k, K, std::make_integer_sequence<int, U - 1>{});
   }
 };
 
-// Tuning per row length (kTpw tiles per wave per row; measured on MI355X at
-// cols = 8192): work-groups per CU in the grid, rows of look-ahead held in
-// registers, and the waves per SIMD the register allocation is held to. Two
-// row buffers of 8 KB kTpw each bound the work-groups a CU can hold; two per
-// CU (32 rows each at 16384 rows) ran faster than three or four, and one per
-// CU slower. A second row of look-ahead gained about 1%, more none. The NVFP4
-// variants, with more arithmetic per element, also ran slowest at three or
-// four per CU.
-template <int kTpw>
+// Tuning per row length (kTpw tiles per wave per row, kW waves per
+// work-group; measured on MI355X): work-groups per CU in the grid, rows of
+// look-ahead held in registers, and the waves per SIMD the register
+// allocation is held to. Two row buffers of 2 KB kW kTpw each bound the
+// work-groups a CU can hold. Rows of 4097..8192 columns run eight waves of
+// one tile each, two work-groups per CU (16 waves per CU): against four waves
+// of two tiles, each wave's share of a row step halves and twice as many
+// waves hide the gathers' LDS latency (16384 x 8192: MXFP4 56.0 -> 55.1 us,
+// NVFP4 + RaZeR 67.8 -> 63.9 us). Three such work-groups per CU (with one row
+// of look-ahead, to fit the registers) ran 11% slower; with four waves, three
+// or four work-groups per CU ran slower than two, and one slower still. A
+// second row of look-ahead gained about 1%, more none. Launching more
+// work-groups than fit at once (each taking fewer rows, placed as slots free
+// up) ran 8-14% slower: every work-group repeats the prologue and the ramp of
+// its row pipeline.
+template <int kTpw, int kW>
 constexpr int perm_wgs_per_cu() {
-  return kTpw == 1 ? 4 : kTpw <= 4 ? 2 : 1;
+  return kW == 8 ? 2 : kTpw == 1 ? 4 : kTpw <= 4 ? 2 : 1;
 }
 template <int kTpw>
 constexpr int perm_ahead() {
   return kTpw <= 2 ? 2 : 1;
 }
-template <int kTpw>
+template <int kTpw, int kW>
 constexpr int perm_waves_cap() {
-  return kTpw == 1 ? 4 : kTpw <= 4 ? 2 : 1;
+  return (perm_wgs_per_cu<kTpw, kW>() * kW + 3) / 4;
 }
 
 #ifndef FP4_PERM_WAVES
-#define FP4_PERM_WAVES perm_waves_cap<kTpw>()
+#define FP4_PERM_WAVES (perm_waves_cap<kTpw, kW>())
 #endif
 #ifndef FP4_PERM_AHEAD
 #define FP4_PERM_AHEAD perm_ahead<kTpw>()
@@ -412,26 +424,26 @@ constexpr int perm_waves_cap() {
 // holds s_t),
 // kFmtNvAmax (no stores; work-group i leaves its largest rotated magnitude in
 // the code slot of chunk i).
-template <int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot>
-__global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void rotq_perm_kernel(
+template <int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot, int kW>
+__global__ __launch_bounds__(64 * kW, FP4_PERM_WAVES) void rotq_perm_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, const float* __restrict__ ts, float* __restrict__ rot,
     RotGeom g) {
   constexpr int kCpl = 2 * kTpw;
   constexpr int kAhead = FP4_PERM_AHEAD;  // rows in flight in registers beyond the next
-  __shared__ __attribute__((aligned(16))) uint8_t sbuf[2 * 8192 * kTpw];
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf[2 * 2048 * kW * kTpw];
   __shared__ float rcp_tab[128];
   const int32_t cpr = g.cols / 8;
   // perm entries first, then rows 0 .. kAhead, so the row loads are in flight
   // while the entries are unpacked
   i32x4_t v[kTpw][4];
-  load_lane_perm<kTpw>(perm, g, v);
+  load_lane_perm<kTpw, kW>(perm, g, v);
   u32x4_t first[kCpl], pre[kAhead][kCpl];
-  load_row<kCpl>(row_rsrc<kRot>(x, codes, scales, rot, blockIdx.x, g).x, cpr, first);
+  auto prow = [&](int32_t j) { return (int32_t)blockIdx.x + j * (int32_t)gridDim.x; };
+  load_row<kCpl, kW>(row_rsrc<kRot>(x, codes, scales, rot, prow(0), g).x, cpr, first);
 #pragma unroll
   for (int j = 1; j <= kAhead; ++j)
-    load_row<kCpl>(row_rsrc<kRot>(x, codes, scales, rot, blockIdx.x + j * gridDim.x, g).x, cpr,
-                   pre[j % kAhead]);
+    load_row<kCpl, kW>(row_rsrc<kRot>(x, codes, scales, rot, prow(j), g).x, cpr, pre[j % kAhead]);
   NvScale ns{1.0f, 1.0f, true};
   if constexpr (kFmt == kFmtNv) {
     const float s_t = *ts;
@@ -439,13 +451,13 @@ __global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void rotq_perm_kernel(
     nv_rcp_table(rcp_tab, s_t);
   }
   uint32_t off[kTpw][8];
-  const int lr = pack_lane_perm<kTpw>(v, g, off);
+  const int lr = pack_lane_perm<kTpw, kW>(v, g, off);
   bf16x8_t a0, a1, m[3][2];
   if constexpr (kFmt == kFmtMxMat)
     matrix_operands(ts, false, m);
   else
     hadamard_operands<kFmt == kFmtMx || kFmt == kFmtMxInt ? 32 : 16>(a0, a1);
-  put_row<kCpl>(sbuf, cpr, first);
+  put_row<kCpl, kW>(sbuf, cpr, first);
   // run length agreed by the whole work-group (this also publishes row r0 and
   // the reciprocal table)
   const int run = __syncthreads_and(lr >= 8) ? 8
@@ -456,15 +468,15 @@ __global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void rotq_perm_kernel(
                                                  {m[2][0], m[2][1]}},
                           codes, scales, rot, g, pre, ns, rcp_tab, &amax};
   if (run == 8)
-    PermRows<8, kTpw, kAhead, kFmt, kHad, kOpt, kRot>::run(c);
+    PermRows<8, kTpw, kAhead, kFmt, kHad, kOpt, kRot, kW>::run(c);
   else if (run == 4)
-    PermRows<4, kTpw, kAhead, kFmt, kHad, kOpt, kRot>::run(c);
+    PermRows<4, kTpw, kAhead, kFmt, kHad, kOpt, kRot, kW>::run(c);
   else if (run == 2)
-    PermRows<2, kTpw, kAhead, kFmt, kHad, kOpt, kRot>::run(c);
+    PermRows<2, kTpw, kAhead, kFmt, kHad, kOpt, kRot, kW>::run(c);
   else
-    PermRows<1, kTpw, kAhead, kFmt, kHad, kOpt, kRot>::run(c);
+    PermRows<1, kTpw, kAhead, kFmt, kHad, kOpt, kRot, kW>::run(c);
   if constexpr (kFmt == kFmtNvAmax) {
-    const float m = block_max(amax, rcp_tab);
+    const float m = block_max<kW>(amax, rcp_tab);
     if (threadIdx.x == 0) *amax_partial_slot(codes, blockIdx.x, g) = __float_as_uint(m);
   }
 }
@@ -588,7 +600,7 @@ __device__ __forceinline__ void dma_prologue(const uint16_t* x, const RotGeom& g
 
 
 template <int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot>
-__global__ __launch_bounds__(kThreads, FP4_PERM_WAVES) void rotq_perm_dma_kernel(
+__global__ __launch_bounds__(kThreads, (perm_waves_cap<kTpw, kWaves>())) void rotq_perm_dma_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, const float* __restrict__ ts, float* __restrict__ rot,
     RotGeom g) {
@@ -729,27 +741,27 @@ __global__ __launch_bounds__(kThreads) void nv_rotq_stream_kernel(
 // only if every CU holds the same number of work-groups: the launch asks for
 // enough (unused) dynamic LDS that no more than perm_wgs_per_cu fit on a CU,
 // and launches exactly that many per CU.
-template <int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot>
+template <int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot, int kW = kWaves>
 static int perm_launch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
                        uint8_t* sc, const float* ts, float* rot, const RotGeom& g,
                        hipStream_t st) {
 #ifdef FP4_PERM_WG_PER_CU
   constexpr int kWgs = FP4_PERM_WG_PER_CU;
 #else
-  constexpr int kWgs = perm_wgs_per_cu<kTpw>();
+  constexpr int kWgs = perm_wgs_per_cu<kTpw, kW>();
 #endif
   const DeviceInfo ci = device_info();
   const int64_t wgs = (int64_t)ci.cus * kWgs;
   const int grid = (int)(s.rows < wgs ? s.rows : wgs);
-  constexpr size_t kStatic = 2 * 8192 * kTpw;
+  constexpr size_t kStatic = 2 * 2048 * kW * kTpw;
   const size_t share = (size_t)ci.lds / kWgs;  // > lds / (kWgs + 1), so kWgs fit, not more
   const size_t pad = share > kStatic + 1024 ? share - kStatic - 1024 : 0;
   if constexpr (kTpw > 4) {  // wide rows: staged by direct-to-LDS loads, one work-group per CU
     hipLaunchKernelGGL((rotq_perm_dma_kernel<kTpw, kFmt, kHad, kOpt, kRot>), dim3(grid),
                        dim3(kThreads), 0, st, x, perm, c, sc, ts, rot, g);
   } else {
-    hipLaunchKernelGGL((rotq_perm_kernel<kTpw, kFmt, kHad, kOpt, kRot>), dim3(grid),
-                       dim3(kThreads), pad, st, x, perm, c, sc, ts, rot, g);
+    hipLaunchKernelGGL((rotq_perm_kernel<kTpw, kFmt, kHad, kOpt, kRot, kW>), dim3(grid),
+                       dim3(64 * kW), pad, st, x, perm, c, sc, ts, rot, g);
   }
   return grid;
 }
@@ -759,10 +771,11 @@ template <int kFmt, bool kHad, bool kOpt, bool kRot>
 static int perm_dispatch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
                          uint8_t* sc, const float* ts, float* rot, const RotGeom& g,
                          hipStream_t st) {
-  // MFMA tiles (32 segments) per wave per row
+  // MFMA tiles (32 segments) per wave per row at four waves per work-group;
+  // rows of up to 8192 columns: eight waves of one tile
   const int64_t tpw = (s.cols + 32 * 32 * kWaves - 1) / (32 * 32 * kWaves);
   if (tpw <= 1) return perm_launch<1, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
-  if (tpw <= 2) return perm_launch<2, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
+  if (tpw <= 2) return perm_launch<1, kFmt, kHad, kOpt, kRot, 8>(s, perm, x, c, sc, ts, rot, g, st);
   if (tpw <= 3) return perm_launch<3, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
   if (tpw <= 4) return perm_launch<4, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
   if (tpw <= 6) return perm_launch<6, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);

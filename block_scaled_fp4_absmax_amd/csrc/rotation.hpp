@@ -400,6 +400,7 @@ __device__ __forceinline__ uint32_t* amax_partial_slot(uint8_t* codes, uint32_t 
 
 // Work-group maximum of a non-negative per-lane value; lane 0 of the
 // work-group receives it. red: kWaves floats of shared memory.
+template <int kW = kWaves>
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
@@ -407,13 +408,13 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   __syncthreads();
   float m = red[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) m = __builtin_fmaxf(m, red[i]);
+  for (int i = 1; i < kW; ++i) m = __builtin_fmaxf(m, red[i]);
   return m;
 }
 
 
 // ---- per-lane permutation entries (MFMA tile layout) ----------------------
-// Lane (n, h) of wave w handles, for i < kTpw, tile t = w + kWaves i: block
+// Lane (n, h) of wave w handles, for i < kTpw, tile t = w + kW i (kW waves): block
 // b = 32 t + n, elements e0 .. e0 + 15 with e0 = 32 b + 16 h, whose row
 // positions are perm[e0 .. e0 + 15]. The positions are the same for every
 // row, so a lane loads them once and keeps them as LDS byte offsets (clamped
@@ -421,14 +422,14 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 
 // Issue the loads of this lane's perm entries (16 per tile, zeros for tiles
 // past the row).
-template <int kTpw>
+template <int kTpw, int kW = kWaves>
 __device__ __forceinline__ void load_lane_perm(const int32_t* __restrict__ perm,
                                                const RotGeom& g, i32x4_t (*v)[4]) {
   const rsrc_t rp = make_rsrc(perm, 4u * (uint32_t)g.cols);
   const int32_t lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < kTpw; ++i) {
-    const int32_t b = 32 * (w + kWaves * i) + n;
+    const int32_t b = 32 * (w + kW * i) + n;
     const uint32_t o = b < g.bpr ? 4u * (32u * b + 16u * h) : kOob;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -440,7 +441,7 @@ __device__ __forceinline__ void load_lane_perm(const int32_t* __restrict__ perm,
 // Clamp to the row, convert to byte offsets packed in pairs, and return the
 // largest run length G in {8, 4, 2, 1} such that the lane's indices form
 // aligned runs of G consecutive channels (lanes without a block: 8).
-template <int kTpw>
+template <int kTpw, int kW = kWaves>
 __device__ __forceinline__ int pack_lane_perm(const i32x4_t (*v)[4], const RotGeom& g,
                                               uint32_t (*off)[8]) {
   const int32_t lane = threadIdx.x & 63, n = lane & 31, w = threadIdx.x >> 6;
@@ -456,7 +457,7 @@ __device__ __forceinline__ int pack_lane_perm(const i32x4_t (*v)[4], const RotGe
       p[4 * q + 2] = min(max(v[i][q].z, 0), cmax);
       p[4 * q + 3] = min(max(v[i][q].w, 0), cmax);
     }
-    if (32 * (w + kWaves * i) + n < g.bpr) {
+    if (32 * (w + kW * i) + n < g.bpr) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         r8 = r8 && p[k] == p[k & 8] + (k & 7) && (p[k & 8] & 7) == 0;
