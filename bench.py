@@ -512,7 +512,13 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     p3 = [fp4.rotate_quantize(t, None, 32, prepare=True) for t in x3s]
     ms = timed(torch, lambda i: p3[i % len(p3)].run(), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c3_mxfp4_h32_quantize"] = gbs(ms, r3 * k3, B_MX)
-    del p3, x3s
+    # the inverse: dequantize + H32 back to bf16 (codes of each input copy)
+    q3s = [fp4.rotate_quantize(t, None, 32)[:2] for t in x3s]
+    o3 = torch.empty_like(x3)
+    d3 = [fp4.dequantize(c, sc, fp4.MXFP4, hadamard=32, out=o3, prepare=True) for c, sc in q3s]
+    ms = timed(torch, lambda i: d3[i % len(d3)].run(), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
+    out["c3_mxfp4_dequantize_h32"] = gbs(ms, r3 * k3, B_MX)
+    del p3, x3s, q3s, d3, o3
     x3f = x3.float()
     q3 = {}
     for fmt, mode, had, name in ((fp4.MXFP4, fp4.PLAIN, 32, "mxfp4"),
@@ -997,8 +1003,8 @@ def kernel_op(torch, fp4, inputs, args):
                 ts_k = r[3] if nv else None
                 ps.append(fp4.dequantize(codes[k], scales[k], fmt, mode, ts_k, perm=perm,
                                          hadamard=blk, out=outs[k], prepare=True))
-            kernel = "dequant_unrotate_kernel<2, " + {fp4.MXFP4: "0,", fp4.NVFP4: "1,",
-                                                       fp4.MXINT4: "2,"}[fmt]
+            kernel = "dequant_unrotate_kernel<" + {fp4.MXFP4: "2, 0,", fp4.NVFP4: "1, 1,",
+                                                    fp4.MXINT4: "1, 2,"}[fmt]
         else:
             ps = [fp4.rotate_quantize(xs[k], perm, blk, codes=codes[k], scales=scales[k],
                                       prepare=True, **kw(k)) for k in range(n)]

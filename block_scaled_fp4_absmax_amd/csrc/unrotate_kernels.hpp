@@ -28,7 +28,27 @@ namespace fp4 {
 // work-group writes the row out with coalesced 16-byte stores. Rows alternate
 // between two LDS buffers with one barrier per row; the codes and scales of
 // the next kAhead rows are in flight in registers. Without a permutation the
-// lane stores its 32 contiguous bytes directly.
+// row takes the same way with the identity (16-byte LDS writes): each lane
+// storing its 32 contiguous bytes directly left every store instruction half
+// of each 128-byte line (MXFP4, 16384 x 8192: 74.8 us, against 61.3 with a
+// permutation).
+
+// The entries of the identity permutation in the layout of load_lane_perm
+// (zeros for tiles past the row).
+template <int kTpw, int kW = kWaves>
+__device__ __forceinline__ void identity_lane_perm(const RotGeom& g, i32x4_t (*v)[4]) {
+  const int32_t lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < kTpw; ++i) {
+    const int32_t b = 32 * (w + kW * i) + n;
+    const int32_t e0 = b < g.bpr ? 32 * b + 16 * h : 0;
+    const int32_t d = b < g.bpr ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[i][q] = i32x4_t{e0 + d * 4 * q, e0 + d * (4 * q + 1), e0 + d * (4 * q + 2),
+                        e0 + d * (4 * q + 3)};
+  }
+}
 
 // Per-row buffer resources of the inverse (empty for rows past the end).
 struct UnrotRsrc {
@@ -53,13 +73,13 @@ struct RowCodes {
 };
 
 // kNv: the lane's 16 elements are NVFP4 block 2 b + h with its own scale byte.
-template <int kTpw, bool kNv>
+template <int kTpw, bool kNv, int kW = kWaves>
 __device__ __forceinline__ void load_codes(const UnrotRsrc& q, const RotGeom& g,
                                            RowCodes<kTpw>& rc) {
   const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
 #pragma unroll
   for (int i = 0; i < kTpw; ++i) {
-    const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kWaves * i) + (int32_t)n;
+    const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kW * i) + (int32_t)n;
     const bool ok = b < g.bpr;
     rc.c[i] = __builtin_bit_cast(
         u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(q.c, ok ? 16u * b + 8u * h : kOob, 0, kNt));
@@ -232,12 +252,12 @@ struct UnrotCtx {
 // choice is a compile-time constant; a tail takes the last steps.
 // kFmt: the C ABI's format number; NVFP4 (kRazer: RaZeR codes) with the
 // 16-point transform, MXFP4 or MXINT4 with the 32-point one.
-template <int G, int kTpw, int kAhead, int kFmt, bool kRazer, bool kHad, bool kPerm>
+template <int G, int kTpw, int kAhead, int kFmt, bool kRazer, bool kHad, int kW>
 struct UnrotRows {
   static constexpr bool kNv = kFmt == 1;
   using Ctx = UnrotCtx<kTpw, kAhead>;
   static constexpr int kCpl = 2 * kTpw;
-  static constexpr uint32_t kBufBytes = 8192u * kTpw;
+  static constexpr uint32_t kBufBytes = 2048u * kW * kTpw;
   static constexpr int kRing = kAhead + 1;
   static constexpr int U = kRing % 2 == 0 ? kRing : 2 * kRing;
 
@@ -247,7 +267,7 @@ struct UnrotRows {
     RowCodes<kTpw>& rc = c.rc[kS % kRing];
     const RotGeom& g = c.g;
     const int32_t G_ = gridDim.x;
-    const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
+    const uint32_t n = threadIdx.x & 31u;
     u32x4_t lo[kTpw], hi[kTpw];
 #pragma unroll
     for (int i = 0; i < kTpw; ++i) {
@@ -258,30 +278,20 @@ struct UnrotRows {
       else
         unrotate_tile<kHad, kFmt == 2>(rc.c[i], rc.s[i], c.a0, c.a1, lo[i], hi[i]);
     }
-    load_codes<kTpw, kNv>(unrot_rsrc(c.codes, c.scales, c.out, r + kRing * G_, g), g, rc);
+    load_codes<kTpw, kNv, kW>(unrot_rsrc(c.codes, c.scales, c.out, r + kRing * G_, g), g, rc);
     const UnrotRsrc q = unrot_rsrc(c.codes, c.scales, c.out, r, g);
-    if constexpr (kPerm) {
 #pragma unroll
-      for (int i = 0; i < kTpw; ++i) {  // lanes without a block (offsets 0) write nothing
-        const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kWaves * i) + (int32_t)n;
-        if (b < g.bpr) scatter_tile<G, kBuf * kBufBytes>(c.sbuf, c.off[i], lo[i], hi[i]);
-      }
-      __syncthreads();
-      const int32_t cpr = g.cols / 8;
+    for (int i = 0; i < kTpw; ++i) {  // lanes without a block (offsets 0) write nothing
+      const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kW * i) + (int32_t)n;
+      if (b < g.bpr) scatter_tile<G, kBuf * kBufBytes>(c.sbuf, c.off[i], lo[i], hi[i]);
+    }
+    __syncthreads();
+    const int32_t cpr = g.cols / 8;
 #pragma unroll
-      for (int i = 0; i < kCpl; ++i) {
-        const int32_t ch = threadIdx.x + i * kThreads;
-        const u32x4_t v = reinterpret_cast<const u32x4_t*>(c.sbuf + kBuf * kBufBytes)[ch < cpr ? ch : 0];
-        __builtin_amdgcn_raw_buffer_store_b128(v, q.o, ch < cpr ? 16u * ch : kOob, 0, kNt);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kTpw; ++i) {
-        const int32_t b = 32 * ((int32_t)(threadIdx.x >> 6) + kWaves * i) + (int32_t)n;
-        const uint32_t o = b < g.bpr ? 64u * b + 32u * h : kOob;
-        __builtin_amdgcn_raw_buffer_store_b128(lo[i], q.o, o, 0, kNt);
-        __builtin_amdgcn_raw_buffer_store_b128(hi[i], q.o, o == kOob ? kOob : o + 16u, 0, kNt);
-      }
+    for (int i = 0; i < kCpl; ++i) {
+      const int32_t ch = threadIdx.x + i * 64 * kW;
+      const u32x4_t v = reinterpret_cast<const u32x4_t*>(c.sbuf + kBuf * kBufBytes)[ch < cpr ? ch : 0];
+      __builtin_amdgcn_raw_buffer_store_b128(v, q.o, ch < cpr ? 16u * ch : kOob, 0, kNt);
     }
   }
 
@@ -312,9 +322,29 @@ struct UnrotRows {
 // codes in flight (a row's codes take 3 registers per tile). One work-group
 // per CU ran about 2% faster than two and 7% faster than four; the
 // look-ahead made little difference.
-template <int kTpw>
+// Eight waves of one tile (two work-groups per CU for MXINT4, one for
+// NVFP4) instead of four waves of two tiles, for rows of 4097..8192 columns
+// in the formats with the most arithmetic per element. 16384 x 8192 with a
+// permutation: NVFP4 + RaZeR 71.1 -> 63.0 us, MXINT4 72.1 -> 62.7 us; MXFP4
+// (61.3 -> 62.2) and the learned matrix (61.8 -> 62.6) keep four waves.
+// FP4_UNROT_W8 = 0 or 1 forces one choice for every format.
+#ifndef FP4_UNROT_W8
+#define FP4_UNROT_W8 (-1)
+#endif
+template <int kFmt, bool kPerm>
+constexpr bool unrot_eight_waves() {
+  return FP4_UNROT_W8 >= 0 ? FP4_UNROT_W8 != 0 : kFmt == 1 || kFmt == 2;
+}
+template <int kTpw, int kW, int kFmt>
 constexpr int unrot_wgs_per_cu() {
-  return kTpw == 1 ? 2 : 1;
+#ifdef FP4_UNROT_W8_WGS
+  if (kW == 8) return FP4_UNROT_W8_WGS;
+#endif
+  return kW == 8 ? (kFmt == 2 ? 2 : 1) : kTpw == 1 ? 2 : 1;
+}
+template <int kTpw, int kW, int kFmt>
+constexpr int unrot_waves_cap() {
+  return kW == 8 ? 2 * unrot_wgs_per_cu<kTpw, kW, kFmt>() : kTpw >= 3 ? 1 : 2;
 }
 #ifndef FP4_UNROT_AHEAD
 #define FP4_UNROT_AHEAD 3
@@ -325,25 +355,27 @@ constexpr int unrot_wgs_per_cu() {
 // one; 3: MXFP4 with the transpose of the learned 32x32 matrix at ts.
 // Wide rows (three or four tiles per wave) run one work-group per CU, one
 // wave per SIMD, so they may use the whole register file.
-template <int kTpw, int kFmt, bool kRazer, bool kHad, bool kPerm>
-__global__ __launch_bounds__(kThreads, kTpw >= 3 ? 1 : 2) void dequant_unrotate_kernel(
+template <int kTpw, int kFmt, bool kRazer, bool kHad, bool kPerm, int kW>
+__global__ __launch_bounds__(64 * kW, (unrot_waves_cap<kTpw, kW, kFmt>())) void dequant_unrotate_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ ts, const int32_t* __restrict__ perm, uint16_t* __restrict__ out,
     RotGeom g) {
   // the learned matrix holds 24 more registers: less look-ahead on wide rows
   constexpr int kAhead = kFmt == 3 && kTpw >= 3 ? 1 : FP4_UNROT_AHEAD;
   constexpr bool kNv = kFmt == 1;
-  __shared__ __attribute__((aligned(16))) uint8_t sbuf[kPerm ? 2 * 8192 * kTpw : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf[2 * 2048 * kW * kTpw];
   i32x4_t v[kTpw][4];
-  if (kPerm) load_lane_perm<kTpw>(perm, g, v);
+  if constexpr (kPerm)
+    load_lane_perm<kTpw, kW>(perm, g, v);
+  else
+    identity_lane_perm<kTpw, kW>(g, v);
   RowCodes<kTpw> rc[kAhead + 1];
 #pragma unroll
   for (int j = 0; j <= kAhead; ++j)
-    load_codes<kTpw, kNv>(unrot_rsrc(codes, scales, out, (int32_t)(blockIdx.x + j * gridDim.x), g),
-                          g, rc[j]);
+    load_codes<kTpw, kNv, kW>(
+        unrot_rsrc(codes, scales, out, (int32_t)(blockIdx.x + j * gridDim.x), g), g, rc[j]);
   uint32_t off[kTpw][8];
-  int lr = 8;
-  if (kPerm) lr = pack_lane_perm<kTpw>(v, g, off);
+  const int lr = pack_lane_perm<kTpw, kW>(v, g, off);
   bf16x8_t a0, a1, m[3][2];
   if constexpr (kFmt == 3)
     matrix_operands(ts, true, m);
@@ -361,42 +393,38 @@ __global__ __launch_bounds__(kThreads, kTpw >= 3 ? 1 : 2) void dequant_unrotate_
                            g,
                            rc,
                            s_t};
-  if constexpr (kPerm) {
-    // run length agreed by the whole work-group
-    const int run = __syncthreads_and(lr >= 8) ? 8
-                    : __syncthreads_and(lr >= 4) ? 4
-                    : __syncthreads_and(lr >= 2) ? 2 : 1;
-    if (run == 8)
-      UnrotRows<8, kTpw, kAhead, kFmt, kRazer, kHad, true>::run(c);
-    else if (run == 4)
-      UnrotRows<4, kTpw, kAhead, kFmt, kRazer, kHad, true>::run(c);
-    else if (run == 2)
-      UnrotRows<2, kTpw, kAhead, kFmt, kRazer, kHad, true>::run(c);
-    else
-      UnrotRows<1, kTpw, kAhead, kFmt, kRazer, kHad, true>::run(c);
-  } else {
-    UnrotRows<8, kTpw, kAhead, kFmt, kRazer, kHad, false>::run(c);
-  }
+  // run length agreed by the whole work-group (8 for the identity)
+  const int run = !kPerm || __syncthreads_and(lr >= 8) ? 8
+                  : __syncthreads_and(lr >= 4) ? 4
+                  : __syncthreads_and(lr >= 2) ? 2 : 1;
+  if (run == 8)
+    UnrotRows<8, kTpw, kAhead, kFmt, kRazer, kHad, kW>::run(c);
+  else if (run == 4)
+    UnrotRows<4, kTpw, kAhead, kFmt, kRazer, kHad, kW>::run(c);
+  else if (run == 2)
+    UnrotRows<2, kTpw, kAhead, kFmt, kRazer, kHad, kW>::run(c);
+  else
+    UnrotRows<1, kTpw, kAhead, kFmt, kRazer, kHad, kW>::run(c);
 }
 
 // ================================ launchers =================================
-template <int kTpw, int kFmt, bool kRazer, bool kHad, bool kPerm>
+template <int kTpw, int kFmt, bool kRazer, bool kHad, bool kPerm, int kW = kWaves>
 static void unrot_launch(const Shape& s, const int32_t* perm, const uint8_t* c, const uint8_t* sc,
                          const float* ts, uint16_t* o, const RotGeom& g, hipStream_t st) {
   // as for the forward kernel: pad LDS so that exactly kWgs work-groups fit per CU
 #ifdef FP4_UNROT_WG_PER_CU
   constexpr int kWgs = FP4_UNROT_WG_PER_CU;
 #else
-  constexpr int kWgs = unrot_wgs_per_cu<kTpw>();
+  constexpr int kWgs = unrot_wgs_per_cu<kTpw, kW, kFmt>();
 #endif
   const DeviceInfo di = device_info();
   const int64_t wgs = (int64_t)di.cus * kWgs;
   const int grid = (int)(s.rows < wgs ? s.rows : wgs);
-  constexpr size_t kStatic = kPerm ? 2 * 8192 * kTpw : 16;
+  constexpr size_t kStatic = 2 * 2048 * kW * kTpw;
   const size_t share = (size_t)di.lds / kWgs;
   const size_t pad = share > kStatic + 1024 ? share - kStatic - 1024 : 0;
-  hipLaunchKernelGGL((dequant_unrotate_kernel<kTpw, kFmt, kRazer, kHad, kPerm>), dim3(grid),
-                     dim3(kThreads), pad, st, c, sc, ts, perm, o, g);
+  hipLaunchKernelGGL((dequant_unrotate_kernel<kTpw, kFmt, kRazer, kHad, kPerm, kW>), dim3(grid),
+                     dim3(64 * kW), pad, st, c, sc, ts, perm, o, g);
 }
 
 template <int kFmt, bool kRazer, bool kHad, bool kPerm>
@@ -405,6 +433,8 @@ static void unrot_dispatch(const Shape& s, const int32_t* perm, const uint8_t* c
                            hipStream_t st) {
   const int64_t tpw = (s.cols + 32 * 32 * kWaves - 1) / (32 * 32 * kWaves);
   if (tpw <= 1) unrot_launch<1, kFmt, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
+  else if (tpw <= 2 && unrot_eight_waves<kFmt, kPerm>())
+    unrot_launch<1, kFmt, kRazer, kHad, kPerm, 8>(s, perm, c, sc, ts, o, g, st);
   else if (tpw <= 2) unrot_launch<2, kFmt, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
   else if (tpw <= 3) unrot_launch<3, kFmt, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);
   else unrot_launch<4, kFmt, kRazer, kHad, kPerm>(s, perm, c, sc, ts, o, g, st);

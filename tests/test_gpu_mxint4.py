@@ -172,7 +172,8 @@ def test_mxint4_rotation_ragged(orc, rows, cols, use_perm):
 
 @pytest.mark.parametrize("rows,cols,kind,had", [
     (256, 4096, 1, 32), (3, 96, 1, 32), (37, 2080, 1, 32), (5, 16384, 1, 32), (1537, 8192, 1, 32),
-    (300, 8192, 4, 32), (300, 8192, 1, 0), (1537, 8192, None, 32)])
+    (300, 8192, 4, 32), (300, 8192, 1, 0), (1537, 8192, None, 32), (7, 5152, 1, 32),
+    (7, 5152, None, 32)])
 def test_mxint4_dequant_unrotate(orc, rows, cols, kind, had):
     note(f"case: MXINT4 dequantize + inverse rotation {rows}x{cols} perm runs={kind} H{had}")
     x = inputs.gen_c3(rows=rows, cols=cols)

@@ -214,7 +214,8 @@ def test_nv_dequant_unrotate_round_trip(orc, razer):
 @pytest.mark.parametrize("rows,cols,kind,had", [
     (3, 96, 1, 16), (37, 2080, 1, 16), (6, 8224, 1, 16), (5, 16384, 1, 16),
     (1537, 8192, 1, 16), (2500, 1024, 1, 16), (300, 8192, 8, 16), (300, 8192, 2, 16),
-    (300, 8192, 1, 0), (1537, 8192, None, 16), (37, 2080, None, 16)])
+    (300, 8192, 1, 0), (1537, 8192, None, 16), (37, 2080, None, 16), (7, 5152, 1, 16),
+    (7, 5152, None, 16), (3, 4128, 1, 16)])
 def test_nv_dequant_unrotate_shapes(orc, rows, cols, kind, had):
     note(f"case: NVFP4 dequantize + inverse rotation {rows}x{cols} perm runs={kind} H{had}")
     x = inputs.gen_c3(rows=rows, cols=cols)

@@ -278,10 +278,11 @@ def test_rotate_grouped_permutation(orc, group):
 
 
 # cols 96 .. 16384 cover one to four MFMA tiles per wave per row (partial
-# tiles at 2080 and 8224); 1537 and 2500 rows give work-groups unequal row
+# tiles at 2080 and 8224; 4128 and 5152 leave waves of the eight-wave
+# work-group without a block); 1537 and 2500 rows give work-groups unequal row
 # counts, odd and even, in the row-at-a-time permuting kernel
 @pytest.mark.parametrize("rows,cols", [(3, 96), (37, 2080), (5, 16384), (6, 8224), (4, 12288),
-                                       (1537, 8192), (2500, 1024)])
+                                       (1537, 8192), (2500, 1024), (7, 5152), (3, 4128)])
 def test_rotate_ragged(orc, rows, cols):
     note(f"case: rotate ragged {rows}x{cols}")
     x = inputs.gen_c3(rows=rows, cols=cols)
@@ -406,7 +407,8 @@ def test_dequant_unrotate(orc, perm_on):
 @pytest.mark.parametrize("rows,cols,kind,had", [
     (3, 96, 1, 32), (37, 2080, 1, 32), (6, 8224, 1, 32), (5, 16384, 1, 32), (4, 12288, 1, 32),
     (1537, 8192, 1, 32), (2500, 1024, 1, 32), (300, 8192, 2, 32), (300, 8192, 4, 32),
-    (300, 8192, 8, 32), (300, 8192, 1, 0), (1537, 8192, None, 32), (37, 2080, None, 32)])
+    (300, 8192, 8, 32), (300, 8192, 1, 0), (1537, 8192, None, 32), (37, 2080, None, 32),
+    (7, 5152, 1, 32), (7, 5152, None, 32), (3, 4128, None, 32)])
 def test_dequant_unrotate_shapes(orc, rows, cols, kind, had):
     note(f"case: dequantize + inverse rotation {rows}x{cols} perm runs={kind} H{had}")
     x = inputs.gen_c3(rows=rows, cols=cols)
