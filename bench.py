@@ -591,6 +591,49 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     del ys, cs, ss
     out["c1_mxfp4"] = c1_rows(torch, fp4, inputs)
     out["c5_layer_nvfp4_razer"] = c5_rows(torch, fp4, inputs)
+    out["wide_rows_8192x28672"] = wide_rows(torch, fp4, inputs)
+    return out
+
+
+def wide_rows(torch, fp4, inputs):
+    """The two-level rotation on rows as wide as the down projection's input
+    (8192 x 28672, the c4 recipe at that width): the LDS-ring permuting kernel
+    per format, beside plain MXFP4 quantization of the same tensor."""
+    rows, cols = 8192, 28672
+    log(f"[bench] generating {rows}x{cols} for the wide-row rotation rows")
+    x = inputs.gen_c4(rows=rows, cols=cols)
+    xs = dev_copies(torch, x, copies_for(x.nbytes))
+    del x
+    n = len(xs)
+    el = rows * cols
+    perm = fp4.build_permutation(fp4.channel_energy(xs[0])).cuda()
+    perm16 = fp4.build_permutation(fp4.channel_energy(xs[0]), 16).cuda()
+    codes = [torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda") for _ in range(n)]
+    s32 = [torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda") for _ in range(n)]
+    s16 = [torch.empty((rows, cols // 16), dtype=torch.uint8, device="cuda") for _ in range(n)]
+    t16 = [fp4.rotate_quantize(xs[k], perm16, 16, codes=codes[k], scales=s16[k], fmt=fp4.NVFP4,
+                               mode=fp4.RAZER)[3] for k in range(n)]
+
+    def row(make, per_el):
+        ps = [make(k) for k in range(n)]
+        ms = timed(torch, lambda i: ps[i % n].run(), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
+        return {"ms": round(ms, 5), "input_GBps": round(el * 2 / ms / 1e6, 1),
+                "algorithmic_GBps": round(el * per_el / ms / 1e6, 1),
+                "frac_hbm": round(el * per_el / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+    out = {
+        "mxfp4_plain_quantize": row(lambda k: fp4.quantize(xs[k], fp4.MXFP4, codes=codes[k],
+                                                           scales=s32[k], prepare=True), B_MX),
+        "mxfp4_perm_h32_quantize": row(lambda k: fp4.rotate_quantize(
+            xs[k], perm, 32, codes=codes[k], scales=s32[k], prepare=True), B_MX),
+        "mxint4_perm_h32_quantize": row(lambda k: fp4.rotate_quantize(
+            xs[k], perm, 32, codes=codes[k], scales=s32[k], fmt=fp4.MXINT4, prepare=True), B_MX),
+        "nvfp4_razer_perm_h16_scale_given": row(lambda k: fp4.rotate_quantize(
+            xs[k], perm16, 16, codes=codes[k], scales=s16[k], fmt=fp4.NVFP4, mode=fp4.RAZER,
+            tensor_scale=t16[k], scale_given=True, prepare=True), B_NV),
+    }
+    del xs, codes, s32, s16
+    torch.cuda.empty_cache()
     return out
 
 

@@ -498,9 +498,9 @@ __global__ __launch_bounds__(64 * kW, FP4_PERM_WAVES) void rotq_perm_kernel(
 // work-group fence would wait for every load in flight.
 // The ring buffers are separate LDS objects so that the compiler sees which
 // buffer each read touches and does not wait for loads into the others.
-template <int kTpw, int kSlot>
+template <int kTpw, int kW, int kSlot>
 __device__ __forceinline__ uint8_t* ring_buf() {
-  __shared__ __attribute__((aligned(16))) uint8_t b[8192 * kTpw];
+  __shared__ __attribute__((aligned(16))) uint8_t b[2048 * kW * kTpw];
   return b;
 }
 
@@ -521,16 +521,16 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// This wave's share of a row: operation u moves chunk c = u kThreads + 64 w +
+// This wave's share of a row: operation u moves chunk c = 64 (u kW + w) +
 // lane (16 bytes) of the row to buf + 16 c; chunks past the row read nothing.
-template <int kCpl>
+template <int kCpl, int kW>
 __device__ __forceinline__ void dma_row(rsrc_t src, uint8_t* buf, int32_t cpr) {
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int u = 0; u < kCpl; ++u) {
-    const int32_t c = threadIdx.x + u * kThreads;
+    const int32_t c = threadIdx.x + u * 64 * kW;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        src, (__attribute__((address_space(3))) void*)(buf + 16 * (u * kThreads + 64 * w)), 16,
+        src, (__attribute__((address_space(3))) void*)(buf + 16 * (u * 64 * kW + 64 * w)), 16,
         c < cpr ? 16u * (uint32_t)c : kOob, 0, 0, kNt);
   }
 }
@@ -552,7 +552,7 @@ __device__ __forceinline__ RowMap row_map(int32_t rows) {
   return RowMap{g, G_, (rows - g + G_ - 1) / G_, (rows + G_ - 1) / G_};
 }
 
-template <int G, int kTpw, int kNB, int kFmt, bool kHad, bool kOpt, bool kRot>
+template <int G, int kTpw, int kNB, int kFmt, bool kHad, bool kOpt, bool kRot, int kW>
 struct DmaRows {
   using Ctx = PermCtx<kTpw, 1>;
   static constexpr int kCpl = 2 * kTpw;
@@ -566,10 +566,10 @@ struct DmaRows {
     constexpr int kSince = kFirst ? kSt : kNB - 1;
     wait_vmcnt<(kNB - 2) * kCpl + kSince * kS>();
     lds_barrier();
-    dma_row<kCpl>(row_rsrc<false>(c.x, c.codes, c.scales, c.rot, m.row(k + kNB - 1), c.g).x,
-                  ring_buf<kTpw, (kSt + kNB - 1) % kNB>(), c.g.cols / 8);
+    dma_row<kCpl, kW>(row_rsrc<false>(c.x, c.codes, c.scales, c.rot, m.row(k + kNB - 1), c.g).x,
+                      ring_buf<kTpw, kW, (kSt + kNB - 1) % kNB>(), c.g.cols / 8);
     __builtin_amdgcn_sched_barrier(0);
-    perm_row<G, 0, kTpw, kFmt, kHad, kOpt, kRot>(c, ring_buf<kTpw, kSt>(), m.row(k));
+    perm_row<G, 0, kTpw, kFmt, kHad, kOpt, kRot, Ctx, kW>(c, ring_buf<kTpw, kW, kSt>(), m.row(k));
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -588,34 +588,35 @@ struct DmaRows {
   }
 };
 
-template <int kTpw, int kNB, int j>
+template <int kTpw, int kW, int kNB, int j>
 __device__ __forceinline__ void dma_prologue(const uint16_t* x, const RotGeom& g,
                                              const RowMap& m) {
   if constexpr (j < kNB - 1) {
-    dma_row<2 * kTpw>(row_rsrc<false>(x, nullptr, nullptr, nullptr, m.row(j), g).x,
-                      ring_buf<kTpw, j>(), g.cols / 8);
-    dma_prologue<kTpw, kNB, j + 1>(x, g, m);
+    dma_row<2 * kTpw, kW>(row_rsrc<false>(x, nullptr, nullptr, nullptr, m.row(j), g).x,
+                          ring_buf<kTpw, kW, j>(), g.cols / 8);
+    dma_prologue<kTpw, kW, kNB, j + 1>(x, g, m);
   }
 }
 
 
-template <int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot>
-__global__ __launch_bounds__(kThreads, (perm_waves_cap<kTpw, kWaves>())) void rotq_perm_dma_kernel(
+template <int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot, int kW, int kWgs>
+__global__ __launch_bounds__(64 * kW, (kW * kWgs + 3) / 4) void rotq_perm_dma_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, const float* __restrict__ ts, float* __restrict__ rot,
     RotGeom g) {
-  // as many row buffers as fit in 152 KB of LDS, at most four
-  constexpr int kNBmax = (152 * 1024) / (8192 * kTpw);
+  // as many row buffers as fit in this work-group's share of 152 KB of LDS
+  // (kWgs work-groups per CU), at most four
+  constexpr int kNBmax = (152 * 1024 / kWgs) / (2048 * kW * kTpw);
   constexpr int kNB = kNBmax < 4 ? kNBmax : 4;
   static_assert(kNB >= 2, "two row buffers at least");
   __shared__ float rcp_tab[128];
-  __shared__ uint32_t vote[kWaves];
+  __shared__ uint32_t vote[kW];
   // perm entries first, then the first kNB - 1 rows, so the row loads are in
   // flight while the entries are unpacked
   i32x4_t v[kTpw][4];
-  load_lane_perm<kTpw>(perm, g, v);
+  load_lane_perm<kTpw, kW>(perm, g, v);
   const RowMap rm = row_map(g.rows);
-  dma_prologue<kTpw, kNB, 0>(x, g, rm);
+  dma_prologue<kTpw, kW, kNB, 0>(x, g, rm);
   NvScale ns{1.0f, 1.0f, true};
   if constexpr (kFmt == kFmtNv) {
     const float s_t = *ts;
@@ -623,7 +624,7 @@ __global__ __launch_bounds__(kThreads, (perm_waves_cap<kTpw, kWaves>())) void ro
     nv_rcp_table(rcp_tab, s_t);
   }
   uint32_t off[kTpw][8];
-  const int lr = pack_lane_perm<kTpw>(v, g, off);
+  const int lr = pack_lane_perm<kTpw, kW>(v, g, off);
   bf16x8_t a0, a1, m[3][2];
   if constexpr (kFmt == kFmtMxMat)
     matrix_operands(ts, false, m);
@@ -639,23 +640,23 @@ __global__ __launch_bounds__(kThreads, (perm_waves_cap<kTpw, kWaves>())) void ro
   lds_barrier();
   uint32_t all = vote[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) all &= vote[i];
+  for (int i = 1; i < kW; ++i) all &= vote[i];
   const int run = (all & 4u) ? 8 : (all & 2u) ? 4 : (all & 1u) ? 2 : 1;
   float amax = 0.0f;
   PermCtx<kTpw, 1> c{x, nullptr, off, a0, a1, {{m[0][0], m[0][1]}, {m[1][0], m[1][1]},
                                                {m[2][0], m[2][1]}},
                      codes, scales, rot, g, nullptr, ns, rcp_tab, &amax};
   if (run == 8)
-    DmaRows<8, kTpw, kNB, kFmt, kHad, kOpt, kRot>::run(c, rm);
+    DmaRows<8, kTpw, kNB, kFmt, kHad, kOpt, kRot, kW>::run(c, rm);
   else if (run == 4)
-    DmaRows<4, kTpw, kNB, kFmt, kHad, kOpt, kRot>::run(c, rm);
+    DmaRows<4, kTpw, kNB, kFmt, kHad, kOpt, kRot, kW>::run(c, rm);
   else if (run == 2)
-    DmaRows<2, kTpw, kNB, kFmt, kHad, kOpt, kRot>::run(c, rm);
+    DmaRows<2, kTpw, kNB, kFmt, kHad, kOpt, kRot, kW>::run(c, rm);
   else
-    DmaRows<1, kTpw, kNB, kFmt, kHad, kOpt, kRot>::run(c, rm);
+    DmaRows<1, kTpw, kNB, kFmt, kHad, kOpt, kRot, kW>::run(c, rm);
   if constexpr (kFmt == kFmtNvAmax) {
     __syncthreads();  // vote[] is reused by block_max
-    const float mx = block_max(amax, reinterpret_cast<float*>(vote));
+    const float mx = block_max<kW>(amax, reinterpret_cast<float*>(vote));
     if (threadIdx.x == 0) *amax_partial_slot(codes, blockIdx.x, g) = __float_as_uint(mx);
   }
 }
@@ -756,13 +757,23 @@ static int perm_launch(const Shape& s, const int32_t* perm, const uint16_t* x, u
   constexpr size_t kStatic = 2 * 2048 * kW * kTpw;
   const size_t share = (size_t)ci.lds / kWgs;  // > lds / (kWgs + 1), so kWgs fit, not more
   const size_t pad = share > kStatic + 1024 ? share - kStatic - 1024 : 0;
-  if constexpr (kTpw > 4) {  // wide rows: staged by direct-to-LDS loads, one work-group per CU
-    hipLaunchKernelGGL((rotq_perm_dma_kernel<kTpw, kFmt, kHad, kOpt, kRot>), dim3(grid),
-                       dim3(kThreads), 0, st, x, perm, c, sc, ts, rot, g);
-  } else {
-    hipLaunchKernelGGL((rotq_perm_kernel<kTpw, kFmt, kHad, kOpt, kRot, kW>), dim3(grid),
-                       dim3(64 * kW), pad, st, x, perm, c, sc, ts, rot, g);
-  }
+  hipLaunchKernelGGL((rotq_perm_kernel<kTpw, kFmt, kHad, kOpt, kRot, kW>), dim3(grid),
+                     dim3(64 * kW), pad, st, x, perm, c, sc, ts, rot, g);
+  return grid;
+}
+
+// Rows of 16385..32768 columns: staged by direct-to-LDS loads, one work-group
+// of kW waves per CU (the ring of row slots takes most of the LDS; kW * 64
+// threads share it).
+template <int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot, int kW, int kWgs = 1>
+static int perm_dma_launch(const Shape& s, const int32_t* perm, const uint16_t* x, uint8_t* c,
+                           uint8_t* sc, const float* ts, float* rot, const RotGeom& g,
+                           hipStream_t st) {
+  const DeviceInfo ci = device_info();
+  const int64_t wgs = (int64_t)ci.cus * kWgs;
+  const int grid = (int)(s.rows < wgs ? s.rows : wgs);
+  hipLaunchKernelGGL((rotq_perm_dma_kernel<kTpw, kFmt, kHad, kOpt, kRot, kW, kWgs>), dim3(grid),
+                     dim3(64 * kW), 0, st, x, perm, c, sc, ts, rot, g);
   return grid;
 }
 
@@ -778,9 +789,11 @@ static int perm_dispatch(const Shape& s, const int32_t* perm, const uint16_t* x,
   if (tpw <= 2) return perm_launch<1, kFmt, kHad, kOpt, kRot, 8>(s, perm, x, c, sc, ts, rot, g, st);
   if (tpw <= 3) return perm_launch<3, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
   if (tpw <= 4) return perm_launch<4, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
-  if (tpw <= 6) return perm_launch<6, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
-  if (tpw <= 7) return perm_launch<7, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
-  return perm_launch<8, kFmt, kHad, kOpt, kRot>(s, perm, x, c, sc, ts, rot, g, st);
+  // rows of 16385..32768 columns: sixteen waves of two tiles (measured on
+  // MI355X at 8192 x 28672 against four waves of seven tiles: MXFP4 107.1 ->
+  // 100.6 us, MXINT4 138.3 -> 104.4, NVFP4 + RaZeR 146.5 -> 111.8; eight waves
+  // of four tiles: 100.0, 112.9, 136.9)
+  return perm_dma_launch<2, kFmt, kHad, kOpt, kRot, 16>(s, perm, x, c, sc, ts, rot, g, st);
 }
 
 template <bool kHad, bool kFloor, bool kRot, bool kInt>

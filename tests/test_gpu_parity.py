@@ -329,8 +329,9 @@ def test_rotate_hadamard_strided(orc, fmt, rows, cols, floor_rule):
 
 
 # rows wider than 16384 take the kernel that stages rows straight into LDS:
-# 6, 7 and 8 MFMA tiles per wave (16416 and 20480 run as 6, with idle tiles),
-# one work-group per CU, row counts below, at and above the grid
+# sixteen waves of two MFMA tiles (16416 and 20480 leave waves and tiles
+# without a block), one work-group per CU, row counts below, at and above the
+# grid
 @pytest.mark.parametrize("rows,cols", [(3, 16416), (37, 20480), (5, 24576), (6, 28672),
                                        (2, 32768), (300, 28672), (1100, 28704)])
 def test_rotate_wide_rows(orc, rows, cols):
