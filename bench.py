@@ -305,7 +305,14 @@ def bench_c4(torch, fp4, inputs, args):
     log(f"[bench] generating c4 {rows}x{cols}")
     x = inputs.gen_c4()
     xs = dev_copies(torch, x, copies_for(x.nbytes))
-    n = len(xs)
+    # the outputs cycle too: enough code (and scale) buffers that what the
+    # steps write also exceeds twice the Infinity Cache, so that no step
+    # overwrites codes still held in the cache (that would spare HBM the
+    # writes); step i reads input copy i % len(xs) and writes buffer i % n
+    nin = len(xs)
+    n = copies_for(rows * cols // 2, nin)
+    n += (-n) % nin
+    xs = [xs[k % nin] for k in range(n)]
     codes = [torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda") for _ in range(n)]
     scales = [torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda") for _ in range(n)]
 
@@ -354,7 +361,7 @@ def bench_c4(torch, fp4, inputs, args):
                                "variance exp(1.5 z); channel permutation + block Hadamard-32 "
                                "+ MXFP4 (E8M0, block 32) quantize + pack",
                    "rows": rows, "cols": cols, "format": "mxfp4", "block": 32,
-                   "rotation": "perm+hadamard32", "input_copies": n},
+                   "rotation": "perm+hadamard32", "input_copies": nin, "output_copies": n},
         "roofline": roofline_c4(elems, ms),
         "extras": extras,
     }
@@ -400,12 +407,14 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
                                                              scales=scales[k], prepare=True)),
                ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxfp4_hadamard_only"] = gbs(ms, el, B_MX)
-    outb = torch.empty_like(xs[0])
-    ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], scales[k], fp4.MXFP4, out=outb,
+    # one output buffer per input copy: the outputs too cycle through more
+    # memory than the 256 MB Infinity Cache holds
+    outs = [torch.empty_like(xs[0]) for _ in range(n)]
+    ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], scales[k], fp4.MXFP4, out=outs[k],
                                                         prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxfp4_dequantize"] = gbs(ms, el, B_MX)
     ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], scales[k], fp4.MXFP4, perm=perm,
-                                                        hadamard=32, out=outb, prepare=True)),
+                                                        hadamard=32, out=outs[k], prepare=True)),
                ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxfp4_dequantize_unrotate"] = gbs(ms, el, B_MX)
 
@@ -426,7 +435,7 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     out["c4_nvfp4_razer_perm_h16_scale_given"] = gbs(ms, el, B_NV)
     ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], s16[k], fp4.NVFP4, fp4.RAZER,
                                                         t16[k], perm=perm16, hadamard=16,
-                                                        out=outb, prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
+                                                        out=outs[k], prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_nvfp4_razer_dequantize_unrotate"] = gbs(ms, el, B_NV)
     xf = xs[0].float()
     for name, (pm, had) in {"perm_h16": (perm16, 16), "h16": (None, 16),
@@ -445,7 +454,7 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
                                                              prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxint4_perm_h32_quantize"] = gbs(ms, el, B_MX)
     ms = timed(torch, per_copy(lambda k: fp4.dequantize(codes[k], scales[k], fp4.MXINT4, perm=perm,
-                                                        hadamard=32, out=outb, prepare=True)),
+                                                        hadamard=32, out=outs[k], prepare=True)),
                ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxint4_dequantize_unrotate"] = gbs(ms, el, B_MX)
     for name, (pm, had) in {"perm_h32": (perm, 32), "h32": (None, 32),
@@ -479,7 +488,7 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
                                                                scales=scales[k], prepare=True)),
                ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxfp4_learned_r_quantize"] = gbs(ms, el, B_MX)
-    ms = timed(torch, per_copy(lambda k: fp4.dequantize_r(codes[k], scales[k], ident, rt, out=outb,
+    ms = timed(torch, per_copy(lambda k: fp4.dequantize_r(codes[k], scales[k], ident, rt, out=outs[k],
                                                           prepare=True)), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c4_mxfp4_learned_r_dequantize"] = gbs(ms, el, B_MX)
     xf, zf = xs[0].float(), zs[0].float()
@@ -514,8 +523,9 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     out["c3_mxfp4_h32_quantize"] = gbs(ms, r3 * k3, B_MX)
     # the inverse: dequantize + H32 back to bf16 (codes of each input copy)
     q3s = [fp4.rotate_quantize(t, None, 32)[:2] for t in x3s]
-    o3 = torch.empty_like(x3)
-    d3 = [fp4.dequantize(c, sc, fp4.MXFP4, hadamard=32, out=o3, prepare=True) for c, sc in q3s]
+    o3 = [torch.empty_like(x3) for _ in q3s]
+    d3 = [fp4.dequantize(c, sc, fp4.MXFP4, hadamard=32, out=o, prepare=True)
+          for (c, sc), o in zip(q3s, o3)]
     ms = timed(torch, lambda i: d3[i % len(d3)].run(), ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c3_mxfp4_dequantize_h32"] = gbs(ms, r3 * k3, B_MX)
     del p3, x3s, q3s, d3, o3
@@ -572,8 +582,8 @@ def extra_rows(torch, fp4, inputs, xs, perm, codes, scales):
     graph_row("c2_nvfp4_plain_quantize_scale_given", q_plain, B_NV)
     for k in range(m):
         fp4.quantize(ys[k], fp4.NVFP4, fp4.RAZER, tensor_scale=tss[k], codes=cs[k], scales=ss[k])
-    ob = torch.empty_like(ys[0])
-    dq = plan(lambda k: fp4.dequantize(cs[k], ss[k], fp4.NVFP4, fp4.RAZER, tss[k], out=ob,
+    obs = [torch.empty_like(ys[0]) for _ in range(m)]
+    dq = plan(lambda k: fp4.dequantize(cs[k], ss[k], fp4.NVFP4, fp4.RAZER, tss[k], out=obs[k],
                                        prepare=True))
     ms = timed(torch, dq, 2 * ROW_STEPS, ROW_WARMUP, ROW_WARM_MS)
     out["c2_nvfp4_razer_dequantize"] = gbs(ms, el2, B_NV)
@@ -604,7 +614,10 @@ def wide_rows(torch, fp4, inputs):
     x = inputs.gen_c4(rows=rows, cols=cols)
     xs = dev_copies(torch, x, copies_for(x.nbytes))
     del x
-    n = len(xs)
+    nin = len(xs)
+    n = copies_for(rows * cols // 2, nin)  # code buffers beyond the cache as well
+    n += (-n) % nin
+    xs = [xs[k % nin] for k in range(n)]
     el = rows * cols
     perm = fp4.build_permutation(fp4.channel_energy(xs[0])).cuda()
     perm16 = fp4.build_permutation(fp4.channel_energy(xs[0]), 16).cuda()
@@ -1021,7 +1034,10 @@ def kernel_op(torch, fp4, inputs, args):
         x = inputs.gen_c4()
         xs = dev_copies(torch, x, copies_for(x.nbytes))
         del x
-        n = len(xs)
+        nin = len(xs)
+        n = copies_for(rows * cols // 2, nin)  # code buffers beyond the cache as well
+        n += (-n) % nin
+        xs = [xs[k % nin] for k in range(n)]
         nv = op in ("c4_perm_nvfp4_razer", "c4_unrot_nvfp4_razer")
         blk = 16 if nv else 32
         perm = fp4.build_permutation(fp4.channel_energy(xs[0]), blk).cuda()

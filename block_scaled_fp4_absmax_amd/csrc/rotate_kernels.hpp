@@ -268,11 +268,12 @@ struct PermCtx {
 template <int G, uint32_t kOff, int kTpw, int kFmt, bool kHad, bool kOpt, bool kRot, class Ctx,
           int kW = kWaves>
 __device__ __forceinline__ void perm_row(const Ctx& c, const uint8_t* buf, int32_t r) {
-    // Cache policy of the code stores, measured on MI355X at 16384 x 8192:
-    // plain write-back stores ran the MX formats faster than nontemporal ones
-    // (MXFP4 55.9 against 59.8 us, MXINT4 60.8 against 62.4), and NVFP4 2%
-    // slower (65.2 against 63.7).
-    constexpr int kCodeAux = kFmt == kFmtNv ? kNt : 0;
+    // Code stores are nontemporal. Write-back stores looked faster for the MX
+    // formats only while the same two code buffers were rewritten in turn
+    // (134 MB, which the 256 MB Infinity Cache keeps, so the rewrites never
+    // reached HBM); with the codes of successive calls spread over 536 MB they
+    // ran 62.5 us against 58.0 (MXFP4, 16384 x 8192).
+    constexpr int kCodeAux = kNt;
     const RotGeom& g = c.g;
     const RowRsrc q = row_rsrc<kRot>(c.x, c.codes, c.scales, c.rot, r, g);
     const uint32_t lane = threadIdx.x & 63u, n = lane & 31u, h = lane >> 5;
