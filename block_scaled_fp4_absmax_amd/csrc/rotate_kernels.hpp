@@ -392,9 +392,9 @@ struct PermRows {
 // work-groups a CU can hold. Rows of 4097..8192 columns run eight waves of
 // one tile each, two work-groups per CU (16 waves per CU): against four waves
 // of two tiles, each wave's share of a row step halves and twice as many
-// waves hide the gathers' LDS latency (16384 x 8192: MXFP4 56.0 -> 55.1 us,
-// NVFP4 + RaZeR 67.8 -> 63.9 us). Three such work-groups per CU (with one row
-// of look-ahead, to fit the registers) ran 11% slower; with four waves, three
+// waves hide the gathers' LDS latency (16384 x 8192: MXFP4 59.5 -> 58.0 us,
+// NVFP4 + RaZeR 65.2 -> 62.9 us). Three such work-groups per CU (with one row
+// of look-ahead, to fit the registers) ran 4% slower; with four waves, three
 // or four work-groups per CU ran slower than two, and one slower still. A
 // second row of look-ahead gained about 1%, more none. Launching more
 // work-groups than fit at once (each taking fewer rows, placed as slots free
