@@ -244,15 +244,24 @@ def sqnr_db(torch, x, xh):
 
 
 def cpu_model():
-    """The host CPU's model name (/proc/cpuinfo), or None."""
+    """The host CPU's model name with its family / model / stepping numbers
+    (/proc/cpuinfo, first processor; a virtual machine may report a generic
+    name), or None."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for ln in fh:
-                if ln.startswith("model name"):
-                    return ln.split(":", 1)[1].strip()
+                if not ln.strip():
+                    break  # end of the first processor's entry
+                k, _, v = ln.partition(":")
+                info[k.strip()] = v.strip()
     except OSError:
-        pass
-    return None
+        return None
+    name = info.get("model name")
+    if name is None:
+        return None
+    ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    return name + (f" ({', '.join(ids)})" if ids else "")
 
 
 def cpu_threads():
