@@ -785,26 +785,29 @@ def gemm_rows(torch, fp4, fmt):
     rows = {}
     for m, n, k in ((4096, 8192, 8192), (4096, 28672, 8192), (4096, 8192, 28672),
                     (16, 8192, 8192), (32, 28672, 8192)):
-        a = torch.randint(0, 256, (m, k // 2), dtype=torch.uint8, device="cuda", generator=g)
-        sa = torch.randint(lo, hi, (m, k // blk), dtype=torch.uint8, device="cuda", generator=g)
-        b = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device="cuda", generator=g)
-        sb = torch.randint(lo, hi, (n, k // blk), dtype=torch.uint8, device="cuda", generator=g)
-        c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        # operand and output sets cycle over more than twice the Infinity Cache,
+        # so no call finds its weights (or overwrites its output) still cached
+        nset = copies_for((m + n) * (k // 2 + k // blk) + 2 * m * n)
+
+        def rnd(shape, a_, b_):
+            return torch.randint(a_, b_, shape, dtype=torch.uint8, device="cuda", generator=g)
+
+        sets = [(rnd((m, k // 2), 0, 256), rnd((m, k // blk), lo, hi),
+                 rnd((n, k // 2), 0, 256), rnd((n, k // blk), lo, hi),
+                 torch.empty((m, n), dtype=torch.bfloat16, device="cuda")) for _ in range(nset)]
         row_major = None
         if not nv:
-            p0 = fp4.gemm(a, sa, b, sb, out=c, prepare=True)
-            ms0 = timed(torch, lambda i: p0.run(), 10, 2, ROW_WARM_MS)
+            p0 = [fp4.gemm(a, sa, b, sb, out=c, prepare=True) for a, sa, b, sb, c in sets]
+            ms0 = timed(torch, lambda i: p0[i % nset].run(), 10, 2, ROW_WARM_MS)
             row_major = {"ms": round(ms0, 4), "frac_mfma_peak": round(
                 2.0 * m * n * k / (ms0 * 1e-3) / 1e12 / peak, 4)}
-            ga = torch.randint(lo, hi, fp4.gemm_scale_shape(m, k), dtype=torch.uint8,
-                               device="cuda", generator=g)
-            gb = torch.randint(lo, hi, fp4.gemm_scale_shape(n, k), dtype=torch.uint8,
-                               device="cuda", generator=g)
-            pg = fp4.gemm(a, ga, b, gb, out=c, prepare=True, a_gemm_scales=True,
-                          b_gemm_scales=True)
+            pl = [fp4.gemm(a, rnd(fp4.gemm_scale_shape(m, k), lo, hi), b,
+                           rnd(fp4.gemm_scale_shape(n, k), lo, hi), out=c, prepare=True,
+                           a_gemm_scales=True, b_gemm_scales=True)
+                  for a, sa, b, sb, c in sets]
         else:
-            pg = fp4.gemm(a, sa, b, sb, out=c, prepare=True, **kw)
-        ms = timed(torch, lambda i: pg.run(), 10, 2, ROW_WARM_MS)
+            pl = [fp4.gemm(a, sa, b, sb, out=c, prepare=True, **kw) for a, sa, b, sb, c in sets]
+        ms = timed(torch, lambda i: pl[i % nset].run(), 10, 2, ROW_WARM_MS)
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         by = (m + n) * (k / 2 + k / blk) + 2 * m * n
         rows[f"{m}x{n}x{k}"] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
@@ -813,32 +816,38 @@ def gemm_rows(torch, fp4, fmt):
         if row_major is not None:
             rows[f"{m}x{n}x{k}"]["scales"] = "GEMM order"
             rows[f"{m}x{n}x{k}"]["row_major_scales"] = row_major
+        rows[f"{m}x{n}x{k}"]["operand_sets"] = nset
         if m <= 32:  # µs-scale launches: also their time replayed from a graph
-            us = graph_us(torch, lambda i: pg.run())
+            us = graph_us(torch, lambda i: pl[i % nset].run(), calls=max(20, nset))
             rows[f"{m}x{n}x{k}"]["graph_us_per_call"] = round(us, 2)
             rows[f"{m}x{n}x{k}"]["graph_frac_mfma_peak"] = round(
                 2.0 * m * n * k / (us * 1e-6) / 1e12 / peak, 4)
         if not nv and m >= 256:
-            rows[f"{m}x{n}x{k}"]["library"] = library_mx_gemm(torch, a, sa, b, sb, peak)
-        del a, sa, b, sb, c
+            rows[f"{m}x{n}x{k}"]["library"] = library_mx_gemm(torch, sets, peak)
+        del sets, pl
     return rows
 
 
-def library_mx_gemm(torch, a, sa, b, sb, peak):
+def library_mx_gemm(torch, sets, peak):
     """The same MXFP4 product through torch._scaled_mm (the ROCm math
     library's block-scaled FP4 GEMM), timed with the same protocol: a
     reference point for the hand-written kernel, not part of the path. Timing
     only (the operands are random bytes; the library's scale layout is not
     checked against ours)."""
     try:
-        A = a.view(torch.float4_e2m1fn_x2)
-        B = b.view(torch.float4_e2m1fn_x2)
-        SA, SB = sa.view(torch.float8_e8m0fnu), sb.view(torch.float8_e8m0fnu)
-        fn = lambda i: torch._scaled_mm(A, B.t(), SA, SB, out_dtype=torch.bfloat16)
+        ops = [(a.view(torch.float4_e2m1fn_x2), b.view(torch.float4_e2m1fn_x2),
+                sa.view(torch.float8_e8m0fnu), sb.view(torch.float8_e8m0fnu))
+               for a, sa, b, sb, _ in sets]
+
+        def fn(i):  # operands cycle as for the hand-written kernel (output allocated per call)
+            A, B, SA, SB = ops[i % len(ops)]
+            return torch._scaled_mm(A, B.t(), SA, SB, out_dtype=torch.bfloat16)
+
         fn(0)
         ms = timed(torch, fn, 10, 2, ROW_WARM_MS)
     except Exception as ex:  # not available in this torch build
         return {"error": f"{type(ex).__name__}: {str(ex)[:120]}"}
+    a, b = sets[0][0], sets[0][2]
     m, k = a.shape[0], 2 * a.shape[1]
     n = b.shape[0]
     tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
